@@ -1,0 +1,395 @@
+"""Checks that pin the CPU oracle to facts other than itself.
+
+Each ``pin_*`` function takes the oracle module (or an object with the same
+functions) and raises AssertionError when the oracle disagrees with a fixed
+fact: a hand-worked fixture, a closed form, an invariant, a textbook special
+case or brute force.  ``test_oracle_pins.py`` runs them on the real oracle;
+``test_oracle_mutations.py`` runs them on deliberately broken copies of oracle
+functions and requires that some pin fails, so the pins are shown to bite.
+"""
+from __future__ import annotations
+
+import cmath
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------- layout
+def pin_mask_golden(o):
+    """Hand-worked masks ("图解 Wan2.1 I2V" §4.1 step 3, §10 Q3/Q6)."""
+    for case in _golden("i2v_mask.json")["cases"]:
+        T = case["T"]
+        m = o.i2v_mask(T, 2, 4, case["known_pixel_frames"])
+        exp = np.array(case["mask_c_by_tau"], dtype=np.float64)
+        assert m.shape == (4, T, 2, 4)
+        for hh in range(2):
+            for ww in range(4):
+                assert np.array_equal(m[:, :, hh, ww], exp), (case, m[:, :, 0, 0])
+    # default = first pixel frame only
+    m = o.i2v_mask(4, 2, 2)
+    assert m[:, 0].min() == 1.0 and m[:, 1:].max() == 0.0
+
+
+def pin_i2v_input(o):
+    """4 + 16 = 20-channel y and a 16 + 20 = 36-channel input ("图解 Wan2.1 I2V" §4.1, §4.2, §8)."""
+    rng = np.random.default_rng(1)
+    x_t = rng.standard_normal((2, 16, 3, 4, 6))
+    z = rng.standard_normal((2, 16, 3, 4, 6))
+    x_in = o.build_i2v_input(x_t, z)
+    assert x_in.shape == (2, 36, 3, 4, 6)
+    assert np.array_equal(x_in[:, :16], x_t)
+    assert np.array_equal(x_in[:, 20:], z)
+    y = x_in[:, 16:]
+    assert y.shape[1] == 20
+    assert np.array_equal(x_in[:, 16:20], np.broadcast_to(o.i2v_mask(3, 4, 6), (2, 4, 3, 4, 6)))
+    # 48-channel latent (TI2V-5B-shaped): 48 + 4 + 48 = 100
+    assert o.build_i2v_input(np.zeros((1, 48, 2, 2, 2)), np.zeros((1, 48, 2, 2, 2))).shape[1] == 100
+
+
+def pin_patchify_golden(o):
+    g = _golden("patchify.json")
+    B, C, T, H, W = g["shape"]
+    x = np.zeros(g["shape"])
+    for c, f, r, col in itertools.product(range(C), range(T), range(H), range(W)):
+        x[0, c, f, r, col] = 1000 * c + 100 * f + 4 * r + col
+    p = o.patchify(x)
+    assert np.array_equal(p[0], np.array(g["tokens"], dtype=np.float64)), p[0]
+    assert np.array_equal(o.unpatchify(p, C, T, H, W), x)
+
+
+def pin_token_counts(o):
+    for case in _golden("token_counts.json")["cases"]:
+        C, T, H, W = case["latent"]
+        p = o.patchify(np.zeros((1, 1, T, H, W)))
+        assert p.shape[1] == case["S"], (case, p.shape)
+
+
+def pin_patch_round_trip(o):
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((2, 3, 3, 4, 6))
+    p = o.patchify(x)
+    assert p.shape == (2, 3 * 2 * 3, 12)
+    assert np.array_equal(o.unpatchify(p, 3, 3, 4, 6), x)
+
+
+def pin_patch_embed_conv(o):
+    """patchify + matrix product equals a direct Conv3d with kernel = stride = (1,2,2)."""
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((1, 3, 2, 4, 6))
+    w = rng.standard_normal((5, 12))
+    b = rng.standard_normal(5)
+    direct = o.conv3d_patch_embed_direct(x, w, b)
+    via = o.patch_embed(o.patchify(x), w, b)
+    assert np.allclose(direct, via, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ embedding
+def pin_sinusoid(o):
+    e = o.sinusoidal_embedding(0.0, 256)
+    assert e.shape == (256,)
+    assert np.array_equal(e, np.concatenate([np.ones(128), np.zeros(128)]))
+    e = o.sinusoidal_embedding(0.37, 256)
+    assert np.allclose(e[:128] ** 2 + e[128:] ** 2, 1.0, atol=1e-14)
+    # frequency 0 (i = 0) is 1: the first pair is (cos 370, sin 370)
+    assert abs(e[0] - math.cos(370.0)) < 1e-12 and abs(e[128] - math.sin(370.0)) < 1e-12
+
+
+def pin_time_embed_identity(o):
+    """With identity weights and zero biases: e = SiLU(emb), e0[j] = SiLU(SiLU(emb))."""
+    d = 256
+    eye = np.eye(d)
+    w = {"wt1": eye, "bt1": np.zeros(d), "wt2": eye, "bt2": np.zeros(d),
+         "wtp": np.concatenate([eye] * 6), "btp": np.zeros(6 * d)}
+    e, e0 = o.time_embed(0.0, w, 256)
+    silu1 = np.array([1.0 / (1.0 + math.exp(-1.0))] * 128 + [0.0] * 128)
+    assert np.allclose(e, silu1, atol=1e-15)
+    s2 = np.array([v / (1.0 + math.exp(-v)) for v in silu1])
+    assert e0.shape == (6, d) and np.allclose(e0, s2[None, :], atol=1e-15)
+
+
+# ---------------------------------------------------------------------- norms
+def pin_layer_norm(o):
+    rng = np.random.default_rng(4)
+    x = 3.0 + 2.5 * rng.standard_normal((7, 64))
+    y = o.layer_norm(x, eps=0.0)
+    assert np.allclose(y.mean(-1), 0.0, atol=1e-12)
+    assert np.allclose(y.var(-1), 1.0, atol=1e-12)
+    # eps enters under the square root with the biased variance
+    y = o.layer_norm(x, eps=0.5)
+    ref = (x - x.mean(-1, keepdims=True)) / np.sqrt(np.var(x, -1, keepdims=True) + 0.5)
+    assert np.allclose(y, ref, atol=1e-12)
+    # a constant row normalises to 0, so modulation returns the shift exactly
+    c = np.full((1, 16), 4.0)
+    shift, scale = rng.standard_normal(16), rng.standard_normal(16)
+    assert np.array_equal(o.modulate(o.layer_norm(c), shift, scale), shift[None])
+    # scale = shift = 0 keeps the normalised row
+    z = np.zeros(64)
+    assert np.array_equal(o.modulate(o.layer_norm(x), z, z), o.layer_norm(x))
+    # affine form
+    wgt, bias = rng.standard_normal(64), rng.standard_normal(64)
+    assert np.allclose(o.layer_norm(x, 1e-6, wgt, bias), o.layer_norm(x, 1e-6) * wgt + bias, atol=1e-12)
+
+
+def pin_rms_norm(o):
+    g = np.linspace(0.5, 1.5, 32)
+    for c in (0.0, 1e-4, 0.3, -2.0, 7.0):
+        y = o.rms_norm(np.full((1, 32), c), g, eps=1e-6)
+        assert np.allclose(y[0], g * c / math.sqrt(c * c + 1e-6), rtol=1e-13, atol=0)
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((5, 48)) * 3
+    y = o.rms_norm(x, np.ones(48), eps=0.0)
+    assert np.allclose(np.sqrt((y * y).mean(-1)), 1.0, atol=1e-13)
+    # per-token scalar: rows scale independently
+    assert np.allclose(o.rms_norm(x * 4.0, np.ones(48), 0.0), y, atol=1e-13)
+
+
+# ----------------------------------------------------------------------- RoPE
+def _textbook_rope_1d(z_pairs, pos, width, base=10000.0):
+    """RoFormer's 1D rotary embedding in complex form: pair m of a width-`width`
+    vector is multiplied by exp(i * pos * base^(-2m/width))."""
+    out = []
+    for m, (a, b) in enumerate(z_pairs):
+        z = complex(a, b) * cmath.exp(1j * pos * base ** (-2.0 * m / width))
+        out.append((z.real, z.imag))
+    return out
+
+
+def pin_rope_segments(o):
+    assert tuple(o.rope_segments(128)) == (44, 42, 42)
+    assert tuple(o.rope_segments(64)) == (24, 20, 20)
+
+
+def pin_rope_identity_and_norm(o):
+    rng = np.random.default_rng(6)
+    for hd in (64, 128):
+        x = rng.standard_normal((5, 3, hd))
+        assert np.array_equal(o.rope_3d(x, np.zeros((5, 3), dtype=int)), x)
+        pos = rng.integers(0, 60, size=(5, 3))
+        y = o.rope_3d(x, pos)
+        # every adjacent channel pair keeps its norm
+        assert np.allclose(y[..., 0::2] ** 2 + y[..., 1::2] ** 2,
+                           x[..., 0::2] ** 2 + x[..., 1::2] ** 2, atol=1e-12)
+
+
+def pin_rope_relative(o):
+    """<R(p) q, R(p') k> depends on p - p' only (per axis)."""
+    rng = np.random.default_rng(7)
+    for hd in (64, 128):
+        q = rng.standard_normal((1, 1, hd))
+        k = rng.standard_normal((1, 1, hd))
+        p1, p2 = np.array([[3, 5, 7]]), np.array([[1, 9, 2]])
+        d = p1 - p2
+        base = (o.rope_3d(q, p1) * o.rope_3d(k, p2)).sum()
+        for shift in ([4, 0, 0], [0, 11, 0], [0, 0, 6], [2, 3, 13]):
+            s = np.array([shift])
+            val = (o.rope_3d(q, p1 + s) * o.rope_3d(k, p2 + s)).sum()
+            assert abs(val - base) < 1e-10, (hd, shift)
+        # and changes when the offset changes
+        val = (o.rope_3d(q, p1 + np.array([[1, 0, 0]])) * o.rope_3d(k, p2)).sum()
+        assert abs(val - base) > 1e-6
+        del d
+
+
+def pin_rope_axes_textbook(o):
+    """Moving along one axis rotates only that axis' channel segment, exactly as the
+    textbook 1D RoPE of the segment's width; the other segments are untouched."""
+    rng = np.random.default_rng(8)
+    for hd in (64, 128):
+        segs = o.rope_segments(hd)
+        starts = [0, segs[0], segs[0] + segs[1]]
+        x = rng.standard_normal((1, 2, hd))
+        for axis in range(3):
+            for p in (1, 5, 37):
+                pos = np.zeros((1, 3), dtype=int)
+                pos[0, axis] = p
+                y = o.rope_3d(x, pos)
+                for h in range(2):
+                    for a2 in range(3):
+                        sl = slice(starts[a2], starts[a2] + segs[a2])
+                        if a2 != axis:
+                            assert np.array_equal(y[0, h, sl], x[0, h, sl])
+                        else:
+                            pairs = list(zip(x[0, h, sl][0::2], x[0, h, sl][1::2]))
+                            ref = _textbook_rope_1d(pairs, p, segs[a2])
+                            got = list(zip(y[0, h, sl][0::2], y[0, h, sl][1::2]))
+                            assert np.allclose(np.array(got), np.array(ref), atol=1e-12), (hd, axis, p)
+
+
+# ------------------------------------------------------------------ attention
+def _brute_attention(q, k, v):
+    """Softmax attention with pure-Python loops: out_i = sum_j w_ij v_j,
+    w_ij = exp(s_ij) / sum_l exp(s_il), s_ij = <q_i, k_j> / sqrt(d)."""
+    nq, d = len(q), len(q[0])
+    out = []
+    for i in range(nq):
+        s = [sum(q[i][c] * k[j][c] for c in range(d)) / math.sqrt(d) for j in range(len(k))]
+        ex = [math.exp(val) for val in s]
+        z = sum(ex)
+        out.append([sum(ex[j] / z * v[j][c] for j in range(len(k))) for c in range(len(v[0]))])
+    return np.array(out)
+
+
+def pin_attention_bruteforce(o):
+    rng = np.random.default_rng(9)
+    for nq, nk, d in ((3, 5, 4), (4, 7, 8), (1, 1, 2)):
+        q, k, v = (rng.standard_normal((n, d)) for n in (nq, nk, nk))
+        assert np.allclose(o.attention(q, k, v), _brute_attention(q.tolist(), k.tolist(), v.tolist()),
+                           atol=1e-12)
+
+
+def pin_attention_special(o):
+    rng = np.random.default_rng(10)
+    q = rng.standard_normal((6, 16)) * 3
+    v = rng.standard_normal((9, 16))
+    # K = 0: uniform weights -> mean of V's rows
+    assert np.allclose(o.attention(q, np.zeros((9, 16)), v), v.mean(0)[None], atol=1e-12)
+    # one key: output is that value row
+    k1, v1 = rng.standard_normal((1, 16)), rng.standard_normal((1, 16))
+    assert np.allclose(o.attention(q, k1, v1), np.repeat(v1, 6, 0), atol=1e-12)
+    # joint permutation of (K, V) rows leaves the output unchanged: no mask, no causality
+    k = rng.standard_normal((9, 16))
+    perm = rng.permutation(9)
+    assert np.allclose(o.attention(q, k, v), o.attention(q, k[perm], v[perm]), atol=1e-12)
+
+
+def pin_attention_lse_merge(o):
+    """Attention over key chunks merged with their log-sum-exp equals attention over all
+    keys -- the identity tile-by-tile (flash / ring) attention relies on."""
+    rng = np.random.default_rng(11)
+    q, k, v = rng.standard_normal((5, 8)), rng.standard_normal((23, 8)), rng.standard_normal((23, 8))
+    full = o.attention(q, k, v)
+    parts, lses = [], []
+    for lo in range(0, 23, 7):
+        kk, vv = k[lo:lo + 7], v[lo:lo + 7]
+        s = q @ kk.T / math.sqrt(8)
+        lse = np.log(np.exp(s).sum(-1))
+        parts.append(o.attention(q, kk, vv))
+        lses.append(lse)
+    lses = np.stack(lses)
+    wts = np.exp(lses - np.log(np.exp(lses).sum(0)))
+    merged = sum(wts[i][:, None] * parts[i] for i in range(len(parts)))
+    assert np.allclose(merged, full, atol=1e-12)
+
+
+# ----------------------------------------------------------------- block / FM
+def _tiny_block_inputs(seed=12, S_grid=(2, 2, 3), dim=24, heads=2, ffn=40, L=5, Li=3):
+    rng = np.random.default_rng(seed)
+    n = lambda *s: 0.2 * rng.standard_normal(s)
+    w = {"mod_bias": n(6, dim), "wq": n(dim, dim), "bq": n(dim), "wk": n(dim, dim), "bk": n(dim),
+         "wv": n(dim, dim), "bv": n(dim), "gq": 1 + n(dim), "gk": 1 + n(dim), "wo": n(dim, dim),
+         "bo": n(dim), "ln3_w": 1 + n(dim), "ln3_b": n(dim), "wcq": n(dim, dim), "bcq": n(dim),
+         "wco": n(dim, dim), "bco": n(dim), "w1": n(ffn, dim), "b1": n(ffn), "w2": n(dim, ffn),
+         "b2": n(dim)}
+    S = S_grid[0] * S_grid[1] * S_grid[2]
+    x = rng.standard_normal((2, S, dim))
+    e0 = n(2, 6, dim)
+    kv = [(n(L, dim), n(L, dim), n(Li, dim), n(Li, dim)) for _ in range(2)]
+    return x, e0, w, kv, S_grid, heads
+
+
+def pin_block_adaln_zero(o):
+    """gate1 = gate2 = 0 and a zero cross-attention output projection make the block the
+    identity, bit for bit ("图解 Wan2.1 I2V" §5.2: gates start at zero so each block starts
+    as the identity)."""
+    x, e0, w, kv, grid, heads = _tiny_block_inputs()
+    w = dict(w)
+    mb = w["mod_bias"].copy()
+    e0 = e0.copy()
+    e0[:, 2, :] = 0.0
+    e0[:, 5, :] = 0.0
+    mb[2] = 0.0
+    mb[5] = 0.0
+    w["mod_bias"] = mb
+    w["wco"] = np.zeros_like(w["wco"])
+    w["bco"] = np.zeros_like(w["bco"])
+    y = o.block_fwd(x, e0, w, kv, grid, heads)
+    assert np.array_equal(y, x)
+    # with only the FFN gate open, the block changes x
+    e0[:, 5, :] = 0.3
+    assert not np.allclose(o.block_fwd(x, e0, w, kv, grid, heads), x)
+
+
+def pin_block_dual_stream_reduces(o):
+    """With a zero image value projection the dual-stream (image + text) cross-attention
+    equals the text-only one ("图解 Wan2.1 I2V" §5.4: the two streams are added)."""
+    x, e0, w, kv, grid, heads = _tiny_block_inputs()
+    kv0 = [(kt, vt, ki, np.zeros_like(vi)) for kt, vt, ki, vi in kv]
+    kv1 = [(kt, vt, None, None) for kt, vt, _, _ in kv]
+    assert np.array_equal(o.block_fwd(x, e0, w, kv0, grid, heads),
+                          o.block_fwd(x, e0, w, kv1, grid, heads))
+
+
+def pin_block_rows_mode(o):
+    """Sampled-row mode returns exactly those rows of the full block output."""
+    x, e0, w, kv, grid, heads = _tiny_block_inputs()
+    full = o.block_fwd(x, e0, w, kv, grid, heads)
+    rows = np.array([0, 3, 11])
+    assert np.allclose(o.block_fwd(x, e0, w, kv, grid, heads, rows=rows), full[:, rows], atol=1e-13)
+
+
+def pin_block_non_causal(o):
+    """Full, non-causal self-attention: perturbing only the last token changes the first
+    token's block output ("图解 Wan2.1 I2V" §5.3; "Wan 技术深度解析" §2.5)."""
+    x, e0, w, kv, grid, heads = _tiny_block_inputs()
+    y = o.block_fwd(x, e0, w, kv, grid, heads)
+    x2 = x.copy()
+    x2[:, -1] += np.linspace(-1.0, 2.0, x.shape[-1])  # perturb the last token only (not by a
+    # constant: LayerNorm would cancel it)
+    y2 = o.block_fwd(x2, e0, w, kv, grid, heads)
+    assert np.all(np.abs(y2[:, 0] - y[:, 0]).max(-1) > 1e-6), "first token must see the last one"
+    # and the perturbation reaches the first token only through self-attention
+    w0 = dict(w)
+    e0z = e0.copy()
+    e0z[:, 2, :] = 0.0
+    w0["mod_bias"] = np.array(w["mod_bias"]).copy()
+    w0["mod_bias"][2] = 0.0
+    assert np.array_equal(o.block_fwd(x2, e0z, w0, kv, grid, heads)[:, 0],
+                          o.block_fwd(x, e0z, w0, kv, grid, heads)[:, 0])
+
+
+def pin_fm_straight_line(o):
+    """Straight path x_t = (1-t) x0 + t x1 with constant velocity x1 - x0: N exact-velocity
+    Euler steps from t = 0 land on x1 ("Wan 技术深度解析" §2.7, §8.3); in the mirrored
+    convention x_t = (1-t) x0 + t eps, v = eps - x0, N steps with dt = -1/N from t = 1 land
+    on x0 ("图解 Wan2.1 I2V" §6, §7)."""
+    rng = np.random.default_rng(13)
+    x0, x1 = rng.standard_normal(1000), rng.standard_normal(1000)
+    for N in (1, 4, 25, 50):
+        x = x0.copy()
+        for _ in range(N):
+            x = o.euler_step(x, x1 - x0, 1.0 / N)
+        assert np.allclose(x, x1, rtol=0, atol=1e-13), N
+        eps = x1
+        x = eps.copy()
+        for _ in range(N):
+            x = o.euler_step(x, eps - x0, -1.0 / N)
+        assert np.allclose(x, x0, rtol=0, atol=1e-13), N
+    # a single step of any size along the line stays on the line
+    t, dt = 0.3, 0.45
+    xt = (1 - t) * x0 + t * x1
+    assert np.allclose(o.euler_step(xt, x1 - x0, dt), (1 - t - dt) * x0 + (t + dt) * x1, atol=1e-13)
+
+
+def pin_cfg(o):
+    """v = v_u + s (v_c - v_u): s = 0 gives v_u, s = 1 gives v_c ("图解 Wan2.1 I2V" §7)."""
+    rng = np.random.default_rng(14)
+    vc, vu = rng.standard_normal(100), rng.standard_normal(100)
+    assert np.array_equal(o.cfg_combine(vc, vu, 0.0), vu)
+    assert np.allclose(o.cfg_combine(vc, vu, 1.0), vc, rtol=0, atol=1e-15)
+    assert np.allclose(o.cfg_combine(vc, vu, 5.0), vu + 5.0 * (vc - vu), atol=1e-14)
+    x = rng.standard_normal(100)
+    assert np.array_equal(o.cfg_euler(x, vc, None, 7.0, -0.1), o.euler_step(x, vc, -0.1))
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

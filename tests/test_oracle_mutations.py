@@ -1,0 +1,180 @@
+"""Planted mistakes in the CPU oracle must be caught by its pins (no GPU).
+
+Each case swaps one oracle function for a plausible wrong version (a dropped
+term, a wrong sign, index or layout) inside the oracle module and requires that
+at least one pin in ``oracle_pins`` fails.  The mistakes are planted in the
+oracle, on the CPU, never in the HIP path.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import wan_oracle as wo
+from tests import oracle_pins as pins
+
+
+def _mask_raw_reshape(T, H, W, known_pixel_frames=None):
+    F = 4 * (T - 1) + 1
+    known = np.zeros(F) if known_pixel_frames is None else np.asarray(known_pixel_frames, float)
+    if known_pixel_frames is None:
+        known[0] = 1
+    seq = np.concatenate([np.repeat(known[:1], 4), known[1:]])
+    m = seq.reshape(4, T)  # raw reshape instead of grouping 4 entries per latent frame
+    return np.broadcast_to(m[:, :, None, None], (4, T, H, W)).copy()
+
+
+def _patchify_kw_kh(x):
+    x = np.asarray(x, float)
+    B, C, T, H, W = x.shape
+    p = wo.__dict__["_orig_patchify"](x)
+    return p.reshape(B, -1, C, 2, 2).transpose(0, 1, 2, 4, 3).reshape(B, -1, 4 * C)
+
+
+def _rope_variant(kind):
+    def rope(x, pos, theta=10000.0):
+        x = np.asarray(x, float)
+        N, H, hd = x.shape
+        segs = list(wo.rope_segments(hd))
+        if kind == "segments_swapped":
+            segs = [segs[1], segs[0], segs[2]]
+        out = x.copy()
+        c0 = 0
+        for axis, n in enumerate(segs):
+            for m in range(n // 2):
+                width = hd if kind == "freq_over_head_dim" else n
+                ang = pos[:, axis] * theta ** (-2.0 * m / width)
+                c, s = np.cos(ang)[:, None], np.sin(ang)[:, None]
+                if kind == "rotate_half":
+                    i0, i1 = c0 + m, c0 + m + n // 2
+                else:
+                    i0, i1 = c0 + 2 * m, c0 + 2 * m + 1
+                a, b = x[:, :, i0], x[:, :, i1]
+                if kind == "sign":
+                    out[:, :, i0], out[:, :, i1] = a * c + b * s, -a * s + b * c
+                else:
+                    out[:, :, i0], out[:, :, i1] = a * c - b * s, a * s + b * c
+            c0 += n
+        return out
+    return rope
+
+
+def _attention_variant(kind):
+    def attn(q, k, v):
+        q, k, v = (np.asarray(a, float) for a in (q, k, v))
+        scale = 1.0 / q.shape[-1] if kind == "scale_1_over_d" else 1.0 / math.sqrt(q.shape[-1])
+        s = q @ k.T * scale
+        axis = 0 if kind == "softmax_over_queries" else -1
+        p = np.exp(s - s.max(axis=axis, keepdims=True))
+        p = p / p.sum(axis=axis, keepdims=True)
+        return p @ v
+    return attn
+
+
+def _ln_unbiased(x, eps=1e-6, weight=None, bias=None):
+    x = np.asarray(x, float)
+    mu = x.mean(-1, keepdims=True)
+    y = (x - mu) / np.sqrt(x.var(-1, ddof=1, keepdims=True) + eps)
+    if weight is not None:
+        y = y * weight
+    if bias is not None:
+        y = y + bias
+    return y
+
+
+def _rms_sum(x, g, eps=1e-6):
+    x = np.asarray(x, float)
+    return x / np.sqrt((x * x).sum(-1, keepdims=True) + eps) * g
+
+
+def _modulate_no_one(xn, shift, scale):
+    return np.asarray(xn) * np.asarray(scale) + np.asarray(shift)
+
+
+def _euler_wrong_sign(x, v, dt):
+    return np.asarray(x) - dt * np.asarray(v)
+
+
+def _cfg_swapped(v_cond, v_uncond, s):
+    return np.asarray(v_cond) + s * (np.asarray(v_uncond) - np.asarray(v_cond))
+
+
+def _sinusoid_sin_first(t, freq_dim=256, t_scale=1000.0, base=10000.0):
+    e = wo.__dict__["_orig_sinusoidal_embedding"](t, freq_dim, t_scale, base)
+    h = freq_dim // 2
+    return np.concatenate([e[h:], e[:h]])
+
+
+def _time_embed_no_silu(t, w, freq_dim=256):
+    emb = wo.sinusoidal_embedding(t, freq_dim)
+    e = wo.linear(wo.silu(wo.linear(emb, w["wt1"], w["bt1"])), w["wt2"], w["bt2"])
+    return e, wo.linear(e, w["wtp"], w["btp"]).reshape(6, -1)
+
+
+def _mha_joint_softmax_factory():
+    orig_block = wo.block_fwd
+
+    def block(x, e0, w, kv, grid, heads, rows=None, **kw):
+        # one softmax over the concatenated image + text keys instead of two
+        kv2 = []
+        for kt, vt, ki, vi in kv:
+            if ki is None:
+                kv2.append((kt, vt, None, None))
+            else:
+                kv2.append((np.concatenate([ki, kt]), np.concatenate([vi, vt]), None, None))
+        return orig_block(x, e0, w, kv2, grid, heads, rows=rows, **kw)
+    return block
+
+
+def _block_ungated_factory():
+    orig_block = wo.block_fwd
+
+    def block(x, e0, w, kv, grid, heads, rows=None, **kw):
+        # gate1 dropped: the self-attention branch is added with weight 1
+        w2 = dict(w)
+        mb = np.array(w["mod_bias"], float).copy()
+        e0 = np.array(e0, float).copy()
+        e0[:, 2, :] = 1.0
+        mb[2] = 0.0
+        w2["mod_bias"] = mb
+        return orig_block(x, e0, w2, kv, grid, heads, rows=rows, **kw)
+    return block
+
+
+MUTANTS = {
+    "mask_raw_reshape": ("i2v_mask", lambda: _mask_raw_reshape),
+    "patch_vector_kw_kh": ("patchify", lambda: _patchify_kw_kh),
+    "rope_rotate_half_pairs": ("rope_3d", lambda: _rope_variant("rotate_half")),
+    "rope_freq_over_head_dim": ("rope_3d", lambda: _rope_variant("freq_over_head_dim")),
+    "rope_sign": ("rope_3d", lambda: _rope_variant("sign")),
+    "rope_segments_swapped": ("rope_3d", lambda: _rope_variant("segments_swapped")),
+    "attention_scale_1_over_d": ("attention", lambda: _attention_variant("scale_1_over_d")),
+    "attention_softmax_axis": ("attention", lambda: _attention_variant("softmax_over_queries")),
+    "layer_norm_unbiased_var": ("layer_norm", lambda: _ln_unbiased),
+    "rms_norm_sum_not_mean": ("rms_norm", lambda: _rms_sum),
+    "modulate_drops_one": ("modulate", lambda: _modulate_no_one),
+    "euler_wrong_sign": ("euler_step", lambda: _euler_wrong_sign),
+    "cfg_roles_swapped": ("cfg_combine", lambda: _cfg_swapped),
+    "sinusoid_sin_first": ("sinusoidal_embedding", lambda: _sinusoid_sin_first),
+    "time_projection_no_silu": ("time_embed", lambda: _time_embed_no_silu),
+    "cross_joint_softmax": ("block_fwd", _mha_joint_softmax_factory),
+    "self_attention_ungated": ("block_fwd", _block_ungated_factory),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    target, factory = MUTANTS[name]
+    monkeypatch.setitem(wo.__dict__, "_orig_patchify", wo.patchify)
+    monkeypatch.setitem(wo.__dict__, "_orig_sinusoidal_embedding", wo.sinusoidal_embedding)
+    mutant = factory()
+    monkeypatch.setattr(wo, target, mutant)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(wo)
+        except AssertionError:
+            caught.append(pin.__name__)
+        except Exception as exc:  # a crash on a planted mistake also counts as caught
+            caught.append(f"{pin.__name__}({type(exc).__name__})")
+    assert caught, f"no pin caught the planted mistake {name}"
