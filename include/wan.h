@@ -1,0 +1,230 @@
+/*
+ * wan.h -- C ABI of libwan.so: one Wan-style video DiT denoise step on an
+ * AMD Instinct MI355X (gfx950), built from hand-written HIP kernels.
+ *
+ * Pages cited (titles as they appear on them):
+ *   [I2V]  "图解 Wan2.1 I2V：从一张图到一段视频，模型到底发生了什么" (liyongzhi.xyz)
+ *   [DEEP] "Wan（通义万相）：大规模视频生成基础模型 — 技术深度解析 & Wan2.1 vs Wan2.2对比"
+ *          (devpress.csdn.net)
+ *   [TI2V] "Wan2.2 TI2V-5B" (lnwmold.com)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are caller-owned DEVICE pointers, dense and row-major in the
+ *    layouts stated, 16-byte aligned.  Host pointers are named *_host.
+ *  - Every call is asynchronous on `stream` (NULL = the default stream).  The
+ *    library never allocates, frees or synchronises and keeps no pointer after
+ *    it returns; buffers must stay alive until the stream has consumed them.
+ *  - Return value: WAN_OK (0) or a negative wan_status.  Argument errors are
+ *    detected on the host before anything is enqueued.  A failed launch
+ *    returns WAN_EHIP; device faults surface at the caller's next
+ *    synchronisation.  wan_last_error() gives a thread-local message.
+ *  - Linear weights are stored [out, in] (y = x W^T + b).  "dtype" tensors are
+ *    float (WAN_F32) or bf16 (WAN_BF16, raw 16-bit storage); biases, gains,
+ *    modulation, latents and the residual stream are always float32.
+ *  - Outputs never alias inputs, except the in-place x of wan_dit_block_fwd
+ *    and wan_fm_euler_step.
+ */
+#ifndef WAN_H
+#define WAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The same type as HIP's hipStream_t. */
+typedef struct ihipStream_t* wan_stream_t;
+
+typedef enum {
+  WAN_OK = 0,
+  WAN_EINVAL = -1,       /* bad argument: null/misaligned pointer, inconsistent or non-positive size */
+  WAN_EUNSUPPORTED = -2, /* valid but not built: head_dim not 64/128, dim > 6144, flags != 0, ... */
+  WAN_EWORKSPACE = -3,   /* ws_bytes below the size the matching *_workspace_bytes() returns */
+  WAN_EHIP = -4          /* a HIP launch failed */
+} wan_status;
+
+typedef enum { WAN_F32 = 0, WAN_BF16 = 1 } wan_dtype;
+
+/* Latent [B, C, T, H, W] float32; H and W even.  Tokens S = T * (H/2) * (W/2) ([I2V] §5.1). */
+typedef struct {
+  int32_t B, C, T, H, W;
+} wan_latent_shape;
+
+/* Token grid (frames, rows, columns) = (T, H/2, W/2): the 3D RoPE positions ([I2V] §5.3). */
+typedef struct {
+  int32_t T, Hp, Wp;
+} wan_grid;
+
+/* Block hyper-parameters.  dim = heads * head_dim; head_dim 64 or 128; dim % 8 == 0, dim <= 6144;
+ * text_len > 0 text keys; img_len >= 0 image keys (0 = single-stream cross-attention).
+ * Proposed eps 1e-6 for both norms and rope_theta 10000.  flags must be 0 (reserved). */
+typedef struct {
+  int32_t dim, heads, head_dim, ffn_dim;
+  int32_t text_len, img_len;
+  int32_t dtype; /* wan_dtype */
+  uint32_t flags;
+  float ln_eps, rms_eps, rope_theta;
+} wan_block_cfg;
+
+/* Weights of one DiT block ([I2V] §5.2-§5.5; per-block modulation bias [DEEP] §2.5).
+ * dtype matrices: wqkv [3*dim, dim] = rows [W_q; W_k; W_v]; wo, wcq, wco [dim, dim];
+ * w1 [ffn_dim, dim]; w2 [dim, ffn_dim].  float32 vectors: mod_bias [6, dim] (chunks shift1, scale1,
+ * gate1, shift2, scale2, gate2); bqkv [3*dim]; gq, gk [dim] RMSNorm gains; bo; ln3_w, ln3_b [dim]
+ * (affine LayerNorm before cross-attention); bcq, bco [dim]; b1 [ffn_dim]; b2 [dim].
+ * Bias pointers may be NULL (zero bias); all others are required. */
+typedef struct {
+  const float* mod_bias;
+  const void* wqkv;
+  const float* bqkv;
+  const float *gq, *gk;
+  const void* wo;
+  const float* bo;
+  const float *ln3_w, *ln3_b;
+  const void* wcq;
+  const float* bcq;
+  const void* wco;
+  const float* bco;
+  const void* w1;
+  const float* b1;
+  const void* w2;
+  const float* b2;
+} wan_block_weights;
+
+/* Cross-attention keys/values of one block, computed once per generation by wan_cross_kv_fwd
+ * (context and weights do not change across sampling steps, [I2V] §7).
+ *   k_txt  [B, text_len, dim] dtype;   vt_txt [B, heads, head_dim, Lpad_txt] dtype (V transposed
+ *   per head, zero for keys >= text_len);  Lpad = text_len rounded up to a multiple of 64.
+ *   k_img / vt_img likewise with img_len (NULL when img_len == 0). */
+typedef struct {
+  const void *k_txt, *vt_txt, *k_img, *vt_img;
+} wan_cross_kv;
+
+/* Cross-attention K/V projection weights of one block: text [W_k; W_v] = wkv_txt [2*dim, dim]
+ * (+ bkv_txt [2*dim]); image (img_len > 0) wkv_img [2*dim, dim] (+ bkv_img). */
+typedef struct {
+  const void* wkv_txt;
+  const float* bkv_txt;
+  const void* wkv_img;
+  const float* bkv_img;
+} wan_cross_kv_weights;
+
+/* Timestep MLP shared by all blocks ([I2V] §5.2; [DEEP] §2.5): wt1 [dim, freq_dim], wt2 [dim, dim],
+ * wtp [6*dim, dim] dtype; biases float32 (may be NULL). */
+typedef struct {
+  const void* wt1;
+  const float* bt1;
+  const void* wt2;
+  const float* bt2;
+  const void* wtp;
+  const float* btp;
+} wan_time_weights;
+
+/* Head ([I2V] §5.5): head_mod [2, dim] float32 (shift, scale biases); wh [4*C_out, dim] dtype;
+ * bh [4*C_out] float32 (may be NULL). */
+typedef struct {
+  const float* head_mod;
+  const void* wh;
+  const float* bh;
+} wan_head_weights;
+
+/* ---------------------------------------------------------------------------------------------- */
+
+/* a1 -- image-to-video input ([I2V] §4.1 steps 3-4, §4.2; layout of the mask per §10 Q3/Q6).
+ * x_in [B, 2C+4, T, H, W] = [x_t, mask, z_img] along channels; mask channel c of latent frame t is
+ * entry 4t+c of the pixel-frame flag sequence (frame 0's flag repeated 4 times, then frames 1..F-1,
+ * F = 4(T-1)+1).  known_pixel_frames_host: F host bytes (nonzero = known), or NULL for "frame 0
+ * only".  x_t, z_img [B, C, T, H, W] float32.  T <= 64.  Bit-exact copy. */
+int wan_build_i2v_input(const float* x_t, const float* z_img, const uint8_t* known_pixel_frames_host,
+                        wan_latent_shape shape, float* x_in, wan_stream_t stream);
+
+/* a2 -- (1,2,2) patchify ([I2V] §5.1): p[b, (f*Hp+i)*Wp+j, c*4+kh*2+kw] = x[b, c, f, 2i+kh, 2j+kw].
+ * x [B, C, T, H, W] float32 -> p [B, S, 4C] float32.  Bit-exact copy. */
+int wan_patchify(const float* x, wan_latent_shape shape, float* p, wan_stream_t stream);
+
+/* a11 (layout part) -- inverse of wan_patchify: p [B, S, 4C] -> x [B, C, T, H, W] float32. */
+int wan_unpatchify(const float* p, wan_latent_shape shape, float* x, wan_stream_t stream);
+
+/* a3 -- patch embedding ([I2V] §5.1, the Conv3d with kernel = stride = (1,2,2) as a matrix
+ * product): x [B*S, dim] float32 = p [B*S, 4*C_in] float32 @ w_pe^T + b_pe; w_pe [dim, 4*C_in]
+ * dtype (the Conv3d weight [dim, C_in, 1, 2, 2] flattened), b_pe [dim] float32 or NULL.
+ * 4*C_in % 8 == 0.  Workspace: wan_patch_embed_workspace_bytes(). */
+size_t wan_patch_embed_workspace_bytes(const wan_block_cfg* cfg, int64_t tokens, int32_t in_channels);
+int wan_patch_embed(const wan_block_cfg* cfg, const float* p, int64_t tokens, int32_t in_channels,
+                    const void* w_pe, const float* b_pe, float* x, void* ws, size_t ws_bytes, wan_stream_t stream);
+
+/* a4 -- timestep embedding ([I2V] §5.2; [DEEP] §2.5): for each row b, with tau = 1000 * t[b],
+ * emb = [cos(tau f_i) | sin(tau f_i)], f_i = 10000^(-i/(freq_dim/2));
+ * e[b] = wt2 SiLU(wt1 emb + bt1) + bt2  -> e [B, dim] float32;
+ * e0[b] = wtp SiLU(e[b]) + btp          -> e0 [B, 6, dim] float32 (e0 doubles as scratch).
+ * t_host: B host floats; 1 <= B <= 4; freq_dim even, freq_dim % 8 == 0. */
+int wan_time_embed(const wan_block_cfg* cfg, int32_t freq_dim, const wan_time_weights* w, const float* t_host,
+                   int32_t B, float* e, float* e0, wan_stream_t stream);
+
+/* Context embedding, once per generation ([I2V] §7 steps 1-2: umT5 [512, 4096] -> MLP -> [512, dim];
+ * CLIP [257, 1280] -> MLPProj -> [257, dim]): out = GELU(ctx w1^T + b1) w2^T + b2.
+ * ctx [rows, in_dim] dtype; w1 [dim, in_dim], w2 [dim, dim] dtype; out [rows, dim] dtype.
+ * in_dim % 8 == 0.  Workspace: wan_context_embed_workspace_bytes(). */
+size_t wan_context_embed_workspace_bytes(const wan_block_cfg* cfg, int64_t rows);
+int wan_context_embed(const wan_block_cfg* cfg, const void* ctx, int64_t rows, int32_t in_dim, const void* w1,
+                      const float* b1, const void* w2, const float* b2, void* out, void* ws, size_t ws_bytes,
+                      wan_stream_t stream);
+
+/* Cross-attention keys/values of one block ([I2V] §5.4: k = Linear_k(context), v = Linear_v(context);
+ * separate image projections for the CLIP tokens).  txt_emb [B, text_len, dim] dtype; img_emb
+ * [B, img_len, dim] dtype (ignored when img_len == 0).  Writes the buffers named in `out` (layouts as
+ * in wan_cross_kv; the caller allocates them: wan_cross_kv_buffer_bytes gives each size).
+ * Workspace: wan_cross_kv_workspace_bytes(). */
+size_t wan_cross_kv_buffer_bytes(const wan_block_cfg* cfg, int32_t B, int32_t which /*0 k_txt,1 vt_txt,2 k_img,3 vt_img*/);
+size_t wan_cross_kv_workspace_bytes(const wan_block_cfg* cfg, int32_t B);
+int wan_cross_kv_fwd(const wan_block_cfg* cfg, const wan_cross_kv_weights* w, const void* txt_emb,
+                     const void* img_emb, int32_t B, const wan_cross_kv* out, void* ws, size_t ws_bytes,
+                     wan_stream_t stream);
+
+/* a5-a10 -- one DiT block, in place on x [B, S, dim] float32 (S = grid.T * grid.Hp * grid.Wp),
+ * in the order of [I2V] §5.3-§5.5:
+ *   mod = e0[b] + mod_bias -> (shift1, scale1, gate1, shift2, scale2, gate2)   ([I2V] §5.2)
+ *   u = LN(x)(1 + scale1) + shift1;  q, k = RoPE3D(RMSNorm(u W_{q,k}^T + b) * g);  v = u W_v^T + b
+ *   x += gate1 * (Attn(q, k, v) W_o^T + b_o)                    (full, non-causal, [DEEP] §2.5)
+ *   x += CrossAttn(LN_affine(x)) W_co^T + b_co                   (text, or image + text, [I2V] §5.4)
+ *   x += gate2 * FFN(LN(x)(1 + scale2) + shift2),  FFN = Linear -> GELU -> Linear
+ * e0 [B, 6, dim] float32 from wan_time_embed; kv from wan_cross_kv_fwd.  LN has no affine (except the
+ * cross-attention pre-norm), eps = cfg->ln_eps; attention scale 1/sqrt(head_dim).
+ * Workspace: wan_dit_block_workspace_bytes() (about B*S*(6*dim + ffn_dim) dtype elements). */
+size_t wan_dit_block_workspace_bytes(const wan_block_cfg* cfg, wan_grid grid, int32_t B);
+int wan_dit_block_fwd(const wan_block_cfg* cfg, const wan_block_weights* w, wan_grid grid, int32_t B, float* x,
+                      const float* e0, const wan_cross_kv* kv, void* ws, size_t ws_bytes, wan_stream_t stream);
+
+/* a11 -- head ([I2V] §5.5): (shift, scale) = head_mod + e[b];
+ * out [B*S, 4*C_out] float32 = (LN(x)(1 + scale) + shift) wh^T + bh, x [B, S, dim] float32,
+ * e [B, dim] float32.  Follow with wan_unpatchify.  Workspace: wan_head_workspace_bytes(). */
+size_t wan_head_workspace_bytes(const wan_block_cfg* cfg, int64_t tokens);
+int wan_head_fwd(const wan_block_cfg* cfg, const wan_head_weights* w, int32_t out_channels, int32_t B, int32_t S,
+                 const float* x, const float* e, float* out, void* ws, size_t ws_bytes, wan_stream_t stream);
+
+/* a12 -- classifier-free guidance + flow-matching Euler step ([I2V] §7; [DEEP] §2.7), in place:
+ * v = v_uncond + guidance * (v_cond - v_uncond)   (v = v_cond when v_uncond is NULL);
+ * x <- x + dt * v, dt signed (t runs 1 -> 0, so dt < 0).  x, v_cond, v_uncond: n float32 each.
+ * Computed as fma(dt, fma(guidance, v_c - v_u, v_u), x). */
+int wan_fm_euler_step(float* x, const float* v_cond, const float* v_uncond, float guidance, float dt, int64_t n,
+                      wan_stream_t stream);
+
+/* a7 on its own -- full non-causal self-attention with 3D RoPE on q and k ([I2V] §5.3 ②) and no
+ * projections or norms: q, k, v [B, S, heads, head_dim] dtype -> o [B, S, heads, head_dim] dtype,
+ * S = grid.T * grid.Hp * grid.Wp.  Workspace: wan_attention_workspace_bytes(). */
+size_t wan_attention_workspace_bytes(int32_t dtype, wan_grid grid, int32_t B, int32_t heads, int32_t head_dim);
+int wan_attention_fwd(int32_t dtype, const void* q, const void* k, const void* v, wan_grid grid, int32_t B,
+                      int32_t heads, int32_t head_dim, float rope_theta, void* o, void* ws, size_t ws_bytes,
+                      wan_stream_t stream);
+
+/* Human-readable name of a wan_status; message of the last failed call on this thread. */
+const char* wan_status_string(int status);
+const char* wan_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WAN_H */

@@ -1,0 +1,136 @@
+"""Single HIP entry points against the oracle: attention (with 3D RoPE), patch embedding,
+timestep embedding, context MLP, cross-attention K/V and head."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import wan_inputs as wi
+from tests.gpu_util import case, dev, host, rel_l2, require_gpu
+from video_diffusion_transformer_step_amd import _lib as L
+from video_diffusion_transformer_step_amd import runtime as R
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 1e-2}
+
+
+def _tdt(dtype):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("hd", [64, 128])
+@pytest.mark.parametrize("grid,B,H", [((3, 6, 10), 1, 2), ((2, 4, 4), 2, 3), ((1, 1, 1), 1, 1),
+                                      ((5, 7, 9), 1, 2)],
+                         ids=["180tok", "32tok-B2", "1tok", "315tok"])
+def test_attention_rope_small(dtype, hd, grid, B, H):
+    """Full attention with RoPE at sizes spanning several 64-key tiles and 128-query tiles with
+    ragged tails, every output element compared."""
+    require_gpu()
+    case(f"attention dtype={dtype} hd={hd} grid={grid} B={B} H={H}")
+    S = grid[0] * grid[1] * grid[2]
+    rng = np.random.default_rng(hd + S)
+    q, k, v = (rng.standard_normal((B, S, H, hd)).astype(np.float32) for _ in range(3))
+    if dtype == "bf16":
+        q, k, v = wi.bf16_round(q), wi.bf16_round(k), wi.bf16_round(v)
+    td = _tdt(dtype)
+    qd, kd, vd = dev(q, td), dev(k, td), dev(v, td)
+    o = torch.empty_like(qd)
+    ws = torch.empty(L.attention_ws_bytes(L.dtype_code(td), grid, B, H, hd), dtype=torch.uint8, device="cuda")
+    L.attention_fwd(qd, kd, vd, grid, o, ws)
+    got = host(o)
+    for b in range(B):
+        ref = oracle.self_attention_rope_only(q[b], k[b], v[b], grid)
+        assert rel_l2(got[b], ref) <= TOL[dtype] * (0.1 if dtype == "f32" else 1.0), rel_l2(got[b], ref)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_patch_embed(dtype):
+    require_gpu()
+    c = wi.get_config("C0").replace(dtype=dtype)
+    case(f"patch_embed {dtype}")
+    mw = wi.make_model_weights(c, seed=1)
+    x_t, z = wi.make_latents(c, seed=1)
+    x_in = oracle.build_i2v_input(x_t, z)
+    p = oracle.patchify(x_in).astype(np.float32)
+    cfg = R.cfg_of(c)
+    out = torch.empty((1, c.S, c.dim), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(L.patch_embed_ws_bytes(cfg, c.S, c.in_channels), 16), dtype=torch.uint8, device="cuda")
+    L.patch_embed(cfg, dev(p), c.in_channels, dev(mw["w_pe"], _tdt(dtype)), dev(mw["b_pe"]), out, ws)
+    ref = oracle.patch_embed(p, mw["w_pe"], mw["b_pe"])
+    # bf16 mode rounds the patch vectors to bf16 before the product
+    assert rel_l2(host(out), ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("cfg_name,dtype", [("C0", "f32"), ("C0", "bf16"), ("C1", "bf16"), ("C4", "bf16")])
+def test_time_embed(cfg_name, dtype):
+    require_gpu()
+    c = wi.get_config(cfg_name).replace(dtype=dtype)
+    case(f"time_embed {cfg_name} {dtype}")
+    mw = wi.make_model_weights(c, seed=2)
+    model = R.DeviceModel(mw, dtype)
+    cfg = R.cfg_of(c)
+    ts = [0.5, 0.125] if c.B > 1 else [0.5]
+    B = len(ts)
+    e = torch.empty((B, c.dim), dtype=torch.float32, device="cuda")
+    e0 = torch.empty((B, 6, c.dim), dtype=torch.float32, device="cuda")
+    L.time_embed(cfg, c.freq_dim, model.tw, ts, e, e0)
+    ge, ge0 = host(e), host(e0)
+    for b, t in enumerate(ts):
+        re, re0 = oracle.time_embed(t, mw, c.freq_dim)
+        assert rel_l2(ge[b], re) <= TOL[dtype] * 0.1, rel_l2(ge[b], re)
+        assert rel_l2(ge0[b], re0) <= TOL[dtype] * 0.1, rel_l2(ge0[b], re0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_context_embed_and_cross_kv(dtype):
+    require_gpu()
+    c = wi.get_config("C0").replace(dtype=dtype, img_len=9, img_dim=32)
+    case(f"context_embed + cross_kv {dtype}")
+    mw = wi.make_model_weights(c, seed=3)
+    bw = wi.make_block_weights(c, 0, seed=3)
+    txt, img = wi.make_contexts(c, seed=3)
+    model = R.DeviceModel(mw, dtype)
+    t_emb, i_emb = R.embed_contexts(c, model, txt, img, c.B)
+    ref_t = oracle.context_embed(txt[0], mw["wtx1"], mw["btx1"], mw["wtx2"], mw["btx2"])
+    ref_i = oracle.context_embed(img, mw["wim1"], mw["bim1"], mw["wim2"], mw["bim2"])
+    assert rel_l2(host(t_emb)[0], ref_t) <= TOL[dtype]
+    assert rel_l2(host(i_emb)[0], ref_i) <= TOL[dtype]
+    blk = R.DeviceBlock(bw, dtype)
+    (kc,) = R.cross_kv_all(c, [blk], t_emb, i_emb, c.B)
+    # K [B, L, dim]; V^T [B, H, hd, Lpad] zero-padded
+    te, ie = host(t_emb)[0], host(i_emb)[0]
+    k_ref, v_ref = oracle.cross_kv(te, bw["wck"], bw["bck"], bw["wcv"], bw["bcv"])
+    es = 2 if dtype == "bf16" else 4
+    td = _tdt(dtype)
+    k_got = kc.bufs[0].view(td).float().cpu().numpy().reshape(c.text_len, c.dim)
+    Lp = 64
+    vt_got = kc.bufs[1].view(td).float().cpu().numpy().reshape(c.heads, c.head_dim, Lp)
+    assert rel_l2(k_got, k_ref) <= TOL[dtype]
+    v_from_t = vt_got[:, :, :c.text_len].transpose(2, 0, 1).reshape(c.text_len, c.dim)
+    assert rel_l2(v_from_t, v_ref) <= TOL[dtype]
+    assert np.all(vt_got[:, :, c.text_len:] == 0.0)
+    ki_ref, vi_ref = oracle.cross_kv(ie, bw["wki"], bw["bki"], bw["wvi"], bw["bvi"])
+    ki_got = kc.bufs[2].view(td).float().cpu().numpy().reshape(c.img_len, c.dim)
+    assert rel_l2(ki_got, ki_ref) <= TOL[dtype]
+    del es
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_head(dtype):
+    require_gpu()
+    c = wi.get_config("C0").replace(dtype=dtype)
+    case(f"head {dtype}")
+    mw = wi.make_model_weights(c, seed=4)
+    model = R.DeviceModel(mw, dtype)
+    rng = np.random.default_rng(4)
+    B = 2
+    x = rng.standard_normal((B, c.S, c.dim)).astype(np.float32)
+    e = (0.1 * rng.standard_normal((B, c.dim))).astype(np.float32)
+    cfg = R.cfg_of(c)
+    out = torch.empty((B, c.S, 4 * c.out_channels), dtype=torch.float32, device="cuda")
+    ws = torch.empty(L.head_ws_bytes(cfg, B * c.S), dtype=torch.uint8, device="cuda")
+    L.head_fwd(cfg, model.hw, c.out_channels, B, c.S, dev(x), dev(e), out, ws)
+    ref = oracle.head_fwd(x, e, mw)
+    assert rel_l2(host(out), ref) <= TOL[dtype]

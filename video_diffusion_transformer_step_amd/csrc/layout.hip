@@ -1,0 +1,195 @@
+// Bandwidth-bound layout kernels: image-to-video input build, (1,2,2) patchify /
+// unpatchify, the CFG + flow-matching Euler update, dtype conversion and the
+// per-head transpose of V used by the attention kernels.
+#include "wan_internal.h"
+
+namespace wan {
+
+namespace {
+
+struct MaskBits {
+  uint64_t w[4];  // bit i = entry i of the 4T-entry frame sequence (T <= 64)
+};
+
+// x_in[b, c, t, h, w] = x_t (c < C) | mask (C <= c < C + 4) | z_img (c >= C + 4).
+// "图解 Wan2.1 I2V" §4.1-§4.2: y = [mask (4), image latent (16)], x = [x_t, y]; the
+// mask channel c of latent frame t is entry 4t + c of the frame sequence.
+__global__ __launch_bounds__(256) void i2v_input_kernel(const float* __restrict__ x_t, const float* __restrict__ z,
+                                                         MaskBits bits, int B, int C, int T, int HW,
+                                                         float* __restrict__ x_in) {
+  const int64_t per_b = (int64_t)(2 * C + 4) * T * HW;
+  const int64_t n = (int64_t)B * per_b;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t b = i / per_b;
+    const int64_t r = i - b * per_b;
+    const int c = (int)(r / ((int64_t)T * HW));
+    const int64_t thw = r - (int64_t)c * T * HW;
+    float v;
+    if (c < C) {
+      v = x_t[(b * C + c) * (int64_t)T * HW + thw];
+    } else if (c < C + 4) {
+      const int t = (int)(thw / HW);
+      const int e = 4 * t + (c - C);
+      v = ((bits.w[e >> 6] >> (e & 63)) & 1ull) ? 1.f : 0.f;
+    } else {
+      v = z[(b * C + (c - C - 4)) * (int64_t)T * HW + thw];
+    }
+    x_in[i] = v;
+  }
+}
+
+// p[b, (f*Hp + i)*Wp + j, c*4 + kh*2 + kw] = x[b, c, f, 2i + kh, 2j + kw]   ("图解 Wan2.1 I2V" §5.1)
+// One thread per (b, token, c): reads two 8-byte pairs, writes 16 bytes.
+__global__ __launch_bounds__(256) void patchify_kernel(const float* __restrict__ x, int B, int C, int T, int H,
+                                                        int W, float* __restrict__ p) {
+  const int Hp = H / 2, Wp = W / 2;
+  const int64_t S = (int64_t)T * Hp * Wp;
+  const int64_t n = (int64_t)B * S * C;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i % C);
+    const int64_t bs = i / C;
+    const int64_t s = bs % S;
+    const int64_t b = bs / S;
+    const int j = (int)(s % Wp);
+    const int ii = (int)((s / Wp) % Hp);
+    const int f = (int)(s / ((int64_t)Wp * Hp));
+    const float* src = x + (((b * C + c) * T + f) * H + 2 * ii) * (int64_t)W + 2 * j;
+    const float2 top = *reinterpret_cast<const float2*>(src);
+    const float2 bot = *reinterpret_cast<const float2*>(src + W);
+    *reinterpret_cast<float4*>(p + i * 4) = make_float4(top.x, top.y, bot.x, bot.y);
+  }
+}
+
+__global__ __launch_bounds__(256) void unpatchify_kernel(const float* __restrict__ p, int B, int C, int T, int H,
+                                                          int W, float* __restrict__ x) {
+  const int Hp = H / 2, Wp = W / 2;
+  const int64_t S = (int64_t)T * Hp * Wp;
+  const int64_t n = (int64_t)B * S * C;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i % C);
+    const int64_t bs = i / C;
+    const int64_t s = bs % S;
+    const int64_t b = bs / S;
+    const int j = (int)(s % Wp);
+    const int ii = (int)((s / Wp) % Hp);
+    const int f = (int)(s / ((int64_t)Wp * Hp));
+    const float4 v = *reinterpret_cast<const float4*>(p + i * 4);
+    float* dst = x + (((b * C + c) * T + f) * H + 2 * ii) * (int64_t)W + 2 * j;
+    *reinterpret_cast<float2*>(dst) = make_float2(v.x, v.y);
+    *reinterpret_cast<float2*>(dst + W) = make_float2(v.z, v.w);
+  }
+}
+
+// x <- x + dt * v,  v = v_u + s (v_c - v_u)  (or v = v_c without guidance).
+// "图解 Wan2.1 I2V" §7 (CFG and the Euler step, t from 1 to 0 so dt < 0).
+__device__ __forceinline__ float euler1(float x, float vc, float vu, float s, float dt, bool cfg) {
+  const float v = cfg ? fmaf(s, vc - vu, vu) : vc;
+  return fmaf(dt, v, x);
+}
+
+__global__ __launch_bounds__(256) void euler_kernel(float* __restrict__ x, const float* __restrict__ vc,
+                                                     const float* __restrict__ vu, float s, float dt, int64_t n) {
+  const bool cfg = vu != nullptr;
+  const int64_t n4 = n / 4;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+    float4 xv = reinterpret_cast<float4*>(x)[i];
+    const float4 c = reinterpret_cast<const float4*>(vc)[i];
+    const float4 u = cfg ? reinterpret_cast<const float4*>(vu)[i] : c;
+    xv.x = euler1(xv.x, c.x, u.x, s, dt, cfg);
+    xv.y = euler1(xv.y, c.y, u.y, s, dt, cfg);
+    xv.z = euler1(xv.z, c.z, u.z, s, dt, cfg);
+    xv.w = euler1(xv.w, c.w, u.w, s, dt, cfg);
+    reinterpret_cast<float4*>(x)[i] = xv;
+  }
+  // tail (n % 4 elements), handled by the first threads
+  const int64_t t = n4 * 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < n) x[t] = euler1(x[t], vc[t], cfg ? vu[t] : 0.f, s, dt, cfg);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ in, T* __restrict__ out, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = from_f32<T>(in[i]);
+}
+
+// V^T[b, h, d, j] = V[b, j, h*hd + d] (+col0) for j < S, 0 for S <= j < Spad.  One workgroup per
+// (64-token tile, head, batch row); LDS tile [64][hd + 1] elements.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_heads_kernel(const T* __restrict__ v, int64_t ld, int64_t col0,
+                                                               int S, int H, int hd, int Spad, T* __restrict__ vt) {
+  __shared__ T tile[64 * (128 + 1)];
+  const int j0 = blockIdx.x * 64, h = blockIdx.y, b = blockIdx.z;
+  const int P = hd + 1;
+  for (int e = threadIdx.x; e < 64 * hd; e += 256) {
+    const int r = e / hd, d = e % hd;
+    const int j = j0 + r;
+    tile[r * P + d] = (j < S) ? v[((int64_t)b * S + j) * ld + col0 + (int64_t)h * hd + d] : from_f32<T>(0.f);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 64 * hd; e += 256) {
+    const int d = e / 64, r = e % 64;
+    const int j = j0 + r;
+    if (j < Spad) vt[(((int64_t)b * H + h) * hd + d) * Spad + j] = tile[r * P + d];
+  }
+}
+
+inline unsigned grid_for(int64_t n, int per_thread = 1) {
+  int64_t blocks = ceil_div(ceil_div(n, per_thread), 256);
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  return (unsigned)blocks;
+}
+
+}  // namespace
+
+hipError_t launch_i2v_input(const float* x_t, const float* z_img, const uint64_t mask_bits[4], int B, int C, int T,
+                            int H, int W, float* x_in, hipStream_t s) {
+  MaskBits bits{{mask_bits[0], mask_bits[1], mask_bits[2], mask_bits[3]}};
+  const int64_t n = (int64_t)B * (2 * C + 4) * T * H * W;
+  hipLaunchKernelGGL(i2v_input_kernel, dim3(grid_for(n)), dim3(256), 0, s, x_t, z_img, bits, B, C, T, H * W, x_in);
+  return hipGetLastError();
+}
+
+hipError_t launch_patchify(const float* x, int B, int C, int T, int H, int W, float* p, hipStream_t s) {
+  const int64_t n = (int64_t)B * T * (H / 2) * (W / 2) * C;
+  hipLaunchKernelGGL(patchify_kernel, dim3(grid_for(n)), dim3(256), 0, s, x, B, C, T, H, W, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpatchify(const float* p, int B, int C, int T, int H, int W, float* x, hipStream_t s) {
+  const int64_t n = (int64_t)B * T * (H / 2) * (W / 2) * C;
+  hipLaunchKernelGGL(unpatchify_kernel, dim3(grid_for(n)), dim3(256), 0, s, p, B, C, T, H, W, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_euler(float* x, const float* v_c, const float* v_u, float guidance, float dt, int64_t n,
+                        hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(euler_kernel, dim3(grid_for(n, 4)), dim3(256), 0, s, x, v_c, v_u, guidance, dt, n);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_convert(const float* in, T* out, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(convert_kernel<T>, dim3(grid_for(n)), dim3(256), 0, s, in, out, n);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_transpose_heads(const T* v, int64_t ld, int64_t col0, int B, int S, int H, int hd, int Spad,
+                                  T* vt, hipStream_t s) {
+  if (hd > 128) return hipErrorInvalidValue;
+  dim3 grid((unsigned)ceil_div(Spad, 64), (unsigned)H, (unsigned)B);
+  hipLaunchKernelGGL(transpose_heads_kernel<T>, grid, dim3(256), 0, s, v, ld, col0, S, H, hd, Spad, vt);
+  return hipGetLastError();
+}
+
+template hipError_t launch_convert<float>(const float*, float*, int64_t, hipStream_t);
+template hipError_t launch_convert<bf16>(const float*, bf16*, int64_t, hipStream_t);
+template hipError_t launch_transpose_heads<float>(const float*, int64_t, int64_t, int, int, int, int, int, float*,
+                                                  hipStream_t);
+template hipError_t launch_transpose_heads<bf16>(const bf16*, int64_t, int64_t, int, int, int, int, int, bf16*,
+                                                 hipStream_t);
+
+}  // namespace wan

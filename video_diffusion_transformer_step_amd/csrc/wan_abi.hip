@@ -1,0 +1,506 @@
+// C ABI of libwan.so: argument validation, workspace planning and the launch
+// sequence of each entry point declared in include/wan.h.  No allocation, no
+// synchronisation: every call only enqueues kernels on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "wan.h"
+#include "wan_internal.h"
+
+using namespace wan;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+#define WAN_TRY(expr)                                                                      \
+  do {                                                                                     \
+    int rc_ = (expr);                                                                      \
+    if (rc_ != WAN_OK) return rc_;                                                         \
+  } while (0)
+
+#define HIP_TRY(expr)                                                                      \
+  do {                                                                                     \
+    hipError_t e_ = (expr);                                                                \
+    if (e_ != hipSuccess) return fail(WAN_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+inline hipStream_t hs(wan_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+int need_ptr(const void* p, const char* name) {
+  if (!p) return fail(WAN_EINVAL, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) & 15u) return fail(WAN_EINVAL, "%s is not 16-byte aligned", name);
+  return WAN_OK;
+}
+int opt_ptr(const void* p, const char* name) { return p ? need_ptr(p, name) : WAN_OK; }
+
+int check_shape(const wan_latent_shape& s) {
+  if (s.B <= 0 || s.C <= 0 || s.T <= 0 || s.H <= 0 || s.W <= 0)
+    return fail(WAN_EINVAL, "latent shape must be positive (B=%d C=%d T=%d H=%d W=%d)", s.B, s.C, s.T, s.H, s.W);
+  if ((s.H & 1) || (s.W & 1)) return fail(WAN_EINVAL, "H (%d) and W (%d) must be even for (1,2,2) patches", s.H, s.W);
+  return WAN_OK;
+}
+
+int check_grid(const wan_grid& g) {
+  if (g.T <= 0 || g.Hp <= 0 || g.Wp <= 0) return fail(WAN_EINVAL, "grid must be positive (%d,%d,%d)", g.T, g.Hp, g.Wp);
+  if ((int64_t)g.T * g.Hp * g.Wp > (1ll << 30)) return fail(WAN_EUNSUPPORTED, "too many tokens");
+  return WAN_OK;
+}
+
+int check_dtype(int32_t dtype) {
+  if (dtype != WAN_F32 && dtype != WAN_BF16) return fail(WAN_EINVAL, "unknown dtype %d", dtype);
+  return WAN_OK;
+}
+
+int check_cfg(const wan_block_cfg* c) {
+  if (!c) return fail(WAN_EINVAL, "cfg is NULL");
+  WAN_TRY(check_dtype(c->dtype));
+  if (c->flags != 0) return fail(WAN_EUNSUPPORTED, "cfg->flags must be 0 (got 0x%x)", c->flags);
+  if (c->heads <= 0 || c->head_dim <= 0 || c->dim != c->heads * c->head_dim)
+    return fail(WAN_EINVAL, "dim (%d) must equal heads (%d) * head_dim (%d)", c->dim, c->heads, c->head_dim);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(WAN_EUNSUPPORTED, "head_dim %d not supported (64 or 128)", c->head_dim);
+  if (c->dim % 8 != 0 || c->dim > 6144) return fail(WAN_EUNSUPPORTED, "dim %d must be a multiple of 8 and <= 6144", c->dim);
+  if (c->ffn_dim <= 0 || c->ffn_dim % 8 != 0) return fail(WAN_EINVAL, "ffn_dim %d must be a positive multiple of 8", c->ffn_dim);
+  if (c->text_len <= 0 || c->img_len < 0) return fail(WAN_EINVAL, "text_len must be > 0 and img_len >= 0");
+  if (!(c->ln_eps >= 0.f) || !(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f))
+    return fail(WAN_EINVAL, "eps must be >= 0 and rope_theta > 0");
+  return WAN_OK;
+}
+
+inline size_t esize(int32_t dtype) { return dtype == WAN_BF16 ? 2 : 4; }
+inline size_t a256(size_t x) { return (x + 255) & ~size_t(255); }
+inline int64_t pad64(int64_t L) { return round_up(L, 64); }
+
+// Bump allocator over the caller's workspace.
+struct Carve {
+  char* base;
+  size_t off = 0;
+  template <typename T>
+  T* take(size_t count) {
+    T* p = reinterpret_cast<T*>(base ? base + off : nullptr);
+    off += a256(count * sizeof(T));
+    return p;
+  }
+};
+
+// ---------------------------------------------------------------- block plan
+template <typename T>
+struct BlockWs {
+  T *u, *qkv, *vt, *o, *h;
+};
+template <typename T>
+size_t block_plan(const wan_block_cfg& c, const wan_grid& g, int B, char* base, BlockWs<T>* out) {
+  const int64_t S = (int64_t)g.T * g.Hp * g.Wp, BS = (int64_t)B * S, dim = c.dim;
+  Carve cv{base};
+  BlockWs<T> w;
+  w.u = cv.take<T>(BS * dim);
+  w.qkv = cv.take<T>(BS * 3 * dim);
+  w.vt = cv.take<T>((size_t)B * dim * pad64(S));
+  w.o = cv.take<T>(BS * dim);
+  w.h = cv.take<T>(BS * c.ffn_dim);
+  if (out) *out = w;
+  return cv.off;
+}
+
+template <typename T>
+int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_grid& g, int B, float* x,
+                const float* e0, const wan_cross_kv& kv, void* ws, hipStream_t st) {
+  BlockWs<T> w;
+  block_plan<T>(c, g, B, reinterpret_cast<char*>(ws), &w);
+  const int S = g.T * g.Hp * g.Wp, BS = B * S, dim = c.dim, H = c.heads, hd = c.head_dim;
+  const int Spad = (int)pad64(S);
+  const float scale = 1.f / sqrtf((float)hd);
+  // self-attention branch
+  HIP_TRY(launch_ln_mod<T>(x, BS, dim, S, 0, e0, W.mod_bias, 0, 1, c.ln_eps, w.u, st));
+  HIP_TRY((gemm_store<T, T>(w.u, dim, (const T*)W.wqkv, dim, BS, 3 * dim, dim, W.bqkv, ACT_NONE, w.qkv, 3 * dim, st)));
+  HIP_TRY(launch_qk_norm_rope<T>(w.qkv, w.qkv + dim, 3 * dim, w.qkv, w.qkv + dim, 3 * dim, B, g.T, g.Hp, g.Wp, H, hd,
+                                 W.gq, W.gk, 1, c.rms_eps, c.rope_theta, st));
+  HIP_TRY(launch_transpose_heads<T>(w.qkv, 3 * dim, 2 * dim, B, S, H, hd, Spad, w.vt, st));
+  KVStream self{w.qkv + dim, (int64_t)S * 3 * dim, 3 * dim, w.vt, S, Spad};
+  HIP_TRY(launch_attention<T>(w.qkv, (int64_t)S * 3 * dim, 3 * dim, self, self, 1, B, S, H, hd, scale, w.o,
+                              (int64_t)S * dim, dim, st));
+  HIP_TRY(gemm_residual<T>(w.o, dim, (const T*)W.wo, dim, BS, dim, dim, W.bo, e0, W.mod_bias, 2, S, x, dim, st));
+  // cross-attention branch (no adaLN, no RoPE)
+  HIP_TRY(launch_ln_mod<T>(x, BS, dim, S, 1, W.ln3_w, W.ln3_b, 0, 0, c.ln_eps, w.u, st));
+  T* qc = w.qkv;  // reuse: [BS, dim]
+  HIP_TRY((gemm_store<T, T>(w.u, dim, (const T*)W.wcq, dim, BS, dim, dim, W.bcq, ACT_NONE, qc, dim, st)));
+  const int Lt = c.text_len, Li = c.img_len;
+  KVStream st_txt{kv.k_txt, (int64_t)Lt * dim, dim, kv.vt_txt, Lt, (int)pad64(Lt)};
+  KVStream st_img{kv.k_img, (int64_t)Li * dim, dim, kv.vt_img, Li, (int)pad64(Li > 0 ? Li : 1)};
+  HIP_TRY(launch_attention<T>(qc, (int64_t)S * dim, dim, st_txt, st_img, Li > 0 ? 2 : 1, B, S, H, hd, scale, w.o,
+                              (int64_t)S * dim, dim, st));
+  HIP_TRY(gemm_residual<T>(w.o, dim, (const T*)W.wco, dim, BS, dim, dim, W.bco, nullptr, nullptr, 0, S, x, dim, st));
+  // FFN branch
+  HIP_TRY(launch_ln_mod<T>(x, BS, dim, S, 0, e0, W.mod_bias, 3, 4, c.ln_eps, w.u, st));
+  HIP_TRY((gemm_store<T, T>(w.u, dim, (const T*)W.w1, dim, BS, c.ffn_dim, dim, W.b1, ACT_GELU, w.h, c.ffn_dim, st)));
+  HIP_TRY(gemm_residual<T>(w.h, c.ffn_dim, (const T*)W.w2, c.ffn_dim, BS, dim, c.ffn_dim, W.b2, e0, W.mod_bias, 5, S,
+                           x, dim, st));
+  return WAN_OK;
+}
+
+int check_block_weights(const wan_block_cfg& c, const wan_block_weights* w) {
+  if (!w) return fail(WAN_EINVAL, "weights is NULL");
+  WAN_TRY(need_ptr(w->mod_bias, "mod_bias"));
+  WAN_TRY(need_ptr(w->wqkv, "wqkv"));
+  WAN_TRY(opt_ptr(w->bqkv, "bqkv"));
+  WAN_TRY(need_ptr(w->gq, "gq"));
+  WAN_TRY(need_ptr(w->gk, "gk"));
+  WAN_TRY(need_ptr(w->wo, "wo"));
+  WAN_TRY(opt_ptr(w->bo, "bo"));
+  WAN_TRY(need_ptr(w->ln3_w, "ln3_w"));
+  WAN_TRY(need_ptr(w->ln3_b, "ln3_b"));
+  WAN_TRY(need_ptr(w->wcq, "wcq"));
+  WAN_TRY(opt_ptr(w->bcq, "bcq"));
+  WAN_TRY(need_ptr(w->wco, "wco"));
+  WAN_TRY(opt_ptr(w->bco, "bco"));
+  WAN_TRY(need_ptr(w->w1, "w1"));
+  WAN_TRY(opt_ptr(w->b1, "b1"));
+  WAN_TRY(need_ptr(w->w2, "w2"));
+  WAN_TRY(opt_ptr(w->b2, "b2"));
+  (void)c;
+  return WAN_OK;
+}
+
+int check_kv(const wan_block_cfg& c, const wan_cross_kv* kv, bool is_output) {
+  if (!kv) return fail(WAN_EINVAL, "cross kv is NULL");
+  WAN_TRY(need_ptr(kv->k_txt, "k_txt"));
+  WAN_TRY(need_ptr(kv->vt_txt, "vt_txt"));
+  if (c.img_len > 0) {
+    WAN_TRY(need_ptr(kv->k_img, "k_img"));
+    WAN_TRY(need_ptr(kv->vt_img, "vt_img"));
+  }
+  (void)is_output;
+  return WAN_OK;
+}
+
+}  // namespace
+
+// Definitions below take their C linkage from the declarations in wan.h.
+
+const char* wan_status_string(int status) {
+  switch (status) {
+    case WAN_OK: return "WAN_OK";
+    case WAN_EINVAL: return "WAN_EINVAL";
+    case WAN_EUNSUPPORTED: return "WAN_EUNSUPPORTED";
+    case WAN_EWORKSPACE: return "WAN_EWORKSPACE";
+    case WAN_EHIP: return "WAN_EHIP";
+    default: return "WAN_E?";
+  }
+}
+
+const char* wan_last_error(void) { return g_err; }
+
+int wan_build_i2v_input(const float* x_t, const float* z_img, const uint8_t* known_pixel_frames_host,
+                        wan_latent_shape s, float* x_in, wan_stream_t stream) {
+  WAN_TRY(check_shape(s));
+  if (s.T > 64) return fail(WAN_EUNSUPPORTED, "T = %d > 64 latent frames", s.T);
+  WAN_TRY(need_ptr(x_t, "x_t"));
+  WAN_TRY(need_ptr(z_img, "z_img"));
+  WAN_TRY(need_ptr(x_in, "x_in"));
+  const int F = 4 * (s.T - 1) + 1;
+  uint64_t bits[4] = {0, 0, 0, 0};
+  for (int e = 0; e < 4 * s.T; ++e) {
+    const int frame = e < 4 ? 0 : e - 3;  // entries 0..3 repeat frame 0; entry e >= 4 is frame e - 3
+    const bool known = known_pixel_frames_host ? known_pixel_frames_host[frame] != 0 : frame == 0;
+    if (known) bits[e >> 6] |= 1ull << (e & 63);
+  }
+  (void)F;
+  HIP_TRY(launch_i2v_input(x_t, z_img, bits, s.B, s.C, s.T, s.H, s.W, x_in, hs(stream)));
+  return WAN_OK;
+}
+
+int wan_patchify(const float* x, wan_latent_shape s, float* p, wan_stream_t stream) {
+  WAN_TRY(check_shape(s));
+  WAN_TRY(need_ptr(x, "x"));
+  WAN_TRY(need_ptr(p, "p"));
+  HIP_TRY(launch_patchify(x, s.B, s.C, s.T, s.H, s.W, p, hs(stream)));
+  return WAN_OK;
+}
+
+int wan_unpatchify(const float* p, wan_latent_shape s, float* x, wan_stream_t stream) {
+  WAN_TRY(check_shape(s));
+  WAN_TRY(need_ptr(p, "p"));
+  WAN_TRY(need_ptr(x, "x"));
+  HIP_TRY(launch_unpatchify(p, s.B, s.C, s.T, s.H, s.W, x, hs(stream)));
+  return WAN_OK;
+}
+
+size_t wan_patch_embed_workspace_bytes(const wan_block_cfg* cfg, int64_t tokens, int32_t in_channels) {
+  if (!cfg || tokens <= 0 || in_channels <= 0) return 0;
+  return cfg->dtype == WAN_BF16 ? a256((size_t)tokens * 4 * in_channels * 2) : 0;
+}
+
+int wan_patch_embed(const wan_block_cfg* cfg, const float* p, int64_t tokens, int32_t in_channels, const void* w_pe,
+                    const float* b_pe, float* x, void* ws, size_t ws_bytes, wan_stream_t stream) {
+  WAN_TRY(check_cfg(cfg));
+  if (tokens <= 0 || tokens > (1ll << 30) || in_channels <= 0) return fail(WAN_EINVAL, "tokens / in_channels must be positive");
+  const int K = 4 * in_channels;
+  if (K % 8 != 0) return fail(WAN_EUNSUPPORTED, "4*in_channels = %d must be a multiple of 8", K);
+  WAN_TRY(need_ptr(p, "p"));
+  WAN_TRY(need_ptr(w_pe, "w_pe"));
+  WAN_TRY(opt_ptr(b_pe, "b_pe"));
+  WAN_TRY(need_ptr(x, "x"));
+  const size_t need = wan_patch_embed_workspace_bytes(cfg, tokens, in_channels);
+  if (ws_bytes < need) return fail(WAN_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (need) WAN_TRY(need_ptr(ws, "ws"));
+  const int M = (int)tokens;
+  if (cfg->dtype == WAN_BF16) {
+    bf16* pb = reinterpret_cast<bf16*>(ws);
+    HIP_TRY(launch_convert<bf16>(p, pb, (int64_t)M * K, hs(stream)));
+    HIP_TRY((gemm_store<bf16, float>(pb, K, (const bf16*)w_pe, K, M, cfg->dim, K, b_pe, ACT_NONE, x, cfg->dim, hs(stream))));
+  } else {
+    HIP_TRY((gemm_store<float, float>(p, K, (const float*)w_pe, K, M, cfg->dim, K, b_pe, ACT_NONE, x, cfg->dim, hs(stream))));
+  }
+  return WAN_OK;
+}
+
+int wan_time_embed(const wan_block_cfg* cfg, int32_t freq_dim, const wan_time_weights* w, const float* t_host,
+                   int32_t B, float* e, float* e0, wan_stream_t stream) {
+  WAN_TRY(check_cfg(cfg));
+  if (B < 1 || B > 4) return fail(WAN_EUNSUPPORTED, "time embedding batch %d not in [1, 4]", B);
+  if (freq_dim <= 0 || freq_dim % 8 != 0 || freq_dim > 2 * cfg->dim)
+    return fail(WAN_EINVAL, "freq_dim %d must be a positive multiple of 8 and <= 2*dim", freq_dim);
+  if (!w || !t_host) return fail(WAN_EINVAL, "weights / t_host is NULL");
+  WAN_TRY(need_ptr(w->wt1, "wt1"));
+  WAN_TRY(need_ptr(w->wt2, "wt2"));
+  WAN_TRY(need_ptr(w->wtp, "wtp"));
+  WAN_TRY(opt_ptr(w->bt1, "bt1"));
+  WAN_TRY(opt_ptr(w->bt2, "bt2"));
+  WAN_TRY(opt_ptr(w->btp, "btp"));
+  WAN_TRY(need_ptr(e, "e"));
+  WAN_TRY(need_ptr(e0, "e0"));
+  const int dim = cfg->dim;
+  float* h = e0;                          // scratch [B, dim]
+  float* emb = e0 + (int64_t)4 * B * dim;  // scratch [B, freq_dim]
+  hipStream_t st = hs(stream);
+  HIP_TRY(launch_sinusoid(t_host, B, freq_dim, emb, st));
+  if (cfg->dtype == WAN_BF16) {
+    HIP_TRY(gemv<bf16>((const bf16*)w->wt1, dim, freq_dim, emb, B, w->bt1, ACT_NONE, ACT_SILU, h, st));
+    HIP_TRY(gemv<bf16>((const bf16*)w->wt2, dim, dim, h, B, w->bt2, ACT_NONE, ACT_NONE, e, st));
+    HIP_TRY(gemv<bf16>((const bf16*)w->wtp, 6 * dim, dim, e, B, w->btp, ACT_SILU, ACT_NONE, e0, st));
+  } else {
+    HIP_TRY(gemv<float>((const float*)w->wt1, dim, freq_dim, emb, B, w->bt1, ACT_NONE, ACT_SILU, h, st));
+    HIP_TRY(gemv<float>((const float*)w->wt2, dim, dim, h, B, w->bt2, ACT_NONE, ACT_NONE, e, st));
+    HIP_TRY(gemv<float>((const float*)w->wtp, 6 * dim, dim, e, B, w->btp, ACT_SILU, ACT_NONE, e0, st));
+  }
+  return WAN_OK;
+}
+
+size_t wan_context_embed_workspace_bytes(const wan_block_cfg* cfg, int64_t rows) {
+  if (!cfg || rows <= 0) return 0;
+  return a256((size_t)rows * cfg->dim * esize(cfg->dtype));
+}
+
+template <typename T>
+static int context_embed_t(const wan_block_cfg& c, const void* ctx, int rows, int in_dim, const void* w1,
+                           const float* b1, const void* w2, const float* b2, void* out, void* ws, hipStream_t st) {
+  T* hid = reinterpret_cast<T*>(ws);
+  HIP_TRY((gemm_store<T, T>((const T*)ctx, in_dim, (const T*)w1, in_dim, rows, c.dim, in_dim, b1, ACT_GELU, hid, c.dim, st)));
+  HIP_TRY((gemm_store<T, T>(hid, c.dim, (const T*)w2, c.dim, rows, c.dim, c.dim, b2, ACT_NONE, (T*)out, c.dim, st)));
+  return WAN_OK;
+}
+
+int wan_context_embed(const wan_block_cfg* cfg, const void* ctx, int64_t rows, int32_t in_dim, const void* w1,
+                      const float* b1, const void* w2, const float* b2, void* out, void* ws, size_t ws_bytes,
+                      wan_stream_t stream) {
+  WAN_TRY(check_cfg(cfg));
+  if (rows <= 0 || rows > (1 << 24) || in_dim <= 0 || in_dim % 8 != 0)
+    return fail(WAN_EINVAL, "rows must be positive and in_dim a positive multiple of 8");
+  WAN_TRY(need_ptr(ctx, "ctx"));
+  WAN_TRY(need_ptr(w1, "w1"));
+  WAN_TRY(need_ptr(w2, "w2"));
+  WAN_TRY(opt_ptr(b1, "b1"));
+  WAN_TRY(opt_ptr(b2, "b2"));
+  WAN_TRY(need_ptr(out, "out"));
+  const size_t need = wan_context_embed_workspace_bytes(cfg, rows);
+  if (ws_bytes < need) return fail(WAN_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  WAN_TRY(need_ptr(ws, "ws"));
+  if (cfg->dtype == WAN_BF16)
+    return context_embed_t<bf16>(*cfg, ctx, (int)rows, in_dim, w1, b1, w2, b2, out, ws, hs(stream));
+  return context_embed_t<float>(*cfg, ctx, (int)rows, in_dim, w1, b1, w2, b2, out, ws, hs(stream));
+}
+
+size_t wan_cross_kv_buffer_bytes(const wan_block_cfg* cfg, int32_t B, int32_t which) {
+  if (!cfg || B <= 0) return 0;
+  const size_t es = esize(cfg->dtype);
+  const int64_t L = (which < 2) ? cfg->text_len : cfg->img_len;
+  if (L <= 0) return 0;
+  if (which == 0 || which == 2) return (size_t)B * L * cfg->dim * es;
+  if (which == 1 || which == 3) return (size_t)B * cfg->dim * pad64(L) * es;
+  return 0;
+}
+
+size_t wan_cross_kv_workspace_bytes(const wan_block_cfg* cfg, int32_t B) {
+  if (!cfg || B <= 0) return 0;
+  const int64_t L = cfg->text_len > cfg->img_len ? cfg->text_len : cfg->img_len;
+  return a256((size_t)B * L * cfg->dim * esize(cfg->dtype));
+}
+
+template <typename T>
+static int cross_kv_t(const wan_block_cfg& c, const wan_cross_kv_weights& w, const void* txt, const void* img, int B,
+                      const wan_cross_kv& out, void* ws, hipStream_t st) {
+  const int dim = c.dim;
+  T* tmp = reinterpret_cast<T*>(ws);
+  for (int which = 0; which < 2; ++which) {
+    const int L = which == 0 ? c.text_len : c.img_len;
+    if (L <= 0) continue;
+    const T* ctx = (const T*)(which == 0 ? txt : img);
+    const T* wkv = (const T*)(which == 0 ? w.wkv_txt : w.wkv_img);
+    const float* bkv = which == 0 ? w.bkv_txt : w.bkv_img;
+    T* k = (T*)(which == 0 ? out.k_txt : out.k_img);
+    T* vt = (T*)(which == 0 ? out.vt_txt : out.vt_img);
+    const int M = B * L;
+    HIP_TRY((gemm_store<T, T>(ctx, dim, wkv, dim, M, dim, dim, bkv, ACT_NONE, k, dim, st)));
+    HIP_TRY((gemm_store<T, T>(ctx, dim, wkv + (int64_t)dim * dim, dim, M, dim, dim, bkv ? bkv + dim : nullptr,
+                              ACT_NONE, tmp, dim, st)));
+    HIP_TRY(launch_transpose_heads<T>(tmp, dim, 0, B, L, c.heads, c.head_dim, (int)pad64(L), vt, st));
+  }
+  return WAN_OK;
+}
+
+int wan_cross_kv_fwd(const wan_block_cfg* cfg, const wan_cross_kv_weights* w, const void* txt_emb, const void* img_emb,
+                     int32_t B, const wan_cross_kv* out, void* ws, size_t ws_bytes, wan_stream_t stream) {
+  WAN_TRY(check_cfg(cfg));
+  if (B <= 0) return fail(WAN_EINVAL, "B must be positive");
+  if (!w) return fail(WAN_EINVAL, "weights is NULL");
+  WAN_TRY(need_ptr(w->wkv_txt, "wkv_txt"));
+  WAN_TRY(opt_ptr(w->bkv_txt, "bkv_txt"));
+  WAN_TRY(need_ptr(txt_emb, "txt_emb"));
+  if (cfg->img_len > 0) {
+    WAN_TRY(need_ptr(w->wkv_img, "wkv_img"));
+    WAN_TRY(opt_ptr(w->bkv_img, "bkv_img"));
+    WAN_TRY(need_ptr(img_emb, "img_emb"));
+  }
+  WAN_TRY(check_kv(*cfg, out, true));
+  const size_t need = wan_cross_kv_workspace_bytes(cfg, B);
+  if (ws_bytes < need) return fail(WAN_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  WAN_TRY(need_ptr(ws, "ws"));
+  if (cfg->dtype == WAN_BF16) return cross_kv_t<bf16>(*cfg, *w, txt_emb, img_emb, B, *out, ws, hs(stream));
+  return cross_kv_t<float>(*cfg, *w, txt_emb, img_emb, B, *out, ws, hs(stream));
+}
+
+size_t wan_dit_block_workspace_bytes(const wan_block_cfg* cfg, wan_grid grid, int32_t B) {
+  if (!cfg || B <= 0 || grid.T <= 0 || grid.Hp <= 0 || grid.Wp <= 0) return 0;
+  if (cfg->dtype == WAN_BF16) return block_plan<bf16>(*cfg, grid, B, nullptr, nullptr);
+  return block_plan<float>(*cfg, grid, B, nullptr, nullptr);
+}
+
+int wan_dit_block_fwd(const wan_block_cfg* cfg, const wan_block_weights* w, wan_grid grid, int32_t B, float* x,
+                      const float* e0, const wan_cross_kv* kv, void* ws, size_t ws_bytes, wan_stream_t stream) {
+  WAN_TRY(check_cfg(cfg));
+  WAN_TRY(check_grid(grid));
+  if (B <= 0) return fail(WAN_EINVAL, "B must be positive");
+  if ((int64_t)B * grid.T * grid.Hp * grid.Wp > (1ll << 30)) return fail(WAN_EUNSUPPORTED, "too many rows");
+  WAN_TRY(check_block_weights(*cfg, w));
+  WAN_TRY(need_ptr(x, "x"));
+  WAN_TRY(need_ptr(e0, "e0"));
+  WAN_TRY(check_kv(*cfg, kv, false));
+  const size_t need = wan_dit_block_workspace_bytes(cfg, grid, B);
+  if (ws_bytes < need) return fail(WAN_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  WAN_TRY(need_ptr(ws, "ws"));
+  if (cfg->dtype == WAN_BF16) return block_fwd_t<bf16>(*cfg, *w, grid, B, x, e0, *kv, ws, hs(stream));
+  return block_fwd_t<float>(*cfg, *w, grid, B, x, e0, *kv, ws, hs(stream));
+}
+
+size_t wan_head_workspace_bytes(const wan_block_cfg* cfg, int64_t tokens) {
+  if (!cfg || tokens <= 0) return 0;
+  return a256((size_t)tokens * cfg->dim * esize(cfg->dtype));
+}
+
+int wan_head_fwd(const wan_block_cfg* cfg, const wan_head_weights* w, int32_t out_channels, int32_t B, int32_t S,
+                 const float* x, const float* e, float* out, void* ws, size_t ws_bytes, wan_stream_t stream) {
+  WAN_TRY(check_cfg(cfg));
+  if (B <= 0 || S <= 0 || out_channels <= 0) return fail(WAN_EINVAL, "B, S, out_channels must be positive");
+  if ((4 * out_channels) % 8 != 0) return fail(WAN_EUNSUPPORTED, "4*out_channels must be a multiple of 8");
+  if (!w) return fail(WAN_EINVAL, "weights is NULL");
+  WAN_TRY(need_ptr(w->head_mod, "head_mod"));
+  WAN_TRY(need_ptr(w->wh, "wh"));
+  WAN_TRY(opt_ptr(w->bh, "bh"));
+  WAN_TRY(need_ptr(x, "x"));
+  WAN_TRY(need_ptr(e, "e"));
+  WAN_TRY(need_ptr(out, "out"));
+  const int64_t rows = (int64_t)B * S;
+  const size_t need = wan_head_workspace_bytes(cfg, rows);
+  if (ws_bytes < need) return fail(WAN_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  WAN_TRY(need_ptr(ws, "ws"));
+  const int N = 4 * out_channels, dim = cfg->dim;
+  hipStream_t st = hs(stream);
+  if (cfg->dtype == WAN_BF16) {
+    bf16* u = reinterpret_cast<bf16*>(ws);
+    HIP_TRY(launch_ln_mod<bf16>(x, rows, dim, S, 2, w->head_mod, e, 0, 1, cfg->ln_eps, u, st));
+    HIP_TRY((gemm_store<bf16, float>(u, dim, (const bf16*)w->wh, dim, (int)rows, N, dim, w->bh, ACT_NONE, out, N, st)));
+  } else {
+    float* u = reinterpret_cast<float*>(ws);
+    HIP_TRY(launch_ln_mod<float>(x, rows, dim, S, 2, w->head_mod, e, 0, 1, cfg->ln_eps, u, st));
+    HIP_TRY((gemm_store<float, float>(u, dim, (const float*)w->wh, dim, (int)rows, N, dim, w->bh, ACT_NONE, out, N, st)));
+  }
+  return WAN_OK;
+}
+
+int wan_fm_euler_step(float* x, const float* v_cond, const float* v_uncond, float guidance, float dt, int64_t n,
+                      wan_stream_t stream) {
+  if (n < 0) return fail(WAN_EINVAL, "n must be >= 0");
+  WAN_TRY(need_ptr(x, "x"));
+  WAN_TRY(need_ptr(v_cond, "v_cond"));
+  WAN_TRY(opt_ptr(v_uncond, "v_uncond"));
+  HIP_TRY(launch_euler(x, v_cond, v_uncond, guidance, dt, n, hs(stream)));
+  return WAN_OK;
+}
+
+size_t wan_attention_workspace_bytes(int32_t dtype, wan_grid g, int32_t B, int32_t heads, int32_t head_dim) {
+  if ((dtype != WAN_F32 && dtype != WAN_BF16) || B <= 0 || heads <= 0 || head_dim <= 0) return 0;
+  if (g.T <= 0 || g.Hp <= 0 || g.Wp <= 0) return 0;
+  const int64_t S = (int64_t)g.T * g.Hp * g.Wp, dim = (int64_t)heads * head_dim;
+  const size_t es = esize(dtype);
+  return 2 * a256((size_t)B * S * dim * es) + a256((size_t)B * dim * pad64(S) * es);
+}
+
+template <typename T>
+static int attention_t(const T* q, const T* k, const T* v, const wan_grid& g, int B, int H, int hd, float theta, T* o,
+                       void* ws, hipStream_t st) {
+  const int S = g.T * g.Hp * g.Wp, dim = H * hd, Spad = (int)pad64(S);
+  Carve cv{reinterpret_cast<char*>(ws)};
+  T* qr = cv.take<T>((size_t)B * S * dim);
+  T* kr = cv.take<T>((size_t)B * S * dim);
+  T* vt = cv.take<T>((size_t)B * dim * Spad);
+  HIP_TRY(launch_qk_norm_rope<T>(q, k, dim, qr, kr, dim, B, g.T, g.Hp, g.Wp, H, hd, nullptr, nullptr, 0, 0.f, theta, st));
+  HIP_TRY(launch_transpose_heads<T>(v, dim, 0, B, S, H, hd, Spad, vt, st));
+  KVStream s0{kr, (int64_t)S * dim, dim, vt, S, Spad};
+  HIP_TRY(launch_attention<T>(qr, (int64_t)S * dim, dim, s0, s0, 1, B, S, H, hd, 1.f / sqrtf((float)hd), o,
+                              (int64_t)S * dim, dim, st));
+  return WAN_OK;
+}
+
+int wan_attention_fwd(int32_t dtype, const void* q, const void* k, const void* v, wan_grid grid, int32_t B,
+                      int32_t heads, int32_t head_dim, float rope_theta, void* o, void* ws, size_t ws_bytes,
+                      wan_stream_t stream) {
+  WAN_TRY(check_dtype(dtype));
+  WAN_TRY(check_grid(grid));
+  if (B <= 0 || heads <= 0) return fail(WAN_EINVAL, "B and heads must be positive");
+  if (head_dim != 64 && head_dim != 128) return fail(WAN_EUNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if (heads * head_dim > 6144) return fail(WAN_EUNSUPPORTED, "heads*head_dim > 6144");
+  if (!(rope_theta > 0.f)) return fail(WAN_EINVAL, "rope_theta must be > 0");
+  if ((int64_t)B * grid.T * grid.Hp * grid.Wp > (1ll << 30)) return fail(WAN_EUNSUPPORTED, "too many rows");
+  WAN_TRY(need_ptr(q, "q"));
+  WAN_TRY(need_ptr(k, "k"));
+  WAN_TRY(need_ptr(v, "v"));
+  WAN_TRY(need_ptr(o, "o"));
+  const size_t need = wan_attention_workspace_bytes(dtype, grid, B, heads, head_dim);
+  if (ws_bytes < need) return fail(WAN_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  WAN_TRY(need_ptr(ws, "ws"));
+  if (dtype == WAN_BF16)
+    return attention_t<bf16>((const bf16*)q, (const bf16*)k, (const bf16*)v, grid, B, heads, head_dim, rope_theta,
+                             (bf16*)o, ws, hs(stream));
+  return attention_t<float>((const float*)q, (const float*)k, (const float*)v, grid, B, heads, head_dim, rope_theta,
+                            (float*)o, ws, hs(stream));
+}

@@ -1,0 +1,81 @@
+// Shared device helpers for the gfx950 (CDNA4) kernels of the Wan DiT step.
+//
+// Storage types: float (f32 mode) and bf16 (__bf16, bf16 mode).  GEMM and
+// attention operands are one of the two; accumulation, norms, statistics,
+// modulation, the residual stream and latents are always fp32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wan {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// 16-byte load/store unit used for every global <-> LDS move.
+struct alignas(16) u32x4 {
+  uint32_t x, y, z, w;
+};
+
+template <typename T> struct dtype_traits;
+template <> struct dtype_traits<float> {
+  static constexpr int per16 = 4;  // elements per 16 bytes
+};
+template <> struct dtype_traits<bf16> {
+  static constexpr int per16 = 8;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+
+// Wave-wide (64 lanes) reductions.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA 32x32 helpers.  One "k-chunk" is 32 bytes of K per operand row: lane l
+// supplies row (l % 32) and the 16 bytes at byte offset (l / 32) * 16 of the
+// chunk.  For bf16 that is one v_mfma_f32_32x32x16_bf16 (8 elements per lane);
+// for f32 it is four v_mfma_f32_32x32x2_f32, instruction i taking element i of
+// the lane's 4 (lane half h then holds k = 4h + i, so A and B agree on k).
+// Output layout (both): lane l holds column (l % 32) and rows
+// (j / 4) * 8 + (l / 32) * 4 + (j % 4), j = 0..15.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void mfma_chunk(const u32x4& a, const u32x4& b, f32x16& acc, bf16) {
+  bf16x8 av = __builtin_bit_cast(bf16x8, a);
+  bf16x8 bv = __builtin_bit_cast(bf16x8, b);
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mfma_chunk(const u32x4& a, const u32x4& b, f32x16& acc, float) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+__host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ __forceinline__ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+}  // namespace wan

@@ -1,0 +1,78 @@
+// Internal launchers shared by the kernel files and the C-ABI layer.
+// Every launcher enqueues on `stream` and returns hipGetLastError() of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wan_common.h"
+
+namespace wan {
+
+// Activation applied in a GEMM / GEMV epilogue.
+enum Act { ACT_NONE = 0, ACT_GELU = 1, ACT_SILU = 2 };
+
+// ---- layout (layout.hip) ----------------------------------------------------
+hipError_t launch_i2v_input(const float* x_t, const float* z_img, const uint64_t mask_bits[4], int B, int C,
+                            int T, int H, int W, float* x_in, hipStream_t s);
+hipError_t launch_patchify(const float* x, int B, int C, int T, int H, int W, float* p, hipStream_t s);
+hipError_t launch_unpatchify(const float* p, int B, int C, int T, int H, int W, float* x, hipStream_t s);
+hipError_t launch_euler(float* x, const float* v_c, const float* v_u, float guidance, float dt, int64_t n,
+                        hipStream_t s);
+template <typename T>
+hipError_t launch_convert(const float* in, T* out, int64_t n, hipStream_t s);
+// V [B, S, *] rows (row stride ld elements, head h at column col0 + h*hd) -> V^T [B, H, hd, Spad],
+// zero-filled for tokens S..Spad-1.
+template <typename T>
+hipError_t launch_transpose_heads(const T* v, int64_t ld, int64_t col0, int B, int S, int H, int hd, int Spad,
+                                  T* vt, hipStream_t s);
+
+// ---- norms (norm.hip) -------------------------------------------------------
+// Row-wise LayerNorm of fp32 x [rows, dim] followed by one of:
+//  mode 0 (adaLN):   u = LN(x) * (1 + (e0[b][c_scale] + mb[c_scale])) + (e0[b][c_shift] + mb[c_shift])
+//                    with e0 [B, 6, dim], mb = per-block modulation bias [6, dim], b = row / S;
+//  mode 1 (affine):  u = LN(x) * w + bias (w = p0, bias = p1, each [dim]);
+//  mode 2 (head):    u = LN(x) * (1 + (hm[1] + e[b])) + (hm[0] + e[b]) with hm = p0 [2, dim], e = p1 [B, dim].
+template <typename T>
+hipError_t launch_ln_mod(const float* x, int64_t rows, int dim, int S, int mode, const float* p0, const float* p1,
+                         int c_shift, int c_scale, float eps, T* u, hipStream_t s);
+// In-place RMSNorm (optional) + gain + 3D RoPE on the q and k column blocks of token rows.
+template <typename T>
+hipError_t launch_qk_norm_rope(const T* q_in, const T* k_in, int64_t ld_in, T* q_out, T* k_out, int64_t ld_out,
+                               int B, int T_, int Hp, int Wp, int heads, int hd, const float* gq,
+                               const float* gk, int do_norm, float eps, float theta, hipStream_t s);
+
+// ---- GEMM (gemm.hip) --------------------------------------------------------
+// C[m, n] = sum_k A[m, k] * W[n, k]   (A [M, K] row-major, W [N, K] row-major)
+// Epilogues:
+//   store:      out[m, n] = act(C + bias[n])  (OutT = T or float)
+//   residual:   x[m, n] += g(m, n) * (C + bias[n]), g = e0[m / S][chunk][n] + mb[chunk][n], or 1 if e0 null.
+template <typename T, typename OutT>
+hipError_t gemm_store(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const float* bias,
+                      int act, OutT* out, int64_t ldo, hipStream_t s);
+template <typename T>
+hipError_t gemm_residual(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const float* bias,
+                         const float* e0, const float* mb, int chunk, int S, float* x, int64_t ldx, hipStream_t s);
+// y[b, n] = out_act(sum_k W[n, k] * in_act(x[b, k]) + bias[n]) for b < B (fp32 x, y).
+template <typename T>
+hipError_t gemv(const T* W, int N, int K, const float* x, int B, const float* bias, int in_act, int out_act,
+                float* y, hipStream_t s);
+hipError_t launch_sinusoid(const float* t_host, int B, int freq_dim, float* emb, hipStream_t s);
+
+// ---- attention (attention.hip) ----------------------------------------------
+// Flash attention, non-causal, over one or two key/value streams whose outputs are summed.
+// q:  element (b, s, h, d) at q[b*q_bs + s*q_ss + h*hd + d]
+// k:  element (b, j, h, d) at k[b*k_bs + j*k_ss + h*hd + d]
+// vt: element (b, h, d, j) at vt[((b*H + h)*hd + d)*Lpad + j]  (zero beyond L)
+// o:  element (b, s, h, d) at o[b*o_bs + s*o_ss + h*hd + d]
+struct KVStream {
+  const void* k;
+  int64_t k_bs, k_ss;
+  const void* vt;
+  int L, Lpad;
+};
+template <typename T>
+hipError_t launch_attention(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0, KVStream s1, int nstreams, int B,
+                            int S, int H, int hd, float scale, T* o, int64_t o_bs, int64_t o_ss, hipStream_t s);
+
+}  // namespace wan

@@ -1,0 +1,190 @@
+"""Device-resident weights and the denoise-step call sequence over the C ABI.
+
+Uploads weights once (packing W_q/W_k/W_v and the cross-attention W_k/W_v into
+the fused layouts include/wan.h documents), keeps the ctypes structs that point
+at them, and calls the library's entry points in the order of one DiT
+evaluation ("图解 Wan2.1 I2V" §7): [I2V input] -> patchify -> patch embedding ->
+timestep embedding -> blocks -> head -> unpatchify -> CFG + Euler.  No
+arithmetic happens here.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+def _dt(dtype: str):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def to_dev(a, dtype=torch.float32, device="cuda"):
+    """Upload a host array (values already representable in `dtype`)."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(device=device).to(dtype).contiguous()
+
+
+class _Keep:
+    """Holds device tensors referenced by a ctypes struct."""
+
+    def __init__(self):
+        self.t = {}
+
+    def put(self, name, tensor):
+        self.t[name] = tensor
+        return None if tensor is None else tensor.data_ptr()
+
+
+def cfg_of(c, dtype=None):
+    """BlockCfg from a workload description (attributes dim, heads, head_dim, ffn_dim,
+    text_len, img_len, dtype, ln_eps, rms_eps, rope_theta)."""
+    d = dtype if dtype is not None else c.dtype
+    return L.block_cfg(c.dim, c.heads, c.head_dim, c.ffn_dim, max(c.text_len, 1), c.img_len,
+                       L.WAN_BF16 if d == "bf16" else L.WAN_F32, c.ln_eps, c.rms_eps, c.rope_theta)
+
+
+class DeviceBlock:
+    """One block's weights on the device + its BlockWeights / CrossKVWeights structs."""
+
+    def __init__(self, w: dict, dtype: str, device="cuda", tensors=None):
+        wd = _dt(dtype)
+        k = _Keep()
+        if tensors is not None:  # already-on-device tensors (benchmark path)
+            g = tensors
+        else:
+            g = {}
+            g["wqkv"] = to_dev(np.concatenate([w["wq"], w["wk"], w["wv"]]), wd, device)
+            g["bqkv"] = to_dev(np.concatenate([w["bq"], w["bk"], w["bv"]]), torch.float32, device)
+            for n in ("wo", "wcq", "wco", "w1", "w2"):
+                g[n] = to_dev(w[n], wd, device)
+            for n in ("mod_bias", "gq", "gk", "bo", "ln3_w", "ln3_b", "bcq", "bco", "b1", "b2"):
+                g[n] = to_dev(w[n], torch.float32, device)
+            g["wkv_txt"] = to_dev(np.concatenate([w["wck"], w["wcv"]]), wd, device)
+            g["bkv_txt"] = to_dev(np.concatenate([w["bck"], w["bcv"]]), torch.float32, device)
+            if "wki" in w:
+                g["wkv_img"] = to_dev(np.concatenate([w["wki"], w["wvi"]]), wd, device)
+                g["bkv_img"] = to_dev(np.concatenate([w["bki"], w["bvi"]]), torch.float32, device)
+        self.bw = L.BlockWeights(*[k.put(n, g[n]) for n in (
+            "mod_bias", "wqkv", "bqkv", "gq", "gk", "wo", "bo", "ln3_w", "ln3_b", "wcq", "bcq", "wco", "bco",
+            "w1", "b1", "w2", "b2")])
+        self.kvw = L.CrossKVWeights(k.put("wkv_txt", g["wkv_txt"]), k.put("bkv_txt", g["bkv_txt"]),
+                                    k.put("wkv_img", g.get("wkv_img")), k.put("bkv_img", g.get("bkv_img")))
+        self._keep = k
+
+
+class CrossKVCache:
+    """Per-block cross-attention K / V^T buffers (computed once per generation)."""
+
+    def __init__(self, cfg: L.BlockCfg, B: int, device="cuda"):
+        self.bufs = [torch.empty(max(L.cross_kv_buffer_bytes(cfg, B, i), 16), dtype=torch.uint8, device=device)
+                     if (i < 2 or cfg.img_len > 0) else None for i in range(4)]
+        self.kv = L.CrossKV(*[None if b is None else b.data_ptr() for b in self.bufs])
+
+
+class DeviceModel:
+    """Model-level weights: patch embedding, timestep MLP, context MLPs, head."""
+
+    def __init__(self, w: dict, dtype: str, device="cuda"):
+        wd = _dt(dtype)
+        k = _Keep()
+        f = lambda n: to_dev(w[n], torch.float32, device)
+        m = lambda n: to_dev(w[n], wd, device)
+        self.w_pe, self.b_pe = m("w_pe"), f("b_pe")
+        self.tw = L.TimeWeights(k.put("wt1", m("wt1")), k.put("bt1", f("bt1")), k.put("wt2", m("wt2")),
+                                k.put("bt2", f("bt2")), k.put("wtp", m("wtp")), k.put("btp", f("btp")))
+        self.hw = L.HeadWeights(k.put("head_mod", f("head_mod")), k.put("wh", m("wh")), k.put("bh", f("bh")))
+        self.txt = (m("wtx1"), f("btx1"), m("wtx2"), f("btx2"))
+        self.img = (m("wim1"), f("bim1"), m("wim2"), f("bim2")) if "wim1" in w else None
+        self._keep = k
+
+
+@dataclass
+class StepBuffers:
+    x_in: torch.Tensor
+    p: torch.Tensor
+    x: torch.Tensor
+    e: torch.Tensor
+    e0: torch.Tensor
+    head_out: torch.Tensor
+    v: torch.Tensor
+    ws: torch.Tensor
+
+
+def embed_contexts(c, model: DeviceModel, ctx_txt, ctx_img, B, device="cuda"):
+    """Context MLPs, once per generation.  ctx_txt [B, L, text_dim] host; ctx_img [Li, img_dim] host
+    (shared by all rows).  Returns (txt_emb [B, L, dim], img_emb [B, Li, dim] or None) device tensors."""
+    cfg = cfg_of(c)
+    wd = _dt(c.dtype)
+    txt = to_dev(ctx_txt, wd, device)
+    out_t = torch.empty((B, c.text_len, c.dim), dtype=wd, device=device)
+    rows = B * max(c.text_len, c.img_len)
+    ws = torch.empty(max(L.context_embed_ws_bytes(cfg, rows), 16), dtype=torch.uint8, device=device)
+    L.context_embed(cfg, txt, *model.txt, out_t, ws)
+    out_i = None
+    if c.img_len > 0:
+        img = to_dev(np.broadcast_to(ctx_img[None], (B,) + ctx_img.shape), wd, device)
+        out_i = torch.empty((B, c.img_len, c.dim), dtype=wd, device=device)
+        L.context_embed(cfg, img, *model.img, out_i, ws)
+    return out_t, out_i
+
+
+def cross_kv_all(c, blocks, txt_emb, img_emb, B, device="cuda"):
+    cfg = cfg_of(c)
+    ws = torch.empty(max(L.cross_kv_ws_bytes(cfg, B), 16), dtype=torch.uint8, device=device)
+    caches = []
+    for blk in blocks:
+        kc = CrossKVCache(cfg, B, device)
+        L.cross_kv_fwd(cfg, blk.kvw, txt_emb, img_emb, B, kc.kv, ws)
+        caches.append(kc)
+    return caches
+
+
+def alloc_step(c, B, device="cuda") -> StepBuffers:
+    cfg = cfg_of(c)
+    S = c.S
+    ws_bytes = max(L.block_ws_bytes(cfg, c.grid, B), L.patch_embed_ws_bytes(cfg, B * S, c.in_channels),
+                   L.head_ws_bytes(cfg, B * S), 16)
+    f32 = torch.float32
+    return StepBuffers(
+        x_in=torch.empty((B, c.in_channels, c.T, c.H, c.W), dtype=f32, device=device),
+        p=torch.empty((B, S, 4 * c.in_channels), dtype=f32, device=device),
+        x=torch.empty((B, S, c.dim), dtype=f32, device=device),
+        e=torch.empty((B, c.dim), dtype=f32, device=device),
+        e0=torch.empty((B, 6, c.dim), dtype=f32, device=device),
+        head_out=torch.empty((B, S, 4 * c.out_channels), dtype=f32, device=device),
+        v=torch.empty((B, c.out_channels, c.T, c.H, c.W), dtype=f32, device=device),
+        ws=torch.empty(ws_bytes, dtype=torch.uint8, device=device),
+    )
+
+
+def dit_forward(c, model: DeviceModel, blocks, caches, x_latent, z_img, t, buf: StepBuffers, B,
+                known_pixel_frames=None):
+    """One DiT evaluation over B rows sharing the latent x_latent [1, C, T, H, W] (CFG rows see the same
+    x_in).  Result in buf.v [B, C_out, T, H, W]."""
+    cfg = cfg_of(c)
+    one = x_latent.shape[0]
+    for b in range(B):
+        src = x_latent[b % one:b % one + 1]
+        if c.i2v:
+            L.build_i2v_input(src, z_img[b % one:b % one + 1], buf.x_in[b:b + 1], known_pixel_frames)
+            L.patchify(buf.x_in[b:b + 1], buf.p[b:b + 1])
+        else:
+            L.patchify(src, buf.p[b:b + 1])
+    L.patch_embed(cfg, buf.p, c.in_channels, model.w_pe, model.b_pe, buf.x, buf.ws)
+    L.time_embed(cfg, c.freq_dim, model.tw, [t] * B, buf.e, buf.e0)
+    for blk, kc in zip(blocks, caches):
+        L.dit_block_fwd(cfg, blk.bw, c.grid, B, buf.x, buf.e0, kc.kv, buf.ws)
+    L.head_fwd(cfg, model.hw, c.out_channels, B, c.S, buf.x, buf.e, buf.head_out, buf.ws)
+    L.unpatchify(buf.head_out, buf.v)
+    return buf.v
+
+
+def denoise_step(c, model, blocks, caches, x_latent, z_img, t, dt, guidance, buf: StepBuffers, B,
+                 known_pixel_frames=None):
+    """x_latent <- x_latent + dt * v, v = CFG(v_cond, v_uncond) when B == 2 (row 0 conditional)."""
+    v = dit_forward(c, model, blocks, caches, x_latent, z_img, t, buf, B, known_pixel_frames)
+    L.fm_euler_step(x_latent, v[0:1], v[1:2] if B > 1 else None, guidance, dt)
+    return x_latent
