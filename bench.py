@@ -1,0 +1,284 @@
+#!/usr/bin/env python3
+"""Benchmark: one Wan-style video DiT denoise step on one MI355X.
+
+Workload (default): the Wan2.1-1.3B-shaped text-to-video step at 480p x 81 frames --
+latent [16, 21, 60, 104] -> 32760 tokens, dim 1536, 12 heads x 128, FFN 8960, 512 text
+tokens, 32 blocks (the layer count the "图解 Wan2.1 I2V" page gives for 1.3B, §8).
+A step = patchify -> patch embedding -> timestep embedding -> 32 blocks -> head ->
+unpatchify -> flow-matching Euler update, all through libwan.so; inputs and weights
+are resident in HBM before timing starts (context embedding and cross-attention K/V
+are computed once per generation, outside the timed region).
+
+Prints one JSON line with ms per step, the self-attention kernel's TFLOP/s against the
+bf16 dense MFMA peak (timed with HIP events around that kernel inside the timed
+region), a per-kernel breakdown (one extra untimed step) and the CPU oracle's time on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+METRIC = "ms per DiT denoise step + attention TFLOP/s (% MFMA peak) at 32760 tokens"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "self_attn_counters.json")
+ATTN_SRC = os.path.join(ROOT, "video_diffusion_transformer_step_amd", "csrc", "attention.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def block_flops(c):
+    """Algorithmic FLOPs of one block (2MNK per GEMM; 4 B S^2 dim for self-attention, the forward
+    constant of the cost model on the "Wan 技术深度解析" page, §5.1)."""
+    S, d, f, B = c.S, c.dim, c.ffn_dim, c.B
+    gemm = 2 * B * S * d * (3 * d) + 2 * B * S * d * d * 3 + 2 * 2 * B * S * d * f
+    attn = 4 * B * S * S * d
+    cross = 4 * B * S * (c.text_len + c.img_len) * d
+    return gemm + attn + cross, attn
+
+
+def step_flops(c, layers):
+    blk, attn = block_flops(c)
+    S, d = c.S, c.dim
+    extra = 2 * c.B * S * 4 * c.in_channels * d + 2 * c.B * S * d * 4 * c.out_channels
+    return layers * blk + extra, attn
+
+
+def device_block_tensors(c, gen, device="cuda"):
+    """Random-init weights of one block, drawn on the device from a seeded generator:
+    matrices and biases N(0, 0.02), norm gains 1 + N(0, 0.02)."""
+    import torch
+    bf = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+    d, f = c.dim, c.ffn_dim
+
+    def n(*shape, dtype=torch.float32, mean=0.0):
+        return (torch.randn(*shape, generator=gen, device=device) * 0.02 + mean).to(dtype).contiguous()
+
+    g = {"wqkv": n(3 * d, d, dtype=bf), "bqkv": n(3 * d), "wo": n(d, d, dtype=bf), "wcq": n(d, d, dtype=bf),
+         "wco": n(d, d, dtype=bf), "w1": n(f, d, dtype=bf), "w2": n(d, f, dtype=bf), "mod_bias": n(6, d),
+         "gq": n(d, mean=1.0), "gk": n(d, mean=1.0), "bo": n(d), "ln3_w": n(d, mean=1.0), "ln3_b": n(d),
+         "bcq": n(d), "bco": n(d), "b1": n(f), "b2": n(d), "wkv_txt": n(2 * d, d, dtype=bf),
+         "bkv_txt": n(2 * d)}
+    if c.img_len:
+        g["wkv_img"] = n(2 * d, d, dtype=bf)
+        g["bkv_img"] = n(2 * d)
+    return g
+
+
+def counters_traffic(launch_ms):
+    """HBM bytes per launch of the self-attention kernel from committed rocprofv3 counter
+    runs, only while the kernel source is the one the counters were taken on."""
+    try:
+        with open(COUNTERS_FILE) as fh:
+            rec = json.load(fh)
+        src_hash = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+        if rec.get("attention_hip_sha256") != src_hash:
+            return None
+        return float(rec["hbm_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def cpu_baseline(c, layers, seed=0):
+    """The CPU oracle on a bounded sample: one block in sampled-row mode (K/V for all tokens,
+    then R1 and R2 query rows), extrapolated to all S rows and `layers` blocks."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+    import wan_inputs as wi
+    cores = len(os.sched_getaffinity(0))
+    with threadpoolctl.threadpool_limits(cores):
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+        mw = wi.make_model_weights(c, seed=seed)
+        bw = wi.make_block_weights(c, 0, seed=seed)
+        x = wi.normal(seed, c, "x_block", (1, c.S, c.dim), quantize=False)
+        _, e0 = oracle.time_embed(c.t, mw, c.freq_dim)
+        txt, _ = wi.make_contexts(c, seed=seed)
+        temb = oracle.context_embed(txt[0], mw["wtx1"], mw["btx1"], mw["wtx2"], mw["btx2"])
+        kv = [oracle.cross_kv(temb, bw["wck"], bw["bck"], bw["wcv"], bw["bcv"]) + (None, None)]
+        R1, R2 = 8, 40
+        rows = wi.sample_rows(c, R2, seed=seed)
+        t = time.perf_counter()
+        oracle.block_fwd(x, e0[None], bw, kv, c.grid, c.heads, rows=rows[:R1])
+        t1 = time.perf_counter() - t
+        t = time.perf_counter()
+        oracle.block_fwd(x, e0[None], bw, kv, c.grid, c.heads, rows=rows)
+        t2 = time.perf_counter() - t
+    per_row = max(t2 - t1, 0.0) / (R2 - R1)
+    fixed = max(t1 - R1 * per_row, 0.0)
+    block_s = fixed + c.S * per_row
+    return {
+        "value": round(layers * block_s * 1e3, 1), "unit": "ms/step", "cores": int(threads), "kind": "oracle",
+        "sample": (f"one {c.S}-token block in sampled-row mode (LN/K/V for all tokens, then {R1} and {R2} query "
+                   f"rows: {t1:.2f} s and {t2:.2f} s), extrapolated as (fixed {fixed:.2f} s + {c.S} rows x "
+                   f"{per_row * 1e3:.1f} ms) x {layers} blocks; float64 NumPy, {threads} BLAS threads "
+                   f"of {cores} cores"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="C1", help="workload preset (C1 = 1.3B-shaped 32760-token step)")
+    ap.add_argument("--layers", type=int, default=None, help="blocks per step (default: the preset's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import wan_inputs as wi
+    from video_diffusion_transformer_step_amd import _lib as L
+    from video_diffusion_transformer_step_amd import runtime as R
+
+    if not os.path.exists(L.LIB_PATH):
+        from video_diffusion_transformer_step_amd.build import build
+        build()
+    L.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    c = wi.get_config(args.config)
+    layers = args.layers or c.layers
+    seed = 0
+    log(f"workload {c.name}: latent [{c.in_channels},{c.T},{c.H},{c.W}] -> S={c.S}, dim={c.dim}, "
+        f"{c.heads}x{c.head_dim}, ffn={c.ffn_dim}, {layers} blocks, B={c.B}")
+
+    # ---- resident inputs and weights
+    t = time.perf_counter()
+    mw = wi.make_model_weights(c, seed=seed)
+    model = R.DeviceModel(mw, c.dtype)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234)
+    blocks = [R.DeviceBlock(None, c.dtype, tensors=device_block_tensors(c, gen)) for _ in range(layers)]
+    x_t, z = wi.make_latents(c, seed=seed)
+    txt, img = wi.make_contexts(c, seed=seed)
+    t_emb, i_emb = R.embed_contexts(c, model, txt, img, c.B)
+    caches = R.cross_kv_all(c, blocks, t_emb, i_emb, c.B)
+    buf = R.alloc_step(c, c.B)
+    xg = torch.from_numpy(x_t).cuda()
+    zg = torch.from_numpy(z).cuda() if z is not None else None
+    torch.cuda.synchronize()
+    log(f"setup {time.perf_counter() - t:.1f} s; weights {sum(p.numel() * p.element_size() for b in blocks for p in b._keep.t.values() if p is not None) / 1e9:.2f} GB")
+
+    total = args.warmup + args.steps
+    dt = -1.0 / max(total, 1)
+
+    def step(k):
+        R.denoise_step(c, model, blocks, caches, xg, zg, 1.0 + k * dt, dt, c.guidance, buf, c.B)
+
+    for k in range(args.warmup):
+        step(k)
+        torch.cuda.synchronize()
+        log(f"warmup step {k} done")
+
+    # ---- timed region: K steps; self-attention launches bracketed by HIP events on their stream
+    timer = L.KernelTimer(capacity=args.steps * layers, kernels=("self_attn",))
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    with timer:
+        for k in range(args.steps):
+            step(args.warmup + k)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    gpu_ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    attn_ms = timer.times_ms().get("self_attn", [])
+    attn_avg = float(np.mean(attn_ms)) if attn_ms else float("nan")
+    log(f"timed {args.steps} steps: {ms_per_step:.2f} ms/step (events {gpu_ms_per_step:.2f}); "
+        f"self-attention {attn_avg:.3f} ms/launch over {len(attn_ms)} launches")
+    assert np.isfinite(xg.float().cpu().numpy()).all(), "non-finite latent after the timed steps"
+
+    flops_step, attn_flops = step_flops(c, layers)
+    attn_tflops = attn_flops / (attn_avg * 1e-3) / 1e12
+    step_tflops = flops_step / (ms_per_step * 1e-3) / 1e12
+
+    # ---- per-kernel breakdown (one extra, untimed step with every block kernel bracketed)
+    breakdown = None
+    if not args.no_breakdown:
+        bt = L.KernelTimer(capacity=layers * len(L.KERNEL_IDS), kernels=tuple(L.KERNEL_IDS))
+        with bt:
+            step(total)
+        bd = bt.times_ms()
+        blk_flops, _ = block_flops(c)
+        S, d, f = c.S, c.dim, c.ffn_dim
+        fl = {"qkv_gemm": 2 * S * d * 3 * d, "self_attn": 4 * S * S * d, "o_gemm": 2 * S * d * d,
+              "cross_q_gemm": 2 * S * d * d, "cross_attn": 4 * S * (c.text_len + c.img_len) * d,
+              "cross_o_gemm": 2 * S * d * d, "ffn1_gemm": 2 * S * d * f, "ffn2_gemm": 2 * S * f * d}
+        breakdown = {}
+        for k_, v in bd.items():
+            ms = float(np.mean(v))
+            e = {"ms": round(ms, 4)}
+            if k_ in fl:
+                e["tflops"] = round(fl[k_] * c.B / (ms * 1e-3) / 1e12, 1)
+            breakdown[k_] = e
+        breakdown["block_sum_ms"] = round(sum(e["ms"] for e in breakdown.values()), 3)
+        log(f"breakdown: {json.dumps(breakdown)}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t = time.perf_counter()
+        cpu = cpu_baseline(c, layers, seed=seed)
+        log(f"cpu baseline {time.perf_counter() - t:.1f} s: {cpu['value']} ms/step")
+
+    traffic = counters_traffic(attn_avg)
+    out = {
+        "metric": METRIC,
+        "value": round(ms_per_step, 3),
+        "unit": "ms/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c.dtype,
+        "data": "synthetic (seeded N(0,1) latent and text context; random-init N(0,0.02) weights)",
+        "config": {"workload": (f"{c.name}: Wan2.1-1.3B-shaped text-to-video denoise step, latent "
+                                f"[{c.latent_channels},{c.T},{c.H},{c.W}] -> {c.S} tokens, {layers} blocks"),
+                   "global_batch": c.B, "seq_len": c.S, "layers": layers, "dim": c.dim, "heads": c.heads,
+                   "head_dim": c.head_dim, "ffn_dim": c.ffn_dim, "text_len": c.text_len,
+                   "parallelism": "single GPU"},
+        "ms_per_block": round(ms_per_step / layers, 3),
+        "step_tflops": round(step_tflops, 1),
+        "step_frac_of_bf16_peak": round(step_tflops / PEAK_BF16_TFLOPS, 4),
+        "attention_tflops": round(attn_tflops, 1),
+        "attention_frac_of_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"kernel": "self-attention (flash, bf16 MFMA)", "bound": "mfma",
+                     "achieved": round(attn_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "launch_ms": round(attn_avg, 4), "flops_per_launch": attn_flops},
+        "breakdown_ms_per_block": breakdown,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -219,6 +219,22 @@ int wan_attention_fwd(int32_t dtype, const void* q, const void* k, const void* v
                       int32_t heads, int32_t head_dim, float rope_theta, void* o, void* ws, size_t ws_bytes,
                       wan_stream_t stream);
 
+/* Kernel timing (measurement only).  wan_profile_begin hands the library `capacity` caller-created
+ * HIP events (hipEvent_t, passed as void*) for starts and stops plus an int32 tag array; until
+ * wan_profile_end, each launch inside wan_dit_block_fwd whose id bit is set in kernel_mask is
+ * bracketed by hipEventRecord(start[i]) / hipEventRecord(stop[i]) on the launch stream, and tags[i]
+ * receives its wan_kernel_id, until capacity pairs are used.  The arrays must stay valid until
+ * wan_profile_end, which returns the number of pairs recorded and disables recording.  Process-wide
+ * state, not thread-safe; calls that overlap on several threads must not use it. */
+typedef enum {
+  WAN_K_LN1 = 0, WAN_K_QKV_GEMM = 1, WAN_K_QK_NORM_ROPE = 2, WAN_K_V_TRANSPOSE = 3, WAN_K_SELF_ATTN = 4,
+  WAN_K_O_GEMM = 5, WAN_K_LN3 = 6, WAN_K_CROSS_Q_GEMM = 7, WAN_K_CROSS_ATTN = 8, WAN_K_CROSS_O_GEMM = 9,
+  WAN_K_LN2 = 10, WAN_K_FFN1_GEMM = 11, WAN_K_FFN2_GEMM = 12
+} wan_kernel_id;
+int wan_profile_begin(void* const* start_events, void* const* stop_events, int32_t* tags, int32_t capacity,
+                      uint32_t kernel_mask);
+int32_t wan_profile_end(void);
+
 /* Human-readable name of a wan_status; message of the last failed call on this thread. */
 const char* wan_status_string(int status);
 const char* wan_last_error(void);

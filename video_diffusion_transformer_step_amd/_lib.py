@@ -79,6 +79,9 @@ _SIGS = {
     "wan_attention_workspace_bytes": ([C.c_int32, Grid, C.c_int32, C.c_int32, C.c_int32], C.c_size_t),
     "wan_attention_fwd": ([C.c_int32, vp, vp, vp, Grid, C.c_int32, C.c_int32, C.c_int32, C.c_float, vp, vp,
                            C.c_size_t, vp], C.c_int),
+    "wan_profile_begin": ([C.POINTER(C.c_void_p), C.POINTER(C.c_void_p), C.POINTER(C.c_int32), C.c_int32,
+                           C.c_uint32], C.c_int),
+    "wan_profile_end": ([], C.c_int32),
     "wan_status_string": ([C.c_int], C.c_char_p),
     "wan_last_error": ([], C.c_char_p),
 }
@@ -235,3 +238,44 @@ def attention_fwd(q, k, v, grid, o, ws, rope_theta=10000.0, stream=None):
     _check(lib().wan_attention_fwd(dtype_code(q.dtype), _p(q), _p(k), _p(v), Grid(*grid), B, H, hd,
                                    float(rope_theta), _p(o), _p(ws), ws.numel() * ws.element_size(),
                                    _stream(stream)), "wan_attention_fwd")
+
+
+KERNEL_IDS = ["ln1", "qkv_gemm", "qk_norm_rope", "v_transpose", "self_attn", "o_gemm", "ln3", "cross_q_gemm",
+              "cross_attn", "cross_o_gemm", "ln2", "ffn1_gemm", "ffn2_gemm"]
+
+
+class KernelTimer:
+    """Records HIP events around selected kernels of wan_dit_block_fwd (wan_profile_begin/end)."""
+
+    def __init__(self, capacity, kernels=("self_attn",)):
+        import torch
+        self.capacity = capacity
+        self.starts = [torch.cuda.Event(enable_timing=True) for _ in range(capacity)]
+        self.stops = [torch.cuda.Event(enable_timing=True) for _ in range(capacity)]
+        for e in self.starts + self.stops:
+            e.record()  # materialise the underlying hipEvent_t
+        self._s = (C.c_void_p * capacity)(*[e.cuda_event for e in self.starts])
+        self._e = (C.c_void_p * capacity)(*[e.cuda_event for e in self.stops])
+        self._tags = (C.c_int32 * capacity)()
+        self.mask = 0
+        for k in kernels:
+            self.mask |= 1 << KERNEL_IDS.index(k)
+        self.n = 0
+
+    def __enter__(self):
+        _check(lib().wan_profile_begin(self._s, self._e, self._tags, self.capacity, self.mask), "wan_profile_begin")
+        return self
+
+    def __exit__(self, *exc):
+        self.n = lib().wan_profile_end()
+        return False
+
+    def times_ms(self):
+        """{kernel name: [ms per launch]} (synchronises)."""
+        import torch
+        torch.cuda.synchronize()
+        out = {}
+        for i in range(self.n):
+            out.setdefault(KERNEL_IDS[self._tags[i]], []).append(self.starts[i].elapsed_time(self.stops[i]))
+        return out
+

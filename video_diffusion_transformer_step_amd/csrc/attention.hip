@@ -23,7 +23,6 @@ namespace wan {
 
 namespace {
 
-constexpr int QT = 128;  // queries per workgroup
 constexpr int KT = 64;   // keys per tile
 constexpr float RESCALE_THRESHOLD = 8.f;
 
@@ -43,10 +42,10 @@ struct AttnCfg {
   static constexpr int ND = HD / 32;                    // 32-wide d blocks of O^T
 };
 
-template <typename T, int HD>
+template <typename T, int HD, int QB>
 struct StreamState {
-  f32x16 o[AttnCfg<T, HD>::ND];
-  float m, l;
+  f32x16 o[QB][AttnCfg<T, HD>::ND];
+  float m[QB], l[QB];
 };
 
 template <typename T, int HD>
@@ -88,10 +87,11 @@ __device__ __forceinline__ void store_kv_tile(T* buf, int tid, const u32x4* rk, 
   }
 }
 
-// One key/value stream for the wave's 32 queries; accumulates into st.
-template <typename T, int HD>
-__device__ __forceinline__ void attend_stream(const u32x4 (&qf)[AttnCfg<T, HD>::NCH], const KVStream& kv, int b,
-                                              int h, int H, float c_log2, T* smem, StreamState<T, HD>& st) {
+// One key/value stream for the wave's QB x 32 queries; accumulates into st.  Every K / V^T
+// fragment read from LDS feeds QB MFMAs (one per 32-query block).
+template <typename T, int HD, int QB>
+__device__ __forceinline__ void attend_stream(const u32x4 (&qf)[QB][AttnCfg<T, HD>::NCH], const KVStream& kv, int b,
+                                              int h, int H, float c_log2, T* smem, StreamState<T, HD, QB>& st) {
   using C = AttnCfg<T, HD>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int lrow = lane & 31, lhalf = lane >> 5;
@@ -112,16 +112,18 @@ __device__ __forceinline__ void attend_stream(const u32x4 (&qf)[AttnCfg<T, HD>::
     const T* kb_lds = smem + buf * C::BUF;
     const T* vb_lds = kb_lds + C::KBUF;
 
-    // S^T for two 32-key blocks.
-    f32x16 s[2];
+    // S^T for two 32-key blocks and QB query blocks.
+    f32x16 s[QB][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = zero16();
+#pragma unroll
+      for (int q = 0; q < QB; ++q) s[q][kb] = zero16();
       const T* kr = kb_lds + (kb * 32 + lrow) * C::KROW + lhalf * C::E16;
 #pragma unroll
       for (int c = 0; c < C::NCH; ++c) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(kr + c * 2 * C::E16);
-        mfma_chunk(a, qf[c], s[kb], T());
+#pragma unroll
+        for (int q = 0; q < QB; ++q) mfma_chunk(a, qf[q][c], s[q][kb], T());
       }
     }
     // mask keys beyond L (only the last tile can hold any)
@@ -131,53 +133,67 @@ __device__ __forceinline__ void attend_stream(const u32x4 (&qf)[AttnCfg<T, HD>::
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = j0 + kb * 32 + (r >> 2) * 8 + lhalf * 4 + (r & 3);
-          if (key >= kv.L) s[kb][r] = (-__builtin_inff());
+          if (key >= kv.L) {
+#pragma unroll
+            for (int q = 0; q < QB; ++q) s[q][kb][r] = (-__builtin_inff());
+          }
         }
     }
-    float mx = (-__builtin_inff());
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int q = 0; q < QB; ++q) {
+      float mx = (-__builtin_inff());
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mnew = mx * c_log2;
-    const bool need = mnew > st.m + RESCALE_THRESHOLD;
-    if (__ballot(need) != 0ull) {
-      const float mm = need ? mnew : st.m;
-      const float alpha = exp2f(st.m - mm);  // 0 on the first tile (st.m = -inf)
-      st.m = mm;
-      st.l *= alpha;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int d = 0; d < C::ND; ++d)
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[q][kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mnew = mx * c_log2;
+      const bool need = mnew > st.m[q] + RESCALE_THRESHOLD;
+      if (__ballot(need) != 0ull) {
+        const float mm = need ? mnew : st.m[q];
+        const float alpha = __builtin_amdgcn_exp2f(st.m[q] - mm);  // 0 on the first tile (m = -inf)
+        st.m[q] = mm;
+        st.l[q] *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) st.o[d][r] *= alpha;
-    }
-    const float negm = -st.m;
+        for (int d = 0; d < C::ND; ++d)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(fmaf(s[kb][r], c_log2, negm));
-        s[kb][r] = p;
-        st.l += p;
+          for (int r = 0; r < 16; ++r) st.o[q][d][r] *= alpha;
       }
+      const float negm = -st.m[q];
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          // raw v_exp_f32: the argument is <= RESCALE_THRESHOLD or -inf, so no range fix-up is needed
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[q][kb][r], c_log2, negm));
+          s[q][kb][r] = p;
+          lsum += p;
+        }
+      st.l[q] += lsum;
+    }
 
     // O^T += V^T P^T
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {  // 16-key chunks
         const int kb = c >> 1, r0 = (c & 1) * 8;
-        bf16x8 pk;
+        u32x4 pb[QB];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pk[i] = (bf16)s[kb][r0 + i];
-        const u32x4 pb = __builtin_bit_cast(u32x4, pk);
+        for (int q = 0; q < QB; ++q) {
+          bf16x8 pk;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) pk[i] = (bf16)s[q][kb][r0 + i];
+          pb[q] = __builtin_bit_cast(u32x4, pk);
+        }
 #pragma unroll
         for (int d = 0; d < C::ND; ++d) {
           const T* vr = vb_lds + (d * 32 + lrow) * C::VROW + c * 16 + lhalf * 4;
           const uint2 lo = *reinterpret_cast<const uint2*>(vr);
           const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
           const u32x4 a{lo.x, lo.y, hi.x, hi.y};
-          mfma_chunk(a, pb, st.o[d], T());
+#pragma unroll
+          for (int q = 0; q < QB; ++q) mfma_chunk(a, pb[q], st.o[q][d], T());
         }
       }
     } else {
@@ -185,13 +201,16 @@ __device__ __forceinline__ void attend_stream(const u32x4 (&qf)[AttnCfg<T, HD>::
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const u32x4 pb{__float_as_uint(s[kb][4 * g]), __float_as_uint(s[kb][4 * g + 1]),
-                         __float_as_uint(s[kb][4 * g + 2]), __float_as_uint(s[kb][4 * g + 3])};
 #pragma unroll
           for (int d = 0; d < C::ND; ++d) {
             const T* vr = vb_lds + (d * 32 + lrow) * C::VROW + kb * 32 + g * 8 + lhalf * 4;
             const u32x4 a = *reinterpret_cast<const u32x4*>(vr);
-            mfma_chunk(a, pb, st.o[d], T());
+#pragma unroll
+            for (int q = 0; q < QB; ++q) {
+              const u32x4 pb{__float_as_uint(s[q][kb][4 * g]), __float_as_uint(s[q][kb][4 * g + 1]),
+                             __float_as_uint(s[q][kb][4 * g + 2]), __float_as_uint(s[q][kb][4 * g + 3])};
+              mfma_chunk(a, pb, st.o[q][d], T());
+            }
           }
         }
     }
@@ -200,49 +219,67 @@ __device__ __forceinline__ void attend_stream(const u32x4 (&qf)[AttnCfg<T, HD>::
   }
 }
 
-template <typename T, int HD, int NS>
-__global__ __launch_bounds__(256, 2) void attention_kernel(const T* __restrict__ q, int64_t q_bs, int64_t q_ss,
-                                                            KVStream s0, KVStream s1, int S, int H, float c_log2,
-                                                            T* __restrict__ o, int64_t o_bs, int64_t o_ss) {
+template <typename T, int HD, int NS, int QB>
+__global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void attention_kernel(
+    const T* __restrict__ q, int64_t q_bs, int64_t q_ss, KVStream s0, KVStream s1, int S, int H, float c_log2,
+    T* __restrict__ o, int64_t o_bs, int64_t o_ss) {
   using C = AttnCfg<T, HD>;
   __shared__ u32x4 smem_raw[2 * C::BUF * sizeof(T) / 16];
   T* smem = reinterpret_cast<T*>(smem_raw);
   const int h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 31, lhalf = lane >> 5;
-  const int qrow = blockIdx.x * QT + wave * 32 + lrow;
+  const int qrow0 = blockIdx.x * (4 * QB * 32) + wave * (QB * 32) + lrow;
 
   // Q^T as the B operand: lane holds query qrow, 16 bytes per 32-byte chunk of hd.
-  u32x4 qf[C::NCH];
-  const T* qp = q + (int64_t)b * q_bs + (int64_t)qrow * q_ss + (int64_t)h * HD + lhalf * C::E16;
+  u32x4 qf[QB][C::NCH];
 #pragma unroll
-  for (int c = 0; c < C::NCH; ++c)
-    qf[c] = (qrow < S) ? *reinterpret_cast<const u32x4*>(qp + c * 2 * C::E16) : u32x4{0, 0, 0, 0};
-
-  StreamState<T, HD> st;
-  f32x16 acc[C::ND];
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = qrow0 + qb * 32;
+    const T* qp = q + (int64_t)b * q_bs + (int64_t)qrow * q_ss + (int64_t)h * HD + lhalf * C::E16;
 #pragma unroll
-  for (int d = 0; d < C::ND; ++d) {
-    st.o[d] = zero16();
-    acc[d] = zero16();
+    for (int c = 0; c < C::NCH; ++c)
+      qf[qb][c] = (qrow < S) ? *reinterpret_cast<const u32x4*>(qp + c * 2 * C::E16) : u32x4{0, 0, 0, 0};
   }
+
+  StreamState<T, HD, QB> st;
+  f32x16 acc[QB][C::ND];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int d = 0; d < C::ND; ++d) {
+      st.o[qb][d] = zero16();
+      if (NS > 1) acc[qb][d] = zero16();
+    }
 #pragma unroll
   for (int si = 0; si < NS; ++si) {
-    st.m = (-__builtin_inff());
-    st.l = 0.f;
-    if (si > 0) {
 #pragma unroll
-      for (int d = 0; d < C::ND; ++d) st.o[d] = zero16();
+    for (int qb = 0; qb < QB; ++qb) {
+      st.m[qb] = (-__builtin_inff());
+      st.l[qb] = 0.f;
+      if (si > 0) {
+#pragma unroll
+        for (int d = 0; d < C::ND; ++d) st.o[qb][d] = zero16();
+      }
     }
-    attend_stream<T, HD>(qf, si == 0 ? s0 : s1, b, h, H, c_log2, smem, st);
-    const float inv = 1.f / (st.l + __shfl_xor(st.l, 32, 64));
+    attend_stream<T, HD, QB>(qf, si == 0 ? s0 : s1, b, h, H, c_log2, smem, st);
 #pragma unroll
-    for (int d = 0; d < C::ND; ++d)
+    for (int qb = 0; qb < QB; ++qb) {
+      const float inv = 1.f / (st.l[qb] + __shfl_xor(st.l[qb], 32, 64));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[d][r] += st.o[d][r] * inv;
+      for (int d = 0; d < C::ND; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (NS > 1) acc[qb][d][r] += st.o[qb][d][r] * inv;
+          else acc[qb][d][r] = st.o[qb][d][r] * inv;
+        }
+    }
   }
 
-  if (qrow < S) {
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = qrow0 + qb * 32;
+    if (qrow >= S) continue;
     T* op = o + (int64_t)b * o_bs + (int64_t)qrow * o_ss + (int64_t)h * HD;
 #pragma unroll
     for (int d = 0; d < C::ND; ++d)
@@ -252,26 +289,31 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const T* __restrict__
         if constexpr (sizeof(T) == 2) {
           bf16x4 v;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = (bf16)acc[d][4 * g + i];
+          for (int i = 0; i < 4; ++i) v[i] = (bf16)acc[qb][d][4 * g + i];
           *reinterpret_cast<bf16x4*>(op + dd) = v;
         } else {
           *reinterpret_cast<float4*>(op + dd) =
-              make_float4(acc[d][4 * g], acc[d][4 * g + 1], acc[d][4 * g + 2], acc[d][4 * g + 3]);
+              make_float4(acc[qb][d][4 * g], acc[qb][d][4 * g + 1], acc[qb][d][4 * g + 2], acc[qb][d][4 * g + 3]);
         }
       }
   }
 }
 
+#ifndef WAN_ATTN_QB
+#define WAN_ATTN_QB 1
+#endif
+
 template <typename T, int HD>
 hipError_t launch_hd(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0, KVStream s1, int nstreams, int B, int S,
                      int H, float c_log2, T* o, int64_t o_bs, int64_t o_ss, hipStream_t s) {
-  dim3 grid((unsigned)ceil_div(S, QT), (unsigned)H, (unsigned)B);
+  constexpr int QB = (sizeof(T) == 2 && HD == 128) ? WAN_ATTN_QB : 1;
+  dim3 grid((unsigned)ceil_div(S, 4 * QB * 32), (unsigned)H, (unsigned)B);
   if (nstreams == 2)
-    hipLaunchKernelGGL((attention_kernel<T, HD, 2>), grid, dim3(256), 0, s, q, q_bs, q_ss, s0, s1, S, H, c_log2, o,
-                       o_bs, o_ss);
+    hipLaunchKernelGGL((attention_kernel<T, HD, 2, 1>), dim3((unsigned)ceil_div(S, 128), H, B), dim3(256), 0, s, q,
+                       q_bs, q_ss, s0, s1, S, H, c_log2, o, o_bs, o_ss);
   else
-    hipLaunchKernelGGL((attention_kernel<T, HD, 1>), grid, dim3(256), 0, s, q, q_bs, q_ss, s0, s1, S, H, c_log2, o,
-                       o_bs, o_ss);
+    hipLaunchKernelGGL((attention_kernel<T, HD, 1, QB>), grid, dim3(256), 0, s, q, q_bs, q_ss, s0, s1, S, H, c_log2,
+                       o, o_bs, o_ss);
   return hipGetLastError();
 }
 

@@ -4,17 +4,31 @@
 //
 // Every linear layer computes y = x W^T + b with W stored [out, in] ("图解 Wan2.1
 // I2V" §5.3-§5.5 and the Conv3d patch embedding of §5.1), so both operands are
-// contiguous along K (an "NT" product).  One workgroup owns a BM x BN output tile;
-// K advances 128 bytes at a time (64 bf16 or 32 fp32), staged through
-// double-buffered LDS with register prefetch of the next K tile.  Each wave
-// computes a (BM/WM) x (BN/WN) sub-tile with 32x32 MFMA blocks.  Epilogues fuse
-// the bias, GELU / SiLU, the fp32 store and the adaLN-gated residual update
-// x += gate * (.) ("图解 Wan2.1 I2V" §5.2).
+// contiguous along K (an "NT" product).
+//
+// Design (gfx950):
+//  * one workgroup owns a BM x BN output tile; K advances 128 bytes per step (64
+//    bf16 / 32 fp32), staged through double-buffered, row-padded LDS with
+//    register prefetch of the next step (one barrier per step);
+//  * each wave computes a (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks.  The
+//    MFMA is issued as C^T = W A^T (A-operand = weight rows), so a lane's
+//    accumulator holds 4 consecutive output columns of one row: the epilogue
+//    reads bias / gate / residual and writes results 4 columns (8 or 16 bytes)
+//    at a time;
+//  * loads are predicate-free: out-of-range rows are clamped to the last valid
+//    row (their results are never stored); only a final partial K step zero-fills;
+//  * the 1D grid is remapped so each XCD (blockIdx % 8) receives a contiguous run
+//    of tiles, grouped GROUP_M row-tiles at a time, so concurrent tiles share A
+//    rows and W columns in that XCD's L2;
+//  * epilogues fuse the bias, GELU / SiLU, the output cast and the adaLN-gated
+//    residual update x += gate * (.) ("图解 Wan2.1 I2V" §5.2).
 #include "wan_internal.h"
 
 namespace wan {
 
 namespace {
+
+constexpr int GROUP_M = 8;
 
 __device__ __forceinline__ float apply_act(float v, int act) {
   if (act == ACT_GELU) return 0.5f * v * (1.f + erff(v * 0.70710678118654752f));
@@ -22,16 +36,30 @@ __device__ __forceinline__ float apply_act(float v, int act) {
   return v;
 }
 
+// Epilogues receive four consecutive columns n..n+3 of row m.
 template <typename OutT>
 struct EpiStore {
   OutT* out;
   int64_t ldo;
   const float* bias;
   int act;
-  __device__ __forceinline__ void operator()(int m, int n, float v) const {
-    if (bias) v += bias[n];
-    v = apply_act(v, act);
-    out[(int64_t)m * ldo + n] = from_f32<OutT>(v);
+  __device__ __forceinline__ void operator()(int m, int n, float4 v) const {
+    if (bias) {
+      const float4 b = *reinterpret_cast<const float4*>(bias + n);
+      v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+    }
+    if (act != ACT_NONE) {
+      v.x = apply_act(v.x, act); v.y = apply_act(v.y, act);
+      v.z = apply_act(v.z, act); v.w = apply_act(v.w, act);
+    }
+    OutT* p = out + (int64_t)m * ldo + n;
+    if constexpr (sizeof(OutT) == 2) {
+      bf16x4 o;
+      o[0] = (bf16)v.x; o[1] = (bf16)v.y; o[2] = (bf16)v.z; o[3] = (bf16)v.w;
+      *reinterpret_cast<bf16x4*>(p) = o;
+    } else {
+      *reinterpret_cast<float4*>(p) = v;
+    }
   }
 };
 
@@ -42,72 +70,105 @@ struct EpiResidual {
   const float* e0;  // [B, 6, N] or null (gate 1)
   const float* mb;  // [6, N]
   int chunk, S, N;
-  __device__ __forceinline__ void operator()(int m, int n, float v) const {
-    if (bias) v += bias[n];
-    float g = 1.f;
-    if (e0) {
-      const int b = m / S;
-      g = e0[((int64_t)b * 6 + chunk) * N + n] + mb[(int64_t)chunk * N + n];
+  __device__ __forceinline__ void operator()(int m, int n, float4 v) const {
+    if (bias) {
+      const float4 b = *reinterpret_cast<const float4*>(bias + n);
+      v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
     }
     float* p = x + (int64_t)m * ldx + n;
-    *p = *p + g * v;
+    float4 r = *reinterpret_cast<const float4*>(p);
+    if (e0) {
+      const int b = m / S;
+      const float4 g = *reinterpret_cast<const float4*>(e0 + ((int64_t)b * 6 + chunk) * N + n);
+      const float4 h = *reinterpret_cast<const float4*>(mb + (int64_t)chunk * N + n);
+      r.x = fmaf(g.x + h.x, v.x, r.x); r.y = fmaf(g.y + h.y, v.y, r.y);
+      r.z = fmaf(g.z + h.z, v.z, r.z); r.w = fmaf(g.w + h.w, v.w, r.w);
+    } else {
+      r.x += v.x; r.y += v.y; r.z += v.z; r.w += v.w;
+    }
+    *reinterpret_cast<float4*>(p) = r;
   }
 };
 
-// BM x BN tile, WM x WN waves.  BK = 128 bytes of K.
+// Map a linear block id to (tile_m, tile_n): XCD-contiguous runs, then GROUP_M-row groups.
+__device__ __forceinline__ void tile_coords(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int n = tiles_m * tiles_n;
+  const int q = n >> 3, r = n & 7;
+  const int xcd = id & 7, k = id >> 3;
+  const int t = xcd * q + min(xcd, r) + k;  // bijection on [0, n)
+  const int per_group = GROUP_M * tiles_n;
+  const int g = t / per_group;
+  const int first_m = g * GROUP_M;
+  const int gsz = min(tiles_m - first_m, GROUP_M);
+  const int w = t - g * per_group;
+  tm = first_m + w % gsz;
+  tn = w / gsz;
+}
+
 template <typename T, int BM, int BN, int WM, int WN, class Epi>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restrict__ A, int64_t lda,
                                                                const T* __restrict__ W, int64_t ldw, int M,
-                                                               int N, int K, Epi epi) {
+                                                               int N, int K, int tiles_m, int tiles_n, Epi epi) {
   constexpr int NT = WM * WN * 64;
   constexpr int E16 = dtype_traits<T>::per16;  // elements per 16 bytes
-  constexpr int BK = 8 * E16;                  // 128 bytes
-  constexpr int ROW = BK + E16;                // padded LDS row (144 bytes): conflict-free 16 B reads
+  constexpr int BK = 8 * E16;                  // 128 bytes of K per step
+  constexpr int ROW = BK + E16;                // padded LDS row (144 bytes): conflict-free 16-byte reads
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
-  constexpr int AC = BM * 8 / NT, BC = BN * 8 / NT;  // 16-byte chunks per thread
+  constexpr int AC = BM * 8 / NT, BC = BN * 8 / NT;  // 16-byte chunks per thread per step
+  constexpr int STAGE = (BM + BN) * ROW;
   static_assert(AC * NT == BM * 8 && BC * NT == BN * 8, "tile / thread mismatch");
-  __shared__ u32x4 smem_raw[2 * (BM + BN) * ROW * sizeof(T) / 16];
+  __shared__ u32x4 smem_raw[2 * STAGE * sizeof(T) / 16];
   T* smem = reinterpret_cast<T*>(smem_raw);
 
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
+  // Per-thread global source rows (clamped into range) and LDS destinations.
+  const T* pa[AC];
+  const T* pb[BC];
+  int la[AC], lb[BC];
+#pragma unroll
+  for (int i = 0; i < AC; ++i) {
+    const int c = tid + i * NT, r = c >> 3, kc = (c & 7) * E16;
+    pa[i] = A + (int64_t)min(m0 + r, M - 1) * lda + kc;
+    la[i] = r * ROW + kc;
+  }
+#pragma unroll
+  for (int i = 0; i < BC; ++i) {
+    const int c = tid + i * NT, r = c >> 3, kc = (c & 7) * E16;
+    pb[i] = W + (int64_t)min(n0 + r, N - 1) * ldw + kc;
+    lb[i] = BM * ROW + r * ROW + kc;
+  }
+
   u32x4 ra[AC], rb[BC];
-  auto load_tile = [&](int k0) {
+  auto load_full = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < AC; ++i) ra[i] = *reinterpret_cast<const u32x4*>(pa[i] + k0);
+#pragma unroll
+    for (int i = 0; i < BC; ++i) rb[i] = *reinterpret_cast<const u32x4*>(pb[i] + k0);
+  };
+  auto load_tail = [&](int k0) {  // last, partial K step: zero-fill k >= K
 #pragma unroll
     for (int i = 0; i < AC; ++i) {
-      const int c = tid + i * NT, r = c >> 3, kk = k0 + (c & 7) * E16;
-      const int gm = m0 + r;
-      if (gm < M && kk < K)
-        ra[i] = *reinterpret_cast<const u32x4*>(A + (int64_t)gm * lda + kk);
-      else
-        ra[i] = u32x4{0, 0, 0, 0};
+      const int kk = k0 + ((tid + i * NT) & 7) * E16;
+      ra[i] = kk < K ? *reinterpret_cast<const u32x4*>(pa[i] + k0) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < BC; ++i) {
-      const int c = tid + i * NT, r = c >> 3, kk = k0 + (c & 7) * E16;
-      const int gn = n0 + r;
-      if (gn < N && kk < K)
-        rb[i] = *reinterpret_cast<const u32x4*>(W + (int64_t)gn * ldw + kk);
-      else
-        rb[i] = u32x4{0, 0, 0, 0};
+      const int kk = k0 + ((tid + i * NT) & 7) * E16;
+      rb[i] = kk < K ? *reinterpret_cast<const u32x4*>(pb[i] + k0) : u32x4{0, 0, 0, 0};
     }
   };
-  auto store_tile = [&](int buf) {
-    T* sa = smem + buf * (BM + BN) * ROW;
-    T* sb = sa + BM * ROW;
+  auto store_stage = [&](int buf) {
+    T* st = smem + buf * STAGE;
 #pragma unroll
-    for (int i = 0; i < AC; ++i) {
-      const int c = tid + i * NT;
-      *reinterpret_cast<u32x4*>(sa + (c >> 3) * ROW + (c & 7) * E16) = ra[i];
-    }
+    for (int i = 0; i < AC; ++i) *reinterpret_cast<u32x4*>(st + la[i]) = ra[i];
 #pragma unroll
-    for (int i = 0; i < BC; ++i) {
-      const int c = tid + i * NT;
-      *reinterpret_cast<u32x4*>(sb + (c >> 3) * ROW + (c & 7) * E16) = rb[i];
-    }
+    for (int i = 0; i < BC; ++i) *reinterpret_cast<u32x4*>(st + lb[i]) = rb[i];
   };
 
   f32x16 acc[FM][FN];
@@ -117,15 +178,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restric
     for (int j = 0; j < FN; ++j) acc[i][j] = zero16();
 
   const int nk = (K + BK - 1) / BK;
-  load_tile(0);
-  store_tile(0);
+  const int nfull = K / BK;
+  if (nfull > 0) load_full(0); else load_tail(0);
+  store_stage(0);
   __syncthreads();
   const int lrow = lane & 31, lhalf = lane >> 5;
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) load_tile((kt + 1) * BK);
-    const T* sa = smem + buf * (BM + BN) * ROW + (wm * TM + lrow) * ROW + lhalf * E16;
-    const T* sb = smem + buf * (BM + BN) * ROW + BM * ROW + (wn * TN + lrow) * ROW + lhalf * E16;
+    if (kt + 1 < nfull) load_full((kt + 1) * BK);
+    else if (kt + 1 < nk) load_tail((kt + 1) * BK);
+    const T* sa = smem + buf * STAGE + (wm * TM + lrow) * ROW + lhalf * E16;
+    const T* sb = smem + buf * STAGE + BM * ROW + (wn * TN + lrow) * ROW + lhalf * E16;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       u32x4 af[FM], bfr[FN];
@@ -136,32 +199,64 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restric
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) mfma_chunk(af[i], bfr[j], acc[i][j], T());
+        for (int j = 0; j < FN; ++j) mfma_chunk(bfr[j], af[i], acc[i][j], T());  // C^T = W A^T
     }
-    if (kt + 1 < nk) store_tile(buf ^ 1);
+    if (kt + 1 < nk) store_stage(buf ^ 1);
     __syncthreads();
   }
 
+  // acc[i][j]: lane holds row m = m0 + wm*TM + i*32 + lrow and columns
+  // n = n0 + wn*TN + j*32 + g*8 + lhalf*4 + (0..3) in elements 4g..4g+3.
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < FM; ++i) {
+    const int m = m0 + wm * TM + i * 32 + lrow;
+    if (m >= M) continue;
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * TM + i * 32 + (r >> 2) * 8 + lhalf * 4 + (r & 3);
-        const int n = n0 + wn * TN + j * 32 + lrow;
-        if (m < M && n < N) epi(m, n, acc[i][j][r]);
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * TN + j * 32 + g * 8 + lhalf * 4;
+        if (n < N)
+          epi(m, n, make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]));
       }
+  }
 }
 
+template <typename T, int BM, int BN, int WM, int WN, class Epi>
+hipError_t launch_cfg(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const Epi& epi,
+                      hipStream_t s) {
+  const int tm = (int)ceil_div(M, BM), tn = (int)ceil_div(N, BN);
+  hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, WM, WN, Epi>), dim3((unsigned)(tm * tn)), dim3(WM * WN * 64), 0,
+                     s, A, lda, W, ldw, M, N, K, tm, tn, epi);
+  return hipGetLastError();
+}
+
+#ifndef WAN_GEMM_FORCE
+#define WAN_GEMM_FORCE 0
+#endif
+
+// Tile choice for bf16 products with many rows: 256 x 256 with 8 waves (64 x 128 each) when N is a
+// multiple of 256, 256 x 128 with 8 waves otherwise; 128 x 128 with 4 waves for small M or fp32.
 template <typename T, class Epi>
 hipError_t run_gemm(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const Epi& epi,
                     hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  constexpr int BM = 128, BN = 128;
-  dim3 grid((unsigned)ceil_div(N, BN), (unsigned)ceil_div(M, BM));
-  hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, 2, 2, Epi>), grid, dim3(256), 0, s, A, lda, W, ldw, M, N, K, epi);
-  return hipGetLastError();
+  if (N % 4 != 0 || K % dtype_traits<T>::per16 != 0) return hipErrorInvalidValue;
+  int cfg = 0;
+  if constexpr (sizeof(T) == 2) {
+    if (M >= 4096 && N % 256 == 0 && N >= 1024) cfg = 4;
+    else if (M >= 4096 && N % 128 == 0 && N >= 1024) cfg = 5;
+  }
+  if (WAN_GEMM_FORCE && sizeof(T) == 2) cfg = WAN_GEMM_FORCE - 1;
+  if constexpr (sizeof(T) == 2) {
+    if (cfg == 1) return launch_cfg<T, 256, 128, 2, 2>(A, lda, W, ldw, M, N, K, epi, s);
+    if (cfg == 2) return launch_cfg<T, 256, 256, 2, 2>(A, lda, W, ldw, M, N, K, epi, s);
+    if (cfg == 3) return launch_cfg<T, 256, 256, 2, 4>(A, lda, W, ldw, M, N, K, epi, s);
+    if (cfg == 4) return launch_cfg<T, 256, 256, 4, 2>(A, lda, W, ldw, M, N, K, epi, s);
+    if (cfg == 5) return launch_cfg<T, 256, 128, 4, 2>(A, lda, W, ldw, M, N, K, epi, s);
+    if (cfg == 6) return launch_cfg<T, 128, 256, 2, 4>(A, lda, W, ldw, M, N, K, epi, s);
+  }
+  return launch_cfg<T, 128, 128, 2, 2>(A, lda, W, ldw, M, N, K, epi, s);
 }
 
 // ---------------------------------------------------------------------------

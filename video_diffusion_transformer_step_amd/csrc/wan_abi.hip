@@ -36,6 +36,37 @@ int fail(int code, const char* fmt, ...) {
 
 inline hipStream_t hs(wan_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Kernel-timing hook (wan_profile_begin / wan_profile_end): caller-owned events recorded on the
+// launch stream around the selected kernels of wan_dit_block_fwd.  Process-wide, not thread-safe.
+struct Profile {
+  hipEvent_t* starts = nullptr;
+  hipEvent_t* stops = nullptr;
+  int32_t* tags = nullptr;
+  int32_t cap = 0, n = 0;
+  uint32_t mask = 0;
+};
+Profile g_prof;
+
+struct ProfScope {
+  int slot = -1;
+  hipStream_t st;
+  ProfScope(int id, hipStream_t s) : st(s) {
+    if (g_prof.cap > 0 && (g_prof.mask >> id & 1u) && g_prof.n < g_prof.cap) {
+      slot = g_prof.n++;
+      g_prof.tags[slot] = id;
+      (void)hipEventRecord(g_prof.starts[slot], st);
+    }
+  }
+  ~ProfScope() {
+    if (slot >= 0) (void)hipEventRecord(g_prof.stops[slot], st);
+  }
+};
+#define PROF_TRY(id, expr)            \
+  do {                                \
+    ProfScope prof_(id, st);          \
+    HIP_TRY(expr);                    \
+  } while (0)
+
 int need_ptr(const void* p, const char* name) {
   if (!p) return fail(WAN_EINVAL, "%s is NULL", name);
   if (reinterpret_cast<uintptr_t>(p) & 15u) return fail(WAN_EINVAL, "%s is not 16-byte aligned", name);
@@ -121,29 +152,29 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
   const int Spad = (int)pad64(S);
   const float scale = 1.f / sqrtf((float)hd);
   // self-attention branch
-  HIP_TRY(launch_ln_mod<T>(x, BS, dim, S, 0, e0, W.mod_bias, 0, 1, c.ln_eps, w.u, st));
-  HIP_TRY((gemm_store<T, T>(w.u, dim, (const T*)W.wqkv, dim, BS, 3 * dim, dim, W.bqkv, ACT_NONE, w.qkv, 3 * dim, st)));
-  HIP_TRY(launch_qk_norm_rope<T>(w.qkv, w.qkv + dim, 3 * dim, w.qkv, w.qkv + dim, 3 * dim, B, g.T, g.Hp, g.Wp, H, hd,
+  PROF_TRY(WAN_K_LN1, launch_ln_mod<T>(x, BS, dim, S, 0, e0, W.mod_bias, 0, 1, c.ln_eps, w.u, st));
+  PROF_TRY(WAN_K_QKV_GEMM, (gemm_store<T, T>(w.u, dim, (const T*)W.wqkv, dim, BS, 3 * dim, dim, W.bqkv, ACT_NONE, w.qkv, 3 * dim, st)));
+  PROF_TRY(WAN_K_QK_NORM_ROPE, launch_qk_norm_rope<T>(w.qkv, w.qkv + dim, 3 * dim, w.qkv, w.qkv + dim, 3 * dim, B, g.T, g.Hp, g.Wp, H, hd,
                                  W.gq, W.gk, 1, c.rms_eps, c.rope_theta, st));
-  HIP_TRY(launch_transpose_heads<T>(w.qkv, 3 * dim, 2 * dim, B, S, H, hd, Spad, w.vt, st));
+  PROF_TRY(WAN_K_V_TRANSPOSE, launch_transpose_heads<T>(w.qkv, 3 * dim, 2 * dim, B, S, H, hd, Spad, w.vt, st));
   KVStream self{w.qkv + dim, (int64_t)S * 3 * dim, 3 * dim, w.vt, S, Spad};
-  HIP_TRY(launch_attention<T>(w.qkv, (int64_t)S * 3 * dim, 3 * dim, self, self, 1, B, S, H, hd, scale, w.o,
+  PROF_TRY(WAN_K_SELF_ATTN, launch_attention<T>(w.qkv, (int64_t)S * 3 * dim, 3 * dim, self, self, 1, B, S, H, hd, scale, w.o,
                               (int64_t)S * dim, dim, st));
-  HIP_TRY(gemm_residual<T>(w.o, dim, (const T*)W.wo, dim, BS, dim, dim, W.bo, e0, W.mod_bias, 2, S, x, dim, st));
+  PROF_TRY(WAN_K_O_GEMM, gemm_residual<T>(w.o, dim, (const T*)W.wo, dim, BS, dim, dim, W.bo, e0, W.mod_bias, 2, S, x, dim, st));
   // cross-attention branch (no adaLN, no RoPE)
-  HIP_TRY(launch_ln_mod<T>(x, BS, dim, S, 1, W.ln3_w, W.ln3_b, 0, 0, c.ln_eps, w.u, st));
+  PROF_TRY(WAN_K_LN3, launch_ln_mod<T>(x, BS, dim, S, 1, W.ln3_w, W.ln3_b, 0, 0, c.ln_eps, w.u, st));
   T* qc = w.qkv;  // reuse: [BS, dim]
-  HIP_TRY((gemm_store<T, T>(w.u, dim, (const T*)W.wcq, dim, BS, dim, dim, W.bcq, ACT_NONE, qc, dim, st)));
+  PROF_TRY(WAN_K_CROSS_Q_GEMM, (gemm_store<T, T>(w.u, dim, (const T*)W.wcq, dim, BS, dim, dim, W.bcq, ACT_NONE, qc, dim, st)));
   const int Lt = c.text_len, Li = c.img_len;
   KVStream st_txt{kv.k_txt, (int64_t)Lt * dim, dim, kv.vt_txt, Lt, (int)pad64(Lt)};
   KVStream st_img{kv.k_img, (int64_t)Li * dim, dim, kv.vt_img, Li, (int)pad64(Li > 0 ? Li : 1)};
-  HIP_TRY(launch_attention<T>(qc, (int64_t)S * dim, dim, st_txt, st_img, Li > 0 ? 2 : 1, B, S, H, hd, scale, w.o,
+  PROF_TRY(WAN_K_CROSS_ATTN, launch_attention<T>(qc, (int64_t)S * dim, dim, st_txt, st_img, Li > 0 ? 2 : 1, B, S, H, hd, scale, w.o,
                               (int64_t)S * dim, dim, st));
-  HIP_TRY(gemm_residual<T>(w.o, dim, (const T*)W.wco, dim, BS, dim, dim, W.bco, nullptr, nullptr, 0, S, x, dim, st));
+  PROF_TRY(WAN_K_CROSS_O_GEMM, gemm_residual<T>(w.o, dim, (const T*)W.wco, dim, BS, dim, dim, W.bco, nullptr, nullptr, 0, S, x, dim, st));
   // FFN branch
-  HIP_TRY(launch_ln_mod<T>(x, BS, dim, S, 0, e0, W.mod_bias, 3, 4, c.ln_eps, w.u, st));
-  HIP_TRY((gemm_store<T, T>(w.u, dim, (const T*)W.w1, dim, BS, c.ffn_dim, dim, W.b1, ACT_GELU, w.h, c.ffn_dim, st)));
-  HIP_TRY(gemm_residual<T>(w.h, c.ffn_dim, (const T*)W.w2, c.ffn_dim, BS, dim, c.ffn_dim, W.b2, e0, W.mod_bias, 5, S,
+  PROF_TRY(WAN_K_LN2, launch_ln_mod<T>(x, BS, dim, S, 0, e0, W.mod_bias, 3, 4, c.ln_eps, w.u, st));
+  PROF_TRY(WAN_K_FFN1_GEMM, (gemm_store<T, T>(w.u, dim, (const T*)W.w1, dim, BS, c.ffn_dim, dim, W.b1, ACT_GELU, w.h, c.ffn_dim, st)));
+  PROF_TRY(WAN_K_FFN2_GEMM, gemm_residual<T>(w.h, c.ffn_dim, (const T*)W.w2, c.ffn_dim, BS, dim, c.ffn_dim, W.b2, e0, W.mod_bias, 5, S,
                            x, dim, st));
   return WAN_OK;
 }
@@ -503,4 +534,24 @@ int wan_attention_fwd(int32_t dtype, const void* q, const void* k, const void* v
                              (bf16*)o, ws, hs(stream));
   return attention_t<float>((const float*)q, (const float*)k, (const float*)v, grid, B, heads, head_dim, rope_theta,
                             (float*)o, ws, hs(stream));
+}
+
+int wan_profile_begin(void* const* start_events, void* const* stop_events, int32_t* tags, int32_t capacity,
+                      uint32_t kernel_mask) {
+  if (capacity < 0) return fail(WAN_EINVAL, "capacity must be >= 0");
+  if (capacity > 0 && (!start_events || !stop_events || !tags))
+    return fail(WAN_EINVAL, "event / tag arrays are NULL");
+  g_prof.starts = reinterpret_cast<hipEvent_t*>(const_cast<void**>(start_events));
+  g_prof.stops = reinterpret_cast<hipEvent_t*>(const_cast<void**>(stop_events));
+  g_prof.tags = tags;
+  g_prof.cap = capacity;
+  g_prof.n = 0;
+  g_prof.mask = kernel_mask;
+  return WAN_OK;
+}
+
+int32_t wan_profile_end(void) {
+  const int32_t n = g_prof.n;
+  g_prof = Profile{};
+  return n;
 }

@@ -23,7 +23,7 @@ def _dt(dtype: str):
 
 def to_dev(a, dtype=torch.float32, device="cuda"):
     """Upload a host array (values already representable in `dtype`)."""
-    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    t = torch.from_numpy(np.array(a, dtype=np.float32, copy=True))
     return t.to(device=device).to(dtype).contiguous()
 
 
