@@ -95,8 +95,10 @@ typedef struct {
 
 /* Cross-attention keys/values of one block, computed once per generation by wan_cross_kv_fwd
  * (context and weights do not change across sampling steps, [I2V] §7).
- *   k_txt  [B, text_len, dim] dtype;   vt_txt [B, heads, head_dim, Lpad_txt] dtype (V transposed
- *   per head, zero for keys >= text_len);  Lpad = text_len rounded up to a multiple of 64.
+ *   k_txt  [B, text_len, dim] dtype;   vt_txt [B, heads, head_dim, Lpad_txt] dtype: V transposed
+ *   per head, zero for keys >= text_len, Lpad = text_len rounded up to a multiple of 64.  In bf16
+ *   the key axis is stored permuted within each 16-key group (position p holds key p with bits 2
+ *   and 3 swapped: keys 0-3, 8-11, 4-7, 12-15), the order the attention kernel's MFMA operands use.
  *   k_img / vt_img likewise with img_len (NULL when img_len == 0). */
 typedef struct {
   const void *k_txt, *vt_txt, *k_img, *vt_img;

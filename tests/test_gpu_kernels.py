@@ -108,6 +108,12 @@ def test_context_embed_and_cross_kv(dtype):
     Lp = 64
     vt_got = kc.bufs[1].view(td).float().cpu().numpy().reshape(c.heads, c.head_dim, Lp)
     assert rel_l2(k_got, k_ref) <= TOL[dtype]
+    if dtype == "bf16":  # bf16 V^T stores keys permuted within 16-key groups (bits 2 and 3 swapped)
+        pos = np.arange(Lp)
+        key = (pos & ~12) | ((pos & 4) << 1) | ((pos & 8) >> 1)
+        unperm = np.empty_like(vt_got)
+        unperm[:, :, key] = vt_got
+        vt_got = unperm
     v_from_t = vt_got[:, :, :c.text_len].transpose(2, 0, 1).reshape(c.text_len, c.dim)
     assert rel_l2(v_from_t, v_ref) <= TOL[dtype]
     assert np.all(vt_got[:, :, c.text_len:] == 0.0)

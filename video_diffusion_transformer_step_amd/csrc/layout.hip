@@ -112,8 +112,11 @@ __global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ 
     out[i] = from_f32<T>(in[i]);
 }
 
-// V^T[b, h, d, j] = V[b, j, h*hd + d] (+col0) for j < S, 0 for S <= j < Spad.  One workgroup per
-// (64-token tile, head, batch row); LDS tile [64][hd + 1] elements.
+// V^T[b, h, d, pos] = V[b, key(pos), h*hd + d] (+col0) for key < S, 0 for S <= key < Spad.
+// In bf16 the keys are permuted within each 16-key group, key(pos) = pos with bits 2 and 3 swapped
+// ([0-3, 8-11, 4-7, 12-15]), so that the 8 keys one attention MFMA lane-half consumes are one
+// contiguous 16-byte chunk; fp32 keeps the natural order.  One workgroup per (64-token tile, head,
+// batch row); LDS tile [64][hd + 1] elements.
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_heads_kernel(const T* __restrict__ v, int64_t ld, int64_t col0,
                                                                int S, int H, int hd, int Spad, T* __restrict__ vt) {
@@ -127,8 +130,9 @@ __global__ __launch_bounds__(256) void transpose_heads_kernel(const T* __restric
   }
   __syncthreads();
   for (int e = threadIdx.x; e < 64 * hd; e += 256) {
-    const int d = e / 64, r = e % 64;
-    const int j = j0 + r;
+    const int d = e / 64, pos = e % 64;
+    const int r = (sizeof(T) == 2) ? ((pos & ~12) | ((pos & 4) << 1) | ((pos & 8) >> 1)) : pos;
+    const int j = j0 + pos;
     if (j < Spad) vt[(((int64_t)b * H + h) * hd + d) * Spad + j] = tile[r * P + d];
   }
 }

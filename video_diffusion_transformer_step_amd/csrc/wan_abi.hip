@@ -159,7 +159,7 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
   PROF_TRY(WAN_K_V_TRANSPOSE, launch_transpose_heads<T>(w.qkv, 3 * dim, 2 * dim, B, S, H, hd, Spad, w.vt, st));
   KVStream self{w.qkv + dim, (int64_t)S * 3 * dim, 3 * dim, w.vt, S, Spad};
   PROF_TRY(WAN_K_SELF_ATTN, launch_attention<T>(w.qkv, (int64_t)S * 3 * dim, 3 * dim, self, self, 1, B, S, H, hd, scale, w.o,
-                              (int64_t)S * dim, dim, st));
+                              (int64_t)S * dim, dim, 0, st));
   PROF_TRY(WAN_K_O_GEMM, gemm_residual<T>(w.o, dim, (const T*)W.wo, dim, BS, dim, dim, W.bo, e0, W.mod_bias, 2, S, x, dim, st));
   // cross-attention branch (no adaLN, no RoPE)
   PROF_TRY(WAN_K_LN3, launch_ln_mod<T>(x, BS, dim, S, 1, W.ln3_w, W.ln3_b, 0, 0, c.ln_eps, w.u, st));
@@ -169,7 +169,7 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
   KVStream st_txt{kv.k_txt, (int64_t)Lt * dim, dim, kv.vt_txt, Lt, (int)pad64(Lt)};
   KVStream st_img{kv.k_img, (int64_t)Li * dim, dim, kv.vt_img, Li, (int)pad64(Li > 0 ? Li : 1)};
   PROF_TRY(WAN_K_CROSS_ATTN, launch_attention<T>(qc, (int64_t)S * dim, dim, st_txt, st_img, Li > 0 ? 2 : 1, B, S, H, hd, scale, w.o,
-                              (int64_t)S * dim, dim, st));
+                              (int64_t)S * dim, dim, 1, st));
   PROF_TRY(WAN_K_CROSS_O_GEMM, gemm_residual<T>(w.o, dim, (const T*)W.wco, dim, BS, dim, dim, W.bco, nullptr, nullptr, 0, S, x, dim, st));
   // FFN branch
   PROF_TRY(WAN_K_LN2, launch_ln_mod<T>(x, BS, dim, S, 0, e0, W.mod_bias, 3, 4, c.ln_eps, w.u, st));
@@ -508,7 +508,7 @@ static int attention_t(const T* q, const T* k, const T* v, const wan_grid& g, in
   HIP_TRY(launch_transpose_heads<T>(v, dim, 0, B, S, H, hd, Spad, vt, st));
   KVStream s0{kr, (int64_t)S * dim, dim, vt, S, Spad};
   HIP_TRY(launch_attention<T>(qr, (int64_t)S * dim, dim, s0, s0, 1, B, S, H, hd, 1.f / sqrtf((float)hd), o,
-                              (int64_t)S * dim, dim, st));
+                              (int64_t)S * dim, dim, 0, st));
   return WAN_OK;
 }
 

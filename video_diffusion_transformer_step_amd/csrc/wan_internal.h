@@ -73,6 +73,7 @@ struct KVStream {
 };
 template <typename T>
 hipError_t launch_attention(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0, KVStream s1, int nstreams, int B,
-                            int S, int H, int hd, float scale, T* o, int64_t o_bs, int64_t o_ss, hipStream_t s);
+                            int S, int H, int hd, float scale, T* o, int64_t o_bs, int64_t o_ss, int kind,
+                            hipStream_t s);  // kind: 0 self-attention, 1 cross-attention (separate kernel symbols)
 
 }  // namespace wan
