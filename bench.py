@@ -135,10 +135,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="C1", help="workload preset (C1 = 1.3B-shaped 32760-token step)")
+    ap.add_argument("--config", default="t2v-1.3b", help="workload preset (t2v-1.3b = 1.3B-shaped 32760-token step)")
     ap.add_argument("--layers", type=int, default=None, help="blocks per step (default: the preset's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after the timed region, run one plain device copy of this many bytes (a known-size "
+                         "reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -239,6 +242,16 @@ def main():
             breakdown[k_] = e
         breakdown["block_sum_ms"] = round(sum(e["ms"] for e in breakdown.values()), 3)
         log(f"breakdown: {json.dumps(breakdown)}")
+
+    if args.copy_bytes > 0:
+        n = args.copy_bytes // 4
+        src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {n * 4} bytes (counter calibration)")
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -72,16 +72,16 @@ def _check(c, got, ref, x, rows=None, tol=None):
 
 
 SMALL = [
-    ("C0", {}),                                                   # tiny I2V block, fp32, text only
-    ("C0", {"img_len": 9, "img_dim": 32}),                        # + image stream (dual cross-attention)
-    ("C0", {"dtype": "bf16"}),
-    ("C0", {"T": 3, "H": 12, "W": 20, "B": 2, "img_len": 7, "img_dim": 32}),  # 180 tokens, 2 rows
-    ("C0", {"dtype": "bf16", "T": 3, "H": 12, "W": 20, "B": 2, "dim": 256, "heads": 2, "head_dim": 128,
+    ("tiny", {}),                                                   # tiny I2V block, fp32, text only
+    ("tiny", {"img_len": 9, "img_dim": 32}),                        # + image stream (dual cross-attention)
+    ("tiny", {"dtype": "bf16"}),
+    ("tiny", {"T": 3, "H": 12, "W": 20, "B": 2, "img_len": 7, "img_dim": 32}),  # 180 tokens, 2 rows
+    ("tiny", {"dtype": "bf16", "T": 3, "H": 12, "W": 20, "B": 2, "dim": 256, "heads": 2, "head_dim": 128,
             "ffn_dim": 640, "text_len": 70, "img_len": 9, "img_dim": 32}),  # hd 128, ragged tiles
 ]
 
 
-@pytest.mark.parametrize("name,over", SMALL, ids=["C0", "C0-dual", "C0-bf16", "C0-180tok-B2", "bf16-hd128-ragged"])
+@pytest.mark.parametrize("name,over", SMALL, ids=["tiny", "tiny-dual", "tiny-bf16", "tiny-180tok-B2", "bf16-hd128-ragged"])
 def test_block_small_full(name, over):
     require_gpu()
     c = wi.get_config(name).replace(**over)
@@ -96,7 +96,7 @@ def test_block_deterministic_and_adaln_zero():
     """Two runs are bitwise equal; with gate1 = gate2 = 0 and a zero cross-attention output
     projection the block leaves x unchanged bit for bit."""
     require_gpu()
-    c = wi.get_config("C0").replace(dtype="bf16", T=3, H=12, W=20, img_len=5, img_dim=32)
+    c = wi.get_config("tiny").replace(dtype="bf16", T=3, H=12, W=20, img_len=5, img_dim=32)
     case("block determinism + adaLN-Zero")
     x, e0, t_emb, i_emb, bw = _inputs(c)
     a, b = _gpu_block(c, x, e0, t_emb, i_emb, bw, repeat=2)
@@ -115,14 +115,14 @@ def test_block_deterministic_and_adaln_zero():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["C1", pytest.param("C2", marks=pytest.mark.slow)])
+@pytest.mark.parametrize("name", ["t2v-1.3b", "ti2v-5b", pytest.param("i2v-14b", marks=pytest.mark.slow)])
 def test_block_full_size_sampled_rows(name):
     """Workload-size block (32760 tokens), checked on sampled query rows: the oracle computes
     K/V for every token and the rest only for those rows."""
     require_gpu()
     c = wi.get_config(name)
     case(f"block full size {c.name}")
-    rows = wi.sample_rows(c, 48 if name == "C2" else 96, seed=1)
+    rows = wi.sample_rows(c, {"t2v-1.3b": 96, "ti2v-5b": 48, "i2v-14b": 48}[name], seed=1)
     x, e0, t_emb, i_emb, bw = _inputs(c, seed=1)
     got, = _gpu_block(c, x, e0, t_emb, i_emb, bw)
     ref = _oracle_block(c, x, e0, t_emb, i_emb, bw, rows=rows)

@@ -48,7 +48,7 @@ def test_attention_rope_small(dtype, hd, grid, B, H):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_patch_embed(dtype):
     require_gpu()
-    c = wi.get_config("C0").replace(dtype=dtype)
+    c = wi.get_config("tiny").replace(dtype=dtype)
     case(f"patch_embed {dtype}")
     mw = wi.make_model_weights(c, seed=1)
     x_t, z = wi.make_latents(c, seed=1)
@@ -63,7 +63,7 @@ def test_patch_embed(dtype):
     assert rel_l2(host(out), ref) <= TOL[dtype]
 
 
-@pytest.mark.parametrize("cfg_name,dtype", [("C0", "f32"), ("C0", "bf16"), ("C1", "bf16"), ("C4", "bf16")])
+@pytest.mark.parametrize("cfg_name,dtype", [("tiny", "f32"), ("tiny", "bf16"), ("t2v-1.3b", "bf16"), ("ti2v-5b", "bf16")])
 def test_time_embed(cfg_name, dtype):
     require_gpu()
     c = wi.get_config(cfg_name).replace(dtype=dtype)
@@ -86,7 +86,7 @@ def test_time_embed(cfg_name, dtype):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_context_embed_and_cross_kv(dtype):
     require_gpu()
-    c = wi.get_config("C0").replace(dtype=dtype, img_len=9, img_dim=32)
+    c = wi.get_config("tiny").replace(dtype=dtype, img_len=9, img_dim=32)
     case(f"context_embed + cross_kv {dtype}")
     mw = wi.make_model_weights(c, seed=3)
     bw = wi.make_block_weights(c, 0, seed=3)
@@ -126,7 +126,7 @@ def test_context_embed_and_cross_kv(dtype):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_head(dtype):
     require_gpu()
-    c = wi.get_config("C0").replace(dtype=dtype)
+    c = wi.get_config("tiny").replace(dtype=dtype)
     case(f"head {dtype}")
     mw = wi.make_model_weights(c, seed=4)
     model = R.DeviceModel(mw, dtype)
@@ -140,3 +140,26 @@ def test_head(dtype):
     L.head_fwd(cfg, model.hw, c.out_channels, B, c.S, dev(x), dev(e), out, ws)
     ref = oracle.head_fwd(x, e, mw)
     assert rel_l2(host(out), ref) <= TOL[dtype]
+
+
+@pytest.mark.timeout(900)
+def test_attention_720p_stress_sampled_rows():
+    """75600-token self-attention with 3D RoPE (40 heads x 128, q/k/v ~N(0,1) bf16) checked on sampled
+    query rows: the oracle rotates every key and evaluates those rows' softmax over all keys."""
+    require_gpu()
+    c = wi.get_config("attn-720p")
+    case("attention 720p stress (75600 tokens)")
+    q, k, v = wi.make_attention_qkv(c, seed=3)
+    td = torch.bfloat16
+    qd, kd, vd = dev(q, td), dev(k, td), dev(v, td)
+    o = torch.empty_like(qd)
+    ws = torch.empty(L.attention_ws_bytes(L.WAN_BF16, c.grid, c.B, c.heads, c.head_dim), dtype=torch.uint8,
+                     device="cuda")
+    L.attention_fwd(qd, kd, vd, c.grid, o, ws)
+    rows = wi.sample_rows(c, 24, seed=3)
+    got = o[0, torch.from_numpy(rows).cuda()].float().cpu().numpy()
+    del qd, kd, vd, o, ws
+    ref = oracle.self_attention_rope_only(q[0], k[0], v[0], c.grid, rows=rows)
+    err = rel_l2(got, ref)
+    print(f"[attn-720p] sampled-row rel-L2 {err:.3e}")
+    assert err <= TOL["bf16"]

@@ -78,8 +78,8 @@ def _check(c, x_t, gpu_traj, traj):
 def test_step_tiny_i2v(dtype):
     """Tiny image-to-video block config: one block, one Euler step (t = 0.5, dt = -0.1)."""
     require_gpu()
-    c = wi.get_config("C0").replace(dtype=dtype)
-    case(f"step C0 {dtype}")
+    c = wi.get_config("tiny").replace(dtype=dtype)
+    case(f"step tiny {dtype}")
     x_t, gt, ot = _run(c, layers=1, steps=1, t0=c.t, dt=c.dt)
     _check(c, x_t, gt, ot)
 
@@ -89,7 +89,7 @@ def test_step_cfg_two_rows(dtype):
     """Classifier-free guidance: two rows (conditional / unconditional text), shared latent,
     dual-stream cross-attention, 2 blocks, 3 Euler steps from t = 1."""
     require_gpu()
-    c = wi.get_config("C0").replace(dtype=dtype, B=2, img_len=9, img_dim=32, T=3, H=8, W=12, guidance=5.0)
+    c = wi.get_config("tiny").replace(dtype=dtype, B=2, img_len=9, img_dim=32, T=3, H=8, W=12, guidance=5.0)
     case(f"step CFG {dtype}")
     x_t, gt, ot = _run(c, layers=2, steps=3, t0=1.0)
     _check(c, x_t, gt, ot)
@@ -100,7 +100,7 @@ def test_step_ti2v_shaped_reduced_chain():
     512 text tokens, CFG batch 2, 4 Euler steps from t = 1) on a 32-token latent [48, 2, 8, 8]
     with 3 blocks instead of 30, so the oracle finishes in seconds."""
     require_gpu()
-    c = wi.get_config("C4").replace(T=2, H=8, W=8)
+    c = wi.get_config("ti2v-5b").replace(T=2, H=8, W=8)
     case("step TI2V-shaped reduced chain")
     x_t, gt, ot = _run(c, layers=3, steps=4, t0=1.0)
     _check(c, x_t, gt, ot)

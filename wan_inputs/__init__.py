@@ -5,7 +5,7 @@ benchmark.  It draws random numbers and rounds them to bf16-representable values
 it holds none of the method's arithmetic (no norm, no projection, no attention).
 
 Every tensor is drawn from its own NumPy PCG64 stream keyed by
-``SeedSequence([seed, config_id, tensor_id, block])`` so any one tensor can be
+``SeedSequence([seed, stream_id, tensor_id, block])`` so any one tensor can be
 regenerated on its own.  Distributions follow the workload description:
 latents, contexts and self-attention stress inputs ~N(0,1); weight matrices and
 biases ~N(0, 0.02); norm gains 1 + N(0, 0.02).
@@ -27,7 +27,7 @@ __all__ = ["WanConfig", "CONFIGS", "get_config", "rng", "bf16_round", "normal",
 class WanConfig:
     """Shapes of one workload.  Latent dims are (C, T, H, W); tokens S = T*(H/2)*(W/2)."""
     name: str
-    config_id: int
+    stream_id: int
     dtype: str            # "f32" or "bf16": the arithmetic type of GEMM / attention operands
     B: int                # batch rows seen by the DiT (2 with classifier-free guidance)
     latent_channels: int  # C of x_t (16 for Wan2.1, 48 for the TI2V-5B-shaped case)
@@ -73,19 +73,19 @@ class WanConfig:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads.  C1's layer count (32) is the 1.3B figure from the
-# "图解 Wan2.1 I2V" page's summary table (§8); C2's 40 is the 14B figure there.
+# The five workloads.  The 1.3B layer count (32) comes from the
+# "图解 Wan2.1 I2V" page's summary table (§8); the 14B one (40) is there too.
 CONFIGS = {
-    "C0": WanConfig("tiny-i2v-block-f32", 0, "f32", 1, 16, True, 2, 8, 8,
-                    128, 2, 64, 512, 16, 64, 0, 0, 1, t=0.5, dt=-0.1),
-    "C1": WanConfig("wan2.1-1.3b-t2v-block-bf16", 1, "bf16", 1, 16, False, 21, 60, 104,
-                    1536, 12, 128, 8960, 512, 4096, 0, 0, 32, t=0.5, dt=-0.1),
-    "C2": WanConfig("wan-14b-i2v-block-bf16", 2, "bf16", 2, 16, True, 21, 60, 104,
-                    5120, 40, 128, 13824, 512, 4096, 257, 1280, 40, t=0.5, dt=-0.1),
-    "C3": WanConfig("720p-self-attention-bf16", 3, "bf16", 1, 16, False, 21, 90, 160,
-                    5120, 40, 128, 0, 0, 0, 0, 0, 0),
-    "C4": WanConfig("ti2v-5b-sampling-bf16", 4, "bf16", 2, 48, True, 31, 44, 80,
-                    3072, 24, 128, 14336, 512, 4096, 0, 0, 30, t=1.0, dt=-0.25,
+    "tiny": WanConfig("tiny-i2v-block-f32", 0, "f32", 1, 16, True, 2, 8, 8,
+                   128, 2, 64, 512, 16, 64, 0, 0, 1, t=0.5, dt=-0.1),
+    "t2v-1.3b": WanConfig("wan2.1-1.3b-t2v-block-bf16", 1, "bf16", 1, 16, False, 21, 60, 104,
+                   1536, 12, 128, 8960, 512, 4096, 0, 0, 32, t=0.5, dt=-0.1),
+    "i2v-14b": WanConfig("wan-14b-i2v-block-bf16", 2, "bf16", 2, 16, True, 21, 60, 104,
+                   5120, 40, 128, 13824, 512, 4096, 257, 1280, 40, t=0.5, dt=-0.1),
+    "attn-720p": WanConfig("720p-self-attention-bf16", 3, "bf16", 1, 16, False, 21, 90, 160,
+                   5120, 40, 128, 0, 0, 0, 0, 0, 0),
+    "ti2v-5b": WanConfig("ti2v-5b-sampling-bf16", 4, "bf16", 2, 48, True, 31, 44, 80,
+                   3072, 24, 128, 14336, 512, 4096, 0, 0, 30, t=1.0, dt=-0.25,
                     guidance=5.0, steps=4),
 }
 
@@ -114,8 +114,8 @@ BLOCK_MATRICES = ("wq", "wk", "wv", "wo", "wcq", "wck", "wcv", "wki", "wvi", "wc
 MODEL_MATRICES = ("w_pe", "wt1", "wt2", "wtp", "wtx1", "wtx2", "wim1", "wim2", "wh")
 
 
-def rng(seed: int, config_id: int, tensor: str, block: int = 0) -> np.random.Generator:
-    ss = np.random.SeedSequence([seed, config_id, TENSOR_IDS[tensor], block])
+def rng(seed: int, stream_id: int, tensor: str, block: int = 0) -> np.random.Generator:
+    ss = np.random.SeedSequence([seed, stream_id, TENSOR_IDS[tensor], block])
     return np.random.Generator(np.random.PCG64(ss))
 
 
@@ -130,7 +130,7 @@ def normal(seed, cfg: WanConfig, tensor: str, shape, std=1.0, mean=0.0, block=0,
            quantize=None) -> np.ndarray:
     """float32 N(mean, std^2) draw; bf16-representable when the config is bf16 and
     ``quantize`` is not False (``quantize=True`` forces it)."""
-    g = rng(seed, cfg.config_id, tensor, block)
+    g = rng(seed, cfg.stream_id, tensor, block)
     a = g.standard_normal(size=shape, dtype=np.float32)
     if std != 1.0:
         a *= np.float32(std)
@@ -220,7 +220,7 @@ def sample_rows(cfg: WanConfig, R: int, seed: int = 0) -> np.ndarray:
     S = cfg.S
     hw = (cfg.H // 2) * (cfg.W // 2)
     fixed = {0, S - 1} | {f * hw for f in range(min(3, cfg.T))}
-    g = rng(seed, cfg.config_id, "rows")
+    g = rng(seed, cfg.stream_id, "rows")
     rest = g.choice(S, size=min(S, R + len(fixed)), replace=False)
     rows = list(sorted(fixed))
     for r in rest:
