@@ -6,20 +6,25 @@
 // I2V" §5.3-§5.5 and the Conv3d patch embedding of §5.1), so both operands are
 // contiguous along K (an "NT" product).
 //
-// Design (gfx950):
-//  * one workgroup owns a BM x BN output tile; K advances 128 bytes per step (64
-//    bf16 / 32 fp32), staged through double-buffered, row-padded LDS with
-//    register prefetch of the next step (one barrier per step);
-//  * each wave computes a (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks.  The
-//    MFMA is issued as C^T = W A^T (A-operand = weight rows), so a lane's
+// Two kernels share the tile order and the epilogues:
+//  * gemm_lds_kernel (bf16, K a multiple of 128; the block's large products):
+//    256 x 256 tiles, 8 waves of 64 x 128, K steps of 32 copied global -> LDS by
+//    asynchronous global_load_lds_dwordx4 into a ring of four stages, two steps
+//    ahead of their use (no staging registers);
+//  * gemm_nt_kernel (everything else): K steps of 128 bytes staged through
+//    double-buffered, row-padded LDS with register prefetch of the next step;
+//    loads are predicate-free (out-of-range rows clamped, a final partial K step
+//    zero-filled).
+// Common to both:
+//  * the MFMA is issued as C^T = W A^T (A-operand = weight rows), so a lane's
 //    accumulator holds 4 consecutive output columns of one row: the epilogue
 //    reads bias / gate / residual and writes results 4 columns (8 or 16 bytes)
 //    at a time;
-//  * loads are predicate-free: out-of-range rows are clamped to the last valid
-//    row (their results are never stored); only a final partial K step zero-fills;
 //  * the 1D grid is remapped so each XCD (blockIdx % 8) receives a contiguous run
 //    of tiles, grouped GROUP_M row-tiles at a time, so concurrent tiles share A
 //    rows and W columns in that XCD's L2;
+//  * k is accumulated in increasing order in every configuration, so all tile
+//    shapes give bitwise-identical results;
 //  * epilogues fuse the bias, GELU / SiLU, the output cast and the adaLN-gated
 //    residual update x += gate * (.) ("图解 Wan2.1 I2V" §5.2).
 #include "wan_internal.h"
@@ -37,20 +42,19 @@ __device__ __forceinline__ float apply_act(float v, int act) {
 }
 
 // Epilogues receive four consecutive columns n..n+3 of row m.
-template <typename OutT>
+template <typename OutT, int ACT>
 struct EpiStore {
   OutT* out;
   int64_t ldo;
   const float* bias;
-  int act;
   __device__ __forceinline__ void operator()(int m, int n, float4 v) const {
     if (bias) {
       const float4 b = *reinterpret_cast<const float4*>(bias + n);
       v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
     }
-    if (act != ACT_NONE) {
-      v.x = apply_act(v.x, act); v.y = apply_act(v.y, act);
-      v.z = apply_act(v.z, act); v.w = apply_act(v.w, act);
+    if constexpr (ACT != ACT_NONE) {
+      v.x = apply_act(v.x, ACT); v.y = apply_act(v.y, ACT);
+      v.z = apply_act(v.z, ACT); v.w = apply_act(v.w, ACT);
     }
     OutT* p = out + (int64_t)m * ldo + n;
     if constexpr (sizeof(OutT) == 2) {
@@ -222,6 +226,186 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restric
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 GEMM with asynchronous global -> LDS copies and a ring of ST LDS stages.
+//
+// One workgroup = WM x WN waves owning a BM x BN tile; a wave owns (BM/WM) x (BN/WN) (128 x 128:
+// 16 MFMA blocks, 256 accumulator registers, so one wave per SIMD).  Each K step of BK elements
+// is copied by global_load_lds_dwordx4 straight into LDS, ST - 1 steps ahead of its use, so the
+// copies need no staging registers and have ST - 1 steps of MFMA work to land.  Row r of a stage
+// holds BK * 2 bytes; its 16-byte chunk c sits at slot c ^ ((r / RPB) % CH) (RPB rows share one
+// 256-byte bank window), which makes the 16 rows one ds_read_b128 phase reads hit 16 distinct
+// bank groups.  The copy instead permutes which global chunk each lane fetches: lanes still write
+// LDS linearly.  Requires K % BK == 0 (callers fall back to gemm_nt_kernel otherwise).
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+// s_waitcnt with only the vector-memory counter constrained to <= n (gfx9 encoding).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int BM, int BN, int BK, int NW>
+struct LdsGemmCfg {
+  static constexpr int CH = BK / 8;        // 16-byte chunks per row
+  static constexpr int RPB = 16 / CH;      // rows per 256-byte bank window
+  static constexpr int ROWB = BK * 2;      // bytes per row
+  static constexpr int ABYTES = BM * ROWB, BBYTES = BN * ROWB;
+  static constexpr int LA = ABYTES / 1024 / NW, LB = BBYTES / 1024 / NW;  // copies per wave per stage
+  static_assert(CH >= 1 && CH <= 16 && LA * NW * 1024 == ABYTES && LB * NW * 1024 == BBYTES, "shape");
+  __device__ static __forceinline__ int off(int r, int c) { return r * ROWB + ((c ^ ((r / RPB) & (CH - 1))) << 4); }
+};
+
+template <int BM, int BN, int BK, int NW>
+struct LdsCopyPlan {
+  using C = LdsGemmCfg<BM, BN, BK, NW>;
+  const bf16* ga[C::LA];
+  const bf16* gb[C::LB];
+  __device__ __forceinline__ LdsCopyPlan(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int m0, int n0,
+                                         int M, int N) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < C::LA; ++i) {
+      const int p = (i * NW + wave) * 64 + lane, r = p / C::CH, s = p % C::CH;
+      const int c = s ^ ((r / C::RPB) & (C::CH - 1));
+      ga[i] = A + (int64_t)min(m0 + r, M - 1) * lda + c * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < C::LB; ++i) {
+      const int p = (i * NW + wave) * 64 + lane, r = p / C::CH, s = p % C::CH;
+      const int c = s ^ ((r / C::RPB) & (C::CH - 1));
+      gb[i] = W + (int64_t)min(n0 + r, N - 1) * ldw + c * 8;
+    }
+  }
+  __device__ __forceinline__ void issue(int k0, char* sa, char* sb) const {
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < C::LA; ++i)
+      __builtin_amdgcn_global_load_lds((glb_void*)(ga[i] + k0), (lds_void*)(sa + (i * NW + wave) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < C::LB; ++i)
+      __builtin_amdgcn_global_load_lds((glb_void*)(gb[i] + k0), (lds_void*)(sb + (i * NW + wave) * 1024), 16, 0, 0);
+  }
+};
+
+template <int BM, int BN, int BK, int ST, int WM, int WN>
+struct LdsSlots {
+  char* a[4];
+  char* b[4];
+};
+
+// One K step kt with static ring slot P = kt % ST.  The K loop runs a multiple of ST steps and
+// always refills the freed slot (past the last stage it re-copies stage 0, which is never read), so
+// the body is straight-line code with a constant wait count: at the start of step kt exactly
+// ST - 2 later stages are in flight.
+template <int BM, int BN, int BK, int ST, int WM, int WN, int P>
+__device__ __forceinline__ void lds_gemm_step(const LdsCopyPlan<BM, BN, BK, WM * WN>& cp,
+                                              const LdsSlots<BM, BN, BK, ST, WM, WN>& sl, int kt, int nk,
+                                              f32x16 (&acc)[BM / WM / 32][BN / WN / 32]) {
+  using C = LdsGemmCfg<BM, BN, BK, WM * WN>;
+  constexpr int FM = BM / WM / 32, FN = BN / WN / 32, PER = C::LA + C::LB;
+  wait_vmcnt<(ST - 2) * PER>();  // this wave's copies of stage kt have landed
+  // Every wave's copies of stage kt are visible and slot (kt - 1) % ST is free after this barrier.
+  // A bare s_barrier: __syncthreads()'s workgroup fence would also wait for the copies of the later
+  // stages still in flight.  The wavefront-scope fences only keep the compiler from moving LDS
+  // accesses across the barrier; they emit no instructions.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // Refill the slot freed by the barrier with stage kt + ST - 1: with two slots right away (the copy
+  // then has this whole step to land), with more slots after this step's LDS reads.
+  constexpr int Q = (P + ST - 1) % ST;
+  const int kn = kt + ST - 1;
+  if constexpr (ST == 2) cp.issue((kn < nk ? kn : 0) * BK, sl.a[Q], sl.b[Q]);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lrow = lane & 31, lhalf = lane >> 5;
+  const int wm = wave / WN, wn = wave % WN;
+  const char* sa = sl.a[P];
+  const char* sb = sl.b[P];
+#pragma unroll
+  for (int kc = 0; kc < BK / 16; ++kc) {
+    u32x4 af[FM], bfr[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      af[i] = *reinterpret_cast<const u32x4*>(sa + C::off(wm * (BM / WM) + i * 32 + lrow, kc * 2 + lhalf));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      bfr[j] = *reinterpret_cast<const u32x4*>(sb + C::off(wn * (BN / WN) + j * 32 + lrow, kc * 2 + lhalf));
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) mfma_chunk(bfr[j], af[i], acc[i][j], bf16());  // C^T = W A^T
+  }
+  if constexpr (ST > 2) cp.issue((kn < nk ? kn : 0) * BK, sl.a[Q], sl.b[Q]);
+}
+
+template <int BM, int BN, int BK, int ST, int WM, int WN, class Epi>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(const bf16* __restrict__ A, int64_t lda,
+                                                                const bf16* __restrict__ W, int64_t ldw, int M,
+                                                                int N, int K, int tiles_m, int tiles_n, Epi epi) {
+  constexpr int NW = WM * WN;
+  using C = LdsGemmCfg<BM, BN, BK, NW>;
+  constexpr int FM = BM / WM / 32, FN = BN / WN / 32;
+  static_assert(ST >= 2 && ST <= 4, "stages");
+  // One __shared__ object per ring slot, so the compiler can tell a slot being read from the slots
+  // with copies in flight (it then needs no vmcnt wait before the reads).
+  __shared__ u32x4 a0[C::ABYTES / 16], a1[C::ABYTES / 16], a2[ST > 2 ? C::ABYTES / 16 : 1],
+      a3[ST > 3 ? C::ABYTES / 16 : 1];
+  __shared__ u32x4 b0[C::BBYTES / 16], b1[C::BBYTES / 16], b2[ST > 2 ? C::BBYTES / 16 : 1],
+      b3[ST > 3 ? C::BBYTES / 16 : 1];
+  const LdsSlots<BM, BN, BK, ST, WM, WN> sl{{(char*)a0, (char*)a1, (char*)a2, (char*)a3},
+                                            {(char*)b0, (char*)b1, (char*)b2, (char*)b3}};
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const LdsCopyPlan<BM, BN, BK, NW> cp(A, lda, W, ldw, m0, n0, M, N);
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = zero16();
+
+  const int nk = K / BK;  // a multiple of ST
+#pragma unroll
+  for (int s = 0; s < ST - 1; ++s) cp.issue(s * BK, sl.a[s], sl.b[s]);
+  for (int kt = 0; kt < nk; kt += ST) {
+    lds_gemm_step<BM, BN, BK, ST, WM, WN, 0>(cp, sl, kt, nk, acc);
+    lds_gemm_step<BM, BN, BK, ST, WM, WN, 1>(cp, sl, kt + 1, nk, acc);
+    if constexpr (ST > 2) lds_gemm_step<BM, BN, BK, ST, WM, WN, 2 % ST>(cp, sl, kt + 2, nk, acc);
+    if constexpr (ST > 3) lds_gemm_step<BM, BN, BK, ST, WM, WN, 3 % ST>(cp, sl, kt + 3, nk, acc);
+  }
+  wait_vmcnt<0>();  // the surplus copies past the last stage land before the LDS is released
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lrow = lane & 31, lhalf = lane >> 5;
+  const int wm = wave / WN, wn = wave % WN;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = m0 + wm * (BM / WM) + i * 32 + lrow;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * (BN / WN) + j * 32 + g * 8 + lhalf * 4;
+        if (n < N)
+          epi(m, n, make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]));
+      }
+  }
+}
+
+template <int BM, int BN, int BK, int ST, int WM, int WN, class Epi>
+hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K, const Epi& epi,
+                      hipStream_t s) {
+  const int tm = (int)ceil_div(M, BM), tn = (int)ceil_div(N, BN);
+  hipLaunchKernelGGL((gemm_lds_kernel<BM, BN, BK, ST, WM, WN, Epi>), dim3((unsigned)(tm * tn)), dim3(WM * WN * 64),
+                     0, s, A, lda, W, ldw, M, N, K, tm, tn, epi);
+  return hipGetLastError();
+}
+
 template <typename T, int BM, int BN, int WM, int WN, class Epi>
 hipError_t launch_cfg(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const Epi& epi,
                       hipStream_t s) {
@@ -235,26 +419,23 @@ hipError_t launch_cfg(const T* A, int64_t lda, const T* W, int64_t ldw, int M, i
 #define WAN_GEMM_FORCE 0
 #endif
 
-// Tile choice for bf16 products with many rows: 256 x 256 with 8 waves (64 x 128 each) when N is a
-// multiple of 256, 256 x 128 with 8 waves otherwise; 128 x 128 with 4 waves for small M or fp32.
+// Tile choice.  bf16 products with many rows and K a multiple of 128 use the asynchronous-copy
+// kernel (256 x 256 tiles, 8 waves of 64 x 128, BK 32, four LDS stages); other bf16 products with
+// many rows use the register-staged kernel with 256-row tiles; small products and fp32 use 128 x 128.
 template <typename T, class Epi>
 hipError_t run_gemm(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const Epi& epi,
                     hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (N % 4 != 0 || K % dtype_traits<T>::per16 != 0) return hipErrorInvalidValue;
-  int cfg = 0;
   if constexpr (sizeof(T) == 2) {
-    if (M >= 4096 && N % 256 == 0 && N >= 1024) cfg = 4;
-    else if (M >= 4096 && N % 128 == 0 && N >= 1024) cfg = 5;
-  }
-  if (WAN_GEMM_FORCE && sizeof(T) == 2) cfg = WAN_GEMM_FORCE - 1;
-  if constexpr (sizeof(T) == 2) {
-    if (cfg == 1) return launch_cfg<T, 256, 128, 2, 2>(A, lda, W, ldw, M, N, K, epi, s);
-    if (cfg == 2) return launch_cfg<T, 256, 256, 2, 2>(A, lda, W, ldw, M, N, K, epi, s);
-    if (cfg == 3) return launch_cfg<T, 256, 256, 2, 4>(A, lda, W, ldw, M, N, K, epi, s);
-    if (cfg == 4) return launch_cfg<T, 256, 256, 4, 2>(A, lda, W, ldw, M, N, K, epi, s);
-    if (cfg == 5) return launch_cfg<T, 256, 128, 4, 2>(A, lda, W, ldw, M, N, K, epi, s);
-    if (cfg == 6) return launch_cfg<T, 128, 256, 2, 4>(A, lda, W, ldw, M, N, K, epi, s);
+    int cfg = 0;
+    if (M >= 4096 && N >= 1024 && K % 128 == 0 && lda % 8 == 0 && ldw % 8 == 0) cfg = 1;
+    else if (M >= 4096 && N % 256 == 0 && N >= 1024) cfg = 2;
+    else if (M >= 4096 && N % 128 == 0 && N >= 1024) cfg = 3;
+    if (WAN_GEMM_FORCE) cfg = WAN_GEMM_FORCE;
+    if (cfg == 1) return launch_lds<256, 256, 32, 4, 4, 2>(A, lda, W, ldw, M, N, K, epi, s);
+    if (cfg == 2) return launch_cfg<T, 256, 256, 4, 2>(A, lda, W, ldw, M, N, K, epi, s);
+    if (cfg == 3) return launch_cfg<T, 256, 128, 4, 2>(A, lda, W, ldw, M, N, K, epi, s);
   }
   return launch_cfg<T, 128, 128, 2, 2>(A, lda, W, ldw, M, N, K, epi, s);
 }
@@ -315,8 +496,9 @@ __global__ void sinusoid_kernel(SinArgs a, int B, int freq_dim, float* __restric
 template <typename T, typename OutT>
 hipError_t gemm_store(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const float* bias,
                       int act, OutT* out, int64_t ldo, hipStream_t s) {
-  EpiStore<OutT> epi{out, ldo, bias, act};
-  return run_gemm<T>(A, lda, W, ldw, M, N, K, epi, s);
+  if (act == ACT_GELU) return run_gemm<T>(A, lda, W, ldw, M, N, K, EpiStore<OutT, ACT_GELU>{out, ldo, bias}, s);
+  if (act == ACT_SILU) return run_gemm<T>(A, lda, W, ldw, M, N, K, EpiStore<OutT, ACT_SILU>{out, ldo, bias}, s);
+  return run_gemm<T>(A, lda, W, ldw, M, N, K, EpiStore<OutT, ACT_NONE>{out, ldo, bias}, s);
 }
 
 template <typename T>
