@@ -8,22 +8,27 @@
 // branches share q, each has its own softmax, outputs are added).
 //
 // How (gfx950):
-//  * one workgroup = 4 waves = 128 queries of one (b, head); each wave owns 32
-//    queries, held in registers as the B operand of S^T = K Q^T.  MFMA lane l then
-//    holds query (l % 32) and 16 keys per 32-key block, so the row max / sum are
-//    in-lane plus one exchange with lane l ^ 32, and the same registers (as bf16)
-//    are the B operand of O^T = V^T P^T: P never leaves registers;
+//  * each wave owns 32 queries, held in registers as the B operand of
+//    S^T = K Q^T.  MFMA lane l then holds query (l % 32) and 16 keys per 32-key
+//    block, so the row max / sum are in-lane plus one exchange with lane l ^ 32,
+//    and the same registers (as bf16) are the B operand of O^T = V^T P^T: P never
+//    leaves registers;
 //  * K tiles [64 keys][hd] and V^T tiles [hd][64 keys] are copied global -> LDS
 //    asynchronously (global_load_lds_dwordx4, no register staging) into
 //    XOR-swizzled layouts that make every MFMA operand read a conflict-free 16-byte
 //    ds_read_b128.  V^T arrives with its keys permuted within each 16-key group
 //    ([0-3, 8-11, 4-7, 12-15]) so the 8 keys one MFMA lane-half needs are contiguous;
-//  * software pipeline: K runs one tile ahead of V (two LDS slots each), and the
-//    S MFMAs of tile t+1 sit in the same basic block as the exponentials and PV
-//    MFMAs of tile t, so the matrix and vector pipes overlap within a wave;
+//  * bf16 runs the ping-pong kernel: 8 waves (two per SIMD) share each K / V^T
+//    tile, and two groups of 4 waves run half a tile apart so that one wave of a
+//    SIMD does softmax + S(t+1) while the other does its PV products; fp32 runs a
+//    4-wave kernel with one barrier per tile;
+//  * operand reads are software-pipelined in small scheduling regions
+//    (sched_barrier) so every LDS read has work to land behind;
 //  * the running maximum only moves when a score exceeds it by more than 2^8 (exp2
 //    units), so the O rescale is rare and p <= 256 stays safe in bf16;
-//    log2(e)/sqrt(hd) is folded into one fma feeding the raw v_exp_f32.
+//    log2(e)/sqrt(hd) is folded into one fma feeding the raw v_exp_f32;
+//  * workgroups are ordered XCD-aware: each XCD's L2 serves a contiguous run of
+//    query tiles of the same heads.
 #include "wan_internal.h"
 
 namespace wan {
@@ -31,6 +36,7 @@ namespace wan {
 namespace {
 
 constexpr int KT = 64;  // keys per tile
+
 constexpr float RESCALE_THRESHOLD = 8.f;
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -47,8 +53,6 @@ struct AttnCfg {
   static constexpr int VMASK = (VCHUNKS < 16 ? VCHUNKS : 16) - 1;
   static constexpr int KBYTES = KT * HD * (int)sizeof(T);  // one K tile
   static constexpr int VBYTES = HD * KT * (int)sizeof(T);  // one V^T tile
-  static constexpr int KLOADS = KBYTES / 16 / 256;         // direct loads per thread per K tile
-  static constexpr int VLOADS = VBYTES / 16 / 256;
   static constexpr int NCH = HD * (int)sizeof(T) / 32;      // 32-byte k-chunks along hd
   static constexpr int ND = HD / 32;                        // 32-wide d blocks of O^T
   // swizzled byte offset of logical 16-byte chunk c of row r
@@ -56,70 +60,114 @@ struct AttnCfg {
   __device__ static __forceinline__ int voff(int r, int c) { return (r * VCHUNKS + (c ^ ((r / VR) & VMASK))) * 16; }
 };
 
-// Per-thread pieces of the asynchronous tile copies, fixed for the whole key loop: the tile row and
-// the 16-byte chunk this lane copies for each of its wave-instructions, and the LDS destination.
-template <typename T, int HD>
+// Per-thread pieces of the asynchronous tile copies (NW waves share each tile), fixed for the whole
+// key loop.  A copy's global address is a wave-uniform base (advanced per tile) plus this lane's
+// 32-bit byte offset; the LDS destination of wave-instruction i is (i * NW + wave) KB into the slot.
+template <typename T, int HD, int NW>
 struct CopyPlan {
   using C = AttnCfg<T, HD>;
-  int krow[C::KLOADS], kcol[C::KLOADS];  // K: key row in the tile, element column
-  int voff[C::VLOADS];                   // V^T: element offset of (d row, column) from the tile start
-  __device__ __forceinline__ CopyPlan(int Lpad) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  static constexpr int KL = C::KBYTES / 1024 / NW;  // copies per wave per K tile
+  static constexpr int VL = C::VBYTES / 1024 / NW;  // copies per wave per V^T tile
+  static_assert(KL * NW * 1024 == C::KBYTES && VL * NW * 1024 == C::VBYTES, "tile / wave split");
+  uint32_t kofs[KL];  // K: byte offset of (tile row, logical chunk) from the tile's first row
+  uint32_t vofs[VL];  // V^T: byte offset of (d row, logical chunk) from the tile start
+  int wave;           // wave index, uniform
+  __device__ __forceinline__ CopyPlan(int64_t k_ss, int Lpad) {
+    const int lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-    for (int i = 0; i < C::KLOADS; ++i) {
-      const int p = (i * 4 + wave) * 64 + lane;  // 16-byte position in the tile
+    for (int i = 0; i < KL; ++i) {
+      const int p = (i * NW + wave) * 64 + lane;  // 16-byte position in the tile
       const int r = p / C::KCHUNKS;
-      krow[i] = r;
-      kcol[i] = ((p % C::KCHUNKS) ^ ((r / C::KR) & C::KMASK)) * C::E16;  // logical chunk stored there
+      const int col = ((p % C::KCHUNKS) ^ ((r / C::KR) & C::KMASK)) * C::E16;  // logical chunk stored there
+      kofs[i] = (uint32_t)(((int64_t)r * k_ss + col) * (int64_t)sizeof(T));
     }
 #pragma unroll
-    for (int i = 0; i < C::VLOADS; ++i) {
-      const int p = (i * 4 + wave) * 64 + lane;
+    for (int i = 0; i < VL; ++i) {
+      const int p = (i * NW + wave) * 64 + lane;
       const int r = p / C::VCHUNKS;  // d row
-      voff[i] = r * Lpad + ((p % C::VCHUNKS) ^ ((r / C::VR) & C::VMASK)) * C::E16;
+      vofs[i] = (uint32_t)(((int64_t)r * Lpad + ((p % C::VCHUNKS) ^ ((r / C::VR) & C::VMASK)) * C::E16) *
+                           (int64_t)sizeof(T));
     }
   }
 };
 
-// Issue the asynchronous copies of one K tile (keys j0..j0+63, clamped to L-1: rows past L are
-// masked out of the softmax) into kslot.  Wave-instruction (i, wave) fills 1 KB of LDS.
-template <typename T, int HD>
-__device__ __forceinline__ void load_k_tile(const CopyPlan<T, HD>& cp, const T* __restrict__ kbase, int64_t k_ss,
-                                            int L, int j0, char* kslot) {
+// A wave-uniform pointer held in scalar registers (the per-tile base of the copies).
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
+// Issue the asynchronous copies of one K tile (keys j0..j0+63) into kslot.  In the last, partial
+// tile the rows past L are clamped to L - 1 (their scores are masked out of the softmax).
+template <typename T, int HD, int NW>
+__device__ __forceinline__ void load_k_tile(const CopyPlan<T, HD, NW>& cp, const T* __restrict__ kbase,
+                                            int64_t k_ss, int L, int j0, char* kslot) {
   using C = AttnCfg<T, HD>;
-  const int wave = threadIdx.x >> 6;
+  using CP = CopyPlan<T, HD, NW>;
+  if (j0 + KT <= L) {
+    const char* base = uniform_ptr(kbase + (int64_t)j0 * k_ss);
 #pragma unroll
-  for (int i = 0; i < C::KLOADS; ++i) {
-    const int j = min(j0 + cp.krow[i], L - 1);
-    const T* src = kbase + (int64_t)j * k_ss + cp.kcol[i];
-    __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(kslot + (i * 4 + wave) * 1024), 16, 0, 0);
+    for (int i = 0; i < CP::KL; ++i)
+      __builtin_amdgcn_global_load_lds((glb_void*)(base + cp.kofs[i]), (lds_void*)(kslot + (i * NW + cp.wave) * 1024),
+                                       16, 0, 0);
+  } else {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < CP::KL; ++i) {
+      const int p = (i * NW + cp.wave) * 64 + lane;
+      const int r = p / C::KCHUNKS;
+      const int col = ((p % C::KCHUNKS) ^ ((r / C::KR) & C::KMASK)) * C::E16;
+      const T* src = kbase + (int64_t)min(j0 + r, L - 1) * k_ss + col;
+      __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(kslot + (i * NW + cp.wave) * 1024), 16, 0, 0);
+    }
   }
 }
 
-template <typename T, int HD>
-__device__ __forceinline__ void load_v_tile(const CopyPlan<T, HD>& cp, const T* __restrict__ vtb, int j0,
+// Issue the copies of one V^T tile (columns j0..j0+63 of the [hd][Lpad] rows; j0 < Lpad).
+template <typename T, int HD, int NW>
+__device__ __forceinline__ void load_v_tile(const CopyPlan<T, HD, NW>& cp, const T* __restrict__ vtb, int j0,
                                             char* vslot) {
-  using C = AttnCfg<T, HD>;
-  const int wave = threadIdx.x >> 6;
+  const char* base = uniform_ptr(vtb + j0);
 #pragma unroll
-  for (int i = 0; i < C::VLOADS; ++i) {
-    const T* src = vtb + j0 + cp.voff[i];
-    __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(vslot + (i * 4 + wave) * 1024), 16, 0, 0);
-  }
+  for (int i = 0; i < CopyPlan<T, HD, NW>::VL; ++i)
+    __builtin_amdgcn_global_load_lds((glb_void*)(base + cp.vofs[i]), (lds_void*)(vslot + (i * NW + cp.wave) * 1024),
+                                     16, 0, 0);
 }
+
+// Per-lane byte offsets of the MFMA operand reads (loop invariant).  K fragment (kb, c) of this lane
+// is at k[c] + kb * KB32 in a K slot; V^T fragment (d, chunk index i) at v[i] + d * VD32 in a V slot.
+// The swizzle key of a row only depends on the lane's row within its 32-row block, so one offset per
+// chunk serves every block.
+template <typename T, int HD>
+struct FragAddr {
+  using C = AttnCfg<T, HD>;
+  static constexpr int NV = sizeof(T) == 2 ? 4 : 8;  // V^T chunks this lane reads per tile
+  static constexpr int KB32 = 32 * C::KCHUNKS * 16, VD32 = 32 * C::VCHUNKS * 16;
+  uint32_t k[C::NCH], v[NV];
+  __device__ __forceinline__ FragAddr() {
+    const int lane = threadIdx.x & 63, lrow = lane & 31, lhalf = lane >> 5;
+#pragma unroll
+    for (int c = 0; c < C::NCH; ++c) k[c] = (uint32_t)C::koff(lrow, 2 * c + lhalf);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = (uint32_t)C::voff(lrow, 2 * i + lhalf);
+  }
+};
 
 // S^T (two 32-key blocks) of the wave's 32 queries against the K tile in kslot.
 template <typename T, int HD>
-__device__ __forceinline__ void scores(const u32x4 (&qf)[AttnCfg<T, HD>::NCH], const char* kslot, f32x16 (&s)[2]) {
+__device__ __forceinline__ void scores(const u32x4 (&qf)[AttnCfg<T, HD>::NCH], const FragAddr<T, HD>& fa,
+                                       const char* kslot, f32x16 (&s)[2]) {
   using C = AttnCfg<T, HD>;
-  const int lane = threadIdx.x & 63, lrow = lane & 31, lhalf = lane >> 5;
   s[0] = zero16();
   s[1] = zero16();
 #pragma unroll
   for (int c = 0; c < C::NCH; ++c)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(kslot + C::koff(kb * 32 + lrow, 2 * c + lhalf));
+      const u32x4 a = *reinterpret_cast<const u32x4*>(kslot + fa.k[c] + kb * FragAddr<T, HD>::KB32);
       mfma_chunk(a, qf[c], s[kb], T());
     }
 }
@@ -133,31 +181,20 @@ struct Slots {
   char *k0, *k1, *v0, *v1;  // four distinct __shared__ arrays (distinct objects for alias analysis)
 };
 
-// One pipelined tile step t with static slot parity P = t % 2: issue V(t+1) -> v[1-P] and
-// K(t+2) -> k[P]; softmax of S(t); S(t+1) from k[1-P]; O^T += V^T P^T from v[P].
-template <typename T, int HD, int P>
-__device__ __forceinline__ void tile_step(const u32x4 (&qf)[AttnCfg<T, HD>::NCH], const KVStream& kv,
-                                          const CopyPlan<T, HD>& cp, const T* __restrict__ kbase,
-                                          const T* __restrict__ vtb, int t, int nt, float c_log2,
-                                          const Slots<T, HD>& sl, f32x16 (&s)[2], f32x16 (&sn)[2],
-                                          f32x16 (&o)[AttnCfg<T, HD>::ND], SoftState& st) {
+// Online-softmax bookkeeping of one tile's scores s (keys j0.. of a stream with L keys): masks keys
+// >= L and moves the running maximum lazily (rescaling O and l when it does).
+template <typename T, int HD>
+__device__ __forceinline__ void softmax_prep(f32x16 (&s)[2], int j0, int L, float c_log2,
+                                             f32x16 (&o)[AttnCfg<T, HD>::ND], SoftState& st) {
   using C = AttnCfg<T, HD>;
-  const int lane = threadIdx.x & 63, lrow = lane & 31, lhalf = lane >> 5;
-  char* k_this = P ? sl.k1 : sl.k0;
-  char* k_next = P ? sl.k0 : sl.k1;
-  char* v_this = P ? sl.v1 : sl.v0;
-  char* v_next = P ? sl.v0 : sl.v1;
-  const int j0 = t * KT;
-  if (t + 1 < nt) load_v_tile<T, HD>(cp, vtb, j0 + KT, v_next);
-  if (t + 2 < nt) load_k_tile<T, HD>(cp, kbase, kv.k_ss, kv.L, j0 + 2 * KT, k_this);
-
-  if (j0 + KT > kv.L) {  // mask keys beyond L (only the last tile can hold any)
+  const int lhalf = (threadIdx.x & 63) >> 5;
+  if (j0 + KT > L) {  // mask keys beyond L (only the last tile can hold any)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = j0 + kb * 32 + (r >> 2) * 8 + lhalf * 4 + (r & 3);
-        if (key >= kv.L) s[kb][r] = -__builtin_inff();
+        if (key >= L) s[kb][r] = -__builtin_inff();
       }
   }
   float mx = fmaxf(s[0][0], s[0][1]);
@@ -178,39 +215,125 @@ __device__ __forceinline__ void tile_step(const u32x4 (&qf)[AttnCfg<T, HD>::NCH]
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
   }
+}
+
+// bf16 softmax half of a tile: the exponentials of S(t) (in s, after softmax_prep) packed into the
+// PV operands pf, interleaved with S(t+1) = K(t+1) Q^T from kslot into sn.  Software-pipelined in
+// small scheduling regions (the compiler moves nothing across a sched_barrier): region c issues the
+// LDS reads of K chunk c + 1, then 32 / NCH exponentials and the two MFMAs of chunk c.  On a
+// stream's last tile kslot holds a stale tile with no copy in flight; the S(t+1) so computed is
+// never used.
+template <typename T, int HD>
+__device__ __forceinline__ void softmax_and_next_scores(const u32x4 (&qf)[AttnCfg<T, HD>::NCH],
+                                                        const FragAddr<T, HD>& fa, const char* kslot,
+                                                        f32x16 (&s)[2], f32x16 (&sn)[2], float c_log2,
+                                                        SoftState& st, u32x4 (&pf)[4]) {
+  using C = AttnCfg<T, HD>;
+  constexpr int EPC = 32 / C::NCH;  // exponentials per S chunk
   const float negm = -st.m;
   float lsum = 0.f;
+  sn[0] = zero16();
+  sn[1] = zero16();
+  u32x4 kf[2][2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
+    kf[0][kb] = *reinterpret_cast<const u32x4*>(kslot + fa.k[0] + kb * FragAddr<T, HD>::KB32);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+  for (int c = 0; c < C::NCH; ++c) {
+    if (c + 1 < C::NCH) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        kf[(c + 1) & 1][kb] = *reinterpret_cast<const u32x4*>(kslot + fa.k[c + 1] + kb * FragAddr<T, HD>::KB32);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the reads go out before this region's work
+#pragma unroll
+    for (int e = c * EPC; e < (c + 1) * EPC; ++e) {
       // raw v_exp_f32: the argument is <= RESCALE_THRESHOLD or -inf, so no range fix-up is needed
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c_log2, negm));
-      s[kb][r] = p;
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[e >> 4][e & 15], c_log2, negm));
+      s[e >> 4][e & 15] = p;
       lsum += p;
     }
-  st.l += lsum;
-
-  // S of the next tile, independent of the exponentials and PV products around it so the compiler
-  // interleaves them (on the last step it reads a stale slot -- no copy is in flight -- and is unused).
-  scores<T, HD>(qf, k_next, sn);
-
-  // O^T += V^T P^T
-  if constexpr (sizeof(T) == 2) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {  // 16-key chunks; this lane half's 8 keys are 16-byte chunk 2c + lhalf
-      const int kb = c >> 1, r0 = (c & 1) * 8;
+    if (((c + 1) * EPC) % 8 == 0) {  // a 16-key P chunk is complete: pack this lane half's 8 keys
+      const int pc = (c + 1) * EPC / 8 - 1, kb = pc >> 1, r0 = (pc & 1) * 8;
       bf16x8 pk;
 #pragma unroll
       for (int i = 0; i < 8; ++i) pk[i] = (bf16)s[kb][r0 + i];
-      const u32x4 pb = __builtin_bit_cast(u32x4, pk);
-#pragma unroll
-      for (int d = 0; d < C::ND; ++d) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(v_this + C::voff(d * 32 + lrow, 2 * c + lhalf));
-        mfma_chunk(a, pb, o[d], T());
-      }
+      pf[pc] = __builtin_bit_cast(u32x4, pk);
     }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) mfma_chunk(kf[c & 1][kb], qf[c], sn[kb], T());
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  st.l += lsum;
+}
+
+// bf16 O^T += V^T P^T for one tile (V^T tile in vslot): units of two MFMAs, each reading its V^T
+// fragments one unit ahead.
+template <typename T, int HD>
+__device__ __forceinline__ void pv_products(const FragAddr<T, HD>& fa, const char* vslot, const u32x4 (&pf)[4],
+                                            f32x16 (&o)[AttnCfg<T, HD>::ND]) {
+  using C = AttnCfg<T, HD>;
+  constexpr int DP = C::ND / 2, NU = 4 * DP;  // unit u = (16-key chunk u / DP, d-blocks 2 (u % DP) + 0, 1)
+  u32x4 va[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) va[0][j] = *reinterpret_cast<const u32x4*>(vslot + fa.v[0] + j * FragAddr<T, HD>::VD32);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    if (u + 1 < NU) {
+      const int c1 = (u + 1) / DP, d1 = ((u + 1) % DP) * 2;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        va[(u + 1) & 1][j] = *reinterpret_cast<const u32x4*>(vslot + fa.v[c1] + (d1 + j) * FragAddr<T, HD>::VD32);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const int c = u / DP, d0 = (u % DP) * 2;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) mfma_chunk(va[u & 1][j], pf[c], o[d0 + j], T());
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Four-wave kernel (fp32, and bf16 when WAN_ATTN_PP is 0): one barrier per tile.
+// ---------------------------------------------------------------------------
+
+// One pipelined tile step t with static slot parity P = t % 2: issue V(t+1) -> v[1-P] and
+// K(t+2) -> k[P]; softmax of S(t); S(t+1) from k[1-P]; O^T += V^T P^T from v[P].
+template <typename T, int HD, int P>
+__device__ __forceinline__ void tile_step(const u32x4 (&qf)[AttnCfg<T, HD>::NCH], const FragAddr<T, HD>& fa,
+                                          const KVStream& kv, const CopyPlan<T, HD, 4>& cp,
+                                          const T* __restrict__ kbase, const T* __restrict__ vtb, int t, int nt,
+                                          float c_log2, const Slots<T, HD>& sl, f32x16 (&s)[2], f32x16 (&sn)[2],
+                                          f32x16 (&o)[AttnCfg<T, HD>::ND], SoftState& st) {
+  using C = AttnCfg<T, HD>;
+  char* k_this = P ? sl.k1 : sl.k0;
+  char* k_next = P ? sl.k0 : sl.k1;
+  char* v_this = P ? sl.v1 : sl.v0;
+  char* v_next = P ? sl.v0 : sl.v1;
+  const int j0 = t * KT;
+  if (t + 1 < nt) load_v_tile<T, HD, 4>(cp, vtb, j0 + KT, v_next);
+  if (t + 2 < nt) load_k_tile<T, HD, 4>(cp, kbase, kv.k_ss, kv.L, j0 + 2 * KT, k_this);
+  softmax_prep<T, HD>(s, j0, kv.L, c_log2, o, st);
+  if constexpr (sizeof(T) == 2) {
+    u32x4 pf[4];
+    // on the last step S(t+1) reads a stale slot (no copy is in flight) and is unused
+    softmax_and_next_scores<T, HD>(qf, fa, k_next, s, sn, c_log2, st, pf);
+    pv_products<T, HD>(fa, v_this, pf, o);
   } else {
+    const float negm = -st.m;
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c_log2, negm));
+        s[kb][r] = p;
+        lsum += p;
+      }
+    st.l += lsum;
+    scores<T, HD>(qf, fa, k_next, sn);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -220,7 +343,7 @@ __device__ __forceinline__ void tile_step(const u32x4 (&qf)[AttnCfg<T, HD>::NCH]
 #pragma unroll
         for (int d = 0; d < C::ND; ++d) {
           // keys kb*32 + g*8 + lhalf*4 .. +3 = 16-byte chunk kb*8 + g*2 + lhalf of the fp32 V^T row
-          const u32x4 a = *reinterpret_cast<const u32x4*>(v_this + C::voff(d * 32 + lrow, kb * 8 + g * 2 + lhalf));
+          const u32x4 a = *reinterpret_cast<const u32x4*>(v_this + fa.v[kb * 4 + g] + d * FragAddr<T, HD>::VD32);
           mfma_chunk(a, pb, o[d], T());
         }
       }
@@ -231,30 +354,92 @@ __device__ __forceinline__ void tile_step(const u32x4 (&qf)[AttnCfg<T, HD>::NCH]
 
 // One key/value stream for the wave's 32 queries; accumulates O^T (unnormalised) and (m, l).
 template <typename T, int HD>
-__device__ __forceinline__ void attend_stream(const u32x4 (&qf)[AttnCfg<T, HD>::NCH], const KVStream& kv, int b,
-                                              int h, int H, float c_log2, const Slots<T, HD>& sl,
-                                              f32x16 (&o)[AttnCfg<T, HD>::ND], SoftState& st) {
+__device__ __forceinline__ void attend_stream(const u32x4 (&qf)[AttnCfg<T, HD>::NCH], const FragAddr<T, HD>& fa,
+                                              const KVStream& kv, int b, int h, int H, float c_log2,
+                                              const Slots<T, HD>& sl, f32x16 (&o)[AttnCfg<T, HD>::ND],
+                                              SoftState& st) {
   const T* kbase = reinterpret_cast<const T*>(kv.k) + (int64_t)b * kv.k_bs + (int64_t)h * HD;
   const T* vtb = reinterpret_cast<const T*>(kv.vt) + ((int64_t)b * H + h) * HD * (int64_t)kv.Lpad;
   const int nt = (kv.L + KT - 1) / KT;
 
-  const CopyPlan<T, HD> cp(kv.Lpad);
+  const CopyPlan<T, HD, 4> cp(kv.k_ss, kv.Lpad);
   __syncthreads();  // earlier users of the LDS slots are done
-  load_k_tile<T, HD>(cp, kbase, kv.k_ss, kv.L, 0, sl.k0);
-  load_v_tile<T, HD>(cp, vtb, 0, sl.v0);
-  load_k_tile<T, HD>(cp, kbase, kv.k_ss, kv.L, KT, sl.k1);  // clamped rows when nt == 1 (unused)
+  load_k_tile<T, HD, 4>(cp, kbase, kv.k_ss, kv.L, 0, sl.k0);
+  load_v_tile<T, HD, 4>(cp, vtb, 0, sl.v0);
+  load_k_tile<T, HD, 4>(cp, kbase, kv.k_ss, kv.L, KT, sl.k1);  // clamped rows when nt == 1 (unused)
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   f32x16 sa[2], sb[2];
-  scores<T, HD>(qf, sl.k0, sa);
+  scores<T, HD>(qf, fa, sl.k0, sa);
   __syncthreads();  // every wave has read K(0) before step 0 refills its slot with K(2)
   for (int t = 0; t < nt; t += 2) {
-    tile_step<T, HD, 0>(qf, kv, cp, kbase, vtb, t, nt, c_log2, sl, sa, sb, o, st);
-    if (t + 1 < nt) tile_step<T, HD, 1>(qf, kv, cp, kbase, vtb, t + 1, nt, c_log2, sl, sb, sa, o, st);
+    tile_step<T, HD, 0>(qf, fa, kv, cp, kbase, vtb, t, nt, c_log2, sl, sa, sb, o, st);
+    if (t + 1 < nt) tile_step<T, HD, 1>(qf, fa, kv, cp, kbase, vtb, t + 1, nt, c_log2, sl, sb, sa, o, st);
   }
 }
 
+// Workgroup id -> (query tile, head, batch row), XCD-aware: workgroup ids are dealt round-robin to
+// the 8 XCDs; each XCD gets a contiguous run of (batch, head, query tile) so the workgroups sharing
+// an L2 stream the same head's K/V.
+__device__ __forceinline__ void attn_tile_coords(int& qt, int& h, int& b) {
+  const int nq = gridDim.x, nh = gridDim.y;
+  const int n = nq * nh * gridDim.z;
+  const int lin = blockIdx.x + nq * (blockIdx.y + nh * blockIdx.z);
+  const int xcd = lin & 7;
+  const int t = xcd * (n >> 3) + min(xcd, n & 7) + (lin >> 3);  // bijection on [0, n)
+  qt = t % nq;
+  h = (t / nq) % nh;
+  b = t / (nq * nh);
+}
+
+// Normalise one stream's O^T by its row sums and add it into acc (first stream: assign).
+template <typename T, int HD>
+__device__ __forceinline__ void finish_stream(int si, const f32x16 (&o)[AttnCfg<T, HD>::ND], const SoftState& st,
+                                              f32x16 (&acc)[AttnCfg<T, HD>::ND]) {
+  const float inv = 1.f / (st.l + __shfl_xor(st.l, 32, 64));
+#pragma unroll
+  for (int d = 0; d < AttnCfg<T, HD>::ND; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[d][r] = (si == 0 ? 0.f : acc[d][r]) + o[d][r] * inv;
+}
+
+// Write the wave's O rows (lane: query qrow, d = 32 dblk + 8 g + 4 lhalf + 0..3).
+template <typename T, int HD>
+__device__ __forceinline__ void store_rows(const f32x16 (&acc)[AttnCfg<T, HD>::ND], T* __restrict__ out,
+                                           int64_t o_bs, int64_t o_ss, int b, int h, int qrow, int S) {
+  const int lhalf = (threadIdx.x & 63) >> 5;
+  if (qrow >= S) return;
+  T* op = out + (int64_t)b * o_bs + (int64_t)qrow * o_ss + (int64_t)h * HD;
+#pragma unroll
+  for (int d = 0; d < AttnCfg<T, HD>::ND; ++d)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int dd = d * 32 + g * 8 + lhalf * 4;
+      if constexpr (sizeof(T) == 2) {
+        bf16x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = (bf16)acc[d][4 * g + i];
+        *reinterpret_cast<bf16x4*>(op + dd) = v;
+      } else {
+        *reinterpret_cast<float4*>(op + dd) =
+            make_float4(acc[d][4 * g], acc[d][4 * g + 1], acc[d][4 * g + 2], acc[d][4 * g + 3]);
+      }
+    }
+}
+
+// Q^T as the B operand: lane holds query qrow (clamped), 16 bytes per 32-byte chunk of hd.
+template <typename T, int HD>
+__device__ __forceinline__ void load_q(const T* __restrict__ q, int64_t q_bs, int64_t q_ss, int b, int h, int qrow,
+                                       int S, u32x4 (&qf)[AttnCfg<T, HD>::NCH]) {
+  using C = AttnCfg<T, HD>;
+  const int lhalf = (threadIdx.x & 63) >> 5;
+  const T* qp = q + (int64_t)b * q_bs + (int64_t)min(qrow, S - 1) * q_ss + (int64_t)h * HD + lhalf * C::E16;
+#pragma unroll
+  for (int c = 0; c < C::NCH; ++c) qf[c] = *reinterpret_cast<const u32x4*>(qp + c * 2 * C::E16);
+}
+
+// One workgroup = 4 waves = 128 queries of one (b, head).
 template <typename T, int HD, int NS, int KIND>
 __global__ __launch_bounds__(256, 2) void attention_kernel(const T* __restrict__ q, int64_t q_bs, int64_t q_ss,
                                                             KVStream s0, KVStream s1, int S, int H, float c_log2,
@@ -263,16 +448,13 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const T* __restrict__
   __shared__ u32x4 k0_raw[C::KBYTES / 16], k1_raw[C::KBYTES / 16], v0_raw[C::VBYTES / 16], v1_raw[C::VBYTES / 16];
   const Slots<T, HD> sl{reinterpret_cast<char*>(k0_raw), reinterpret_cast<char*>(k1_raw),
                         reinterpret_cast<char*>(v0_raw), reinterpret_cast<char*>(v1_raw)};
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lrow = lane & 31, lhalf = lane >> 5;
-  const int qrow = blockIdx.x * 128 + wave * 32 + lrow;
-
-  // Q^T as the B operand: lane holds query qrow, 16 bytes per 32-byte chunk of hd.
+  int qt, h, b;
+  attn_tile_coords(qt, h, b);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int qrow = qt * 128 + wave * 32 + (lane & 31);
+  const FragAddr<T, HD> fa;
   u32x4 qf[C::NCH];
-  const T* qp = q + (int64_t)b * q_bs + (int64_t)min(qrow, S - 1) * q_ss + (int64_t)h * HD + lhalf * C::E16;
-#pragma unroll
-  for (int c = 0; c < C::NCH; ++c) qf[c] = *reinterpret_cast<const u32x4*>(qp + c * 2 * C::E16);
+  load_q<T, HD>(q, q_bs, q_ss, b, h, qrow, S, qf);
 
   f32x16 o[C::ND], acc[C::ND];
   SoftState st;
@@ -282,45 +464,173 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const T* __restrict__
     for (int d = 0; d < C::ND; ++d) o[d] = zero16();
     st.m = -__builtin_inff();
     st.l = 0.f;
-    attend_stream<T, HD>(qf, si == 0 ? s0 : s1, b, h, H, c_log2, sl, o, st);
-    const float inv = 1.f / (st.l + __shfl_xor(st.l, 32, 64));
-#pragma unroll
-    for (int d = 0; d < C::ND; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[d][r] = (si == 0 ? 0.f : acc[d][r]) + o[d][r] * inv;
+    attend_stream<T, HD>(qf, fa, si == 0 ? s0 : s1, b, h, H, c_log2, sl, o, st);
+    finish_stream<T, HD>(si, o, st, acc);
   }
-
-  if (qrow < S) {
-    T* op = out + (int64_t)b * o_bs + (int64_t)qrow * o_ss + (int64_t)h * HD;
-#pragma unroll
-    for (int d = 0; d < C::ND; ++d)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dd = d * 32 + g * 8 + lhalf * 4;
-        if constexpr (sizeof(T) == 2) {
-          bf16x4 v;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = (bf16)acc[d][4 * g + i];
-          *reinterpret_cast<bf16x4*>(op + dd) = v;
-        } else {
-          *reinterpret_cast<float4*>(op + dd) =
-              make_float4(acc[d][4 * g], acc[d][4 * g + 1], acc[d][4 * g + 2], acc[d][4 * g + 3]);
-        }
-      }
-  }
+  store_rows<T, HD>(acc, out, o_bs, o_ss, b, h, qrow, S);
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong kernel (bf16): one workgroup = 8 waves = 256 queries of one (b, head), two waves per
+// SIMD.  Each wave alternates A(t) = softmax of S(t) + the MFMAs of S(t+1) (vector-heavy) and
+// B(t) = O^T += V^T P^T (matrix only), with a workgroup barrier between the two.  Waves 4-7
+// (group 1) pass one extra barrier at the start and waves 0-3 (group 0) one at the end, so group 1
+// runs a half tile behind: between two barriers one wave of each SIMD is in A and the other in B,
+// and the SIMD's matrix and vector units work at the same time.
+//
+// Copies (all 8 waves take a share of each tile; tile t lives in slot t % 2).  With b_k the k-th
+// barrier of the workgroup: K(t) is last read by group 1's A(t-1), which ends at b_2t, so K(t+2) is
+// copied right after b_2t and is first read after b_2t+2; V^T(t-1) is last read by group 1's
+// B(t-1), which ends at b_2t+1, so V^T(t+1) is copied right after b_2t+1 and first read after
+// b_2t+3.  Every copy thus has two phases to land; a wave waits at a barrier only for the copies it
+// issued two phases before.
+// ---------------------------------------------------------------------------
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Barrier between phases.  The copies this wave issued in the previous phase (LAST of them) stay in
+// flight: a bare s_barrier (the workgroup fence of __syncthreads() would wait for them); the
+// wavefront-scope fences only stop the compiler from moving LDS accesses across it.
+template <int LAST>
+__device__ __forceinline__ void phase_barrier(int last) {
+  if (last) wait_vm<LAST>(); else wait_vm<0>();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Tile t (static slot parity P = t % 2) as seen by one wave: barrier, A(t), barrier, B(t).  s holds
+// S(t) on entry, sn receives S(t+1).  `last` counts the copies this wave issued in its previous phase.
+template <typename T, int HD, int P>
+__device__ __forceinline__ void pp_tile(const u32x4 (&qf)[AttnCfg<T, HD>::NCH], const FragAddr<T, HD>& fa,
+                                        const KVStream& kv, const CopyPlan<T, HD, 8>& cp,
+                                        const T* __restrict__ kbase, const T* __restrict__ vtb, int t, int nt,
+                                        int grp, float c_log2, const Slots<T, HD>& sl, f32x16 (&s)[2],
+                                        f32x16 (&sn)[2], f32x16 (&o)[AttnCfg<T, HD>::ND], SoftState& st,
+                                        int& last) {
+  using CP = CopyPlan<T, HD, 8>;
+  static_assert(CP::KL == CP::VL, "equal K and V^T copy counts");
+  char* k_this = P ? sl.k1 : sl.k0;  // K(t) -> K(t+2)
+  char* k_next = P ? sl.k0 : sl.k1;  // K(t+1) -> K(t+3)
+  char* v_this = P ? sl.v1 : sl.v0;  // V^T(t)
+  char* v_next = P ? sl.v0 : sl.v1;  // V^T(t-1) -> V^T(t+1)
+  const int j0 = t * KT;
+  // ---- A(t)
+  phase_barrier<CP::KL>(last);
+  last = 0;
+  if (grp == 0) {
+    if (t + 2 < nt) { load_k_tile<T, HD, 8>(cp, kbase, kv.k_ss, kv.L, j0 + 2 * KT, k_this); last = 1; }
+  } else {
+    if (t >= 1 && t + 1 < nt) { load_v_tile<T, HD, 8>(cp, vtb, j0 + KT, v_next); last = 1; }
+  }
+  softmax_prep<T, HD>(s, j0, kv.L, c_log2, o, st);
+  u32x4 pf[4];
+  softmax_and_next_scores<T, HD>(qf, fa, k_next, s, sn, c_log2, st, pf);
+  // ---- B(t)
+  phase_barrier<CP::KL>(last);
+  last = 0;
+  if (grp == 0) {
+    if (t >= 1 && t + 1 < nt) { load_v_tile<T, HD, 8>(cp, vtb, j0 + KT, v_next); last = 1; }
+  } else {
+    if (t + 3 < nt) { load_k_tile<T, HD, 8>(cp, kbase, kv.k_ss, kv.L, j0 + 3 * KT, k_next); last = 1; }
+  }
+  pv_products<T, HD>(fa, v_this, pf, o);
+}
+
+template <typename T, int HD>
+__device__ __forceinline__ void attend_stream_pp(const u32x4 (&qf)[AttnCfg<T, HD>::NCH], const FragAddr<T, HD>& fa,
+                                                 const KVStream& kv, int b, int h, int H, int grp, float c_log2,
+                                                 const Slots<T, HD>& sl, f32x16 (&o)[AttnCfg<T, HD>::ND],
+                                                 SoftState& st) {
+  using CP = CopyPlan<T, HD, 8>;
+  const T* kbase = reinterpret_cast<const T*>(kv.k) + (int64_t)b * kv.k_bs + (int64_t)h * HD;
+  const T* vtb = reinterpret_cast<const T*>(kv.vt) + ((int64_t)b * H + h) * HD * (int64_t)kv.Lpad;
+  const int nt = (kv.L + KT - 1) / KT;
+
+  const CP cp(kv.k_ss, kv.Lpad);
+  __syncthreads();  // earlier users of the LDS slots are done
+  load_k_tile<T, HD, 8>(cp, kbase, kv.k_ss, kv.L, 0, sl.k0);
+  load_k_tile<T, HD, 8>(cp, kbase, kv.k_ss, kv.L, KT, sl.k1);  // clamped rows when nt == 1 (unused)
+  load_v_tile<T, HD, 8>(cp, vtb, 0, sl.v0);
+  if (nt > 1) load_v_tile<T, HD, 8>(cp, vtb, KT, sl.v1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  f32x16 sa[2], sb[2];
+  scores<T, HD>(qf, fa, sl.k0, sa);
+  int last = 0;
+  if (grp == 1) {  // group 1 starts a phase late; after this barrier K(0) is read by all: copy K(2)
+    phase_barrier<CP::KL>(0);
+    if (2 < nt) { load_k_tile<T, HD, 8>(cp, kbase, kv.k_ss, kv.L, 2 * KT, sl.k0); last = 1; }
+  }
+  for (int t = 0; t < nt; t += 2) {
+    pp_tile<T, HD, 0>(qf, fa, kv, cp, kbase, vtb, t, nt, grp, c_log2, sl, sa, sb, o, st, last);
+    if (t + 1 < nt) pp_tile<T, HD, 1>(qf, fa, kv, cp, kbase, vtb, t + 1, nt, grp, c_log2, sl, sb, sa, o, st, last);
+  }
+  if (grp == 0) phase_barrier<CP::KL>(0);  // group 0 passes the barrier ending group 1's last B
+}
+
+template <typename T, int HD, int NS, int KIND>
+__global__ __launch_bounds__(512, 1) void attention_pp_kernel(const T* __restrict__ q, int64_t q_bs, int64_t q_ss,
+                                                               KVStream s0, KVStream s1, int S, int H, float c_log2,
+                                                               T* __restrict__ out, int64_t o_bs, int64_t o_ss) {
+  using C = AttnCfg<T, HD>;
+  __shared__ u32x4 k0_raw[C::KBYTES / 16], k1_raw[C::KBYTES / 16], v0_raw[C::VBYTES / 16], v1_raw[C::VBYTES / 16];
+  const Slots<T, HD> sl{reinterpret_cast<char*>(k0_raw), reinterpret_cast<char*>(k1_raw),
+                        reinterpret_cast<char*>(v0_raw), reinterpret_cast<char*>(v1_raw)};
+  int qt, h, b;
+  attn_tile_coords(qt, h, b);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave >> 2;
+  const int qrow = qt * 256 + wave * 32 + (lane & 31);
+  const FragAddr<T, HD> fa;
+  u32x4 qf[C::NCH];
+  load_q<T, HD>(q, q_bs, q_ss, b, h, qrow, S, qf);
+
+  f32x16 o[C::ND], acc[C::ND];
+  SoftState st;
+#pragma unroll
+  for (int si = 0; si < NS; ++si) {
+#pragma unroll
+    for (int d = 0; d < C::ND; ++d) o[d] = zero16();
+    st.m = -__builtin_inff();
+    st.l = 0.f;
+    attend_stream_pp<T, HD>(qf, fa, si == 0 ? s0 : s1, b, h, H, grp, c_log2, sl, o, st);
+    finish_stream<T, HD>(si, o, st, acc);
+  }
+  store_rows<T, HD>(acc, out, o_bs, o_ss, b, h, qrow, S);
+}
+
+#ifndef WAN_ATTN_PP
+#define WAN_ATTN_PP 1
+#endif
+
 // KIND only separates the self-attention (0) and cross-attention (1) kernel symbols in profiles.
+// bf16 uses the ping-pong kernel (256 queries per workgroup), fp32 the four-wave kernel.
 template <typename T, int HD, int KIND>
 hipError_t launch_hd(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0, KVStream s1, int nstreams, int B, int S,
                      int H, float c_log2, T* o, int64_t o_bs, int64_t o_ss, hipStream_t s) {
-  dim3 grid((unsigned)ceil_div(S, 128), (unsigned)H, (unsigned)B);
-  if (nstreams == 2)
-    hipLaunchKernelGGL((attention_kernel<T, HD, 2, KIND>), grid, dim3(256), 0, s, q, q_bs, q_ss, s0, s1, S, H, c_log2,
-                       o, o_bs, o_ss);
-  else
-    hipLaunchKernelGGL((attention_kernel<T, HD, 1, KIND>), grid, dim3(256), 0, s, q, q_bs, q_ss, s0, s1, S, H, c_log2,
-                       o, o_bs, o_ss);
+  if constexpr (sizeof(T) == 2 && WAN_ATTN_PP) {
+    dim3 grid((unsigned)ceil_div(S, 256), (unsigned)H, (unsigned)B);
+    if (nstreams == 2)
+      hipLaunchKernelGGL((attention_pp_kernel<T, HD, 2, KIND>), grid, dim3(512), 0, s, q, q_bs, q_ss, s0, s1, S, H,
+                         c_log2, o, o_bs, o_ss);
+    else
+      hipLaunchKernelGGL((attention_pp_kernel<T, HD, 1, KIND>), grid, dim3(512), 0, s, q, q_bs, q_ss, s0, s1, S, H,
+                         c_log2, o, o_bs, o_ss);
+  } else {
+    dim3 grid((unsigned)ceil_div(S, 128), (unsigned)H, (unsigned)B);
+    if (nstreams == 2)
+      hipLaunchKernelGGL((attention_kernel<T, HD, 2, KIND>), grid, dim3(256), 0, s, q, q_bs, q_ss, s0, s1, S, H,
+                         c_log2, o, o_bs, o_ss);
+    else
+      hipLaunchKernelGGL((attention_kernel<T, HD, 1, KIND>), grid, dim3(256), 0, s, q, q_bs, q_ss, s0, s1, S, H,
+                         c_log2, o, o_bs, o_ss);
+  }
   return hipGetLastError();
 }
 
