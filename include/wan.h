@@ -194,7 +194,7 @@ int wan_cross_kv_fwd(const wan_block_cfg* cfg, const wan_cross_kv_weights* w, co
  *   x += gate2 * FFN(LN(x)(1 + scale2) + shift2),  FFN = Linear -> GELU -> Linear
  * e0 [B, 6, dim] float32 from wan_time_embed; kv from wan_cross_kv_fwd.  LN has no affine (except the
  * cross-attention pre-norm), eps = cfg->ln_eps; attention scale 1/sqrt(head_dim).
- * Workspace: wan_dit_block_workspace_bytes() (about B*S*(6*dim + ffn_dim) dtype elements). */
+ * Workspace: wan_dit_block_workspace_bytes() (about B*S*(5*dim + ffn_dim) dtype elements). */
 size_t wan_dit_block_workspace_bytes(const wan_block_cfg* cfg, wan_grid grid, int32_t B);
 int wan_dit_block_fwd(const wan_block_cfg* cfg, const wan_block_weights* w, wan_grid grid, int32_t B, float* x,
                       const float* e0, const wan_cross_kv* kv, void* ws, size_t ws_bytes, wan_stream_t stream);
@@ -227,9 +227,11 @@ int wan_attention_fwd(int32_t dtype, const void* q, const void* k, const void* v
  * bracketed by hipEventRecord(start[i]) / hipEventRecord(stop[i]) on the launch stream, and tags[i]
  * receives its wan_kernel_id, until capacity pairs are used.  The arrays must stay valid until
  * wan_profile_end, which returns the number of pairs recorded and disables recording.  Process-wide
- * state, not thread-safe; calls that overlap on several threads must not use it. */
+ * state, not thread-safe; calls that overlap on several threads must not use it.
+ * Ids name the block's launches in order; WAN_K_VT_TAIL is the zero fill of the padded keys of V^T
+ * (the Q/K/V GEMM writes V^T itself). */
 typedef enum {
-  WAN_K_LN1 = 0, WAN_K_QKV_GEMM = 1, WAN_K_QK_NORM_ROPE = 2, WAN_K_V_TRANSPOSE = 3, WAN_K_SELF_ATTN = 4,
+  WAN_K_LN1 = 0, WAN_K_QKV_GEMM = 1, WAN_K_QK_NORM_ROPE = 2, WAN_K_VT_TAIL = 3, WAN_K_SELF_ATTN = 4,
   WAN_K_O_GEMM = 5, WAN_K_LN3 = 6, WAN_K_CROSS_Q_GEMM = 7, WAN_K_CROSS_ATTN = 8, WAN_K_CROSS_O_GEMM = 9,
   WAN_K_LN2 = 10, WAN_K_FFN1_GEMM = 11, WAN_K_FFN2_GEMM = 12
 } wan_kernel_id;

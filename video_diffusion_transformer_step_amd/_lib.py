@@ -240,7 +240,7 @@ def attention_fwd(q, k, v, grid, o, ws, rope_theta=10000.0, stream=None):
                                    _stream(stream)), "wan_attention_fwd")
 
 
-KERNEL_IDS = ["ln1", "qkv_gemm", "qk_norm_rope", "v_transpose", "self_attn", "o_gemm", "ln3", "cross_q_gemm",
+KERNEL_IDS = ["ln1", "qkv_gemm", "qk_norm_rope", "vt_tail", "self_attn", "o_gemm", "ln3", "cross_q_gemm",
               "cross_attn", "cross_o_gemm", "ln2", "ffn1_gemm", "ffn2_gemm"]
 
 

@@ -67,6 +67,44 @@ struct EpiStore {
   }
 };
 
+// Q/K/V projection: columns [0, vcol0) (q, k) are stored row-major like EpiStore; columns >= vcol0
+// (v) go straight to the per-head transposed layout V^T[b, h, d, pos] the attention kernels read
+// (pos = token within its batch row, bf16 keys permuted within 16-key groups: position p holds key
+// p with bits 2 and 3 swapped).
+template <typename T>
+struct EpiQKV {
+  T* out;
+  int64_t ldo;
+  const float* bias;
+  T* vt;
+  int vcol0, S, H, hd, Spad;
+  __device__ __forceinline__ void operator()(int m, int n, float4 v) const {
+    if (bias) {
+      const float4 b = *reinterpret_cast<const float4*>(bias + n);
+      v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+    }
+    if (n < vcol0) {
+      T* p = out + (int64_t)m * ldo + n;
+      if constexpr (sizeof(T) == 2) {
+        bf16x4 o;
+        o[0] = (bf16)v.x; o[1] = (bf16)v.y; o[2] = (bf16)v.z; o[3] = (bf16)v.w;
+        *reinterpret_cast<bf16x4*>(p) = o;
+      } else {
+        *reinterpret_cast<float4*>(p) = v;
+      }
+    } else {
+      const int nn = n - vcol0, h = nn / hd, d = nn - h * hd;  // 4 channels d..d+3 of head h
+      const int b = m / S, pos = m - b * S;
+      const int pp = sizeof(T) == 2 ? ((pos & ~12) | ((pos & 4) << 1) | ((pos & 8) >> 1)) : pos;
+      T* p = vt + (((int64_t)b * H + h) * hd + d) * Spad + pp;
+      p[0] = from_f32<T>(v.x);
+      p[Spad] = from_f32<T>(v.y);
+      p[2 * (int64_t)Spad] = from_f32<T>(v.z);
+      p[3 * (int64_t)Spad] = from_f32<T>(v.w);
+    }
+  }
+};
+
 struct EpiResidual {
   float* x;
   int64_t ldx;
@@ -502,6 +540,13 @@ hipError_t gemm_store(const T* A, int64_t lda, const T* W, int64_t ldw, int M, i
 }
 
 template <typename T>
+hipError_t gemm_qkv(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int dim, int K, const float* bias,
+                    T* qk, int64_t ldo, T* vt, int S, int H, int hd, int Spad, hipStream_t s) {
+  if (hd % 4 != 0) return hipErrorInvalidValue;
+  return run_gemm<T>(A, lda, W, ldw, M, 3 * dim, K, EpiQKV<T>{qk, ldo, bias, vt, 2 * dim, S, H, hd, Spad}, s);
+}
+
+template <typename T>
 hipError_t gemm_residual(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const float* bias,
                          const float* e0, const float* mb, int chunk, int S, float* x, int64_t ldx, hipStream_t s) {
   EpiResidual epi{x, ldx, bias, e0, mb, chunk, S, N};
@@ -532,6 +577,10 @@ template hipError_t gemm_store<bf16, bf16>(const bf16*, int64_t, const bf16*, in
                                            int, bf16*, int64_t, hipStream_t);
 template hipError_t gemm_store<bf16, float>(const bf16*, int64_t, const bf16*, int64_t, int, int, int,
                                             const float*, int, float*, int64_t, hipStream_t);
+template hipError_t gemm_qkv<float>(const float*, int64_t, const float*, int64_t, int, int, int, const float*, float*,
+                                    int64_t, float*, int, int, int, int, hipStream_t);
+template hipError_t gemm_qkv<bf16>(const bf16*, int64_t, const bf16*, int64_t, int, int, int, const float*, bf16*,
+                                   int64_t, bf16*, int, int, int, int, hipStream_t);
 template hipError_t gemm_residual<float>(const float*, int64_t, const float*, int64_t, int, int, int, const float*,
                                          const float*, const float*, int, int, float*, int64_t, hipStream_t);
 template hipError_t gemm_residual<bf16>(const bf16*, int64_t, const bf16*, int64_t, int, int, int, const float*,

@@ -137,6 +137,16 @@ __global__ __launch_bounds__(256) void transpose_heads_kernel(const T* __restric
   }
 }
 
+template <typename T>
+__global__ __launch_bounds__(256) void vt_tail_zero_kernel(T* __restrict__ vt, int64_t rows, int S, int Spad) {
+  const int w = Spad - S;
+  const int64_t n = rows * w;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / w;
+    vt[r * Spad + S + (i - r * w)] = from_f32<T>(0.f);
+  }
+}
+
 inline unsigned grid_for(int64_t n, int per_thread = 1) {
   int64_t blocks = ceil_div(ceil_div(n, per_thread), 256);
   if (blocks > 65536) blocks = 65536;
@@ -189,6 +199,15 @@ hipError_t launch_transpose_heads(const T* v, int64_t ld, int64_t col0, int B, i
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_vt_tail_zero(T* vt, int64_t rows, int S, int Spad, hipStream_t s) {
+  if (Spad <= S || rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(vt_tail_zero_kernel<T>, dim3(grid_for(rows * (Spad - S))), dim3(256), 0, s, vt, rows, S, Spad);
+  return hipGetLastError();
+}
+
+template hipError_t launch_vt_tail_zero<float>(float*, int64_t, int, int, hipStream_t);
+template hipError_t launch_vt_tail_zero<bf16>(bf16*, int64_t, int, int, hipStream_t);
 template hipError_t launch_convert<float>(const float*, float*, int64_t, hipStream_t);
 template hipError_t launch_convert<bf16>(const float*, bf16*, int64_t, hipStream_t);
 template hipError_t launch_transpose_heads<float>(const float*, int64_t, int64_t, int, int, int, int, int, float*,

@@ -1,7 +1,8 @@
 // Row-wise normalisation kernels (HBM-bound): LayerNorm + adaLN modulation,
 // affine LayerNorm, the head's modulated LayerNorm, and the Q/K RMSNorm + gain +
-// 3D RoPE pass.  One 64-lane wave owns one token row; the row stays in registers
-// between the statistics and the write.
+// 3D RoPE pass.  A 64-lane wave owns a few consecutive token rows, one at a time; a
+// row stays in registers between the statistics and the write, and per-channel
+// parameters are kept in registers across the wave's rows.
 #include "wan_internal.h"
 
 namespace wan {
@@ -23,68 +24,109 @@ template <> __device__ __forceinline__ void store4<bf16>(bf16* p, float a, float
   *reinterpret_cast<bf16x4*>(p) = v;
 }
 
+constexpr int LN_ROWS = 4;  // rows per wave: the per-channel modulation is loaded once per wave (dim <= 3072)
+
 // LayerNorm (biased variance, no affine) then modulation; see launch_ln_mod in wan_internal.h.
 // "图解 Wan2.1 I2V" §5.2: x' = norm(x) * (1 + scale) + shift; the cross-attention pre-norm (mode 1)
-// and the head (mode 2, §5.5) reuse the same row statistics.
-template <typename T>
+// and the head (mode 2, §5.5) reuse the same row statistics.  A wave normalises LN_ROWS
+// consecutive rows; for rows of up to 3072 channels the (shift, 1 + scale) vectors of its lanes'
+// channels are formed once and re-formed only when the batch row changes.  NC = float4 chunks per
+// lane (dim <= 256 NC).
+template <typename T, int NC>
 __global__ __launch_bounds__(256) void ln_mod_kernel(const float* __restrict__ x, int64_t rows, int dim, int S,
                                                       int mode, const float* __restrict__ p0,
                                                       const float* __restrict__ p1, int c_shift, int c_scale,
                                                       float eps, T* __restrict__ u) {
+  constexpr bool CACHE = NC <= 12;
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * LN_ROWS;
   const int n4 = dim >> 2;
-  const float4* xr = reinterpret_cast<const float4*>(x + row * dim);
-  float4 v[LN_MAX4];
-  float sum = 0.f;
-#pragma unroll
-  for (int i = 0; i < LN_MAX4; ++i) {
-    const int idx = i * 64 + lane;
-    if (idx < n4) {
-      v[i] = xr[idx];
-      sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+  float4 sh[CACHE ? NC : 1], sc[CACHE ? NC : 1];
+  // (shift, 1 + scale) of float4 chunk idx (channels 4 idx ..) for batch row b
+  auto modulation = [&](int64_t b, int idx, float4& vsh, float4& vsc) {
+    const int c = idx * 4;
+    if (mode == 0) {
+      const float4 es = *reinterpret_cast<const float4*>(p0 + (b * 6 + c_shift) * dim + c);
+      const float4 ms = *reinterpret_cast<const float4*>(p1 + (int64_t)c_shift * dim + c);
+      const float4 ec = *reinterpret_cast<const float4*>(p0 + (b * 6 + c_scale) * dim + c);
+      const float4 mc = *reinterpret_cast<const float4*>(p1 + (int64_t)c_scale * dim + c);
+      vsh = make_float4(es.x + ms.x, es.y + ms.y, es.z + ms.z, es.w + ms.w);
+      vsc = make_float4(1.f + (ec.x + mc.x), 1.f + (ec.y + mc.y), 1.f + (ec.z + mc.z), 1.f + (ec.w + mc.w));
+    } else if (mode == 1) {
+      vsc = *reinterpret_cast<const float4*>(p0 + c);
+      vsh = *reinterpret_cast<const float4*>(p1 + c);
+    } else {
+      const float4 h0 = *reinterpret_cast<const float4*>(p0 + c);
+      const float4 h1 = *reinterpret_cast<const float4*>(p0 + dim + c);
+      const float4 e = *reinterpret_cast<const float4*>(p1 + b * dim + c);
+      vsh = make_float4(h0.x + e.x, h0.y + e.y, h0.z + e.z, h0.w + e.w);
+      vsc = make_float4(1.f + (h1.x + e.x), 1.f + (h1.y + e.y), 1.f + (h1.z + e.z), 1.f + (h1.w + e.w));
     }
-  }
-  const float mean = wave_sum(sum) / (float)dim;
-  float sq = 0.f;
+  };
+  // rows are software-pipelined: the next row's loads are issued before this row's reductions
+  float4 vn[NC];
+  auto load_row = [&](int64_t row) {
+    const float4* xr = reinterpret_cast<const float4*>(x + row * dim);
 #pragma unroll
-  for (int i = 0; i < LN_MAX4; ++i) {
-    const int idx = i * 64 + lane;
-    if (idx < n4) {
-      const float a = v[i].x - mean, b = v[i].y - mean, c = v[i].z - mean, d = v[i].w - mean;
-      sq += (a * a + b * b) + (c * c + d * d);
+    for (int i = 0; i < NC; ++i) {
+      const int idx = i * 64 + lane;
+      if (idx < n4) vn[i] = xr[idx];
     }
-  }
-  const float rstd = 1.f / sqrtf(wave_sum(sq) / (float)dim + eps);
-  const int64_t b = row / S;
-  T* ur = u + row * dim;
+  };
+  if (row0 >= rows) return;
+  if constexpr (CACHE) load_row(row0);  // (wide rows: no registers to spare for the next row)
+  int64_t bcur = -1;
+  for (int rr = 0; rr < LN_ROWS; ++rr) {
+    const int64_t row = row0 + rr;
+    if (row >= rows) return;
+    if constexpr (!CACHE) load_row(row);
+    float4 v[NC];
 #pragma unroll
-  for (int i = 0; i < LN_MAX4; ++i) {
-    const int idx = i * 64 + lane;
-    if (idx < n4) {
-      const int c = idx * 4;
-      float n0 = (v[i].x - mean) * rstd, n1 = (v[i].y - mean) * rstd;
-      float n2 = (v[i].z - mean) * rstd, n3 = (v[i].w - mean) * rstd;
-      float4 sh, sc;
-      if (mode == 0) {
-        const float4 es = *reinterpret_cast<const float4*>(p0 + (b * 6 + c_shift) * dim + c);
-        const float4 ms = *reinterpret_cast<const float4*>(p1 + (int64_t)c_shift * dim + c);
-        const float4 ec = *reinterpret_cast<const float4*>(p0 + (b * 6 + c_scale) * dim + c);
-        const float4 mc = *reinterpret_cast<const float4*>(p1 + (int64_t)c_scale * dim + c);
-        sh = make_float4(es.x + ms.x, es.y + ms.y, es.z + ms.z, es.w + ms.w);
-        sc = make_float4(1.f + (ec.x + mc.x), 1.f + (ec.y + mc.y), 1.f + (ec.z + mc.z), 1.f + (ec.w + mc.w));
-      } else if (mode == 1) {
-        sc = *reinterpret_cast<const float4*>(p0 + c);
-        sh = *reinterpret_cast<const float4*>(p1 + c);
-      } else {
-        const float4 h0 = *reinterpret_cast<const float4*>(p0 + c);
-        const float4 h1 = *reinterpret_cast<const float4*>(p0 + dim + c);
-        const float4 e = *reinterpret_cast<const float4*>(p1 + b * dim + c);
-        sh = make_float4(h0.x + e.x, h0.y + e.y, h0.z + e.z, h0.w + e.w);
-        sc = make_float4(1.f + (h1.x + e.x), 1.f + (h1.y + e.y), 1.f + (h1.z + e.z), 1.f + (h1.w + e.w));
+    for (int i = 0; i < NC; ++i) v[i] = vn[i];
+    if (CACHE && rr + 1 < LN_ROWS && row + 1 < rows) load_row(row + 1);
+    const int64_t b = row / S;
+    if (CACHE && b != bcur) {  // modulation of this batch row (uniform branch)
+      bcur = b;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int idx = i * 64 + lane;
+        if (idx < n4) modulation(b, idx, sh[CACHE ? i : 0], sc[CACHE ? i : 0]);
       }
-      store4<T>(ur + c, fmaf(n0, sc.x, sh.x), fmaf(n1, sc.y, sh.y), fmaf(n2, sc.z, sh.z), fmaf(n3, sc.w, sh.w));
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int idx = i * 64 + lane;
+      if (idx < n4) sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    }
+    const float mean = wave_sum(sum) / (float)dim;
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int idx = i * 64 + lane;
+      if (idx < n4) {
+        const float a = v[i].x - mean, bb = v[i].y - mean, c = v[i].z - mean, d = v[i].w - mean;
+        sq += (a * a + bb * bb) + (c * c + d * d);
+      }
+    }
+    const float rstd = 1.f / sqrtf(wave_sum(sq) / (float)dim + eps);
+    T* ur = u + row * dim;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int idx = i * 64 + lane;
+      if (idx < n4) {
+        float4 vsh, vsc;
+        if constexpr (CACHE) {
+          vsh = sh[i];
+          vsc = sc[i];
+        } else {
+          modulation(b, idx, vsh, vsc);
+        }
+        const float n0 = (v[i].x - mean) * rstd, n1 = (v[i].y - mean) * rstd;
+        const float n2 = (v[i].z - mean) * rstd, n3 = (v[i].w - mean) * rstd;
+        store4<T>(ur + idx * 4, fmaf(n0, vsc.x, vsh.x), fmaf(n1, vsc.y, vsh.y), fmaf(n2, vsc.z, vsh.z),
+                  fmaf(n3, vsc.w, vsh.w));
+      }
     }
   }
 }
@@ -114,78 +156,118 @@ template <> __device__ __forceinline__ void store8<float>(float* p, const float 
 }
 
 constexpr int QK_MAX8 = 12;  // 8-element chunks per lane: dim <= 12 * 512 = 6144
+constexpr int QK_ROWS = 2;   // token rows per wave
 
-// One row of q or k: optional RMSNorm over the full row ("图解 Wan2.1 I2V" §5.3 ①), gain, then
-// 3D RoPE per head (§5.3 ②): head channels split into time / height / width segments of
+// 3D RoPE ("图解 Wan2.1 I2V" §5.3 ②): head channels split into time / height / width segments of
 // sizes hd - 4*(hd/6), 2*(hd/6), 2*(hd/6); pair (2m, 2m+1) of a segment of width n rotates by
-// pos * theta^(-2m/n), pos being the token's frame / row / column index.
-template <typename T>
-__device__ __forceinline__ void norm_rope_row(const T* __restrict__ in, T* __restrict__ out, int dim, int hd,
-                                              const float* __restrict__ g, int do_norm, float eps,
-                                              float log2_theta, int f, int i, int j, int lane) {
-  float v[QK_MAX8][8];
-  float sq = 0.f;
-#pragma unroll
-  for (int c = 0; c < QK_MAX8; ++c) {
-    const int c0 = c * 512 + lane * 8;
-    if (c0 < dim) {
-      load8<T>(in + c0, v[c]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sq += v[c][e] * v[c][e];
-    }
-  }
-  float r = 1.f;
-  if (do_norm) r = 1.f / sqrtf(wave_sum(sq) / (float)dim + eps);
+// pos * theta^(-2m/n), pos being the token's frame / row / column index.  A lane's 8-channel
+// chunks all sit at the same offset within their heads (hd divides 512), so its 4 pairs' angles
+// serve every chunk of the row and both q and k.
+__device__ __forceinline__ void rope_angles(int d0, int hd, float log2_theta, int f, int i, int j, float (&cs)[4],
+                                            float (&sn)[4]) {
   const int q6 = hd / 6;
   const int dT = hd - 4 * q6, dH = 2 * q6;
 #pragma unroll
-  for (int c = 0; c < QK_MAX8; ++c) {
+  for (int p = 0; p < 4; ++p) {
+    const int d = d0 + 2 * p;
+    int m, n, pos;
+    if (d < dT) {
+      m = d >> 1; n = dT; pos = f;
+    } else if (d < dT + dH) {
+      m = (d - dT) >> 1; n = dH; pos = i;
+    } else {
+      m = (d - dT - dH) >> 1; n = dH; pos = j;
+    }
+    const float freq = exp2f(-(float)(2 * m) / (float)n * log2_theta);
+    sincosf((float)pos * freq, &sn[p], &cs[p]);
+  }
+}
+
+// The q and k rows of one token: RMSNorm over the full row ("图解 Wan2.1 I2V" §5.3 ①, optional), the
+// gains (this lane's in gq / gk), then the rotation by the lane's pair angles.  Both rows are loaded
+// before either reduction so their loads are in flight together.
+template <typename T, int NC8>
+__device__ __forceinline__ void norm_rope_qk(const T* __restrict__ qi, const T* __restrict__ ki, T* __restrict__ qo,
+                                             T* __restrict__ ko, int dim, const float (&gq)[NC8][8],
+                                             const float (&gk)[NC8][8], int do_norm, float eps, const float (&cs)[4],
+                                             const float (&sn)[4], int lane) {
+  float vq[NC8][8], vk[NC8][8];
+#pragma unroll
+  for (int c = 0; c < NC8; ++c) {
     const int c0 = c * 512 + lane * 8;
     if (c0 < dim) {
-      float o[8];
+      load8<T>(qi + c0, vq[c]);
+      load8<T>(ki + c0, vk[c]);
+    }
+  }
+  float sq = 0.f, sk = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC8; ++c) {
+    const int c0 = c * 512 + lane * 8;
+    if (c0 < dim) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sq += vq[c][e] * vq[c][e];
+        sk += vk[c][e] * vk[c][e];
+      }
+    }
+  }
+  float rq = 1.f, rk = 1.f;
+  if (do_norm) {
+    rq = 1.f / sqrtf(wave_sum(sq) / (float)dim + eps);
+    rk = 1.f / sqrtf(wave_sum(sk) / (float)dim + eps);
+  }
+#pragma unroll
+  for (int c = 0; c < NC8; ++c) {
+    const int c0 = c * 512 + lane * 8;
+    if (c0 < dim) {
+      float oq[8], ok[8];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const int ch = c0 + 2 * p;
-        const int d = ch % hd;
-        int m, n, pos;
-        if (d < dT) {
-          m = d >> 1; n = dT; pos = f;
-        } else if (d < dT + dH) {
-          m = (d - dT) >> 1; n = dH; pos = i;
-        } else {
-          m = (d - dT - dH) >> 1; n = dH; pos = j;
-        }
-        float a = v[c][2 * p] * r, b = v[c][2 * p + 1] * r;
-        if (g) {
-          a *= g[ch];
-          b *= g[ch + 1];
-        }
-        const float freq = exp2f(-(float)(2 * m) / (float)n * log2_theta);
-        float sn, cs;
-        sincosf((float)pos * freq, &sn, &cs);
-        o[2 * p] = a * cs - b * sn;
-        o[2 * p + 1] = a * sn + b * cs;
+        const float a = vq[c][2 * p] * rq * gq[c][2 * p], b = vq[c][2 * p + 1] * rq * gq[c][2 * p + 1];
+        oq[2 * p] = a * cs[p] - b * sn[p];
+        oq[2 * p + 1] = a * sn[p] + b * cs[p];
+        const float ak = vk[c][2 * p] * rk * gk[c][2 * p], bk = vk[c][2 * p + 1] * rk * gk[c][2 * p + 1];
+        ok[2 * p] = ak * cs[p] - bk * sn[p];
+        ok[2 * p + 1] = ak * sn[p] + bk * cs[p];
       }
-      store8<T>(out + c0, o);
+      store8<T>(qo + c0, oq);
+      store8<T>(ko + c0, ok);
     }
   }
 }
 
-template <typename T>
+// NC8 = 8-channel chunks per lane (dim <= 512 NC8).
+template <typename T, int NC8>
 __global__ __launch_bounds__(256) void qk_norm_rope_kernel(const T* q_in, const T* k_in, int64_t ld_in, T* q_out,
                                                             T* k_out, int64_t ld_out, int64_t rows, int S, int Hp,
                                                             int Wp, int dim, int hd, const float* __restrict__ gq,
                                                             const float* __restrict__ gk, int do_norm, float eps,
                                                             float log2_theta) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int s = (int)(row % S);
-  const int jj = s % Wp, ii = (s / Wp) % Hp, ff = s / (Wp * Hp);
-  norm_rope_row<T>(q_in + row * ld_in, q_out + row * ld_out, dim, hd, gq, do_norm, eps, log2_theta, ff, ii, jj,
-                   lane);
-  norm_rope_row<T>(k_in + row * ld_in, k_out + row * ld_out, dim, hd, gk, do_norm, eps, log2_theta, ff, ii, jj,
-                   lane);
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * QK_ROWS;
+  if (row0 >= rows) return;
+  float gql[NC8][8], gkl[NC8][8];
+#pragma unroll
+  for (int c = 0; c < NC8; ++c) {
+    const int c0 = c * 512 + lane * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      gql[c][e] = (c0 < dim && gq) ? gq[c0 + e] : 1.f;
+      gkl[c][e] = (c0 < dim && gk) ? gk[c0 + e] : 1.f;
+    }
+  }
+  const int d0 = (lane * 8) % hd;
+  for (int rr = 0; rr < QK_ROWS; ++rr) {
+    const int64_t row = row0 + rr;
+    if (row >= rows) return;
+    const int s = (int)(row % S);
+    const int jj = s % Wp, ii = (s / Wp) % Hp, ff = s / (Wp * Hp);
+    float cs[4], sn[4];
+    rope_angles(d0, hd, log2_theta, ff, ii, jj, cs, sn);
+    norm_rope_qk<T, NC8>(q_in + row * ld_in, k_in + row * ld_in, q_out + row * ld_out, k_out + row * ld_out, dim,
+                         gql, gkl, do_norm, eps, cs, sn, lane);
+  }
 }
 
 }  // namespace
@@ -195,8 +277,16 @@ hipError_t launch_ln_mod(const float* x, int64_t rows, int dim, int S, int mode,
                          int c_shift, int c_scale, float eps, T* u, hipStream_t s) {
   if (dim % 4 != 0 || dim > LN_MAX4 * 256) return hipErrorInvalidValue;
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(ln_mod_kernel<T>, dim3((unsigned)ceil_div(rows, 4)), dim3(256), 0, s, x, rows, dim, S, mode,
-                     p0, p1, c_shift, c_scale, eps, u);
+  const dim3 grid((unsigned)ceil_div(rows, 4 * LN_ROWS));
+  if (dim <= 6 * 256)
+    hipLaunchKernelGGL((ln_mod_kernel<T, 6>), grid, dim3(256), 0, s, x, rows, dim, S, mode, p0, p1, c_shift, c_scale,
+                       eps, u);
+  else if (dim <= 12 * 256)
+    hipLaunchKernelGGL((ln_mod_kernel<T, 12>), grid, dim3(256), 0, s, x, rows, dim, S, mode, p0, p1, c_shift,
+                       c_scale, eps, u);
+  else
+    hipLaunchKernelGGL((ln_mod_kernel<T, LN_MAX4>), grid, dim3(256), 0, s, x, rows, dim, S, mode, p0, p1, c_shift,
+                       c_scale, eps, u);
   return hipGetLastError();
 }
 
@@ -205,12 +295,21 @@ hipError_t launch_qk_norm_rope(const T* q_in, const T* k_in, int64_t ld_in, T* q
                                int B, int T_, int Hp, int Wp, int heads, int hd, const float* gq, const float* gk,
                                int do_norm, float eps, float theta, hipStream_t s) {
   const int dim = heads * hd;
-  if (dim % 8 != 0 || dim > QK_MAX8 * 512 || hd % 8 != 0) return hipErrorInvalidValue;
+  if (dim % 8 != 0 || dim > QK_MAX8 * 512 || hd % 8 != 0 || 512 % hd != 0) return hipErrorInvalidValue;
   const int S = T_ * Hp * Wp;
   const int64_t rows = (int64_t)B * S;
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(qk_norm_rope_kernel<T>, dim3((unsigned)ceil_div(rows, 4)), dim3(256), 0, s, q_in, k_in, ld_in,
-                     q_out, k_out, ld_out, rows, S, Hp, Wp, dim, hd, gq, gk, do_norm, eps, log2f(theta));
+  const dim3 grid((unsigned)ceil_div(rows, 4 * QK_ROWS));
+  const float l2t = log2f(theta);
+  if (dim <= 3 * 512)
+    hipLaunchKernelGGL((qk_norm_rope_kernel<T, 3>), grid, dim3(256), 0, s, q_in, k_in, ld_in, q_out, k_out, ld_out,
+                       rows, S, Hp, Wp, dim, hd, gq, gk, do_norm, eps, l2t);
+  else if (dim <= 6 * 512)
+    hipLaunchKernelGGL((qk_norm_rope_kernel<T, 6>), grid, dim3(256), 0, s, q_in, k_in, ld_in, q_out, k_out, ld_out,
+                       rows, S, Hp, Wp, dim, hd, gq, gk, do_norm, eps, l2t);
+  else
+    hipLaunchKernelGGL((qk_norm_rope_kernel<T, QK_MAX8>), grid, dim3(256), 0, s, q_in, k_in, ld_in, q_out, k_out,
+                       ld_out, rows, S, Hp, Wp, dim, hd, gq, gk, do_norm, eps, l2t);
   return hipGetLastError();
 }
 

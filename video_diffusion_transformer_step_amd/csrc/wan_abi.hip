@@ -135,7 +135,7 @@ size_t block_plan(const wan_block_cfg& c, const wan_grid& g, int B, char* base, 
   Carve cv{base};
   BlockWs<T> w;
   w.u = cv.take<T>(BS * dim);
-  w.qkv = cv.take<T>(BS * 3 * dim);
+  w.qkv = cv.take<T>(BS * 2 * dim);  // q | k per token (v goes to vt)
   w.vt = cv.take<T>((size_t)B * dim * pad64(S));
   w.o = cv.take<T>(BS * dim);
   w.h = cv.take<T>(BS * c.ffn_dim);
@@ -153,12 +153,14 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
   const float scale = 1.f / sqrtf((float)hd);
   // self-attention branch
   PROF_TRY(WAN_K_LN1, launch_ln_mod<T>(x, BS, dim, S, 0, e0, W.mod_bias, 0, 1, c.ln_eps, w.u, st));
-  PROF_TRY(WAN_K_QKV_GEMM, (gemm_store<T, T>(w.u, dim, (const T*)W.wqkv, dim, BS, 3 * dim, dim, W.bqkv, ACT_NONE, w.qkv, 3 * dim, st)));
-  PROF_TRY(WAN_K_QK_NORM_ROPE, launch_qk_norm_rope<T>(w.qkv, w.qkv + dim, 3 * dim, w.qkv, w.qkv + dim, 3 * dim, B, g.T, g.Hp, g.Wp, H, hd,
+  // q, k -> qkv[:, 0 .. 2 dim) (row stride 2 dim); v -> V^T directly
+  PROF_TRY(WAN_K_VT_TAIL, launch_vt_tail_zero<T>(w.vt, (int64_t)B * dim, S, Spad, st));
+  PROF_TRY(WAN_K_QKV_GEMM, gemm_qkv<T>(w.u, dim, (const T*)W.wqkv, dim, BS, dim, dim, W.bqkv, w.qkv, 2 * dim, w.vt, S, H,
+                                       hd, Spad, st));
+  PROF_TRY(WAN_K_QK_NORM_ROPE, launch_qk_norm_rope<T>(w.qkv, w.qkv + dim, 2 * dim, w.qkv, w.qkv + dim, 2 * dim, B, g.T, g.Hp, g.Wp, H, hd,
                                  W.gq, W.gk, 1, c.rms_eps, c.rope_theta, st));
-  PROF_TRY(WAN_K_V_TRANSPOSE, launch_transpose_heads<T>(w.qkv, 3 * dim, 2 * dim, B, S, H, hd, Spad, w.vt, st));
-  KVStream self{w.qkv + dim, (int64_t)S * 3 * dim, 3 * dim, w.vt, S, Spad};
-  PROF_TRY(WAN_K_SELF_ATTN, launch_attention<T>(w.qkv, (int64_t)S * 3 * dim, 3 * dim, self, self, 1, B, S, H, hd, scale, w.o,
+  KVStream self{w.qkv + dim, (int64_t)S * 2 * dim, 2 * dim, w.vt, S, Spad};
+  PROF_TRY(WAN_K_SELF_ATTN, launch_attention<T>(w.qkv, (int64_t)S * 2 * dim, 2 * dim, self, self, 1, B, S, H, hd, scale, w.o,
                               (int64_t)S * dim, dim, 0, st));
   PROF_TRY(WAN_K_O_GEMM, gemm_residual<T>(w.o, dim, (const T*)W.wo, dim, BS, dim, dim, W.bo, e0, W.mod_bias, 2, S, x, dim, st));
   // cross-attention branch (no adaLN, no RoPE)

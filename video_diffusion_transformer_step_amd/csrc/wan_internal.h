@@ -27,6 +27,10 @@ template <typename T>
 hipError_t launch_transpose_heads(const T* v, int64_t ld, int64_t col0, int B, int S, int H, int hd, int Spad,
                                   T* vt, hipStream_t s);
 
+// Zero V^T[r, S .. Spad) for rows r < rows (row stride Spad): the padded keys of the last tile.
+template <typename T>
+hipError_t launch_vt_tail_zero(T* vt, int64_t rows, int S, int Spad, hipStream_t s);
+
 // ---- norms (norm.hip) -------------------------------------------------------
 // Row-wise LayerNorm of fp32 x [rows, dim] followed by one of:
 //  mode 0 (adaLN):   u = LN(x) * (1 + (e0[b][c_scale] + mb[c_scale])) + (e0[b][c_shift] + mb[c_shift])
@@ -50,6 +54,12 @@ hipError_t launch_qk_norm_rope(const T* q_in, const T* k_in, int64_t ld_in, T* q
 template <typename T, typename OutT>
 hipError_t gemm_store(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const float* bias,
                       int act, OutT* out, int64_t ldo, hipStream_t s);
+// Q/K/V projection (N = 3 dim): q, k columns to qk[m, 0 .. 2 dim) (row stride ldo), v columns to
+// V^T [B, H, hd, Spad] (keys permuted within 16-key groups for bf16; see launch_transpose_heads);
+// m = b * S + pos.  The V^T tail pos in [S, Spad) is not written.
+template <typename T>
+hipError_t gemm_qkv(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int dim, int K, const float* bias,
+                    T* qk, int64_t ldo, T* vt, int S, int H, int hd, int Spad, hipStream_t s);
 template <typename T>
 hipError_t gemm_residual(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const float* bias,
                          const float* e0, const float* mb, int chunk, int S, float* x, int64_t ldx, hipStream_t s);
