@@ -21,8 +21,8 @@
 //    reads bias / gate / residual and writes results 4 columns (8 or 16 bytes)
 //    at a time;
 //  * the 1D grid is remapped so each XCD (blockIdx % 8) receives a contiguous run
-//    of tiles, grouped GROUP_M row-tiles at a time, so concurrent tiles share A
-//    rows and W columns in that XCD's L2;
+//    of tiles, grouped a few row-tiles at a time (group_m), so concurrent tiles
+//    share A rows and W columns in that XCD's L2;
 //  * k is accumulated in increasing order in every configuration, so all tile
 //    shapes give bitwise-identical results;
 //  * epilogues fuse the bias, GELU / SiLU, the output cast and the adaLN-gated
@@ -33,10 +33,22 @@ namespace wan {
 
 namespace {
 
-constexpr int GROUP_M = 8;
+
+// Exact GELU x * Phi(x) = x/2 (1 + erf(x / sqrt 2)), with erf from Abramowitz & Stegun, Handbook of
+// Mathematical Functions, formula 7.1.26 (absolute error <= 1.5e-7): for z >= 0,
+// erf(z) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2), t = 1 / (1 + p z).
+__device__ __forceinline__ float gelu_erf(float x) {
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.f));
+  const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f),
+                                      -0.284496736f), 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);  // exp(-z^2); 0 for large z
+  const float erf_abs = 1.f - poly * e;
+  return 0.5f * x * (1.f + copysignf(erf_abs, x));
+}
 
 __device__ __forceinline__ float apply_act(float v, int act) {
-  if (act == ACT_GELU) return 0.5f * v * (1.f + erff(v * 0.70710678118654752f));
+  if (act == ACT_GELU) return gelu_erf(v);
   if (act == ACT_SILU) return v / (1.f + __expf(-v));
   return v;
 }
@@ -132,25 +144,31 @@ struct EpiResidual {
   }
 };
 
-// Map a linear block id to (tile_m, tile_n): XCD-contiguous runs, then GROUP_M-row groups.
-__device__ __forceinline__ void tile_coords(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
+// Map a linear block id to (tile_m, tile_n): XCD-contiguous runs, then groups of gm row-tiles
+// (column tiles vary slowest inside a group).
+__device__ __forceinline__ void tile_coords(int id, int tiles_m, int tiles_n, int gm, int& tm, int& tn) {
   const int n = tiles_m * tiles_n;
   const int q = n >> 3, r = n & 7;
   const int xcd = id & 7, k = id >> 3;
   const int t = xcd * q + min(xcd, r) + k;  // bijection on [0, n)
-  const int per_group = GROUP_M * tiles_n;
+  const int per_group = gm * tiles_n;
   const int g = t / per_group;
-  const int first_m = g * GROUP_M;
-  const int gsz = min(tiles_m - first_m, GROUP_M);
+  const int first_m = g * gm;
+  const int gsz = min(tiles_m - first_m, gm);
   const int w = t - g * per_group;
   tm = first_m + w % gsz;
   tn = w / gsz;
 }
 
+// Row-group size of the tile order (measured on the block's shapes): wide products (>= 32 column
+// tiles) share weights best in groups of 4, long-K products in groups of 2, the rest in groups of 8.
+inline int group_m(int tiles_n, int K) { return tiles_n >= 32 ? 4 : (K >= 4096 ? 2 : 8); }
+
 template <typename T, int BM, int BN, int WM, int WN, class Epi>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restrict__ A, int64_t lda,
                                                                const T* __restrict__ W, int64_t ldw, int M,
-                                                               int N, int K, int tiles_m, int tiles_n, Epi epi) {
+                                                               int N, int K, int tiles_m, int tiles_n, int gm,
+                                                               Epi epi) {
   constexpr int NT = WM * WN * 64;
   constexpr int E16 = dtype_traits<T>::per16;  // elements per 16 bytes
   constexpr int BK = 8 * E16;                  // 128 bytes of K per step
@@ -164,7 +182,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restric
   T* smem = reinterpret_cast<T*>(smem_raw);
 
   int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  tile_coords(blockIdx.x, tiles_m, tiles_n, gm, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -383,7 +401,8 @@ __device__ __forceinline__ void lds_gemm_step(const LdsCopyPlan<BM, BN, BK, WM *
 template <int BM, int BN, int BK, int ST, int WM, int WN, class Epi>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(const bf16* __restrict__ A, int64_t lda,
                                                                 const bf16* __restrict__ W, int64_t ldw, int M,
-                                                                int N, int K, int tiles_m, int tiles_n, Epi epi) {
+                                                                int N, int K, int tiles_m, int tiles_n, int gm,
+                                                               Epi epi) {
   constexpr int NW = WM * WN;
   using C = LdsGemmCfg<BM, BN, BK, NW>;
   constexpr int FM = BM / WM / 32, FN = BN / WN / 32;
@@ -397,7 +416,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(const bf16* __res
   const LdsSlots<BM, BN, BK, ST, WM, WN> sl{{(char*)a0, (char*)a1, (char*)a2, (char*)a3},
                                             {(char*)b0, (char*)b1, (char*)b2, (char*)b3}};
   int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  tile_coords(blockIdx.x, tiles_m, tiles_n, gm, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const LdsCopyPlan<BM, BN, BK, NW> cp(A, lda, W, ldw, m0, n0, M, N);
 
@@ -440,7 +459,7 @@ hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, in
                       hipStream_t s) {
   const int tm = (int)ceil_div(M, BM), tn = (int)ceil_div(N, BN);
   hipLaunchKernelGGL((gemm_lds_kernel<BM, BN, BK, ST, WM, WN, Epi>), dim3((unsigned)(tm * tn)), dim3(WM * WN * 64),
-                     0, s, A, lda, W, ldw, M, N, K, tm, tn, epi);
+                     0, s, A, lda, W, ldw, M, N, K, tm, tn, group_m(tn, K), epi);
   return hipGetLastError();
 }
 
@@ -449,7 +468,7 @@ hipError_t launch_cfg(const T* A, int64_t lda, const T* W, int64_t ldw, int M, i
                       hipStream_t s) {
   const int tm = (int)ceil_div(M, BM), tn = (int)ceil_div(N, BN);
   hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, WM, WN, Epi>), dim3((unsigned)(tm * tn)), dim3(WM * WN * 64), 0,
-                     s, A, lda, W, ldw, M, N, K, tm, tn, epi);
+                     s, A, lda, W, ldw, M, N, K, tm, tn, group_m(tn, K), epi);
   return hipGetLastError();
 }
 

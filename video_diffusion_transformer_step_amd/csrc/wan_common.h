@@ -35,31 +35,56 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
 
-// Wave-wide (64 lanes) reductions.  The first four butterfly steps stay inside 16-lane rows and use
-// DPP lane permutes (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror), the
-// last two cross rows through ds_bpermute.  Every step pairs lanes symmetrically, so all lanes end
+// Wave-wide (64 lanes) reductions without LDS traffic.  The first four butterfly steps stay inside
+// 16-lane rows and use DPP lane permutes (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror, row_mirror); the last two exchange 16-lane rows and 32-lane halves with
+// v_permlane16_swap / v_permlane32_swap.  Every step pairs lanes symmetrically, so all lanes end
 // with the same bits.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
+// (a, b) = (v of this lane, v of lane ^ 16) or (v, v of lane ^ 32), in some order per lane.
+__device__ __forceinline__ void swap16(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+// v + (v of lane ^ 32), v max (v of lane ^ 32)
+__device__ __forceinline__ float half_sum(float v) {
+  float a, b;
+  swap32(v, a, b);
+  return a + b;
+}
+__device__ __forceinline__ float half_max(float v) {
+  float a, b;
+  swap32(v, a, b);
+  return fmaxf(a, b);
+}
 __device__ __forceinline__ float wave_sum(float v) {
+  float a, b;
   v += dpp_f32<0xB1>(v);
   v += dpp_f32<0x4E>(v);
   v += dpp_f32<0x141>(v);
   v += dpp_f32<0x140>(v);
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
+  swap16(v, a, b);
+  v = a + b;
+  return half_sum(v);
 }
 __device__ __forceinline__ float wave_max(float v) {
+  float a, b;
   v = fmaxf(v, dpp_f32<0xB1>(v));
   v = fmaxf(v, dpp_f32<0x4E>(v));
   v = fmaxf(v, dpp_f32<0x141>(v));
   v = fmaxf(v, dpp_f32<0x140>(v));
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  v = fmaxf(v, __shfl_xor(v, 32, 64));
-  return v;
+  swap16(v, a, b);
+  v = fmaxf(a, b);
+  return half_max(v);
 }
 
 // ---------------------------------------------------------------------------
