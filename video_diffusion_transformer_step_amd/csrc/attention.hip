@@ -18,10 +18,10 @@
 //    XOR-swizzled layouts that make every MFMA operand read a conflict-free 16-byte
 //    ds_read_b128.  V^T arrives with its keys permuted within each 16-key group
 //    ([0-3, 8-11, 4-7, 12-15]) so the 8 keys one MFMA lane-half needs are contiguous;
-//  * bf16 runs the ping-pong kernel: 8 waves (two per SIMD) share each K / V^T
-//    tile, and two groups of 4 waves run half a tile apart so that one wave of a
-//    SIMD does softmax + S(t+1) while the other does its PV products; fp32 runs a
-//    4-wave kernel with one barrier per tile;
+//  * bf16 self-attention runs the ping-pong kernel: 8 waves (two per SIMD) share
+//    each K / V^T tile, and two groups of 4 waves run half a tile apart so that one
+//    wave of a SIMD does softmax + S(t+1) while the other does its PV products;
+//    cross-attention and fp32 run a 4-wave kernel with one barrier per tile;
 //  * operand reads are software-pipelined in small scheduling regions
 //    (sched_barrier) so every LDS read has work to land behind;
 //  * the running maximum only moves when a score exceeds it by more than 2^8 (exp2
@@ -610,11 +610,12 @@ __global__ __launch_bounds__(512, 1) void attention_pp_kernel(const T* __restric
 #endif
 
 // KIND only separates the self-attention (0) and cross-attention (1) kernel symbols in profiles.
-// bf16 uses the ping-pong kernel (256 queries per workgroup), fp32 the four-wave kernel.
+// bf16 self-attention uses the ping-pong kernel (256 queries per workgroup); cross-attention (a few
+// hundred keys, where the per-stream prologue dominates) and fp32 use the four-wave kernel.
 template <typename T, int HD, int KIND>
 hipError_t launch_hd(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0, KVStream s1, int nstreams, int B, int S,
                      int H, float c_log2, T* o, int64_t o_bs, int64_t o_ss, hipStream_t s) {
-  if constexpr (sizeof(T) == 2 && WAN_ATTN_PP) {
+  if constexpr (sizeof(T) == 2 && WAN_ATTN_PP && KIND == 0) {
     dim3 grid((unsigned)ceil_div(S, 256), (unsigned)H, (unsigned)B);
     if (nstreams == 2)
       hipLaunchKernelGGL((attention_pp_kernel<T, HD, 2, KIND>), grid, dim3(512), 0, s, q, q_bs, q_ss, s0, s1, S, H,

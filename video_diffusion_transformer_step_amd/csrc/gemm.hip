@@ -133,10 +133,13 @@ struct EpiResidual {
     float4 r = *reinterpret_cast<const float4*>(p);
     if (e0) {
       const int b = m / S;
-      const float4 g = *reinterpret_cast<const float4*>(e0 + ((int64_t)b * 6 + chunk) * N + n);
-      const float4 h = *reinterpret_cast<const float4*>(mb + (int64_t)chunk * N + n);
-      r.x = fmaf(g.x + h.x, v.x, r.x); r.y = fmaf(g.y + h.y, v.y, r.y);
-      r.z = fmaf(g.z + h.z, v.z, r.z); r.w = fmaf(g.w + h.w, v.w, r.w);
+      float4 g = *reinterpret_cast<const float4*>(e0 + ((int64_t)b * 6 + chunk) * N + n);
+      if (mb) {
+        const float4 h = *reinterpret_cast<const float4*>(mb + (int64_t)chunk * N + n);
+        g.x += h.x; g.y += h.y; g.z += h.z; g.w += h.w;
+      }
+      r.x = fmaf(g.x, v.x, r.x); r.y = fmaf(g.y, v.y, r.y);
+      r.z = fmaf(g.z, v.z, r.z); r.w = fmaf(g.w, v.w, r.w);
     } else {
       r.x += v.x; r.y += v.y; r.z += v.z; r.w += v.w;
     }

@@ -137,6 +137,13 @@ __global__ __launch_bounds__(256) void transpose_heads_kernel(const T* __restric
   }
 }
 
+__global__ __launch_bounds__(256) void mod_combine_kernel(const float* __restrict__ e0, const float* __restrict__ mb,
+                                                          int B, int dim, float* __restrict__ mod) {
+  const int64_t n = (int64_t)B * 6 * dim;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    mod[i] = e0[i] + mb[i % (6 * (int64_t)dim)];
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void vt_tail_zero_kernel(T* __restrict__ vt, int64_t rows, int S, int Spad) {
   const int w = Spad - S;
@@ -196,6 +203,13 @@ hipError_t launch_transpose_heads(const T* v, int64_t ld, int64_t col0, int B, i
   if (hd > 128) return hipErrorInvalidValue;
   dim3 grid((unsigned)ceil_div(Spad, 64), (unsigned)H, (unsigned)B);
   hipLaunchKernelGGL(transpose_heads_kernel<T>, grid, dim3(256), 0, s, v, ld, col0, S, H, hd, Spad, vt);
+  return hipGetLastError();
+}
+
+hipError_t launch_mod_combine(const float* e0, const float* mb, int B, int dim, float* mod, hipStream_t s) {
+  const int64_t n = (int64_t)B * 6 * dim;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mod_combine_kernel, dim3(grid_for(n)), dim3(256), 0, s, e0, mb, B, dim, mod);
   return hipGetLastError();
 }
 

@@ -47,11 +47,16 @@ __global__ __launch_bounds__(256) void ln_mod_kernel(const float* __restrict__ x
     const int c = idx * 4;
     if (mode == 0) {
       const float4 es = *reinterpret_cast<const float4*>(p0 + (b * 6 + c_shift) * dim + c);
-      const float4 ms = *reinterpret_cast<const float4*>(p1 + (int64_t)c_shift * dim + c);
       const float4 ec = *reinterpret_cast<const float4*>(p0 + (b * 6 + c_scale) * dim + c);
-      const float4 mc = *reinterpret_cast<const float4*>(p1 + (int64_t)c_scale * dim + c);
-      vsh = make_float4(es.x + ms.x, es.y + ms.y, es.z + ms.z, es.w + ms.w);
-      vsc = make_float4(1.f + (ec.x + mc.x), 1.f + (ec.y + mc.y), 1.f + (ec.z + mc.z), 1.f + (ec.w + mc.w));
+      if (p1) {
+        const float4 ms = *reinterpret_cast<const float4*>(p1 + (int64_t)c_shift * dim + c);
+        const float4 mc = *reinterpret_cast<const float4*>(p1 + (int64_t)c_scale * dim + c);
+        vsh = make_float4(es.x + ms.x, es.y + ms.y, es.z + ms.z, es.w + ms.w);
+        vsc = make_float4(1.f + (ec.x + mc.x), 1.f + (ec.y + mc.y), 1.f + (ec.z + mc.z), 1.f + (ec.w + mc.w));
+      } else {
+        vsh = es;
+        vsc = make_float4(1.f + ec.x, 1.f + ec.y, 1.f + ec.z, 1.f + ec.w);
+      }
     } else if (mode == 1) {
       vsc = *reinterpret_cast<const float4*>(p0 + c);
       vsh = *reinterpret_cast<const float4*>(p1 + c);

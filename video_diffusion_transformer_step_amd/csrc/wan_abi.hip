@@ -128,6 +128,7 @@ struct Carve {
 template <typename T>
 struct BlockWs {
   T *u, *qkv, *vt, *o, *h;
+  float* mod;  // [B, 6, dim]: e0 + the block's modulation bias
 };
 template <typename T>
 size_t block_plan(const wan_block_cfg& c, const wan_grid& g, int B, char* base, BlockWs<T>* out) {
@@ -139,6 +140,7 @@ size_t block_plan(const wan_block_cfg& c, const wan_grid& g, int B, char* base, 
   w.vt = cv.take<T>((size_t)B * dim * pad64(S));
   w.o = cv.take<T>(BS * dim);
   w.h = cv.take<T>(BS * c.ffn_dim);
+  w.mod = cv.take<float>((size_t)B * 6 * dim);
   if (out) *out = w;
   return cv.off;
 }
@@ -152,7 +154,9 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
   const int Spad = (int)pad64(S);
   const float scale = 1.f / sqrtf((float)hd);
   // self-attention branch
-  PROF_TRY(WAN_K_LN1, launch_ln_mod<T>(x, BS, dim, S, 0, e0, W.mod_bias, 0, 1, c.ln_eps, w.u, st));
+  // the block's six modulation vectors e0 + mod_bias ("Wan 技术深度解析" §2.5), formed once
+  HIP_TRY(launch_mod_combine(e0, W.mod_bias, B, dim, w.mod, st));
+  PROF_TRY(WAN_K_LN1, launch_ln_mod<T>(x, BS, dim, S, 0, w.mod, nullptr, 0, 1, c.ln_eps, w.u, st));
   // q, k -> qkv[:, 0 .. 2 dim) (row stride 2 dim); v -> V^T directly
   PROF_TRY(WAN_K_VT_TAIL, launch_vt_tail_zero<T>(w.vt, (int64_t)B * dim, S, Spad, st));
   PROF_TRY(WAN_K_QKV_GEMM, gemm_qkv<T>(w.u, dim, (const T*)W.wqkv, dim, BS, dim, dim, W.bqkv, w.qkv, 2 * dim, w.vt, S, H,
@@ -162,7 +166,7 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
   KVStream self{w.qkv + dim, (int64_t)S * 2 * dim, 2 * dim, w.vt, S, Spad};
   PROF_TRY(WAN_K_SELF_ATTN, launch_attention<T>(w.qkv, (int64_t)S * 2 * dim, 2 * dim, self, self, 1, B, S, H, hd, scale, w.o,
                               (int64_t)S * dim, dim, 0, st));
-  PROF_TRY(WAN_K_O_GEMM, gemm_residual<T>(w.o, dim, (const T*)W.wo, dim, BS, dim, dim, W.bo, e0, W.mod_bias, 2, S, x, dim, st));
+  PROF_TRY(WAN_K_O_GEMM, gemm_residual<T>(w.o, dim, (const T*)W.wo, dim, BS, dim, dim, W.bo, w.mod, nullptr, 2, S, x, dim, st));
   // cross-attention branch (no adaLN, no RoPE)
   PROF_TRY(WAN_K_LN3, launch_ln_mod<T>(x, BS, dim, S, 1, W.ln3_w, W.ln3_b, 0, 0, c.ln_eps, w.u, st));
   T* qc = w.qkv;  // reuse: [BS, dim]
@@ -174,9 +178,9 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
                               (int64_t)S * dim, dim, 1, st));
   PROF_TRY(WAN_K_CROSS_O_GEMM, gemm_residual<T>(w.o, dim, (const T*)W.wco, dim, BS, dim, dim, W.bco, nullptr, nullptr, 0, S, x, dim, st));
   // FFN branch
-  PROF_TRY(WAN_K_LN2, launch_ln_mod<T>(x, BS, dim, S, 0, e0, W.mod_bias, 3, 4, c.ln_eps, w.u, st));
+  PROF_TRY(WAN_K_LN2, launch_ln_mod<T>(x, BS, dim, S, 0, w.mod, nullptr, 3, 4, c.ln_eps, w.u, st));
   PROF_TRY(WAN_K_FFN1_GEMM, (gemm_store<T, T>(w.u, dim, (const T*)W.w1, dim, BS, c.ffn_dim, dim, W.b1, ACT_GELU, w.h, c.ffn_dim, st)));
-  PROF_TRY(WAN_K_FFN2_GEMM, gemm_residual<T>(w.h, c.ffn_dim, (const T*)W.w2, c.ffn_dim, BS, dim, c.ffn_dim, W.b2, e0, W.mod_bias, 5, S,
+  PROF_TRY(WAN_K_FFN2_GEMM, gemm_residual<T>(w.h, c.ffn_dim, (const T*)W.w2, c.ffn_dim, BS, dim, c.ffn_dim, W.b2, w.mod, nullptr, 5, S,
                            x, dim, st));
   return WAN_OK;
 }

@@ -27,6 +27,10 @@ template <typename T>
 hipError_t launch_transpose_heads(const T* v, int64_t ld, int64_t col0, int B, int S, int H, int hd, int Spad,
                                   T* vt, hipStream_t s);
 
+// mod[b, c, n] = e0[b, c, n] + mb[c, n] for b < B, c < 6, n < dim: a block's six modulation vectors
+// (e0 [B, 6, dim] from the shared timestep MLP, mb [6, dim] the block's own bias).
+hipError_t launch_mod_combine(const float* e0, const float* mb, int B, int dim, float* mod, hipStream_t s);
+
 // Zero V^T[r, S .. Spad) for rows r < rows (row stride Spad): the padded keys of the last tile.
 template <typename T>
 hipError_t launch_vt_tail_zero(T* vt, int64_t rows, int S, int Spad, hipStream_t s);
@@ -34,7 +38,8 @@ hipError_t launch_vt_tail_zero(T* vt, int64_t rows, int S, int Spad, hipStream_t
 // ---- norms (norm.hip) -------------------------------------------------------
 // Row-wise LayerNorm of fp32 x [rows, dim] followed by one of:
 //  mode 0 (adaLN):   u = LN(x) * (1 + (e0[b][c_scale] + mb[c_scale])) + (e0[b][c_shift] + mb[c_shift])
-//                    with e0 [B, 6, dim], mb = per-block modulation bias [6, dim], b = row / S;
+//                    with e0 = p0 [B, 6, dim], mb = p1 per-block modulation bias [6, dim] (null: p0
+//                    already holds the sums), b = row / S;
 //  mode 1 (affine):  u = LN(x) * w + bias (w = p0, bias = p1, each [dim]);
 //  mode 2 (head):    u = LN(x) * (1 + (hm[1] + e[b])) + (hm[0] + e[b]) with hm = p0 [2, dim], e = p1 [B, dim].
 template <typename T>
@@ -50,7 +55,8 @@ hipError_t launch_qk_norm_rope(const T* q_in, const T* k_in, int64_t ld_in, T* q
 // C[m, n] = sum_k A[m, k] * W[n, k]   (A [M, K] row-major, W [N, K] row-major)
 // Epilogues:
 //   store:      out[m, n] = act(C + bias[n])  (OutT = T or float)
-//   residual:   x[m, n] += g(m, n) * (C + bias[n]), g = e0[m / S][chunk][n] + mb[chunk][n], or 1 if e0 null.
+//   residual:   x[m, n] += g(m, n) * (C + bias[n]), g = e0[m / S][chunk][n] + mb[chunk][n] (mb null: no
+//               addition), or 1 if e0 null.
 template <typename T, typename OutT>
 hipError_t gemm_store(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const float* bias,
                       int act, OutT* out, int64_t ldo, hipStream_t s);
