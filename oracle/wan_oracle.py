@@ -22,7 +22,7 @@ __all__ = [
     "i2v_mask", "build_i2v_input", "patchify", "unpatchify", "linear", "patch_embed",
     "conv3d_patch_embed_direct", "sinusoidal_embedding", "silu", "gelu", "time_embed",
     "layer_norm", "modulate", "rms_norm", "rope_segments", "rope_3d", "token_positions",
-    "attention", "multihead_attention", "context_embed", "cross_kv", "block_fwd",
+    "attention", "attention_lse", "lse_merge", "multihead_attention", "context_embed", "cross_kv", "block_fwd",
     "head_fwd", "cfg_combine", "euler_step", "cfg_euler", "dit_fwd", "sample",
     "self_attention_rope_only",
 ]
@@ -303,6 +303,39 @@ def attention(q, k, v):
     return p @ v
 
 
+def attention_lse(q, k, v):
+    """(o, lse) for one head: o = attention(q, k, v) and lse [Nq] the natural
+    log of the softmax normaliser, lse_i = log sum_j exp(<q_i, k_j> / sqrt(d)).
+
+    [Wan-deep-dive §5.2] shards the sequence across GPUs with RingAttention (the
+    outer level of 2D context parallelism): each GPU attends its queries to one
+    key/value shard at a time.  Reading: the page does not spell out how the
+    per-shard results combine; the normaliser of each shard travels with its
+    output as this log-sum-exp, and ``lse_merge`` combines them exactly.
+    """
+    q, k, v = _a(q), _a(k), _a(v)
+    s = (q @ k.T) / math.sqrt(q.shape[-1])
+    m = s.max(axis=-1, keepdims=True)
+    p = np.exp(s - m)
+    z = p.sum(axis=-1, keepdims=True)
+    return (p / z) @ v, (m + np.log(z))[:, 0]
+
+
+def lse_merge(outs, lses):
+    """Combine attention results over disjoint key chunks of the same queries.
+
+    outs[n] [Nq, dv] and lses[n] [Nq] from ``attention_lse`` on chunk n.  The
+    softmax over the union of the chunks weighs chunk n's normalised output by
+    its share of the total normaliser: with lse = log sum_n exp(lses[n]),
+    o = sum_n exp(lses[n] - lse) * outs[n].  Returns (o, lse).
+    """
+    L = np.stack([_a(x) for x in lses])          # [N, Nq]
+    m = L.max(axis=0)
+    lse = m + np.log(np.exp(L - m).sum(axis=0))
+    o = sum(np.exp(L[n] - lse)[:, None] * _a(outs[n]) for n in range(len(outs)))
+    return o, lse
+
+
 def multihead_attention(q, k, v, heads: int):
     """q [Nq, heads*hd], k/v [Nk, heads*hd] -> o [Nq, heads*hd], head by head."""
     q, k, v = _a(q), _a(k), _a(v)
@@ -534,6 +567,10 @@ PARITY = {
                "1D complex-exponential RoPE special case",
     "attention": "pinned: brute-force pure-Python softmax; K = 0 -> mean of V; single key; "
                  "joint permutation of keys; key-chunked log-sum-exp merge",
+    "attention_lse": "pinned: K = 0 -> lse = log Nk; single key -> lse = its scaled score; "
+                     "brute-force pure-Python log of the normaliser",
+    "lse_merge": "pinned: merging key chunks reproduces attention() and attention_lse() over "
+                 "all keys (for several chunkings, one-key chunks included); one part -> itself",
     "block_fwd": "pinned parts (norms, RoPE, attention, cross-attention single/dual equality, "
                  "adaLN-Zero identity); composition order is a reading: parity unpinned "
                  "beyond those identities",

@@ -263,23 +263,43 @@ def pin_attention_special(o):
     assert np.allclose(o.attention(q, k, v), o.attention(q, k[perm], v[perm]), atol=1e-12)
 
 
-def pin_attention_lse_merge(o):
-    """Attention over key chunks merged with their log-sum-exp equals attention over all
-    keys -- the identity tile-by-tile (flash / ring) attention relies on."""
+def pin_attention_lse_special(o):
+    """Closed forms of the log-sum-exp: all-zero keys give log(Nk) (every score is 0); a single
+    key gives its own scaled score; small cases match a pure-Python sum of exponentials."""
     rng = np.random.default_rng(11)
-    q, k, v = rng.standard_normal((5, 8)), rng.standard_normal((23, 8)), rng.standard_normal((23, 8))
-    full = o.attention(q, k, v)
-    parts, lses = [], []
-    for lo in range(0, 23, 7):
-        kk, vv = k[lo:lo + 7], v[lo:lo + 7]
-        s = q @ kk.T / math.sqrt(8)
-        lse = np.log(np.exp(s).sum(-1))
-        parts.append(o.attention(q, kk, vv))
-        lses.append(lse)
-    lses = np.stack(lses)
-    wts = np.exp(lses - np.log(np.exp(lses).sum(0)))
-    merged = sum(wts[i][:, None] * parts[i] for i in range(len(parts)))
-    assert np.allclose(merged, full, atol=1e-12)
+    q = rng.standard_normal((6, 16)) * 3
+    v = rng.standard_normal((9, 16))
+    _, lse = o.attention_lse(q, np.zeros((9, 16)), v)
+    assert np.allclose(lse, math.log(9.0), atol=1e-12)
+    k1 = rng.standard_normal((1, 16))
+    _, lse1 = o.attention_lse(q, k1, v[:1])
+    assert np.allclose(lse1, (q @ k1[0]) / 4.0, atol=1e-12)
+    for nq, nk, d in ((3, 5, 4), (2, 7, 8)):
+        qq, kk, vv = (rng.standard_normal((n, d)) for n in (nq, nk, nk))
+        out, lse = o.attention_lse(qq, kk, vv)
+        ref = [math.log(sum(math.exp(sum(qq[i][c] * kk[j][c] for c in range(d)) / math.sqrt(d))
+                            for j in range(nk))) for i in range(nq)]
+        assert np.allclose(lse, ref, atol=1e-12)
+        assert np.allclose(out, _brute_attention(qq.tolist(), kk.tolist(), vv.tolist()), atol=1e-12)
+
+
+def pin_attention_lse_merge(o):
+    """Attention over disjoint key chunks, merged through their log-sum-exp, equals attention
+    over all keys -- the identity that tile-by-tile and sequence-sharded (ring) attention rely
+    on.  Several chunkings, one-key chunks included; a single part merges to itself."""
+    rng = np.random.default_rng(12)
+    q, k, v = rng.standard_normal((5, 8)) * 2, rng.standard_normal((23, 8)), rng.standard_normal((23, 8))
+    full, full_lse = o.attention_lse(q, k, v)
+    assert np.allclose(full, o.attention(q, k, v), atol=1e-12)
+    for cuts in ((0, 7, 14, 21, 23), (0, 1, 23), (0, 11, 12, 23), (0, 23)):
+        outs, lses = [], []
+        for lo, hi in zip(cuts[:-1], cuts[1:]):
+            oo, ll = o.attention_lse(q, k[lo:hi], v[lo:hi])
+            outs.append(oo)
+            lses.append(ll)
+        merged, mlse = o.lse_merge(outs, lses)
+        assert np.allclose(merged, full, atol=1e-12), cuts
+        assert np.allclose(mlse, full_lse, atol=1e-12), cuts
 
 
 # ----------------------------------------------------------------- block / FM

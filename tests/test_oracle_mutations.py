@@ -71,6 +71,31 @@ def _attention_variant(kind):
     return attn
 
 
+def _lse_variant(kind):
+    def attention_lse(q, k, v):
+        q, k, v = (np.asarray(a, float) for a in (q, k, v))
+        s = q @ k.T / math.sqrt(q.shape[-1])
+        m = s.max(-1, keepdims=True)
+        p = np.exp(s - m)
+        z = p.sum(-1, keepdims=True)
+        if kind == "log2":
+            lse = (m + np.log2(z))[:, 0]
+        elif kind == "no_scale":
+            lse = np.log(np.exp(q @ k.T).sum(-1))
+        else:  # max dropped
+            lse = np.log(z)[:, 0]
+        return (p / z) @ v, lse
+    return attention_lse
+
+
+def _lse_merge_max_weights(outs, lses):
+    # weights relative to the largest chunk normaliser instead of the total one
+    L = np.stack([np.asarray(x, float) for x in lses])
+    m = L.max(0)
+    o = sum(np.exp(L[n] - m)[:, None] * np.asarray(outs[n], float) for n in range(len(outs)))
+    return o, m + np.log(np.exp(L - m).sum(0))
+
+
 def _ln_unbiased(x, eps=1e-6, weight=None, bias=None):
     x = np.asarray(x, float)
     mu = x.mean(-1, keepdims=True)
@@ -150,6 +175,10 @@ MUTANTS = {
     "rope_segments_swapped": ("rope_3d", lambda: _rope_variant("segments_swapped")),
     "attention_scale_1_over_d": ("attention", lambda: _attention_variant("scale_1_over_d")),
     "attention_softmax_axis": ("attention", lambda: _attention_variant("softmax_over_queries")),
+    "lse_log2": ("attention_lse", lambda: _lse_variant("log2")),
+    "lse_no_scale": ("attention_lse", lambda: _lse_variant("no_scale")),
+    "lse_max_dropped": ("attention_lse", lambda: _lse_variant("max_dropped")),
+    "lse_merge_max_weights": ("lse_merge", lambda: _lse_merge_max_weights),
     "layer_norm_unbiased_var": ("layer_norm", lambda: _ln_unbiased),
     "rms_norm_sum_not_mean": ("rms_norm", lambda: _rms_sum),
     "modulate_drops_one": ("modulate", lambda: _modulate_no_one),
