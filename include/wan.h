@@ -221,6 +221,30 @@ int wan_attention_fwd(int32_t dtype, const void* q, const void* k, const void* v
                       int32_t heads, int32_t head_dim, float rope_theta, void* o, void* ws, size_t ws_bytes,
                       wan_stream_t stream);
 
+/* Sequence-sharded (ring) attention pieces.  [DEEP] §5.2 runs the DiT's attention with 2D context
+ * parallelism whose outer level, RingAttention, shards the sequence: each GPU attends its own queries
+ * to one key/value shard at a time and combines the partial results.  These two calls are that
+ * per-shard step and that combination, on one GPU.
+ *
+ * wan_attention_partial_fwd: q [B, Sq, heads, head_dim] attends to one key/value chunk
+ * k, v [B, Sk, heads, head_dim] (all dtype; no RoPE or norm is applied here, so pass rotated q and k):
+ *   o   [B, Sq, heads, head_dim] dtype = softmax(q k^T / sqrt(head_dim)) v over the chunk's keys;
+ *   lse [B, heads, Sq] float32 (NULL = not written) = ln sum_j exp(q k_j / sqrt(head_dim)).
+ * head_dim 64 or 128.  Workspace: wan_attention_partial_workspace_bytes() (the chunk's V^T).
+ *
+ * wan_attention_lse_merge: combines n_parts (1..16) results for the same queries over disjoint key
+ * chunks: lse = ln sum_n exp(lse_parts[n]); o = sum_n exp(lse_parts[n] - lse) * o_parts[n], which is
+ * attention over the union of the chunks.  o_parts and lse_parts are HOST arrays of n_parts device
+ * pointers ([B, S, heads, head_dim] dtype and [B, heads, S] float32); o has o_parts' layout; lse
+ * (NULL = not written) has lse_parts' layout.  Outputs must not alias the inputs. */
+size_t wan_attention_partial_workspace_bytes(int32_t dtype, int32_t B, int32_t Sk, int32_t heads, int32_t head_dim);
+int wan_attention_partial_fwd(int32_t dtype, const void* q, const void* k, const void* v, int32_t B, int32_t Sq,
+                              int32_t Sk, int32_t heads, int32_t head_dim, void* o, float* lse, void* ws,
+                              size_t ws_bytes, wan_stream_t stream);
+int wan_attention_lse_merge(int32_t dtype, int32_t n_parts, const void* const* o_parts, const float* const* lse_parts,
+                            int32_t B, int32_t S, int32_t heads, int32_t head_dim, void* o, float* lse,
+                            wan_stream_t stream);
+
 /* Kernel timing (measurement only).  wan_profile_begin hands the library `capacity` caller-created
  * HIP events (hipEvent_t, passed as void*) for starts and stops plus an int32 tag array; until
  * wan_profile_end, each launch inside wan_dit_block_fwd whose id bit is set in kernel_mask is

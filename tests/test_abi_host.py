@@ -129,6 +129,31 @@ def test_other_entry_validation(lib):
                                  None) == L.WAN_EINVAL
 
 
+def test_ring_attention_validation(lib):
+    need = lib.wan_attention_partial_workspace_bytes(L.WAN_BF16, 1, 100, 2, 64)
+    assert need >= 2 * 64 * 128 * 2  # V^T of 100 keys padded to 128
+    args = lambda **kw: dict(dict(dt=L.WAN_BF16, B=1, Sq=50, Sk=100, H=2, hd=64, lse=FAKE, ws=need), **kw)
+
+    def part(a):
+        return lib.wan_attention_partial_fwd(a["dt"], FAKE, FAKE, FAKE, a["B"], a["Sq"], a["Sk"], a["H"], a["hd"],
+                                             FAKE, a["lse"], FAKE, a["ws"], None)
+    assert part(args(hd=96)) == L.WAN_EUNSUPPORTED
+    assert part(args(Sk=0)) == L.WAN_EINVAL
+    assert part(args(dt=3)) == L.WAN_EINVAL
+    assert part(args(lse=FAKE + 2)) == L.WAN_EINVAL           # misaligned lse
+    assert part(args(ws=need - 1)) == L.WAN_EWORKSPACE
+
+    def merge(n, lse_ptr=FAKE, hd=64):
+        op = (C.c_void_p * max(n, 1))(*([FAKE] * max(n, 1)))
+        lp = (C.c_void_p * max(n, 1))(*([lse_ptr] * max(n, 1)))
+        return lib.wan_attention_lse_merge(L.WAN_BF16, n, op, lp, 1, 50, 2, hd, FAKE, None, None)
+    assert merge(0) == L.WAN_EINVAL
+    assert merge(17) == L.WAN_EINVAL
+    assert merge(2, hd=96) == L.WAN_EUNSUPPORTED
+    assert merge(2, lse_ptr=FAKE + 1) == L.WAN_EINVAL
+    assert "lse_parts" in _err(lib)
+
+
 def test_status_strings(lib):
     assert lib.wan_status_string(L.WAN_EWORKSPACE) == b"WAN_EWORKSPACE"
     assert lib.wan_status_string(0) == b"WAN_OK"

@@ -79,6 +79,11 @@ _SIGS = {
     "wan_attention_workspace_bytes": ([C.c_int32, Grid, C.c_int32, C.c_int32, C.c_int32], C.c_size_t),
     "wan_attention_fwd": ([C.c_int32, vp, vp, vp, Grid, C.c_int32, C.c_int32, C.c_int32, C.c_float, vp, vp,
                            C.c_size_t, vp], C.c_int),
+    "wan_attention_partial_workspace_bytes": ([C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32], C.c_size_t),
+    "wan_attention_partial_fwd": ([C.c_int32, vp, vp, vp, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, vp,
+                                   vp, vp, C.c_size_t, vp], C.c_int),
+    "wan_attention_lse_merge": ([C.c_int32, C.c_int32, C.POINTER(C.c_void_p), C.POINTER(C.c_void_p), C.c_int32,
+                                 C.c_int32, C.c_int32, C.c_int32, vp, vp, vp], C.c_int),
     "wan_profile_begin": ([C.POINTER(C.c_void_p), C.POINTER(C.c_void_p), C.POINTER(C.c_int32), C.c_int32,
                            C.c_uint32], C.c_int),
     "wan_profile_end": ([], C.c_int32),
@@ -238,6 +243,30 @@ def attention_fwd(q, k, v, grid, o, ws, rope_theta=10000.0, stream=None):
     _check(lib().wan_attention_fwd(dtype_code(q.dtype), _p(q), _p(k), _p(v), Grid(*grid), B, H, hd,
                                    float(rope_theta), _p(o), _p(ws), ws.numel() * ws.element_size(),
                                    _stream(stream)), "wan_attention_fwd")
+
+
+def attention_partial_ws_bytes(dtype, B, Sk, heads, head_dim):
+    return lib().wan_attention_partial_workspace_bytes(dtype, B, Sk, heads, head_dim)
+
+
+def attention_partial_fwd(q, k, v, o, lse, ws, stream=None):
+    """q [B, Sq, H, hd], k/v [B, Sk, H, hd] (rotated already) -> o [B, Sq, H, hd], lse [B, H, Sq] fp32
+    (lse may be None)."""
+    B, Sq, H, hd = q.shape
+    Sk = k.shape[1]
+    _check(lib().wan_attention_partial_fwd(dtype_code(q.dtype), _p(q), _p(k), _p(v), B, Sq, Sk, H, hd, _p(o), _p(lse),
+                                           _p(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "wan_attention_partial_fwd")
+
+
+def attention_lse_merge(o_parts, lse_parts, o, lse=None, stream=None):
+    """Merge results over disjoint key chunks: o_parts [B, S, H, hd], lse_parts [B, H, S] fp32."""
+    n = len(o_parts)
+    B, S, H, hd = o.shape
+    op = (C.c_void_p * n)(*[t.data_ptr() for t in o_parts])
+    lp = (C.c_void_p * n)(*[t.data_ptr() for t in lse_parts])
+    _check(lib().wan_attention_lse_merge(dtype_code(o.dtype), n, op, lp, B, S, H, hd, _p(o), _p(lse),
+                                         _stream(stream)), "wan_attention_lse_merge")
 
 
 KERNEL_IDS = ["ln1", "qkv_gemm", "qk_norm_rope", "vt_tail", "self_attn", "o_gemm", "ln3", "cross_q_gemm",

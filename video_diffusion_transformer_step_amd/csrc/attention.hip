@@ -404,6 +404,15 @@ __device__ __forceinline__ void finish_stream(int si, const f32x16 (&o)[AttnCfg<
     for (int r = 0; r < 16; ++r) acc[d][r] = (si == 0 ? 0.f : acc[d][r]) + o[d][r] * inv;
 }
 
+// Natural log of the row's softmax normaliser: the online state keeps sum_j exp(scale s_j) as 2^m * l
+// (m in log2 units, l split over the two lane halves).  Layout [B, H, S]; lanes of the low half write.
+__device__ __forceinline__ void write_lse(const SoftState& st, float* __restrict__ lse, int b, int h, int H,
+                                          int qrow, int S) {
+  const float l = st.l + __shfl_xor(st.l, 32, 64);
+  if ((threadIdx.x & 32) == 0 && qrow < S)
+    lse[((int64_t)b * H + h) * S + qrow] = (st.m + log2f(l)) * 0.69314718055994531f;
+}
+
 // Write the wave's O rows (lane: query qrow, d = 32 dblk + 8 g + 4 lhalf + 0..3).
 template <typename T, int HD>
 __device__ __forceinline__ void store_rows(const f32x16 (&acc)[AttnCfg<T, HD>::ND], T* __restrict__ out,
@@ -443,7 +452,8 @@ __device__ __forceinline__ void load_q(const T* __restrict__ q, int64_t q_bs, in
 template <typename T, int HD, int NS, int KIND>
 __global__ __launch_bounds__(256, 2) void attention_kernel(const T* __restrict__ q, int64_t q_bs, int64_t q_ss,
                                                             KVStream s0, KVStream s1, int S, int H, float c_log2,
-                                                            T* __restrict__ out, int64_t o_bs, int64_t o_ss) {
+                                                            T* __restrict__ out, int64_t o_bs, int64_t o_ss,
+                                                            float* __restrict__ lse) {
   using C = AttnCfg<T, HD>;
   __shared__ u32x4 k0_raw[C::KBYTES / 16], k1_raw[C::KBYTES / 16], v0_raw[C::VBYTES / 16], v1_raw[C::VBYTES / 16];
   const Slots<T, HD> sl{reinterpret_cast<char*>(k0_raw), reinterpret_cast<char*>(k1_raw),
@@ -467,6 +477,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const T* __restrict__
     attend_stream<T, HD>(qf, fa, si == 0 ? s0 : s1, b, h, H, c_log2, sl, o, st);
     finish_stream<T, HD>(si, o, st, acc);
   }
+  if (NS == 1 && lse != nullptr) write_lse(st, lse, b, h, H, qrow, S);
   store_rows<T, HD>(acc, out, o_bs, o_ss, b, h, qrow, S);
 }
 
@@ -576,7 +587,8 @@ __device__ __forceinline__ void attend_stream_pp(const u32x4 (&qf)[AttnCfg<T, HD
 template <typename T, int HD, int NS, int KIND>
 __global__ __launch_bounds__(512, 1) void attention_pp_kernel(const T* __restrict__ q, int64_t q_bs, int64_t q_ss,
                                                                KVStream s0, KVStream s1, int S, int H, float c_log2,
-                                                               T* __restrict__ out, int64_t o_bs, int64_t o_ss) {
+                                                               T* __restrict__ out, int64_t o_bs, int64_t o_ss,
+                                                               float* __restrict__ lse) {
   using C = AttnCfg<T, HD>;
   __shared__ u32x4 k0_raw[C::KBYTES / 16], k1_raw[C::KBYTES / 16], v0_raw[C::VBYTES / 16], v1_raw[C::VBYTES / 16];
   const Slots<T, HD> sl{reinterpret_cast<char*>(k0_raw), reinterpret_cast<char*>(k1_raw),
@@ -602,6 +614,7 @@ __global__ __launch_bounds__(512, 1) void attention_pp_kernel(const T* __restric
     attend_stream_pp<T, HD>(qf, fa, si == 0 ? s0 : s1, b, h, H, grp, c_log2, sl, o, st);
     finish_stream<T, HD>(si, o, st, acc);
   }
+  if (NS == 1 && lse != nullptr) write_lse(st, lse, b, h, H, qrow, S);
   store_rows<T, HD>(acc, out, o_bs, o_ss, b, h, qrow, S);
 }
 
@@ -614,23 +627,23 @@ __global__ __launch_bounds__(512, 1) void attention_pp_kernel(const T* __restric
 // hundred keys, where the per-stream prologue dominates) and fp32 use the four-wave kernel.
 template <typename T, int HD, int KIND>
 hipError_t launch_hd(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0, KVStream s1, int nstreams, int B, int S,
-                     int H, float c_log2, T* o, int64_t o_bs, int64_t o_ss, hipStream_t s) {
+                     int H, float c_log2, T* o, int64_t o_bs, int64_t o_ss, float* lse, hipStream_t s) {
   if constexpr (sizeof(T) == 2 && WAN_ATTN_PP && KIND == 0) {
     dim3 grid((unsigned)ceil_div(S, 256), (unsigned)H, (unsigned)B);
     if (nstreams == 2)
       hipLaunchKernelGGL((attention_pp_kernel<T, HD, 2, KIND>), grid, dim3(512), 0, s, q, q_bs, q_ss, s0, s1, S, H,
-                         c_log2, o, o_bs, o_ss);
+                         c_log2, o, o_bs, o_ss, lse);
     else
       hipLaunchKernelGGL((attention_pp_kernel<T, HD, 1, KIND>), grid, dim3(512), 0, s, q, q_bs, q_ss, s0, s1, S, H,
-                         c_log2, o, o_bs, o_ss);
+                         c_log2, o, o_bs, o_ss, lse);
   } else {
     dim3 grid((unsigned)ceil_div(S, 128), (unsigned)H, (unsigned)B);
     if (nstreams == 2)
       hipLaunchKernelGGL((attention_kernel<T, HD, 2, KIND>), grid, dim3(256), 0, s, q, q_bs, q_ss, s0, s1, S, H,
-                         c_log2, o, o_bs, o_ss);
+                         c_log2, o, o_bs, o_ss, lse);
     else
       hipLaunchKernelGGL((attention_kernel<T, HD, 1, KIND>), grid, dim3(256), 0, s, q, q_bs, q_ss, s0, s1, S, H,
-                         c_log2, o, o_bs, o_ss);
+                         c_log2, o, o_bs, o_ss, lse);
   }
   return hipGetLastError();
 }
@@ -640,26 +653,125 @@ hipError_t launch_hd(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0, KVStre
 template <typename T>
 hipError_t launch_attention(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0, KVStream s1, int nstreams, int B,
                             int S, int H, int hd, float scale, T* o, int64_t o_bs, int64_t o_ss, int kind,
-                            hipStream_t s) {
+                            hipStream_t s, float* lse) {
   if (S <= 0 || B <= 0 || H <= 0) return hipSuccess;
   if (nstreams < 1 || nstreams > 2) return hipErrorInvalidValue;
   if (s0.L <= 0 || s0.Lpad % KT != 0 || s0.Lpad < s0.L) return hipErrorInvalidValue;
   if (nstreams == 2 && (s1.L <= 0 || s1.Lpad % KT != 0 || s1.Lpad < s1.L)) return hipErrorInvalidValue;
+  if (nstreams == 2 && lse != nullptr) return hipErrorInvalidValue;  // one normaliser per stream
   const float c_log2 = scale * 1.4426950408889634f;
   if (hd == 128) {
-    if (kind) return launch_hd<T, 128, 1>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, s);
-    return launch_hd<T, 128, 0>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, s);
+    if (kind) return launch_hd<T, 128, 1>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, s);
+    return launch_hd<T, 128, 0>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, s);
   }
   if (hd == 64) {
-    if (kind) return launch_hd<T, 64, 1>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, s);
-    return launch_hd<T, 64, 0>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, s);
+    if (kind) return launch_hd<T, 64, 1>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, s);
+    return launch_hd<T, 64, 0>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, s);
   }
   return hipErrorInvalidValue;
 }
 
+namespace {
+
+// Merge of attention results over disjoint key chunks of the same queries (sequence-sharded
+// attention, the RingAttention level of "Wan 技术深度解析" §5.2):
+// with lse = log sum_n exp(lse_n), o = sum_n exp(lse_n - lse) o_n.
+// One thread per 8 channels of one (row, head); a (row, head) pair's hd/8 threads sit in one wave,
+// and consecutive pairs are consecutive heads of a row, so the o reads are contiguous.
+struct MergeParts {
+  const void* o[MERGE_MAX_PARTS];
+  const float* lse[MERGE_MAX_PARTS];
+};
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&v)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    const u32x4 r = *reinterpret_cast<const u32x4*>(p);
+    const T* e = reinterpret_cast<const T*>(&r);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = to_f32(e[i]);
+  } else {
+    const float4 a = reinterpret_cast<const float4*>(p)[0], c = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = c.x, v[5] = c.y, v[6] = c.z, v[7] = c.w;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void lse_merge_kernel(MergeParts parts, int n, int64_t pairs, int S, int H,
+                                                        int hd, T* __restrict__ out, float* __restrict__ lse_out) {
+  const int cpp = hd >> 3;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= pairs * cpp) return;
+  const int64_t pair = t / cpp;  // row * H + h, row = b * S + s
+  const int c = (int)(t - pair * cpp);
+  const int64_t row = pair / H;
+  const int h = (int)(pair - row * H);
+  const int64_t b = row / S;
+  const int64_t li = (b * H + h) * S + (row - b * S);
+  float w[MERGE_MAX_PARTS];
+  float m = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < MERGE_MAX_PARTS; ++i)
+    if (i < n) {
+      w[i] = parts.lse[i][li];
+      m = fmaxf(m, w[i]);
+    }
+  float z = 0.f;
+#pragma unroll
+  for (int i = 0; i < MERGE_MAX_PARTS; ++i)
+    if (i < n) {
+      w[i] = expf(w[i] - m);
+      z += w[i];
+    }
+  const float inv = 1.f / z;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int64_t off = pair * hd + c * 8;
+#pragma unroll
+  for (int i = 0; i < MERGE_MAX_PARTS; ++i)
+    if (i < n) {
+      float v[8];
+      load8(reinterpret_cast<const T*>(parts.o[i]) + off, v);
+      const float wi = w[i] * inv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(wi, v[e], acc[e]);
+    }
+  if constexpr (sizeof(T) == 2) {
+    bf16x4 lo, hi;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) lo[e] = (bf16)acc[e], hi[e] = (bf16)acc[4 + e];
+    reinterpret_cast<bf16x4*>(out + off)[0] = lo;
+    reinterpret_cast<bf16x4*>(out + off)[1] = hi;
+  } else {
+    reinterpret_cast<float4*>(out + off)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    reinterpret_cast<float4*>(out + off)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
+  if (lse_out != nullptr && c == 0) lse_out[li] = m + logf(z);
+}
+
+}  // namespace
+
+template <typename T>
+hipError_t launch_lse_merge(const void* const* o_parts, const float* const* lse_parts, int n, int B, int S, int H,
+                            int hd, T* o, float* lse, hipStream_t s) {
+  if (n < 1 || n > MERGE_MAX_PARTS || hd % 8 != 0) return hipErrorInvalidValue;
+  if (B <= 0 || S <= 0 || H <= 0) return hipSuccess;
+  MergeParts mp{};
+  for (int i = 0; i < n; ++i) mp.o[i] = o_parts[i], mp.lse[i] = lse_parts[i];
+  const int64_t pairs = (int64_t)B * S * H;
+  const int64_t threads = pairs * (hd / 8);
+  hipLaunchKernelGGL(lse_merge_kernel<T>, dim3((unsigned)ceil_div(threads, 256)), dim3(256), 0, s, mp, n, pairs, S, H,
+                     hd, o, lse);
+  return hipGetLastError();
+}
+
+template hipError_t launch_lse_merge<float>(const void* const*, const float* const*, int, int, int, int, int, float*,
+                                            float*, hipStream_t);
+template hipError_t launch_lse_merge<bf16>(const void* const*, const float* const*, int, int, int, int, int, bf16*,
+                                           float*, hipStream_t);
+
 template hipError_t launch_attention<float>(const float*, int64_t, int64_t, KVStream, KVStream, int, int, int, int,
-                                            int, float, float*, int64_t, int64_t, int, hipStream_t);
+                                            int, float, float*, int64_t, int64_t, int, hipStream_t, float*);
 template hipError_t launch_attention<bf16>(const bf16*, int64_t, int64_t, KVStream, KVStream, int, int, int, int,
-                                           int, float, bf16*, int64_t, int64_t, int, hipStream_t);
+                                           int, float, bf16*, int64_t, int64_t, int, hipStream_t, float*);
 
 }  // namespace wan

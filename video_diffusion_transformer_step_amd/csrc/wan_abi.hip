@@ -542,6 +542,70 @@ int wan_attention_fwd(int32_t dtype, const void* q, const void* k, const void* v
                             (float*)o, ws, hs(stream));
 }
 
+size_t wan_attention_partial_workspace_bytes(int32_t dtype, int32_t B, int32_t Sk, int32_t heads, int32_t head_dim) {
+  if ((dtype != WAN_F32 && dtype != WAN_BF16) || B <= 0 || Sk <= 0 || heads <= 0 || head_dim <= 0) return 0;
+  return a256((size_t)B * heads * head_dim * pad64(Sk) * esize(dtype));
+}
+
+template <typename T>
+static int attention_partial_t(const T* q, const T* k, const T* v, int B, int Sq, int Sk, int H, int hd, T* o,
+                               float* lse, void* ws, hipStream_t st) {
+  const int64_t dim = (int64_t)H * hd;
+  const int Skpad = (int)pad64(Sk);
+  T* vt = reinterpret_cast<T*>(ws);
+  HIP_TRY(launch_transpose_heads<T>(v, dim, 0, B, Sk, H, hd, Skpad, vt, st));
+  KVStream s0{k, (int64_t)Sk * dim, dim, vt, Sk, Skpad};
+  HIP_TRY(launch_attention<T>(q, (int64_t)Sq * dim, dim, s0, s0, 1, B, Sq, H, hd, 1.f / sqrtf((float)hd), o,
+                              (int64_t)Sq * dim, dim, 0, st, lse));
+  return WAN_OK;
+}
+
+int wan_attention_partial_fwd(int32_t dtype, const void* q, const void* k, const void* v, int32_t B, int32_t Sq,
+                              int32_t Sk, int32_t heads, int32_t head_dim, void* o, float* lse, void* ws,
+                              size_t ws_bytes, wan_stream_t stream) {
+  WAN_TRY(check_dtype(dtype));
+  if (B <= 0 || Sq <= 0 || Sk <= 0 || heads <= 0) return fail(WAN_EINVAL, "B, Sq, Sk and heads must be positive");
+  if (head_dim != 64 && head_dim != 128) return fail(WAN_EUNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if (heads * head_dim > 6144) return fail(WAN_EUNSUPPORTED, "heads*head_dim > 6144");
+  if ((int64_t)B * Sq > (1ll << 30) || (int64_t)B * Sk > (1ll << 30)) return fail(WAN_EUNSUPPORTED, "too many rows");
+  WAN_TRY(need_ptr(q, "q"));
+  WAN_TRY(need_ptr(k, "k"));
+  WAN_TRY(need_ptr(v, "v"));
+  WAN_TRY(need_ptr(o, "o"));
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3)) return fail(WAN_EINVAL, "lse is not 4-byte aligned");
+  const size_t need = wan_attention_partial_workspace_bytes(dtype, B, Sk, heads, head_dim);
+  if (ws_bytes < need) return fail(WAN_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  WAN_TRY(need_ptr(ws, "ws"));
+  if (dtype == WAN_BF16)
+    return attention_partial_t<bf16>((const bf16*)q, (const bf16*)k, (const bf16*)v, B, Sq, Sk, heads, head_dim,
+                                     (bf16*)o, lse, ws, hs(stream));
+  return attention_partial_t<float>((const float*)q, (const float*)k, (const float*)v, B, Sq, Sk, heads, head_dim,
+                                    (float*)o, lse, ws, hs(stream));
+}
+
+int wan_attention_lse_merge(int32_t dtype, int32_t n_parts, const void* const* o_parts, const float* const* lse_parts,
+                            int32_t B, int32_t S, int32_t heads, int32_t head_dim, void* o, float* lse,
+                            wan_stream_t stream) {
+  WAN_TRY(check_dtype(dtype));
+  if (n_parts < 1 || n_parts > MERGE_MAX_PARTS) return fail(WAN_EINVAL, "n_parts %d not in 1..%d", n_parts, MERGE_MAX_PARTS);
+  if (B <= 0 || S <= 0 || heads <= 0) return fail(WAN_EINVAL, "B, S and heads must be positive");
+  if (head_dim != 64 && head_dim != 128) return fail(WAN_EUNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if ((int64_t)B * S * heads * head_dim > (1ll << 40)) return fail(WAN_EUNSUPPORTED, "too many elements");
+  if (!o_parts || !lse_parts) return fail(WAN_EINVAL, "o_parts / lse_parts are NULL");
+  for (int i = 0; i < n_parts; ++i) {
+    WAN_TRY(need_ptr(o_parts[i], "o_parts[i]"));
+    if (!lse_parts[i] || (reinterpret_cast<uintptr_t>(lse_parts[i]) & 3))
+      return fail(WAN_EINVAL, "lse_parts[%d] is NULL or not 4-byte aligned", i);
+  }
+  WAN_TRY(need_ptr(o, "o"));
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3)) return fail(WAN_EINVAL, "lse is not 4-byte aligned");
+  if (dtype == WAN_BF16)
+    HIP_TRY(launch_lse_merge<bf16>(o_parts, lse_parts, n_parts, B, S, heads, head_dim, (bf16*)o, lse, hs(stream)));
+  else
+    HIP_TRY(launch_lse_merge<float>(o_parts, lse_parts, n_parts, B, S, heads, head_dim, (float*)o, lse, hs(stream)));
+  return WAN_OK;
+}
+
 int wan_profile_begin(void* const* start_events, void* const* stop_events, int32_t* tags, int32_t capacity,
                       uint32_t kernel_mask) {
   if (capacity < 0) return fail(WAN_EINVAL, "capacity must be >= 0");

@@ -87,9 +87,19 @@ struct KVStream {
   const void* vt;
   int L, Lpad;
 };
+// kind: 0 self-attention, 1 cross-attention (separate kernel symbols).  lse (one stream only; NULL = not
+// written): [B, H, S] float32, the natural log of each query row's softmax normaliser.
 template <typename T>
 hipError_t launch_attention(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0, KVStream s1, int nstreams, int B,
                             int S, int H, int hd, float scale, T* o, int64_t o_bs, int64_t o_ss, int kind,
-                            hipStream_t s);  // kind: 0 self-attention, 1 cross-attention (separate kernel symbols)
+                            hipStream_t s, float* lse = nullptr);
+
+// Combine n (1..MERGE_MAX_PARTS) attention results of the same queries over disjoint key chunks:
+// o_parts[i] [B, S, H, hd] T, lse_parts[i] [B, H, S] float32 (host arrays of device pointers);
+// lse = log sum_i exp(lse_i), o = sum_i exp(lse_i - lse) o_i; lse may be NULL.
+constexpr int MERGE_MAX_PARTS = 16;
+template <typename T>
+hipError_t launch_lse_merge(const void* const* o_parts, const float* const* lse_parts, int n, int B, int S, int H,
+                            int hd, T* o, float* lse, hipStream_t s);
 
 }  // namespace wan
