@@ -245,6 +245,34 @@ int wan_attention_lse_merge(int32_t dtype, int32_t n_parts, const void* const* o
                             int32_t B, int32_t S, int32_t heads, int32_t head_dim, void* o, float* lse,
                             wan_stream_t stream);
 
+/* Quantised (FP8) attention.  [DEEP] §5.3 lists an FP8 FlashAttention-3 among the inference
+ * optimisations: Q.K inner products in INT8, O = P.V in FP8, FP32 accumulation across key blocks.
+ * Codes (readings of the page, which names only the formats):
+ *   q8  int8 [B, Sq, heads, head_dim], sq float32 [B, heads, Sq]: one symmetric group per (token, head),
+ *       scale = amax / 127, code = round-half-even(x * (127 / amax)) clamped to +-127;
+ *   k8  int8 [B, Sk, heads, head_dim], sk float32 [B, heads, ceil(Sk / 64)]: one group per (head, block
+ *       of 64 consecutive keys), same rule;
+ *   v8t uint8 OCP E4M3 [B, heads, head_dim, Skpad], Skpad = Sk rounded up to 64, zero past Sk;
+ *       sv float32 [B, heads, head_dim]: one group per (head, channel) over all keys,
+ *       scale = amax / 448, code = e4m3(clamp(x * (448 / amax), -448, 448)) rounded to nearest even.
+ *       Within each 64-key tile, byte h*32 + kb*16 + r holds key kb*32 + (r/4)*8 + h*4 + r%4
+ *       (h, kb in {0, 1}, r < 16): the order in which the P.V product reads the keys.
+ *   A group whose amax is 0 has scale 0 and zero codes.  Quotients and products are float32, IEEE
+ *   rounded, so the codes are a fixed function of the inputs.
+ * wan_attention_q8_quantize: q [B, Sq, heads, head_dim] and k, v [B, Sk, heads, head_dim] bf16 (rotated
+ *   already) -> the codes above.  Workspace: wan_attention_q8_quantize_workspace_bytes() (a bf16 V^T).
+ * wan_attention_q8_fwd: codes -> o [B, Sq, heads, head_dim] bf16 = softmax(q k^T / sqrt(head_dim)) v
+ *   computed from the codes (exact int32 Q.K, P rounded to E4M3 after a shift that keeps it in
+ *   [0, 256], fp32 accumulation), and lse [B, heads, Sq] float32 (NULL = not written) as for
+ *   wan_attention_partial_fwd.  head_dim 128.  sv must be 16-byte aligned. */
+size_t wan_attention_q8_quantize_workspace_bytes(int32_t B, int32_t Sk, int32_t heads, int32_t head_dim);
+int wan_attention_q8_quantize(const void* q, const void* k, const void* v, int32_t B, int32_t Sq, int32_t Sk,
+                              int32_t heads, int32_t head_dim, void* q8, float* sq, void* k8, float* sk, void* v8t,
+                              float* sv, void* ws, size_t ws_bytes, wan_stream_t stream);
+int wan_attention_q8_fwd(const void* q8, const float* sq, const void* k8, const float* sk, const void* v8t,
+                         const float* sv, int32_t B, int32_t Sq, int32_t Sk, int32_t heads, int32_t head_dim, void* o,
+                         float* lse, wan_stream_t stream);
+
 /* Kernel timing (measurement only).  wan_profile_begin hands the library `capacity` caller-created
  * HIP events (hipEvent_t, passed as void*) for starts and stops plus an int32 tag array; until
  * wan_profile_end, each launch inside wan_dit_block_fwd whose id bit is set in kernel_mask is

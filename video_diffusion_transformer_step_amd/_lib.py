@@ -84,6 +84,11 @@ _SIGS = {
                                    vp, vp, C.c_size_t, vp], C.c_int),
     "wan_attention_lse_merge": ([C.c_int32, C.c_int32, C.POINTER(C.c_void_p), C.POINTER(C.c_void_p), C.c_int32,
                                  C.c_int32, C.c_int32, C.c_int32, vp, vp, vp], C.c_int),
+    "wan_attention_q8_quantize_workspace_bytes": ([C.c_int32, C.c_int32, C.c_int32, C.c_int32], C.c_size_t),
+    "wan_attention_q8_quantize": ([vp, vp, vp, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, vp, vp, vp, vp,
+                                   vp, vp, vp, C.c_size_t, vp], C.c_int),
+    "wan_attention_q8_fwd": ([vp, vp, vp, vp, vp, vp, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, vp, vp,
+                              vp], C.c_int),
     "wan_profile_begin": ([C.POINTER(C.c_void_p), C.POINTER(C.c_void_p), C.POINTER(C.c_int32), C.c_int32,
                            C.c_uint32], C.c_int),
     "wan_profile_end": ([], C.c_int32),
@@ -267,6 +272,42 @@ def attention_lse_merge(o_parts, lse_parts, o, lse=None, stream=None):
     lp = (C.c_void_p * n)(*[t.data_ptr() for t in lse_parts])
     _check(lib().wan_attention_lse_merge(dtype_code(o.dtype), n, op, lp, B, S, H, hd, _p(o), _p(lse),
                                          _stream(stream)), "wan_attention_lse_merge")
+
+
+class Q8Codes:
+    """Device buffers of the quantised attention inputs (layouts as in wan.h)."""
+
+    def __init__(self, B, Sq, Sk, H, hd, device="cuda"):
+        import torch
+        nb = -(-Sk // 64)
+        skpad = nb * 64
+        self.shape = (B, Sq, Sk, H, hd)
+        self.q8 = torch.empty((B, Sq, H, hd), dtype=torch.int8, device=device)
+        self.sq = torch.empty((B, H, Sq), dtype=torch.float32, device=device)
+        self.k8 = torch.empty((B, Sk, H, hd), dtype=torch.int8, device=device)
+        self.sk = torch.empty((B, H, nb), dtype=torch.float32, device=device)
+        self.v8t = torch.empty((B, H, hd, skpad), dtype=torch.uint8, device=device)
+        self.sv = torch.empty((B, H, hd), dtype=torch.float32, device=device)
+
+
+def attention_q8_quantize(q, k, v, codes: Q8Codes, ws, stream=None):
+    B, Sq, H, hd = q.shape
+    Sk = k.shape[1]
+    c = codes
+    _check(lib().wan_attention_q8_quantize(_p(q), _p(k), _p(v), B, Sq, Sk, H, hd, _p(c.q8), _p(c.sq), _p(c.k8),
+                                           _p(c.sk), _p(c.v8t), _p(c.sv), _p(ws), ws.numel() * ws.element_size(),
+                                           _stream(stream)), "wan_attention_q8_quantize")
+
+
+def attention_q8_quantize_ws_bytes(B, Sk, H, hd):
+    return lib().wan_attention_q8_quantize_workspace_bytes(B, Sk, H, hd)
+
+
+def attention_q8_fwd(codes: Q8Codes, o, lse=None, stream=None):
+    B, Sq, Sk, H, hd = codes.shape
+    c = codes
+    _check(lib().wan_attention_q8_fwd(_p(c.q8), _p(c.sq), _p(c.k8), _p(c.sk), _p(c.v8t), _p(c.sv), B, Sq, Sk, H, hd,
+                                      _p(o), _p(lse), _stream(stream)), "wan_attention_q8_fwd")
 
 
 KERNEL_IDS = ["ln1", "qkv_gemm", "qk_norm_rope", "vt_tail", "self_attn", "o_gemm", "ln3", "cross_q_gemm",

@@ -618,6 +618,311 @@ __global__ __launch_bounds__(512, 1) void attention_pp_kernel(const T* __restric
   store_rows<T, HD>(acc, out, o_bs, o_ss, b, h, qrow, S);
 }
 
+// ---------------------------------------------------------------------------
+// Quantised ping-pong kernel ("Wan 技术深度解析" §5.3, FlashAttention-3 FP8: Q.K inner products in
+// INT8, O = P.V in FP8, FP32 accumulation across key tiles).  Same schedule, copies and barriers as
+// the bf16 ping-pong kernel; per 64-key tile and wave:
+//  * S^T = K Q^T from INT8 codes: 8 v_mfma_i32_32x32x32_i8 (exact int32 dot products; K codes in
+//    LDS, the wave's Q codes in registers);
+//  * scores in exp2 units are s * (c_log2 * sq[query] * sk[tile]), with sq the query's INT8 scale
+//    and sk the tile's; the running max moves only when a score exceeds it by more than Q8_TAU;
+//  * P' = 2^(score - m + Q8_BIAS) <= 2^(Q8_TAU + Q8_BIAS) = 256 is rounded to E4M3 (its normal range
+//    then covers 2^-12 of the running max) and O^T += V^T P'^T runs as 4
+//    v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) on E4M3 V^T codes whose keys are stored in
+//    the order a lane half consumes them;
+//  * the row sum l accumulates the fp32 P' (the bias cancels in O / l), and the per-channel V scales
+//    are applied once, in the final normalisation.
+// ---------------------------------------------------------------------------
+constexpr float Q8_TAU = 2.f;
+constexpr float Q8_BIAS = 6.f;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+struct KVq8 {
+  const uint8_t* k;   // INT8 K codes [B, L, H, hd]
+  int64_t k_bs, k_ss; // byte strides
+  const float* sk;    // [B, H, nb] per-64-key-block K scales
+  const uint8_t* vt;  // E4M3 V^T codes [B, H, hd, Lpad], keys in P.V order within each 64-key tile
+  const float* sv;    // [B, H, hd] V channel scales
+  int L, Lpad;
+};
+
+template <int HD>
+struct FragQ8 {
+  using C = AttnCfg<uint8_t, HD>;
+  static constexpr int KB32 = 32 * C::KCHUNKS * 16, VD32 = 32 * C::VCHUNKS * 16;
+  uint32_t k[C::NCH], v[2];
+  __device__ __forceinline__ FragQ8() {
+    const int lane = threadIdx.x & 63, lrow = lane & 31, lhalf = lane >> 5;
+#pragma unroll
+    for (int c = 0; c < C::NCH; ++c) k[c] = (uint32_t)C::koff(lrow, 2 * c + lhalf);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) v[i] = (uint32_t)C::voff(lrow, 2 * lhalf + i);
+  }
+};
+
+__device__ __forceinline__ void mfma_i8(const u32x4& a, const u32x4& b, v16i& acc) {
+  acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(v4i, a), __builtin_bit_cast(v4i, b), acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ v16i zero16i() {
+  v16i z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0;
+  return z;
+}
+
+template <int HD>
+__device__ __forceinline__ void scores_q8(const u32x4 (&qf)[AttnCfg<uint8_t, HD>::NCH], const FragQ8<HD>& fa,
+                                          const char* kslot, v16i (&s)[2]) {
+  s[0] = zero16i();
+  s[1] = zero16i();
+#pragma unroll
+  for (int c = 0; c < AttnCfg<uint8_t, HD>::NCH; ++c)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      mfma_i8(*reinterpret_cast<const u32x4*>(kslot + fa.k[c] + kb * FragQ8<HD>::KB32), qf[c], s[kb]);
+}
+
+// Scores of tile t as floats (exp2 units before the max shift) -> running max bookkeeping.  Masks
+// keys >= L.  Returns the tile's multiplier.
+template <int HD>
+__device__ __forceinline__ float softmax_prep_q8(v16i (&si)[2], int j0, int L, float cq, float skt,
+                                                 f32x16 (&o)[AttnCfg<uint8_t, HD>::ND], SoftState& st,
+                                                 f32x16 (&f)[2]) {
+  const int lhalf = (threadIdx.x & 63) >> 5;
+  // > 0 so that masked keys (-inf) stay -inf; a zero multiplier (all-zero query or key block) makes
+  // every score ~0, which is the exact result up to 1e-30 * |s|.
+  const float mul = fmaxf(cq * skt, 1e-30f);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) f[kb][r] = (float)si[kb][r];
+  if (j0 + KT > L) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + kb * 32 + (r >> 2) * 8 + lhalf * 4 + (r & 3);
+        if (key >= L) f[kb][r] = -__builtin_inff();
+      }
+  }
+  float mx = fmaxf(f[0][0], f[0][1]);
+#pragma unroll
+  for (int r = 2; r < 16; ++r) mx = fmaxf(mx, f[0][r]);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, f[1][r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float mnew = mx * mul;
+  const bool need = mnew > st.m + Q8_TAU;
+  if (__ballot(need) != 0ull) {
+    const float mm = need ? mnew : st.m;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - mm);  // 0 on the first tile (m = -inf)
+    st.m = mm;
+    st.l *= alpha;
+#pragma unroll
+    for (int d = 0; d < AttnCfg<uint8_t, HD>::ND; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+  }
+  return mul;
+}
+
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// Exponentials of tile t (f, after softmax_prep_q8) packed to E4M3 in pf (byte kb*16 + r = key
+// kb*32 + (r/4)*8 + lhalf*4 + r%4), interleaved with S(t+1) from kslot into sn.
+template <int HD>
+__device__ __forceinline__ void softmax_and_next_scores_q8(const u32x4 (&qf)[AttnCfg<uint8_t, HD>::NCH],
+                                                           const FragQ8<HD>& fa, const char* kslot, f32x16 (&f)[2],
+                                                           v16i (&sn)[2], float mul, SoftState& st,
+                                                           uint32_t (&pf)[8]) {
+  constexpr int NCH = AttnCfg<uint8_t, HD>::NCH;
+  constexpr int EPC = 32 / NCH;  // exponentials per region
+  const float negm = Q8_BIAS - st.m;
+  float lsum = 0.f;
+  sn[0] = zero16i();
+  sn[1] = zero16i();
+  u32x4 kf[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) kf[0][kb] = *reinterpret_cast<const u32x4*>(kslot + fa.k[0] + kb * FragQ8<HD>::KB32);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    if (c + 1 < NCH) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        kf[(c + 1) & 1][kb] = *reinterpret_cast<const u32x4*>(kslot + fa.k[c + 1] + kb * FragQ8<HD>::KB32);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int e = c * EPC; e < (c + 1) * EPC; ++e) {
+      // argument <= Q8_TAU + Q8_BIAS = 8 or -inf: raw v_exp_f32, P' <= 256 < 448 (no E4M3 overflow)
+      const float p = __builtin_amdgcn_exp2f(fmaf(f[e >> 4][e & 15], mul, negm));
+      f[e >> 4][e & 15] = p;
+      lsum += p;
+    }
+#pragma unroll
+    for (int w = (c * EPC) / 4; w < ((c + 1) * EPC) / 4; ++w)
+      pf[w] = pack_e4m3x4(f[w >> 2][(w & 3) * 4], f[w >> 2][(w & 3) * 4 + 1], f[w >> 2][(w & 3) * 4 + 2],
+                          f[w >> 2][(w & 3) * 4 + 3]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) mfma_i8(kf[c & 1][kb], qf[c], sn[kb]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  st.l += lsum;
+}
+
+// O^T += V^T P'^T for one tile: one 32x32x64 FP8 product per 32-channel block of hd.
+template <int HD>
+__device__ __forceinline__ void pv_products_q8(const FragQ8<HD>& fa, const char* vslot, const uint32_t (&pf)[8],
+                                               f32x16 (&o)[AttnCfg<uint8_t, HD>::ND]) {
+  constexpr int ND = AttnCfg<uint8_t, HD>::ND;
+  const v8i pb = {(int)pf[0], (int)pf[1], (int)pf[2], (int)pf[3], (int)pf[4], (int)pf[5], (int)pf[6], (int)pf[7]};
+  u32x4 va[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) va[0][i] = *reinterpret_cast<const u32x4*>(vslot + fa.v[i]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int d = 0; d < ND; ++d) {
+    if (d + 1 < ND) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        va[(d + 1) & 1][i] = *reinterpret_cast<const u32x4*>(vslot + fa.v[i] + (d + 1) * FragQ8<HD>::VD32);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const u32x4& a0 = va[d & 1][0];
+    const u32x4& a1 = va[d & 1][1];
+    const v8i pa = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+    o[d] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pa, pb, o[d], 0, 0, 0, 127, 0, 127);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int HD, int P>
+__device__ __forceinline__ void pp_tile_q8(const u32x4 (&qf)[AttnCfg<uint8_t, HD>::NCH], const FragQ8<HD>& fa,
+                                           const KVq8& kv, const CopyPlan<uint8_t, HD, 8>& cp,
+                                           const uint8_t* __restrict__ kbase, const uint8_t* __restrict__ vtb,
+                                           const float* __restrict__ skb, int t, int nt, int grp, float cq,
+                                           const Slots<uint8_t, HD>& sl, v16i (&s)[2], v16i (&sn)[2],
+                                           f32x16 (&o)[AttnCfg<uint8_t, HD>::ND], SoftState& st, int& last) {
+  using CP = CopyPlan<uint8_t, HD, 8>;
+  static_assert(CP::KL == CP::VL, "equal K and V^T copy counts");
+  char* k_this = P ? sl.k1 : sl.k0;
+  char* k_next = P ? sl.k0 : sl.k1;
+  char* v_this = P ? sl.v1 : sl.v0;
+  char* v_next = P ? sl.v0 : sl.v1;
+  const int j0 = t * KT;
+  // ---- A(t)
+  phase_barrier<CP::KL>(last);
+  last = 0;
+  if (grp == 0) {
+    if (t + 2 < nt) { load_k_tile<uint8_t, HD, 8>(cp, kbase, kv.k_ss, kv.L, j0 + 2 * KT, k_this); last = 1; }
+  } else {
+    if (t >= 1 && t + 1 < nt) { load_v_tile<uint8_t, HD, 8>(cp, vtb, j0 + KT, v_next); last = 1; }
+  }
+  f32x16 f[2];
+  const float mul = softmax_prep_q8<HD>(s, j0, kv.L, cq, skb[t], o, st, f);
+  uint32_t pf[8];
+  softmax_and_next_scores_q8<HD>(qf, fa, k_next, f, sn, mul, st, pf);
+  // ---- B(t)
+  phase_barrier<CP::KL>(last);
+  last = 0;
+  if (grp == 0) {
+    if (t >= 1 && t + 1 < nt) { load_v_tile<uint8_t, HD, 8>(cp, vtb, j0 + KT, v_next); last = 1; }
+  } else {
+    if (t + 3 < nt) { load_k_tile<uint8_t, HD, 8>(cp, kbase, kv.k_ss, kv.L, j0 + 3 * KT, k_next); last = 1; }
+  }
+  pv_products_q8<HD>(fa, v_this, pf, o);
+}
+
+template <int HD>
+__global__ __launch_bounds__(512, 1) void attention_q8_kernel(const uint8_t* __restrict__ q, int64_t q_bs,
+                                                              int64_t q_ss, const float* __restrict__ sq, KVq8 kv,
+                                                              int S, int H, float c_log2, bf16* __restrict__ out,
+                                                              int64_t o_bs, int64_t o_ss, float* __restrict__ lse) {
+  using C = AttnCfg<uint8_t, HD>;
+  using CP = CopyPlan<uint8_t, HD, 8>;
+  __shared__ u32x4 k0_raw[C::KBYTES / 16], k1_raw[C::KBYTES / 16], v0_raw[C::VBYTES / 16], v1_raw[C::VBYTES / 16];
+  const Slots<uint8_t, HD> sl{reinterpret_cast<char*>(k0_raw), reinterpret_cast<char*>(k1_raw),
+                              reinterpret_cast<char*>(v0_raw), reinterpret_cast<char*>(v1_raw)};
+  int qt, h, b;
+  attn_tile_coords(qt, h, b);
+  const int lane = threadIdx.x & 63, lhalf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave >> 2;
+  const int qrow = qt * 256 + wave * 32 + (lane & 31);
+  const FragQ8<HD> fa;
+  u32x4 qf[C::NCH];
+  load_q<uint8_t, HD>(q, q_bs, q_ss, b, h, qrow, S, qf);
+  const float cq = c_log2 * sq[((int64_t)b * H + h) * S + min(qrow, S - 1)];
+
+  const uint8_t* kbase = kv.k + (int64_t)b * kv.k_bs + (int64_t)h * HD;
+  const uint8_t* vtb = kv.vt + ((int64_t)b * H + h) * HD * (int64_t)kv.Lpad;
+  const int nt = (kv.L + KT - 1) / KT;
+  const float* skb = kv.sk + ((int64_t)b * H + h) * nt;
+
+  f32x16 o[C::ND];
+#pragma unroll
+  for (int d = 0; d < C::ND; ++d) o[d] = zero16();
+  SoftState st{-__builtin_inff(), 0.f};
+
+  const CP cp(kv.k_ss, kv.Lpad);
+  load_k_tile<uint8_t, HD, 8>(cp, kbase, kv.k_ss, kv.L, 0, sl.k0);
+  load_k_tile<uint8_t, HD, 8>(cp, kbase, kv.k_ss, kv.L, KT, sl.k1);  // clamped rows when nt == 1 (unused)
+  load_v_tile<uint8_t, HD, 8>(cp, vtb, 0, sl.v0);
+  if (nt > 1) load_v_tile<uint8_t, HD, 8>(cp, vtb, KT, sl.v1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  v16i sa[2], sb[2];
+  scores_q8<HD>(qf, fa, sl.k0, sa);
+  int last = 0;
+  if (grp == 1) {
+    phase_barrier<CP::KL>(0);
+    if (2 < nt) { load_k_tile<uint8_t, HD, 8>(cp, kbase, kv.k_ss, kv.L, 2 * KT, sl.k0); last = 1; }
+  }
+  for (int t = 0; t < nt; t += 2) {
+    pp_tile_q8<HD, 0>(qf, fa, kv, cp, kbase, vtb, skb, t, nt, grp, cq, sl, sa, sb, o, st, last);
+    if (t + 1 < nt) pp_tile_q8<HD, 1>(qf, fa, kv, cp, kbase, vtb, skb, t + 1, nt, grp, cq, sl, sb, sa, o, st, last);
+  }
+  if (grp == 0) phase_barrier<CP::KL>(0);
+
+  // O^T / l, times the V channel scale of each output channel d = 32 dblk + 8 g + 4 lhalf + i.
+  const float lt = st.l + __shfl_xor(st.l, 32, 64);
+  const float inv = 1.f / lt;
+  if (lse != nullptr && lhalf == 0 && qrow < S)
+    lse[((int64_t)b * H + h) * S + qrow] = (st.m - Q8_BIAS + log2f(lt)) * 0.69314718055994531f;
+  const float* svb = kv.sv + ((int64_t)b * H + h) * HD;
+  f32x16 acc[C::ND];
+#pragma unroll
+  for (int d = 0; d < C::ND; ++d)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 sc = *reinterpret_cast<const float4*>(svb + d * 32 + g * 8 + lhalf * 4);
+      acc[d][4 * g] = o[d][4 * g] * inv * sc.x;
+      acc[d][4 * g + 1] = o[d][4 * g + 1] * inv * sc.y;
+      acc[d][4 * g + 2] = o[d][4 * g + 2] * inv * sc.z;
+      acc[d][4 * g + 3] = o[d][4 * g + 3] * inv * sc.w;
+    }
+  store_rows<bf16, HD>(acc, out, o_bs, o_ss, b, h, qrow, S);
+}
+
+template <int HD>
+hipError_t launch_q8_hd(const uint8_t* q, int64_t q_bs, int64_t q_ss, const float* sq, const KVq8& kv, int B, int S,
+                        int H, float c_log2, bf16* o, int64_t o_bs, int64_t o_ss, float* lse, hipStream_t s) {
+  dim3 grid((unsigned)ceil_div(S, 256), (unsigned)H, (unsigned)B);
+  hipLaunchKernelGGL((attention_q8_kernel<HD>), grid, dim3(512), 0, s, q, q_bs, q_ss, sq, kv, S, H, c_log2, o, o_bs,
+                     o_ss, lse);
+  return hipGetLastError();
+}
+
 #ifndef WAN_ATTN_PP
 #define WAN_ATTN_PP 1
 #endif
@@ -668,6 +973,20 @@ hipError_t launch_attention(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0,
     if (kind) return launch_hd<T, 64, 1>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, s);
     return launch_hd<T, 64, 0>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, s);
   }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attention_q8(const uint8_t* q8, const float* sq, const uint8_t* k8, const float* sk,
+                               const uint8_t* v8t, const float* sv, int B, int S, int L, int H, int hd, bf16* o,
+                               float* lse, hipStream_t s) {
+  if (S <= 0 || B <= 0 || H <= 0) return hipSuccess;
+  if (L <= 0) return hipErrorInvalidValue;
+  const int64_t dim = (int64_t)H * hd;
+  const KVq8 kv{k8, (int64_t)L * dim, dim, sk, v8t, sv, L, (int)round_up(L, KT)};
+  const float c_log2 = 1.4426950408889634f / sqrtf((float)hd);
+  // head_dim 128 only: a 64-key tile of 64-byte rows is too small to split over the 8 waves' copies
+  if (hd == 128)
+    return launch_q8_hd<128>(q8, (int64_t)S * dim, dim, sq, kv, B, S, H, c_log2, o, (int64_t)S * dim, dim, lse, s);
   return hipErrorInvalidValue;
 }
 

@@ -1,0 +1,207 @@
+// Quantisation of attention inputs for the FP8 attention path ("Wan 技术深度解析" §5.3: Q.K inner
+// products in INT8, O = P.V in FP8 with FP32 accumulation across key blocks).
+//
+//  * Q -> INT8 per (token, head): scale = amax / 127, code = rne(x * (127 / amax)), clamped to
+//    +-127 (float32 quotients and product, IEEE-rounded, so codes are a fixed function of x);
+//  * K -> INT8 per (head, block of 64 consecutive keys), same rule;
+//  * V -> FP8 E4M3 (OCP) per (head, channel) over all keys: scale = amax / 448,
+//    code = e4m3(clamp(x * (448 / amax), -448, 448)), written as V^T [B, H, hd, Lpad] with the keys of
+//    each 64-key tile in the order the FP8 P.V product reads them (wan.h documents it).
+// A group whose amax is 0 gets scale 0 and zero codes.
+#include "wan_internal.h"
+
+namespace wan {
+
+namespace {
+
+// Max over each aligned group of 16 (W16) or 8 lanes; every lane of the group gets the result.
+template <int W>
+__device__ __forceinline__ float group_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f32<0x141>(v));  // row_half_mirror: 8-lane groups
+  if constexpr (W == 16) v = fmaxf(v, dpp_f32<0x140>(v));  // row_mirror: 16-lane rows
+  return v;
+}
+
+__device__ __forceinline__ int8_t i8_code(float x, float inv) {
+  return (int8_t)fminf(fmaxf(rintf(x * inv), -127.f), 127.f);
+}
+
+// One thread = 8 consecutive channels of one token; a (token, head) group is HD / 8 lanes.
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void quant_q_kernel(const T* __restrict__ x, int64_t ld, int64_t rows, int S,
+                                                      int H, int8_t* __restrict__ codes, float* __restrict__ scales) {
+  constexpr int G = HD / 8;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_row = (int64_t)H * G;
+  const bool live = t < rows * per_row;
+  const int64_t tt = live ? t : 0;
+  const int64_t row = tt / per_row;
+  const int c8 = (int)(tt - row * per_row);  // 8-channel chunk within the row
+  const int h = c8 / G;
+  float v[8];
+  const u32x4 raw = *reinterpret_cast<const u32x4*>(x + row * ld + c8 * 8);
+  const bf16* e = reinterpret_cast<const bf16*>(&raw);
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = (float)e[i];
+    m = fmaxf(m, fabsf(v[i]));
+  }
+  m = group_max<G>(m);  // groups never straddle a wave; dead lanes only see dead lanes' zeros
+  if (!live) return;
+  const float inv = m > 0.f ? 127.f / m : 0.f;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo |= (uint32_t)(uint8_t)i8_code(v[i], inv) << (8 * i);
+    hi |= (uint32_t)(uint8_t)i8_code(v[4 + i], inv) << (8 * i);
+  }
+  *reinterpret_cast<uint2*>(codes + row * (int64_t)H * HD + c8 * 8) = make_uint2(lo, hi);
+  if (c8 % G == 0) {
+    const int64_t b = row / S, s = row - b * S;
+    scales[(b * H + h) * S + s] = m > 0.f ? m / 127.f : 0.f;
+  }
+}
+
+// One workgroup = one (batch row, head, 64-key block).
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void quant_k_kernel(const T* __restrict__ x, int64_t ld, int S, int H,
+                                                      int8_t* __restrict__ codes, float* __restrict__ scales) {
+  constexpr int G = HD / 8, PER = 64 * G / 256;  // 8-channel chunks per thread
+  __shared__ float red[4];
+  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int nb = (int)ceil_div(S, 64);
+  float v[PER][8];
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = i * 256 + threadIdx.x;
+    const int key = blk * 64 + idx / G, c8 = idx % G;
+    if (key < S) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(x + ((int64_t)b * S + key) * ld + h * HD + c8 * 8);
+      const bf16* e = reinterpret_cast<const bf16*>(&raw);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        v[i][j] = (float)e[j];
+        m = fmaxf(m, fabsf(v[i][j]));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[i][j] = 0.f;
+    }
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float inv = m > 0.f ? 127.f / m : 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = i * 256 + threadIdx.x;
+    const int key = blk * 64 + idx / G, c8 = idx % G;
+    if (key >= S) continue;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo |= (uint32_t)(uint8_t)i8_code(v[i][j], inv) << (8 * j);
+      hi |= (uint32_t)(uint8_t)i8_code(v[i][4 + j], inv) << (8 * j);
+    }
+    *reinterpret_cast<uint2*>(codes + ((int64_t)b * S + key) * H * HD + h * HD + c8 * 8) = make_uint2(lo, hi);
+  }
+  if (threadIdx.x == 0) scales[((int64_t)b * H + h) * nb + blk] = m > 0.f ? m / 127.f : 0.f;
+}
+
+// Four fp32 values -> four E4M3 codes (round to nearest even; |y| <= 448 so no NaN).
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// One workgroup = one V^T row (batch row, head, channel d) of Lpad keys.  Input: bf16 V^T whose keys
+// are permuted within 16-key groups (position p holds key p with bits 2 and 3 swapped, the layout of
+// the bf16 attention); output: E4M3 V^T whose 64-key tiles hold at position h*32 + kb*16 + r the key
+// kb*32 + (r/4)*8 + h*4 + r%4, i.e. the 32 keys one lane half of the P.V product consumes are
+// contiguous.  Position r of an output 16-byte group reads input position kb*32 + h*8 + (r%8) +
+// 16 (r/8).
+__global__ __launch_bounds__(256) void quant_vt_kernel(const bf16* __restrict__ vt, int Lpad,
+                                                       uint8_t* __restrict__ out, float* __restrict__ scales) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const bf16* src = vt + row * Lpad;
+  float m = 0.f;
+  for (int c = threadIdx.x; c < Lpad / 8; c += 256) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(src + c * 8);
+    const bf16* e = reinterpret_cast<const bf16*>(&raw);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf((float)e[j]));
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float inv = m > 0.f ? 448.f / m : 0.f;
+  uint8_t* dst = out + row * Lpad;
+  for (int g = threadIdx.x; g < Lpad / 16; g += 256) {  // output group g: 16 positions
+    const int tile = g >> 2, hh = (g >> 1) & 1, kb = g & 1;
+    const bf16* s0 = src + tile * 64 + kb * 32 + hh * 8;
+    const u32x4 r0 = *reinterpret_cast<const u32x4*>(s0);
+    const u32x4 r1 = *reinterpret_cast<const u32x4*>(s0 + 16);
+    const bf16* e0 = reinterpret_cast<const bf16*>(&r0);
+    const bf16* e1 = reinterpret_cast<const bf16*>(&r1);
+    float y[16];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      y[j] = fminf(fmaxf((float)e0[j] * inv, -448.f), 448.f);
+      y[8 + j] = fminf(fmaxf((float)e1[j] * inv, -448.f), 448.f);
+    }
+    u32x4 o;
+    o.x = e4m3x4(y[0], y[1], y[2], y[3]);
+    o.y = e4m3x4(y[4], y[5], y[6], y[7]);
+    o.z = e4m3x4(y[8], y[9], y[10], y[11]);
+    o.w = e4m3x4(y[12], y[13], y[14], y[15]);
+    // output positions of group g: tile*64 + hh*32 + kb*16 + r
+    *reinterpret_cast<u32x4*>(dst + tile * 64 + hh * 32 + kb * 16) = o;
+  }
+  if (threadIdx.x == 0) scales[row] = m > 0.f ? m / 448.f : 0.f;
+}
+
+}  // namespace
+
+hipError_t launch_quant_q(const bf16* x, int64_t ld, int B, int S, int H, int hd, int8_t* codes, float* scales,
+                          hipStream_t s) {
+  const int64_t rows = (int64_t)B * S, threads = rows * H * (hd / 8);
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid((unsigned)ceil_div(threads, 256));
+  if (hd == 128)
+    hipLaunchKernelGGL((quant_q_kernel<bf16, 128>), grid, dim3(256), 0, s, x, ld, rows, S, H, codes, scales);
+  else if (hd == 64)
+    hipLaunchKernelGGL((quant_q_kernel<bf16, 64>), grid, dim3(256), 0, s, x, ld, rows, S, H, codes, scales);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_k(const bf16* x, int64_t ld, int B, int S, int H, int hd, int8_t* codes, float* scales,
+                          hipStream_t s) {
+  if (B <= 0 || S <= 0) return hipSuccess;
+  const dim3 grid((unsigned)ceil_div(S, 64), (unsigned)H, (unsigned)B);
+  if (hd == 128)
+    hipLaunchKernelGGL((quant_k_kernel<bf16, 128>), grid, dim3(256), 0, s, x, ld, S, H, codes, scales);
+  else if (hd == 64)
+    hipLaunchKernelGGL((quant_k_kernel<bf16, 64>), grid, dim3(256), 0, s, x, ld, S, H, codes, scales);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_vt(const bf16* vt, int64_t rows, int Lpad, uint8_t* out, float* scales, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (Lpad % 64 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_vt_kernel, dim3((unsigned)rows), dim3(256), 0, s, vt, Lpad, out, scales);
+  return hipGetLastError();
+}
+
+}  // namespace wan

@@ -606,6 +606,67 @@ int wan_attention_lse_merge(int32_t dtype, int32_t n_parts, const void* const* o
   return WAN_OK;
 }
 
+size_t wan_attention_q8_quantize_workspace_bytes(int32_t B, int32_t Sk, int32_t heads, int32_t head_dim) {
+  if (B <= 0 || Sk <= 0 || heads <= 0 || head_dim <= 0) return 0;
+  return a256((size_t)B * heads * head_dim * pad64(Sk) * 2);
+}
+
+static int check_q8_shape(int32_t B, int32_t Sq, int32_t Sk, int32_t heads, int32_t head_dim) {
+  if (B <= 0 || Sq <= 0 || Sk <= 0 || heads <= 0) return fail(WAN_EINVAL, "B, Sq, Sk and heads must be positive");
+  if (head_dim != 128) return fail(WAN_EUNSUPPORTED, "head_dim %d not supported by the quantised path (128)", head_dim);
+  if (heads * head_dim > 6144) return fail(WAN_EUNSUPPORTED, "heads*head_dim > 6144");
+  if ((int64_t)B * Sq > (1ll << 30) || (int64_t)B * Sk > (1ll << 30)) return fail(WAN_EUNSUPPORTED, "too many rows");
+  return WAN_OK;
+}
+
+static int need_f32(const void* p, const char* name) {
+  if (!p || (reinterpret_cast<uintptr_t>(p) & 3)) return fail(WAN_EINVAL, "%s is NULL or not 4-byte aligned", name);
+  return WAN_OK;
+}
+
+int wan_attention_q8_quantize(const void* q, const void* k, const void* v, int32_t B, int32_t Sq, int32_t Sk,
+                              int32_t heads, int32_t head_dim, void* q8, float* sq, void* k8, float* sk, void* v8t,
+                              float* sv, void* ws, size_t ws_bytes, wan_stream_t stream) {
+  WAN_TRY(check_q8_shape(B, Sq, Sk, heads, head_dim));
+  WAN_TRY(need_ptr(q, "q"));
+  WAN_TRY(need_ptr(k, "k"));
+  WAN_TRY(need_ptr(v, "v"));
+  WAN_TRY(need_ptr(q8, "q8"));
+  WAN_TRY(need_ptr(k8, "k8"));
+  WAN_TRY(need_ptr(v8t, "v8t"));
+  WAN_TRY(need_f32(sq, "sq"));
+  WAN_TRY(need_f32(sk, "sk"));
+  WAN_TRY(need_ptr(sv, "sv"));
+  const size_t need = wan_attention_q8_quantize_workspace_bytes(B, Sk, heads, head_dim);
+  if (ws_bytes < need) return fail(WAN_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  WAN_TRY(need_ptr(ws, "ws"));
+  const int dim = heads * head_dim, Skpad = (int)pad64(Sk);
+  const hipStream_t st = hs(stream);
+  bf16* vt = reinterpret_cast<bf16*>(ws);
+  HIP_TRY(launch_quant_q((const bf16*)q, dim, B, Sq, heads, head_dim, (int8_t*)q8, sq, st));
+  HIP_TRY(launch_quant_k((const bf16*)k, dim, B, Sk, heads, head_dim, (int8_t*)k8, sk, st));
+  HIP_TRY(launch_transpose_heads<bf16>((const bf16*)v, dim, 0, B, Sk, heads, head_dim, Skpad, vt, st));
+  HIP_TRY(launch_quant_vt(vt, (int64_t)B * dim, Skpad, (uint8_t*)v8t, sv, st));
+  return WAN_OK;
+}
+
+int wan_attention_q8_fwd(const void* q8, const float* sq, const void* k8, const float* sk, const void* v8t,
+                         const float* sv, int32_t B, int32_t Sq, int32_t Sk, int32_t heads, int32_t head_dim, void* o,
+                         float* lse, wan_stream_t stream) {
+  WAN_TRY(check_q8_shape(B, Sq, Sk, heads, head_dim));
+  WAN_TRY(need_ptr(q8, "q8"));
+  WAN_TRY(need_ptr(k8, "k8"));
+  WAN_TRY(need_ptr(v8t, "v8t"));
+  WAN_TRY(need_f32(sq, "sq"));
+  WAN_TRY(need_f32(sk, "sk"));
+  WAN_TRY(need_ptr(sv, "sv"));
+  WAN_TRY(need_ptr(o, "o"));
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3)) return fail(WAN_EINVAL, "lse is not 4-byte aligned");
+  HIP_TRY(launch_attention_q8((const uint8_t*)q8, sq, (const uint8_t*)k8, sk, (const uint8_t*)v8t, sv, B, Sq, Sk,
+                              heads, head_dim, (bf16*)o, lse, hs(stream)));
+  return WAN_OK;
+}
+
 int wan_profile_begin(void* const* start_events, void* const* stop_events, int32_t* tags, int32_t capacity,
                       uint32_t kernel_mask) {
   if (capacity < 0) return fail(WAN_EINVAL, "capacity must be >= 0");

@@ -28,6 +28,9 @@ template <> struct dtype_traits<float> {
 template <> struct dtype_traits<bf16> {
   static constexpr int per16 = 8;
 };
+template <> struct dtype_traits<uint8_t> {  // INT8 / FP8 codes
+  static constexpr int per16 = 16;
+};
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
