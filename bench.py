@@ -28,6 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (int8: 5.0 POP/s)
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 METRIC = "ms per DiT denoise step + attention TFLOP/s (% MFMA peak) at 32760 tokens"
@@ -139,6 +140,8 @@ def main():
     ap.add_argument("--layers", type=int, default=None, help="blocks per step (default: the preset's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the second measurement with the quantised (INT8 Q.K / FP8 P.V) self-attention")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many bytes (a known-size "
                          "reference for HBM byte counters)")
@@ -253,6 +256,41 @@ def main():
         log(f"copied {n * 4} bytes (counter calibration)")
         del src, dst
 
+    # ---- the same step with the quantised self-attention (reported beside the bf16 headline)
+    fp8 = None
+    if not args.no_fp8 and c.dtype == "bf16" and c.head_dim == 128:
+        buf8 = R.alloc_step(c, c.B, fp8_attn=True)
+        x8 = torch.from_numpy(x_t).cuda()
+
+        def step8(k):
+            R.denoise_step(c, model, blocks, caches, x8, zg, 1.0 + k * dt, dt, c.guidance, buf8, c.B, fp8_attn=True)
+
+        for k in range(args.warmup):
+            step8(k)
+        torch.cuda.synchronize()
+        t8 = L.KernelTimer(capacity=args.steps * layers * 4, kernels=("self_attn", "quant"))
+        t0 = time.perf_counter()
+        with t8:
+            for k in range(args.steps):
+                step8(args.warmup + k)
+        torch.cuda.synchronize()
+        ms8 = (time.perf_counter() - t0) * 1e3 / args.steps
+        tm = t8.times_ms()
+        a8 = float(np.mean(tm.get("self_attn", [float("nan")])))
+        q8 = float(np.sum(tm.get("quant", [0.0]))) / (args.steps * layers)
+        tf8 = attn_flops / (a8 * 1e-3) / 1e12
+        assert np.isfinite(x8.float().cpu().numpy()).all(), "non-finite latent after the quantised steps"
+        fp8 = {"ms_per_step": round(ms8, 3), "ms_per_block": round(ms8 / layers, 3),
+               "attention_ms": round(a8, 4), "attention_tflops": round(tf8, 1),
+               "attention_frac_of_fp8_peak": round(tf8 / PEAK_FP8_TFLOPS, 4),
+               "attention_frac_of_bf16_peak": round(tf8 / PEAK_BF16_TFLOPS, 4),
+               "quantise_ms_per_block": round(q8, 4),
+               "step_speedup_vs_bf16": round(ms_per_step / ms8, 3),
+               "note": "self-attention in INT8 (Q.K) / FP8 E4M3 (P.V); every other kernel as in the bf16 step"}
+        log(f"quantised self-attention: {ms8:.2f} ms/step, attention {a8:.3f} ms ({tf8:.0f} TFLOP/s), "
+            f"quantisers {q8:.3f} ms/block")
+        del buf8, x8
+
     cpu = None
     if not args.no_cpu_baseline:
         t = time.perf_counter()
@@ -288,6 +326,7 @@ def main():
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "launch_ms": round(attn_avg, 4), "flops_per_launch": attn_flops},
         "breakdown_ms_per_block": breakdown,
+        "fp8_attention_step": fp8,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -60,7 +60,12 @@ typedef struct {
 
 /* Block hyper-parameters.  dim = heads * head_dim; head_dim 64 or 128; dim % 8 == 0, dim <= 6144;
  * text_len > 0 text keys; img_len >= 0 image keys (0 = single-stream cross-attention).
- * Proposed eps 1e-6 for both norms and rope_theta 10000.  flags must be 0 (reserved). */
+ * Proposed eps 1e-6 for both norms and rope_theta 10000.  flags: 0, or WAN_FLAG_FP8_ATTN. */
+/* WAN_FLAG_FP8_ATTN: the block's self-attention runs the quantised path of wan_attention_q8_fwd (INT8
+ * Q.K, E4M3 P.V; [DEEP] §5.3) on the rotated q, k and v it computes; requires dtype WAN_BF16 and
+ * head_dim 128.  Everything else in the block is unchanged. */
+#define WAN_FLAG_FP8_ATTN 1u
+
 typedef struct {
   int32_t dim, heads, head_dim, ffn_dim;
   int32_t text_len, img_len;
@@ -281,11 +286,12 @@ int wan_attention_q8_fwd(const void* q8, const float* sq, const void* k8, const 
  * wan_profile_end, which returns the number of pairs recorded and disables recording.  Process-wide
  * state, not thread-safe; calls that overlap on several threads must not use it.
  * Ids name the block's launches in order; WAN_K_VT_TAIL is the zero fill of the padded keys of V^T
- * (the Q/K/V GEMM writes V^T itself). */
+ * (the Q/K/V GEMM writes V^T itself); WAN_K_QUANT marks the three quantiser launches that precede
+ * the self-attention under WAN_FLAG_FP8_ATTN. */
 typedef enum {
   WAN_K_LN1 = 0, WAN_K_QKV_GEMM = 1, WAN_K_QK_NORM_ROPE = 2, WAN_K_VT_TAIL = 3, WAN_K_SELF_ATTN = 4,
   WAN_K_O_GEMM = 5, WAN_K_LN3 = 6, WAN_K_CROSS_Q_GEMM = 7, WAN_K_CROSS_ATTN = 8, WAN_K_CROSS_O_GEMM = 9,
-  WAN_K_LN2 = 10, WAN_K_FFN1_GEMM = 11, WAN_K_FFN2_GEMM = 12
+  WAN_K_LN2 = 10, WAN_K_FFN1_GEMM = 11, WAN_K_FFN2_GEMM = 12, WAN_K_QUANT = 13
 } wan_kernel_id;
 int wan_profile_begin(void* const* start_events, void* const* stop_events, int32_t* tags, int32_t capacity,
                       uint32_t kernel_mask);

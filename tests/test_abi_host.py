@@ -81,9 +81,16 @@ def test_block_validation(lib):
         assert lib.wan_dit_block_fwd(C.byref(cfg), C.byref(w), g, 1, FAKE, FAKE, C.byref(kv), FAKE, ws_need,
                                      None) == code, _err(lib)
     c = _cfg()
-    c.flags = 1
+    c.flags = L.WAN_FLAG_FP8_ATTN  # the quantised self-attention needs bf16 and head_dim 128
     assert lib.wan_dit_block_fwd(C.byref(c), C.byref(w), g, 1, FAKE, FAKE, C.byref(kv), FAKE, ws_need,
                                  None) == L.WAN_EUNSUPPORTED
+    c.flags = 4  # unknown bit
+    assert lib.wan_dit_block_fwd(C.byref(c), C.byref(w), g, 1, FAKE, FAKE, C.byref(kv), FAKE, ws_need,
+                                 None) == L.WAN_EUNSUPPORTED
+    b16 = _cfg(dtype=L.WAN_BF16, dim=256, heads=2, head_dim=128)
+    plain = lib.wan_dit_block_workspace_bytes(C.byref(b16), g, 1)
+    b16.flags = L.WAN_FLAG_FP8_ATTN
+    assert lib.wan_dit_block_workspace_bytes(C.byref(b16), g, 1) > plain  # room for the codes
     # too small a workspace
     assert lib.wan_dit_block_fwd(C.byref(_cfg()), C.byref(w), g, 1, FAKE, FAKE, C.byref(kv), FAKE, ws_need - 1,
                                  None) == L.WAN_EWORKSPACE

@@ -35,11 +35,11 @@ def _inputs(c, seed=0):
     return x, e0, t_emb, i_emb, bw
 
 
-def _gpu_block(c, x, e0, t_emb, i_emb, bw, repeat=1):
+def _gpu_block(c, x, e0, t_emb, i_emb, bw, repeat=1, fp8_attn=False):
     td = torch.bfloat16 if c.dtype == "bf16" else torch.float32
     blk = R.DeviceBlock(bw, c.dtype)
     (kc,) = R.cross_kv_all(c, [blk], dev(t_emb, td), None if i_emb is None else dev(i_emb, td), c.B)
-    cfg = R.cfg_of(c)
+    cfg = R.cfg_of(c, fp8_attn=fp8_attn)
     ws = torch.empty(L.block_ws_bytes(cfg, c.grid, c.B), dtype=torch.uint8, device="cuda")
     outs = []
     for _ in range(repeat):
@@ -127,3 +127,33 @@ def test_block_full_size_sampled_rows(name):
     got, = _gpu_block(c, x, e0, t_emb, i_emb, bw)
     ref = _oracle_block(c, x, e0, t_emb, i_emb, bw, rows=rows)
     _check(c, got, ref, x, rows=rows)
+
+
+# Quantised self-attention (WAN_FLAG_FP8_ATTN): its output carries the E4M3-bounded error of the
+# quantised path (<= 2^-4 rel-L2, see test_gpu_fp8.py); it reaches dx through W_o and gate1 while the
+# other branches keep bf16 accuracy, so dx is held to the same 2^-4.
+FP8_TOL = 2.0 ** -4
+
+
+def test_block_fp8_attention_small():
+    require_gpu()
+    c = wi.get_config("tiny").replace(dtype="bf16", T=3, H=12, W=20, B=2, dim=256, heads=2, head_dim=128,
+                                      ffn_dim=640, text_len=70, img_len=9, img_dim=32)
+    case(f"block fp8 attention {c.name} S={c.S}")
+    x, e0, t_emb, i_emb, bw = _inputs(c)
+    got, = _gpu_block(c, x, e0, t_emb, i_emb, bw, fp8_attn=True)
+    ref = _oracle_block(c, x, e0, t_emb, i_emb, bw)
+    _check(c, got, ref, x, tol=FP8_TOL)
+
+
+@pytest.mark.timeout(900)
+def test_block_fp8_attention_full_size():
+    """The 32760-token 1.3B-shaped block with the quantised self-attention, sampled query rows."""
+    require_gpu()
+    c = wi.get_config("t2v-1.3b")
+    case(f"block fp8 attention full size {c.name}")
+    rows = wi.sample_rows(c, 64, seed=3)
+    x, e0, t_emb, i_emb, bw = _inputs(c, seed=3)
+    got, = _gpu_block(c, x, e0, t_emb, i_emb, bw, fp8_attn=True)
+    ref = _oracle_block(c, x, e0, t_emb, i_emb, bw, rows=rows)
+    _check(c, got, ref, x, rows=rows, tol=FP8_TOL)

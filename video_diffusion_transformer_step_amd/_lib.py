@@ -148,9 +148,12 @@ def dtype_code(torch_dtype):
     raise ValueError(f"unsupported dtype {torch_dtype}")
 
 
+WAN_FLAG_FP8_ATTN = 1
+
+
 def block_cfg(dim, heads, head_dim, ffn_dim, text_len, img_len, dtype, ln_eps=1e-6, rms_eps=1e-6,
-              rope_theta=10000.0):
-    return BlockCfg(dim, heads, head_dim, ffn_dim, text_len, img_len, dtype, 0, ln_eps, rms_eps, rope_theta)
+              rope_theta=10000.0, flags=0):
+    return BlockCfg(dim, heads, head_dim, ffn_dim, text_len, img_len, dtype, flags, ln_eps, rms_eps, rope_theta)
 
 
 def latent_shape(x):
@@ -311,7 +314,7 @@ def attention_q8_fwd(codes: Q8Codes, o, lse=None, stream=None):
 
 
 KERNEL_IDS = ["ln1", "qkv_gemm", "qk_norm_rope", "vt_tail", "self_attn", "o_gemm", "ln3", "cross_q_gemm",
-              "cross_attn", "cross_o_gemm", "ln2", "ffn1_gemm", "ffn2_gemm"]
+              "cross_attn", "cross_o_gemm", "ln2", "ffn1_gemm", "ffn2_gemm", "quant"]
 
 
 class KernelTimer:

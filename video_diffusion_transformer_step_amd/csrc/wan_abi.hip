@@ -95,7 +95,9 @@ int check_dtype(int32_t dtype) {
 int check_cfg(const wan_block_cfg* c) {
   if (!c) return fail(WAN_EINVAL, "cfg is NULL");
   WAN_TRY(check_dtype(c->dtype));
-  if (c->flags != 0) return fail(WAN_EUNSUPPORTED, "cfg->flags must be 0 (got 0x%x)", c->flags);
+  if (c->flags & ~WAN_FLAG_FP8_ATTN) return fail(WAN_EUNSUPPORTED, "unknown cfg->flags bits 0x%x", c->flags);
+  if ((c->flags & WAN_FLAG_FP8_ATTN) && (c->dtype != WAN_BF16 || c->head_dim != 128))
+    return fail(WAN_EUNSUPPORTED, "WAN_FLAG_FP8_ATTN needs dtype WAN_BF16 and head_dim 128");
   if (c->heads <= 0 || c->head_dim <= 0 || c->dim != c->heads * c->head_dim)
     return fail(WAN_EINVAL, "dim (%d) must equal heads (%d) * head_dim (%d)", c->dim, c->heads, c->head_dim);
   if (c->head_dim != 64 && c->head_dim != 128)
@@ -129,6 +131,9 @@ template <typename T>
 struct BlockWs {
   T *u, *qkv, *vt, *o, *h;
   float* mod;  // [B, 6, dim]: e0 + the block's modulation bias
+  // quantised self-attention (WAN_FLAG_FP8_ATTN only): codes and scales of q, k, v
+  uint8_t *q8, *k8, *v8t;
+  float *sq, *sk, *sv;
 };
 template <typename T>
 size_t block_plan(const wan_block_cfg& c, const wan_grid& g, int B, char* base, BlockWs<T>* out) {
@@ -141,6 +146,16 @@ size_t block_plan(const wan_block_cfg& c, const wan_grid& g, int B, char* base, 
   w.o = cv.take<T>(BS * dim);
   w.h = cv.take<T>(BS * c.ffn_dim);
   w.mod = cv.take<float>((size_t)B * 6 * dim);
+  w.q8 = w.k8 = w.v8t = nullptr;
+  w.sq = w.sk = w.sv = nullptr;
+  if (c.flags & WAN_FLAG_FP8_ATTN) {
+    w.q8 = cv.take<uint8_t>(BS * dim);
+    w.k8 = cv.take<uint8_t>(BS * dim);
+    w.v8t = cv.take<uint8_t>((size_t)B * dim * pad64(S));
+    w.sq = cv.take<float>((size_t)B * c.heads * S);
+    w.sk = cv.take<float>((size_t)B * c.heads * (pad64(S) / 64));
+    w.sv = cv.take<float>((size_t)B * dim);
+  }
   if (out) *out = w;
   return cv.off;
 }
@@ -163,9 +178,19 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
                                        hd, Spad, st));
   PROF_TRY(WAN_K_QK_NORM_ROPE, launch_qk_norm_rope<T>(w.qkv, w.qkv + dim, 2 * dim, w.qkv, w.qkv + dim, 2 * dim, B, g.T, g.Hp, g.Wp, H, hd,
                                  W.gq, W.gk, 1, c.rms_eps, c.rope_theta, st));
-  KVStream self{w.qkv + dim, (int64_t)S * 2 * dim, 2 * dim, w.vt, S, Spad};
-  PROF_TRY(WAN_K_SELF_ATTN, launch_attention<T>(w.qkv, (int64_t)S * 2 * dim, 2 * dim, self, self, 1, B, S, H, hd, scale, w.o,
-                              (int64_t)S * dim, dim, 0, st));
+  if constexpr (sizeof(T) == 2) {
+    if (c.flags & WAN_FLAG_FP8_ATTN) {  // quantised self-attention ("Wan 技术深度解析" §5.3)
+      PROF_TRY(WAN_K_QUANT, launch_quant_q(w.qkv, 2 * dim, B, S, H, hd, (int8_t*)w.q8, w.sq, st));
+      PROF_TRY(WAN_K_QUANT, launch_quant_k(w.qkv + dim, 2 * dim, B, S, H, hd, (int8_t*)w.k8, w.sk, st));
+      PROF_TRY(WAN_K_QUANT, launch_quant_vt(w.vt, (int64_t)B * dim, Spad, w.v8t, w.sv, st));
+      PROF_TRY(WAN_K_SELF_ATTN, launch_attention_q8(w.q8, w.sq, w.k8, w.sk, w.v8t, w.sv, B, S, S, H, hd, w.o, nullptr, st));
+    }
+  }
+  if (!(c.flags & WAN_FLAG_FP8_ATTN)) {
+    KVStream self{w.qkv + dim, (int64_t)S * 2 * dim, 2 * dim, w.vt, S, Spad};
+    PROF_TRY(WAN_K_SELF_ATTN, launch_attention<T>(w.qkv, (int64_t)S * 2 * dim, 2 * dim, self, self, 1, B, S, H, hd,
+                                                  scale, w.o, (int64_t)S * dim, dim, 0, st));
+  }
   PROF_TRY(WAN_K_O_GEMM, gemm_residual<T>(w.o, dim, (const T*)W.wo, dim, BS, dim, dim, W.bo, w.mod, nullptr, 2, S, x, dim, st));
   // cross-attention branch (no adaLN, no RoPE)
   PROF_TRY(WAN_K_LN3, launch_ln_mod<T>(x, BS, dim, S, 1, W.ln3_w, W.ln3_b, 0, 0, c.ln_eps, w.u, st));

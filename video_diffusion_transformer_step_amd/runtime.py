@@ -38,12 +38,14 @@ class _Keep:
         return None if tensor is None else tensor.data_ptr()
 
 
-def cfg_of(c, dtype=None):
+def cfg_of(c, dtype=None, fp8_attn=False):
     """BlockCfg from a workload description (attributes dim, heads, head_dim, ffn_dim,
-    text_len, img_len, dtype, ln_eps, rms_eps, rope_theta)."""
+    text_len, img_len, dtype, ln_eps, rms_eps, rope_theta); fp8_attn selects the quantised
+    self-attention (WAN_FLAG_FP8_ATTN)."""
     d = dtype if dtype is not None else c.dtype
     return L.block_cfg(c.dim, c.heads, c.head_dim, c.ffn_dim, max(c.text_len, 1), c.img_len,
-                       L.WAN_BF16 if d == "bf16" else L.WAN_F32, c.ln_eps, c.rms_eps, c.rope_theta)
+                       L.WAN_BF16 if d == "bf16" else L.WAN_F32, c.ln_eps, c.rms_eps, c.rope_theta,
+                       L.WAN_FLAG_FP8_ATTN if fp8_attn else 0)
 
 
 class DeviceBlock:
@@ -142,8 +144,8 @@ def cross_kv_all(c, blocks, txt_emb, img_emb, B, device="cuda"):
     return caches
 
 
-def alloc_step(c, B, device="cuda") -> StepBuffers:
-    cfg = cfg_of(c)
+def alloc_step(c, B, device="cuda", fp8_attn=False) -> StepBuffers:
+    cfg = cfg_of(c, fp8_attn=fp8_attn)
     S = c.S
     ws_bytes = max(L.block_ws_bytes(cfg, c.grid, B), L.patch_embed_ws_bytes(cfg, B * S, c.in_channels),
                    L.head_ws_bytes(cfg, B * S), 16)
@@ -161,10 +163,11 @@ def alloc_step(c, B, device="cuda") -> StepBuffers:
 
 
 def dit_forward(c, model: DeviceModel, blocks, caches, x_latent, z_img, t, buf: StepBuffers, B,
-                known_pixel_frames=None):
+                known_pixel_frames=None, fp8_attn=False):
     """One DiT evaluation over B rows sharing the latent x_latent [1, C, T, H, W] (CFG rows see the same
-    x_in).  Result in buf.v [B, C_out, T, H, W]."""
-    cfg = cfg_of(c)
+    x_in).  Result in buf.v [B, C_out, T, H, W].  fp8_attn: quantised self-attention in every block
+    (buf must come from alloc_step(..., fp8_attn=True))."""
+    cfg = cfg_of(c, fp8_attn=fp8_attn)
     one = x_latent.shape[0]
     for b in range(B):
         src = x_latent[b % one:b % one + 1]
@@ -183,8 +186,8 @@ def dit_forward(c, model: DeviceModel, blocks, caches, x_latent, z_img, t, buf: 
 
 
 def denoise_step(c, model, blocks, caches, x_latent, z_img, t, dt, guidance, buf: StepBuffers, B,
-                 known_pixel_frames=None):
+                 known_pixel_frames=None, fp8_attn=False):
     """x_latent <- x_latent + dt * v, v = CFG(v_cond, v_uncond) when B == 2 (row 0 conditional)."""
-    v = dit_forward(c, model, blocks, caches, x_latent, z_img, t, buf, B, known_pixel_frames)
+    v = dit_forward(c, model, blocks, caches, x_latent, z_img, t, buf, B, known_pixel_frames, fp8_attn)
     L.fm_euler_step(x_latent, v[0:1], v[1:2] if B > 1 else None, guidance, dt)
     return x_latent
