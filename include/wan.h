@@ -257,7 +257,7 @@ int wan_attention_lse_merge(int32_t dtype, int32_t n_parts, const void* const* o
  *       scale = amax / 127, code = round-half-even(x * (127 / amax)) clamped to +-127;
  *   k8  int8 [B, Sk, heads, head_dim], sk float32 [B, heads, ceil(Sk / 64)]: one group per (head, block
  *       of 64 consecutive keys), same rule;
- *   v8t uint8 OCP E4M3 [B, heads, head_dim, Skpad], Skpad = Sk rounded up to 64, zero past Sk;
+ *   v8t uint8 OCP E4M3 [B, heads, head_dim, Skpad], Skpad = Sk rounded up to 128, zero past Sk;
  *       sv float32 [B, heads, head_dim]: one group per (head, channel) over all keys,
  *       scale = amax / 448, code = e4m3(clamp(x * (448 / amax), -448, 448)) rounded to nearest even.
  *       Within each 64-key tile, byte h*32 + kb*16 + r holds key kb*32 + (r/4)*8 + h*4 + r%4

@@ -63,7 +63,7 @@ def _run(q, k, v):
 def _expected_v8t(v):
     codes, scales = OQ.quant_v_e4m3(v)  # codes [B, S, H, d]
     B, S, H, d = v.shape
-    pad = -(-S // 64) * 64
+    pad = -(-S // 128) * 128
     vt = np.zeros((B, H, d, pad), np.uint8)
     vt[:, :, :, :S] = codes.transpose(0, 2, 3, 1)
     p2k = _pos_to_key()

@@ -283,7 +283,7 @@ class Q8Codes:
     def __init__(self, B, Sq, Sk, H, hd, device="cuda"):
         import torch
         nb = -(-Sk // 64)
-        skpad = nb * 64
+        skpad = -(-Sk // 128) * 128
         self.shape = (B, Sq, Sk, H, hd)
         self.q8 = torch.empty((B, Sq, H, hd), dtype=torch.int8, device=device)
         self.sq = torch.empty((B, H, Sq), dtype=torch.float32, device=device)

@@ -630,8 +630,9 @@ __global__ __launch_bounds__(512, 1) void attention_pp_kernel(const T* __restric
 //    then covers 2^-12 of the running max) and O^T += V^T P'^T runs as 4
 //    v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) on E4M3 V^T codes whose keys are stored in
 //    the order a lane half consumes them;
-//  * the row sum l accumulates the fp32 P' (the bias cancels in O / l), and the per-channel V scales
-//    are applied once, in the final normalisation.
+//  * the row sum l is one more FP8 product per tile, of an all-ones operand with the same E4M3 P'
+//    (so numerator and denominator see the same rounded weights, and every lane holds its query's
+//    l); the bias cancels in O / l, and the per-channel V scales are applied once, at the end.
 // ---------------------------------------------------------------------------
 constexpr float Q8_TAU = 2.f;
 constexpr float Q8_BIAS = 6.f;
@@ -688,11 +689,13 @@ __device__ __forceinline__ void scores_q8(const u32x4 (&qf)[AttnCfg<uint8_t, HD>
 
 // Scores of tile t as floats (exp2 units before the max shift) -> running max bookkeeping.  Masks
 // keys >= L.  Returns the tile's multiplier.
+// The int32 scores are converted to float in the same registers (f aliases si's storage).
 template <int HD>
 __device__ __forceinline__ float softmax_prep_q8(v16i (&si)[2], int j0, int L, float cq, float skt,
-                                                 f32x16 (&o)[AttnCfg<uint8_t, HD>::ND], SoftState& st,
-                                                 f32x16 (&f)[2]) {
+                                                 f32x16 (&o)[AttnCfg<uint8_t, HD>::ND], f32x16& lacc,
+                                                 SoftState& st) {
   const int lhalf = (threadIdx.x & 63) >> 5;
+  f32x16 (&f)[2] = reinterpret_cast<f32x16(&)[2]>(si);
   // > 0 so that masked keys (-inf) stay -inf; a zero multiplier (all-zero query or key block) makes
   // every score ~0, which is the exact result up to 1e-30 * |s|.
   const float mul = fmaxf(cq * skt, 1e-30f);
@@ -721,7 +724,8 @@ __device__ __forceinline__ float softmax_prep_q8(v16i (&si)[2], int j0, int L, f
     const float mm = need ? mnew : st.m;
     const float alpha = __builtin_amdgcn_exp2f(st.m - mm);  // 0 on the first tile (m = -inf)
     st.m = mm;
-    st.l *= alpha;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) lacc[r] *= alpha;
 #pragma unroll
     for (int d = 0; d < AttnCfg<uint8_t, HD>::ND; ++d)
 #pragma unroll
@@ -741,12 +745,11 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
 template <int HD>
 __device__ __forceinline__ void softmax_and_next_scores_q8(const u32x4 (&qf)[AttnCfg<uint8_t, HD>::NCH],
                                                            const FragQ8<HD>& fa, const char* kslot, f32x16 (&f)[2],
-                                                           v16i (&sn)[2], float mul, SoftState& st,
+                                                           v16i (&sn)[2], float mul, const SoftState& st,
                                                            uint32_t (&pf)[8]) {
   constexpr int NCH = AttnCfg<uint8_t, HD>::NCH;
   constexpr int EPC = 32 / NCH;  // exponentials per region
   const float negm = Q8_BIAS - st.m;
-  float lsum = 0.f;
   sn[0] = zero16i();
   sn[1] = zero16i();
   u32x4 kf[2][2];
@@ -764,9 +767,7 @@ __device__ __forceinline__ void softmax_and_next_scores_q8(const u32x4 (&qf)[Att
 #pragma unroll
     for (int e = c * EPC; e < (c + 1) * EPC; ++e) {
       // argument <= Q8_TAU + Q8_BIAS = 8 or -inf: raw v_exp_f32, P' <= 256 < 448 (no E4M3 overflow)
-      const float p = __builtin_amdgcn_exp2f(fmaf(f[e >> 4][e & 15], mul, negm));
-      f[e >> 4][e & 15] = p;
-      lsum += p;
+      f[e >> 4][e & 15] = __builtin_amdgcn_exp2f(fmaf(f[e >> 4][e & 15], mul, negm));
     }
 #pragma unroll
     for (int w = (c * EPC) / 4; w < ((c + 1) * EPC) / 4; ++w)
@@ -776,15 +777,18 @@ __device__ __forceinline__ void softmax_and_next_scores_q8(const u32x4 (&qf)[Att
     for (int kb = 0; kb < 2; ++kb) mfma_i8(kf[c & 1][kb], qf[c], sn[kb]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  st.l += lsum;
 }
 
 // O^T += V^T P'^T for one tile: one 32x32x64 FP8 product per 32-channel block of hd.
 template <int HD>
 __device__ __forceinline__ void pv_products_q8(const FragQ8<HD>& fa, const char* vslot, const uint32_t (&pf)[8],
-                                               f32x16 (&o)[AttnCfg<uint8_t, HD>::ND]) {
+                                               f32x16 (&o)[AttnCfg<uint8_t, HD>::ND], f32x16& lacc, int j0, int L) {
   constexpr int ND = AttnCfg<uint8_t, HD>::ND;
   const v8i pb = {(int)pf[0], (int)pf[1], (int)pf[2], (int)pf[3], (int)pf[4], (int)pf[5], (int)pf[6], (int)pf[7]};
+  // l: an all-ones E4M3 operand times P' (keys >= L of the last tile excluded: their P' is 0 anyway)
+  constexpr int ONE4 = 0x38383838;
+  const v8i ones = {ONE4, ONE4, ONE4, ONE4, ONE4, ONE4, ONE4, ONE4};
+  lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pb, lacc, 0, 0, 0, 127, 0, 127);
   u32x4 va[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) va[0][i] = *reinterpret_cast<const u32x4*>(vslot + fa.v[i]);
@@ -811,7 +815,8 @@ __device__ __forceinline__ void pp_tile_q8(const u32x4 (&qf)[AttnCfg<uint8_t, HD
                                            const uint8_t* __restrict__ kbase, const uint8_t* __restrict__ vtb,
                                            const float* __restrict__ skb, int t, int nt, int grp, float cq,
                                            const Slots<uint8_t, HD>& sl, v16i (&s)[2], v16i (&sn)[2],
-                                           f32x16 (&o)[AttnCfg<uint8_t, HD>::ND], SoftState& st, int& last) {
+                                           f32x16 (&o)[AttnCfg<uint8_t, HD>::ND], f32x16& lacc, SoftState& st,
+                                           int& last) {
   using CP = CopyPlan<uint8_t, HD, 8>;
   static_assert(CP::KL == CP::VL, "equal K and V^T copy counts");
   char* k_this = P ? sl.k1 : sl.k0;
@@ -827,10 +832,9 @@ __device__ __forceinline__ void pp_tile_q8(const u32x4 (&qf)[AttnCfg<uint8_t, HD
   } else {
     if (t >= 1 && t + 1 < nt) { load_v_tile<uint8_t, HD, 8>(cp, vtb, j0 + KT, v_next); last = 1; }
   }
-  f32x16 f[2];
-  const float mul = softmax_prep_q8<HD>(s, j0, kv.L, cq, skb[t], o, st, f);
+  const float mul = softmax_prep_q8<HD>(s, j0, kv.L, cq, skb[t], o, lacc, st);
   uint32_t pf[8];
-  softmax_and_next_scores_q8<HD>(qf, fa, k_next, f, sn, mul, st, pf);
+  softmax_and_next_scores_q8<HD>(qf, fa, k_next, reinterpret_cast<f32x16(&)[2]>(s), sn, mul, st, pf);
   // ---- B(t)
   phase_barrier<CP::KL>(last);
   last = 0;
@@ -839,7 +843,7 @@ __device__ __forceinline__ void pp_tile_q8(const u32x4 (&qf)[AttnCfg<uint8_t, HD
   } else {
     if (t + 3 < nt) { load_k_tile<uint8_t, HD, 8>(cp, kbase, kv.k_ss, kv.L, j0 + 3 * KT, k_next); last = 1; }
   }
-  pv_products_q8<HD>(fa, v_this, pf, o);
+  pv_products_q8<HD>(fa, v_this, pf, o, lacc, j0, kv.L);
 }
 
 template <int HD>
@@ -871,6 +875,7 @@ __global__ __launch_bounds__(512, 1) void attention_q8_kernel(const uint8_t* __r
   f32x16 o[C::ND];
 #pragma unroll
   for (int d = 0; d < C::ND; ++d) o[d] = zero16();
+  f32x16 lacc = zero16();  // every element: the query's running sum of E4M3 P'
   SoftState st{-__builtin_inff(), 0.f};
 
   const CP cp(kv.k_ss, kv.Lpad);
@@ -889,13 +894,14 @@ __global__ __launch_bounds__(512, 1) void attention_q8_kernel(const uint8_t* __r
     if (2 < nt) { load_k_tile<uint8_t, HD, 8>(cp, kbase, kv.k_ss, kv.L, 2 * KT, sl.k0); last = 1; }
   }
   for (int t = 0; t < nt; t += 2) {
-    pp_tile_q8<HD, 0>(qf, fa, kv, cp, kbase, vtb, skb, t, nt, grp, cq, sl, sa, sb, o, st, last);
-    if (t + 1 < nt) pp_tile_q8<HD, 1>(qf, fa, kv, cp, kbase, vtb, skb, t + 1, nt, grp, cq, sl, sb, sa, o, st, last);
+    pp_tile_q8<HD, 0>(qf, fa, kv, cp, kbase, vtb, skb, t, nt, grp, cq, sl, sa, sb, o, lacc, st, last);
+    if (t + 1 < nt)
+      pp_tile_q8<HD, 1>(qf, fa, kv, cp, kbase, vtb, skb, t + 1, nt, grp, cq, sl, sb, sa, o, lacc, st, last);
   }
   if (grp == 0) phase_barrier<CP::KL>(0);
 
   // O^T / l, times the V channel scale of each output channel d = 32 dblk + 8 g + 4 lhalf + i.
-  const float lt = st.l + __shfl_xor(st.l, 32, 64);
+  const float lt = lacc[0];
   const float inv = 1.f / lt;
   if (lse != nullptr && lhalf == 0 && qrow < S)
     lse[((int64_t)b * H + h) * S + qrow] = (st.m - Q8_BIAS + log2f(lt)) * 0.69314718055994531f;
@@ -982,7 +988,7 @@ hipError_t launch_attention_q8(const uint8_t* q8, const float* sq, const uint8_t
   if (S <= 0 || B <= 0 || H <= 0) return hipSuccess;
   if (L <= 0) return hipErrorInvalidValue;
   const int64_t dim = (int64_t)H * hd;
-  const KVq8 kv{k8, (int64_t)L * dim, dim, sk, v8t, sv, L, (int)round_up(L, KT)};
+  const KVq8 kv{k8, (int64_t)L * dim, dim, sk, v8t, sv, L, (int)round_up(L, 128)};  // E4M3 V^T row stride
   const float c_log2 = 1.4426950408889634f / sqrtf((float)hd);
   // head_dim 128 only: a 64-key tile of 64-byte rows is too small to split over the 8 waves' copies
   if (hd == 128)

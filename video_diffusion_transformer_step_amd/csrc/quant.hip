@@ -5,8 +5,9 @@
 //    +-127 (float32 quotients and product, IEEE-rounded, so codes are a fixed function of x);
 //  * K -> INT8 per (head, block of 64 consecutive keys), same rule;
 //  * V -> FP8 E4M3 (OCP) per (head, channel) over all keys: scale = amax / 448,
-//    code = e4m3(clamp(x * (448 / amax), -448, 448)), written as V^T [B, H, hd, Lpad] with the keys of
-//    each 64-key tile in the order the FP8 P.V product reads them (wan.h documents it).
+//    code = e4m3(clamp(x * (448 / amax), -448, 448)), written as V^T [B, H, hd, Lpad] (Lpad a multiple
+//    of 128, zero past the keys) with the keys of each 64-key tile in the order the FP8 P.V product
+//    reads them (wan.h documents it).
 // A group whose amax is 0 gets scale 0 and zero codes.
 #include "wan_internal.h"
 
@@ -120,19 +121,19 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   return (uint32_t)w;
 }
 
-// One workgroup = one V^T row (batch row, head, channel d) of Lpad keys.  Input: bf16 V^T whose keys
+// One workgroup = one V^T row (batch row, head, channel d).  Input: bf16 V^T rows of Lpad_in keys whose keys
 // are permuted within 16-key groups (position p holds key p with bits 2 and 3 swapped, the layout of
 // the bf16 attention); output: E4M3 V^T whose 64-key tiles hold at position h*32 + kb*16 + r the key
 // kb*32 + (r/4)*8 + h*4 + r%4, i.e. the 32 keys one lane half of the P.V product consumes are
 // contiguous.  Position r of an output 16-byte group reads input position kb*32 + h*8 + (r%8) +
-// 16 (r/8).
-__global__ __launch_bounds__(256) void quant_vt_kernel(const bf16* __restrict__ vt, int Lpad,
+// 16 (r/8).  Output rows have Lpad_out >= Lpad_in keys; positions past Lpad_in are zero.
+__global__ __launch_bounds__(256) void quant_vt_kernel(const bf16* __restrict__ vt, int Lpad_in, int Lpad_out,
                                                        uint8_t* __restrict__ out, float* __restrict__ scales) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
-  const bf16* src = vt + row * Lpad;
+  const bf16* src = vt + row * Lpad_in;
   float m = 0.f;
-  for (int c = threadIdx.x; c < Lpad / 8; c += 256) {
+  for (int c = threadIdx.x; c < Lpad_in / 8; c += 256) {
     const u32x4 raw = *reinterpret_cast<const u32x4*>(src + c * 8);
     const bf16* e = reinterpret_cast<const bf16*>(&raw);
 #pragma unroll
@@ -143,9 +144,13 @@ __global__ __launch_bounds__(256) void quant_vt_kernel(const bf16* __restrict__ 
   __syncthreads();
   m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float inv = m > 0.f ? 448.f / m : 0.f;
-  uint8_t* dst = out + row * Lpad;
-  for (int g = threadIdx.x; g < Lpad / 16; g += 256) {  // output group g: 16 positions
+  uint8_t* dst = out + row * Lpad_out;
+  for (int g = threadIdx.x; g < Lpad_out / 16; g += 256) {  // output group g: 16 positions
     const int tile = g >> 2, hh = (g >> 1) & 1, kb = g & 1;
+    if (tile * 64 >= Lpad_in) {
+      *reinterpret_cast<u32x4*>(dst + g * 16) = u32x4{0u, 0u, 0u, 0u};
+      continue;
+    }
     const bf16* s0 = src + tile * 64 + kb * 32 + hh * 8;
     const u32x4 r0 = *reinterpret_cast<const u32x4*>(s0);
     const u32x4 r1 = *reinterpret_cast<const u32x4*>(s0 + 16);
@@ -197,10 +202,11 @@ hipError_t launch_quant_k(const bf16* x, int64_t ld, int B, int S, int H, int hd
   return hipGetLastError();
 }
 
-hipError_t launch_quant_vt(const bf16* vt, int64_t rows, int Lpad, uint8_t* out, float* scales, hipStream_t s) {
+hipError_t launch_quant_vt(const bf16* vt, int64_t rows, int Lpad_in, int Lpad_out, uint8_t* out, float* scales,
+                           hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (Lpad % 64 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(quant_vt_kernel, dim3((unsigned)rows), dim3(256), 0, s, vt, Lpad, out, scales);
+  if (Lpad_in % 64 != 0 || Lpad_out % 64 != 0 || Lpad_out < Lpad_in) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_vt_kernel, dim3((unsigned)rows), dim3(256), 0, s, vt, Lpad_in, Lpad_out, out, scales);
   return hipGetLastError();
 }
 

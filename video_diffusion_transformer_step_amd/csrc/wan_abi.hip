@@ -151,7 +151,7 @@ size_t block_plan(const wan_block_cfg& c, const wan_grid& g, int B, char* base, 
   if (c.flags & WAN_FLAG_FP8_ATTN) {
     w.q8 = cv.take<uint8_t>(BS * dim);
     w.k8 = cv.take<uint8_t>(BS * dim);
-    w.v8t = cv.take<uint8_t>((size_t)B * dim * pad64(S));
+    w.v8t = cv.take<uint8_t>((size_t)B * dim * round_up(S, 128));
     w.sq = cv.take<float>((size_t)B * c.heads * S);
     w.sk = cv.take<float>((size_t)B * c.heads * (pad64(S) / 64));
     w.sv = cv.take<float>((size_t)B * dim);
@@ -182,7 +182,7 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
     if (c.flags & WAN_FLAG_FP8_ATTN) {  // quantised self-attention ("Wan 技术深度解析" §5.3)
       PROF_TRY(WAN_K_QUANT, launch_quant_q(w.qkv, 2 * dim, B, S, H, hd, (int8_t*)w.q8, w.sq, st));
       PROF_TRY(WAN_K_QUANT, launch_quant_k(w.qkv + dim, 2 * dim, B, S, H, hd, (int8_t*)w.k8, w.sk, st));
-      PROF_TRY(WAN_K_QUANT, launch_quant_vt(w.vt, (int64_t)B * dim, Spad, w.v8t, w.sv, st));
+      PROF_TRY(WAN_K_QUANT, launch_quant_vt(w.vt, (int64_t)B * dim, Spad, (int)round_up(S, 128), w.v8t, w.sv, st));
       PROF_TRY(WAN_K_SELF_ATTN, launch_attention_q8(w.q8, w.sq, w.k8, w.sk, w.v8t, w.sv, B, S, S, H, hd, w.o, nullptr, st));
     }
   }
@@ -671,7 +671,7 @@ int wan_attention_q8_quantize(const void* q, const void* k, const void* v, int32
   HIP_TRY(launch_quant_q((const bf16*)q, dim, B, Sq, heads, head_dim, (int8_t*)q8, sq, st));
   HIP_TRY(launch_quant_k((const bf16*)k, dim, B, Sk, heads, head_dim, (int8_t*)k8, sk, st));
   HIP_TRY(launch_transpose_heads<bf16>((const bf16*)v, dim, 0, B, Sk, heads, head_dim, Skpad, vt, st));
-  HIP_TRY(launch_quant_vt(vt, (int64_t)B * dim, Skpad, (uint8_t*)v8t, sv, st));
+  HIP_TRY(launch_quant_vt(vt, (int64_t)B * dim, Skpad, (int)round_up(Sk, 128), (uint8_t*)v8t, sv, st));
   return WAN_OK;
 }
 

@@ -95,7 +95,7 @@ hipError_t launch_attention(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0,
                             hipStream_t s, float* lse = nullptr);
 
 // Quantised attention (INT8 Q.K, FP8 P.V): q8 [B, S, H, hd] INT8 codes with sq [B, H, S]; k8 [B, L, H, hd]
-// INT8 codes with sk [B, H, ceil(L / 64)]; v8t [B, H, hd, round_up(L, 64)] E4M3 codes (keys in P.V
+// INT8 codes with sk [B, H, ceil(L / 64)]; v8t [B, H, hd, round_up(L, 128)] E4M3 codes (keys in P.V
 // order, zero past L) with sv [B, H, hd]; o [B, S, H, hd] bf16; lse [B, H, S] or NULL.
 hipError_t launch_attention_q8(const uint8_t* q8, const float* sq, const uint8_t* k8, const float* sk,
                                const uint8_t* v8t, const float* sv, int B, int S, int L, int H, int hd, bf16* o,
@@ -107,9 +107,11 @@ hipError_t launch_quant_q(const bf16* x, int64_t ld, int B, int S, int H, int hd
                           hipStream_t s);  // codes [B*S, H*hd], scales [B, H, S]
 hipError_t launch_quant_k(const bf16* x, int64_t ld, int B, int S, int H, int hd, int8_t* codes, float* scales,
                           hipStream_t s);  // codes [B*S, H*hd], scales [B, H, ceil(S / 64)]
-// bf16 V^T rows (keys in the bf16 attention's order, Lpad a multiple of 64) -> E4M3 V^T rows in the
-// quantised attention's order, scales [rows].
-hipError_t launch_quant_vt(const bf16* vt, int64_t rows, int Lpad, uint8_t* out, float* scales, hipStream_t s);
+// bf16 V^T rows of Lpad_in keys (the bf16 attention's order, Lpad_in a multiple of 64) -> E4M3 V^T rows of
+// Lpad_out >= Lpad_in keys (multiple of 64, zero past Lpad_in) in the quantised attention's order,
+// scales [rows].
+hipError_t launch_quant_vt(const bf16* vt, int64_t rows, int Lpad_in, int Lpad_out, uint8_t* out, float* scales,
+                           hipStream_t s);
 
 // Combine n (1..MERGE_MAX_PARTS) attention results of the same queries over disjoint key chunks:
 // o_parts[i] [B, S, H, hd] T, lse_parts[i] [B, H, S] float32 (host arrays of device pointers);
