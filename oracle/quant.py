@@ -18,13 +18,17 @@ Readings (the page gives no granularity, rounding or encoding):
   code = e4m3(clamp(x * (448 / amax), -448, 448)).
 * The attention result is softmax(q k^T / sqrt(d)) v as in ``wan_oracle.attention``; the quantised
   path is compared with that definition within an error bound derived from the code precisions.
+
+[Wan-deep-dive §5.3] also lists FP8 GEMMs: weights quantised per tensor, activations per token.
+Reading: both in E4M3 with scale = amax / 448 and code = e4m3(clamp(x * (448 / amax), -448, 448)) (the
+same rule as V); the product is y = (sum_k a_code w_code) * (s_row * s_w) + bias.
 """
 from __future__ import annotations
 
 import numpy as np
 
 __all__ = ["e4m3_values", "e4m3_encode", "e4m3_decode", "int8_group", "quant_q_int8", "quant_k_int8",
-           "quant_v_e4m3"]
+           "quant_v_e4m3", "e4m3_group", "quant_rows_e4m3", "quant_tensor_e4m3", "gemm_e4m3"]
 
 KEY_BLOCK = 64  # keys per K scale group
 
@@ -127,3 +131,37 @@ def quant_v_e4m3(v):
             codes[b, :, h, :] = np.where(amax[None, :] > 0, c, 0)
             scales[b, h] = np.where(amax > 0, (amax / np.float32(448)).astype(np.float32), 0)
     return codes, scales
+
+
+def e4m3_group(x):
+    """E4M3 codes of one group of float32 values: (codes uint8, scale float32), scale = amax / 448."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
+    if amax == 0:
+        return np.zeros(x.shape, np.uint8), np.float32(0)
+    inv = np.float32(448) / amax
+    y = np.clip((x * inv).astype(np.float32), -448, 448)
+    return e4m3_encode(y), np.float32(amax / np.float32(448))
+
+
+def quant_rows_e4m3(x):
+    """Per-token activation codes: x [M, K] -> (codes [M, K], scales [M])."""
+    x = np.asarray(x, dtype=np.float32)
+    codes = np.empty(x.shape, np.uint8)
+    scales = np.empty(x.shape[0], np.float32)
+    for m in range(x.shape[0]):
+        codes[m], scales[m] = e4m3_group(x[m])
+    return codes, scales
+
+
+def quant_tensor_e4m3(w):
+    """Per-tensor weight codes: w [N, K] -> (codes [N, K], scale)."""
+    return e4m3_group(np.asarray(w, dtype=np.float32))
+
+
+def gemm_e4m3(a_codes, a_scales, w_codes, w_scale, bias=None):
+    """y [M, N] = (decode(a) decode(w)^T) * (a_scale[m] * w_scale) + bias, in float64."""
+    a = e4m3_decode(a_codes) * np.asarray(a_scales, np.float64)[:, None]
+    w = e4m3_decode(w_codes) * float(w_scale)
+    y = a @ w.T
+    return y if bias is None else y + np.asarray(bias, np.float64)

@@ -84,7 +84,33 @@ def pin_v_channels(q):
     assert np.all(err <= bound)
 
 
-PINS = [pin_e4m3_defining_values, pin_e4m3_matches_library, pin_int8_group, pin_k_blocks, pin_v_channels]
+def pin_rows_and_tensor(q):
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((5, 96)) * rng.uniform(0.01, 10, (5, 1))).astype(np.float32)
+    x[2] = 0.0
+    codes, scales = q.quant_rows_e4m3(x)
+    assert scales[2] == 0 and not codes[2].any()
+    for m in (0, 1, 3, 4):  # each row's largest magnitude maps to +-448, independently of the others
+        assert np.max(np.abs(q.e4m3_decode(codes[m]))) == 448.0
+        assert scales[m] == np.float32(np.max(np.abs(x[m])) / np.float32(448))
+    c2, s2 = q.quant_rows_e4m3(x[[4, 0]])
+    assert np.array_equal(c2[1], codes[0]) and s2[1] == scales[0]
+    w = rng.standard_normal((7, 96)).astype(np.float32)
+    wc, ws = q.quant_tensor_e4m3(w)
+    assert np.max(np.abs(q.e4m3_decode(wc))) == 448.0 and ws == np.float32(np.abs(w).max() / np.float32(448))
+    # the scaled product of exactly representable codes is the plain product
+    y = q.gemm_e4m3(codes, scales, wc, ws)
+    ref = (q.e4m3_decode(codes) * scales[:, None].astype(np.float64)) @ (q.e4m3_decode(wc) * float(ws)).T
+    assert np.allclose(y, ref, rtol=1e-12, atol=0)
+    # and approximates x w^T within the E4M3 rounding of both operands
+    exact = x.astype(np.float64) @ w.astype(np.float64).T
+    rows = [0, 1, 3, 4]
+    rel = np.linalg.norm(y[rows] - exact[rows]) / np.linalg.norm(exact[rows])
+    assert rel < 2.0 ** -4, rel
+
+
+PINS = [pin_e4m3_defining_values, pin_e4m3_matches_library, pin_int8_group, pin_k_blocks, pin_v_channels,
+        pin_rows_and_tensor]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
