@@ -256,40 +256,48 @@ def main():
         log(f"copied {n * 4} bytes (counter calibration)")
         del src, dst
 
-    # ---- the same step with the quantised self-attention (reported beside the bf16 headline)
-    fp8 = None
-    if not args.no_fp8 and c.dtype == "bf16" and c.head_dim == 128:
-        buf8 = R.alloc_step(c, c.B, fp8_attn=True)
-        x8 = torch.from_numpy(x_t).cuda()
+    # ---- the same step on the FP8 paths (reported beside the bf16 headline): the quantised
+    # self-attention alone, then with the E4M3 Q/K/V, O, FFN1, FFN2 products as well
+    fp8 = {}
+    if not args.no_fp8 and c.dtype == "bf16" and c.head_dim == 128 and c.dim % 256 == 0 and c.ffn_dim % 256 == 0:
+        for b in blocks:
+            b.enable_e4m3()
+        for key, gemm8, note in (
+                ("fp8_attention_step", False,
+                 "self-attention in INT8 (Q.K) / FP8 E4M3 (P.V); every other kernel as in the bf16 step"),
+                ("fp8_step", True,
+                 "self-attention as above; Q/K/V, O, FFN1, FFN2 products in E4M3 (per-token activation, per-tensor "
+                 "weight scales); the rest (norms, cross-attention, head) as in the bf16 step")):
+            buf8 = R.alloc_step(c, c.B, fp8_attn=True, fp8_gemm=gemm8)
+            x8 = torch.from_numpy(x_t).cuda()
 
-        def step8(k):
-            R.denoise_step(c, model, blocks, caches, x8, zg, 1.0 + k * dt, dt, c.guidance, buf8, c.B, fp8_attn=True)
+            def step8(k):
+                R.denoise_step(c, model, blocks, caches, x8, zg, 1.0 + k * dt, dt, c.guidance, buf8, c.B,
+                               fp8_attn=True, fp8_gemm=gemm8)
 
-        for k in range(args.warmup):
-            step8(k)
-        torch.cuda.synchronize()
-        t8 = L.KernelTimer(capacity=args.steps * layers * 4, kernels=("self_attn", "quant"))
-        t0 = time.perf_counter()
-        with t8:
-            for k in range(args.steps):
-                step8(args.warmup + k)
-        torch.cuda.synchronize()
-        ms8 = (time.perf_counter() - t0) * 1e3 / args.steps
-        tm = t8.times_ms()
-        a8 = float(np.mean(tm.get("self_attn", [float("nan")])))
-        q8 = float(np.sum(tm.get("quant", [0.0]))) / (args.steps * layers)
-        tf8 = attn_flops / (a8 * 1e-3) / 1e12
-        assert np.isfinite(x8.float().cpu().numpy()).all(), "non-finite latent after the quantised steps"
-        fp8 = {"ms_per_step": round(ms8, 3), "ms_per_block": round(ms8 / layers, 3),
-               "attention_ms": round(a8, 4), "attention_tflops": round(tf8, 1),
-               "attention_frac_of_fp8_peak": round(tf8 / PEAK_FP8_TFLOPS, 4),
-               "attention_frac_of_bf16_peak": round(tf8 / PEAK_BF16_TFLOPS, 4),
-               "quantise_ms_per_block": round(q8, 4),
-               "step_speedup_vs_bf16": round(ms_per_step / ms8, 3),
-               "note": "self-attention in INT8 (Q.K) / FP8 E4M3 (P.V); every other kernel as in the bf16 step"}
-        log(f"quantised self-attention: {ms8:.2f} ms/step, attention {a8:.3f} ms ({tf8:.0f} TFLOP/s), "
-            f"quantisers {q8:.3f} ms/block")
-        del buf8, x8
+            for k in range(args.warmup):
+                step8(k)
+            torch.cuda.synchronize()
+            t8 = L.KernelTimer(capacity=args.steps * layers * 8, kernels=("self_attn", "quant"))
+            t0 = time.perf_counter()
+            with t8:
+                for k in range(args.steps):
+                    step8(args.warmup + k)
+            torch.cuda.synchronize()
+            ms8 = (time.perf_counter() - t0) * 1e3 / args.steps
+            tm = t8.times_ms()
+            a8 = float(np.mean(tm.get("self_attn", [float("nan")])))
+            q8 = float(np.sum(tm.get("quant", [0.0]))) / (args.steps * layers)
+            tf8 = attn_flops / (a8 * 1e-3) / 1e12
+            assert np.isfinite(x8.float().cpu().numpy()).all(), "non-finite latent after the FP8 steps"
+            fp8[key] = {"ms_per_step": round(ms8, 3), "ms_per_block": round(ms8 / layers, 3),
+                        "attention_ms": round(a8, 4), "attention_tflops": round(tf8, 1),
+                        "attention_frac_of_fp8_peak": round(tf8 / PEAK_FP8_TFLOPS, 4),
+                        "attention_frac_of_bf16_peak": round(tf8 / PEAK_BF16_TFLOPS, 4),
+                        "quantise_ms_per_block": round(q8, 4),
+                        "step_speedup_vs_bf16": round(ms_per_step / ms8, 3), "note": note}
+            log(f"{key}: {ms8:.2f} ms/step, attention {a8:.3f} ms ({tf8:.0f} TFLOP/s), quantisers {q8:.3f} ms/block")
+            del buf8, x8
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -326,7 +334,8 @@ def main():
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "launch_ms": round(attn_avg, 4), "flops_per_launch": attn_flops},
         "breakdown_ms_per_block": breakdown,
-        "fp8_attention_step": fp8,
+        "fp8_attention_step": fp8.get("fp8_attention_step"),
+        "fp8_step": fp8.get("fp8_step"),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -60,11 +60,15 @@ typedef struct {
 
 /* Block hyper-parameters.  dim = heads * head_dim; head_dim 64 or 128; dim % 8 == 0, dim <= 6144;
  * text_len > 0 text keys; img_len >= 0 image keys (0 = single-stream cross-attention).
- * Proposed eps 1e-6 for both norms and rope_theta 10000.  flags: 0, or WAN_FLAG_FP8_ATTN. */
+ * Proposed eps 1e-6 for both norms and rope_theta 10000.  flags: 0 or WAN_FLAG_FP8_ATTN | WAN_FLAG_FP8_GEMM. */
 /* WAN_FLAG_FP8_ATTN: the block's self-attention runs the quantised path of wan_attention_q8_fwd (INT8
  * Q.K, E4M3 P.V; [DEEP] §5.3) on the rotated q, k and v it computes; requires dtype WAN_BF16 and
  * head_dim 128.  Everything else in the block is unchanged. */
 #define WAN_FLAG_FP8_ATTN 1u
+/* WAN_FLAG_FP8_GEMM: the Q/K/V, O, FFN1 and FFN2 products run in E4M3 as in wan_gemm_e4m3 (activations
+ * quantised per token inside the block, weights taken from w->e4m3); requires dtype WAN_BF16 and dim
+ * and ffn_dim multiples of 256.  The cross-attention products stay bf16. */
+#define WAN_FLAG_FP8_GEMM 2u
 
 typedef struct {
   int32_t dim, heads, head_dim, ffn_dim;
@@ -79,7 +83,14 @@ typedef struct {
  * w1 [ffn_dim, dim]; w2 [dim, ffn_dim].  float32 vectors: mod_bias [6, dim] (chunks shift1, scale1,
  * gate1, shift2, scale2, gate2); bqkv [3*dim]; gq, gk [dim] RMSNorm gains; bo; ln3_w, ln3_b [dim]
  * (affine LayerNorm before cross-attention); bcq, bco [dim]; b1 [ffn_dim]; b2 [dim].
- * Bias pointers may be NULL (zero bias); all others are required. */
+ * Bias pointers may be NULL (zero bias); all others are required.  e4m3: NULL, or (required under
+ * WAN_FLAG_FP8_GEMM) the E4M3 codes of wqkv, wo, w1, w2 with one float32 device scale each, as made by
+ * wan_quantize_tensor_e4m3. */
+typedef struct {
+  const void *wqkv, *wo, *w1, *w2;
+  const float *s_wqkv, *s_wo, *s_w1, *s_w2;
+} wan_block_weights_e4m3;
+
 typedef struct {
   const float* mod_bias;
   const void* wqkv;
@@ -96,6 +107,7 @@ typedef struct {
   const float* b1;
   const void* w2;
   const float* b2;
+  const wan_block_weights_e4m3* e4m3;
 } wan_block_weights;
 
 /* Cross-attention keys/values of one block, computed once per generation by wan_cross_kv_fwd
@@ -277,6 +289,23 @@ int wan_attention_q8_quantize(const void* q, const void* k, const void* v, int32
 int wan_attention_q8_fwd(const void* q8, const float* sq, const void* k8, const float* sk, const void* v8t,
                          const float* sv, int32_t B, int32_t Sq, int32_t Sk, int32_t heads, int32_t head_dim, void* o,
                          float* lse, wan_stream_t stream);
+
+/* FP8 GEMMs.  [DEEP] §5.3 also lists FP8 GEMMs with weights quantised per tensor and activations per
+ * token.  Codes are OCP E4M3 as above, scale = amax / 448, code = e4m3(clamp(x * (448 / amax))).
+ * wan_quantize_rows_e4m3: x [rows, cols] bf16 (row stride ld elements, cols % 8 == 0) -> codes uint8
+ *   [rows, cols] (row stride ldc bytes, % 16 == 0) and scales float32 [rows], one per row.
+ * wan_quantize_tensor_e4m3: x [n] bf16 (n % 8 == 0) -> codes [n] and one float32 scale, both on the
+ *   device; ws: at least 256 bytes of device scratch.
+ * wan_gemm_e4m3: y [M, N] bf16 (row stride ldy elements) = act((A W^T) * a_scales[m] * w_scale[0] + bias[n])
+ *   from codes A [M, K] (row stride lda bytes) and W [N, K] (row stride ldw bytes); K % 256 == 0,
+ *   N % 4 == 0, strides % 16 == 0; act 0 = none, 1 = GELU (erf); bias may be NULL. */
+int wan_quantize_rows_e4m3(const void* x, int64_t ld, int32_t rows, int32_t cols, void* codes, int64_t ldc,
+                           float* scales, wan_stream_t stream);
+int wan_quantize_tensor_e4m3(const void* x, int64_t n, void* codes, float* scale, void* ws, size_t ws_bytes,
+                             wan_stream_t stream);
+int wan_gemm_e4m3(const void* a, int64_t lda, const float* a_scales, const void* w, int64_t ldw, const float* w_scale,
+                  int32_t M, int32_t N, int32_t K, const float* bias, int32_t act, void* y, int64_t ldy,
+                  wan_stream_t stream);
 
 /* Kernel timing (measurement only).  wan_profile_begin hands the library `capacity` caller-created
  * HIP events (hipEvent_t, passed as void*) for starts and stops plus an int32 tag array; until

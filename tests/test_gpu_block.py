@@ -35,11 +35,13 @@ def _inputs(c, seed=0):
     return x, e0, t_emb, i_emb, bw
 
 
-def _gpu_block(c, x, e0, t_emb, i_emb, bw, repeat=1, fp8_attn=False):
+def _gpu_block(c, x, e0, t_emb, i_emb, bw, repeat=1, fp8_attn=False, fp8_gemm=False):
     td = torch.bfloat16 if c.dtype == "bf16" else torch.float32
     blk = R.DeviceBlock(bw, c.dtype)
+    if fp8_gemm:
+        blk.enable_e4m3()
     (kc,) = R.cross_kv_all(c, [blk], dev(t_emb, td), None if i_emb is None else dev(i_emb, td), c.B)
-    cfg = R.cfg_of(c, fp8_attn=fp8_attn)
+    cfg = R.cfg_of(c, fp8_attn=fp8_attn, fp8_gemm=fp8_gemm)
     ws = torch.empty(L.block_ws_bytes(cfg, c.grid, c.B), dtype=torch.uint8, device="cuda")
     outs = []
     for _ in range(repeat):
@@ -157,3 +159,32 @@ def test_block_fp8_attention_full_size():
     got, = _gpu_block(c, x, e0, t_emb, i_emb, bw, fp8_attn=True)
     ref = _oracle_block(c, x, e0, t_emb, i_emb, bw, rows=rows)
     _check(c, got, ref, x, rows=rows, tol=FP8_TOL)
+
+
+# The whole FP8 row (quantised self-attention and E4M3 Q/K/V, O, FFN1, FFN2 products).  Each E4M3
+# product carries <= 2^-4 rel-L2 (test_gpu_fp8_gemm.py); the FFN branch chains two (FFN1's error enters
+# FFN2's input), so a branch output carries up to ~2 x 2^-4 and dx is held to 2^-3.
+FP8_ALL_TOL = 2.0 ** -3
+
+
+def test_block_fp8_all_small():
+    require_gpu()
+    c = wi.get_config("tiny").replace(dtype="bf16", T=3, H=12, W=20, B=2, dim=256, heads=2, head_dim=128,
+                                      ffn_dim=768, text_len=70, img_len=9, img_dim=32)
+    case(f"block fp8 attention + e4m3 gemms {c.name} S={c.S}")
+    x, e0, t_emb, i_emb, bw = _inputs(c)
+    got, = _gpu_block(c, x, e0, t_emb, i_emb, bw, fp8_attn=True, fp8_gemm=True)
+    ref = _oracle_block(c, x, e0, t_emb, i_emb, bw)
+    _check(c, got, ref, x, tol=FP8_ALL_TOL)
+
+
+@pytest.mark.timeout(900)
+def test_block_fp8_all_full_size():
+    require_gpu()
+    c = wi.get_config("t2v-1.3b")
+    case(f"block fp8 attention + e4m3 gemms full size {c.name}")
+    rows = wi.sample_rows(c, 64, seed=4)
+    x, e0, t_emb, i_emb, bw = _inputs(c, seed=4)
+    got, = _gpu_block(c, x, e0, t_emb, i_emb, bw, fp8_attn=True, fp8_gemm=True)
+    ref = _oracle_block(c, x, e0, t_emb, i_emb, bw, rows=rows)
+    _check(c, got, ref, x, rows=rows, tol=FP8_ALL_TOL)

@@ -33,9 +33,13 @@ class BlockCfg(C.Structure):
                 ("ln_eps", C.c_float), ("rms_eps", C.c_float), ("rope_theta", C.c_float)]
 
 
+class BlockWeightsE4M3(C.Structure):
+    _fields_ = [(n, vp) for n in ("wqkv", "wo", "w1", "w2", "s_wqkv", "s_wo", "s_w1", "s_w2")]
+
+
 class BlockWeights(C.Structure):
     _fields_ = [(n, vp) for n in ("mod_bias", "wqkv", "bqkv", "gq", "gk", "wo", "bo", "ln3_w", "ln3_b", "wcq",
-                                  "bcq", "wco", "bco", "w1", "b1", "w2", "b2")]
+                                  "bcq", "wco", "bco", "w1", "b1", "w2", "b2")] + [("e4m3", C.POINTER(BlockWeightsE4M3))]
 
 
 class CrossKV(C.Structure):
@@ -89,6 +93,10 @@ _SIGS = {
                                    vp, vp, vp, C.c_size_t, vp], C.c_int),
     "wan_attention_q8_fwd": ([vp, vp, vp, vp, vp, vp, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, vp, vp,
                               vp], C.c_int),
+    "wan_quantize_rows_e4m3": ([vp, C.c_int64, C.c_int32, C.c_int32, vp, C.c_int64, vp, vp], C.c_int),
+    "wan_quantize_tensor_e4m3": ([vp, C.c_int64, vp, vp, vp, C.c_size_t, vp], C.c_int),
+    "wan_gemm_e4m3": ([vp, C.c_int64, vp, vp, C.c_int64, vp, C.c_int32, C.c_int32, C.c_int32, vp, C.c_int32, vp,
+                       C.c_int64, vp], C.c_int),
     "wan_profile_begin": ([C.POINTER(C.c_void_p), C.POINTER(C.c_void_p), C.POINTER(C.c_int32), C.c_int32,
                            C.c_uint32], C.c_int),
     "wan_profile_end": ([], C.c_int32),
@@ -149,6 +157,7 @@ def dtype_code(torch_dtype):
 
 
 WAN_FLAG_FP8_ATTN = 1
+WAN_FLAG_FP8_GEMM = 2
 
 
 def block_cfg(dim, heads, head_dim, ffn_dim, text_len, img_len, dtype, ln_eps=1e-6, rms_eps=1e-6,
@@ -311,6 +320,28 @@ def attention_q8_fwd(codes: Q8Codes, o, lse=None, stream=None):
     c = codes
     _check(lib().wan_attention_q8_fwd(_p(c.q8), _p(c.sq), _p(c.k8), _p(c.sk), _p(c.v8t), _p(c.sv), B, Sq, Sk, H, hd,
                                       _p(o), _p(lse), _stream(stream)), "wan_attention_q8_fwd")
+
+
+def quantize_rows_e4m3(x, codes, scales, stream=None):
+    """x [rows, cols] bf16 -> codes uint8 [rows, cols], scales float32 [rows]."""
+    rows, cols = x.shape
+    _check(lib().wan_quantize_rows_e4m3(_p(x), x.stride(0), rows, cols, _p(codes), codes.stride(0), _p(scales),
+                                        _stream(stream)), "wan_quantize_rows_e4m3")
+
+
+def quantize_tensor_e4m3(x, codes, scale, ws, stream=None):
+    """x bf16 (any shape, n % 8 == 0) -> codes uint8 (same shape), scale float32 [1] (device)."""
+    _check(lib().wan_quantize_tensor_e4m3(_p(x), x.numel(), _p(codes), _p(scale), _p(ws),
+                                          ws.numel() * ws.element_size(), _stream(stream)),
+           "wan_quantize_tensor_e4m3")
+
+
+def gemm_e4m3(a_codes, a_scales, w_codes, w_scale, y, bias=None, act=0, stream=None):
+    M, K = a_codes.shape
+    N = w_codes.shape[0]
+    _check(lib().wan_gemm_e4m3(_p(a_codes), a_codes.stride(0), _p(a_scales), _p(w_codes), w_codes.stride(0),
+                               _p(w_scale), M, N, K, _p(bias), act, _p(y), y.stride(0), _stream(stream)),
+           "wan_gemm_e4m3")
 
 
 KERNEL_IDS = ["ln1", "qkv_gemm", "qk_norm_rope", "vt_tail", "self_attn", "o_gemm", "ln3", "cross_q_gemm",

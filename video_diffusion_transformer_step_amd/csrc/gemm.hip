@@ -360,7 +360,12 @@ struct LdsSlots {
 // always refills the freed slot (past the last stage it re-copies stage 0, which is never read), so
 // the body is straight-line code with a constant wait count: at the start of step kt exactly
 // ST - 2 later stages are in flight.
-template <int BM, int BN, int BK, int ST, int WM, int WN, int P>
+//
+// F8: the operands are E4M3 codes.  A row of 2 BK codes occupies the bytes of BK bf16 elements, so
+// the copies and the LDS layout are unchanged; each K step is then one
+// v_mfma_scale_f32_32x32x64_f8f6f4 per output block (unit block scales) on 32-byte fragments
+// (lane half h reads 16-byte chunks 2h and 2h + 1 of its row, the same k for A and W).
+template <int BM, int BN, int BK, int ST, int WM, int WN, int P, bool F8 = false>
 __device__ __forceinline__ void lds_gemm_step(const LdsCopyPlan<BM, BN, BK, WM * WN>& cp,
                                               const LdsSlots<BM, BN, BK, ST, WM, WN>& sl, int kt, int nk,
                                               f32x16 (&acc)[BM / WM / 32][BN / WN / 32]) {
@@ -384,6 +389,33 @@ __device__ __forceinline__ void lds_gemm_step(const LdsCopyPlan<BM, BN, BK, WM *
   const int wm = wave / WN, wn = wave % WN;
   const char* sa = sl.a[P];
   const char* sb = sl.b[P];
+  if constexpr (F8) {
+    static_assert(BK == 32, "one 64-code step per E4M3 product");
+    u32x4 af[FM][2], bfr[FN][2];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+        af[i][x] = *reinterpret_cast<const u32x4*>(sa + C::off(wm * (BM / WM) + i * 32 + lrow, 2 * lhalf + x));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+        bfr[j][x] = *reinterpret_cast<const u32x4*>(sb + C::off(wn * (BN / WN) + j * 32 + lrow, 2 * lhalf + x));
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        typedef int v8i_t __attribute__((ext_vector_type(8)));
+        const v8i_t a = {(int)bfr[j][0].x, (int)bfr[j][0].y, (int)bfr[j][0].z, (int)bfr[j][0].w,
+                         (int)bfr[j][1].x, (int)bfr[j][1].y, (int)bfr[j][1].z, (int)bfr[j][1].w};
+        const v8i_t b = {(int)af[i][0].x, (int)af[i][0].y, (int)af[i][0].z, (int)af[i][0].w,
+                         (int)af[i][1].x, (int)af[i][1].y, (int)af[i][1].z, (int)af[i][1].w};
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 0, 0, 0, 127, 0, 127);
+      }
+    if constexpr (ST > 2) cp.issue((kn < nk ? kn : 0) * BK, sl.a[Q], sl.b[Q]);
+    return;
+  }
 #pragma unroll
   for (int kc = 0; kc < BK / 16; ++kc) {
     u32x4 af[FM], bfr[FN];
@@ -401,7 +433,7 @@ __device__ __forceinline__ void lds_gemm_step(const LdsCopyPlan<BM, BN, BK, WM *
   if constexpr (ST > 2) cp.issue((kn < nk ? kn : 0) * BK, sl.a[Q], sl.b[Q]);
 }
 
-template <int BM, int BN, int BK, int ST, int WM, int WN, class Epi>
+template <int BM, int BN, int BK, int ST, int WM, int WN, class Epi, bool F8 = false>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(const bf16* __restrict__ A, int64_t lda,
                                                                 const bf16* __restrict__ W, int64_t ldw, int M,
                                                                 int N, int K, int tiles_m, int tiles_n, int gm,
@@ -433,10 +465,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(const bf16* __res
 #pragma unroll
   for (int s = 0; s < ST - 1; ++s) cp.issue(s * BK, sl.a[s], sl.b[s]);
   for (int kt = 0; kt < nk; kt += ST) {
-    lds_gemm_step<BM, BN, BK, ST, WM, WN, 0>(cp, sl, kt, nk, acc);
-    lds_gemm_step<BM, BN, BK, ST, WM, WN, 1>(cp, sl, kt + 1, nk, acc);
-    if constexpr (ST > 2) lds_gemm_step<BM, BN, BK, ST, WM, WN, 2 % ST>(cp, sl, kt + 2, nk, acc);
-    if constexpr (ST > 3) lds_gemm_step<BM, BN, BK, ST, WM, WN, 3 % ST>(cp, sl, kt + 3, nk, acc);
+    lds_gemm_step<BM, BN, BK, ST, WM, WN, 0, F8>(cp, sl, kt, nk, acc);
+    lds_gemm_step<BM, BN, BK, ST, WM, WN, 1, F8>(cp, sl, kt + 1, nk, acc);
+    if constexpr (ST > 2) lds_gemm_step<BM, BN, BK, ST, WM, WN, 2 % ST, F8>(cp, sl, kt + 2, nk, acc);
+    if constexpr (ST > 3) lds_gemm_step<BM, BN, BK, ST, WM, WN, 3 % ST, F8>(cp, sl, kt + 3, nk, acc);
   }
   wait_vmcnt<0>();  // the surplus copies past the last stage land before the LDS is released
 
@@ -457,13 +489,39 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(const bf16* __res
   }
 }
 
-template <int BM, int BN, int BK, int ST, int WM, int WN, class Epi>
+template <int BM, int BN, int BK, int ST, int WM, int WN, class Epi, bool F8 = false>
 hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K, const Epi& epi,
                       hipStream_t s) {
   const int tm = (int)ceil_div(M, BM), tn = (int)ceil_div(N, BN);
-  hipLaunchKernelGGL((gemm_lds_kernel<BM, BN, BK, ST, WM, WN, Epi>), dim3((unsigned)(tm * tn)), dim3(WM * WN * 64),
-                     0, s, A, lda, W, ldw, M, N, K, tm, tn, group_m(tn, K), epi);
+  hipLaunchKernelGGL((gemm_lds_kernel<BM, BN, BK, ST, WM, WN, Epi, F8>), dim3((unsigned)(tm * tn)),
+                     dim3(WM * WN * 64), 0, s, A, lda, W, ldw, M, N, K, tm, tn, group_m(tn, K), epi);
   return hipGetLastError();
+}
+
+// Epilogue wrapper of the E4M3 products: the accumulator times (row scale * tensor scale), then the
+// wrapped epilogue.
+template <class Epi>
+struct EpiScaled {
+  const float* row_scale;
+  const float* w_scale;  // one value, on the device
+  Epi inner;
+  __device__ __forceinline__ void operator()(int m, int n, float4 v) const {
+    const float sc = row_scale[m] * *w_scale;
+    v.x *= sc; v.y *= sc; v.z *= sc; v.w *= sc;
+    inner(m, n, v);
+  }
+};
+
+// E4M3 product ("Wan 技术深度解析" §5.3: per-token activation, per-tensor weight scales): A codes [M, K]
+// (row stride lda bytes) with per-row scales, W codes [N, K] (row stride ldw bytes) with one tensor scale.  K a multiple of 256, strides multiples of 16 bytes.
+template <class Epi>
+hipError_t run_gemm_e4m3(const uint8_t* A, int64_t lda, const float* a_scales, const uint8_t* W, int64_t ldw,
+                         const float* w_scale, int M, int N, int K, const Epi& epi, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (N % 4 != 0 || K % 256 != 0 || lda % 16 != 0 || ldw % 16 != 0) return hipErrorInvalidValue;
+  return launch_lds<256, 256, 32, 4, 4, 2, EpiScaled<Epi>, true>(
+      reinterpret_cast<const bf16*>(A), lda / 2, reinterpret_cast<const bf16*>(W), ldw / 2, M, N, K / 2,
+      EpiScaled<Epi>{a_scales, w_scale, epi}, s);
 }
 
 template <typename T, int BM, int BN, int WM, int WN, class Epi>
@@ -573,6 +631,28 @@ hipError_t gemm_residual(const T* A, int64_t lda, const T* W, int64_t ldw, int M
                          const float* e0, const float* mb, int chunk, int S, float* x, int64_t ldx, hipStream_t s) {
   EpiResidual epi{x, ldx, bias, e0, mb, chunk, S, N};
   return run_gemm<T>(A, lda, W, ldw, M, N, K, epi, s);
+}
+
+hipError_t gemm_e4m3_store(const uint8_t* A, int64_t lda, const float* a_scales, const uint8_t* W, int64_t ldw,
+                           const float* w_scale, int M, int N, int K, const float* bias, int act, bf16* out, int64_t ldo,
+                           hipStream_t s) {
+  if (act == ACT_GELU)
+    return run_gemm_e4m3(A, lda, a_scales, W, ldw, w_scale, M, N, K, EpiStore<bf16, ACT_GELU>{out, ldo, bias}, s);
+  return run_gemm_e4m3(A, lda, a_scales, W, ldw, w_scale, M, N, K, EpiStore<bf16, ACT_NONE>{out, ldo, bias}, s);
+}
+
+hipError_t gemm_qkv_e4m3(const uint8_t* A, int64_t lda, const float* a_scales, const uint8_t* W, int64_t ldw,
+                         const float* w_scale, int M, int dim, int K, const float* bias, bf16* qk, int64_t ldo, bf16* vt,
+                         int S, int H, int hd, int Spad, hipStream_t s) {
+  if (hd % 4 != 0) return hipErrorInvalidValue;
+  return run_gemm_e4m3(A, lda, a_scales, W, ldw, w_scale, M, 3 * dim, K,
+                       EpiQKV<bf16>{qk, ldo, bias, vt, 2 * dim, S, H, hd, Spad}, s);
+}
+
+hipError_t gemm_e4m3_residual(const uint8_t* A, int64_t lda, const float* a_scales, const uint8_t* W, int64_t ldw,
+                              const float* w_scale, int M, int N, int K, const float* bias, const float* e0, const float* mb,
+                              int chunk, int S, float* x, int64_t ldx, hipStream_t s) {
+  return run_gemm_e4m3(A, lda, a_scales, W, ldw, w_scale, M, N, K, EpiResidual{x, ldx, bias, e0, mb, chunk, S, N}, s);
 }
 
 template <typename T>

@@ -9,6 +9,8 @@
 //    of 128, zero past the keys) with the keys of each 64-key tile in the order the FP8 P.V product
 //    reads them (wan.h documents it).
 // A group whose amax is 0 gets scale 0 and zero codes.
+#include <algorithm>
+
 #include "wan_internal.h"
 
 namespace wan {
@@ -173,7 +175,93 @@ __global__ __launch_bounds__(256) void quant_vt_kernel(const bf16* __restrict__ 
   if (threadIdx.x == 0) scales[row] = m > 0.f ? m / 448.f : 0.f;
 }
 
+// Per-row E4M3 codes (scale = amax / 448): one workgroup per row of `cols` bf16 values (cols % 8 == 0).
+__global__ __launch_bounds__(256) void quant_rows_kernel(const bf16* __restrict__ x, int64_t ld, int cols,
+                                                         uint8_t* __restrict__ codes, int64_t ldc,
+                                                         float* __restrict__ scales) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const bf16* src = x + row * ld;
+  float m = 0.f;
+  for (int c = threadIdx.x; c < cols / 8; c += 256) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(src + c * 8);
+    const bf16* e = reinterpret_cast<const bf16*>(&raw);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf((float)e[j]));
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float inv = m > 0.f ? 448.f / m : 0.f;
+  uint8_t* dst = codes + row * ldc;
+  for (int c = threadIdx.x; c < cols / 8; c += 256) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(src + c * 8);
+    const bf16* e = reinterpret_cast<const bf16*>(&raw);
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = fminf(fmaxf((float)e[j] * inv, -448.f), 448.f);
+    *reinterpret_cast<uint2*>(dst + c * 8) = make_uint2(e4m3x4(y[0], y[1], y[2], y[3]), e4m3x4(y[4], y[5], y[6], y[7]));
+  }
+  if (threadIdx.x == 0) scales[row] = m > 0.f ? m / 448.f : 0.f;
+}
+
+// Per-tensor E4M3 codes: amax over the whole tensor (non-negative floats order like their bits, so an
+// unsigned atomic max collects it), then the codes.
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* p, uint32_t v) { *p = v; }
+
+__global__ __launch_bounds__(256) void amax_kernel(const bf16* __restrict__ x, int64_t n8, uint32_t* amax_bits) {
+  __shared__ float red[4];
+  float m = 0.f;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < n8; c += (int64_t)gridDim.x * 256) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(x + c * 8);
+    const bf16* e = reinterpret_cast<const bf16*>(&raw);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf((float)e[j]));
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicMax(amax_bits, __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
+}
+
+__global__ __launch_bounds__(256) void quant_tensor_kernel(const bf16* __restrict__ x, int64_t n8,
+                                                           const uint32_t* __restrict__ amax_bits,
+                                                           uint8_t* __restrict__ codes, float* __restrict__ scale) {
+  const float m = __uint_as_float(*amax_bits);
+  const float inv = m > 0.f ? 448.f / m : 0.f;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < n8; c += (int64_t)gridDim.x * 256) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(x + c * 8);
+    const bf16* e = reinterpret_cast<const bf16*>(&raw);
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = fminf(fmaxf((float)e[j] * inv, -448.f), 448.f);
+    *reinterpret_cast<uint2*>(codes + c * 8) = make_uint2(e4m3x4(y[0], y[1], y[2], y[3]), e4m3x4(y[4], y[5], y[6], y[7]));
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) *scale = m > 0.f ? m / 448.f : 0.f;
+}
+
 }  // namespace
+
+hipError_t launch_quant_rows_e4m3(const bf16* x, int64_t ld, int rows, int cols, uint8_t* codes, int64_t ldc,
+                                  float* scales, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (cols <= 0 || cols % 8 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)rows), dim3(256), 0, s, x, ld, cols, codes, ldc, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_tensor_e4m3(const bf16* x, int64_t n, uint8_t* codes, float* scale, uint32_t* amax_word,
+                                    hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (n % 8 != 0) return hipErrorInvalidValue;
+  const int64_t n8 = n / 8;
+  const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(n8, 256), 2048);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(1), 0, s, amax_word, 0u);
+  hipLaunchKernelGGL(amax_kernel, dim3(blocks), dim3(256), 0, s, x, n8, amax_word);
+  hipLaunchKernelGGL(quant_tensor_kernel, dim3(blocks), dim3(256), 0, s, x, n8, amax_word, codes, scale);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_q(const bf16* x, int64_t ld, int B, int S, int H, int hd, int8_t* codes, float* scales,
                           hipStream_t s) {

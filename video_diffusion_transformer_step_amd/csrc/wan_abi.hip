@@ -6,6 +6,8 @@
 #include <string.h>
 
 #include "wan.h"
+#include <algorithm>
+
 #include "wan_internal.h"
 
 using namespace wan;
@@ -73,6 +75,10 @@ int need_ptr(const void* p, const char* name) {
   return WAN_OK;
 }
 int opt_ptr(const void* p, const char* name) { return p ? need_ptr(p, name) : WAN_OK; }
+int need_f32(const void* p, const char* name) {
+  if (!p || (reinterpret_cast<uintptr_t>(p) & 3)) return fail(WAN_EINVAL, "%s is NULL or not 4-byte aligned", name);
+  return WAN_OK;
+}
 
 int check_shape(const wan_latent_shape& s) {
   if (s.B <= 0 || s.C <= 0 || s.T <= 0 || s.H <= 0 || s.W <= 0)
@@ -95,9 +101,12 @@ int check_dtype(int32_t dtype) {
 int check_cfg(const wan_block_cfg* c) {
   if (!c) return fail(WAN_EINVAL, "cfg is NULL");
   WAN_TRY(check_dtype(c->dtype));
-  if (c->flags & ~WAN_FLAG_FP8_ATTN) return fail(WAN_EUNSUPPORTED, "unknown cfg->flags bits 0x%x", c->flags);
+  if (c->flags & ~(WAN_FLAG_FP8_ATTN | WAN_FLAG_FP8_GEMM))
+    return fail(WAN_EUNSUPPORTED, "unknown cfg->flags bits 0x%x", c->flags);
   if ((c->flags & WAN_FLAG_FP8_ATTN) && (c->dtype != WAN_BF16 || c->head_dim != 128))
     return fail(WAN_EUNSUPPORTED, "WAN_FLAG_FP8_ATTN needs dtype WAN_BF16 and head_dim 128");
+  if ((c->flags & WAN_FLAG_FP8_GEMM) && (c->dtype != WAN_BF16 || c->dim % 256 != 0 || c->ffn_dim % 256 != 0))
+    return fail(WAN_EUNSUPPORTED, "WAN_FLAG_FP8_GEMM needs dtype WAN_BF16 and dim, ffn_dim multiples of 256");
   if (c->heads <= 0 || c->head_dim <= 0 || c->dim != c->heads * c->head_dim)
     return fail(WAN_EINVAL, "dim (%d) must equal heads (%d) * head_dim (%d)", c->dim, c->heads, c->head_dim);
   if (c->head_dim != 64 && c->head_dim != 128)
@@ -134,6 +143,9 @@ struct BlockWs {
   // quantised self-attention (WAN_FLAG_FP8_ATTN only): codes and scales of q, k, v
   uint8_t *q8, *k8, *v8t;
   float *sq, *sk, *sv;
+  // E4M3 products (WAN_FLAG_FP8_GEMM only): per-token codes of the current product's input
+  uint8_t* a8;
+  float* sa;
 };
 template <typename T>
 size_t block_plan(const wan_block_cfg& c, const wan_grid& g, int B, char* base, BlockWs<T>* out) {
@@ -156,6 +168,12 @@ size_t block_plan(const wan_block_cfg& c, const wan_grid& g, int B, char* base, 
     w.sk = cv.take<float>((size_t)B * c.heads * (pad64(S) / 64));
     w.sv = cv.take<float>((size_t)B * dim);
   }
+  w.a8 = nullptr;
+  w.sa = nullptr;
+  if (c.flags & WAN_FLAG_FP8_GEMM) {
+    w.a8 = cv.take<uint8_t>(BS * std::max<int64_t>(dim, c.ffn_dim));
+    w.sa = cv.take<float>(BS);
+  }
   if (out) *out = w;
   return cv.off;
 }
@@ -174,8 +192,16 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
   PROF_TRY(WAN_K_LN1, launch_ln_mod<T>(x, BS, dim, S, 0, w.mod, nullptr, 0, 1, c.ln_eps, w.u, st));
   // q, k -> qkv[:, 0 .. 2 dim) (row stride 2 dim); v -> V^T directly
   PROF_TRY(WAN_K_VT_TAIL, launch_vt_tail_zero<T>(w.vt, (int64_t)B * dim, S, Spad, st));
-  PROF_TRY(WAN_K_QKV_GEMM, gemm_qkv<T>(w.u, dim, (const T*)W.wqkv, dim, BS, dim, dim, W.bqkv, w.qkv, 2 * dim, w.vt, S, H,
-                                       hd, Spad, st));
+  const bool f8g = (c.flags & WAN_FLAG_FP8_GEMM) != 0;
+  const wan_block_weights_e4m3* Q8 = W.e4m3;
+  if (f8g) {  // E4M3 products ("Wan 技术深度解析" §5.3): per-token codes of u, then the product
+    PROF_TRY(WAN_K_QUANT, launch_quant_rows_e4m3((const bf16*)w.u, dim, BS, dim, w.a8, dim, w.sa, st));
+    PROF_TRY(WAN_K_QKV_GEMM, gemm_qkv_e4m3(w.a8, dim, w.sa, (const uint8_t*)Q8->wqkv, dim, Q8->s_wqkv, BS, dim, dim,
+                                           W.bqkv, (bf16*)w.qkv, 2 * dim, (bf16*)w.vt, S, H, hd, Spad, st));
+  } else {
+    PROF_TRY(WAN_K_QKV_GEMM, gemm_qkv<T>(w.u, dim, (const T*)W.wqkv, dim, BS, dim, dim, W.bqkv, w.qkv, 2 * dim, w.vt,
+                                         S, H, hd, Spad, st));
+  }
   PROF_TRY(WAN_K_QK_NORM_ROPE, launch_qk_norm_rope<T>(w.qkv, w.qkv + dim, 2 * dim, w.qkv, w.qkv + dim, 2 * dim, B, g.T, g.Hp, g.Wp, H, hd,
                                  W.gq, W.gk, 1, c.rms_eps, c.rope_theta, st));
   if constexpr (sizeof(T) == 2) {
@@ -191,7 +217,14 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
     PROF_TRY(WAN_K_SELF_ATTN, launch_attention<T>(w.qkv, (int64_t)S * 2 * dim, 2 * dim, self, self, 1, B, S, H, hd,
                                                   scale, w.o, (int64_t)S * dim, dim, 0, st));
   }
-  PROF_TRY(WAN_K_O_GEMM, gemm_residual<T>(w.o, dim, (const T*)W.wo, dim, BS, dim, dim, W.bo, w.mod, nullptr, 2, S, x, dim, st));
+  if (f8g) {
+    PROF_TRY(WAN_K_QUANT, launch_quant_rows_e4m3((const bf16*)w.o, dim, BS, dim, w.a8, dim, w.sa, st));
+    PROF_TRY(WAN_K_O_GEMM, gemm_e4m3_residual(w.a8, dim, w.sa, (const uint8_t*)Q8->wo, dim, Q8->s_wo, BS, dim, dim, W.bo,
+                                              w.mod, nullptr, 2, S, x, dim, st));
+  } else {
+    PROF_TRY(WAN_K_O_GEMM, gemm_residual<T>(w.o, dim, (const T*)W.wo, dim, BS, dim, dim, W.bo, w.mod, nullptr, 2, S, x,
+                                            dim, st));
+  }
   // cross-attention branch (no adaLN, no RoPE)
   PROF_TRY(WAN_K_LN3, launch_ln_mod<T>(x, BS, dim, S, 1, W.ln3_w, W.ln3_b, 0, 0, c.ln_eps, w.u, st));
   T* qc = w.qkv;  // reuse: [BS, dim]
@@ -204,9 +237,20 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
   PROF_TRY(WAN_K_CROSS_O_GEMM, gemm_residual<T>(w.o, dim, (const T*)W.wco, dim, BS, dim, dim, W.bco, nullptr, nullptr, 0, S, x, dim, st));
   // FFN branch
   PROF_TRY(WAN_K_LN2, launch_ln_mod<T>(x, BS, dim, S, 0, w.mod, nullptr, 3, 4, c.ln_eps, w.u, st));
-  PROF_TRY(WAN_K_FFN1_GEMM, (gemm_store<T, T>(w.u, dim, (const T*)W.w1, dim, BS, c.ffn_dim, dim, W.b1, ACT_GELU, w.h, c.ffn_dim, st)));
-  PROF_TRY(WAN_K_FFN2_GEMM, gemm_residual<T>(w.h, c.ffn_dim, (const T*)W.w2, c.ffn_dim, BS, dim, c.ffn_dim, W.b2, w.mod, nullptr, 5, S,
-                           x, dim, st));
+  if (f8g) {
+    const int F = c.ffn_dim;
+    PROF_TRY(WAN_K_QUANT, launch_quant_rows_e4m3((const bf16*)w.u, dim, BS, dim, w.a8, dim, w.sa, st));
+    PROF_TRY(WAN_K_FFN1_GEMM, gemm_e4m3_store(w.a8, dim, w.sa, (const uint8_t*)Q8->w1, dim, Q8->s_w1, BS, F, dim, W.b1,
+                                              ACT_GELU, (bf16*)w.h, F, st));
+    PROF_TRY(WAN_K_QUANT, launch_quant_rows_e4m3((const bf16*)w.h, F, BS, F, w.a8, F, w.sa, st));
+    PROF_TRY(WAN_K_FFN2_GEMM, gemm_e4m3_residual(w.a8, F, w.sa, (const uint8_t*)Q8->w2, F, Q8->s_w2, BS, dim, F, W.b2,
+                                                 w.mod, nullptr, 5, S, x, dim, st));
+  } else {
+    PROF_TRY(WAN_K_FFN1_GEMM, (gemm_store<T, T>(w.u, dim, (const T*)W.w1, dim, BS, c.ffn_dim, dim, W.b1, ACT_GELU, w.h,
+                                                c.ffn_dim, st)));
+    PROF_TRY(WAN_K_FFN2_GEMM, gemm_residual<T>(w.h, c.ffn_dim, (const T*)W.w2, c.ffn_dim, BS, dim, c.ffn_dim, W.b2, w.mod,
+                                               nullptr, 5, S, x, dim, st));
+  }
   return WAN_OK;
 }
 
@@ -229,7 +273,18 @@ int check_block_weights(const wan_block_cfg& c, const wan_block_weights* w) {
   WAN_TRY(opt_ptr(w->b1, "b1"));
   WAN_TRY(need_ptr(w->w2, "w2"));
   WAN_TRY(opt_ptr(w->b2, "b2"));
-  (void)c;
+  if (c.flags & WAN_FLAG_FP8_GEMM) {
+    const wan_block_weights_e4m3* q = w->e4m3;
+    if (!q) return fail(WAN_EINVAL, "WAN_FLAG_FP8_GEMM needs weights->e4m3");
+    WAN_TRY(need_ptr(q->wqkv, "e4m3->wqkv"));
+    WAN_TRY(need_ptr(q->wo, "e4m3->wo"));
+    WAN_TRY(need_ptr(q->w1, "e4m3->w1"));
+    WAN_TRY(need_ptr(q->w2, "e4m3->w2"));
+    WAN_TRY(need_f32(q->s_wqkv, "e4m3->s_wqkv"));
+    WAN_TRY(need_f32(q->s_wo, "e4m3->s_wo"));
+    WAN_TRY(need_f32(q->s_w1, "e4m3->s_w1"));
+    WAN_TRY(need_f32(q->s_w2, "e4m3->s_w2"));
+  }
   return WAN_OK;
 }
 
@@ -644,11 +699,6 @@ static int check_q8_shape(int32_t B, int32_t Sq, int32_t Sk, int32_t heads, int3
   return WAN_OK;
 }
 
-static int need_f32(const void* p, const char* name) {
-  if (!p || (reinterpret_cast<uintptr_t>(p) & 3)) return fail(WAN_EINVAL, "%s is NULL or not 4-byte aligned", name);
-  return WAN_OK;
-}
-
 int wan_attention_q8_quantize(const void* q, const void* k, const void* v, int32_t B, int32_t Sq, int32_t Sk,
                               int32_t heads, int32_t head_dim, void* q8, float* sq, void* k8, float* sk, void* v8t,
                               float* sv, void* ws, size_t ws_bytes, wan_stream_t stream) {
@@ -689,6 +739,48 @@ int wan_attention_q8_fwd(const void* q8, const float* sq, const void* k8, const 
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3)) return fail(WAN_EINVAL, "lse is not 4-byte aligned");
   HIP_TRY(launch_attention_q8((const uint8_t*)q8, sq, (const uint8_t*)k8, sk, (const uint8_t*)v8t, sv, B, Sq, Sk,
                               heads, head_dim, (bf16*)o, lse, hs(stream)));
+  return WAN_OK;
+}
+
+int wan_quantize_rows_e4m3(const void* x, int64_t ld, int32_t rows, int32_t cols, void* codes, int64_t ldc,
+                           float* scales, wan_stream_t stream) {
+  if (rows <= 0 || cols <= 0 || cols % 8 != 0) return fail(WAN_EINVAL, "rows > 0 and cols a positive multiple of 8");
+  if (ld < cols || ld % 8 != 0 || ldc < cols || ldc % 16 != 0) return fail(WAN_EINVAL, "bad row strides");
+  WAN_TRY(need_ptr(x, "x"));
+  WAN_TRY(need_ptr(codes, "codes"));
+  WAN_TRY(need_f32(scales, "scales"));
+  HIP_TRY(launch_quant_rows_e4m3((const bf16*)x, ld, rows, cols, (uint8_t*)codes, ldc, scales, hs(stream)));
+  return WAN_OK;
+}
+
+int wan_quantize_tensor_e4m3(const void* x, int64_t n, void* codes, float* scale, void* ws, size_t ws_bytes,
+                             wan_stream_t stream) {
+  if (n <= 0 || n % 8 != 0) return fail(WAN_EINVAL, "n must be a positive multiple of 8");
+  WAN_TRY(need_ptr(x, "x"));
+  WAN_TRY(need_ptr(codes, "codes"));
+  WAN_TRY(need_f32(scale, "scale"));
+  if (ws_bytes < 256) return fail(WAN_EWORKSPACE, "workspace %zu < 256 bytes", ws_bytes);
+  WAN_TRY(need_ptr(ws, "ws"));
+  HIP_TRY(launch_quant_tensor_e4m3((const bf16*)x, n, (uint8_t*)codes, scale, (uint32_t*)ws, hs(stream)));
+  return WAN_OK;
+}
+
+int wan_gemm_e4m3(const void* a, int64_t lda, const float* a_scales, const void* w, int64_t ldw, const float* w_scale,
+                  int32_t M, int32_t N, int32_t K, const float* bias, int32_t act, void* y, int64_t ldy,
+                  wan_stream_t stream) {
+  if (M <= 0 || N <= 0 || N % 4 != 0) return fail(WAN_EINVAL, "M > 0 and N a positive multiple of 4");
+  if (K <= 0 || K % 256 != 0) return fail(WAN_EUNSUPPORTED, "K %d must be a positive multiple of 256", K);
+  if (lda < K || ldw < K || lda % 16 != 0 || ldw % 16 != 0 || ldy < N || ldy % 4 != 0)
+    return fail(WAN_EINVAL, "bad row strides");
+  if (act != ACT_NONE && act != ACT_GELU) return fail(WAN_EINVAL, "act must be 0 or 1");
+  WAN_TRY(need_ptr(a, "a"));
+  WAN_TRY(need_ptr(w, "w"));
+  WAN_TRY(need_f32(a_scales, "a_scales"));
+  WAN_TRY(need_f32(w_scale, "w_scale"));
+  WAN_TRY(opt_ptr(bias, "bias"));
+  WAN_TRY(need_ptr(y, "y"));
+  HIP_TRY(gemm_e4m3_store((const uint8_t*)a, lda, a_scales, (const uint8_t*)w, ldw, w_scale, M, N, K, bias, act,
+                          (bf16*)y, ldy, hs(stream)));
   return WAN_OK;
 }
 

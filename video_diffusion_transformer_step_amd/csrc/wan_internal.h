@@ -69,6 +69,18 @@ hipError_t gemm_qkv(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int
 template <typename T>
 hipError_t gemm_residual(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const float* bias,
                          const float* e0, const float* mb, int chunk, int S, float* x, int64_t ldx, hipStream_t s);
+// E4M3 products: C = (sum_k A[m, k] W[n, k]) * a_scales[m] * w_scale[0] over E4M3 codes (A row stride
+// lda bytes, W row stride ldw bytes, K % 256 == 0, strides % 16 == 0), then the store (bf16 out, act
+// NONE or GELU) or residual epilogue.
+hipError_t gemm_e4m3_store(const uint8_t* A, int64_t lda, const float* a_scales, const uint8_t* W, int64_t ldw,
+                           const float* w_scale, int M, int N, int K, const float* bias, int act, bf16* out,
+                           int64_t ldo, hipStream_t s);
+hipError_t gemm_e4m3_residual(const uint8_t* A, int64_t lda, const float* a_scales, const uint8_t* W, int64_t ldw,
+                              const float* w_scale, int M, int N, int K, const float* bias, const float* e0,
+                              const float* mb, int chunk, int S, float* x, int64_t ldx, hipStream_t s);
+hipError_t gemm_qkv_e4m3(const uint8_t* A, int64_t lda, const float* a_scales, const uint8_t* W, int64_t ldw,
+                         const float* w_scale, int M, int dim, int K, const float* bias, bf16* qk, int64_t ldo, bf16* vt,
+                         int S, int H, int hd, int Spad, hipStream_t s);
 // y[b, n] = out_act(sum_k W[n, k] * in_act(x[b, k]) + bias[n]) for b < B (fp32 x, y).
 template <typename T>
 hipError_t gemv(const T* W, int N, int K, const float* x, int B, const float* bias, int in_act, int out_act,
@@ -112,6 +124,13 @@ hipError_t launch_quant_k(const bf16* x, int64_t ld, int B, int S, int H, int hd
 // scales [rows].
 hipError_t launch_quant_vt(const bf16* vt, int64_t rows, int Lpad_in, int Lpad_out, uint8_t* out, float* scales,
                            hipStream_t s);
+
+// E4M3 codes of activations per row (scale = amax / 448 per row) and of a whole tensor (one scale,
+// written to *scale on the device; amax_word is a 4-byte device scratch word).
+hipError_t launch_quant_rows_e4m3(const bf16* x, int64_t ld, int rows, int cols, uint8_t* codes, int64_t ldc,
+                                  float* scales, hipStream_t s);
+hipError_t launch_quant_tensor_e4m3(const bf16* x, int64_t n, uint8_t* codes, float* scale, uint32_t* amax_word,
+                                    hipStream_t s);
 
 // Combine n (1..MERGE_MAX_PARTS) attention results of the same queries over disjoint key chunks:
 // o_parts[i] [B, S, H, hd] T, lse_parts[i] [B, H, S] float32 (host arrays of device pointers);

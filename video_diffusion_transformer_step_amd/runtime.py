@@ -9,6 +9,7 @@ arithmetic happens here.
 """
 from __future__ import annotations
 
+import ctypes
 from dataclasses import dataclass
 
 import numpy as np
@@ -38,14 +39,15 @@ class _Keep:
         return None if tensor is None else tensor.data_ptr()
 
 
-def cfg_of(c, dtype=None, fp8_attn=False):
+def cfg_of(c, dtype=None, fp8_attn=False, fp8_gemm=False):
     """BlockCfg from a workload description (attributes dim, heads, head_dim, ffn_dim,
     text_len, img_len, dtype, ln_eps, rms_eps, rope_theta); fp8_attn selects the quantised
-    self-attention (WAN_FLAG_FP8_ATTN)."""
+    self-attention (WAN_FLAG_FP8_ATTN), fp8_gemm the E4M3 products (WAN_FLAG_FP8_GEMM; the blocks
+    need DeviceBlock.enable_e4m3())."""
     d = dtype if dtype is not None else c.dtype
+    flags = (L.WAN_FLAG_FP8_ATTN if fp8_attn else 0) | (L.WAN_FLAG_FP8_GEMM if fp8_gemm else 0)
     return L.block_cfg(c.dim, c.heads, c.head_dim, c.ffn_dim, max(c.text_len, 1), c.img_len,
-                       L.WAN_BF16 if d == "bf16" else L.WAN_F32, c.ln_eps, c.rms_eps, c.rope_theta,
-                       L.WAN_FLAG_FP8_ATTN if fp8_attn else 0)
+                       L.WAN_BF16 if d == "bf16" else L.WAN_F32, c.ln_eps, c.rms_eps, c.rope_theta, flags)
 
 
 class DeviceBlock:
@@ -75,6 +77,23 @@ class DeviceBlock:
         self.kvw = L.CrossKVWeights(k.put("wkv_txt", g["wkv_txt"]), k.put("bkv_txt", g["bkv_txt"]),
                                     k.put("wkv_img", g.get("wkv_img")), k.put("bkv_img", g.get("bkv_img")))
         self._keep = k
+
+    def enable_e4m3(self):
+        """E4M3 codes of wqkv, wo, w1, w2 with one scale each (wan_quantize_tensor_e4m3), linked into bw
+        for WAN_FLAG_FP8_GEMM.  bf16 blocks only."""
+        k = self._keep
+        ws = torch.empty(256, dtype=torch.uint8, device=k.t["wqkv"].device)
+        ptrs, scales = [], []
+        for n in ("wqkv", "wo", "w1", "w2"):
+            src = k.t[n]
+            codes = torch.empty(src.shape, dtype=torch.uint8, device=src.device)
+            scale = torch.empty(1, dtype=torch.float32, device=src.device)
+            L.quantize_tensor_e4m3(src, codes, scale, ws)
+            ptrs.append(k.put(n + "_e4m3", codes))
+            scales.append(k.put(n + "_scale", scale))
+        self._e4m3 = L.BlockWeightsE4M3(*ptrs, *scales)
+        self.bw.e4m3 = ctypes.pointer(self._e4m3)
+        return self
 
 
 class CrossKVCache:
@@ -144,8 +163,8 @@ def cross_kv_all(c, blocks, txt_emb, img_emb, B, device="cuda"):
     return caches
 
 
-def alloc_step(c, B, device="cuda", fp8_attn=False) -> StepBuffers:
-    cfg = cfg_of(c, fp8_attn=fp8_attn)
+def alloc_step(c, B, device="cuda", fp8_attn=False, fp8_gemm=False) -> StepBuffers:
+    cfg = cfg_of(c, fp8_attn=fp8_attn, fp8_gemm=fp8_gemm)
     S = c.S
     ws_bytes = max(L.block_ws_bytes(cfg, c.grid, B), L.patch_embed_ws_bytes(cfg, B * S, c.in_channels),
                    L.head_ws_bytes(cfg, B * S), 16)
@@ -163,11 +182,11 @@ def alloc_step(c, B, device="cuda", fp8_attn=False) -> StepBuffers:
 
 
 def dit_forward(c, model: DeviceModel, blocks, caches, x_latent, z_img, t, buf: StepBuffers, B,
-                known_pixel_frames=None, fp8_attn=False):
+                known_pixel_frames=None, fp8_attn=False, fp8_gemm=False):
     """One DiT evaluation over B rows sharing the latent x_latent [1, C, T, H, W] (CFG rows see the same
-    x_in).  Result in buf.v [B, C_out, T, H, W].  fp8_attn: quantised self-attention in every block
-    (buf must come from alloc_step(..., fp8_attn=True))."""
-    cfg = cfg_of(c, fp8_attn=fp8_attn)
+    x_in).  Result in buf.v [B, C_out, T, H, W].  fp8_attn / fp8_gemm: quantised self-attention / E4M3
+    products in every block (buf from alloc_step with the same flags)."""
+    cfg = cfg_of(c, fp8_attn=fp8_attn, fp8_gemm=fp8_gemm)
     one = x_latent.shape[0]
     for b in range(B):
         src = x_latent[b % one:b % one + 1]
@@ -186,8 +205,8 @@ def dit_forward(c, model: DeviceModel, blocks, caches, x_latent, z_img, t, buf: 
 
 
 def denoise_step(c, model, blocks, caches, x_latent, z_img, t, dt, guidance, buf: StepBuffers, B,
-                 known_pixel_frames=None, fp8_attn=False):
+                 known_pixel_frames=None, fp8_attn=False, fp8_gemm=False):
     """x_latent <- x_latent + dt * v, v = CFG(v_cond, v_uncond) when B == 2 (row 0 conditional)."""
-    v = dit_forward(c, model, blocks, caches, x_latent, z_img, t, buf, B, known_pixel_frames, fp8_attn)
+    v = dit_forward(c, model, blocks, caches, x_latent, z_img, t, buf, B, known_pixel_frames, fp8_attn, fp8_gemm)
     L.fm_euler_step(x_latent, v[0:1], v[1:2] if B > 1 else None, guidance, dt)
     return x_latent
