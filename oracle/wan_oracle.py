@@ -23,7 +23,7 @@ __all__ = [
     "conv3d_patch_embed_direct", "sinusoidal_embedding", "silu", "gelu", "time_embed",
     "layer_norm", "modulate", "rms_norm", "rope_segments", "rope_3d", "token_positions",
     "attention", "attention_lse", "lse_merge", "multihead_attention", "context_embed", "cross_kv", "block_fwd",
-    "head_fwd", "cfg_combine", "euler_step", "cfg_euler", "dit_fwd", "sample",
+    "head_fwd", "cfg_combine", "euler_step", "cfg_euler", "dit_fwd", "sample", "sample_cached",
     "self_attention_rope_only",
 ]
 
@@ -382,7 +382,7 @@ def cross_kv(ctx_emb, wk, bk, wv, bv):
 # a5..a10: one DiT block
 # ---------------------------------------------------------------------------
 def block_fwd(x, e0, w: dict, kv, grid, heads: int, rows=None,
-              ln_eps: float = 1e-6, rms_eps: float = 1e-6, theta: float = 10000.0):
+              ln_eps: float = 1e-6, rms_eps: float = 1e-6, theta: float = 10000.0, attn_cache=None):
     """One DiT block on [B, S, dim] tokens.
 
     Follows [I2V-illustrated §5.2-§5.5] in the order self-attention ->
@@ -406,6 +406,12 @@ def block_fwd(x, e0, w: dict, kv, grid, heads: int, rows=None,
     are computed for all S tokens and everything else only for those query
     rows; the result is then [B, len(rows), dim] and equals those rows of the
     full output exactly (every step but self-attention is token-local).
+
+    attn_cache (the attention cache of [Wan-deep-dive §5.3], which reuses attention outputs across
+    sampling steps): None, or {"mode": "store" | "reuse", "y": array [B, len(rows), dim]}.  Reading:
+    the cached quantity is the self-attention layer's output y = o W_o^T + b_o before the gate; "store"
+    computes and records it, "reuse" skips the self-attention layer and uses the recorded y, with
+    the current step's gate1.
     """
     x, e0 = _a(x), _a(e0)
     B, S, dim = x.shape
@@ -418,14 +424,20 @@ def block_fwd(x, e0, w: dict, kv, grid, heads: int, rows=None,
         mod = e0[b] + _a(w["mod_bias"])
         shift1, scale1, gate1, shift2, scale2, gate2 = mod
         # self-attention
-        u = modulate(layer_norm(x[b], ln_eps), shift1, scale1)
-        k = rms_norm(linear(u, w["wk"], w["bk"]), w["gk"], rms_eps)
-        v = linear(u, w["wv"], w["bv"])
-        q = rms_norm(linear(u[rows], w["wq"], w["bq"]), w["gq"], rms_eps)
-        q = rope_3d(q.reshape(len(rows), heads, hd), pos[rows], theta).reshape(len(rows), dim)
-        k = rope_3d(k.reshape(S, heads, hd), pos, theta).reshape(S, dim)
-        o = multihead_attention(q, k, v, heads)
-        xr = x[b, rows] + gate1 * linear(o, w["wo"], w["bo"])
+        if attn_cache is not None and attn_cache["mode"] == "reuse":
+            ya = _a(attn_cache["y"][b])
+        else:
+            u = modulate(layer_norm(x[b], ln_eps), shift1, scale1)
+            k = rms_norm(linear(u, w["wk"], w["bk"]), w["gk"], rms_eps)
+            v = linear(u, w["wv"], w["bv"])
+            q = rms_norm(linear(u[rows], w["wq"], w["bq"]), w["gq"], rms_eps)
+            q = rope_3d(q.reshape(len(rows), heads, hd), pos[rows], theta).reshape(len(rows), dim)
+            k = rope_3d(k.reshape(S, heads, hd), pos, theta).reshape(S, dim)
+            o = multihead_attention(q, k, v, heads)
+            ya = linear(o, w["wo"], w["bo"])
+            if attn_cache is not None:
+                attn_cache["y"][b] = ya
+        xr = x[b, rows] + gate1 * ya
         # cross-attention
         c = layer_norm(xr, ln_eps, w["ln3_w"], w["ln3_b"])
         qc = linear(c, w["wcq"], w["bcq"])
@@ -487,7 +499,7 @@ def cfg_euler(x, v_cond, v_uncond, s: float, dt: float):
 # ---------------------------------------------------------------------------
 def dit_fwd(x_in, t, model_w: dict, blocks_w, ctx_txt, ctx_img, heads: int,
             ln_eps: float = 1e-6, rms_eps: float = 1e-6, theta: float = 10000.0,
-            freq_dim: int = 256, out_channels: int = 16):
+            freq_dim: int = 256, out_channels: int = 16, attn_caches=None):
     """One DiT call v = DiT(x_in, t, context) ([I2V-illustrated §7], sampling loop).
 
     x_in [B, C_in, T, H, W]; t scalar or [B]; ctx_txt [B, L, text_dim];
@@ -522,7 +534,8 @@ def dit_fwd(x_in, t, model_w: dict, blocks_w, ctx_txt, ctx_img, heads: int,
             if img is not None:
                 ki, vi = cross_kv(img, w["wki"], w["bki"], w["wvi"], w["bvi"])
             kv.append((kt, vt, ki, vi))
-        x = block_fwd(x, e0, w, kv, grid, heads, ln_eps=ln_eps, rms_eps=rms_eps, theta=theta)
+        x = block_fwd(x, e0, w, kv, grid, heads, ln_eps=ln_eps, rms_eps=rms_eps, theta=theta,
+                      attn_cache=None if attn_caches is None else attn_caches[i])
         i += 1
     out = head_fwd(x, e, model_w, ln_eps)
     return unpatchify(out, out_channels, T, H, W)
@@ -547,6 +560,45 @@ def sample(x_T, z_img, steps: int, guidance: float, model_w, blocks_w, ctx_txt, 
         x_in = np.repeat(x_in, B, axis=0)
         v = dit_fwd(x_in, t, model_w, blocks_w, ctx_txt, ctx_img, heads, **kw)
         x = cfg_euler(x, v[0:1], v[1:2] if B > 1 else None, guidance, dt)
+        traj.append(x.copy())
+    return x, traj
+
+
+def sample_cached(x_T, z_img, steps: int, guidance: float, model_w, blocks_w, ctx_txt, ctx_img,
+                  heads: int, attn_reuse, cfg_reuse, t0: float = 1.0, known_pixel_frames=None, **kw):
+    """``sample`` with the diffusion cache of [Wan-deep-dive §5.3] (attention cache + CFG cache).
+
+    Reading (the page gives neither the cached quantities nor the schedule):
+    * attention cache: on a step with attn_reuse[k], every block reuses the self-attention layer
+      output y = o W_o^T + b_o it recorded at the last step that computed it (per CFG row), with the
+      current gate (see ``block_fwd``); other steps compute and record it.  attn_reuse[0] must be
+      False.
+    * CFG cache: on a step with cfg_reuse[k], the unconditional row is not evaluated and v_u is the
+      one of the last step that evaluated it; cfg_reuse[0] must be False.  Only the conditional row
+      then runs (its attention cache is updated as usual; the unconditional row's is left as is).
+    With both lists all False this is exactly ``sample``.
+    """
+    x = _a(x_T)
+    Bfull = _a(ctx_txt).shape[0]
+    assert not attn_reuse[0] and not cfg_reuse[0]
+    dt = -t0 / steps
+    nblocks = len(blocks_w)
+    S = x.shape[2] * (x.shape[3] // 2) * (x.shape[4] // 2)
+    dim = _a(model_w["b_pe"]).shape[0]
+    ycache = [np.zeros((Bfull, S, dim)) for _ in range(nblocks)]
+    v_u = None
+    traj = []
+    for k in range(steps):
+        t = t0 + k * dt
+        B = 1 if (cfg_reuse[k] and Bfull > 1) else Bfull
+        x_in = x if z_img is None else build_i2v_input(x, z_img, known_pixel_frames)
+        x_in = np.repeat(x_in, B, axis=0)
+        mode = "reuse" if attn_reuse[k] else "store"
+        caches = [{"mode": mode, "y": ycache[i][:B]} for i in range(nblocks)]
+        v = dit_fwd(x_in, t, model_w, blocks_w, _a(ctx_txt)[:B], ctx_img, heads, attn_caches=caches, **kw)
+        if Bfull > 1 and B > 1:
+            v_u = v[1:2].copy()
+        x = cfg_euler(x, v[0:1], v_u if Bfull > 1 else None, guidance, dt)
         traj.append(x.copy())
     return x, traj
 
@@ -579,4 +631,7 @@ PARITY = {
     "cfg_combine": "pinned: s = 1 -> v_c, s = 0 -> v_u",
     "euler_step": "pinned: straight-line path lands exactly on the endpoint",
     "sample": "pinned through cfg_combine / euler_step; DiT part as block_fwd",
+    "sample_cached": "pinned: no reuse -> sample; attention reuse with gate1 = 0 -> sample; CFG reuse "
+                     "with guidance 1 -> sample; storing changes nothing; reuse of a zero cache -> "
+                     "the block without its self-attention branch",
 }

@@ -412,4 +412,89 @@ def pin_cfg(o):
     assert np.array_equal(o.cfg_euler(x, vc, None, 7.0, -0.1), o.euler_step(x, vc, -0.1))
 
 
+# ------------------------------------------------------------- diffusion cache
+def _tiny_sampling(seed=21):
+    import wan_inputs as wi
+    c = wi.get_config("tiny").replace(B=2, img_len=5, img_dim=32)
+    mw = wi.make_model_weights(c, seed=seed)
+    bws = [wi.make_block_weights(c, i, seed=seed) for i in range(2)]
+    x_t, z = wi.make_latents(c, seed=seed)
+    txt, img = wi.make_contexts(c, seed=seed)
+    kw = dict(ln_eps=c.ln_eps, rms_eps=c.rms_eps, theta=c.rope_theta, freq_dim=c.freq_dim,
+              out_channels=c.out_channels)
+    return c, mw, bws, x_t, z, txt, img, kw
+
+
+def pin_sample_cached_reductions(o):
+    """The cached sampler reduces to the plain one: no reuse gives ``sample`` bit for bit; attention
+    reuse with gate1 = 0 at every t (time projection rows and block bias of that chunk zeroed)
+    gives ``sample`` bit for bit; CFG reuse with guidance 1 gives ``sample`` (v = v_c)."""
+    c, mw, bws, x_t, z, txt, img, kw = _tiny_sampling()
+    steps = 4
+    ref, _ = o.sample(x_t, z, steps, c.guidance, mw, bws, txt, img, c.heads, **kw)
+    got, _ = o.sample_cached(x_t, z, steps, c.guidance, mw, bws, txt, img, c.heads, [False] * 4, [False] * 4, **kw)
+    assert np.array_equal(got, ref)
+    dim = c.dim
+    mw0 = dict(mw)
+    mw0["wtp"] = np.array(mw["wtp"], float).copy()
+    mw0["btp"] = np.array(mw["btp"], float).copy()
+    mw0["wtp"][2 * dim:3 * dim] = 0.0
+    mw0["btp"][2 * dim:3 * dim] = 0.0
+    bws0 = []
+    for w in bws:
+        w0 = dict(w)
+        w0["mod_bias"] = np.array(w["mod_bias"], float).copy()
+        w0["mod_bias"][2] = 0.0
+        bws0.append(w0)
+    ref0, _ = o.sample(x_t, z, steps, c.guidance, mw0, bws0, txt, img, c.heads, **kw)
+    got0, _ = o.sample_cached(x_t, z, steps, c.guidance, mw0, bws0, txt, img, c.heads,
+                              [False, True, False, True], [False] * 4, **kw)
+    assert np.array_equal(got0, ref0)
+    ref1, _ = o.sample(x_t, z, steps, 1.0, mw, bws, txt, img, c.heads, **kw)
+    got1, _ = o.sample_cached(x_t, z, steps, 1.0, mw, bws, txt, img, c.heads, [False] * 4,
+                              [False, False, True, True], **kw)
+    assert np.allclose(got1, ref1, rtol=0, atol=1e-12)
+
+
+def pin_attention_cache_modes(o):
+    """Storing the self-attention output changes nothing; reusing a zero cache equals the block with
+    its self-attention branch gated off; reusing the stored value at the same inputs reproduces the
+    block."""
+    x, e0, w, kv, grid, heads = _tiny_block_inputs()
+    ref = o.block_fwd(x, e0, w, kv, grid, heads)
+    cache = {"mode": "store", "y": np.zeros(x.shape)}
+    assert np.array_equal(o.block_fwd(x, e0, w, kv, grid, heads, attn_cache=cache), ref)
+    assert np.abs(cache["y"]).max() > 0
+    again = o.block_fwd(x, e0, w, kv, grid, heads, attn_cache={"mode": "reuse", "y": cache["y"]})
+    assert np.array_equal(again, ref)
+    e0z, wz = np.array(e0, float).copy(), dict(w)
+    e0z[:, 2] = 0.0
+    wz["mod_bias"] = np.array(w["mod_bias"], float).copy()
+    wz["mod_bias"][2] = 0.0
+    off = o.block_fwd(x, e0z, wz, kv, grid, heads)
+    zero = o.block_fwd(x, e0, w, kv, grid, heads, attn_cache={"mode": "reuse", "y": np.zeros(x.shape)})
+    assert np.array_equal(zero, off)
+
+
+def pin_cfg_cache_uses_last_uncond(o):
+    """A CFG-reuse step combines the fresh conditional velocity with the unconditional one of the
+    previous step, composed here from ``dit_fwd`` and ``cfg_euler`` directly."""
+    c, mw, bws, x_t, z, txt, img, kw = _tiny_sampling()
+    steps, dt = 3, -1.0 / 3
+    got, _ = o.sample_cached(x_t, z, steps, c.guidance, mw, bws, txt, img, c.heads, [False] * 3,
+                             [False, False, True], **kw)
+    x = np.array(x_t, float)
+    for k in range(steps):
+        t = 1.0 + k * dt
+        x_in = o.build_i2v_input(x, z)
+        if k < 2:
+            v = o.dit_fwd(np.repeat(x_in, 2, axis=0), t, mw, bws, txt, img, c.heads, **kw)
+            v_u = v[1:2]
+            x = o.cfg_euler(x, v[0:1], v_u, c.guidance, dt)
+        else:
+            v_c = o.dit_fwd(x_in, t, mw, bws, np.asarray(txt)[:1], img, c.heads, **kw)
+            x = o.cfg_euler(x, v_c, v_u, c.guidance, dt)
+    assert np.allclose(got, x, rtol=0, atol=1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
