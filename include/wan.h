@@ -216,6 +216,19 @@ size_t wan_dit_block_workspace_bytes(const wan_block_cfg* cfg, wan_grid grid, in
 int wan_dit_block_fwd(const wan_block_cfg* cfg, const wan_block_weights* w, wan_grid grid, int32_t B, float* x,
                       const float* e0, const wan_cross_kv* kv, void* ws, size_t ws_bytes, wan_stream_t stream);
 
+/* Attention cache ([DEEP] §5.3: attention outputs reused across sampling steps).  Same as
+ * wan_dit_block_fwd, with the self-attention layer's output y = o W_o^T + b_o (before the gate) kept in
+ * attn_y [B, S, dim] float32 (caller-owned, one per block and batch row set):
+ *   WAN_ATTN_CACHE_OFF    attn_y unused (this is wan_dit_block_fwd);
+ *   WAN_ATTN_CACHE_STORE  the block computes as usual and writes y to attn_y;
+ *   WAN_ATTN_CACHE_REUSE  the block skips LN1, the Q/K/V product, the norms and RoPE, the attention
+ *                         and the O product, and adds gate1 * attn_y (gate1 of this call's e0) to x.
+ * The other branches always run.  Which steps reuse is the caller's schedule. */
+typedef enum { WAN_ATTN_CACHE_OFF = 0, WAN_ATTN_CACHE_STORE = 1, WAN_ATTN_CACHE_REUSE = 2 } wan_attn_cache_mode;
+int wan_dit_block_fwd_cached(const wan_block_cfg* cfg, const wan_block_weights* w, wan_grid grid, int32_t B, float* x,
+                             const float* e0, const wan_cross_kv* kv, float* attn_y, int32_t attn_mode, void* ws,
+                             size_t ws_bytes, wan_stream_t stream);
+
 /* a11 -- head ([I2V] §5.5): (shift, scale) = head_mod + e[b];
  * out [B*S, 4*C_out] float32 = (LN(x)(1 + scale) + shift) wh^T + bh, x [B, S, dim] float32,
  * e [B, dim] float32.  Follow with wan_unpatchify.  Workspace: wan_head_workspace_bytes(). */

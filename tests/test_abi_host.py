@@ -106,6 +106,18 @@ def test_block_validation(lib):
     assert "w1" in _err(lib)
     assert lib.wan_dit_block_fwd(C.byref(_cfg(img_len=4)), C.byref(w), g, 1, FAKE, FAKE, C.byref(kv), FAKE,
                                  ws_need * 2, None) == L.WAN_EINVAL
+    # the attention-cache entry: mode outside 0..2, or a cache mode without the y buffer
+    blk = lib.wan_dit_block_fwd_cached
+    assert blk(C.byref(_cfg()), C.byref(w), g, 1, FAKE, FAKE, C.byref(kv), FAKE, 3, FAKE, ws_need,
+               None) == L.WAN_EINVAL
+    assert "attn_mode" in _err(lib)
+    for mode in (L.WAN_ATTN_CACHE_STORE, L.WAN_ATTN_CACHE_REUSE):
+        assert blk(C.byref(_cfg()), C.byref(w), g, 1, FAKE, FAKE, C.byref(kv), None, mode, FAKE, ws_need,
+                   None) == L.WAN_EINVAL
+        assert "attn_y" in _err(lib)
+    # the other checks still run behind a valid mode
+    assert blk(C.byref(_cfg()), C.byref(w), g, 1, FAKE, FAKE, C.byref(kv), FAKE, L.WAN_ATTN_CACHE_REUSE, FAKE,
+               ws_need - 1, None) == L.WAN_EWORKSPACE
 
 
 def test_other_entry_validation(lib):

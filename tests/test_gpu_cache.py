@@ -1,0 +1,97 @@
+"""Diffusion cache (attention-output cache + CFG cache) against the oracle's cached sampler and
+block: a small sampling run with both kinds of reuse, and a store-then-reuse pair of the 32760-token
+block on sampled rows.  Tolerances as for the uncached path (fp32 1e-4, bf16 1e-2)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import wan_inputs as wi
+from tests.gpu_util import case, dev, host, rel_l2, require_gpu
+from tests.test_gpu_block import _inputs
+from video_diffusion_transformer_step_amd import _lib as L
+from video_diffusion_transformer_step_amd import runtime as R
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 1e-2}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_sample_cached_small(dtype):
+    """CFG sampling (2 rows), 2 blocks, 5 steps: attention reuse on steps 2 and 4, CFG reuse on 3 and 4."""
+    require_gpu()
+    c = wi.get_config("tiny").replace(dtype=dtype, B=2, img_len=5, img_dim=32)
+    case(f"sample cached tiny {dtype}")
+    steps, layers = 5, 2
+    attn_reuse = [False, False, True, False, True]
+    cfg_reuse = [False, False, False, True, True]
+    mw = wi.make_model_weights(c, seed=3)
+    bws = [wi.make_block_weights(c, i, seed=3) for i in range(layers)]
+    x_t, z = wi.make_latents(c, seed=3)
+    txt, img = wi.make_contexts(c, seed=3)
+    model = R.DeviceModel(mw, c.dtype)
+    blocks = [R.DeviceBlock(w, c.dtype) for w in bws]
+    t_emb, i_emb = R.embed_contexts(c, model, txt, img, c.B)
+    caches = R.cross_kv_all(c, blocks, t_emb, i_emb, c.B)
+    buf = R.alloc_step(c, c.B)
+    ac = R.AttnCache(c, layers, c.B)
+    xg = dev(x_t)
+    R.sample_cached(c, model, blocks, caches, xg, dev(z) if z is not None else None, steps, c.guidance, buf, c.B,
+                    attn_reuse, cfg_reuse, ac)
+    got = host(xg)
+    ref, _ = oracle.sample_cached(x_t, z, steps, c.guidance, mw, bws, txt, img, c.heads, attn_reuse, cfg_reuse,
+                                  ln_eps=c.ln_eps, rms_eps=c.rms_eps, theta=c.rope_theta, freq_dim=c.freq_dim,
+                                  out_channels=c.out_channels)
+    x0 = np.asarray(x_t, np.float64)
+    e, e_dx = rel_l2(got, ref), rel_l2(got - x0, ref - x0)
+    # the cache must matter: the uncached sampler's total update differs by far more than the tolerance
+    plain, _ = oracle.sample(x_t, z, steps, c.guidance, mw, bws, txt, img, c.heads, ln_eps=c.ln_eps,
+                             rms_eps=c.rms_eps, theta=c.rope_theta, freq_dim=c.freq_dim, out_channels=c.out_channels)
+    moved = rel_l2(ref - x0, plain - x0)
+    print(f"[cache {dtype}] rel-L2 vs cached oracle: x {e:.3e}, x - x_T {e_dx:.3e}; cached vs plain sampler "
+          f"update {moved:.3e}", flush=True)
+    assert e <= TOL[dtype]
+    assert moved > 5 * TOL[dtype]
+
+
+@pytest.mark.timeout(900)
+def test_block_cache_store_then_reuse_full_size():
+    """The 32760-token block: store at one step's e0, then reuse at another's; the reuse output against
+    the oracle block reusing its own stored y, sampled rows."""
+    require_gpu()
+    c = wi.get_config("t2v-1.3b")
+    case(f"block cache store/reuse full size {c.name}")
+    rows = wi.sample_rows(c, 48, seed=5)
+    x, e0, t_emb, i_emb, bw = _inputs(c, seed=5)
+    _, e0b = oracle.time_embed(0.25, wi.make_model_weights(c, seed=5), c.freq_dim)
+    e0b = np.broadcast_to(e0b[None], e0.shape).astype(np.float32)
+    td = torch.bfloat16
+    blk = R.DeviceBlock(bw, c.dtype)
+    (kc,) = R.cross_kv_all(c, [blk], dev(t_emb, td), None if i_emb is None else dev(i_emb, td), c.B)
+    cfg = R.cfg_of(c)
+    ws = torch.empty(L.block_ws_bytes(cfg, c.grid, c.B), dtype=torch.uint8, device="cuda")
+    y = torch.zeros((c.B, c.S, c.dim), dtype=torch.float32, device="cuda")
+    x1 = dev(x)
+    L.dit_block_fwd(cfg, blk.bw, c.grid, c.B, x1, dev(e0), kc.kv, ws, attn_y=y, attn_mode=L.WAN_ATTN_CACHE_STORE)
+    x2 = dev(x)
+    L.dit_block_fwd(cfg, blk.bw, c.grid, c.B, x2, dev(e0b), kc.kv, ws, attn_y=y, attn_mode=L.WAN_ATTN_CACHE_REUSE)
+    got_store, got_reuse = host(x1), host(x2)
+    # oracle: store at e0 on the sampled rows, reuse at e0b
+    cache = {"mode": "store", "y": np.zeros((c.B, len(rows), c.dim))}
+    kv = []
+    for b in range(c.B):
+        kt, vt = oracle.cross_kv(t_emb[b], bw["wck"], bw["bck"], bw["wcv"], bw["bcv"])
+        kv.append((kt, vt, None, None))
+    ref_store = oracle.block_fwd(x, e0, bw, kv, c.grid, c.heads, rows=rows, ln_eps=c.ln_eps, rms_eps=c.rms_eps,
+                                 theta=c.rope_theta, attn_cache=cache)
+    cache["mode"] = "reuse"
+    ref_reuse = oracle.block_fwd(x, e0b, bw, kv, c.grid, c.heads, rows=rows, ln_eps=c.ln_eps, rms_eps=c.rms_eps,
+                                 theta=c.rope_theta, attn_cache=cache)
+    xr = x[:, rows]
+    for name, g, r in (("store", got_store[:, rows], ref_store), ("reuse", got_reuse[:, rows], ref_reuse)):
+        e = rel_l2(g - xr, r - xr)
+        print(f"[cache full size] {name}: rel-L2 dx {e:.3e}", flush=True)
+        assert e <= TOL["bf16"]
+    # the cached y is the stored layer output: reuse differs from a fresh block at e0b only through it
+    assert np.abs(host(y)).max() > 0

@@ -76,6 +76,8 @@ _SIGS = {
     "wan_dit_block_workspace_bytes": ([C.POINTER(BlockCfg), Grid, C.c_int32], C.c_size_t),
     "wan_dit_block_fwd": ([C.POINTER(BlockCfg), C.POINTER(BlockWeights), Grid, C.c_int32, vp, vp, C.POINTER(CrossKV),
                            vp, C.c_size_t, vp], C.c_int),
+    "wan_dit_block_fwd_cached": ([C.POINTER(BlockCfg), C.POINTER(BlockWeights), Grid, C.c_int32, vp, vp,
+                                  C.POINTER(CrossKV), vp, C.c_int32, vp, C.c_size_t, vp], C.c_int),
     "wan_head_workspace_bytes": ([C.POINTER(BlockCfg), C.c_int64], C.c_size_t),
     "wan_head_fwd": ([C.POINTER(BlockCfg), C.POINTER(HeadWeights), C.c_int32, C.c_int32, C.c_int32, vp, vp, vp, vp,
                       C.c_size_t, vp], C.c_int),
@@ -237,9 +239,18 @@ def block_ws_bytes(cfg, grid, B):
     return lib().wan_dit_block_workspace_bytes(C.byref(cfg), Grid(*grid), B)
 
 
-def dit_block_fwd(cfg, bw: BlockWeights, grid, B, x, e0, kv: CrossKV, ws, stream=None):
-    _check(lib().wan_dit_block_fwd(C.byref(cfg), C.byref(bw), Grid(*grid), B, _p(x), _p(e0), C.byref(kv), _p(ws),
-                                   ws.numel() * ws.element_size(), _stream(stream)), "wan_dit_block_fwd")
+WAN_ATTN_CACHE_OFF, WAN_ATTN_CACHE_STORE, WAN_ATTN_CACHE_REUSE = 0, 1, 2
+
+
+def dit_block_fwd(cfg, bw: BlockWeights, grid, B, x, e0, kv: CrossKV, ws, stream=None, attn_y=None,
+                  attn_mode=WAN_ATTN_CACHE_OFF):
+    if attn_mode == WAN_ATTN_CACHE_OFF:
+        _check(lib().wan_dit_block_fwd(C.byref(cfg), C.byref(bw), Grid(*grid), B, _p(x), _p(e0), C.byref(kv),
+                                       _p(ws), ws.numel() * ws.element_size(), _stream(stream)), "wan_dit_block_fwd")
+    else:
+        _check(lib().wan_dit_block_fwd_cached(C.byref(cfg), C.byref(bw), Grid(*grid), B, _p(x), _p(e0), C.byref(kv),
+                                              _p(attn_y), attn_mode, _p(ws), ws.numel() * ws.element_size(),
+                                              _stream(stream)), "wan_dit_block_fwd_cached")
 
 
 def head_ws_bytes(cfg, tokens):

@@ -124,11 +124,13 @@ struct EpiResidual {
   const float* e0;  // [B, 6, N] or null (gate 1)
   const float* mb;  // [6, N]
   int chunk, S, N;
+  float* y = nullptr;  // optional: also record the branch output C + bias (row stride N)
   __device__ __forceinline__ void operator()(int m, int n, float4 v) const {
     if (bias) {
       const float4 b = *reinterpret_cast<const float4*>(bias + n);
       v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
     }
+    if (y) *reinterpret_cast<float4*>(y + (int64_t)m * N + n) = v;
     float* p = x + (int64_t)m * ldx + n;
     float4 r = *reinterpret_cast<const float4*>(p);
     if (e0) {
@@ -628,8 +630,9 @@ hipError_t gemm_qkv(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int
 
 template <typename T>
 hipError_t gemm_residual(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const float* bias,
-                         const float* e0, const float* mb, int chunk, int S, float* x, int64_t ldx, hipStream_t s) {
-  EpiResidual epi{x, ldx, bias, e0, mb, chunk, S, N};
+                         const float* e0, const float* mb, int chunk, int S, float* x, int64_t ldx, hipStream_t s,
+                         float* ystore) {
+  EpiResidual epi{x, ldx, bias, e0, mb, chunk, S, N, ystore};
   return run_gemm<T>(A, lda, W, ldw, M, N, K, epi, s);
 }
 
@@ -651,8 +654,9 @@ hipError_t gemm_qkv_e4m3(const uint8_t* A, int64_t lda, const float* a_scales, c
 
 hipError_t gemm_e4m3_residual(const uint8_t* A, int64_t lda, const float* a_scales, const uint8_t* W, int64_t ldw,
                               const float* w_scale, int M, int N, int K, const float* bias, const float* e0, const float* mb,
-                              int chunk, int S, float* x, int64_t ldx, hipStream_t s) {
-  return run_gemm_e4m3(A, lda, a_scales, W, ldw, w_scale, M, N, K, EpiResidual{x, ldx, bias, e0, mb, chunk, S, N}, s);
+                              int chunk, int S, float* x, int64_t ldx, hipStream_t s, float* ystore) {
+  return run_gemm_e4m3(A, lda, a_scales, W, ldw, w_scale, M, N, K,
+                       EpiResidual{x, ldx, bias, e0, mb, chunk, S, N, ystore}, s);
 }
 
 template <typename T>
@@ -684,9 +688,9 @@ template hipError_t gemm_qkv<float>(const float*, int64_t, const float*, int64_t
 template hipError_t gemm_qkv<bf16>(const bf16*, int64_t, const bf16*, int64_t, int, int, int, const float*, bf16*,
                                    int64_t, bf16*, int, int, int, int, hipStream_t);
 template hipError_t gemm_residual<float>(const float*, int64_t, const float*, int64_t, int, int, int, const float*,
-                                         const float*, const float*, int, int, float*, int64_t, hipStream_t);
+                                         const float*, const float*, int, int, float*, int64_t, hipStream_t, float*);
 template hipError_t gemm_residual<bf16>(const bf16*, int64_t, const bf16*, int64_t, int, int, int, const float*,
-                                        const float*, const float*, int, int, float*, int64_t, hipStream_t);
+                                        const float*, const float*, int, int, float*, int64_t, hipStream_t, float*);
 template hipError_t gemv<float>(const float*, int, int, const float*, int, const float*, int, int, float*,
                                 hipStream_t);
 template hipError_t gemv<bf16>(const bf16*, int, int, const float*, int, const float*, int, int, float*,

@@ -137,6 +137,25 @@ __global__ __launch_bounds__(256) void transpose_heads_kernel(const T* __restric
   }
 }
 
+// x += g * y over float4 groups: row m = i / d4, channels 4 (i % d4) ..; g from the row's batch entry.
+__global__ __launch_bounds__(256) void gated_add_kernel(float* __restrict__ x, const float* __restrict__ y,
+                                                        const float* __restrict__ mod, int chunk, int64_t n4, int d4,
+                                                        int S) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = i / d4;
+    const int c4 = (int)(i - m * d4);
+    const int64_t b = m / S;
+    const float4 g = reinterpret_cast<const float4*>(mod + (b * 6 + chunk) * (int64_t)d4 * 4)[c4];
+    const float4 v = reinterpret_cast<const float4*>(y)[i];
+    float4 r = reinterpret_cast<float4*>(x)[i];
+    r.x = fmaf(g.x, v.x, r.x);
+    r.y = fmaf(g.y, v.y, r.y);
+    r.z = fmaf(g.z, v.z, r.z);
+    r.w = fmaf(g.w, v.w, r.w);
+    reinterpret_cast<float4*>(x)[i] = r;
+  }
+}
+
 __global__ __launch_bounds__(256) void mod_combine_kernel(const float* __restrict__ e0, const float* __restrict__ mb,
                                                           int B, int dim, float* __restrict__ mod) {
   const int64_t n = (int64_t)B * 6 * dim;
@@ -203,6 +222,15 @@ hipError_t launch_transpose_heads(const T* v, int64_t ld, int64_t col0, int B, i
   if (hd > 128) return hipErrorInvalidValue;
   dim3 grid((unsigned)ceil_div(Spad, 64), (unsigned)H, (unsigned)B);
   hipLaunchKernelGGL(transpose_heads_kernel<T>, grid, dim3(256), 0, s, v, ld, col0, S, H, hd, Spad, vt);
+  return hipGetLastError();
+}
+
+hipError_t launch_gated_add(float* x, const float* y, const float* mod, int chunk, int64_t rows, int dim, int S,
+                            hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (dim % 4 != 0) return hipErrorInvalidValue;
+  const int64_t n4 = rows * (dim / 4);
+  hipLaunchKernelGGL(gated_add_kernel, dim3(grid_for(n4)), dim3(256), 0, s, x, y, mod, chunk, n4, dim / 4, S);
   return hipGetLastError();
 }
 

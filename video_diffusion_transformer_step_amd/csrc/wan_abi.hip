@@ -180,7 +180,8 @@ size_t block_plan(const wan_block_cfg& c, const wan_grid& g, int B, char* base, 
 
 template <typename T>
 int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_grid& g, int B, float* x,
-                const float* e0, const wan_cross_kv& kv, void* ws, hipStream_t st) {
+                const float* e0, const wan_cross_kv& kv, void* ws, hipStream_t st, float* attn_y = nullptr,
+                int attn_mode = WAN_ATTN_CACHE_OFF) {
   BlockWs<T> w;
   block_plan<T>(c, g, B, reinterpret_cast<char*>(ws), &w);
   const int S = g.T * g.Hp * g.Wp, BS = B * S, dim = c.dim, H = c.heads, hd = c.head_dim;
@@ -189,42 +190,48 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
   // self-attention branch
   // the block's six modulation vectors e0 + mod_bias ("Wan 技术深度解析" §2.5), formed once
   HIP_TRY(launch_mod_combine(e0, W.mod_bias, B, dim, w.mod, st));
-  PROF_TRY(WAN_K_LN1, launch_ln_mod<T>(x, BS, dim, S, 0, w.mod, nullptr, 0, 1, c.ln_eps, w.u, st));
-  // q, k -> qkv[:, 0 .. 2 dim) (row stride 2 dim); v -> V^T directly
-  PROF_TRY(WAN_K_VT_TAIL, launch_vt_tail_zero<T>(w.vt, (int64_t)B * dim, S, Spad, st));
   const bool f8g = (c.flags & WAN_FLAG_FP8_GEMM) != 0;
   const wan_block_weights_e4m3* Q8 = W.e4m3;
-  if (f8g) {  // E4M3 products ("Wan 技术深度解析" §5.3): per-token codes of u, then the product
-    PROF_TRY(WAN_K_QUANT, launch_quant_rows_e4m3((const bf16*)w.u, dim, BS, dim, w.a8, dim, w.sa, st));
-    PROF_TRY(WAN_K_QKV_GEMM, gemm_qkv_e4m3(w.a8, dim, w.sa, (const uint8_t*)Q8->wqkv, dim, Q8->s_wqkv, BS, dim, dim,
-                                           W.bqkv, (bf16*)w.qkv, 2 * dim, (bf16*)w.vt, S, H, hd, Spad, st));
+  if (attn_mode == WAN_ATTN_CACHE_REUSE) {
+    // attention cache ("Wan 技术深度解析" §5.3): the layer output y recorded at an earlier step, gated now
+    PROF_TRY(WAN_K_O_GEMM, launch_gated_add(x, attn_y, w.mod, 2, (int64_t)BS, dim, S, st));
   } else {
-    PROF_TRY(WAN_K_QKV_GEMM, gemm_qkv<T>(w.u, dim, (const T*)W.wqkv, dim, BS, dim, dim, W.bqkv, w.qkv, 2 * dim, w.vt,
-                                         S, H, hd, Spad, st));
-  }
-  PROF_TRY(WAN_K_QK_NORM_ROPE, launch_qk_norm_rope<T>(w.qkv, w.qkv + dim, 2 * dim, w.qkv, w.qkv + dim, 2 * dim, B, g.T, g.Hp, g.Wp, H, hd,
-                                 W.gq, W.gk, 1, c.rms_eps, c.rope_theta, st));
-  if constexpr (sizeof(T) == 2) {
-    if (c.flags & WAN_FLAG_FP8_ATTN) {  // quantised self-attention ("Wan 技术深度解析" §5.3)
-      PROF_TRY(WAN_K_QUANT, launch_quant_q(w.qkv, 2 * dim, B, S, H, hd, (int8_t*)w.q8, w.sq, st));
-      PROF_TRY(WAN_K_QUANT, launch_quant_k(w.qkv + dim, 2 * dim, B, S, H, hd, (int8_t*)w.k8, w.sk, st));
-      PROF_TRY(WAN_K_QUANT, launch_quant_vt(w.vt, (int64_t)B * dim, Spad, (int)round_up(S, 128), w.v8t, w.sv, st));
-      PROF_TRY(WAN_K_SELF_ATTN, launch_attention_q8(w.q8, w.sq, w.k8, w.sk, w.v8t, w.sv, B, S, S, H, hd, w.o, nullptr, st));
+    float* ystore = attn_mode == WAN_ATTN_CACHE_STORE ? attn_y : nullptr;
+    PROF_TRY(WAN_K_LN1, launch_ln_mod<T>(x, BS, dim, S, 0, w.mod, nullptr, 0, 1, c.ln_eps, w.u, st));
+    // q, k -> qkv[:, 0 .. 2 dim) (row stride 2 dim); v -> V^T directly
+    PROF_TRY(WAN_K_VT_TAIL, launch_vt_tail_zero<T>(w.vt, (int64_t)B * dim, S, Spad, st));
+    if (f8g) {  // E4M3 products ("Wan 技术深度解析" §5.3): per-token codes of u, then the product
+      PROF_TRY(WAN_K_QUANT, launch_quant_rows_e4m3((const bf16*)w.u, dim, BS, dim, w.a8, dim, w.sa, st));
+      PROF_TRY(WAN_K_QKV_GEMM, gemm_qkv_e4m3(w.a8, dim, w.sa, (const uint8_t*)Q8->wqkv, dim, Q8->s_wqkv, BS, dim, dim,
+                                             W.bqkv, (bf16*)w.qkv, 2 * dim, (bf16*)w.vt, S, H, hd, Spad, st));
+    } else {
+      PROF_TRY(WAN_K_QKV_GEMM, gemm_qkv<T>(w.u, dim, (const T*)W.wqkv, dim, BS, dim, dim, W.bqkv, w.qkv, 2 * dim, w.vt,
+                                           S, H, hd, Spad, st));
     }
-  }
-  if (!(c.flags & WAN_FLAG_FP8_ATTN)) {
-    KVStream self{w.qkv + dim, (int64_t)S * 2 * dim, 2 * dim, w.vt, S, Spad};
-    PROF_TRY(WAN_K_SELF_ATTN, launch_attention<T>(w.qkv, (int64_t)S * 2 * dim, 2 * dim, self, self, 1, B, S, H, hd,
-                                                  scale, w.o, (int64_t)S * dim, dim, 0, st));
-  }
-  if (f8g) {
-    PROF_TRY(WAN_K_QUANT, launch_quant_rows_e4m3((const bf16*)w.o, dim, BS, dim, w.a8, dim, w.sa, st));
-    PROF_TRY(WAN_K_O_GEMM, gemm_e4m3_residual(w.a8, dim, w.sa, (const uint8_t*)Q8->wo, dim, Q8->s_wo, BS, dim, dim, W.bo,
-                                              w.mod, nullptr, 2, S, x, dim, st));
-  } else {
-    PROF_TRY(WAN_K_O_GEMM, gemm_residual<T>(w.o, dim, (const T*)W.wo, dim, BS, dim, dim, W.bo, w.mod, nullptr, 2, S, x,
-                                            dim, st));
-  }
+    PROF_TRY(WAN_K_QK_NORM_ROPE, launch_qk_norm_rope<T>(w.qkv, w.qkv + dim, 2 * dim, w.qkv, w.qkv + dim, 2 * dim, B, g.T, g.Hp, g.Wp, H, hd,
+                                   W.gq, W.gk, 1, c.rms_eps, c.rope_theta, st));
+    if constexpr (sizeof(T) == 2) {
+      if (c.flags & WAN_FLAG_FP8_ATTN) {  // quantised self-attention ("Wan 技术深度解析" §5.3)
+        PROF_TRY(WAN_K_QUANT, launch_quant_q(w.qkv, 2 * dim, B, S, H, hd, (int8_t*)w.q8, w.sq, st));
+        PROF_TRY(WAN_K_QUANT, launch_quant_k(w.qkv + dim, 2 * dim, B, S, H, hd, (int8_t*)w.k8, w.sk, st));
+        PROF_TRY(WAN_K_QUANT, launch_quant_vt(w.vt, (int64_t)B * dim, Spad, (int)round_up(S, 128), w.v8t, w.sv, st));
+        PROF_TRY(WAN_K_SELF_ATTN, launch_attention_q8(w.q8, w.sq, w.k8, w.sk, w.v8t, w.sv, B, S, S, H, hd, w.o, nullptr, st));
+      }
+    }
+    if (!(c.flags & WAN_FLAG_FP8_ATTN)) {
+      KVStream self{w.qkv + dim, (int64_t)S * 2 * dim, 2 * dim, w.vt, S, Spad};
+      PROF_TRY(WAN_K_SELF_ATTN, launch_attention<T>(w.qkv, (int64_t)S * 2 * dim, 2 * dim, self, self, 1, B, S, H, hd,
+                                                    scale, w.o, (int64_t)S * dim, dim, 0, st));
+    }
+    if (f8g) {
+      PROF_TRY(WAN_K_QUANT, launch_quant_rows_e4m3((const bf16*)w.o, dim, BS, dim, w.a8, dim, w.sa, st));
+      PROF_TRY(WAN_K_O_GEMM, gemm_e4m3_residual(w.a8, dim, w.sa, (const uint8_t*)Q8->wo, dim, Q8->s_wo, BS, dim, dim, W.bo,
+                                                w.mod, nullptr, 2, S, x, dim, st, ystore));
+    } else {
+      PROF_TRY(WAN_K_O_GEMM, gemm_residual<T>(w.o, dim, (const T*)W.wo, dim, BS, dim, dim, W.bo, w.mod, nullptr, 2, S, x,
+                                              dim, st, ystore));
+    }
+  }  // self-attention branch
   // cross-attention branch (no adaLN, no RoPE)
   PROF_TRY(WAN_K_LN3, launch_ln_mod<T>(x, BS, dim, S, 1, W.ln3_w, W.ln3_b, 0, 0, c.ln_eps, w.u, st));
   T* qc = w.qkv;  // reuse: [BS, dim]
@@ -514,6 +521,15 @@ size_t wan_dit_block_workspace_bytes(const wan_block_cfg* cfg, wan_grid grid, in
 
 int wan_dit_block_fwd(const wan_block_cfg* cfg, const wan_block_weights* w, wan_grid grid, int32_t B, float* x,
                       const float* e0, const wan_cross_kv* kv, void* ws, size_t ws_bytes, wan_stream_t stream) {
+  return wan_dit_block_fwd_cached(cfg, w, grid, B, x, e0, kv, nullptr, WAN_ATTN_CACHE_OFF, ws, ws_bytes, stream);
+}
+
+int wan_dit_block_fwd_cached(const wan_block_cfg* cfg, const wan_block_weights* w, wan_grid grid, int32_t B, float* x,
+                             const float* e0, const wan_cross_kv* kv, float* attn_y, int32_t attn_mode, void* ws,
+                             size_t ws_bytes, wan_stream_t stream) {
+  if (attn_mode != WAN_ATTN_CACHE_OFF && attn_mode != WAN_ATTN_CACHE_STORE && attn_mode != WAN_ATTN_CACHE_REUSE)
+    return fail(WAN_EINVAL, "attn_mode %d not in 0..2", attn_mode);
+  if (attn_mode != WAN_ATTN_CACHE_OFF) WAN_TRY(need_ptr(attn_y, "attn_y"));
   WAN_TRY(check_cfg(cfg));
   WAN_TRY(check_grid(grid));
   if (B <= 0) return fail(WAN_EINVAL, "B must be positive");
@@ -525,8 +541,9 @@ int wan_dit_block_fwd(const wan_block_cfg* cfg, const wan_block_weights* w, wan_
   const size_t need = wan_dit_block_workspace_bytes(cfg, grid, B);
   if (ws_bytes < need) return fail(WAN_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   WAN_TRY(need_ptr(ws, "ws"));
-  if (cfg->dtype == WAN_BF16) return block_fwd_t<bf16>(*cfg, *w, grid, B, x, e0, *kv, ws, hs(stream));
-  return block_fwd_t<float>(*cfg, *w, grid, B, x, e0, *kv, ws, hs(stream));
+  if (cfg->dtype == WAN_BF16)
+    return block_fwd_t<bf16>(*cfg, *w, grid, B, x, e0, *kv, ws, hs(stream), attn_y, attn_mode);
+  return block_fwd_t<float>(*cfg, *w, grid, B, x, e0, *kv, ws, hs(stream), attn_y, attn_mode);
 }
 
 size_t wan_head_workspace_bytes(const wan_block_cfg* cfg, int64_t tokens) {

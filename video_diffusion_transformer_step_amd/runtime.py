@@ -182,10 +182,12 @@ def alloc_step(c, B, device="cuda", fp8_attn=False, fp8_gemm=False) -> StepBuffe
 
 
 def dit_forward(c, model: DeviceModel, blocks, caches, x_latent, z_img, t, buf: StepBuffers, B,
-                known_pixel_frames=None, fp8_attn=False, fp8_gemm=False):
+                known_pixel_frames=None, fp8_attn=False, fp8_gemm=False, attn_cache=None,
+                attn_mode=0):
     """One DiT evaluation over B rows sharing the latent x_latent [1, C, T, H, W] (CFG rows see the same
     x_in).  Result in buf.v [B, C_out, T, H, W].  fp8_attn / fp8_gemm: quantised self-attention / E4M3
-    products in every block (buf from alloc_step with the same flags)."""
+    products in every block (buf from alloc_step with the same flags).  attn_cache / attn_mode: the
+    attention cache of every block (AttnCache, its rows 0 .. B-1) and WAN_ATTN_CACHE_STORE / _REUSE."""
     cfg = cfg_of(c, fp8_attn=fp8_attn, fp8_gemm=fp8_gemm)
     one = x_latent.shape[0]
     for b in range(B):
@@ -195,18 +197,57 @@ def dit_forward(c, model: DeviceModel, blocks, caches, x_latent, z_img, t, buf: 
             L.patchify(buf.x_in[b:b + 1], buf.p[b:b + 1])
         else:
             L.patchify(src, buf.p[b:b + 1])
-    L.patch_embed(cfg, buf.p, c.in_channels, model.w_pe, model.b_pe, buf.x, buf.ws)
+    L.patch_embed(cfg, buf.p[:B], c.in_channels, model.w_pe, model.b_pe, buf.x, buf.ws)
     L.time_embed(cfg, c.freq_dim, model.tw, [t] * B, buf.e, buf.e0)
-    for blk, kc in zip(blocks, caches):
-        L.dit_block_fwd(cfg, blk.bw, c.grid, B, buf.x, buf.e0, kc.kv, buf.ws)
+    for i, (blk, kc) in enumerate(zip(blocks, caches)):
+        if attn_cache is None or attn_mode == L.WAN_ATTN_CACHE_OFF:
+            L.dit_block_fwd(cfg, blk.bw, c.grid, B, buf.x, buf.e0, kc.kv, buf.ws)
+        else:
+            L.dit_block_fwd(cfg, blk.bw, c.grid, B, buf.x, buf.e0, kc.kv, buf.ws, attn_y=attn_cache.t[i],
+                            attn_mode=attn_mode)
     L.head_fwd(cfg, model.hw, c.out_channels, B, c.S, buf.x, buf.e, buf.head_out, buf.ws)
     L.unpatchify(buf.head_out, buf.v)
     return buf.v
 
 
 def denoise_step(c, model, blocks, caches, x_latent, z_img, t, dt, guidance, buf: StepBuffers, B,
-                 known_pixel_frames=None, fp8_attn=False, fp8_gemm=False):
+                 known_pixel_frames=None, fp8_attn=False, fp8_gemm=False, attn_cache=None, attn_mode=0):
     """x_latent <- x_latent + dt * v, v = CFG(v_cond, v_uncond) when B == 2 (row 0 conditional)."""
-    v = dit_forward(c, model, blocks, caches, x_latent, z_img, t, buf, B, known_pixel_frames, fp8_attn, fp8_gemm)
+    v = dit_forward(c, model, blocks, caches, x_latent, z_img, t, buf, B, known_pixel_frames, fp8_attn, fp8_gemm,
+                    attn_cache, attn_mode)
     L.fm_euler_step(x_latent, v[0:1], v[1:2] if B > 1 else None, guidance, dt)
+    return x_latent
+
+
+class AttnCache:
+    """The attention cache of every block: y [B, S, dim] float32 per block (the self-attention layer
+    output before its gate, as wan_dit_block_fwd_cached keeps it)."""
+
+    def __init__(self, c, nblocks, B, device="cuda"):
+        self.t = [torch.zeros((B, c.S, c.dim), dtype=torch.float32, device=device) for _ in range(nblocks)]
+
+    def rows(self, B):
+        """A view on the first B batch rows (same storage)."""
+        v = AttnCache.__new__(AttnCache)
+        v.t = [t[:B] for t in self.t]
+        return v
+
+
+def sample_cached(c, model, blocks, caches, x_latent, z_img, steps, guidance, buf: StepBuffers, B, attn_reuse,
+                  cfg_reuse, attn_cache: AttnCache, t0=1.0, known_pixel_frames=None, fp8_attn=False, fp8_gemm=False):
+    """Euler sampling with the diffusion cache: on steps with attn_reuse[k] every block reuses its cached
+    self-attention output; on steps with cfg_reuse[k] only the conditional row runs and the unconditional
+    velocity of the last full step is reused.  Both lists start with False.  Returns the latent (in place)."""
+    assert not attn_reuse[0] and not cfg_reuse[0]
+    dt = -t0 / steps
+    v_u = torch.empty_like(buf.v[0:1]) if B > 1 else None
+    for k in range(steps):
+        t = t0 + k * dt
+        Bk = 1 if (cfg_reuse[k] and B > 1) else B
+        mode = L.WAN_ATTN_CACHE_REUSE if attn_reuse[k] else L.WAN_ATTN_CACHE_STORE
+        v = dit_forward(c, model, blocks, caches, x_latent, z_img, t, buf, Bk, known_pixel_frames, fp8_attn,
+                        fp8_gemm, attn_cache.rows(Bk), mode)
+        if B > 1 and Bk > 1:
+            v_u.copy_(v[1:2])
+        L.fm_euler_step(x_latent, v[0:1], v_u, guidance, dt)
     return x_latent
