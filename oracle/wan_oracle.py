@@ -24,7 +24,7 @@ __all__ = [
     "layer_norm", "modulate", "rms_norm", "rope_segments", "rope_3d", "token_positions",
     "attention", "attention_lse", "lse_merge", "multihead_attention", "context_embed", "cross_kv", "block_fwd",
     "head_fwd", "cfg_combine", "euler_step", "cfg_euler", "dit_fwd", "sample", "sample_cached",
-    "self_attention_rope_only",
+    "self_attention_rope_only", "snr", "t_moe_from_snr", "expert_for_step", "sample_two_expert",
 ]
 
 f64 = np.float64
@@ -603,6 +603,56 @@ def sample_cached(x_T, z_img, steps: int, guidance: float, model_w, blocks_w, ct
     return x, traj
 
 
+# ---------------------------------------------------------------------------
+# next row: the Wan2.2 timestep-level two-expert switch
+# ---------------------------------------------------------------------------
+def snr(t):
+    """Signal-to-noise ratio of the straight path x_t = (1 - t) x0 + t eps ([I2V-illustrated §7]):
+    the signal weight squared over the noise weight squared, ((1 - t) / t)^2; infinite at t = 0."""
+    t = _a(t)
+    with np.errstate(divide="ignore"):
+        return ((1.0 - t) / t) ** 2
+
+
+def t_moe_from_snr(snr_min: float) -> float:
+    """The switch time of [Wan-deep-dive §7.2]: the t at which the SNR is half of snr_min.
+
+    On the straight path SNR falls monotonically from infinity (t = 0) to 0 (t = 1), so the
+    solution is unique: (1 - t) / t = sqrt(snr_min / 2).  With snr_min = 0 (a schedule that starts at
+    pure noise, t = 1) it is t = 1 and the high-noise expert never runs.
+    """
+    return 1.0 / (1.0 + math.sqrt(snr_min / 2.0))
+
+
+def expert_for_step(t: float, t_moe: float) -> int:
+    """0 = the high-noise expert (t > t_moe), 1 = the low-noise expert (t <= t_moe)
+    ([Wan-deep-dive §7.2], its phase table)."""
+    return 0 if t > t_moe else 1
+
+
+def sample_two_expert(x_T, z_img, steps: int, guidance: float, experts, t_moe: float, ctx_txt, ctx_img,
+                      heads: int, t0: float = 1.0, known_pixel_frames=None, **kw):
+    """``sample`` with the timestep-level two-expert switch of [Wan-deep-dive §7.2]: experts =
+    ((model_w, blocks_w) of the high-noise expert, (model_w, blocks_w) of the low-noise one), each a
+    whole DiT; step k evaluates the expert ``expert_for_step(t_k, t_moe)`` selects.  Schedule, CFG and
+    the Euler update as in ``sample``.  Returns the final latent, the per-step list and the expert
+    index of each step."""
+    x = _a(x_T)
+    B = _a(ctx_txt).shape[0]
+    dt = -t0 / steps
+    traj, used = [], []
+    for k in range(steps):
+        t = t0 + k * dt
+        e = expert_for_step(t, t_moe)
+        model_w, blocks_w = experts[e]
+        x_in = x if z_img is None else build_i2v_input(x, z_img, known_pixel_frames)
+        x_in = np.repeat(x_in, B, axis=0)
+        v = dit_fwd(x_in, t, model_w, blocks_w, ctx_txt, ctx_img, heads, **kw)
+        x = cfg_euler(x, v[0:1], v[1:2] if B > 1 else None, guidance, dt)
+        traj.append(x.copy())
+        used.append(e)
+    return x, traj, used
+
 # Parity status of each function, as checked by the CPU tests.
 PARITY = {
     "i2v_mask": "pinned: hand-worked fixtures (first frame; first+last frame); 4+16=20 channels",
@@ -631,6 +681,15 @@ PARITY = {
     "cfg_combine": "pinned: s = 1 -> v_c, s = 0 -> v_u",
     "euler_step": "pinned: straight-line path lands exactly on the endpoint",
     "sample": "pinned through cfg_combine / euler_step; DiT part as block_fwd",
+    "snr": "pinned: t = 1 -> 0, t = 1/2 -> 1, t -> 0 -> infinity; equals the squared ratio of the "
+           "coefficients of x0 and eps in the straight path at hand-picked t",
+    "t_moe_from_snr": "pinned: snr_min = 2 -> 1/2; snr_min = 0 -> 1; snr(t_moe) = snr_min / 2 by "
+                      "bisection on the monotone snr",
+    "expert_for_step": "pinned: the boundary t = t_moe goes to the low-noise expert; hand-worked "
+                       "sequence for 4 steps from t = 1 at t_moe = 1/2",
+    "sample_two_expert": "pinned: the same expert twice -> sample; t_moe >= t0 -> sample with the "
+                         "low-noise expert; a mixed run equals the high expert's first k steps of "
+                         "sample followed by sample with the low expert from t_k",
     "sample_cached": "pinned: no reuse -> sample; attention reuse with gate1 = 0 -> sample; CFG reuse "
                      "with guidance 1 -> sample; storing changes nothing; reuse of a zero cache -> "
                      "the block without its self-attention branch",

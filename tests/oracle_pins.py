@@ -497,4 +497,57 @@ def pin_cfg_cache_uses_last_uncond(o):
     assert np.allclose(got, x, rtol=0, atol=1e-12)
 
 
+def pin_snr_and_switch_time(o):
+    """SNR of the straight path: 0 at pure noise, 1 where signal and noise weigh the same, and the
+    empirical power ratio of (1 - t) x0 against t eps on unit-variance draws.  The switch time: the
+    hand-worked values snr_min = 2 -> t = 1/2 and snr_min = 0 -> t = 1, and elsewhere the root of
+    snr(t) = snr_min / 2 found by bisection."""
+    assert o.snr(1.0) == 0.0 and o.snr(0.5) == 1.0 and o.snr(0.2) == 16.0
+    assert o.snr(1e-9) > 1e15
+    rng = np.random.default_rng(3)
+    x0, eps = rng.standard_normal(400000), rng.standard_normal(400000)
+    for t in (0.1, 0.3, 0.75, 0.95):
+        ratio = np.mean(((1 - t) * x0) ** 2) / np.mean((t * eps) ** 2)
+        assert abs(ratio / o.snr(t) - 1) < 0.02, (t, ratio)
+    assert o.t_moe_from_snr(2.0) == 0.5 and o.t_moe_from_snr(0.0) == 1.0
+    for snr_min in (0.01, 1.0, 7.0, 100.0):
+        lo, hi = 1e-12, 1.0  # snr decreases in t: snr(lo) > target > snr(hi) = 0
+        for _ in range(200):
+            mid = 0.5 * (lo + hi)
+            lo, hi = (mid, hi) if o.snr(mid) > snr_min / 2 else (lo, mid)
+        assert abs(o.t_moe_from_snr(snr_min) - 0.5 * (lo + hi)) < 1e-12
+
+
+def pin_expert_switch_sequence(o):
+    """The boundary step t = t_moe runs the low-noise expert; 4 steps from t = 1 with t_moe = 1/2 visit
+    t = 1, 3/4, 1/2, 1/4 -> high, high, low, low."""
+    assert o.expert_for_step(0.5, 0.5) == 1 and o.expert_for_step(0.5 + 1e-9, 0.5) == 0
+    assert o.expert_for_step(1.0, 1.0) == 1 and o.expert_for_step(0.0, 0.0) == 1
+    c, mw, bws, x_t, z, txt, img, kw = _tiny_sampling()
+    _, _, used = o.sample_two_expert(x_t, z, 4, c.guidance, [(mw, bws), (mw, bws)], 0.5, txt, img, c.heads, **kw)
+    assert used == [0, 0, 1, 1]
+
+
+def pin_sample_two_expert_reductions(o):
+    """The same expert twice is ``sample``; t_moe >= t0 runs only the low-noise expert; a run that
+    switches after k steps equals the high expert's first k steps of ``sample`` followed by ``sample``
+    with the low expert from t_k for the remaining steps (same step size)."""
+    import wan_inputs as wi
+    c, mw, bws, x_t, z, txt, img, kw = _tiny_sampling()
+    mw2 = wi.make_model_weights(c, seed=77)
+    bws2 = [wi.make_block_weights(c, i, seed=77) for i in range(2)]
+    hi, lo = (mw, bws), (mw2, bws2)
+    steps = 4
+    ref_hi, traj_hi = o.sample(x_t, z, steps, c.guidance, mw, bws, txt, img, c.heads, **kw)
+    got, _, _ = o.sample_two_expert(x_t, z, steps, c.guidance, [hi, hi], 0.5, txt, img, c.heads, **kw)
+    assert np.array_equal(got, ref_hi)
+    ref_lo, _ = o.sample(x_t, z, steps, c.guidance, mw2, bws2, txt, img, c.heads, **kw)
+    got, _, used = o.sample_two_expert(x_t, z, steps, c.guidance, [hi, lo], 1.0, txt, img, c.heads, **kw)
+    assert used == [1] * steps and np.array_equal(got, ref_lo)
+    got, _, used = o.sample_two_expert(x_t, z, steps, c.guidance, [hi, lo], 0.5, txt, img, c.heads, **kw)
+    assert used == [0, 0, 1, 1]
+    ref, _ = o.sample(traj_hi[1], z, 2, c.guidance, mw2, bws2, txt, img, c.heads, t0=0.5, **kw)
+    assert np.allclose(got, ref, rtol=0, atol=1e-12)
+    assert not np.allclose(got, ref_hi, rtol=0, atol=1e-3)  # the second expert matters
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -166,6 +166,24 @@ def _block_ungated_factory():
     return block
 
 
+def _expert_boundary_high(t, t_moe):
+    return 0 if t >= t_moe else 1  # the boundary step given to the high-noise expert
+
+
+def _expert_swapped(t, t_moe):
+    return 1 if t > t_moe else 0
+
+
+def _t_moe_full_snr(snr_min):
+    return 1.0 / (1.0 + math.sqrt(snr_min))  # SNR(t) = snr_min instead of snr_min / 2
+
+
+def _snr_not_squared(t):
+    t = np.asarray(t, float)
+    with np.errstate(divide="ignore"):
+        return (1.0 - t) / t
+
+
 MUTANTS = {
     "mask_raw_reshape": ("i2v_mask", lambda: _mask_raw_reshape),
     "patch_vector_kw_kh": ("patchify", lambda: _patchify_kw_kh),
@@ -188,6 +206,10 @@ MUTANTS = {
     "time_projection_no_silu": ("time_embed", lambda: _time_embed_no_silu),
     "cross_joint_softmax": ("block_fwd", _mha_joint_softmax_factory),
     "self_attention_ungated": ("block_fwd", _block_ungated_factory),
+    "expert_boundary_to_high": ("expert_for_step", lambda: _expert_boundary_high),
+    "experts_swapped": ("expert_for_step", lambda: _expert_swapped),
+    "t_moe_full_snr": ("t_moe_from_snr", lambda: _t_moe_full_snr),
+    "snr_not_squared": ("snr", lambda: _snr_not_squared),
 }
 
 
