@@ -134,6 +134,44 @@ def cpu_baseline(c, layers, seed=0):
     }
 
 
+def measure_two_expert(c, model, blocks, caches, layers, x_t, zg, txt, img, steps, warmup):
+    """Wan2.2's two-expert sampling on this workload: a second, independently drawn DiT of the same
+    shape is made resident beside the first, and sampling switches from the first (high-noise) to the
+    second (low-noise) at t_moe = 1/2.  Times whole sampling runs of 2 * steps Euler steps from t = 1,
+    half on each expert."""
+    import torch
+
+    from video_diffusion_transformer_step_amd import runtime as R
+    import wan_inputs as wi
+
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4321)
+    model2 = R.DeviceModel(wi.make_model_weights(c, seed=1), c.dtype)
+    blocks2 = [R.DeviceBlock(None, c.dtype, tensors=device_block_tensors(c, gen)) for _ in range(layers)]
+    t_emb, i_emb = R.embed_contexts(c, model2, txt, img, c.B)
+    caches2 = R.cross_kv_all(c, blocks2, t_emb, i_emb, c.B)
+    experts = [(model, blocks, caches), (model2, blocks2, caches2)]
+    buf = R.alloc_step(c, c.B)
+    n = 2 * steps
+    x = torch.from_numpy(x_t).cuda()
+    for _ in range(max(warmup, 1)):
+        R.sample_two_expert(c, experts, x, zg, 2, c.guidance, buf, c.B, 0.5)
+    torch.cuda.synchronize()
+    x = torch.from_numpy(x_t).cuda()
+    t0 = time.perf_counter()
+    used = R.sample_two_expert(c, experts, x, zg, n, c.guidance, buf, c.B, 0.5)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / n
+    gb = sum(p.numel() * p.element_size() for bl in (blocks, blocks2) for b in bl for p in b._keep.t.values()
+             if p is not None) / 1e9
+    del experts, blocks2, caches2, model2, buf, x
+    torch.cuda.empty_cache()
+    return {"t_moe": 0.5, "steps": n, "experts_used": used, "ms_per_step": round(ms, 3),
+            "block_weights_resident_gb": round(gb, 2),
+            "note": ("two independently drawn DiTs of the workload's shape, both resident in HBM; the switch "
+                     "at t_moe changes which weights the next step reads (no reload)")}
+
+
 # Diffusion-cache schedule used for the reported average (a reading: the pages name the two caches and
 # their combined gain but give no schedule).  50 Euler steps with CFG; the self-attention output is
 # reused on every other step from step 10 to 39, and the unconditional velocity from step 35 on.
@@ -215,6 +253,8 @@ def main():
                     help="skip the second measurement with the quantised (INT8 Q.K / FP8 P.V) self-attention")
     ap.add_argument("--no-cache", action="store_true",
                     help="skip the diffusion-cache measurement (attention-output and CFG reuse)")
+    ap.add_argument("--no-two-expert", action="store_true",
+                    help="skip the two-expert (high-noise / low-noise DiT) sampling measurement")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many bytes (a known-size "
                          "reference for HBM byte counters)")
@@ -377,6 +417,13 @@ def main():
         cache = measure_diffusion_cache(c, model, blocks, layers, x_t, zg, img, args.steps, args.warmup)
         log(f"diffusion cache: {json.dumps(cache)}")
 
+    two_expert = None
+    if not args.no_two_expert:
+        two_expert = measure_two_expert(c, model, blocks, caches, layers, x_t, zg, txt, img, args.steps,
+                                        args.warmup)
+        two_expert["ms_per_step_vs_one_expert"] = round(two_expert["ms_per_step"] / ms_per_step, 3)
+        log(f"two experts: {json.dumps(two_expert)}")
+
     cpu = None
     if not args.no_cpu_baseline:
         t = time.perf_counter()
@@ -415,6 +462,7 @@ def main():
         "fp8_attention_step": fp8.get("fp8_attention_step"),
         "fp8_step": fp8.get("fp8_step"),
         "diffusion_cache": cache,
+        "two_expert": two_expert,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -251,3 +251,27 @@ def sample_cached(c, model, blocks, caches, x_latent, z_img, steps, guidance, bu
             v_u.copy_(v[1:2])
         L.fm_euler_step(x_latent, v[0:1], v_u, guidance, dt)
     return x_latent
+
+
+def expert_for_step(t, t_moe):
+    """Wan2.2's timestep-level expert choice ("Wan 技术深度解析" §7.2): 0 = the high-noise expert while
+    t > t_moe, 1 = the low-noise expert from t <= t_moe on."""
+    return 0 if t > t_moe else 1
+
+
+def sample_two_expert(c, experts, x_latent, z_img, steps, guidance, buf: StepBuffers, B, t_moe, t0=1.0,
+                      known_pixel_frames=None, fp8_attn=False, fp8_gemm=False):
+    """Euler sampling over two whole DiTs that split the schedule at t_moe: experts = ((model, blocks,
+    caches) of the high-noise expert, (model, blocks, caches) of the low-noise one), both resident.
+    Returns the expert index of each step; the latent is updated in place."""
+    dt = -t0 / steps
+    used = []
+    for k in range(steps):
+        t = t0 + k * dt
+        e = expert_for_step(t, t_moe)
+        model, blocks, caches = experts[e]
+        denoise_step(c, model, blocks, caches, x_latent, z_img, t, dt, guidance, buf, B, known_pixel_frames,
+                     fp8_attn, fp8_gemm)
+        used.append(e)
+    return used
+
