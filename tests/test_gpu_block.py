@@ -116,6 +116,36 @@ def test_block_deterministic_and_adaln_zero():
     assert np.array_equal(got.astype(np.float32), x)
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,over", [("tiny", {"dtype": "bf16", "T": 2, "H": 4, "W": 12, "dim": 256, "heads": 2,
+                                                  "head_dim": 128, "ffn_dim": 640}),
+                                        ("t2v-1.3b", {})], ids=["24tok", "32760tok"])
+def test_block_independent_of_workspace_contents(name, over):
+    """S mod 16 = 8 (24 and 32760 tokens): in bf16 V^T some padded keys of the last 16-key group sit
+    below position S.  The block must not read them as anything but zero: a workspace pre-filled with
+    NaN bytes gives the same bits as one pre-filled with zeros."""
+    require_gpu()
+    c = wi.get_config(name).replace(**over)
+    assert c.S % 16 == 8
+    case(f"block workspace contents {c.name} S={c.S}")
+    x, e0, t_emb, i_emb, bw = _inputs(c, seed=2)
+    blk = R.DeviceBlock(bw, c.dtype)
+    (kc,) = R.cross_kv_all(c, [blk], dev(t_emb, torch.bfloat16), None if i_emb is None else dev(i_emb, torch.bfloat16),
+                           c.B)
+    cfg = R.cfg_of(c)
+    outs = []
+    for fill in (0x00, 0xFF):
+        ws = torch.full((L.block_ws_bytes(cfg, c.grid, c.B),), fill, dtype=torch.uint8, device="cuda")
+        xd = dev(x)
+        L.dit_block_fwd(cfg, blk.bw, c.grid, c.B, xd, dev(e0), kc.kv, ws)
+        outs.append(host(xd))
+    assert np.isfinite(outs[1]).all()
+    assert np.array_equal(outs[0], outs[1])
+    if c.S < 1000:
+        ref = _oracle_block(c, x, e0, t_emb, i_emb, bw)
+        _check(c, outs[1], ref, x)
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["t2v-1.3b", "ti2v-5b", pytest.param("i2v-14b", marks=pytest.mark.slow)])
 def test_block_full_size_sampled_rows(name):

@@ -243,8 +243,12 @@ hipError_t launch_mod_combine(const float* e0, const float* mb, int B, int dim, 
 
 template <typename T>
 hipError_t launch_vt_tail_zero(T* vt, int64_t rows, int S, int Spad, hipStream_t s) {
-  if (Spad <= S || rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(vt_tail_zero_kernel<T>, dim3(grid_for(rows * (Spad - S))), dim3(256), 0, s, vt, rows, S, Spad);
+  // bf16 V^T permutes keys within 16-key groups, so a padded key of the last group can sit at a
+  // position below S: clear from the start of that group (the real keys are written afterwards).
+  const int S16 = S & ~15;
+  if (Spad <= S16 || rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(vt_tail_zero_kernel<T>, dim3(grid_for(rows * (Spad - S16))), dim3(256), 0, s, vt, rows, S16,
+                     Spad);
   return hipGetLastError();
 }
 

@@ -36,7 +36,9 @@ hipError_t launch_gated_add(float* x, const float* y, const float* mod, int chun
 // (e0 [B, 6, dim] from the shared timestep MLP, mb [6, dim] the block's own bias).
 hipError_t launch_mod_combine(const float* e0, const float* mb, int B, int dim, float* mod, hipStream_t s);
 
-// Zero V^T[r, S .. Spad) for rows r < rows (row stride Spad): the padded keys of the last tile.
+// Zero V^T[r, S16 .. Spad) for rows r < rows (row stride Spad), S16 = S rounded down to 16: every position
+// that can hold a padded key of the last tile (bf16 V^T permutes keys within 16-key groups).  Runs before
+// the keys < S are written.
 template <typename T>
 hipError_t launch_vt_tail_zero(T* vt, int64_t rows, int S, int Spad, hipStream_t s);
 
@@ -67,7 +69,8 @@ hipError_t gemm_store(const T* A, int64_t lda, const T* W, int64_t ldw, int M, i
                       int act, OutT* out, int64_t ldo, hipStream_t s);
 // Q/K/V projection (N = 3 dim): q, k columns to qk[m, 0 .. 2 dim) (row stride ldo), v columns to
 // V^T [B, H, hd, Spad] (keys permuted within 16-key groups for bf16; see launch_transpose_heads);
-// m = b * S + pos.  The V^T tail pos in [S, Spad) is not written.
+// m = b * S + pos.  Only keys pos < S are written: the positions of keys S .. Spad - 1 are left as they
+// were (launch_vt_tail_zero clears them first).
 template <typename T>
 hipError_t gemm_qkv(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int dim, int K, const float* bias,
                     T* qk, int64_t ldo, T* vt, int S, int H, int hd, int Spad, hipStream_t s);
