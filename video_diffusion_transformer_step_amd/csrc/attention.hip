@@ -27,6 +27,10 @@
 //  * the running maximum only moves when a score exceeds it by more than 2^8 (exp2
 //    units), so the O rescale is rare and p <= 256 stays safe in bf16;
 //    log2(e)/sqrt(hd) is folded into one fma feeding the raw v_exp_f32;
+//  * the ping-pong kernel does not even take a tile's row maxima unless the tile's
+//    weights, computed against the running maximum as it stands, sum past 2^13 in
+//    some lane (or are not finite, as on the first tile); only then does the
+//    maximum move (by the rule above) and the tile get recomputed, so p <= 2^13;
 //  * workgroups are ordered XCD-aware: each XCD's L2 serves a contiguous run of
 //    query tiles of the same heads.
 #include "wan_internal.h"
@@ -264,6 +268,105 @@ __device__ __forceinline__ void softmax_and_next_scores(const u32x4 (&qf)[AttnCf
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) mfma_chunk(kf[c & 1][kb], qf[c], sn[kb], T());
     __builtin_amdgcn_sched_barrier(0);
+  }
+  st.l += lsum;
+}
+
+// Masks the keys >= L of a stream's last tile (j0 + KT > L) to -inf.
+__device__ __forceinline__ void mask_tail(f32x16 (&s)[2], int j0, int L) {
+  const int lhalf = (threadIdx.x & 63) >> 5;
+  if (j0 + KT > L) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + kb * 32 + (r >> 2) * 8 + lhalf * 4 + (r & 3);
+        if (key >= L) s[kb][r] = -__builtin_inff();
+      }
+  }
+}
+
+// Largest per-lane sum of a tile's 32 weights accepted without looking at the row maximum: when the
+// running maximum is current (every weight <= 2^RESCALE_THRESHOLD) the sum is at most 32 * 2^8.
+constexpr float LAZY_SUM_LIMIT = 8192.f;
+
+// The ping-pong kernel's softmax half of a tile (bf16): the weights p = 2^(s c - m) of S(t) against
+// the running maximum m as it stands, packed into the PV operands pf and summed, interleaved with
+// S(t+1) = K(t+1) Q^T from kslot into sn.  s keeps the raw scores.  Only if some lane's sum exceeds LAZY_SUM_LIMIT (or is not
+// finite: the first tile, where m = -inf) does the wave take the row maxima: m then moves, as in
+// softmax_prep, wherever the tile's maximum exceeds it by more than RESCALE_THRESHOLD, O and l are
+// rescaled, and the weights are recomputed.  So every weight stays <= LAZY_SUM_LIMIT.
+template <typename T, int HD>
+__device__ __forceinline__ void softmax_lazy_and_next_scores(const u32x4 (&qf)[AttnCfg<T, HD>::NCH],
+                                                             const FragAddr<T, HD>& fa, const char* kslot,
+                                                             const f32x16 (&s)[2], f32x16 (&sn)[2], float c_log2,
+                                                             f32x16 (&o)[AttnCfg<T, HD>::ND], SoftState& st,
+                                                             u32x4 (&pf)[4]) {
+  using C = AttnCfg<T, HD>;
+  static_assert(sizeof(T) == 2, "bf16 weights");
+  constexpr int EPC = 32 / C::NCH;  // exponentials per S chunk
+  static_assert(EPC <= 8 && 8 % EPC == 0, "a P chunk spans whole S chunks");
+  float negm = -st.m;
+  float lsum = 0.f;
+  sn[0] = zero16();
+  sn[1] = zero16();
+  u32x4 kf[2][2];
+  bf16x8 pk;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+    kf[0][kb] = *reinterpret_cast<const u32x4*>(kslot + fa.k[0] + kb * FragAddr<T, HD>::KB32);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int c = 0; c < C::NCH; ++c) {
+    if (c + 1 < C::NCH) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        kf[(c + 1) & 1][kb] = *reinterpret_cast<const u32x4*>(kslot + fa.k[c + 1] + kb * FragAddr<T, HD>::KB32);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the reads go out before this region's work
+#pragma unroll
+    for (int e = c * EPC; e < (c + 1) * EPC; ++e) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[e >> 4][e & 15], c_log2, negm));
+      pk[e & 7] = (bf16)p;
+      lsum += p;
+    }
+    if (((c + 1) * EPC) % 8 == 0) {  // a 16-key P chunk is complete
+      const int pc = (c + 1) * EPC / 8 - 1;
+      pf[pc] = __builtin_bit_cast(u32x4, pk);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) mfma_chunk(kf[c & 1][kb], qf[c], sn[kb], T());
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (__ballot(!(lsum <= LAZY_SUM_LIMIT)) != 0ull) {
+    float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = mx * c_log2;
+    if (mnew > st.m + RESCALE_THRESHOLD) {
+      const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);  // 0 on the first tile (m = -inf)
+      st.m = mnew;
+      st.l *= alpha;
+#pragma unroll
+      for (int d = 0; d < C::ND; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+    }
+    negm = -st.m;
+    lsum = 0.f;
+#pragma unroll
+    for (int pc = 0; pc < 4; ++pc) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[pc >> 1][(pc & 1) * 8 + i], c_log2, negm));
+        pk[i] = (bf16)p;
+        lsum += p;
+      }
+      pf[pc] = __builtin_bit_cast(u32x4, pk);
+    }
   }
   st.l += lsum;
 }
@@ -537,9 +640,9 @@ __device__ __forceinline__ void pp_tile(const u32x4 (&qf)[AttnCfg<T, HD>::NCH], 
   } else {
     if (t >= 1 && t + 1 < nt) { load_v_tile<T, HD, 8>(cp, vtb, j0 + KT, v_next); last = 1; }
   }
-  softmax_prep<T, HD>(s, j0, kv.L, c_log2, o, st);
+  mask_tail(s, j0, kv.L);
   u32x4 pf[4];
-  softmax_and_next_scores<T, HD>(qf, fa, k_next, s, sn, c_log2, st, pf);
+  softmax_lazy_and_next_scores<T, HD>(qf, fa, k_next, s, sn, c_log2, o, st, pf);
   // ---- B(t)
   phase_barrier<CP::KL>(last);
   last = 0;
