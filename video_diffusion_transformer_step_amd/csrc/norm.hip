@@ -161,30 +161,47 @@ template <> __device__ __forceinline__ void store8<float>(float* p, const float 
 }
 
 constexpr int QK_MAX8 = 12;  // 8-element chunks per lane: dim <= 12 * 512 = 6144
-constexpr int QK_ROWS = 2;   // token rows per wave
+constexpr int QK_ROWS = 4;   // token rows per wave
 
 // 3D RoPE ("图解 Wan2.1 I2V" §5.3 ②): head channels split into time / height / width segments of
 // sizes hd - 4*(hd/6), 2*(hd/6), 2*(hd/6); pair (2m, 2m+1) of a segment of width n rotates by
 // pos * theta^(-2m/n), pos being the token's frame / row / column index.  A lane's 8-channel
-// chunks all sit at the same offset within their heads (hd divides 512), so its 4 pairs' angles
-// serve every chunk of the row and both q and k.
-__device__ __forceinline__ void rope_angles(int d0, int hd, float log2_theta, int f, int i, int j, float (&cs)[4],
-                                            float (&sn)[4]) {
+// chunks all sit at the same offset within their heads (hd divides 512), so its 4 pairs' frequencies
+// (fixed per lane) and angles (per token) serve every chunk of the row and both q and k.
+struct RopeLane {
+  float freq[4];
+  int axis[4];  // 0 frame, 1 row, 2 column
+};
+
+__device__ __forceinline__ RopeLane rope_lane(int d0, int hd, float log2_theta) {
   const int q6 = hd / 6;
   const int dT = hd - 4 * q6, dH = 2 * q6;
+  RopeLane r;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int d = d0 + 2 * p;
-    int m, n, pos;
+    int m, n;
     if (d < dT) {
-      m = d >> 1; n = dT; pos = f;
+      m = d >> 1; n = dT; r.axis[p] = 0;
     } else if (d < dT + dH) {
-      m = (d - dT) >> 1; n = dH; pos = i;
+      m = (d - dT) >> 1; n = dH; r.axis[p] = 1;
     } else {
-      m = (d - dT - dH) >> 1; n = dH; pos = j;
+      m = (d - dT - dH) >> 1; n = dH; r.axis[p] = 2;
     }
-    const float freq = exp2f(-(float)(2 * m) / (float)n * log2_theta);
-    sincosf((float)pos * freq, &sn[p], &cs[p]);
+    r.freq[p] = exp2f(-(float)(2 * m) / (float)n * log2_theta);
+  }
+  return r;
+}
+
+// The lane's pair angles at token position (f, i, j), by the hardware sine / cosine (angles here are
+// at most a few hundred radians, where their error stays near 1e-6).
+__device__ __forceinline__ void rope_angles(const RopeLane& r, int f, int i, int j, float (&cs)[4], float (&sn)[4]) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int pos = r.axis[p] == 0 ? f : (r.axis[p] == 1 ? i : j);
+    const float a = (float)pos * r.freq[p];
+    sn[p] = __sinf(a);
+    cs[p] = __cosf(a);
   }
 }
 
@@ -256,20 +273,27 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(const T* q_in, const 
 #pragma unroll
   for (int c = 0; c < NC8; ++c) {
     const int c0 = c * 512 + lane * 8;
+    if (c0 < dim && gq) {
+      load8<float>(gq + c0, gql[c]);
+    } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      gql[c][e] = (c0 < dim && gq) ? gq[c0 + e] : 1.f;
-      gkl[c][e] = (c0 < dim && gk) ? gk[c0 + e] : 1.f;
+      for (int e = 0; e < 8; ++e) gql[c][e] = 1.f;
+    }
+    if (c0 < dim && gk) {
+      load8<float>(gk + c0, gkl[c]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gkl[c][e] = 1.f;
     }
   }
-  const int d0 = (lane * 8) % hd;
+  const RopeLane rl = rope_lane((lane * 8) % hd, hd, log2_theta);
   for (int rr = 0; rr < QK_ROWS; ++rr) {
     const int64_t row = row0 + rr;
     if (row >= rows) return;
     const int s = (int)(row % S);
     const int jj = s % Wp, ii = (s / Wp) % Hp, ff = s / (Wp * Hp);
     float cs[4], sn[4];
-    rope_angles(d0, hd, log2_theta, ff, ii, jj, cs, sn);
+    rope_angles(rl, ff, ii, jj, cs, sn);
     norm_rope_qk<T, NC8>(q_in + row * ld_in, k_in + row * ld_in, q_out + row * ld_out, k_out + row * ld_out, dim,
                          gql, gkl, do_norm, eps, cs, sn, lane);
   }
