@@ -118,21 +118,25 @@ def test_block_deterministic_and_adaln_zero():
 
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("name,over", [("tiny", {"dtype": "bf16", "T": 2, "H": 4, "W": 12, "dim": 256, "heads": 2,
-                                                  "head_dim": 128, "ffn_dim": 640}),
+                                                  "head_dim": 128, "ffn_dim": 768}),
                                         ("t2v-1.3b", {})], ids=["24tok", "32760tok"])
-def test_block_independent_of_workspace_contents(name, over):
+@pytest.mark.parametrize("fp8", ["bf16", "fp8_attn", "fp8_all"])
+def test_block_independent_of_workspace_contents(name, over, fp8):
     """S mod 16 = 8 (24 and 32760 tokens): in bf16 V^T some padded keys of the last 16-key group sit
-    below position S.  The block must not read them as anything but zero: a workspace pre-filled with
-    NaN bytes gives the same bits as one pre-filled with zeros."""
+    below position S.  The block must not read them, or any other workspace byte it has not written,
+    as anything but zero: a workspace pre-filled with NaN bytes gives the same bits as one pre-filled
+    with zeros, on the bf16 path and on both quantised paths."""
     require_gpu()
     c = wi.get_config(name).replace(**over)
     assert c.S % 16 == 8
-    case(f"block workspace contents {c.name} S={c.S}")
+    case(f"block workspace contents {c.name} S={c.S} {fp8}")
     x, e0, t_emb, i_emb, bw = _inputs(c, seed=2)
     blk = R.DeviceBlock(bw, c.dtype)
+    if fp8 == "fp8_all":
+        blk.enable_e4m3()
     (kc,) = R.cross_kv_all(c, [blk], dev(t_emb, torch.bfloat16), None if i_emb is None else dev(i_emb, torch.bfloat16),
                            c.B)
-    cfg = R.cfg_of(c)
+    cfg = R.cfg_of(c, fp8_attn=fp8 != "bf16", fp8_gemm=fp8 == "fp8_all")
     outs = []
     for fill in (0x00, 0xFF):
         ws = torch.full((L.block_ws_bytes(cfg, c.grid, c.B),), fill, dtype=torch.uint8, device="cuda")
@@ -143,7 +147,7 @@ def test_block_independent_of_workspace_contents(name, over):
     assert np.array_equal(outs[0], outs[1])
     if c.S < 1000:
         ref = _oracle_block(c, x, e0, t_emb, i_emb, bw)
-        _check(c, outs[1], ref, x)
+        _check(c, outs[1], ref, x, tol=None if fp8 == "bf16" else (FP8_TOL if fp8 == "fp8_attn" else FP8_ALL_TOL))
 
 
 @pytest.mark.timeout(900)
