@@ -371,6 +371,122 @@ __device__ __forceinline__ void softmax_lazy_and_next_scores(const u32x4 (&qf)[A
   st.l += lsum;
 }
 
+// The ping-pong kernel's vector half of a tile (bf16, no LDS access): the weights p = 2^(s c - m) of
+// S(t) against the running maximum m as it stands, packed into the PV operands pf and summed.  Only if
+// some lane's sum exceeds LAZY_SUM_LIMIT (or is not finite: the first tile, where m = -inf) does the
+// wave take the row maxima: m then moves, as in softmax_prep, wherever the tile's maximum exceeds it
+// by more than RESCALE_THRESHOLD, O and l are rescaled and the weights recomputed.  So every weight
+// stays <= LAZY_SUM_LIMIT.
+template <typename T, int HD>
+__device__ __forceinline__ void softmax_lazy(const f32x16 (&s)[2], float c_log2, f32x16 (&o)[AttnCfg<T, HD>::ND],
+                                             SoftState& st, u32x4 (&pf)[4]) {
+  using C = AttnCfg<T, HD>;
+  static_assert(sizeof(T) == 2, "bf16 weights");
+  float negm = -st.m;
+  float lsum = 0.f;
+#pragma unroll
+  for (int pc = 0; pc < 4; ++pc) {
+    bf16x8 pk;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // raw v_exp_f32: accepted arguments are <= 13; larger or non-finite ones are redone below
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[pc >> 1][(pc & 1) * 8 + i], c_log2, negm));
+      pk[i] = (bf16)p;
+      lsum += p;
+    }
+    pf[pc] = __builtin_bit_cast(u32x4, pk);
+  }
+  if (__ballot(!(lsum <= LAZY_SUM_LIMIT)) != 0ull) {
+    float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = mx * c_log2;
+    if (mnew > st.m + RESCALE_THRESHOLD) {
+      const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);  // 0 on the first tile (m = -inf)
+      st.m = mnew;
+      st.l *= alpha;
+#pragma unroll
+      for (int d = 0; d < C::ND; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+    }
+    negm = -st.m;
+    lsum = 0.f;
+#pragma unroll
+    for (int pc = 0; pc < 4; ++pc) {
+      bf16x8 pk;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[pc >> 1][(pc & 1) * 8 + i], c_log2, negm));
+        pk[i] = (bf16)p;
+        lsum += p;
+      }
+      pf[pc] = __builtin_bit_cast(u32x4, pk);
+    }
+  }
+  st.l += lsum;
+}
+
+// The ping-pong kernel's matrix half of a tile (bf16): O^T += V^T(t) P^T(t) from vslot, then (if
+// NEXT) S(t+1) = K(t+1) Q^T from kslot into sn.  Units of two MFMAs, each unit's LDS fragments read
+// one unit ahead: the PV units (16-key chunk, pair of d blocks) first, then the S units (hd chunk,
+// both 32-key blocks).
+template <typename T, int HD>
+__device__ __forceinline__ void read_pv_or_s_unit(const FragAddr<T, HD>& fa, const char* vslot, const char* kslot,
+                                                  int u, u32x4& f0, u32x4& f1) {
+  using C = AttnCfg<T, HD>;
+  using F = FragAddr<T, HD>;
+  constexpr int DP = C::ND / 2, NPV = 4 * DP;
+  if (u < NPV) {
+    const int c = u / DP, d0 = (u % DP) * 2;
+    f0 = *reinterpret_cast<const u32x4*>(vslot + fa.v[c] + d0 * F::VD32);
+    f1 = *reinterpret_cast<const u32x4*>(vslot + fa.v[c] + (d0 + 1) * F::VD32);
+  } else {
+    const int c = u - NPV;
+    f0 = *reinterpret_cast<const u32x4*>(kslot + fa.k[c]);
+    f1 = *reinterpret_cast<const u32x4*>(kslot + fa.k[c] + F::KB32);
+  }
+}
+
+template <typename T, int HD, bool NEXT>
+__device__ __forceinline__ void pv_and_next_scores(const FragAddr<T, HD>& fa, const char* vslot, const u32x4 (&pf)[4],
+                                                   f32x16 (&o)[AttnCfg<T, HD>::ND],
+                                                   const u32x4 (&qf)[AttnCfg<T, HD>::NCH], const char* kslot,
+                                                   f32x16 (&sn)[2]) {
+  using C = AttnCfg<T, HD>;
+  constexpr int DP = C::ND / 2, NPV = 4 * DP, NU = NEXT ? NPV + C::NCH : NPV;
+  u32x4 a0, a1, b0, b1;  // fragments of the even / odd units
+  read_pv_or_s_unit<T, HD>(fa, vslot, kslot, 0, a0, a1);
+  if (NEXT) {
+    sn[0] = zero16();
+    sn[1] = zero16();
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    if (u + 1 < NU) {
+      if (u & 1) read_pv_or_s_unit<T, HD>(fa, vslot, kslot, u + 1, a0, a1);
+      else read_pv_or_s_unit<T, HD>(fa, vslot, kslot, u + 1, b0, b1);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the reads go out before this unit's MFMAs
+    const u32x4& f0 = (u & 1) ? b0 : a0;
+    const u32x4& f1 = (u & 1) ? b1 : a1;
+    if (u < NPV) {
+      const int c = u / DP, d0 = (u % DP) * 2;
+      mfma_chunk(f0, pf[c], o[d0], T());
+      mfma_chunk(f1, pf[c], o[d0 + 1], T());
+    } else {
+      const int c = u - NPV;
+      mfma_chunk(f0, qf[c], sn[0], T());
+      mfma_chunk(f1, qf[c], sn[1], T());
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // bf16 O^T += V^T P^T for one tile (V^T tile in vslot): units of two MFMAs, each reading its V^T
 // fragments one unit ahead.
 template <typename T, int HD>
@@ -626,32 +742,31 @@ __device__ __forceinline__ void pp_tile(const u32x4 (&qf)[AttnCfg<T, HD>::NCH], 
                                         f32x16 (&sn)[2], f32x16 (&o)[AttnCfg<T, HD>::ND], SoftState& st,
                                         int& last) {
   using CP = CopyPlan<T, HD, 8>;
-  static_assert(CP::KL == CP::VL, "equal K and V^T copy counts");
+  constexpr int PER = CP::KL + CP::VL;  // copies per wave in a copying phase
   char* k_this = P ? sl.k1 : sl.k0;  // K(t) -> K(t+2)
-  char* k_next = P ? sl.k0 : sl.k1;  // K(t+1) -> K(t+3)
+  char* k_next = P ? sl.k0 : sl.k1;  // K(t+1)
   char* v_this = P ? sl.v1 : sl.v0;  // V^T(t)
   char* v_next = P ? sl.v0 : sl.v1;  // V^T(t-1) -> V^T(t+1)
   const int j0 = t * KT;
-  // ---- A(t)
-  phase_barrier<CP::KL>(last);
+  // the copies of global phase 2t + 1 (group 1's A(t), group 0's B(t)): K(t+2) and V^T(t+1)
+  auto copies = [&]() {
+    if (t + 2 < nt) load_k_tile<T, HD, 8>(cp, kbase, kv.k_ss, kv.L, j0 + 2 * KT, k_this);
+    if (t >= 1 && t + 1 < nt) load_v_tile<T, HD, 8>(cp, vtb, j0 + KT, v_next);
+    last = (t + 2 < nt || (t >= 1 && t + 1 < nt)) ? 1 : 0;
+  };
+  // ---- A(t): the weights of S(t) (vector units only)
+  phase_barrier<PER>(last);
   last = 0;
-  if (grp == 0) {
-    if (t + 2 < nt) { load_k_tile<T, HD, 8>(cp, kbase, kv.k_ss, kv.L, j0 + 2 * KT, k_this); last = 1; }
-  } else {
-    if (t >= 1 && t + 1 < nt) { load_v_tile<T, HD, 8>(cp, vtb, j0 + KT, v_next); last = 1; }
-  }
+  if (grp == 1) copies();
   mask_tail(s, j0, kv.L);
   u32x4 pf[4];
-  softmax_lazy_and_next_scores<T, HD>(qf, fa, k_next, s, sn, c_log2, o, st, pf);
-  // ---- B(t)
-  phase_barrier<CP::KL>(last);
+  softmax_lazy<T, HD>(s, c_log2, o, st, pf);
+  // ---- B(t): O^T += V^T(t) P^T(t), S(t+1) = K(t+1) Q^T (matrix units)
+  phase_barrier<PER>(last);
   last = 0;
-  if (grp == 0) {
-    if (t >= 1 && t + 1 < nt) { load_v_tile<T, HD, 8>(cp, vtb, j0 + KT, v_next); last = 1; }
-  } else {
-    if (t + 3 < nt) { load_k_tile<T, HD, 8>(cp, kbase, kv.k_ss, kv.L, j0 + 3 * KT, k_next); last = 1; }
-  }
-  pv_products<T, HD>(fa, v_this, pf, o);
+  if (grp == 0) copies();
+  // on a stream's last tile k_next holds a stale tile with no copy in flight: S(t+1) is computed and unused
+  pv_and_next_scores<T, HD, true>(fa, v_this, pf, o, qf, k_next, sn);
 }
 
 template <typename T, int HD>
@@ -676,15 +791,12 @@ __device__ __forceinline__ void attend_stream_pp(const u32x4 (&qf)[AttnCfg<T, HD
   f32x16 sa[2], sb[2];
   scores<T, HD>(qf, fa, sl.k0, sa);
   int last = 0;
-  if (grp == 1) {  // group 1 starts a phase late; after this barrier K(0) is read by all: copy K(2)
-    phase_barrier<CP::KL>(0);
-    if (2 < nt) { load_k_tile<T, HD, 8>(cp, kbase, kv.k_ss, kv.L, 2 * KT, sl.k0); last = 1; }
-  }
+  if (grp == 1) phase_barrier<CP::KL + CP::VL>(0);  // group 1 runs a phase late
   for (int t = 0; t < nt; t += 2) {
     pp_tile<T, HD, 0>(qf, fa, kv, cp, kbase, vtb, t, nt, grp, c_log2, sl, sa, sb, o, st, last);
     if (t + 1 < nt) pp_tile<T, HD, 1>(qf, fa, kv, cp, kbase, vtb, t + 1, nt, grp, c_log2, sl, sb, sa, o, st, last);
   }
-  if (grp == 0) phase_barrier<CP::KL>(0);  // group 0 passes the barrier ending group 1's last B
+  if (grp == 0) phase_barrier<CP::KL + CP::VL>(0);  // group 0 passes the barrier ending group 1's last B
 }
 
 template <typename T, int HD, int NS, int KIND>
