@@ -432,7 +432,7 @@ __device__ __forceinline__ void softmax_lazy(const f32x16 (&s)[2], float c_log2,
 
 // The ping-pong kernel's matrix half of a tile (bf16): O^T += V^T(t) P^T(t) from vslot, then (if
 // NEXT) S(t+1) = K(t+1) Q^T from kslot into sn.  Units of two MFMAs, each unit's LDS fragments read
-// one unit ahead: the PV units (16-key chunk, pair of d blocks) first, then the S units (hd chunk,
+// two units ahead: the PV units (16-key chunk, pair of d blocks) first, then the S units (hd chunk,
 // both 32-key blocks).
 template <typename T, int HD>
 __device__ __forceinline__ void read_pv_or_s_unit(const FragAddr<T, HD>& fa, const char* vslot, const char* kslot,
@@ -458,8 +458,9 @@ __device__ __forceinline__ void pv_and_next_scores(const FragAddr<T, HD>& fa, co
                                                    f32x16 (&sn)[2]) {
   using C = AttnCfg<T, HD>;
   constexpr int DP = C::ND / 2, NPV = 4 * DP, NU = NEXT ? NPV + C::NCH : NPV;
-  u32x4 a0, a1, b0, b1;  // fragments of the even / odd units
-  read_pv_or_s_unit<T, HD>(fa, vslot, kslot, 0, a0, a1);
+  u32x4 f[3][2];  // fragments of units u % 3, read two units ahead
+  read_pv_or_s_unit<T, HD>(fa, vslot, kslot, 0, f[0][0], f[0][1]);
+  read_pv_or_s_unit<T, HD>(fa, vslot, kslot, 1, f[1][0], f[1][1]);
   if (NEXT) {
     sn[0] = zero16();
     sn[1] = zero16();
@@ -467,13 +468,10 @@ __device__ __forceinline__ void pv_and_next_scores(const FragAddr<T, HD>& fa, co
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
-    if (u + 1 < NU) {
-      if (u & 1) read_pv_or_s_unit<T, HD>(fa, vslot, kslot, u + 1, a0, a1);
-      else read_pv_or_s_unit<T, HD>(fa, vslot, kslot, u + 1, b0, b1);
-    }
+    if (u + 2 < NU) read_pv_or_s_unit<T, HD>(fa, vslot, kslot, u + 2, f[(u + 2) % 3][0], f[(u + 2) % 3][1]);
     __builtin_amdgcn_sched_barrier(0);  // the reads go out before this unit's MFMAs
-    const u32x4& f0 = (u & 1) ? b0 : a0;
-    const u32x4& f1 = (u & 1) ? b1 : a1;
+    const u32x4& f0 = f[u % 3][0];
+    const u32x4& f1 = f[u % 3][1];
     if (u < NPV) {
       const int c = u / DP, d0 = (u % DP) * 2;
       mfma_chunk(f0, pf[c], o[d0], T());
