@@ -64,8 +64,8 @@ struct AttnCfg {
   __device__ static __forceinline__ int voff(int r, int c) { return (r * VCHUNKS + (c ^ ((r / VR) & VMASK))) * 16; }
 };
 
-// Per-thread pieces of the asynchronous tile copies (NW waves share each tile), fixed for the whole
-// key loop.  A copy's global address is a wave-uniform base (advanced per tile) plus this lane's
+// Per-thread pieces of the asynchronous tile copies (NW waves share each tile: waves w with the same
+// w % NW take the same share), fixed for the whole key loop.  A copy's global address is a wave-uniform base (advanced per tile) plus this lane's
 // 32-bit byte offset; the LDS destination of wave-instruction i is (i * NW + wave) KB into the slot.
 template <typename T, int HD, int NW>
 struct CopyPlan {
@@ -78,7 +78,7 @@ struct CopyPlan {
   int wave;           // wave index, uniform
   __device__ __forceinline__ CopyPlan(int64_t k_ss, int Lpad) {
     const int lane = threadIdx.x & 63;
-    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    wave = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) % NW);
 #pragma unroll
     for (int i = 0; i < KL; ++i) {
       const int p = (i * NW + wave) * 64 + lane;  // 16-byte position in the tile
@@ -700,18 +700,20 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const T* __restrict__
 
 // ---------------------------------------------------------------------------
 // Ping-pong kernel (bf16): one workgroup = 8 waves = 256 queries of one (b, head), two waves per
-// SIMD.  Each wave alternates A(t) = softmax of S(t) + the MFMAs of S(t+1) (vector-heavy) and
-// B(t) = O^T += V^T P^T (matrix only), with a workgroup barrier between the two.  Waves 4-7
-// (group 1) pass one extra barrier at the start and waves 0-3 (group 0) one at the end, so group 1
-// runs a half tile behind: between two barriers one wave of each SIMD is in A and the other in B,
-// and the SIMD's matrix and vector units work at the same time.
+// SIMD.  Each wave alternates A(t) = the weights of S(t) (vector units only, no LDS access) and
+// B(t) = O^T += V^T(t) P^T(t) followed by S(t+1) = K(t+1) Q^T (32 MFMAs), with a workgroup barrier
+// between the two (FlashAttention-3's ping-pong schedule).  Waves 4-7 (group 1) pass one extra
+// barrier at the start and waves 0-3 (group 0) one at the end, so group 1 runs a half tile behind:
+// between two barriers one wave of each SIMD is in A and the other in B, and the SIMD's matrix and
+// vector units work at the same time.
 //
-// Copies (all 8 waves take a share of each tile; tile t lives in slot t % 2).  With b_k the k-th
-// barrier of the workgroup: K(t) is last read by group 1's A(t-1), which ends at b_2t, so K(t+2) is
-// copied right after b_2t and is first read after b_2t+2; V^T(t-1) is last read by group 1's
-// B(t-1), which ends at b_2t+1, so V^T(t+1) is copied right after b_2t+1 and first read after
-// b_2t+3.  Every copy thus has two phases to land; a wave waits at a barrier only for the copies it
-// issued two phases before.
+// Copies (tile t lives in slot t % 2; global phase k runs between barriers b_k and b_k+1, group 0's
+// A(t) and B(t) are phases 2t and 2t+1, group 1's are 2t+1 and 2t+2).  K(t) is last read by group
+// 1's B(t-1) and V^T(t-1) by group 1's B(t-1), both in phase 2t; so K(t+2) and V^T(t+1) are copied
+// in phase 2t+1, by group 1's waves during their vector phase A(t) (copies issued by a wave in its
+// matrix phase slow its MFMA stream), and first read in phase 2t+3 (group 0's B(t+1)).  Every copy
+// thus has two phases to land; a wave waits at a barrier only for the copies it issued in its
+// previous phase to be allowed in flight.
 // ---------------------------------------------------------------------------
 
 template <int N>
@@ -734,22 +736,23 @@ __device__ __forceinline__ void phase_barrier(int last) {
 // S(t) on entry, sn receives S(t+1).  `last` counts the copies this wave issued in its previous phase.
 template <typename T, int HD, int P>
 __device__ __forceinline__ void pp_tile(const u32x4 (&qf)[AttnCfg<T, HD>::NCH], const FragAddr<T, HD>& fa,
-                                        const KVStream& kv, const CopyPlan<T, HD, 8>& cp,
+                                        const KVStream& kv, const CopyPlan<T, HD, 4>& cp,
                                         const T* __restrict__ kbase, const T* __restrict__ vtb, int t, int nt,
                                         int grp, float c_log2, const Slots<T, HD>& sl, f32x16 (&s)[2],
                                         f32x16 (&sn)[2], f32x16 (&o)[AttnCfg<T, HD>::ND], SoftState& st,
                                         int& last) {
-  using CP = CopyPlan<T, HD, 8>;
-  constexpr int PER = CP::KL + CP::VL;  // copies per wave in a copying phase
+  using CP = CopyPlan<T, HD, 4>;
+  constexpr int PER = CP::KL + CP::VL;  // copies per group-1 wave in its copying phase
   char* k_this = P ? sl.k1 : sl.k0;  // K(t) -> K(t+2)
   char* k_next = P ? sl.k0 : sl.k1;  // K(t+1)
   char* v_this = P ? sl.v1 : sl.v0;  // V^T(t)
   char* v_next = P ? sl.v0 : sl.v1;  // V^T(t-1) -> V^T(t+1)
   const int j0 = t * KT;
-  // the copies of global phase 2t + 1 (group 1's A(t), group 0's B(t)): K(t+2) and V^T(t+1)
+  // the copies of global phase 2t + 1, all by group 1 in its A(t) (so group 0's matrix phase B(t)
+  // issues none): K(t+2) and V^T(t+1)
   auto copies = [&]() {
-    if (t + 2 < nt) load_k_tile<T, HD, 8>(cp, kbase, kv.k_ss, kv.L, j0 + 2 * KT, k_this);
-    if (t >= 1 && t + 1 < nt) load_v_tile<T, HD, 8>(cp, vtb, j0 + KT, v_next);
+    if (t + 2 < nt) load_k_tile<T, HD, 4>(cp, kbase, kv.k_ss, kv.L, j0 + 2 * KT, k_this);
+    if (t >= 1 && t + 1 < nt) load_v_tile<T, HD, 4>(cp, vtb, j0 + KT, v_next);
     last = (t + 2 < nt || (t >= 1 && t + 1 < nt)) ? 1 : 0;
   };
   // ---- A(t): the weights of S(t) (vector units only)
@@ -762,7 +765,6 @@ __device__ __forceinline__ void pp_tile(const u32x4 (&qf)[AttnCfg<T, HD>::NCH], 
   // ---- B(t): O^T += V^T(t) P^T(t), S(t+1) = K(t+1) Q^T (matrix units)
   phase_barrier<PER>(last);
   last = 0;
-  if (grp == 0) copies();
   // on a stream's last tile k_next holds a stale tile with no copy in flight: S(t+1) is computed and unused
   pv_and_next_scores<T, HD, true>(fa, v_this, pf, o, qf, k_next, sn);
 }
@@ -786,15 +788,17 @@ __device__ __forceinline__ void attend_stream_pp(const u32x4 (&qf)[AttnCfg<T, HD
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
+  const CopyPlan<T, HD, 4> cp4(kv.k_ss, kv.Lpad);  // group 1's share of each tile in the key loop
   f32x16 sa[2], sb[2];
   scores<T, HD>(qf, fa, sl.k0, sa);
   int last = 0;
-  if (grp == 1) phase_barrier<CP::KL + CP::VL>(0);  // group 1 runs a phase late
+  using CP4 = CopyPlan<T, HD, 4>;
+  if (grp == 1) phase_barrier<CP4::KL + CP4::VL>(0);  // group 1 runs a phase late
   for (int t = 0; t < nt; t += 2) {
-    pp_tile<T, HD, 0>(qf, fa, kv, cp, kbase, vtb, t, nt, grp, c_log2, sl, sa, sb, o, st, last);
-    if (t + 1 < nt) pp_tile<T, HD, 1>(qf, fa, kv, cp, kbase, vtb, t + 1, nt, grp, c_log2, sl, sb, sa, o, st, last);
+    pp_tile<T, HD, 0>(qf, fa, kv, cp4, kbase, vtb, t, nt, grp, c_log2, sl, sa, sb, o, st, last);
+    if (t + 1 < nt) pp_tile<T, HD, 1>(qf, fa, kv, cp4, kbase, vtb, t + 1, nt, grp, c_log2, sl, sb, sa, o, st, last);
   }
-  if (grp == 0) phase_barrier<CP::KL + CP::VL>(0);  // group 0 passes the barrier ending group 1's last B
+  if (grp == 0) phase_barrier<CP4::KL + CP4::VL>(0);  // group 0 passes the barrier ending group 1's last B
 }
 
 template <typename T, int HD, int NS, int KIND>
