@@ -733,14 +733,14 @@ __device__ __forceinline__ void phase_barrier(int last) {
 }
 
 // Tile t (static slot parity P = t % 2) as seen by one wave: barrier, A(t), barrier, B(t).  s holds
-// S(t) on entry, sn receives S(t+1).  `last` counts the copies this wave issued in its previous phase.
+// S(t) on entry and S(t+1) on exit (S(t) is dead once A(t) has packed its weights).  `last` counts
+// the copies this wave issued in its previous phase.
 template <typename T, int HD, int P>
 __device__ __forceinline__ void pp_tile(const u32x4 (&qf)[AttnCfg<T, HD>::NCH], const FragAddr<T, HD>& fa,
                                         const KVStream& kv, const CopyPlan<T, HD, 4>& cp,
                                         const T* __restrict__ kbase, const T* __restrict__ vtb, int t, int nt,
                                         int grp, float c_log2, const Slots<T, HD>& sl, f32x16 (&s)[2],
-                                        f32x16 (&sn)[2], f32x16 (&o)[AttnCfg<T, HD>::ND], SoftState& st,
-                                        int& last) {
+                                        f32x16 (&o)[AttnCfg<T, HD>::ND], SoftState& st, int& last) {
   using CP = CopyPlan<T, HD, 4>;
   constexpr int PER = CP::KL + CP::VL;  // copies per group-1 wave in its copying phase
   char* k_this = P ? sl.k1 : sl.k0;  // K(t) -> K(t+2)
@@ -766,7 +766,7 @@ __device__ __forceinline__ void pp_tile(const u32x4 (&qf)[AttnCfg<T, HD>::NCH], 
   phase_barrier<PER>(last);
   last = 0;
   // on a stream's last tile k_next holds a stale tile with no copy in flight: S(t+1) is computed and unused
-  pv_and_next_scores<T, HD, true>(fa, v_this, pf, o, qf, k_next, sn);
+  pv_and_next_scores<T, HD, true>(fa, v_this, pf, o, qf, k_next, s);
 }
 
 template <typename T, int HD>
@@ -789,14 +789,14 @@ __device__ __forceinline__ void attend_stream_pp(const u32x4 (&qf)[AttnCfg<T, HD
   __syncthreads();
 
   const CopyPlan<T, HD, 4> cp4(kv.k_ss, kv.Lpad);  // group 1's share of each tile in the key loop
-  f32x16 sa[2], sb[2];
+  f32x16 sa[2];
   scores<T, HD>(qf, fa, sl.k0, sa);
   int last = 0;
   using CP4 = CopyPlan<T, HD, 4>;
   if (grp == 1) phase_barrier<CP4::KL + CP4::VL>(0);  // group 1 runs a phase late
   for (int t = 0; t < nt; t += 2) {
-    pp_tile<T, HD, 0>(qf, fa, kv, cp4, kbase, vtb, t, nt, grp, c_log2, sl, sa, sb, o, st, last);
-    if (t + 1 < nt) pp_tile<T, HD, 1>(qf, fa, kv, cp4, kbase, vtb, t + 1, nt, grp, c_log2, sl, sb, sa, o, st, last);
+    pp_tile<T, HD, 0>(qf, fa, kv, cp4, kbase, vtb, t, nt, grp, c_log2, sl, sa, o, st, last);
+    if (t + 1 < nt) pp_tile<T, HD, 1>(qf, fa, kv, cp4, kbase, vtb, t + 1, nt, grp, c_log2, sl, sa, o, st, last);
   }
   if (grp == 0) phase_barrier<CP4::KL + CP4::VL>(0);  // group 0 passes the barrier ending group 1's last B
 }
