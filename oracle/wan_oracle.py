@@ -368,7 +368,8 @@ def self_attention_rope_only(q, k, v, grid, rows=None, theta: float = 10000.0):
 def context_embed(ctx, w1, b1, w2, b2):
     """Two-layer GELU MLP to the model dim.  [I2V-illustrated §7 steps 1-2]: umT5 output
     [512, 4096] -> MLP -> [512, dim]; CLIP tokens [257, 1280] -> MLPProj -> [257, dim].
-    Reading (parity unpinned): Linear -> GELU -> Linear for both."""
+    Reading: Linear -> GELU -> Linear for both (the implementation is pinned against PyTorch
+    modules; the MLP shape is not on the pages)."""
     return linear(gelu(linear(ctx, w1, b1)), w2, b2)
 
 
@@ -460,8 +461,9 @@ def head_fwd(x, e, w: dict, ln_eps: float = 1e-6):
     """Head: (shift, scale) = head_mod + e; out = (LN(x)(1 + scale) + shift) Wh^T + bh.
 
     [I2V-illustrated §5.5]: a head 'also with AdaLN and unpatchify' maps
-    [B, S, dim] back to the latent.  Reading (parity unpinned beyond shape):
-    two modulation vectors (shift first) from a learned [2, dim] bias plus e.
+    [B, S, dim] back to the latent.  Reading (not on the pages; the implementation is pinned
+    against PyTorch's layer_norm + linear): two modulation vectors (shift first) from a learned
+    [2, dim] bias plus e.
     x [B, S, dim], e [B, dim] -> [B, S, 4*C_out].
     """
     x, e = _a(x), _a(e)
@@ -661,7 +663,8 @@ PARITY = {
     "unpatchify": "pinned: exact inverse of patchify (round trip), hand-worked fixture",
     "patch_embed": "pinned: equals a direct Conv3d (kernel = stride = (1,2,2)) loop",
     "sinusoidal_embedding": "pinned: t = 0 gives [1..1 | 0..0]; unit-modulus (cos,sin) pairs",
-    "time_embed": "parity unpinned beyond shape [6, dim] and an identity-weight special case",
+    "time_embed": "pinned: identity-weight special case; the composition equals PyTorch float64 "
+                  "Linear/SiLU modules with the same weights (the composition itself is a reading)",
     "layer_norm": "pinned: zero mean / unit variance; constant row -> bias; numpy.var cross-check",
     "rms_norm": "pinned: constant row c -> g c / sqrt(c^2 + eps); unit RMS for g = 1",
     "rope_3d": "pinned: segment sizes 44/42/42 and 24/20/20; identity at (0,0,0); norm "
@@ -676,8 +679,10 @@ PARITY = {
     "block_fwd": "pinned parts (norms, RoPE, attention, cross-attention single/dual equality, "
                  "adaLN-Zero identity); composition order is a reading: parity unpinned "
                  "beyond those identities",
-    "head_fwd": "parity unpinned (shape only)",
-    "context_embed": "parity unpinned (shape only)",
+    "head_fwd": "pinned: equals PyTorch layer_norm with weight 1 + scale and bias shift, then linear "
+                "(the two-vector head modulation itself is a reading)",
+    "context_embed": "pinned: equals PyTorch Linear -> exact GELU -> Linear with the same weights "
+                     "(the MLP shape itself is a reading)",
     "cfg_combine": "pinned: s = 1 -> v_c, s = 0 -> v_u",
     "euler_step": "pinned: straight-line path lands exactly on the endpoint",
     "sample": "pinned through cfg_combine / euler_step; DiT part as block_fwd",

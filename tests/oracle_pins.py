@@ -118,6 +118,83 @@ def pin_time_embed_identity(o):
     assert e0.shape == (6, d) and np.allclose(e0, s2[None, :], atol=1e-15)
 
 
+def _torch64():
+    import torch
+    return torch
+
+
+def pin_gelu_library(o):
+    """GELU is the exact x * Phi(x): PyTorch's erf-based GELU (approximate='none'), float64."""
+    torch = _torch64()
+    x = np.linspace(-8.0, 8.0, 2001)
+    ref = torch.nn.functional.gelu(torch.from_numpy(x), approximate="none").numpy()
+    assert np.allclose(o.gelu(x), ref, rtol=0, atol=1e-14)
+
+
+def pin_time_embed_library(o):
+    """e = Linear(SiLU(Linear(sinusoid))), e0 = Linear(SiLU(e)) reshaped [6, dim], against the same
+    composition of PyTorch float64 modules holding the same random weights (sinusoid pinned above)."""
+    torch = _torch64()
+    rng = np.random.default_rng(41)
+    fd, dim = 64, 24
+    w = {"wt1": rng.standard_normal((dim, fd)), "bt1": rng.standard_normal(dim),
+         "wt2": rng.standard_normal((dim, dim)), "bt2": rng.standard_normal(dim),
+         "wtp": rng.standard_normal((6 * dim, dim)), "btp": rng.standard_normal(6 * dim)}
+
+    def lin(a, b):
+        m = torch.nn.Linear(a.shape[1], a.shape[0], dtype=torch.float64)
+        with torch.no_grad():
+            m.weight.copy_(torch.from_numpy(a))
+            m.bias.copy_(torch.from_numpy(b))
+        return m
+    mlp = torch.nn.Sequential(lin(w["wt1"], w["bt1"]), torch.nn.SiLU(), lin(w["wt2"], w["bt2"]))
+    proj = torch.nn.Sequential(torch.nn.SiLU(), lin(w["wtp"], w["btp"]))
+    for t in (0.0, 0.37, 1.0):
+        emb = torch.from_numpy(o.sinusoidal_embedding(t, fd))
+        with torch.no_grad():
+            e_ref = mlp(emb)
+            e0_ref = proj(e_ref).reshape(6, dim)
+        e, e0 = o.time_embed(t, w, fd)
+        assert np.allclose(e, e_ref.numpy(), rtol=1e-12, atol=1e-12)
+        assert np.allclose(e0, e0_ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def pin_context_embed_library(o):
+    """Linear -> exact GELU -> Linear against PyTorch float64 modules with the same weights."""
+    torch = _torch64()
+    rng = np.random.default_rng(43)
+    n, din, dim = 7, 20, 12
+    ctx = rng.standard_normal((n, din))
+    w1, b1 = rng.standard_normal((dim, din)), rng.standard_normal(dim)
+    w2, b2 = rng.standard_normal((dim, dim)), rng.standard_normal(dim)
+    l1 = torch.nn.Linear(din, dim, dtype=torch.float64)
+    l2 = torch.nn.Linear(dim, dim, dtype=torch.float64)
+    with torch.no_grad():
+        l1.weight.copy_(torch.from_numpy(w1)); l1.bias.copy_(torch.from_numpy(b1))
+        l2.weight.copy_(torch.from_numpy(w2)); l2.bias.copy_(torch.from_numpy(b2))
+        ref = l2(torch.nn.functional.gelu(l1(torch.from_numpy(ctx)), approximate="none")).numpy()
+    assert np.allclose(o.context_embed(ctx, w1, b1, w2, b2), ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_head_library(o):
+    """The head's adaLN is a LayerNorm whose affine weight is 1 + scale and bias is shift: PyTorch's
+    layer_norm with that weight and bias, then its linear, per batch row (scale and shift from
+    head_mod + e, shift first)."""
+    torch = _torch64()
+    rng = np.random.default_rng(47)
+    B, S, dim, cout = 2, 5, 16, 8
+    x = rng.standard_normal((B, S, dim))
+    e = rng.standard_normal((B, dim))
+    w = {"head_mod": rng.standard_normal((2, dim)), "wh": rng.standard_normal((cout, dim)),
+         "bh": rng.standard_normal(cout)}
+    got = o.head_fwd(x, e, w, 1e-6)
+    for b in range(B):
+        shift = torch.from_numpy(w["head_mod"][0] + e[b])
+        scale = torch.from_numpy(w["head_mod"][1] + e[b])
+        u = torch.nn.functional.layer_norm(torch.from_numpy(x[b]), (dim,), weight=1.0 + scale, bias=shift, eps=1e-6)
+        ref = torch.nn.functional.linear(u, torch.from_numpy(w["wh"]), torch.from_numpy(w["bh"])).numpy()
+        assert np.allclose(got[b], ref, rtol=1e-12, atol=1e-12)
+
 # ---------------------------------------------------------------------- norms
 def pin_layer_norm(o):
     rng = np.random.default_rng(4)

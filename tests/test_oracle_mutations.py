@@ -184,6 +184,40 @@ def _snr_not_squared(t):
         return (1.0 - t) / t
 
 
+def _head_scale_without_one(x, e, w, ln_eps=1e-6):
+    x, e = np.asarray(x, float), np.asarray(e, float)
+    out = []
+    for b in range(x.shape[0]):
+        mod = np.asarray(w["head_mod"], float) + e[b][None, :]
+        u = wo.layer_norm(x[b], ln_eps) * mod[1] + mod[0]  # scale used without the 1 +
+        out.append(wo.linear(u, w["wh"], w["bh"]))
+    return np.stack(out)
+
+
+def _head_shift_scale_swapped(x, e, w, ln_eps=1e-6):
+    x, e = np.asarray(x, float), np.asarray(e, float)
+    out = []
+    for b in range(x.shape[0]):
+        mod = np.asarray(w["head_mod"], float) + e[b][None, :]
+        u = wo.modulate(wo.layer_norm(x[b], ln_eps), mod[1], mod[0])
+        out.append(wo.linear(u, w["wh"], w["bh"]))
+    return np.stack(out)
+
+
+def _context_embed_tanh_gelu(ctx, w1, b1, w2, b2):
+    h = wo.linear(ctx, w1, b1)
+    g = 0.5 * h * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (h + 0.044715 * h ** 3)))
+    return wo.linear(g, w2, b2)
+
+
+def _time_embed_silu_on_e0(t, w, freq_dim=256):
+    emb = wo.sinusoidal_embedding(t, freq_dim)
+    h = wo.silu(wo.linear(emb, w["wt1"], w["bt1"]))
+    e = wo.linear(h, w["wt2"], w["bt2"])
+    e0 = wo.silu(wo.linear(e, w["wtp"], w["btp"]))  # SiLU after the projection instead of before
+    return e, e0.reshape(6, -1)
+
+
 MUTANTS = {
     "mask_raw_reshape": ("i2v_mask", lambda: _mask_raw_reshape),
     "patch_vector_kw_kh": ("patchify", lambda: _patchify_kw_kh),
@@ -210,6 +244,10 @@ MUTANTS = {
     "experts_swapped": ("expert_for_step", lambda: _expert_swapped),
     "t_moe_full_snr": ("t_moe_from_snr", lambda: _t_moe_full_snr),
     "snr_not_squared": ("snr", lambda: _snr_not_squared),
+    "head_scale_without_one": ("head_fwd", lambda: _head_scale_without_one),
+    "head_shift_scale_swapped": ("head_fwd", lambda: _head_shift_scale_swapped),
+    "context_embed_tanh_gelu": ("context_embed", lambda: _context_embed_tanh_gelu),
+    "time_embed_silu_after_projection": ("time_embed", lambda: _time_embed_silu_on_e0),
 }
 
 
