@@ -223,7 +223,10 @@ int wan_dit_block_fwd(const wan_block_cfg* cfg, const wan_block_weights* w, wan_
  *   WAN_ATTN_CACHE_STORE  the block computes as usual and writes y to attn_y;
  *   WAN_ATTN_CACHE_REUSE  the block skips LN1, the Q/K/V product, the norms and RoPE, the attention
  *                         and the O product, and adds gate1 * attn_y (gate1 of this call's e0) to x.
- * The other branches always run.  Which steps reuse is the caller's schedule. */
+ * The other branches always run.  Which steps reuse is the caller's schedule.  REUSE reads attn_y as an
+ * earlier STORE with the same cfg, grid and B left it; the library cannot check that.  Errors: as
+ * wan_dit_block_fwd, plus WAN_EINVAL for attn_mode outside 0..2 or a NULL / misaligned attn_y in a
+ * cache mode (nothing is enqueued). */
 typedef enum { WAN_ATTN_CACHE_OFF = 0, WAN_ATTN_CACHE_STORE = 1, WAN_ATTN_CACHE_REUSE = 2 } wan_attn_cache_mode;
 int wan_dit_block_fwd_cached(const wan_block_cfg* cfg, const wan_block_weights* w, wan_grid grid, int32_t B, float* x,
                              const float* e0, const wan_cross_kv* kv, float* attn_y, int32_t attn_mode, void* ws,
