@@ -430,24 +430,25 @@ __device__ __forceinline__ void softmax_lazy(const f32x16 (&s)[2], float c_log2,
   st.l += lsum;
 }
 
-// The ping-pong kernel's matrix half of a tile (bf16): O^T += V^T(t) P^T(t) from vslot, then (if
-// NEXT) S(t+1) = K(t+1) Q^T from kslot into sn.  Units of two MFMAs, each unit's LDS fragments read
-// two units ahead: the PV units (16-key chunk, pair of d blocks) first, then the S units (hd chunk,
-// both 32-key blocks).
-template <typename T, int HD>
+// The ping-pong kernel's matrix half of a tile (bf16): (if NEXT) S(t+1) = K(t+1) Q^T from kslot into
+// sn, then O^T += V^T(t) P^T(t) from vslot.  Units of two MFMAs, each unit's LDS fragments read two
+// units ahead: the S units (hd chunk, both 32-key blocks) first, so that the next vector phase, which
+// starts on S(t+1), does not wait on the last MFMAs; then the PV units (16-key chunk, pair of d
+// blocks), whose accumulators the vector phase does not read.
+template <typename T, int HD, bool NEXT>
 __device__ __forceinline__ void read_pv_or_s_unit(const FragAddr<T, HD>& fa, const char* vslot, const char* kslot,
                                                   int u, u32x4& f0, u32x4& f1) {
   using C = AttnCfg<T, HD>;
   using F = FragAddr<T, HD>;
-  constexpr int DP = C::ND / 2, NPV = 4 * DP;
-  if (u < NPV) {
-    const int c = u / DP, d0 = (u % DP) * 2;
+  constexpr int DP = C::ND / 2, NS = NEXT ? C::NCH : 0;
+  if (u >= NS) {
+    const int w = u - NS;
+    const int c = w / DP, d0 = (w % DP) * 2;
     f0 = *reinterpret_cast<const u32x4*>(vslot + fa.v[c] + d0 * F::VD32);
     f1 = *reinterpret_cast<const u32x4*>(vslot + fa.v[c] + (d0 + 1) * F::VD32);
   } else {
-    const int c = u - NPV;
-    f0 = *reinterpret_cast<const u32x4*>(kslot + fa.k[c]);
-    f1 = *reinterpret_cast<const u32x4*>(kslot + fa.k[c] + F::KB32);
+    f0 = *reinterpret_cast<const u32x4*>(kslot + fa.k[u]);
+    f1 = *reinterpret_cast<const u32x4*>(kslot + fa.k[u] + F::KB32);
   }
 }
 
@@ -457,10 +458,10 @@ __device__ __forceinline__ void pv_and_next_scores(const FragAddr<T, HD>& fa, co
                                                    const u32x4 (&qf)[AttnCfg<T, HD>::NCH], const char* kslot,
                                                    f32x16 (&sn)[2]) {
   using C = AttnCfg<T, HD>;
-  constexpr int DP = C::ND / 2, NPV = 4 * DP, NU = NEXT ? NPV + C::NCH : NPV;
+  constexpr int DP = C::ND / 2, NPV = 4 * DP, NS = NEXT ? C::NCH : 0, NU = NS + NPV;
   u32x4 f[3][2];  // fragments of units u % 3, read two units ahead
-  read_pv_or_s_unit<T, HD>(fa, vslot, kslot, 0, f[0][0], f[0][1]);
-  read_pv_or_s_unit<T, HD>(fa, vslot, kslot, 1, f[1][0], f[1][1]);
+  read_pv_or_s_unit<T, HD, NEXT>(fa, vslot, kslot, 0, f[0][0], f[0][1]);
+  read_pv_or_s_unit<T, HD, NEXT>(fa, vslot, kslot, 1, f[1][0], f[1][1]);
   if (NEXT) {
     sn[0] = zero16();
     sn[1] = zero16();
@@ -468,18 +469,18 @@ __device__ __forceinline__ void pv_and_next_scores(const FragAddr<T, HD>& fa, co
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
-    if (u + 2 < NU) read_pv_or_s_unit<T, HD>(fa, vslot, kslot, u + 2, f[(u + 2) % 3][0], f[(u + 2) % 3][1]);
+    if (u + 2 < NU) read_pv_or_s_unit<T, HD, NEXT>(fa, vslot, kslot, u + 2, f[(u + 2) % 3][0], f[(u + 2) % 3][1]);
     __builtin_amdgcn_sched_barrier(0);  // the reads go out before this unit's MFMAs
     const u32x4& f0 = f[u % 3][0];
     const u32x4& f1 = f[u % 3][1];
-    if (u < NPV) {
-      const int c = u / DP, d0 = (u % DP) * 2;
+    if (u >= NS) {
+      const int w = u - NS;
+      const int c = w / DP, d0 = (w % DP) * 2;
       mfma_chunk(f0, pf[c], o[d0], T());
       mfma_chunk(f1, pf[c], o[d0 + 1], T());
     } else {
-      const int c = u - NPV;
-      mfma_chunk(f0, qf[c], sn[0], T());
-      mfma_chunk(f1, qf[c], sn[1], T());
+      mfma_chunk(f0, qf[u], sn[0], T());
+      mfma_chunk(f1, qf[u], sn[1], T());
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -701,7 +702,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const T* __restrict__
 // ---------------------------------------------------------------------------
 // Ping-pong kernel (bf16): one workgroup = 8 waves = 256 queries of one (b, head), two waves per
 // SIMD.  Each wave alternates A(t) = the weights of S(t) (vector units only, no LDS access) and
-// B(t) = O^T += V^T(t) P^T(t) followed by S(t+1) = K(t+1) Q^T (32 MFMAs), with a workgroup barrier
+// B(t) = S(t+1) = K(t+1) Q^T followed by O^T += V^T(t) P^T(t) (32 MFMAs), with a workgroup barrier
 // between the two (FlashAttention-3's ping-pong schedule).  Waves 4-7 (group 1) pass one extra
 // barrier at the start and waves 0-3 (group 0) one at the end, so group 1 runs a half tile behind:
 // between two barriers one wave of each SIMD is in A and the other in B, and the SIMD's matrix and
@@ -762,7 +763,7 @@ __device__ __forceinline__ void pp_tile(const u32x4 (&qf)[AttnCfg<T, HD>::NCH], 
   mask_tail(s, j0, kv.L);
   u32x4 pf[4];
   softmax_lazy<T, HD>(s, c_log2, o, st, pf);
-  // ---- B(t): O^T += V^T(t) P^T(t), S(t+1) = K(t+1) Q^T (matrix units)
+  // ---- B(t): S(t+1) = K(t+1) Q^T, O^T += V^T(t) P^T(t) (matrix units)
   phase_barrier<PER>(last);
   last = 0;
   // on a stream's last tile k_next holds a stale tile with no copy in flight: S(t+1) is computed and unused
