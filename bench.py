@@ -92,6 +92,51 @@ def counters_traffic(launch_ms):
         return None
 
 
+def measure_device():
+    """Device ceilings measured beside the nominal ones: compute units and peak engine clock as the
+    runtime reports them, the matrix-core rate of a kernel issuing only MFMAs on register operands
+    (bf16 and E4M3), and the rate of a plain 1 GiB device-to-device copy."""
+    import torch
+
+    from video_diffusion_transformer_step_amd import _lib as L
+    cus, khz = L.device_info()
+    blocks = cus * 8
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    res = {"compute_units": cus, "clock_mhz": round(khz / 1e3, 1),
+           "nominal_bf16_tflops": round(cus * khz * 1e3 * 4096 / 1e12, 1)}
+    one = {0: 0x3F803F80, 1: 0x38383838}  # bf16 1.0 in both halves; E4M3 1.0 in every byte
+    for kind, key, iters in ((0, "bf16", 4000), (1, "fp8_e4m3", 2000)):
+        L.mfma_peak_probe(kind, one[kind], one[kind], blocks, 16, out)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        ev0.record()
+        for _ in range(reps):
+            flop = L.mfma_peak_probe(kind, one[kind], one[kind], blocks, iters, out)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / reps
+        expect = 64.0 * L.MFMA_PROBE_K[kind] * iters
+        assert bool((out == expect).all()), f"MFMA probe ({key}) returned wrong sums"
+        res[f"measured_{key}_tflops"] = round(flop / (ms * 1e-3) / 1e12, 1)
+    res["sustained_mfma_clock_mhz"] = round(res["measured_bf16_tflops"] * 1e12 / (cus * 4096) / 1e6, 1)
+    del out
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    ev1.record()
+    torch.cuda.synchronize()
+    res["copy_gbs"] = round(2 * 4 * n / (ev0.elapsed_time(ev1) / 5 * 1e-3) / 1e9, 1)
+    del src, dst
+    return res
+
+
 def cpu_baseline(c, layers, seed=0):
     """The CPU oracle on a bounded sample: one block in sampled-row mode (K/V for all tokens,
     then R1 and R2 query rows), extrapolated to all S rows and `layers` blocks."""
@@ -121,6 +166,13 @@ def cpu_baseline(c, layers, seed=0):
         t = time.perf_counter()
         oracle.block_fwd(x, e0[None], bw, kv, c.grid, c.heads, rows=rows)
         t2 = time.perf_counter() - t
+        blas = [i for i in info if i.get("user_api") == "blas"]
+        blas = (f"{blas[0].get('internal_api')} {blas[0].get('version')} ({blas[0].get('architecture')}, "
+                f"{blas[0].get('threading_layer')} threads)") if blas else "none found"
+    with threadpoolctl.threadpool_limits(1):
+        t = time.perf_counter()
+        oracle.block_fwd(x, e0[None], bw, kv, c.grid, c.heads, rows=rows[:R1])
+        t1_one = time.perf_counter() - t
     per_row = max(t2 - t1, 0.0) / (R2 - R1)
     fixed = max(t1 - R1 * per_row, 0.0)
     block_s = fixed + c.S * per_row
@@ -131,6 +183,11 @@ def cpu_baseline(c, layers, seed=0):
                    f"{fixed:.2f} s + {c.S} rows x "
                    f"{per_row * 1e3:.1f} ms) x {layers} blocks; float64 NumPy, {threads} BLAS threads "
                    f"of {cores} cores"),
+        "blas": blas,
+        "one_thread": {"seconds": round(t1_one, 2), "vs_all_threads": round(t1_one / t1, 2),
+                       "value_est": round(layers * block_s * 1e3 * t1_one / t1, 1),
+                       "sample": (f"the {R1}-row call above on one BLAS thread; value_est scales the step "
+                                  f"figure by the two calls' time ratio (an estimate)")},
     }
 
 
@@ -255,6 +312,8 @@ def main():
                     help="skip the diffusion-cache measurement (attention-output and CFG reuse)")
     ap.add_argument("--no-two-expert", action="store_true",
                     help="skip the two-expert (high-noise / low-noise DiT) sampling measurement")
+    ap.add_argument("--no-device-probe", action="store_true",
+                    help="skip the device ceilings (register-only MFMA rate, plain copy rate)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many bytes (a known-size "
                          "reference for HBM byte counters)")
@@ -349,12 +408,18 @@ def main():
         fl = {"qkv_gemm": 2 * S * d * 3 * d, "self_attn": 4 * S * S * d, "o_gemm": 2 * S * d * d,
               "cross_q_gemm": 2 * S * d * d, "cross_attn": 4 * S * (c.text_len + c.img_len) * d,
               "cross_o_gemm": 2 * S * d * d, "ffn1_gemm": 2 * S * d * f, "ffn2_gemm": 2 * S * f * d}
+        # algorithmic bytes of the bandwidth-bound kernels: LN reads fp32 x and writes the bf16 operand;
+        # the QK norm + RoPE pass reads and writes bf16 q and k
+        hbm_bytes = {"ln1": 6 * S * d, "ln2": 6 * S * d, "ln3": 6 * S * d, "qk_norm_rope": 8 * S * d}
         breakdown = {}
         for k_, v in bd.items():
             ms = float(np.mean(v))
             e = {"ms": round(ms, 4)}
             if k_ in fl:
                 e["tflops"] = round(fl[k_] * c.B / (ms * 1e-3) / 1e12, 1)
+            if k_ in hbm_bytes:
+                e["gbs"] = round(hbm_bytes[k_] * c.B / (ms * 1e-3) / 1e9, 1)
+                e["frac_of_hbm"] = round(e["gbs"] / PEAK_HBM_GBS, 3)
             breakdown[k_] = e
         breakdown["block_sum_ms"] = round(sum(e["ms"] for e in breakdown.values()), 3)
         log(f"breakdown: {json.dumps(breakdown)}")
@@ -368,6 +433,11 @@ def main():
         torch.cuda.synchronize()
         log(f"copied {n * 4} bytes (counter calibration)")
         del src, dst
+
+    device = None
+    if not args.no_device_probe:
+        device = measure_device()
+        log(f"device: {json.dumps(device)}")
 
     # ---- the same step on the FP8 paths (reported beside the bf16 headline): the quantised
     # self-attention alone, then with the E4M3 Q/K/V, O, FFN1, FFN2 products as well
@@ -407,6 +477,8 @@ def main():
                         "attention_ms": round(a8, 4), "attention_tflops": round(tf8, 1),
                         "attention_frac_of_fp8_peak": round(tf8 / PEAK_FP8_TFLOPS, 4),
                         "attention_frac_of_bf16_peak": round(tf8 / PEAK_BF16_TFLOPS, 4),
+                        "attention_frac_of_measured_fp8_peak": (round(tf8 / device["measured_fp8_e4m3_tflops"], 4)
+                                                                if device else None),
                         "quantise_ms_per_block": round(q8, 4),
                         "step_speedup_vs_bf16": round(ms_per_step / ms8, 3), "note": note}
             log(f"{key}: {ms8:.2f} ms/step, attention {a8:.3f} ms ({tf8:.0f} TFLOP/s), quantisers {q8:.3f} ms/block")
@@ -452,12 +524,18 @@ def main():
         "ms_per_block": round(ms_per_step / layers, 3),
         "step_tflops": round(step_tflops, 1),
         "step_frac_of_bf16_peak": round(step_tflops / PEAK_BF16_TFLOPS, 4),
+        "step_frac_of_measured_bf16_peak": (round(step_tflops / device["measured_bf16_tflops"], 4)
+                                            if device else None),
         "attention_tflops": round(attn_tflops, 1),
         "attention_frac_of_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": {"kernel": "self-attention (flash, bf16 MFMA)", "bound": "mfma",
                      "achieved": round(attn_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "launch_ms": round(attn_avg, 4), "flops_per_launch": attn_flops},
+                     "launch_ms": round(attn_avg, 4), "flops_per_launch": attn_flops,
+                     "peak_measured": device["measured_bf16_tflops"] if device else None,
+                     "frac_of_measured_peak": (round(attn_tflops / device["measured_bf16_tflops"], 4)
+                                               if device else None)},
+        "device": device,
         "breakdown_ms_per_block": breakdown,
         "fp8_attention_step": fp8.get("fp8_attention_step"),
         "fp8_step": fp8.get("fp8_step"),

@@ -342,6 +342,25 @@ int wan_profile_begin(void* const* start_events, void* const* stop_events, int32
                       uint32_t kernel_mask);
 int32_t wan_profile_end(void);
 
+/* Device ceilings (measurement only): what the roofline fractions of the kernels above are quoted
+ * against, measured on the device at hand beside the nominal figures.
+ * wan_device_info: compute units and peak engine clock (kHz) of the current device, as the HIP
+ *   runtime reports them (hipDeviceAttributeMultiprocessorCount, hipDeviceAttributeClockRate).
+ * wan_mfma_peak_probe: launches `blocks` workgroups of 256 threads (4 waves); each wave issues
+ *   4 * iters matrix-core instructions on register operands only:
+ *     kind 0: v_mfma_f32_32x32x16_bf16, every A element = the bf16 in each half of a_word, B likewise
+ *             from b_word; 32768 flop per instruction and wave;
+ *     kind 1: v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3 with unit block scales, every element = the
+ *             code in each byte of a_word / b_word; 131072 flop per instruction and wave.
+ *   out [blocks * 256] float32 (caller-owned device memory) receives each lane's sum of its four
+ *   accumulators, 64 * K * iters * a * b (K = 16, resp. 64), so a caller can check the work was done.
+ *   Time it with events on `stream`; flop per launch = blocks * 4 * 4 * iters * (flop per instruction).
+ *   Errors: WAN_EINVAL for kind outside 0..1, blocks or iters outside 1..2^20, or a NULL / misaligned
+ *   out (nothing is enqueued). */
+int wan_device_info(int32_t* compute_units, int32_t* clock_khz);
+int wan_mfma_peak_probe(int32_t kind, uint32_t a_word, uint32_t b_word, int32_t blocks, int32_t iters, float* out,
+                        wan_stream_t stream);
+
 /* Human-readable name of a wan_status; message of the last failed call on this thread. */
 const char* wan_status_string(int status);
 const char* wan_last_error(void);

@@ -173,6 +173,15 @@ def test_ring_attention_validation(lib):
     assert "lse_parts" in _err(lib)
 
 
+def test_device_probe_validation(lib):
+    assert lib.wan_device_info(None, None) == L.WAN_EINVAL
+    for kind, blocks, iters, out in ((2, 1, 1, FAKE), (-1, 1, 1, FAKE), (0, 0, 1, FAKE), (1, 1, 0, FAKE),
+                                     (0, 1 << 21, 1, FAKE), (0, 1, 1 << 21, FAKE), (0, 1, 1, None),
+                                     (1, 1, 1, FAKE + 2)):
+        assert lib.wan_mfma_peak_probe(kind, 0, 0, blocks, iters, out, None) == L.WAN_EINVAL, (kind, blocks, iters)
+    assert "aligned" in _err(lib)
+
+
 def test_status_strings(lib):
     assert lib.wan_status_string(L.WAN_EWORKSPACE) == b"WAN_EWORKSPACE"
     assert lib.wan_status_string(0) == b"WAN_OK"

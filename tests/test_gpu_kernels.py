@@ -163,3 +163,22 @@ def test_attention_720p_stress_sampled_rows():
     err = rel_l2(got, ref)
     print(f"[attn-720p] sampled-row rel-L2 {err:.3e}")
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("kind,a_word,b_word,a,b", [(0, 0x3F003F00, 0x3FC03FC0, 0.5, 1.5),
+                                                    (1, 0x30303030, 0x3C3C3C3C, 0.5, 1.5)],
+                         ids=["bf16", "e4m3"])
+def test_mfma_peak_probe_sums(kind, a_word, b_word, a, b):
+    """The register-only MFMA probe did all its instructions: every lane's accumulator sum is
+    64 * K * iters * a * b (bf16 0.5 = 0x3F00, 1.5 = 0x3FC0; E4M3 0.5 = 0x30, 1.5 = 0x3C)."""
+    require_gpu()
+    case(f"mfma probe kind {kind}")
+    cus, khz = L.device_info()
+    assert cus > 0 and khz > 0
+    blocks, iters = 3, 5
+    out = torch.full((blocks * 256,), -1.0, dtype=torch.float32, device="cuda")
+    flop = L.mfma_peak_probe(kind, a_word, b_word, blocks, iters, out)
+    assert flop == blocks * 16 * iters * L.MFMA_PROBE_FLOP[kind]
+    expect = 64.0 * L.MFMA_PROBE_K[kind] * iters * a * b
+    got = host(out)
+    assert np.all(got == expect), (got.min(), got.max(), expect)

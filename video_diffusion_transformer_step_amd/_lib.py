@@ -102,6 +102,8 @@ _SIGS = {
     "wan_profile_begin": ([C.POINTER(C.c_void_p), C.POINTER(C.c_void_p), C.POINTER(C.c_int32), C.c_int32,
                            C.c_uint32], C.c_int),
     "wan_profile_end": ([], C.c_int32),
+    "wan_device_info": ([C.POINTER(C.c_int32), C.POINTER(C.c_int32)], C.c_int),
+    "wan_mfma_peak_probe": ([C.c_int32, C.c_uint32, C.c_uint32, C.c_int32, C.c_int32, vp, vp], C.c_int),
     "wan_status_string": ([C.c_int], C.c_char_p),
     "wan_last_error": ([], C.c_char_p),
 }
@@ -353,6 +355,26 @@ def gemm_e4m3(a_codes, a_scales, w_codes, w_scale, y, bias=None, act=0, stream=N
     _check(lib().wan_gemm_e4m3(_p(a_codes), a_codes.stride(0), _p(a_scales), _p(w_codes), w_codes.stride(0),
                                _p(w_scale), M, N, K, _p(bias), act, _p(y), y.stride(0), _stream(stream)),
            "wan_gemm_e4m3")
+
+
+def device_info():
+    """(compute units, peak engine clock in kHz) of the current device."""
+    cus, khz = C.c_int32(), C.c_int32()
+    _check(lib().wan_device_info(C.byref(cus), C.byref(khz)), "wan_device_info")
+    return cus.value, khz.value
+
+
+MFMA_PROBE_FLOP = {0: 2 * 32 * 32 * 16, 1: 2 * 32 * 32 * 64}  # per instruction and wave
+MFMA_PROBE_K = {0: 16, 1: 64}
+
+
+def mfma_peak_probe(kind, a_word, b_word, blocks, iters, out, stream=None):
+    """Enqueue the register-only MFMA kernel (kind 0 bf16, 1 E4M3); out [blocks * 256] float32.
+    Returns the launch's flop count."""
+    assert out.numel() >= blocks * 256
+    _check(lib().wan_mfma_peak_probe(kind, a_word, b_word, blocks, iters, _p(out), _stream(stream)),
+           "wan_mfma_peak_probe")
+    return blocks * 4 * 4 * iters * MFMA_PROBE_FLOP[kind]
 
 
 KERNEL_IDS = ["ln1", "qkv_gemm", "qk_norm_rope", "vt_tail", "self_attn", "o_gemm", "ln3", "cross_q_gemm",

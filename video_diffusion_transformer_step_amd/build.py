@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libwan.so")
-SOURCES = ["layout.hip", "norm.hip", "gemm.hip", "attention.hip", "quant.hip", "wan_abi.hip"]
+SOURCES = ["layout.hip", "norm.hip", "gemm.hip", "attention.hip", "quant.hip", "probe.hip", "wan_abi.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

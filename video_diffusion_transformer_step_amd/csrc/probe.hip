@@ -1,0 +1,60 @@
+// Device ceilings for the roofline figures: a kernel that issues nothing but matrix-core
+// instructions on register operands (no LDS, no global loads apart from one store per lane at the
+// end), so its rate is what the MFMA units sustain at the clock the chip holds under that load.
+// The step's kernels are quoted against the nominal peak; this gives the measured one beside it.
+#include "wan_internal.h"
+
+namespace wan {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+constexpr int PROBE_THREADS = 256;
+
+// KIND 0: v_mfma_f32_32x32x16_bf16 (a_word, b_word = two equal bf16 halves each);
+// KIND 1: v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3 with unit block scales (four equal code bytes).
+// Four independent accumulators per wave, so an MFMA's result is needed again only four instructions
+// later.  Every lane ends with the sum of its 64 accumulator elements:
+//   64 * K * iters * a * b   (K = 16 for bf16, 64 for E4M3),
+// which the caller can check, so the instruction stream is known to have run in full.
+template <int KIND>
+__global__ __launch_bounds__(PROBE_THREADS) void mfma_peak_kernel(uint32_t a_word, uint32_t b_word, int iters,
+                                                                  float* out) {
+  f32x16 acc0 = {}, acc1 = {}, acc2 = {}, acc3 = {};
+  if constexpr (KIND == 0) {
+    const u32x4 aw = {a_word, a_word, a_word, a_word}, bw = {b_word, b_word, b_word, b_word};
+    const bf16x8 a = __builtin_bit_cast(bf16x8, aw), b = __builtin_bit_cast(bf16x8, bw);
+    for (int i = 0; i < iters; ++i) {
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc1, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc2, 0, 0, 0);
+      acc3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc3, 0, 0, 0);
+    }
+  } else {
+    const int ai = (int)a_word, bi = (int)b_word;
+    const v8i a = {ai, ai, ai, ai, ai, ai, ai, ai}, b = {bi, bi, bi, bi, bi, bi, bi, bi};
+    for (int i = 0; i < iters; ++i) {
+      acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc0, 0, 0, 0, 127, 0, 127);
+      acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc1, 0, 0, 0, 127, 0, 127);
+      acc2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc2, 0, 0, 0, 127, 0, 127);
+      acc3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc3, 0, 0, 0, 127, 0, 127);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) s += (acc0[j] + acc1[j]) + (acc2[j] + acc3[j]);
+  out[(int64_t)blockIdx.x * PROBE_THREADS + threadIdx.x] = s;
+}
+
+}  // namespace
+
+hipError_t launch_mfma_peak(int kind, uint32_t a_word, uint32_t b_word, int blocks, int iters, float* out,
+                            hipStream_t s) {
+  if (kind == 0)
+    hipLaunchKernelGGL(mfma_peak_kernel<0>, dim3(blocks), dim3(PROBE_THREADS), 0, s, a_word, b_word, iters, out);
+  else
+    hipLaunchKernelGGL(mfma_peak_kernel<1>, dim3(blocks), dim3(PROBE_THREADS), 0, s, a_word, b_word, iters, out);
+  return hipGetLastError();
+}
+
+}  // namespace wan

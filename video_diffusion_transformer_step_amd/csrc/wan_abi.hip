@@ -801,6 +801,25 @@ int wan_gemm_e4m3(const void* a, int64_t lda, const float* a_scales, const void*
   return WAN_OK;
 }
 
+int wan_device_info(int32_t* compute_units, int32_t* clock_khz) {
+  if (!compute_units || !clock_khz) return fail(WAN_EINVAL, "compute_units / clock_khz is NULL");
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  HIP_TRY(hipDeviceGetAttribute(compute_units, hipDeviceAttributeMultiprocessorCount, dev));
+  HIP_TRY(hipDeviceGetAttribute(clock_khz, hipDeviceAttributeClockRate, dev));
+  return WAN_OK;
+}
+
+int wan_mfma_peak_probe(int32_t kind, uint32_t a_word, uint32_t b_word, int32_t blocks, int32_t iters, float* out,
+                        wan_stream_t stream) {
+  if (kind != 0 && kind != 1) return fail(WAN_EINVAL, "kind must be 0 (bf16) or 1 (E4M3), got %d", kind);
+  if (blocks < 1 || blocks > (1 << 20)) return fail(WAN_EINVAL, "blocks must be in 1..2^20, got %d", blocks);
+  if (iters < 1 || iters > (1 << 20)) return fail(WAN_EINVAL, "iters must be in 1..2^20, got %d", iters);
+  WAN_TRY(need_f32(out, "out"));
+  HIP_TRY(launch_mfma_peak(kind, a_word, b_word, blocks, iters, out, hs(stream)));
+  return WAN_OK;
+}
+
 int wan_profile_begin(void* const* start_events, void* const* stop_events, int32_t* tags, int32_t capacity,
                       uint32_t kernel_mask) {
   if (capacity < 0) return fail(WAN_EINVAL, "capacity must be >= 0");

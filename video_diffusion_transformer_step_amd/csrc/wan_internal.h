@@ -150,4 +150,11 @@ template <typename T>
 hipError_t launch_lse_merge(const void* const* o_parts, const float* const* lse_parts, int n, int B, int S, int H,
                             int hd, T* o, float* lse, hipStream_t s);
 
+// ---- device ceilings (probe.hip) --------------------------------------------
+// `blocks` workgroups of 256 threads, each wave issuing 4 * iters MFMAs (kind 0 bf16 32x32x16,
+// kind 1 E4M3 32x32x64) on register operands built from a_word / b_word; out [blocks * 256] float32
+// receives each lane's accumulator sum, 64 * K * iters * a * b.
+hipError_t launch_mfma_peak(int kind, uint32_t a_word, uint32_t b_word, int blocks, int iters, float* out,
+                            hipStream_t s);
+
 }  // namespace wan
