@@ -137,6 +137,65 @@ def measure_device():
     return res
 
 
+def measure_sharded(c, ulysses=4, ring=8, reps=10):
+    """One GPU's share of the sequence-parallel self-attention on this workload, timed with events:
+    Ulysses over `ulysses` GPUs (every token, heads / ulysses heads: the unchanged kernel on a head
+    shard), one ring step over `ring` GPUs (an S / ring query shard against one S / ring key/value
+    shard, with its log-sum-exp, via wan_attention_partial_fwd, which also transposes the chunk's V),
+    and the exact merge of `ring` such partial results (wan_attention_lse_merge)."""
+    import torch
+
+    from video_diffusion_transformer_step_amd import _lib as L
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(77)
+    bf, hd, S = torch.bfloat16, c.head_dim, c.S
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(reps):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / reps
+
+    out = {}
+    hs = c.heads // ulysses
+    q, k, v = (torch.randn(c.B, S, hs, hd, generator=gen, device="cuda").to(bf) for _ in range(3))
+    o = torch.empty_like(q)
+    ws = torch.empty(L.attention_partial_ws_bytes(L.WAN_BF16, c.B, S, hs, hd), dtype=torch.uint8, device="cuda")
+    ms = timed(lambda: L.attention_partial_fwd(q, k, v, o, None, ws))
+    fl = 4 * c.B * S * S * hs * hd
+    out["ulysses_shard"] = {"gpus": ulysses, "heads": hs, "tokens": S, "ms": round(ms, 4),
+                            "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                            "frac_of_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del q, k, v, o, ws
+    Sr = (S + ring - 1) // ring
+    q, k, v = (torch.randn(c.B, Sr, c.heads, hd, generator=gen, device="cuda").to(bf) for _ in range(3))
+    o = torch.empty_like(q)
+    lse = torch.empty(c.B, c.heads, Sr, dtype=torch.float32, device="cuda")
+    ws = torch.empty(L.attention_partial_ws_bytes(L.WAN_BF16, c.B, Sr, c.heads, hd), dtype=torch.uint8,
+                     device="cuda")
+    ms = timed(lambda: L.attention_partial_fwd(q, k, v, o, lse, ws))
+    fl = 4 * c.B * Sr * Sr * c.heads * hd
+    out["ring_step"] = {"gpus": ring, "q_tokens": Sr, "kv_tokens": Sr, "heads": c.heads, "ms": round(ms, 4),
+                        "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                        "frac_of_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                        "ring_ms_per_block": round(ms * ring, 3)}
+    o_parts = [torch.randn(c.B, Sr, c.heads, hd, generator=gen, device="cuda").to(bf) for _ in range(ring)]
+    l_parts = [torch.randn(c.B, c.heads, Sr, generator=gen, device="cuda") for _ in range(ring)]
+    ms = timed(lambda: L.attention_lse_merge(o_parts, l_parts, o, lse))
+    nbytes = (ring + 1) * c.B * Sr * c.heads * (hd * 2 + 4)
+    out["lse_merge"] = {"parts": ring, "tokens": Sr, "ms": round(ms, 4),
+                        "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                        "frac_of_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}
+    out["note"] = ("the shard kernels on one GPU at the shapes each GPU would run; no collective is timed "
+                   "(ring_ms_per_block = ring steps x one step, without the merge or the K/V exchange)")
+    return out
+
+
 def cpu_baseline(c, layers, seed=0):
     """The CPU oracle on a bounded sample: one block in sampled-row mode (K/V for all tokens,
     then R1 and R2 query rows), extrapolated to all S rows and `layers` blocks."""
@@ -312,6 +371,8 @@ def main():
                     help="skip the diffusion-cache measurement (attention-output and CFG reuse)")
     ap.add_argument("--no-two-expert", action="store_true",
                     help="skip the two-expert (high-noise / low-noise DiT) sampling measurement")
+    ap.add_argument("--no-sharded", action="store_true",
+                    help="skip the one-GPU shares of sequence-parallel attention (Ulysses head shard, ring step, merge)")
     ap.add_argument("--no-device-probe", action="store_true",
                     help="skip the device ceilings (register-only MFMA rate, plain copy rate)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -439,6 +500,11 @@ def main():
         device = measure_device()
         log(f"device: {json.dumps(device)}")
 
+    sharded = None
+    if not args.no_sharded and c.dtype == "bf16" and c.heads % 4 == 0:
+        sharded = measure_sharded(c)
+        log(f"sharded attention: {json.dumps(sharded)}")
+
     # ---- the same step on the FP8 paths (reported beside the bf16 headline): the quantised
     # self-attention alone, then with the E4M3 Q/K/V, O, FFN1, FFN2 products as well
     fp8 = {}
@@ -539,6 +605,7 @@ def main():
         "breakdown_ms_per_block": breakdown,
         "fp8_attention_step": fp8.get("fp8_attention_step"),
         "fp8_step": fp8.get("fp8_step"),
+        "sharded_attention": sharded,
         "diffusion_cache": cache,
         "two_expert": two_expert,
         "cpu_baseline": cpu,
