@@ -165,7 +165,7 @@ def measure_sharded(c, ulysses=4, ring=8, reps=10):
     hs = c.heads // ulysses
     q, k, v = (torch.randn(c.B, S, hs, hd, generator=gen, device="cuda").to(bf) for _ in range(3))
     o = torch.empty_like(q)
-    ws = torch.empty(L.attention_partial_ws_bytes(L.WAN_BF16, c.B, S, hs, hd), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(L.attention_partial_ws_bytes(L.WAN_BF16, c.B, S, S, hs, hd), dtype=torch.uint8, device="cuda")
     ms = timed(lambda: L.attention_partial_fwd(q, k, v, o, None, ws))
     fl = 4 * c.B * S * S * hs * hd
     out["ulysses_shard"] = {"gpus": ulysses, "heads": hs, "tokens": S, "ms": round(ms, 4),
@@ -176,7 +176,7 @@ def measure_sharded(c, ulysses=4, ring=8, reps=10):
     q, k, v = (torch.randn(c.B, Sr, c.heads, hd, generator=gen, device="cuda").to(bf) for _ in range(3))
     o = torch.empty_like(q)
     lse = torch.empty(c.B, c.heads, Sr, dtype=torch.float32, device="cuda")
-    ws = torch.empty(L.attention_partial_ws_bytes(L.WAN_BF16, c.B, Sr, c.heads, hd), dtype=torch.uint8,
+    ws = torch.empty(L.attention_partial_ws_bytes(L.WAN_BF16, c.B, Sr, Sr, c.heads, hd), dtype=torch.uint8,
                      device="cuda")
     ms = timed(lambda: L.attention_partial_fwd(q, k, v, o, lse, ws))
     fl = 4 * c.B * Sr * Sr * c.heads * hd

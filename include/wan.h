@@ -263,14 +263,19 @@ int wan_attention_fwd(int32_t dtype, const void* q, const void* k, const void* v
  * k, v [B, Sk, heads, head_dim] (all dtype; no RoPE or norm is applied here, so pass rotated q and k):
  *   o   [B, Sq, heads, head_dim] dtype = softmax(q k^T / sqrt(head_dim)) v over the chunk's keys;
  *   lse [B, heads, Sq] float32 (NULL = not written) = ln sum_j exp(q k_j / sqrt(head_dim)).
- * head_dim 64 or 128.  Workspace: wan_attention_partial_workspace_bytes() (the chunk's V^T).
+ * head_dim 64 or 128.  Workspace: wan_attention_partial_workspace_bytes() for the device current at the
+ * call.  It holds the chunk's V^T and, when B * heads query tiles would leave compute units idle, room
+ * for up to 16 key splits.  The call then attends each split in its own workgroups and merges them as
+ * wan_attention_lse_merge does (every split holds >= 256 keys).  A workspace holding only V^T
+ * (B * heads * head_dim * round_up(Sk, 64) dtype elements) runs unsplit; smaller is WAN_EWORKSPACE.
  *
  * wan_attention_lse_merge: combines n_parts (1..16) results for the same queries over disjoint key
  * chunks: lse = ln sum_n exp(lse_parts[n]); o = sum_n exp(lse_parts[n] - lse) * o_parts[n], which is
  * attention over the union of the chunks.  o_parts and lse_parts are HOST arrays of n_parts device
  * pointers ([B, S, heads, head_dim] dtype and [B, heads, S] float32); o has o_parts' layout; lse
  * (NULL = not written) has lse_parts' layout.  Outputs must not alias the inputs. */
-size_t wan_attention_partial_workspace_bytes(int32_t dtype, int32_t B, int32_t Sk, int32_t heads, int32_t head_dim);
+size_t wan_attention_partial_workspace_bytes(int32_t dtype, int32_t B, int32_t Sq, int32_t Sk, int32_t heads,
+                                             int32_t head_dim);
 int wan_attention_partial_fwd(int32_t dtype, const void* q, const void* k, const void* v, int32_t B, int32_t Sq,
                               int32_t Sk, int32_t heads, int32_t head_dim, void* o, float* lse, void* ws,
                               size_t ws_bytes, wan_stream_t stream);

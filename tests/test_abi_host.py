@@ -149,8 +149,12 @@ def test_other_entry_validation(lib):
 
 
 def test_ring_attention_validation(lib):
-    need = lib.wan_attention_partial_workspace_bytes(L.WAN_BF16, 1, 100, 2, 64)
-    assert need >= 2 * 64 * 128 * 2  # V^T of 100 keys padded to 128
+    need = lib.wan_attention_partial_workspace_bytes(L.WAN_BF16, 1, 50, 100, 2, 64)
+    assert need == 2 * 64 * 128 * 2  # V^T of 100 keys padded to 128; too few keys to split
+    # two query tiles against 4096 keys leave the chip idle: the workspace adds key-split parts
+    vt = 2 * 64 * 4096 * 2
+    assert lib.wan_attention_partial_workspace_bytes(L.WAN_BF16, 1, 300, 4096, 2, 64) > vt
+    assert lib.wan_attention_partial_workspace_bytes(L.WAN_BF16, 1, 300, 0, 2, 64) == 0
     args = lambda **kw: dict(dict(dt=L.WAN_BF16, B=1, Sq=50, Sk=100, H=2, hd=64, lse=FAKE, ws=need), **kw)
 
     def part(a):

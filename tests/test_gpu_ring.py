@@ -36,12 +36,19 @@ def _qkv(rng, B, Sq, Sk, H, hd, dtype):
     return q, k, v
 
 
-def _partial(qd, kd, vd, want_lse=True):
+def _vt_bytes(qd, kd):
+    B, _, H, hd = qd.shape
+    return B * H * hd * (-(-kd.shape[1] // 64) * 64) * qd.element_size()
+
+
+def _partial(qd, kd, vd, want_lse=True, unsplit=False):
+    """The chunk attention with the workspace the library asks for (key splits where the grid would
+    leave compute units idle), or, with unsplit, a workspace holding only V^T."""
     B, Sq, H, hd = qd.shape
     o = torch.empty_like(qd)
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device="cuda") if want_lse else None
-    ws = torch.empty(L.attention_partial_ws_bytes(L.dtype_code(qd.dtype), B, kd.shape[1], H, hd),
-                     dtype=torch.uint8, device="cuda")
+    n = _vt_bytes(qd, kd) if unsplit else L.attention_partial_ws_bytes(L.dtype_code(qd.dtype), B, Sq, kd.shape[1], H, hd)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
     L.attention_partial_fwd(qd, kd, vd, o, lse, ws)
     return o, lse
 
@@ -88,6 +95,30 @@ def test_chunks_merge_small(dtype, hd):
     # without the lse output the chunk result is the same attention
     o2, _ = _partial(qd, dev(k[:, 17:145], td), dev(v[:, 17:145], td), want_lse=False)
     assert torch.equal(o2, parts[1])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("hd", [64, 128])
+def test_partial_key_splits_small(dtype, hd):
+    """A grid of one or two query tiles against 3000 keys: the library splits the keys (the last
+    split ragged) and merges; every element of o and lse against the oracle, with and without the lse
+    output, and against the unsplit call (V^T-only workspace)."""
+    require_gpu()
+    B, Sq, Sk, H = 1, 200, 3000, 2
+    case(f"partial key splits dtype={dtype} hd={hd} Sq={Sq} Sk={Sk}")
+    rng = np.random.default_rng(900 + hd)
+    q, k, v = _qkv(rng, B, Sq, Sk, H, hd, dtype)
+    td = _tdt(dtype)
+    qd, kd, vd = dev(q, td), dev(k, td), dev(v, td)
+    assert L.attention_partial_ws_bytes(L.dtype_code(td), B, Sq, Sk, H, hd) > _vt_bytes(qd, kd)  # split taken
+    o, lse = _partial(qd, kd, vd)
+    rows = np.arange(Sq)
+    _check_rows(host(o), host(lse), q, k, v, rows, dtype)
+    o2, _ = _partial(qd, kd, vd, want_lse=False)
+    assert torch.equal(o2, o)
+    o1, lse1 = _partial(qd, kd, vd, unsplit=True)
+    _check_rows(host(o1), host(lse1), q, k, v, rows, dtype)
+    assert rel_l2(host(o), host(o1)) <= TOL[dtype]
 
 
 def test_merge_single_part_is_identity():

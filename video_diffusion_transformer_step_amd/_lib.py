@@ -85,7 +85,8 @@ _SIGS = {
     "wan_attention_workspace_bytes": ([C.c_int32, Grid, C.c_int32, C.c_int32, C.c_int32], C.c_size_t),
     "wan_attention_fwd": ([C.c_int32, vp, vp, vp, Grid, C.c_int32, C.c_int32, C.c_int32, C.c_float, vp, vp,
                            C.c_size_t, vp], C.c_int),
-    "wan_attention_partial_workspace_bytes": ([C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32], C.c_size_t),
+    "wan_attention_partial_workspace_bytes": ([C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32],
+                                              C.c_size_t),
     "wan_attention_partial_fwd": ([C.c_int32, vp, vp, vp, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, vp,
                                    vp, vp, C.c_size_t, vp], C.c_int),
     "wan_attention_lse_merge": ([C.c_int32, C.c_int32, C.POINTER(C.c_void_p), C.POINTER(C.c_void_p), C.c_int32,
@@ -275,8 +276,8 @@ def attention_fwd(q, k, v, grid, o, ws, rope_theta=10000.0, stream=None):
                                    _stream(stream)), "wan_attention_fwd")
 
 
-def attention_partial_ws_bytes(dtype, B, Sk, heads, head_dim):
-    return lib().wan_attention_partial_workspace_bytes(dtype, B, Sk, heads, head_dim)
+def attention_partial_ws_bytes(dtype, B, Sq, Sk, heads, head_dim):
+    return lib().wan_attention_partial_workspace_bytes(dtype, B, Sq, Sk, heads, head_dim)
 
 
 def attention_partial_fwd(q, k, v, o, lse, ws, stream=None):

@@ -611,6 +611,23 @@ __device__ __forceinline__ void attn_tile_coords(int& qt, int& h, int& b) {
   b = t / (nq * nh);
 }
 
+// Key split: grid batch entry b = row * n + i becomes batch row `row` attending to keys
+// [i * chunk, min((i + 1) * chunk, L)) of stream s, with o and lse moved to part i.  chunk is a multiple
+// of the 64-key tile, so every part but the last ends on a whole tile and the bf16 V^T key permutation
+// (within 16-key groups) is undisturbed.
+template <typename T>
+__device__ __forceinline__ void apply_key_split(const KeySplit& ks, int& b, KVStream& s, T* __restrict__& out,
+                                                float* __restrict__& lse) {
+  const int i = b % ks.n;
+  b /= ks.n;
+  const int key0 = i * ks.chunk;
+  s.k = reinterpret_cast<const T*>(s.k) + (int64_t)key0 * s.k_ss;
+  s.vt = reinterpret_cast<const T*>(s.vt) + key0;
+  s.L = min(ks.chunk, s.L - key0);
+  out += (int64_t)i * ks.o_stride;
+  if (lse != nullptr) lse += (int64_t)i * ks.lse_stride;
+}
+
 // Normalise one stream's O^T by its row sums and add it into acc (first stream: assign).
 template <typename T, int HD>
 __device__ __forceinline__ void finish_stream(int si, const f32x16 (&o)[AttnCfg<T, HD>::ND], const SoftState& st,
@@ -671,13 +688,14 @@ template <typename T, int HD, int NS, int KIND>
 __global__ __launch_bounds__(256, 2) void attention_kernel(const T* __restrict__ q, int64_t q_bs, int64_t q_ss,
                                                             KVStream s0, KVStream s1, int S, int H, float c_log2,
                                                             T* __restrict__ out, int64_t o_bs, int64_t o_ss,
-                                                            float* __restrict__ lse) {
+                                                            float* __restrict__ lse, KeySplit ks) {
   using C = AttnCfg<T, HD>;
   __shared__ u32x4 k0_raw[C::KBYTES / 16], k1_raw[C::KBYTES / 16], v0_raw[C::VBYTES / 16], v1_raw[C::VBYTES / 16];
   const Slots<T, HD> sl{reinterpret_cast<char*>(k0_raw), reinterpret_cast<char*>(k1_raw),
                         reinterpret_cast<char*>(v0_raw), reinterpret_cast<char*>(v1_raw)};
   int qt, h, b;
   attn_tile_coords(qt, h, b);
+  if (ks.n > 1) apply_key_split<T>(ks, b, s0, out, lse);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int qrow = qt * 128 + wave * 32 + (lane & 31);
   const FragAddr<T, HD> fa;
@@ -806,13 +824,14 @@ template <typename T, int HD, int NS, int KIND>
 __global__ __launch_bounds__(512, 1) void attention_pp_kernel(const T* __restrict__ q, int64_t q_bs, int64_t q_ss,
                                                                KVStream s0, KVStream s1, int S, int H, float c_log2,
                                                                T* __restrict__ out, int64_t o_bs, int64_t o_ss,
-                                                               float* __restrict__ lse) {
+                                                               float* __restrict__ lse, KeySplit ks) {
   using C = AttnCfg<T, HD>;
   __shared__ u32x4 k0_raw[C::KBYTES / 16], k1_raw[C::KBYTES / 16], v0_raw[C::VBYTES / 16], v1_raw[C::VBYTES / 16];
   const Slots<T, HD> sl{reinterpret_cast<char*>(k0_raw), reinterpret_cast<char*>(k1_raw),
                         reinterpret_cast<char*>(v0_raw), reinterpret_cast<char*>(v1_raw)};
   int qt, h, b;
   attn_tile_coords(qt, h, b);
+  if (ks.n > 1) apply_key_split<T>(ks, b, s0, out, lse);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = wave >> 2;
@@ -1156,23 +1175,24 @@ hipError_t launch_q8_hd(const uint8_t* q, int64_t q_bs, int64_t q_ss, const floa
 // hundred keys, where the per-stream prologue dominates) and fp32 use the four-wave kernel.
 template <typename T, int HD, int KIND>
 hipError_t launch_hd(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0, KVStream s1, int nstreams, int B, int S,
-                     int H, float c_log2, T* o, int64_t o_bs, int64_t o_ss, float* lse, hipStream_t s) {
+                     int H, float c_log2, T* o, int64_t o_bs, int64_t o_ss, float* lse, const KeySplit& ks,
+                     hipStream_t s) {
   if constexpr (sizeof(T) == 2 && WAN_ATTN_PP && KIND == 0) {
-    dim3 grid((unsigned)ceil_div(S, 256), (unsigned)H, (unsigned)B);
+    dim3 grid((unsigned)ceil_div(S, 256), (unsigned)H, (unsigned)(B * ks.n));
     if (nstreams == 2)
       hipLaunchKernelGGL((attention_pp_kernel<T, HD, 2, KIND>), grid, dim3(512), 0, s, q, q_bs, q_ss, s0, s1, S, H,
-                         c_log2, o, o_bs, o_ss, lse);
+                         c_log2, o, o_bs, o_ss, lse, ks);
     else
       hipLaunchKernelGGL((attention_pp_kernel<T, HD, 1, KIND>), grid, dim3(512), 0, s, q, q_bs, q_ss, s0, s1, S, H,
-                         c_log2, o, o_bs, o_ss, lse);
+                         c_log2, o, o_bs, o_ss, lse, ks);
   } else {
-    dim3 grid((unsigned)ceil_div(S, 128), (unsigned)H, (unsigned)B);
+    dim3 grid((unsigned)ceil_div(S, 128), (unsigned)H, (unsigned)(B * ks.n));
     if (nstreams == 2)
       hipLaunchKernelGGL((attention_kernel<T, HD, 2, KIND>), grid, dim3(256), 0, s, q, q_bs, q_ss, s0, s1, S, H,
-                         c_log2, o, o_bs, o_ss, lse);
+                         c_log2, o, o_bs, o_ss, lse, ks);
     else
       hipLaunchKernelGGL((attention_kernel<T, HD, 1, KIND>), grid, dim3(256), 0, s, q, q_bs, q_ss, s0, s1, S, H,
-                         c_log2, o, o_bs, o_ss, lse);
+                         c_log2, o, o_bs, o_ss, lse, ks);
   }
   return hipGetLastError();
 }
@@ -1182,20 +1202,23 @@ hipError_t launch_hd(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0, KVStre
 template <typename T>
 hipError_t launch_attention(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0, KVStream s1, int nstreams, int B,
                             int S, int H, int hd, float scale, T* o, int64_t o_bs, int64_t o_ss, int kind,
-                            hipStream_t s, float* lse) {
+                            hipStream_t s, float* lse, KeySplit ks) {
   if (S <= 0 || B <= 0 || H <= 0) return hipSuccess;
   if (nstreams < 1 || nstreams > 2) return hipErrorInvalidValue;
   if (s0.L <= 0 || s0.Lpad % KT != 0 || s0.Lpad < s0.L) return hipErrorInvalidValue;
   if (nstreams == 2 && (s1.L <= 0 || s1.Lpad % KT != 0 || s1.Lpad < s1.L)) return hipErrorInvalidValue;
   if (nstreams == 2 && lse != nullptr) return hipErrorInvalidValue;  // one normaliser per stream
+  if (ks.n < 1 || (int64_t)B * ks.n > 65535) return hipErrorInvalidValue;
+  if (ks.n > 1 && (nstreams != 1 || ks.chunk <= 0 || ks.chunk % KT != 0 || (int64_t)(ks.n - 1) * ks.chunk >= s0.L))
+    return hipErrorInvalidValue;
   const float c_log2 = scale * 1.4426950408889634f;
   if (hd == 128) {
-    if (kind) return launch_hd<T, 128, 1>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, s);
-    return launch_hd<T, 128, 0>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, s);
+    if (kind) return launch_hd<T, 128, 1>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, ks, s);
+    return launch_hd<T, 128, 0>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, ks, s);
   }
   if (hd == 64) {
-    if (kind) return launch_hd<T, 64, 1>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, s);
-    return launch_hd<T, 64, 0>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, s);
+    if (kind) return launch_hd<T, 64, 1>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, ks, s);
+    return launch_hd<T, 64, 0>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, ks, s);
   }
   return hipErrorInvalidValue;
 }
@@ -1313,8 +1336,21 @@ template hipError_t launch_lse_merge<bf16>(const void* const*, const float* cons
                                            float*, hipStream_t);
 
 template hipError_t launch_attention<float>(const float*, int64_t, int64_t, KVStream, KVStream, int, int, int, int,
-                                            int, float, float*, int64_t, int64_t, int, hipStream_t, float*);
+                                            int, float, float*, int64_t, int64_t, int, hipStream_t, float*, KeySplit);
 template hipError_t launch_attention<bf16>(const bf16*, int64_t, int64_t, KVStream, KVStream, int, int, int, int,
-                                           int, float, bf16*, int64_t, int64_t, int, hipStream_t, float*);
+                                           int, float, bf16*, int64_t, int64_t, int, hipStream_t, float*, KeySplit);
+
+template <typename T>
+void attention_tile(int kind, int& rows, int& per_cu) {
+  if (sizeof(T) == 2 && WAN_ATTN_PP && kind == 0) {
+    rows = 256;  // ping-pong kernel: 8 waves, one workgroup per compute unit
+    per_cu = 1;
+  } else {
+    rows = 128;  // four-wave kernel, __launch_bounds__(256, 2)
+    per_cu = 2;
+  }
+}
+template void attention_tile<float>(int, int&, int&);
+template void attention_tile<bf16>(int, int&, int&);
 
 }  // namespace wan

@@ -7,6 +7,7 @@
 
 #include "wan.h"
 #include <algorithm>
+#include <atomic>
 
 #include "wan_internal.h"
 
@@ -639,23 +640,118 @@ int wan_attention_fwd(int32_t dtype, const void* q, const void* k, const void* v
                             (float*)o, ws, hs(stream));
 }
 
-size_t wan_attention_partial_workspace_bytes(int32_t dtype, int32_t B, int32_t Sk, int32_t heads, int32_t head_dim) {
-  if ((dtype != WAN_F32 && dtype != WAN_BF16) || B <= 0 || Sk <= 0 || heads <= 0 || head_dim <= 0) return 0;
-  return a256((size_t)B * heads * head_dim * pad64(Sk) * esize(dtype));
+namespace {
+
+// Compute units of the current device, queried once per device (256 when no device answers).
+int device_compute_units() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
 
+// Key split of a partial attention whose grid would leave compute units idle: n parts of `chunk` keys
+// (a multiple of 64, at least 256).  Cost in units of one workgroup's 64-key tile:
+//   rounds(n) * (tiles(n) + SPLIT_FIXED_TILES) + merge(n),
+// rounds = ceil(nwg * n / resident slots), tiles = chunk / 64, SPLIT_FIXED_TILES the per-workgroup
+// start and finish (Q load, first tiles, normalisation, store), and merge = the (n + 1) o-part passes
+// of the merge at HBM speed over the time of one tile.  Workspace layout: V^T, then n o-parts
+// [B, Sq, H, hd] and n lse-parts [B, H, Sq], each 256-byte aligned.
+constexpr double SPLIT_FIXED_TILES = 8.0;
+constexpr double SPLIT_CU_FLOPS = 4.9e12;   // one compute unit's bf16 attention rate (flop/s)
+constexpr double SPLIT_MERGE_BW = 4.5e12;   // the merge's bandwidth (B/s)
+struct PartialPlan {
+  int n = 1, chunk = 0;
+  size_t vt_bytes = 0, o_part_bytes = 0, lse_part_bytes = 0, bytes = 0;
+};
+
+PartialPlan partial_plan(int32_t dtype, int B, int Sq, int Sk, int H, int hd) {
+  PartialPlan p;
+  const size_t es = esize(dtype);
+  p.vt_bytes = a256((size_t)B * H * hd * pad64(Sk) * es);
+  p.bytes = p.vt_bytes;
+  p.chunk = (int)pad64(Sk);
+  int rows = 0, per_cu = 0;
+  if (dtype == WAN_BF16)
+    attention_tile<bf16>(0, rows, per_cu);
+  else
+    attention_tile<float>(0, rows, per_cu);
+  const int64_t nwg = ceil_div((int64_t)Sq, (int64_t)rows) * H * B;
+  const int64_t slots = (int64_t)device_compute_units() * per_cu;
+  const double tile_s = (double)rows * 64 * hd * 4 / SPLIT_CU_FLOPS;
+  const double part_tiles = (double)B * Sq * H * hd * es / SPLIT_MERGE_BW / tile_s;
+  double best = (double)ceil_div(nwg, slots) * ((double)ceil_div((int64_t)Sk, (int64_t)64) + SPLIT_FIXED_TILES);
+  for (int n = 2; n <= MERGE_MAX_PARTS && (int64_t)B * n <= 65535; ++n) {
+    const int chunk = (int)pad64(ceil_div((int64_t)Sk, (int64_t)n));
+    if (chunk < 256 || (int64_t)(n - 1) * chunk >= Sk) continue;
+    const double cost = (double)ceil_div(nwg * n, slots) * (chunk / 64 + SPLIT_FIXED_TILES) + (n + 1) * part_tiles;
+    if (cost < best - 1e-9) {
+      best = cost;
+      p.n = n;
+      p.chunk = chunk;
+    }
+  }
+  if (p.n > 1) {
+    p.o_part_bytes = a256((size_t)B * Sq * H * hd * es);
+    p.lse_part_bytes = a256((size_t)B * H * Sq * 4);
+    p.bytes += (size_t)p.n * (p.o_part_bytes + p.lse_part_bytes);
+  }
+  return p;
+}
+
+}  // namespace
+
+size_t wan_attention_partial_workspace_bytes(int32_t dtype, int32_t B, int32_t Sq, int32_t Sk, int32_t heads,
+                                             int32_t head_dim) {
+  if ((dtype != WAN_F32 && dtype != WAN_BF16) || B <= 0 || Sq <= 0 || Sk <= 0 || heads <= 0 || head_dim <= 0) return 0;
+  return partial_plan(dtype, B, Sq, Sk, heads, head_dim).bytes;
+}
+
+namespace {
+
 template <typename T>
-static int attention_partial_t(const T* q, const T* k, const T* v, int B, int Sq, int Sk, int H, int hd, T* o,
-                               float* lse, void* ws, hipStream_t st) {
+int attention_partial_t(const T* q, const T* k, const T* v, int B, int Sq, int Sk, int H, int hd, T* o, float* lse,
+                        void* ws, size_t ws_bytes, hipStream_t st) {
   const int64_t dim = (int64_t)H * hd;
   const int Skpad = (int)pad64(Sk);
   T* vt = reinterpret_cast<T*>(ws);
   HIP_TRY(launch_transpose_heads<T>(v, dim, 0, B, Sk, H, hd, Skpad, vt, st));
   KVStream s0{k, (int64_t)Sk * dim, dim, vt, Sk, Skpad};
-  HIP_TRY(launch_attention<T>(q, (int64_t)Sq * dim, dim, s0, s0, 1, B, Sq, H, hd, 1.f / sqrtf((float)hd), o,
-                              (int64_t)Sq * dim, dim, 0, st, lse));
+  const float scale = 1.f / sqrtf((float)hd);
+  const PartialPlan p = partial_plan(sizeof(T) == 2 ? WAN_BF16 : WAN_F32, B, Sq, Sk, H, hd);
+  if (p.n == 1 || ws_bytes < p.bytes) {  // unsplit (also when the workspace holds only V^T)
+    HIP_TRY(launch_attention<T>(q, (int64_t)Sq * dim, dim, s0, s0, 1, B, Sq, H, hd, scale, o, (int64_t)Sq * dim, dim,
+                                0, st, lse));
+    return WAN_OK;
+  }
+  char* base = reinterpret_cast<char*>(ws) + p.vt_bytes;
+  T* o_parts = reinterpret_cast<T*>(base);
+  float* l_parts = reinterpret_cast<float*>(base + (size_t)p.n * p.o_part_bytes);
+  KeySplit ks;
+  ks.n = p.n;
+  ks.chunk = p.chunk;
+  ks.o_stride = (int64_t)(p.o_part_bytes / sizeof(T));
+  ks.lse_stride = (int64_t)(p.lse_part_bytes / 4);
+  HIP_TRY(launch_attention<T>(q, (int64_t)Sq * dim, dim, s0, s0, 1, B, Sq, H, hd, scale, o_parts, (int64_t)Sq * dim,
+                              dim, 0, st, l_parts, ks));
+  const void* op[MERGE_MAX_PARTS];
+  const float* lp[MERGE_MAX_PARTS];
+  for (int i = 0; i < p.n; ++i) {
+    op[i] = o_parts + i * ks.o_stride;
+    lp[i] = l_parts + i * ks.lse_stride;
+  }
+  HIP_TRY(launch_lse_merge<T>(op, lp, p.n, B, Sq, H, hd, o, lse, st));
   return WAN_OK;
 }
+
+}  // namespace
 
 int wan_attention_partial_fwd(int32_t dtype, const void* q, const void* k, const void* v, int32_t B, int32_t Sq,
                               int32_t Sk, int32_t heads, int32_t head_dim, void* o, float* lse, void* ws,
@@ -670,14 +766,14 @@ int wan_attention_partial_fwd(int32_t dtype, const void* q, const void* k, const
   WAN_TRY(need_ptr(v, "v"));
   WAN_TRY(need_ptr(o, "o"));
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3)) return fail(WAN_EINVAL, "lse is not 4-byte aligned");
-  const size_t need = wan_attention_partial_workspace_bytes(dtype, B, Sk, heads, head_dim);
+  const size_t need = a256((size_t)B * heads * head_dim * pad64(Sk) * esize(dtype));  // V^T: the unsplit minimum
   if (ws_bytes < need) return fail(WAN_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   WAN_TRY(need_ptr(ws, "ws"));
   if (dtype == WAN_BF16)
     return attention_partial_t<bf16>((const bf16*)q, (const bf16*)k, (const bf16*)v, B, Sq, Sk, heads, head_dim,
-                                     (bf16*)o, lse, ws, hs(stream));
+                                     (bf16*)o, lse, ws, ws_bytes, hs(stream));
   return attention_partial_t<float>((const float*)q, (const float*)k, (const float*)v, B, Sq, Sk, heads, head_dim,
-                                    (float*)o, lse, ws, hs(stream));
+                                    (float*)o, lse, ws, ws_bytes, hs(stream));
 }
 
 int wan_attention_lse_merge(int32_t dtype, int32_t n_parts, const void* const* o_parts, const float* const* lse_parts,

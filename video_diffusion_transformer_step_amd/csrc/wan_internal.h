@@ -109,12 +109,24 @@ struct KVStream {
   const void* vt;
   int L, Lpad;
 };
+// Key split (one stream only): the grid runs B * n batch entries; entry b * n + i attends the queries
+// of batch row b to keys [i * chunk, min((i + 1) * chunk, L)) and writes its o at o + i * o_stride and
+// its lse at lse + i * lse_stride, to be combined by launch_lse_merge.  chunk is a multiple of 64 and
+// (n - 1) * chunk < L.  n == 1 (the default) is the plain attention.
+struct KeySplit {
+  int n = 1, chunk = 0;
+  int64_t o_stride = 0, lse_stride = 0;
+};
+// Query rows per workgroup of the kernel launch_attention picks for (T, kind), and how many such
+// workgroups one compute unit holds at once.
+template <typename T>
+void attention_tile(int kind, int& rows, int& per_cu);
 // kind: 0 self-attention, 1 cross-attention (separate kernel symbols).  lse (one stream only; NULL = not
 // written): [B, H, S] float32, the natural log of each query row's softmax normaliser.
 template <typename T>
 hipError_t launch_attention(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0, KVStream s1, int nstreams, int B,
                             int S, int H, int hd, float scale, T* o, int64_t o_bs, int64_t o_ss, int kind,
-                            hipStream_t s, float* lse = nullptr);
+                            hipStream_t s, float* lse = nullptr, KeySplit ks = KeySplit{});
 
 // Quantised attention (INT8 Q.K, FP8 P.V): q8 [B, S, H, hd] INT8 codes with sq [B, H, S]; k8 [B, L, H, hd]
 // INT8 codes with sk [B, H, ceil(L / 64)]; v8t [B, H, hd, round_up(L, 128)] E4M3 codes (keys in P.V
