@@ -150,6 +150,24 @@ def test_block_independent_of_workspace_contents(name, over, fp8):
         _check(c, outs[1], ref, x, tol=None if fp8 == "bf16" else (FP8_TOL if fp8 == "fp8_attn" else FP8_ALL_TOL))
 
 
+def test_block_max_dim():
+    """The widest block the boundary accepts: dim 6144 = 48 heads x 128, bf16, 6 tokens, 16 text keys.
+    The norms hold 96 values of a row per lane and the GEMMs run N up to 18432 and K 6144; every
+    element is compared.  e0 and the text embedding are drawn directly: the time and text MLPs at this
+    width are not under test here."""
+    require_gpu()
+    c = wi.get_config("tiny").replace(name="max-dim-6144-block-bf16", dtype="bf16", dim=6144, heads=48,
+                                      head_dim=128, ffn_dim=512, text_len=16, T=1, H=4, W=6, img_len=0)
+    case(f"block max dim {c.dim} S={c.S}")
+    bw = wi.make_block_weights(c, 0, seed=13)
+    x = wi.normal(13, c, "x_block", (c.B, c.S, c.dim), quantize=False)
+    e0 = wi.normal(13, c, "e0", (c.B, 6, c.dim), std=0.5, quantize=False)
+    t_emb = wi.normal(13, c, "t_emb", (c.B, c.text_len, c.dim))
+    got, = _gpu_block(c, x, e0, t_emb, None, bw)
+    ref = _oracle_block(c, x, e0, t_emb, None, bw)
+    _check(c, got, ref, x)
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["t2v-1.3b", "ti2v-5b", pytest.param("i2v-14b", marks=pytest.mark.slow)])
 def test_block_full_size_sampled_rows(name):

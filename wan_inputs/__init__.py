@@ -107,6 +107,8 @@ TENSOR_IDS = {name: i for i, name in enumerate([
     # activations / inputs
     "x_t", "z_img", "ctx_txt", "ctx_txt_uncond", "ctx_img", "x_block",
     "q", "k", "v", "v_cond", "v_uncond", "x0", "x1", "rows",
+    # drawn directly where the producing MLP is not under test (appended: earlier ids are unchanged)
+    "e0", "t_emb",
 ])}
 
 # Which per-block tensors are weight matrices (bf16 operands in bf16 mode).
