@@ -196,3 +196,21 @@ def test_cross_kv_buffer_sizes(lib):
     assert lib.wan_cross_kv_buffer_bytes(C.byref(c), 2, 0) == 2 * 512 * 5120 * 2
     assert lib.wan_cross_kv_buffer_bytes(C.byref(c), 2, 1) == 2 * 5120 * 512 * 2
     assert lib.wan_cross_kv_buffer_bytes(C.byref(c), 2, 3) == 2 * 5120 * 320 * 2  # 257 -> 320 (64-padded)
+
+
+def test_missing_library_fails_loudly():
+    """Without libwan.so the binding raises; nothing falls back to another implementation."""
+    import subprocess
+    import sys
+    code = ("import video_diffusion_transformer_step_amd._lib as L\n"
+            "L.LIB_PATH = '/nonexistent/libwan.so'\n"
+            "L._lib = None\n"
+            "try:\n"
+            "    L.lib()\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n"
+            "else:\n"
+            "    raise SystemExit('no error')\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert "raised:" in r.stdout and "libwan.so" in r.stdout

@@ -84,6 +84,26 @@ def test_time_embed(cfg_name, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_time_embed_max_batch(dtype):
+    """The largest batch wan_time_embed takes (B = 4) with the schedule's end points t = 1 and t = 0
+    among the rows; each row against the oracle."""
+    require_gpu()
+    c = wi.get_config("tiny").replace(dtype=dtype)
+    case(f"time_embed B=4 {dtype}")
+    mw = wi.make_model_weights(c, seed=4)
+    model = R.DeviceModel(mw, dtype)
+    ts = [1.0, 0.75, 0.0, 0.3]
+    e = torch.empty((4, c.dim), dtype=torch.float32, device="cuda")
+    e0 = torch.empty((4, 6, c.dim), dtype=torch.float32, device="cuda")
+    L.time_embed(R.cfg_of(c), c.freq_dim, model.tw, ts, e, e0)
+    ge, ge0 = host(e), host(e0)
+    for b, t in enumerate(ts):
+        re, re0 = oracle.time_embed(t, mw, c.freq_dim)
+        assert rel_l2(ge[b], re) <= TOL[dtype] * 0.1, (t, rel_l2(ge[b], re))
+        assert rel_l2(ge0[b], re0) <= TOL[dtype] * 0.1, (t, rel_l2(ge0[b], re0))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_context_embed_and_cross_kv(dtype):
     require_gpu()
     c = wi.get_config("tiny").replace(dtype=dtype, img_len=9, img_dim=32)
