@@ -121,6 +121,31 @@ def test_partial_key_splits_small(dtype, hd):
     assert rel_l2(host(o), host(o1)) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("hd", [64, 128])
+def test_attention_sharp_drifting_scores(dtype, hd):
+    """Sharp, drifting softmax rows: q and k scaled by 4 and each key's norm growing along the
+    sequence (x1 to x4), so scores reach hundreds and the row maximum keeps rising from tile to tile.
+    The running maximum then moves (O and l rescaled, weights recomputed) on many tiles rather than on
+    the first only.  Every element of o and lse against the oracle, unsplit and with key splits."""
+    require_gpu()
+    B, Sq, Sk, H = 1, 300, 2000, 2
+    case(f"sharp drifting scores dtype={dtype} hd={hd}")
+    rng = np.random.default_rng(1200 + hd)
+    q = 4.0 * rng.standard_normal((B, Sq, H, hd)).astype(np.float32)
+    grow = (1.0 + 3.0 * np.arange(Sk) / (Sk - 1)).astype(np.float32)[None, :, None, None]
+    k = (4.0 * rng.standard_normal((B, Sk, H, hd)) * grow).astype(np.float32)
+    v = rng.standard_normal((B, Sk, H, hd)).astype(np.float32)
+    if dtype == "bf16":
+        q, k, v = wi.bf16_round(q), wi.bf16_round(k), wi.bf16_round(v)
+    td = _tdt(dtype)
+    qd, kd, vd = dev(q, td), dev(k, td), dev(v, td)
+    rows = np.arange(Sq)
+    for unsplit in (True, False):
+        o, lse = _partial(qd, kd, vd, unsplit=unsplit)
+        _check_rows(host(o), host(lse), q, k, v, rows, dtype)
+
+
 def test_merge_single_part_is_identity():
     """One part merges to itself (weights exp(lse - lse) = 1)."""
     require_gpu()
