@@ -371,6 +371,8 @@ def main():
                     help="skip the diffusion-cache measurement (attention-output and CFG reuse)")
     ap.add_argument("--no-two-expert", action="store_true",
                     help="skip the two-expert (high-noise / low-noise DiT) sampling measurement")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture each timed step as a HIP graph beforehand and replay it (launch-bound small shapes)")
     ap.add_argument("--no-sharded", action="store_true",
                     help="skip the one-GPU shares of sequence-parallel attention (Ulysses head shard, ring step, merge)")
     ap.add_argument("--no-device-probe", action="store_true",
@@ -433,7 +435,14 @@ def main():
         torch.cuda.synchronize()
         log(f"warmup step {k} done")
 
+    graphs = None
+    if args.graph:  # one captured step per timed step (t differs per step); capturing runs nothing
+        graphs = [R.StepGraph(c, model, blocks, caches, xg, zg, 1.0 + (args.warmup + k) * dt, dt, c.guidance, buf,
+                              c.B) for k in range(args.steps)]
+        log(f"captured {len(graphs)} step graphs")
+
     # ---- timed region: K steps; self-attention launches bracketed by HIP events on their stream
+    # (kernel events are recorded only for eager launches; a replayed graph is timed as a whole)
     timer = L.KernelTimer(capacity=args.steps * layers, kernels=("self_attn",))
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -441,13 +450,21 @@ def main():
     ev0.record()
     with timer:
         for k in range(args.steps):
-            step(args.warmup + k)
+            if graphs is not None:
+                graphs[k].replay()
+            else:
+                step(args.warmup + k)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     gpu_ms_per_step = ev0.elapsed_time(ev1) / args.steps
     attn_ms = timer.times_ms().get("self_attn", [])
+    if not attn_ms:  # graph replays record no kernel events: time the launches in one extra eager step
+        t_one = L.KernelTimer(capacity=layers, kernels=("self_attn",))
+        with t_one:
+            step(args.warmup + args.steps)
+        attn_ms = t_one.times_ms().get("self_attn", [])
     attn_avg = float(np.mean(attn_ms)) if attn_ms else float("nan")
     log(f"timed {args.steps} steps: {ms_per_step:.2f} ms/step (events {gpu_ms_per_step:.2f}); "
         f"self-attention {attn_avg:.3f} ms/launch over {len(attn_ms)} launches")
@@ -586,7 +603,7 @@ def main():
                                 f"[{c.latent_channels},{c.T},{c.H},{c.W}] -> {c.S} tokens, {layers} blocks"),
                    "global_batch": c.B, "seq_len": c.S, "layers": layers, "dim": c.dim, "heads": c.heads,
                    "head_dim": c.head_dim, "ffn_dim": c.ffn_dim, "text_len": c.text_len,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", "launch": "hip graph per step" if args.graph else "eager"},
         "ms_per_block": round(ms_per_step / layers, 3),
         "step_tflops": round(step_tflops, 1),
         "step_frac_of_bf16_peak": round(step_tflops / PEAK_BF16_TFLOPS, 4),

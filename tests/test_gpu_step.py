@@ -104,3 +104,42 @@ def test_step_ti2v_shaped_reduced_chain():
     case("step TI2V-shaped reduced chain")
     x_t, gt, ot = _run(c, layers=3, steps=4, t0=1.0)
     _check(c, x_t, gt, ot)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_step_graph_replays_match_eager(dtype):
+    """A captured step (runtime.StepGraph, CFG pair, I2V) replayed three times, with eager library work,
+    a torch copy and a synchronisation between the replays: every replay equals the eager step bit for
+    bit (same kernels, same inputs)."""
+    require_gpu()
+    c = wi.get_config("tiny").replace(dtype=dtype, B=2, img_len=5, img_dim=32, guidance=5.0)
+    case(f"step graph replays {dtype}")
+    mw = wi.make_model_weights(c, seed=9)
+    bws = [wi.make_block_weights(c, i, seed=9) for i in range(2)]
+    x_t, z = wi.make_latents(c, seed=9)
+    txt, img = wi.make_contexts(c, seed=9)
+    model = R.DeviceModel(mw, c.dtype)
+    blocks = [R.DeviceBlock(w, c.dtype) for w in bws]
+    t_emb, i_emb = R.embed_contexts(c, model, txt, img, c.B)
+    caches = R.cross_kv_all(c, blocks, t_emb, i_emb, c.B)
+    zg = dev(z)
+    x0 = dev(x_t)
+    # eager reference, on its own buffers
+    buf_e = R.alloc_step(c, c.B)
+    x_e = x0.clone()
+    R.denoise_step(c, model, blocks, caches, x_e, zg, 0.75, -0.25, c.guidance, buf_e, c.B)
+    ref = host(x_e)
+    # captured step
+    buf_g = R.alloc_step(c, c.B)
+    x_g = x0.clone()
+    g = R.StepGraph(c, model, blocks, caches, x_g, zg, 0.75, -0.25, c.guidance, buf_g, c.B)
+    assert np.array_equal(host(x_g), x_t.astype(np.float32))  # capturing ran nothing
+    for r in range(3):
+        x_g.copy_(x0)
+        g.replay()
+        got = host(x_g)
+        assert np.array_equal(got, ref), (r, float(np.abs(got - ref).max()))
+        # eager work between replays, on the eager buffers
+        x_e.copy_(x0)
+        R.denoise_step(c, model, blocks, caches, x_e, zg, 0.5, -0.25, c.guidance, buf_e, c.B)
+        torch.cuda.synchronize()

@@ -219,6 +219,25 @@ def denoise_step(c, model, blocks, caches, x_latent, z_img, t, dt, guidance, buf
     return x_latent
 
 
+class StepGraph:
+    """One denoise_step captured as a HIP graph (torch.cuda.CUDAGraph) and replayed with one call.
+
+    The library enqueues kernels only (no allocation, memset or synchronisation) and this module adds
+    no device work of its own, so the graph holds exactly the eager step's launches.  The captured
+    step is fixed to its buffers, its t and dt (the time embedding takes t as a host value, baked into
+    the launch), and its guidance: a sampling schedule captures one graph per step.  Capturing
+    records the launches without running them."""
+
+    def __init__(self, c, model, blocks, caches, x_latent, z_img, t, dt, guidance, buf: StepBuffers, B, **kw):
+        self.graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(self.graph):
+            denoise_step(c, model, blocks, caches, x_latent, z_img, t, dt, guidance, buf, B, **kw)
+
+    def replay(self):
+        self.graph.replay()
+
+
 class AttnCache:
     """The attention cache of every block: y [B, S, dim] float32 per block (the self-attention layer
     output before its gate, as wan_dit_block_fwd_cached keeps it)."""
