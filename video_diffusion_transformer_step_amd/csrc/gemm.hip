@@ -167,7 +167,7 @@ __device__ __forceinline__ void tile_coords(int id, int tiles_m, int tiles_n, in
 
 // Row-group size of the tile order (measured on the block's shapes): wide products (>= 32 column
 // tiles) share weights best in groups of 4, long-K products in groups of 2, the rest in groups of 8.
-inline int group_m(int tiles_n, int K) { return tiles_n >= 32 ? 4 : (K >= 4096 ? 2 : 8); }
+inline int group_m(int tiles_n, int K) { return (K >= 4096 && tiles_n < 32) ? 2 : 4; }
 
 template <typename T, int BM, int BN, int WM, int WN, class Epi>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restrict__ A, int64_t lda,
