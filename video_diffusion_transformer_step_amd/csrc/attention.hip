@@ -857,8 +857,10 @@ __global__ __launch_bounds__(512, 1) void attention_pp_kernel(const T* __restric
 
 // ---------------------------------------------------------------------------
 // Quantised ping-pong kernel ("Wan 技术深度解析" §5.3, FlashAttention-3 FP8: Q.K inner products in
-// INT8, O = P.V in FP8, FP32 accumulation across key tiles).  Same schedule, copies and barriers as
-// the bf16 ping-pong kernel; per 64-key tile and wave:
+// INT8, O = P.V in FP8, FP32 accumulation across key tiles).  The two wave groups run a phase apart
+// as in the bf16 ping-pong kernel, but S(t+1) is computed in the vector phase A(t) and the matrix phase
+// B(t) holds only P.V; group 0 copies the K tiles and group 1 the V^T tiles (pp_tile_q8).  Per 64-key
+// tile and wave:
 //  * S^T = K Q^T from INT8 codes: 8 v_mfma_i32_32x32x32_i8 (exact int32 dot products; K codes in
 //    LDS, the wave's Q codes in registers);
 //  * scores in exp2 units are s * (c_log2 * sq[query] * sk[tile]), with sq the query's INT8 scale
@@ -1048,38 +1050,33 @@ __device__ __forceinline__ void pv_products_q8(const FragQ8<HD>& fa, const char*
 
 template <int HD, int P>
 __device__ __forceinline__ void pp_tile_q8(const u32x4 (&qf)[AttnCfg<uint8_t, HD>::NCH], const FragQ8<HD>& fa,
-                                           const KVq8& kv, const CopyPlan<uint8_t, HD, 8>& cp,
+                                           const KVq8& kv, const CopyPlan<uint8_t, HD, 4>& cp,
                                            const uint8_t* __restrict__ kbase, const uint8_t* __restrict__ vtb,
                                            const float* __restrict__ skb, int t, int nt, int grp, float cq,
                                            const Slots<uint8_t, HD>& sl, v16i (&s)[2], v16i (&sn)[2],
-                                           f32x16 (&o)[AttnCfg<uint8_t, HD>::ND], f32x16& lacc, SoftState& st,
-                                           int& last) {
-  using CP = CopyPlan<uint8_t, HD, 8>;
+                                           f32x16 (&o)[AttnCfg<uint8_t, HD>::ND], f32x16& lacc, SoftState& st) {
+  using CP = CopyPlan<uint8_t, HD, 4>;
   static_assert(CP::KL == CP::VL, "equal K and V^T copy counts");
-  char* k_this = P ? sl.k1 : sl.k0;
-  char* k_next = P ? sl.k0 : sl.k1;
-  char* v_this = P ? sl.v1 : sl.v0;
-  char* v_next = P ? sl.v0 : sl.v1;
+  char* k_this = P ? sl.k1 : sl.k0;  // K(t) -> K(t+2)
+  char* k_next = P ? sl.k0 : sl.k1;  // K(t+1)
+  char* v_this = P ? sl.v1 : sl.v0;  // V^T(t)
+  char* v_next = P ? sl.v0 : sl.v1;  // V^T(t-1) -> V^T(t+1)
   const int j0 = t * KT;
-  // ---- A(t)
-  phase_barrier<CP::KL>(last);
-  last = 0;
+  // ---- A(t): S(t+1) = K(t+1) Q^T here, so K(t) is free once the other group's A(t-1) has ended.
+  // Group 0 copies K(t+2) in its A(t) and group 1 copies V^T(t+1) in its A(t); each group copies every
+  // other phase and waits for all its copies at this barrier, two phases after issuing them, before
+  // their first reader: no assumption about the order in which copies complete.
+  phase_barrier<CP::KL>(0);
   if (grp == 0) {
-    if (t + 2 < nt) { load_k_tile<uint8_t, HD, 8>(cp, kbase, kv.k_ss, kv.L, j0 + 2 * KT, k_this); last = 1; }
+    if (t + 2 < nt) load_k_tile<uint8_t, HD, 4>(cp, kbase, kv.k_ss, kv.L, j0 + 2 * KT, k_this);
   } else {
-    if (t >= 1 && t + 1 < nt) { load_v_tile<uint8_t, HD, 8>(cp, vtb, j0 + KT, v_next); last = 1; }
+    if (t >= 1 && t + 1 < nt) load_v_tile<uint8_t, HD, 4>(cp, vtb, j0 + KT, v_next);
   }
   const float mul = softmax_prep_q8<HD>(s, j0, kv.L, cq, skb[t], o, lacc, st);
   uint32_t pf[8];
   softmax_and_next_scores_q8<HD>(qf, fa, k_next, reinterpret_cast<f32x16(&)[2]>(s), sn, mul, st, pf);
-  // ---- B(t)
-  phase_barrier<CP::KL>(last);
-  last = 0;
-  if (grp == 0) {
-    if (t >= 1 && t + 1 < nt) { load_v_tile<uint8_t, HD, 8>(cp, vtb, j0 + KT, v_next); last = 1; }
-  } else {
-    if (t + 3 < nt) { load_k_tile<uint8_t, HD, 8>(cp, kbase, kv.k_ss, kv.L, j0 + 3 * KT, k_next); last = 1; }
-  }
+  // ---- B(t): the batch just issued stays in flight across this barrier
+  phase_barrier<CP::KL>(1);
   pv_products_q8<HD>(fa, v_this, pf, o, lacc, j0, kv.L);
 }
 
@@ -1125,15 +1122,11 @@ __global__ __launch_bounds__(512, 1) void attention_q8_kernel(const uint8_t* __r
 
   v16i sa[2], sb[2];
   scores_q8<HD>(qf, fa, sl.k0, sa);
-  int last = 0;
-  if (grp == 1) {
-    phase_barrier<CP::KL>(0);
-    if (2 < nt) { load_k_tile<uint8_t, HD, 8>(cp, kbase, kv.k_ss, kv.L, 2 * KT, sl.k0); last = 1; }
-  }
+  const CopyPlan<uint8_t, HD, 4> cp4(kv.k_ss, kv.Lpad);  // one group's share of each tile in the key loop
+  if (grp == 1) phase_barrier<CP::KL>(0);                // group 1 runs a phase late
   for (int t = 0; t < nt; t += 2) {
-    pp_tile_q8<HD, 0>(qf, fa, kv, cp, kbase, vtb, skb, t, nt, grp, cq, sl, sa, sb, o, lacc, st, last);
-    if (t + 1 < nt)
-      pp_tile_q8<HD, 1>(qf, fa, kv, cp, kbase, vtb, skb, t + 1, nt, grp, cq, sl, sb, sa, o, lacc, st, last);
+    pp_tile_q8<HD, 0>(qf, fa, kv, cp4, kbase, vtb, skb, t, nt, grp, cq, sl, sa, sb, o, lacc, st);
+    if (t + 1 < nt) pp_tile_q8<HD, 1>(qf, fa, kv, cp4, kbase, vtb, skb, t + 1, nt, grp, cq, sl, sb, sa, o, lacc, st);
   }
   if (grp == 0) phase_barrier<CP::KL>(0);
 
