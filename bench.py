@@ -477,7 +477,7 @@ def main():
     # ---- per-kernel breakdown (one extra, untimed step with every block kernel bracketed)
     breakdown = None
     if not args.no_breakdown:
-        bt = L.KernelTimer(capacity=layers * len(L.KERNEL_IDS), kernels=tuple(L.KERNEL_IDS))
+        bt = L.KernelTimer(capacity=2 * layers * len(L.KERNEL_IDS), kernels=tuple(L.KERNEL_IDS))
         with bt:
             step(total)
         bd = bt.times_ms()
@@ -491,7 +491,7 @@ def main():
         hbm_bytes = {"ln1": 6 * S * d, "ln2": 6 * S * d, "ln3": 6 * S * d, "qk_norm_rope": 8 * S * d}
         breakdown = {}
         for k_, v in bd.items():
-            ms = float(np.mean(v))
+            ms = float(np.sum(v)) / layers  # per block (the I2V cross-attention is two launches)
             e = {"ms": round(ms, 4)}
             if k_ in fl:
                 e["tflops"] = round(fl[k_] * c.B / (ms * 1e-3) / 1e12, 1)

@@ -650,8 +650,11 @@ __device__ __forceinline__ void write_lse(const SoftState& st, float* __restrict
 
 // Write the wave's O rows (lane: query qrow, d = 32 dblk + 8 g + 4 lhalf + 0..3).
 template <typename T, int HD>
+// add: the rows are added to what out holds (a second key/value stream accumulating into the first's
+// result), in fp32 before the store's rounding.
 __device__ __forceinline__ void store_rows(const f32x16 (&acc)[AttnCfg<T, HD>::ND], T* __restrict__ out,
-                                           int64_t o_bs, int64_t o_ss, int b, int h, int qrow, int S) {
+                                           int64_t o_bs, int64_t o_ss, int b, int h, int qrow, int S,
+                                           bool add = false) {
   const int lhalf = (threadIdx.x & 63) >> 5;
   if (qrow >= S) return;
   T* op = out + (int64_t)b * o_bs + (int64_t)qrow * o_ss + (int64_t)h * HD;
@@ -662,12 +665,22 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[AttnCfg<T, HD>::N
       const int dd = d * 32 + g * 8 + lhalf * 4;
       if constexpr (sizeof(T) == 2) {
         bf16x4 v;
+        if (add) {
+          const bf16x4 old = *reinterpret_cast<const bf16x4*>(op + dd);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = (bf16)acc[d][4 * g + i];
+          for (int i = 0; i < 4; ++i) v[i] = (bf16)((float)old[i] + acc[d][4 * g + i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = (bf16)acc[d][4 * g + i];
+        }
         *reinterpret_cast<bf16x4*>(op + dd) = v;
       } else {
-        *reinterpret_cast<float4*>(op + dd) =
-            make_float4(acc[d][4 * g], acc[d][4 * g + 1], acc[d][4 * g + 2], acc[d][4 * g + 3]);
+        float4 v = make_float4(acc[d][4 * g], acc[d][4 * g + 1], acc[d][4 * g + 2], acc[d][4 * g + 3]);
+        if (add) {
+          const float4 old = *reinterpret_cast<const float4*>(op + dd);
+          v = make_float4(old.x + v.x, old.y + v.y, old.z + v.z, old.w + v.w);
+        }
+        *reinterpret_cast<float4*>(op + dd) = v;
       }
     }
 }
@@ -688,7 +701,7 @@ template <typename T, int HD, int NS, int KIND>
 __global__ __launch_bounds__(256, 2) void attention_kernel(const T* __restrict__ q, int64_t q_bs, int64_t q_ss,
                                                             KVStream s0, KVStream s1, int S, int H, float c_log2,
                                                             T* __restrict__ out, int64_t o_bs, int64_t o_ss,
-                                                            float* __restrict__ lse, KeySplit ks) {
+                                                            float* __restrict__ lse, KeySplit ks, int accum) {
   using C = AttnCfg<T, HD>;
   __shared__ u32x4 k0_raw[C::KBYTES / 16], k1_raw[C::KBYTES / 16], v0_raw[C::VBYTES / 16], v1_raw[C::VBYTES / 16];
   const Slots<T, HD> sl{reinterpret_cast<char*>(k0_raw), reinterpret_cast<char*>(k1_raw),
@@ -714,7 +727,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const T* __restrict__
     finish_stream<T, HD>(si, o, st, acc);
   }
   if (NS == 1 && lse != nullptr) write_lse(st, lse, b, h, H, qrow, S);
-  store_rows<T, HD>(acc, out, o_bs, o_ss, b, h, qrow, S);
+  store_rows<T, HD>(acc, out, o_bs, o_ss, b, h, qrow, S, accum != 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1169,7 +1182,7 @@ hipError_t launch_q8_hd(const uint8_t* q, int64_t q_bs, int64_t q_ss, const floa
 template <typename T, int HD, int KIND>
 hipError_t launch_hd(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0, KVStream s1, int nstreams, int B, int S,
                      int H, float c_log2, T* o, int64_t o_bs, int64_t o_ss, float* lse, const KeySplit& ks,
-                     hipStream_t s) {
+                     int accum, hipStream_t s) {
   if constexpr (sizeof(T) == 2 && WAN_ATTN_PP && KIND == 0) {
     dim3 grid((unsigned)ceil_div(S, 256), (unsigned)H, (unsigned)(B * ks.n));
     if (nstreams == 2)
@@ -1182,10 +1195,10 @@ hipError_t launch_hd(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0, KVStre
     dim3 grid((unsigned)ceil_div(S, 128), (unsigned)H, (unsigned)(B * ks.n));
     if (nstreams == 2)
       hipLaunchKernelGGL((attention_kernel<T, HD, 2, KIND>), grid, dim3(256), 0, s, q, q_bs, q_ss, s0, s1, S, H,
-                         c_log2, o, o_bs, o_ss, lse, ks);
+                         c_log2, o, o_bs, o_ss, lse, ks, accum);
     else
       hipLaunchKernelGGL((attention_kernel<T, HD, 1, KIND>), grid, dim3(256), 0, s, q, q_bs, q_ss, s0, s1, S, H,
-                         c_log2, o, o_bs, o_ss, lse, ks);
+                         c_log2, o, o_bs, o_ss, lse, ks, accum);
   }
   return hipGetLastError();
 }
@@ -1195,7 +1208,7 @@ hipError_t launch_hd(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0, KVStre
 template <typename T>
 hipError_t launch_attention(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0, KVStream s1, int nstreams, int B,
                             int S, int H, int hd, float scale, T* o, int64_t o_bs, int64_t o_ss, int kind,
-                            hipStream_t s, float* lse, KeySplit ks) {
+                            hipStream_t s, float* lse, KeySplit ks, bool accumulate) {
   if (S <= 0 || B <= 0 || H <= 0) return hipSuccess;
   if (nstreams < 1 || nstreams > 2) return hipErrorInvalidValue;
   if (s0.L <= 0 || s0.Lpad % KT != 0 || s0.Lpad < s0.L) return hipErrorInvalidValue;
@@ -1204,14 +1217,19 @@ hipError_t launch_attention(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0,
   if (ks.n < 1 || (int64_t)B * ks.n > 65535) return hipErrorInvalidValue;
   if (ks.n > 1 && (nstreams != 1 || ks.chunk <= 0 || ks.chunk % KT != 0 || (int64_t)(ks.n - 1) * ks.chunk >= s0.L))
     return hipErrorInvalidValue;
+  // the ping-pong kernel (bf16 self-attention) stores only; accumulation is the four-wave kernel's
+  if (accumulate && ((sizeof(T) == 2 && WAN_ATTN_PP && kind == 0) || ks.n > 1)) return hipErrorInvalidValue;
+  const int acc = accumulate ? 1 : 0;
   const float c_log2 = scale * 1.4426950408889634f;
   if (hd == 128) {
-    if (kind) return launch_hd<T, 128, 1>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, ks, s);
-    return launch_hd<T, 128, 0>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, ks, s);
+    if (kind)
+      return launch_hd<T, 128, 1>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, ks, acc, s);
+    return launch_hd<T, 128, 0>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, ks, acc, s);
   }
   if (hd == 64) {
-    if (kind) return launch_hd<T, 64, 1>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, ks, s);
-    return launch_hd<T, 64, 0>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, ks, s);
+    if (kind)
+      return launch_hd<T, 64, 1>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, ks, acc, s);
+    return launch_hd<T, 64, 0>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, ks, acc, s);
   }
   return hipErrorInvalidValue;
 }
@@ -1329,9 +1347,9 @@ template hipError_t launch_lse_merge<bf16>(const void* const*, const float* cons
                                            float*, hipStream_t);
 
 template hipError_t launch_attention<float>(const float*, int64_t, int64_t, KVStream, KVStream, int, int, int, int,
-                                            int, float, float*, int64_t, int64_t, int, hipStream_t, float*, KeySplit);
+                                            int, float, float*, int64_t, int64_t, int, hipStream_t, float*, KeySplit, bool);
 template hipError_t launch_attention<bf16>(const bf16*, int64_t, int64_t, KVStream, KVStream, int, int, int, int,
-                                           int, float, bf16*, int64_t, int64_t, int, hipStream_t, float*, KeySplit);
+                                           int, float, bf16*, int64_t, int64_t, int, hipStream_t, float*, KeySplit, bool);
 
 template <typename T>
 void attention_tile(int kind, int& rows, int& per_cu) {

@@ -240,8 +240,13 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
   const int Lt = c.text_len, Li = c.img_len;
   KVStream st_txt{kv.k_txt, (int64_t)Lt * dim, dim, kv.vt_txt, Lt, (int)pad64(Lt)};
   KVStream st_img{kv.k_img, (int64_t)Li * dim, dim, kv.vt_img, Li, (int)pad64(Li > 0 ? Li : 1)};
-  PROF_TRY(WAN_K_CROSS_ATTN, launch_attention<T>(qc, (int64_t)S * dim, dim, st_txt, st_img, Li > 0 ? 2 : 1, B, S, H, hd, scale, w.o,
-                              (int64_t)S * dim, dim, 1, st));
+  // text, then (I2V) image: two launches of the one-stream kernel, the second adding its softmax's
+  // result to the first's (the two-stream kernel holds both streams' state and spills)
+  PROF_TRY(WAN_K_CROSS_ATTN, launch_attention<T>(qc, (int64_t)S * dim, dim, st_txt, st_txt, 1, B, S, H, hd, scale, w.o,
+                                                 (int64_t)S * dim, dim, 1, st));
+  if (Li > 0)
+    PROF_TRY(WAN_K_CROSS_ATTN, launch_attention<T>(qc, (int64_t)S * dim, dim, st_img, st_img, 1, B, S, H, hd, scale,
+                                                   w.o, (int64_t)S * dim, dim, 1, st, nullptr, KeySplit{}, true));
   PROF_TRY(WAN_K_CROSS_O_GEMM, gemm_residual<T>(w.o, dim, (const T*)W.wco, dim, BS, dim, dim, W.bco, nullptr, nullptr, 0, S, x, dim, st));
   // FFN branch
   PROF_TRY(WAN_K_LN2, launch_ln_mod<T>(x, BS, dim, S, 0, w.mod, nullptr, 3, 4, c.ln_eps, w.u, st));
