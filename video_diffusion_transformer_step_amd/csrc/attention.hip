@@ -1,11 +1,12 @@
 // Flash-style attention on 32x32 MFMA for the DiT's full 3D self-attention and
-// its (single- or dual-stream) cross-attention.
+// its cross-attention.
 //
 // What it computes: o = softmax(q k^T / sqrt(hd)) v per (batch row, head), over
 // all keys, no mask ("图解 Wan2.1 I2V" §5.3; "Wan 技术深度解析" §2.5: global,
-// non-causal attention).  With two key/value streams it returns the sum of the
-// two separately normalised attentions ("图解 Wan2.1 I2V" §5.4: image and text
-// branches share q, each has its own softmax, outputs are added).
+// non-causal attention).  One launch attends one key/value stream; with its
+// accumulate flag it adds its result to what o holds, which is how the caller
+// sums two separately normalised attentions ("图解 Wan2.1 I2V" §5.4: image and
+// text branches share q, each has its own softmax, outputs are added).
 //
 // How (gfx950):
 //  * each wave owns 32 queries, held in registers as the B operand of
@@ -630,13 +631,13 @@ __device__ __forceinline__ void apply_key_split(const KeySplit& ks, int& b, KVSt
 
 // Normalise one stream's O^T by its row sums and add it into acc (first stream: assign).
 template <typename T, int HD>
-__device__ __forceinline__ void finish_stream(int si, const f32x16 (&o)[AttnCfg<T, HD>::ND], const SoftState& st,
+__device__ __forceinline__ void finish_stream(const f32x16 (&o)[AttnCfg<T, HD>::ND], const SoftState& st,
                                               f32x16 (&acc)[AttnCfg<T, HD>::ND]) {
   const float inv = 1.f / (st.l + __shfl_xor(st.l, 32, 64));
 #pragma unroll
   for (int d = 0; d < AttnCfg<T, HD>::ND; ++d)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[d][r] = (si == 0 ? 0.f : acc[d][r]) + o[d][r] * inv;
+    for (int r = 0; r < 16; ++r) acc[d][r] = o[d][r] * inv;
 }
 
 // Natural log of the row's softmax normaliser: the online state keeps sum_j exp(scale s_j) as 2^m * l
@@ -650,7 +651,7 @@ __device__ __forceinline__ void write_lse(const SoftState& st, float* __restrict
 
 // Write the wave's O rows (lane: query qrow, d = 32 dblk + 8 g + 4 lhalf + 0..3).
 template <typename T, int HD>
-// add: the rows are added to what out holds (a second key/value stream accumulating into the first's
+// add: the rows are added to what out holds (a second key/value stream's launch adding to the first's
 // result), in fp32 before the store's rounding.
 __device__ __forceinline__ void store_rows(const f32x16 (&acc)[AttnCfg<T, HD>::ND], T* __restrict__ out,
                                            int64_t o_bs, int64_t o_ss, int b, int h, int qrow, int S,
@@ -697,9 +698,9 @@ __device__ __forceinline__ void load_q(const T* __restrict__ q, int64_t q_bs, in
 }
 
 // One workgroup = 4 waves = 128 queries of one (b, head).
-template <typename T, int HD, int NS, int KIND>
+template <typename T, int HD, int KIND>
 __global__ __launch_bounds__(256, 2) void attention_kernel(const T* __restrict__ q, int64_t q_bs, int64_t q_ss,
-                                                            KVStream s0, KVStream s1, int S, int H, float c_log2,
+                                                            KVStream kv, int S, int H, float c_log2,
                                                             T* __restrict__ out, int64_t o_bs, int64_t o_ss,
                                                             float* __restrict__ lse, KeySplit ks, int accum) {
   using C = AttnCfg<T, HD>;
@@ -708,7 +709,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const T* __restrict__
                         reinterpret_cast<char*>(v0_raw), reinterpret_cast<char*>(v1_raw)};
   int qt, h, b;
   attn_tile_coords(qt, h, b);
-  if (ks.n > 1) apply_key_split<T>(ks, b, s0, out, lse);
+  if (ks.n > 1) apply_key_split<T>(ks, b, kv, out, lse);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int qrow = qt * 128 + wave * 32 + (lane & 31);
   const FragAddr<T, HD> fa;
@@ -718,15 +719,12 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const T* __restrict__
   f32x16 o[C::ND], acc[C::ND];
   SoftState st;
 #pragma unroll
-  for (int si = 0; si < NS; ++si) {
-#pragma unroll
-    for (int d = 0; d < C::ND; ++d) o[d] = zero16();
-    st.m = -__builtin_inff();
-    st.l = 0.f;
-    attend_stream<T, HD>(qf, fa, si == 0 ? s0 : s1, b, h, H, c_log2, sl, o, st);
-    finish_stream<T, HD>(si, o, st, acc);
-  }
-  if (NS == 1 && lse != nullptr) write_lse(st, lse, b, h, H, qrow, S);
+  for (int d = 0; d < C::ND; ++d) o[d] = zero16();
+  st.m = -__builtin_inff();
+  st.l = 0.f;
+  attend_stream<T, HD>(qf, fa, kv, b, h, H, c_log2, sl, o, st);
+  finish_stream<T, HD>(o, st, acc);
+  if (lse != nullptr) write_lse(st, lse, b, h, H, qrow, S);
   store_rows<T, HD>(acc, out, o_bs, o_ss, b, h, qrow, S, accum != 0);
 }
 
@@ -833,9 +831,9 @@ __device__ __forceinline__ void attend_stream_pp(const u32x4 (&qf)[AttnCfg<T, HD
   if (grp == 0) phase_barrier<CP4::KL + CP4::VL>(0);  // group 0 passes the barrier ending group 1's last B
 }
 
-template <typename T, int HD, int NS, int KIND>
+template <typename T, int HD, int KIND>
 __global__ __launch_bounds__(512, 1) void attention_pp_kernel(const T* __restrict__ q, int64_t q_bs, int64_t q_ss,
-                                                               KVStream s0, KVStream s1, int S, int H, float c_log2,
+                                                               KVStream kv, int S, int H, float c_log2,
                                                                T* __restrict__ out, int64_t o_bs, int64_t o_ss,
                                                                float* __restrict__ lse, KeySplit ks) {
   using C = AttnCfg<T, HD>;
@@ -844,7 +842,7 @@ __global__ __launch_bounds__(512, 1) void attention_pp_kernel(const T* __restric
                         reinterpret_cast<char*>(v0_raw), reinterpret_cast<char*>(v1_raw)};
   int qt, h, b;
   attn_tile_coords(qt, h, b);
-  if (ks.n > 1) apply_key_split<T>(ks, b, s0, out, lse);
+  if (ks.n > 1) apply_key_split<T>(ks, b, kv, out, lse);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = wave >> 2;
@@ -856,15 +854,12 @@ __global__ __launch_bounds__(512, 1) void attention_pp_kernel(const T* __restric
   f32x16 o[C::ND], acc[C::ND];
   SoftState st;
 #pragma unroll
-  for (int si = 0; si < NS; ++si) {
-#pragma unroll
-    for (int d = 0; d < C::ND; ++d) o[d] = zero16();
-    st.m = -__builtin_inff();
-    st.l = 0.f;
-    attend_stream_pp<T, HD>(qf, fa, si == 0 ? s0 : s1, b, h, H, grp, c_log2, sl, o, st);
-    finish_stream<T, HD>(si, o, st, acc);
-  }
-  if (NS == 1 && lse != nullptr) write_lse(st, lse, b, h, H, qrow, S);
+  for (int d = 0; d < C::ND; ++d) o[d] = zero16();
+  st.m = -__builtin_inff();
+  st.l = 0.f;
+  attend_stream_pp<T, HD>(qf, fa, kv, b, h, H, grp, c_log2, sl, o, st);
+  finish_stream<T, HD>(o, st, acc);
+  if (lse != nullptr) write_lse(st, lse, b, h, H, qrow, S);
   store_rows<T, HD>(acc, out, o_bs, o_ss, b, h, qrow, S);
 }
 
@@ -1180,25 +1175,16 @@ hipError_t launch_q8_hd(const uint8_t* q, int64_t q_bs, int64_t q_ss, const floa
 // bf16 self-attention uses the ping-pong kernel (256 queries per workgroup); cross-attention (a few
 // hundred keys, where the per-stream prologue dominates) and fp32 use the four-wave kernel.
 template <typename T, int HD, int KIND>
-hipError_t launch_hd(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0, KVStream s1, int nstreams, int B, int S,
-                     int H, float c_log2, T* o, int64_t o_bs, int64_t o_ss, float* lse, const KeySplit& ks,
-                     int accum, hipStream_t s) {
+hipError_t launch_hd(const T* q, int64_t q_bs, int64_t q_ss, KVStream kv, int B, int S, int H, float c_log2,
+                     T* o, int64_t o_bs, int64_t o_ss, float* lse, const KeySplit& ks, int accum, hipStream_t s) {
   if constexpr (sizeof(T) == 2 && WAN_ATTN_PP && KIND == 0) {
     dim3 grid((unsigned)ceil_div(S, 256), (unsigned)H, (unsigned)(B * ks.n));
-    if (nstreams == 2)
-      hipLaunchKernelGGL((attention_pp_kernel<T, HD, 2, KIND>), grid, dim3(512), 0, s, q, q_bs, q_ss, s0, s1, S, H,
-                         c_log2, o, o_bs, o_ss, lse, ks);
-    else
-      hipLaunchKernelGGL((attention_pp_kernel<T, HD, 1, KIND>), grid, dim3(512), 0, s, q, q_bs, q_ss, s0, s1, S, H,
-                         c_log2, o, o_bs, o_ss, lse, ks);
+    hipLaunchKernelGGL((attention_pp_kernel<T, HD, KIND>), grid, dim3(512), 0, s, q, q_bs, q_ss, kv, S, H, c_log2, o,
+                       o_bs, o_ss, lse, ks);
   } else {
     dim3 grid((unsigned)ceil_div(S, 128), (unsigned)H, (unsigned)(B * ks.n));
-    if (nstreams == 2)
-      hipLaunchKernelGGL((attention_kernel<T, HD, 2, KIND>), grid, dim3(256), 0, s, q, q_bs, q_ss, s0, s1, S, H,
-                         c_log2, o, o_bs, o_ss, lse, ks, accum);
-    else
-      hipLaunchKernelGGL((attention_kernel<T, HD, 1, KIND>), grid, dim3(256), 0, s, q, q_bs, q_ss, s0, s1, S, H,
-                         c_log2, o, o_bs, o_ss, lse, ks, accum);
+    hipLaunchKernelGGL((attention_kernel<T, HD, KIND>), grid, dim3(256), 0, s, q, q_bs, q_ss, kv, S, H, c_log2, o,
+                       o_bs, o_ss, lse, ks, accum);
   }
   return hipGetLastError();
 }
@@ -1206,16 +1192,13 @@ hipError_t launch_hd(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0, KVStre
 }  // namespace
 
 template <typename T>
-hipError_t launch_attention(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0, KVStream s1, int nstreams, int B,
-                            int S, int H, int hd, float scale, T* o, int64_t o_bs, int64_t o_ss, int kind,
-                            hipStream_t s, float* lse, KeySplit ks, bool accumulate) {
+hipError_t launch_attention(const T* q, int64_t q_bs, int64_t q_ss, KVStream kv, int B, int S, int H, int hd,
+                            float scale, T* o, int64_t o_bs, int64_t o_ss, int kind, hipStream_t s, float* lse,
+                            KeySplit ks, bool accumulate) {
   if (S <= 0 || B <= 0 || H <= 0) return hipSuccess;
-  if (nstreams < 1 || nstreams > 2) return hipErrorInvalidValue;
-  if (s0.L <= 0 || s0.Lpad % KT != 0 || s0.Lpad < s0.L) return hipErrorInvalidValue;
-  if (nstreams == 2 && (s1.L <= 0 || s1.Lpad % KT != 0 || s1.Lpad < s1.L)) return hipErrorInvalidValue;
-  if (nstreams == 2 && lse != nullptr) return hipErrorInvalidValue;  // one normaliser per stream
+  if (kv.L <= 0 || kv.Lpad % KT != 0 || kv.Lpad < kv.L) return hipErrorInvalidValue;
   if (ks.n < 1 || (int64_t)B * ks.n > 65535) return hipErrorInvalidValue;
-  if (ks.n > 1 && (nstreams != 1 || ks.chunk <= 0 || ks.chunk % KT != 0 || (int64_t)(ks.n - 1) * ks.chunk >= s0.L))
+  if (ks.n > 1 && (ks.chunk <= 0 || ks.chunk % KT != 0 || (int64_t)(ks.n - 1) * ks.chunk >= kv.L))
     return hipErrorInvalidValue;
   // the ping-pong kernel (bf16 self-attention) stores only; accumulation is the four-wave kernel's
   if (accumulate && ((sizeof(T) == 2 && WAN_ATTN_PP && kind == 0) || ks.n > 1)) return hipErrorInvalidValue;
@@ -1223,13 +1206,13 @@ hipError_t launch_attention(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0,
   const float c_log2 = scale * 1.4426950408889634f;
   if (hd == 128) {
     if (kind)
-      return launch_hd<T, 128, 1>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, ks, acc, s);
-    return launch_hd<T, 128, 0>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, ks, acc, s);
+      return launch_hd<T, 128, 1>(q, q_bs, q_ss, kv, B, S, H, c_log2, o, o_bs, o_ss, lse, ks, acc, s);
+    return launch_hd<T, 128, 0>(q, q_bs, q_ss, kv, B, S, H, c_log2, o, o_bs, o_ss, lse, ks, acc, s);
   }
   if (hd == 64) {
     if (kind)
-      return launch_hd<T, 64, 1>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, ks, acc, s);
-    return launch_hd<T, 64, 0>(q, q_bs, q_ss, s0, s1, nstreams, B, S, H, c_log2, o, o_bs, o_ss, lse, ks, acc, s);
+      return launch_hd<T, 64, 1>(q, q_bs, q_ss, kv, B, S, H, c_log2, o, o_bs, o_ss, lse, ks, acc, s);
+    return launch_hd<T, 64, 0>(q, q_bs, q_ss, kv, B, S, H, c_log2, o, o_bs, o_ss, lse, ks, acc, s);
   }
   return hipErrorInvalidValue;
 }
@@ -1346,10 +1329,10 @@ template hipError_t launch_lse_merge<float>(const void* const*, const float* con
 template hipError_t launch_lse_merge<bf16>(const void* const*, const float* const*, int, int, int, int, int, bf16*,
                                            float*, hipStream_t);
 
-template hipError_t launch_attention<float>(const float*, int64_t, int64_t, KVStream, KVStream, int, int, int, int,
-                                            int, float, float*, int64_t, int64_t, int, hipStream_t, float*, KeySplit, bool);
-template hipError_t launch_attention<bf16>(const bf16*, int64_t, int64_t, KVStream, KVStream, int, int, int, int,
-                                           int, float, bf16*, int64_t, int64_t, int, hipStream_t, float*, KeySplit, bool);
+template hipError_t launch_attention<float>(const float*, int64_t, int64_t, KVStream, int, int, int, int, float,
+                                            float*, int64_t, int64_t, int, hipStream_t, float*, KeySplit, bool);
+template hipError_t launch_attention<bf16>(const bf16*, int64_t, int64_t, KVStream, int, int, int, int, float, bf16*,
+                                           int64_t, int64_t, int, hipStream_t, float*, KeySplit, bool);
 
 template <typename T>
 void attention_tile(int kind, int& rows, int& per_cu) {

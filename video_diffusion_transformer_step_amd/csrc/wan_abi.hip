@@ -221,7 +221,7 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
     }
     if (!(c.flags & WAN_FLAG_FP8_ATTN)) {
       KVStream self{w.qkv + dim, (int64_t)S * 2 * dim, 2 * dim, w.vt, S, Spad};
-      PROF_TRY(WAN_K_SELF_ATTN, launch_attention<T>(w.qkv, (int64_t)S * 2 * dim, 2 * dim, self, self, 1, B, S, H, hd,
+      PROF_TRY(WAN_K_SELF_ATTN, launch_attention<T>(w.qkv, (int64_t)S * 2 * dim, 2 * dim, self, B, S, H, hd,
                                                     scale, w.o, (int64_t)S * dim, dim, 0, st));
     }
     if (f8g) {
@@ -240,12 +240,12 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
   const int Lt = c.text_len, Li = c.img_len;
   KVStream st_txt{kv.k_txt, (int64_t)Lt * dim, dim, kv.vt_txt, Lt, (int)pad64(Lt)};
   KVStream st_img{kv.k_img, (int64_t)Li * dim, dim, kv.vt_img, Li, (int)pad64(Li > 0 ? Li : 1)};
-  // text, then (I2V) image: two launches of the one-stream kernel, the second adding its softmax's
-  // result to the first's (the two-stream kernel holds both streams' state and spills)
-  PROF_TRY(WAN_K_CROSS_ATTN, launch_attention<T>(qc, (int64_t)S * dim, dim, st_txt, st_txt, 1, B, S, H, hd, scale, w.o,
+  // text, then (I2V) image: two launches, the second adding its softmax's result to the first's (one
+  // launch holding both streams' state would spill registers)
+  PROF_TRY(WAN_K_CROSS_ATTN, launch_attention<T>(qc, (int64_t)S * dim, dim, st_txt, B, S, H, hd, scale, w.o,
                                                  (int64_t)S * dim, dim, 1, st));
   if (Li > 0)
-    PROF_TRY(WAN_K_CROSS_ATTN, launch_attention<T>(qc, (int64_t)S * dim, dim, st_img, st_img, 1, B, S, H, hd, scale,
+    PROF_TRY(WAN_K_CROSS_ATTN, launch_attention<T>(qc, (int64_t)S * dim, dim, st_img, B, S, H, hd, scale,
                                                    w.o, (int64_t)S * dim, dim, 1, st, nullptr, KeySplit{}, true));
   PROF_TRY(WAN_K_CROSS_O_GEMM, gemm_residual<T>(w.o, dim, (const T*)W.wco, dim, BS, dim, dim, W.bco, nullptr, nullptr, 0, S, x, dim, st));
   // FFN branch
@@ -616,7 +616,7 @@ static int attention_t(const T* q, const T* k, const T* v, const wan_grid& g, in
   HIP_TRY(launch_qk_norm_rope<T>(q, k, dim, qr, kr, dim, B, g.T, g.Hp, g.Wp, H, hd, nullptr, nullptr, 0, 0.f, theta, st));
   HIP_TRY(launch_transpose_heads<T>(v, dim, 0, B, S, H, hd, Spad, vt, st));
   KVStream s0{kr, (int64_t)S * dim, dim, vt, S, Spad};
-  HIP_TRY(launch_attention<T>(qr, (int64_t)S * dim, dim, s0, s0, 1, B, S, H, hd, 1.f / sqrtf((float)hd), o,
+  HIP_TRY(launch_attention<T>(qr, (int64_t)S * dim, dim, s0, B, S, H, hd, 1.f / sqrtf((float)hd), o,
                               (int64_t)S * dim, dim, 0, st));
   return WAN_OK;
 }
@@ -732,7 +732,7 @@ int attention_partial_t(const T* q, const T* k, const T* v, int B, int Sq, int S
   const float scale = 1.f / sqrtf((float)hd);
   const PartialPlan p = partial_plan(sizeof(T) == 2 ? WAN_BF16 : WAN_F32, B, Sq, Sk, H, hd);
   if (p.n == 1 || ws_bytes < p.bytes) {  // unsplit (also when the workspace holds only V^T)
-    HIP_TRY(launch_attention<T>(q, (int64_t)Sq * dim, dim, s0, s0, 1, B, Sq, H, hd, scale, o, (int64_t)Sq * dim, dim,
+    HIP_TRY(launch_attention<T>(q, (int64_t)Sq * dim, dim, s0, B, Sq, H, hd, scale, o, (int64_t)Sq * dim, dim,
                                 0, st, lse));
     return WAN_OK;
   }
@@ -744,7 +744,7 @@ int attention_partial_t(const T* q, const T* k, const T* v, int B, int Sq, int S
   ks.chunk = p.chunk;
   ks.o_stride = (int64_t)(p.o_part_bytes / sizeof(T));
   ks.lse_stride = (int64_t)(p.lse_part_bytes / 4);
-  HIP_TRY(launch_attention<T>(q, (int64_t)Sq * dim, dim, s0, s0, 1, B, Sq, H, hd, scale, o_parts, (int64_t)Sq * dim,
+  HIP_TRY(launch_attention<T>(q, (int64_t)Sq * dim, dim, s0, B, Sq, H, hd, scale, o_parts, (int64_t)Sq * dim,
                               dim, 0, st, l_parts, ks));
   const void* op[MERGE_MAX_PARTS];
   const float* lp[MERGE_MAX_PARTS];

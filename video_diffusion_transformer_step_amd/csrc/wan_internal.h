@@ -98,7 +98,7 @@ hipError_t gemv(const T* W, int N, int K, const float* x, int B, const float* bi
 hipError_t launch_sinusoid(const float* t_host, int B, int freq_dim, float* emb, hipStream_t s);
 
 // ---- attention (attention.hip) ----------------------------------------------
-// Flash attention, non-causal, over one or two key/value streams whose outputs are summed.
+// Flash attention, non-causal, over one key/value stream (a second stream adds to the first's output).
 // q:  element (b, s, h, d) at q[b*q_bs + s*q_ss + h*hd + d]
 // k:  element (b, j, h, d) at k[b*k_bs + j*k_ss + h*hd + d]
 // vt: element (b, h, d, j) at vt[((b*H + h)*hd + d)*Lpad + j]  (zero beyond L)
@@ -121,15 +121,14 @@ struct KeySplit {
 // workgroups one compute unit holds at once.
 template <typename T>
 void attention_tile(int kind, int& rows, int& per_cu);
-// kind: 0 self-attention, 1 cross-attention (separate kernel symbols).  lse (one stream only; NULL = not
-// written): [B, H, S] float32, the natural log of each query row's softmax normaliser.  accumulate: the
-// result is added to what o holds (a second stream after a first launch; not with key splits, and not
+// kind: 0 self-attention, 1 cross-attention (separate kernel symbols).  lse (NULL = not written):
+// [B, H, S] float32, the natural log of each query row's softmax normaliser.  accumulate: the result is
+// added to what o holds (a second key/value stream after a first launch; not with key splits, and not
 // for bf16 kind 0, which runs the ping-pong kernel).
 template <typename T>
-hipError_t launch_attention(const T* q, int64_t q_bs, int64_t q_ss, KVStream s0, KVStream s1, int nstreams, int B,
-                            int S, int H, int hd, float scale, T* o, int64_t o_bs, int64_t o_ss, int kind,
-                            hipStream_t s, float* lse = nullptr, KeySplit ks = KeySplit{},
-                            bool accumulate = false);
+hipError_t launch_attention(const T* q, int64_t q_bs, int64_t q_ss, KVStream kv, int B, int S, int H, int hd,
+                            float scale, T* o, int64_t o_bs, int64_t o_ss, int kind, hipStream_t s,
+                            float* lse = nullptr, KeySplit ks = KeySplit{}, bool accumulate = false);
 
 // Quantised attention (INT8 Q.K, FP8 P.V): q8 [B, S, H, hd] INT8 codes with sq [B, H, S]; k8 [B, L, H, hd]
 // INT8 codes with sk [B, H, ceil(L / 64)]; v8t [B, H, hd, round_up(L, 128)] E4M3 codes (keys in P.V
