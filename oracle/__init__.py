@@ -19,7 +19,10 @@ Pages cited (titles as they appear on the pages):
 Parity status per function is listed in ``PARITY``: "pinned" functions are
 checked by the CPU tests against closed forms, invariants, brute force or
 hand-worked fixtures; "parity unpinned" ones only against shape and the
-special cases named there.
+special cases named there.  Parity unpinned: ``time_embed``, ``context_embed``
+and ``head_fwd`` (the pages name these MLPs and the head's adaLN but not their
+layers; the readings taken are implemented as stated and checked against
+PyTorch modules of the same composition).
 """
 from .wan_oracle import *  # noqa: F401,F403
 from .wan_oracle import PARITY, __all__  # noqa: F401

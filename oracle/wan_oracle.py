@@ -663,8 +663,9 @@ PARITY = {
     "unpatchify": "pinned: exact inverse of patchify (round trip), hand-worked fixture",
     "patch_embed": "pinned: equals a direct Conv3d (kernel = stride = (1,2,2)) loop",
     "sinusoidal_embedding": "pinned: t = 0 gives [1..1 | 0..0]; unit-modulus (cos,sin) pairs",
-    "time_embed": "pinned: identity-weight special case; the composition equals PyTorch float64 "
-                  "Linear/SiLU modules with the same weights (the composition itself is a reading)",
+    "time_embed": "parity unpinned (the pages name the MLP and its [6, dim] output, not its layers): "
+                  "the reading's implementation is checked against PyTorch float64 Linear/SiLU modules "
+                  "with the same weights and an identity-weight special case",
     "layer_norm": "pinned: zero mean / unit variance; constant row -> bias; numpy.var cross-check",
     "rms_norm": "pinned: constant row c -> g c / sqrt(c^2 + eps); unit RMS for g = 1",
     "rope_3d": "pinned: segment sizes 44/42/42 and 24/20/20; identity at (0,0,0); norm "
@@ -676,13 +677,17 @@ PARITY = {
                      "brute-force pure-Python log of the normaliser",
     "lse_merge": "pinned: merging key chunks reproduces attention() and attention_lse() over "
                  "all keys (for several chunkings, one-key chunks included); one part -> itself",
-    "block_fwd": "pinned parts (norms, RoPE, attention, cross-attention single/dual equality, "
-                 "adaLN-Zero identity); composition order is a reading: parity unpinned "
-                 "beyond those identities",
-    "head_fwd": "pinned: equals PyTorch layer_norm with weight 1 + scale and bias shift, then linear "
-                "(the two-vector head modulation itself is a reading)",
-    "context_embed": "pinned: equals PyTorch Linear -> exact GELU -> Linear with the same weights "
-                     "(the MLP shape itself is a reading)",
+    "block_fwd": "pinned: adaLN-Zero identity; closed forms of each branch with the others switched "
+                 "off (scale1 = -1 and scale2 = -1 make the branch input equal its shift; uniform "
+                 "attention with identity value/output projections; a constant cross-attention input "
+                 "from ln3_w = 0 with two text keys and one image key; the sign of a two-token RoPE "
+                 "score from the q and k gains); self-attention before cross-attention; sampled-row "
+                 "mode; non-causality",
+    "head_fwd": "parity unpinned (the pages say only that the head has adaLN and unpatchify): the "
+                "reading's implementation equals PyTorch layer_norm with weight 1 + scale and bias "
+                "shift, then linear",
+    "context_embed": "parity unpinned (the pages name an MLP, not its layers): the reading's "
+                     "implementation equals PyTorch Linear -> exact GELU -> Linear with the same weights",
     "cfg_combine": "pinned: s = 1 -> v_c, s = 0 -> v_u",
     "euler_step": "pinned: straight-line path lands exactly on the endpoint",
     "sample": "pinned through cfg_combine / euler_step; DiT part as block_fwd",

@@ -455,6 +455,210 @@ def pin_block_non_causal(o):
                           o.block_fwd(x, e0z, w0, kv, grid, heads)[:, 0])
 
 
+# ------------------------------------------------------ block composition
+# Closed forms of the whole block, each with all but one branch switched off by the pages' own
+# switches (a zero gate, a zero output projection), so that the remaining branch's output is known
+# without running the block's arithmetic: "图解 Wan2.1 I2V" §5.2 (chunk order shift1, scale1, gate1,
+# shift2, scale2, gate2; x' = norm(x)(1 + scale) + shift; x = x + gate * f(x')), §5.3 (q, k through
+# RMSNorm with their own gains, then RoPE), §5.4 (cross-attention takes the plain, not the modulated,
+# norm and is added without a gate), §5.5 (FFN with gate2).
+def _set_mod(e0, w, chunk, value):
+    """Make mod chunk `chunk` (= e0[:, chunk] + mod_bias[chunk]) equal `value` for every row."""
+    e0 = np.array(e0, float).copy()
+    w = dict(w)
+    mb = np.array(w["mod_bias"], float).copy()
+    mb[chunk] = 0.0
+    e0[:, chunk, :] = value
+    w["mod_bias"] = mb
+    return e0, w
+
+
+def _mod(e0, w, b, chunk):
+    return np.asarray(e0, float)[b, chunk] + np.asarray(w["mod_bias"], float)[chunk]
+
+
+def _branch_off(e0, w, which):
+    """Switch branches off: "self" gate1 = 0; "cross" W_co = b_co = 0; "ffn" gate2 = 0."""
+    if "self" in which:
+        e0, w = _set_mod(e0, w, 2, 0.0)
+    if "ffn" in which:
+        e0, w = _set_mod(e0, w, 5, 0.0)
+    if "cross" in which:
+        w = dict(w)
+        w["wco"] = np.zeros_like(w["wco"])
+        w["bco"] = np.zeros_like(w["bco"])
+    return e0, w
+
+
+def _zero_mean_unit_rows(rng, n, dim):
+    """Rows d with mean 0 and mean(d^2) = 1 exactly (up to rounding)."""
+    d = rng.standard_normal((n, dim))
+    d -= d.mean(-1, keepdims=True)
+    return d / np.sqrt((d * d).mean(-1, keepdims=True))
+
+
+def pin_block_self_branch_scale_minus_one(o):
+    """scale1 = -1 makes u = shift1 for every token whatever x is, so every value row is
+    shift1 W_v^T + b_v, attention returns it unchanged (its weights sum to one), and with the cross
+    and FFN branches off the block output is x + gate1 * ((shift1 W_v^T + b_v) W_o^T + b_o).  A swap
+    of shift1 and scale1, or a scale used without its 1 +, makes u depend on x."""
+    x, e0, w, kv, grid, heads = _tiny_block_inputs(seed=31)
+    e0, w = _set_mod(e0, w, 1, -1.0)
+    e0, w = _branch_off(e0, w, ("cross", "ffn"))
+    got = o.block_fwd(x, e0, w, kv, grid, heads)
+    for b in range(x.shape[0]):
+        v = _mod(e0, w, b, 0) @ np.asarray(w["wv"]).T + w["bv"]
+        y = v @ np.asarray(w["wo"]).T + w["bo"]
+        assert np.allclose(got[b], x[b] + _mod(e0, w, b, 2) * y[None, :], rtol=0, atol=1e-12)
+
+
+def pin_block_self_branch_uniform_identity(o):
+    """W_q = W_k = 0 (zero biases) makes q = k = 0, so every score is 0 and attention averages the
+    values; with W_v = W_o = I (zero biases) the self-attention layer returns mean_s(u_s).  Rows
+    x_s = a_s d + c_s with mean(d) = 0 and mean(d^2) = 1 have LN(x_s) = d a_s / sqrt(a_s^2 + eps), so
+    with cross and FFN off the block output is x + gate1 * (d mean_s(a_s / sqrt(a_s^2 + eps))
+    (1 + scale1) + shift1)."""
+    x, e0, w, kv, grid, heads = _tiny_block_inputs(seed=32)
+    rng = np.random.default_rng(32)
+    B, S, dim = x.shape
+    d = _zero_mean_unit_rows(rng, 1, dim)[0]
+    a = rng.uniform(0.5, 2.0, size=(B, S))
+    x = a[:, :, None] * d[None, None, :] + rng.standard_normal((B, S, 1))
+    w = dict(w)
+    for k in ("wq", "wk"):
+        w[k] = np.zeros((dim, dim))
+    for k in ("bq", "bk", "bv", "bo"):
+        w[k] = np.zeros(dim)
+    w["wv"] = np.eye(dim)
+    w["wo"] = np.eye(dim)
+    e0, w = _branch_off(e0, w, ("cross", "ffn"))
+    got = o.block_fwd(x, e0, w, kv, grid, heads)
+    for b in range(B):
+        mean_ln = d * np.mean(a[b] / np.sqrt(a[b] ** 2 + 1e-6))
+        y = mean_ln * (1.0 + _mod(e0, w, b, 1)) + _mod(e0, w, b, 0)
+        assert np.allclose(got[b], x[b] + _mod(e0, w, b, 2) * y[None, :], rtol=0, atol=1e-12)
+
+
+def pin_block_ffn_branch_scale_minus_one(o):
+    """scale2 = -1 makes the FFN input u2 = shift2 for every token; with the self-attention and
+    cross branches off the block output is x + gate2 * (GELU(shift2 W_1^T + b_1) W_2^T + b_2).  GELU
+    here is PyTorch's exact (erf) GELU in float64."""
+    import torch
+    x, e0, w, kv, grid, heads = _tiny_block_inputs(seed=33)
+    e0, w = _set_mod(e0, w, 4, -1.0)
+    e0, w = _branch_off(e0, w, ("self", "cross"))
+    got = o.block_fwd(x, e0, w, kv, grid, heads)
+    for b in range(x.shape[0]):
+        h = _mod(e0, w, b, 3) @ np.asarray(w["w1"]).T + w["b1"]
+        h = torch.nn.functional.gelu(torch.from_numpy(h)).numpy()
+        y = h @ np.asarray(w["w2"]).T + w["b2"]
+        assert np.allclose(got[b], x[b] + _mod(e0, w, b, 5) * y[None, :], rtol=0, atol=1e-12)
+
+
+def _cross_constant(w, kv_b, heads):
+    """Cross branch output when its normalised input is the constant ln3_b (ln3_w = 0): q_c is the
+    same for every token; text has two keys per head, so the softmax is the logistic function of
+    the score difference; the image stream has one key, so its attention returns its value row."""
+    kt, vt, ki, vi = kv_b
+    dim = kt.shape[1]
+    hd = dim // heads
+    q = np.asarray(w["ln3_b"]) @ np.asarray(w["wcq"]).T + w["bcq"]
+    o = np.empty(dim)
+    for h in range(heads):
+        sl = slice(h * hd, (h + 1) * hd)
+        z = (q[sl] @ kt[0, sl] - q[sl] @ kt[1, sl]) / math.sqrt(hd)
+        p0 = 1.0 / (1.0 + math.exp(-z))
+        o[sl] = p0 * vt[0, sl] + (1.0 - p0) * vt[1, sl]
+    if ki is not None:
+        o = o + vi[0]
+    return o @ np.asarray(w["wco"]).T + w["bco"]
+
+
+def _cross_pin_inputs(seed):
+    x, e0, w, kv, grid, heads = _tiny_block_inputs(seed=seed, L=2, Li=1)
+    rng = np.random.default_rng(seed)
+    kv = [(2.0 * kt, vt, ki, vi) for kt, vt, ki, vi in kv]  # sharper text scores
+    w = dict(w)
+    w["ln3_w"] = np.zeros(x.shape[-1])
+    w["ln3_b"] = rng.standard_normal(x.shape[-1])
+    w["wcq"] = 3.0 * np.asarray(w["wcq"])
+    return x, e0, w, kv, grid, heads
+
+
+def pin_block_cross_branch_plain_norm_no_gate(o):
+    """The cross branch takes the affine LayerNorm of x (not the adaLN-modulated one) and adds its
+    output without a gate.  With ln3_w = 0 its normalised input is ln3_b for every token, so with the
+    self-attention branch off (gate1 = 0) and the FFN's weights zero (its output is GELU(0) W_2^T = 0
+    while gate2, shift2 and scale2 stay generic) the block output is x + the closed form of
+    ``_cross_constant`` for every token (two text keys, one image key)."""
+    x, e0, w, kv, grid, heads = _cross_pin_inputs(34)
+    e0, w = _branch_off(e0, w, ("self",))
+    for k in ("w1", "w2"):
+        w[k] = np.zeros_like(w[k])
+    for k in ("b1", "b2"):
+        w[k] = np.zeros_like(w[k])
+    got = o.block_fwd(x, e0, w, kv, grid, heads)
+    for b in range(x.shape[0]):
+        assert np.allclose(got[b], x[b] + _cross_constant(w, kv[b], heads)[None, :], rtol=0, atol=1e-12)
+
+
+def pin_block_order_self_then_cross(o):
+    """Self-attention runs before cross-attention ("图解 Wan2.1 I2V" §5.3-§5.4): with the self branch
+    of ``pin_block_self_branch_uniform_identity`` (output depends on x through LN) and the constant
+    cross branch of ``pin_block_cross_branch_plain_norm_no_gate`` both on, the output is
+    x + gate1 * y(x) + cross; running cross-attention first would feed x + cross to the self branch."""
+    x, e0, w, kv, grid, heads = _cross_pin_inputs(35)
+    rng = np.random.default_rng(35)
+    B, S, dim = x.shape
+    d = _zero_mean_unit_rows(rng, 1, dim)[0]
+    a = rng.uniform(0.5, 2.0, size=(B, S))
+    x = a[:, :, None] * d[None, None, :] + rng.standard_normal((B, S, 1))
+    for k in ("wq", "wk"):
+        w[k] = np.zeros((dim, dim))
+    for k in ("bq", "bk", "bv", "bo"):
+        w[k] = np.zeros(dim)
+    w["wv"] = np.eye(dim)
+    w["wo"] = np.eye(dim)
+    e0, w = _branch_off(e0, w, ("ffn",))
+    got = o.block_fwd(x, e0, w, kv, grid, heads)
+    for b in range(B):
+        mean_ln = d * np.mean(a[b] / np.sqrt(a[b] ** 2 + 1e-6))
+        y = mean_ln * (1.0 + _mod(e0, w, b, 1)) + _mod(e0, w, b, 0)
+        want = x[b] + _mod(e0, w, b, 2) * y[None, :] + _cross_constant(w, kv[b], heads)[None, :]
+        assert np.allclose(got[b], want, rtol=0, atol=1e-12)
+
+
+def pin_block_qk_gains_own_projection(o):
+    """Each of q and k is RMS-normalised with its own gain before RoPE.  Two tokens at frames 0 and 1
+    (grid (2, 1, 1)), one head of width 12 (time segment = channels 0-3, first pair rotating by the
+    frame index times theta^0 = 1 radian).  W_q = W_k = 0 and b_q = b_k = 1 give q = k = 1 (RMS 1),
+    so q^ = R(f) g_q / sqrt(1 + eps) and k^ = R(f) g_k / sqrt(1 + eps).  With g_q = e_0 and
+    g_k = gamma e_1 the scores are s_ij = gamma sin(f_i - f_j) / ((1 + eps) sqrt(12)): zero on the
+    diagonal, -kappa and +kappa off it.  Rows x_0 = d, x_1 = -d (mean 0, mean square 1), shift1 =
+    scale1 = 0 and W_v = W_o = I give u = v = +-d / sqrt(1 + eps), and both outputs equal
+    tanh(kappa / 2) d / sqrt(1 + eps).  Swapping the gains flips kappa's sign."""
+    rng = np.random.default_rng(36)
+    dim, heads, eps, gamma = 12, 1, 1e-6, 6.0
+    n = lambda *s: 0.2 * rng.standard_normal(s)
+    d = _zero_mean_unit_rows(rng, 1, dim)[0]
+    x = np.stack([d, -d])[None]  # [1, 2, dim]
+    w = {"mod_bias": n(6, dim), "wq": np.zeros((dim, dim)), "bq": np.ones(dim), "wk": np.zeros((dim, dim)),
+         "bk": np.ones(dim), "wv": np.eye(dim), "bv": np.zeros(dim), "gq": np.eye(dim)[0],
+         "gk": gamma * np.eye(dim)[1], "wo": np.eye(dim), "bo": np.zeros(dim), "ln3_w": 1 + n(dim),
+         "ln3_b": n(dim), "wcq": n(dim, dim), "bcq": n(dim), "wco": n(dim, dim), "bco": n(dim),
+         "w1": n(20, dim), "b1": n(20), "w2": n(dim, 20), "b2": n(dim)}
+    e0 = n(1, 6, dim)
+    kv = [(n(3, dim), n(3, dim), None, None)]
+    e0, w = _set_mod(e0, w, 0, 0.0)
+    e0, w = _set_mod(e0, w, 1, 0.0)
+    e0, w = _branch_off(e0, w, ("cross", "ffn"))
+    got = o.block_fwd(x, e0, w, kv, (2, 1, 1), heads)
+    kappa = gamma * math.sin(1.0) / ((1.0 + eps) * math.sqrt(dim))
+    y = math.tanh(kappa / 2.0) * d / math.sqrt(1.0 + eps)
+    want = x[0] + _mod(e0, w, 0, 2)[None, :] * y[None, :]
+    assert np.allclose(got[0], want, rtol=0, atol=1e-12)
+
+
 def pin_fm_straight_line(o):
     """Straight path x_t = (1-t) x0 + t x1 with constant velocity x1 - x0: N exact-velocity
     Euler steps from t = 0 land on x1 ("Wan 技术深度解析" §2.7, §8.3); in the mirrored

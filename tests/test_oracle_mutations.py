@@ -218,6 +218,57 @@ def _time_embed_silu_on_e0(t, w, freq_dim=256):
     return e, e0.reshape(6, -1)
 
 
+def _block_source_mutant(*edits):
+    """block_fwd with text substitutions (old -> new) made in its source, so that one line of the
+    composition is planted wrong while the rest stays as written."""
+    def factory():
+        import inspect
+        src = inspect.getsource(wo.__dict__["_orig_block_fwd"])
+        for old, new in edits:
+            assert old in src, old
+            src = src.replace(old, new)
+        ns = {}
+        exec(compile(src, "<block_fwd mutant>", "exec"), wo.__dict__, ns)
+        return ns["block_fwd"]
+    return factory
+
+
+def _block_cross_before_self_factory():
+    # cross-attention first, then self-attention, then the FFN (the order of another page's diagram)
+    def block(x, e0, w, kv, grid, heads, rows=None, ln_eps=1e-6, rms_eps=1e-6, theta=10000.0, attn_cache=None):
+        x, e0 = np.asarray(x, float), np.asarray(e0, float)
+        B, S, dim = x.shape
+        rows = np.arange(S) if rows is None else np.asarray(rows)
+        hd = dim // heads
+        pos = wo.token_positions(grid)
+        out = np.empty((B, len(rows), dim))
+        for b in range(B):
+            shift1, scale1, gate1, shift2, scale2, gate2 = e0[b] + np.asarray(w["mod_bias"], float)
+            kt, vt, ki, vi = kv[b]
+            qc = wo.linear(wo.layer_norm(x[b], ln_eps, w["ln3_w"], w["ln3_b"]), w["wcq"], w["bcq"])
+            oc = wo.multihead_attention(qc, kt, vt, heads)
+            if ki is not None:
+                oc = oc + wo.multihead_attention(qc, ki, vi, heads)
+            xc = x[b] + wo.linear(oc, w["wco"], w["bco"])
+            u = wo.modulate(wo.layer_norm(xc, ln_eps), shift1, scale1)
+            k = wo.rope_3d(wo.rms_norm(wo.linear(u, w["wk"], w["bk"]), w["gk"], rms_eps).reshape(S, heads, hd), pos,
+                           theta).reshape(S, dim)
+            q = wo.rope_3d(wo.rms_norm(wo.linear(u[rows], w["wq"], w["bq"]), w["gq"], rms_eps)
+                           .reshape(len(rows), heads, hd), pos[rows], theta).reshape(len(rows), dim)
+            v = wo.linear(u, w["wv"], w["bv"])
+            xr = xc[rows] + gate1 * wo.linear(wo.multihead_attention(q, k, v, heads), w["wo"], w["bo"])
+            u2 = wo.modulate(wo.layer_norm(xr, ln_eps), shift2, scale2)
+            out[b] = xr + gate2 * wo.linear(wo.gelu(wo.linear(u2, w["w1"], w["b1"])), w["w2"], w["b2"])
+        return out
+    return block
+
+
+_UNPACK = "shift1, scale1, gate1, shift2, scale2, gate2 = mod"
+_LN3 = 'c = layer_norm(xr, ln_eps, w["ln3_w"], w["ln3_b"])'
+_CROSS_ADD = 'xr = xr + linear(oc, w["wco"], w["bco"])'
+_GQ = 'w["gq"], rms_eps)'
+_GK = 'w["gk"], rms_eps)'
+
 MUTANTS = {
     "mask_raw_reshape": ("i2v_mask", lambda: _mask_raw_reshape),
     "patch_vector_kw_kh": ("patchify", lambda: _patchify_kw_kh),
@@ -248,6 +299,35 @@ MUTANTS = {
     "head_shift_scale_swapped": ("head_fwd", lambda: _head_shift_scale_swapped),
     "context_embed_tanh_gelu": ("context_embed", lambda: _context_embed_tanh_gelu),
     "time_embed_silu_after_projection": ("time_embed", lambda: _time_embed_silu_on_e0),
+    "block_shift_scale_swapped": ("block_fwd", _block_source_mutant(
+        (_UNPACK, "scale1, shift1, gate1, scale2, shift2, gate2 = mod"))),
+    "block_ffn_shift_scale_swapped": ("block_fwd", _block_source_mutant(
+        (_UNPACK, "shift1, scale1, gate1, scale2, shift2, gate2 = mod"))),
+    "block_gate_before_scale": ("block_fwd", _block_source_mutant(
+        (_UNPACK, "shift1, gate1, scale1, shift2, gate2, scale2 = mod"))),
+    "block_chunks_ffn_first": ("block_fwd", _block_source_mutant(
+        (_UNPACK, "shift2, scale2, gate2, shift1, scale1, gate1 = mod"))),
+    "block_ln3_affine_dropped": ("block_fwd", _block_source_mutant((_LN3, "c = layer_norm(xr, ln_eps)"))),
+    "block_ln3_weight_bias_swapped": ("block_fwd", _block_source_mutant(
+        (_LN3, 'c = layer_norm(xr, ln_eps, w["ln3_b"], w["ln3_w"])'))),
+    "block_cross_input_adaln": ("block_fwd", _block_source_mutant(
+        (_LN3, "c = modulate(layer_norm(xr, ln_eps), shift2, scale2)"))),
+    "block_cross_gated_by_gate2": ("block_fwd", _block_source_mutant(
+        (_CROSS_ADD, 'xr = xr + gate2 * linear(oc, w["wco"], w["bco"])'))),
+    "block_cross_gated_by_gate1": ("block_fwd", _block_source_mutant(
+        (_CROSS_ADD, 'xr = xr + gate1 * linear(oc, w["wco"], w["bco"])'))),
+    "block_ffn_gated_by_gate1": ("block_fwd", _block_source_mutant(("out[b] = xr + gate2 * y", "out[b] = xr + gate1 * y"))),
+    "block_qk_gains_swapped": ("block_fwd", _block_source_mutant((_GQ, "@@GK@@"), (_GK, _GQ), ("@@GK@@", _GK))),
+    "block_image_stream_dropped": ("block_fwd", _block_source_mutant(
+        ("oc = oc + multihead_attention(qc, k_img, v_img, heads)", "oc = oc"))),
+    "block_rope_before_rmsnorm": ("block_fwd", _block_source_mutant(
+        ('q = rms_norm(linear(u[rows], w["wq"], w["bq"]), w["gq"], rms_eps)', 'q = linear(u[rows], w["wq"], w["bq"])'),
+        ('q = rope_3d(q.reshape(len(rows), heads, hd), pos[rows], theta).reshape(len(rows), dim)',
+         'q = rms_norm(rope_3d(q.reshape(len(rows), heads, hd), pos[rows], theta).reshape(len(rows), dim), '
+         'w["gq"], rms_eps)'))),
+    "block_values_from_unmodulated_norm": ("block_fwd", _block_source_mutant(
+        ('v = linear(u, w["wv"], w["bv"])', 'v = linear(layer_norm(x[b], ln_eps), w["wv"], w["bv"])'))),
+    "block_cross_before_self": ("block_fwd", _block_cross_before_self_factory),
 }
 
 
@@ -256,6 +336,7 @@ def test_planted_mistake_is_caught(name, monkeypatch):
     target, factory = MUTANTS[name]
     monkeypatch.setitem(wo.__dict__, "_orig_patchify", wo.patchify)
     monkeypatch.setitem(wo.__dict__, "_orig_sinusoidal_embedding", wo.sinusoidal_embedding)
+    monkeypatch.setitem(wo.__dict__, "_orig_block_fwd", wo.block_fwd)
     mutant = factory()
     monkeypatch.setattr(wo, target, mutant)
     caught = []
