@@ -63,6 +63,32 @@ def test_patch_embed(dtype):
     assert rel_l2(host(out), ref) <= TOL[dtype]
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["t2v-1.3b", "i2v-14b", "ti2v-5b"])
+def test_patch_embed_full_size(name):
+    """The patch embedding at the workloads' real shapes ("图解 Wan2.1 I2V" §5.1): K = 4 C_in = 64 / 144 / 400
+    channels per patch vector, N = dim = 1536 / 5120 / 3072, M = B S = 32760 / 65520 / 54560 rows, the
+    shapes that take the 256-row tiles with a partial last K step.  Patch vectors ~N(0,1) fp32 (rounded to
+    bf16 inside, like the weights); sampled rows against the oracle's exact product."""
+    require_gpu()
+    c = wi.get_config(name)
+    K, M = 4 * c.in_channels, c.B * c.S
+    case(f"patch_embed full size {name}: M={M} K={K} N={c.dim}")
+    mw = wi.make_model_weights(c, seed=8)
+    p = wi.normal(8, c, "x_block", (M, K), quantize=False)
+    cfg = R.cfg_of(c)
+    out = torch.empty((M, c.dim), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(L.patch_embed_ws_bytes(cfg, M, c.in_channels), 16), dtype=torch.uint8, device="cuda")
+    L.patch_embed(cfg, dev(p), c.in_channels, dev(mw["w_pe"], torch.bfloat16), dev(mw["b_pe"]), out, ws)
+    got = host(out)
+    rows = np.unique(np.concatenate([wi.sample_rows(c.replace(B=1, T=c.T * c.B), 200, seed=8), [M - 1]]))
+    ref = oracle.patch_embed(p[rows], mw["w_pe"], mw["b_pe"])
+    e = rel_l2(got[rows], ref)
+    print(f"[patch_embed {name}] rel-L2 {e:.3e} on {len(rows)} rows", flush=True)
+    assert np.isfinite(got).all()
+    assert e <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("cfg_name,dtype", [("tiny", "f32"), ("tiny", "bf16"), ("t2v-1.3b", "bf16"), ("ti2v-5b", "bf16")])
 def test_time_embed(cfg_name, dtype):
     require_gpu()

@@ -95,15 +95,102 @@ def test_step_cfg_two_rows(dtype):
     _check(c, x_t, gt, ot)
 
 
-def test_step_ti2v_shaped_reduced_chain():
-    """TI2V-5B-shaped dims (48-channel latent, 100-channel input, dim 3072, 24 x 128 heads, FFN 14336,
-    512 text tokens, CFG batch 2, 4 Euler steps from t = 1) on a 32-token latent [48, 2, 8, 8]
-    with 3 blocks instead of 30, so the oracle finishes in seconds."""
+TI2V_LAYERS = 30  # "Wan2.2 TI2V-5B" §2.2: the 5B model's block count
+
+
+@pytest.fixture(scope="module")
+def ti2v_model():
+    """The TI2V-5B-shaped model with all 30 blocks (dim 3072, 24 x 128 heads, FFN 14336, 512 text tokens
+    of dim 4096, 48-channel latent, 100-channel input): host weights in float64 for the oracle and the same
+    values resident on the device.  Shared by the reduced-latent chain and the teacher-forced full-size
+    checks, which differ only in the latent's T, H, W."""
+    c = wi.get_config("ti2v-5b")
+    case(f"TI2V-shaped model: drawing {TI2V_LAYERS} blocks")
+    mw = wi.make_model_weights(c, seed=0)
+    bws32 = wi.make_blocks_weights(c, TI2V_LAYERS, seed=0)
+    model = R.DeviceModel(mw, c.dtype)
+    blocks = []
+    bws = []
+    for w in bws32:
+        blocks.append(R.DeviceBlock(w, c.dtype))
+        bws.append({k: np.asarray(v, np.float64) for k, v in w.items()})
+    del bws32
+    torch.cuda.synchronize()
+    case("TI2V-shaped model resident")
+    return mw, bws, model, blocks
+
+
+@pytest.mark.timeout(900)
+def test_step_ti2v_shaped_reduced_chain(ti2v_model):
+    """All 30 TI2V-5B-shaped blocks (48-channel latent, 100-channel input, dim 3072, 24 x 128 heads,
+    FFN 14336, 512 text tokens, CFG batch 2, 4 Euler steps from t = 1) on a 32-token latent [48, 2, 8, 8],
+    so the oracle runs the whole chain: every step's latent against the oracle's sampler."""
     require_gpu()
     c = wi.get_config("ti2v-5b").replace(T=2, H=8, W=8)
-    case("step TI2V-shaped reduced chain")
-    x_t, gt, ot = _run(c, layers=3, steps=4, t0=1.0)
-    _check(c, x_t, gt, ot)
+    mw, bws, model, blocks = ti2v_model
+    case(f"step TI2V-shaped reduced chain, {TI2V_LAYERS} blocks")
+    x_t, z = wi.make_latents(c, seed=0)
+    txt, img = wi.make_contexts(c, seed=0)
+    t_emb, i_emb = R.embed_contexts(c, model, txt, img, c.B)
+    caches = R.cross_kv_all(c, blocks, t_emb, i_emb, c.B)
+    buf = R.alloc_step(c, c.B)
+    xg, zg = dev(x_t), dev(z)
+    steps, dt = c.steps, -1.0 / c.steps
+    gpu_traj = []
+    for k in range(steps):
+        R.denoise_step(c, model, blocks, caches, xg, zg, 1.0 + k * dt, dt, c.guidance, buf, c.B)
+        gpu_traj.append(host(xg))
+    case("oracle: the 30-block chain, 4 steps")
+    _, traj = oracle.sample(x_t, z, steps, c.guidance, mw, bws, txt, img, c.heads, t0=1.0, ln_eps=c.ln_eps,
+                            rms_eps=c.rms_eps, theta=c.rope_theta, freq_dim=c.freq_dim, out_channels=c.out_channels)
+    x0 = np.asarray(x_t, np.float64)
+    for k, (g, o) in enumerate(zip(gpu_traj, traj)):
+        e_x, e_u = rel_l2(g, o), rel_l2(g - x0, o - x0)
+        print(f"[{c.name} x{TI2V_LAYERS}] step {k}: rel-L2 x={e_x:.3e} x - x_T={e_u:.3e}", flush=True)
+        assert e_x <= TOL[c.dtype] and e_u <= TOL[c.dtype]
+
+
+@pytest.mark.timeout(900)
+def test_step_ti2v_teacher_forced_full_size(ti2v_model):
+    """The full TI2V-5B-shaped sampling run on the GPU (latent [48, 31, 44, 80] -> 27280 tokens, CFG batch 2,
+    30 blocks, 4 Euler steps from t = 1).  Blocks 0, 15 and 29 of steps 0 and 3 are checked teacher-forced:
+    the oracle runs each of them from the GPU's own block input (x, e0 and the embedded text the GPU
+    holds at that point), on sampled query rows, so errors do not compound over the chain."""
+    require_gpu()
+    c = wi.get_config("ti2v-5b")
+    mw, bws, model, blocks = ti2v_model
+    case(f"step TI2V full size: S={c.S}, B={c.B}, {TI2V_LAYERS} blocks, 4 steps")
+    x_t, z = wi.make_latents(c, seed=0)
+    txt, img = wi.make_contexts(c, seed=0)
+    t_emb, i_emb = R.embed_contexts(c, model, txt, img, c.B)
+    caches = R.cross_kv_all(c, blocks, t_emb, i_emb, c.B)
+    buf = R.alloc_step(c, c.B)
+    xg, zg = dev(x_t), dev(z)
+    steps, dt = c.steps, -1.0 / c.steps
+    rows = wi.sample_rows(c, 32, seed=11)
+    taps = {}
+    for k in range(steps):
+        tap = {i: [] for i in (0, 15, 29)} if k in (0, 3) else None
+        R.denoise_step(c, model, blocks, caches, xg, zg, 1.0 + k * dt, dt, c.guidance, buf, c.B, tap=tap)
+        if tap is not None:
+            for i, lst in tap.items():
+                d = lst[0]
+                taps[(k, i)] = {"x_in": host(d["x_in"]), "e0": host(d["e0"]), "x_out": host(d["x_out"])[:, rows]}
+            del tap
+    assert np.isfinite(host(xg)).all()
+    t_emb_h = host(t_emb)
+    kv = {}
+    for (k, i), d in sorted(taps.items()):
+        case(f"oracle: step {k} block {i}, {len(rows)} rows")
+        if i not in kv:
+            kv[i] = [oracle.cross_kv(t_emb_h[b], bws[i]["wck"], bws[i]["bck"], bws[i]["wcv"], bws[i]["bcv"]) + (None, None)
+                     for b in range(c.B)]
+        ref = oracle.block_fwd(d["x_in"], d["e0"], bws[i], kv[i], c.grid, c.heads, rows=rows, ln_eps=c.ln_eps,
+                               rms_eps=c.rms_eps, theta=c.rope_theta)
+        xin = d["x_in"][:, rows]
+        e_x, e_dx = rel_l2(d["x_out"], ref), rel_l2(d["x_out"] - xin, ref - xin)
+        print(f"[{c.name} teacher-forced] step {k} block {i}: rel-L2 x_out={e_x:.3e} dx={e_dx:.3e}", flush=True)
+        assert e_x <= TOL[c.dtype] and e_dx <= TOL[c.dtype]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

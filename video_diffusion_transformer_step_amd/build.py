@@ -26,22 +26,21 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-I", INCLUDE, 
          "-Wno-unused-command-line-argument"]
 
 
-def _compile(src: str, build_dir: str = BUILD, defines=()) -> str:
+def _compile(src: str, build_dir: str = BUILD) -> str:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(jobs: int = 8, verbose: bool = False, out: str = LIB, defines=()) -> str:
-    """Compile every HIP source and link `out` (default: the in-tree libwan.so).  `defines` are
-    extra -D macros (tuning variants)."""
+def build(jobs: int = 8, verbose: bool = False, out: str = LIB) -> str:
+    """Compile every HIP source and link `out` (default: the in-tree libwan.so)."""
     build_dir = BUILD if out == LIB else out + ".objs"
     os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(SOURCES)))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, build_dir, defines), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, build_dir), SOURCES))
     tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

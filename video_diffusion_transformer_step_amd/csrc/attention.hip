@@ -515,7 +515,7 @@ __device__ __forceinline__ void pv_products(const FragAddr<T, HD>& fa, const cha
 }
 
 // ---------------------------------------------------------------------------
-// Four-wave kernel (fp32, and bf16 when WAN_ATTN_PP is 0): one barrier per tile.
+// Four-wave kernel (fp32, and bf16 cross-attention): one barrier per tile.
 // ---------------------------------------------------------------------------
 
 // One pipelined tile step t with static slot parity P = t % 2: issue V(t+1) -> v[1-P] and
@@ -1167,17 +1167,13 @@ hipError_t launch_q8_hd(const uint8_t* q, int64_t q_bs, int64_t q_ss, const floa
   return hipGetLastError();
 }
 
-#ifndef WAN_ATTN_PP
-#define WAN_ATTN_PP 1
-#endif
-
 // KIND only separates the self-attention (0) and cross-attention (1) kernel symbols in profiles.
 // bf16 self-attention uses the ping-pong kernel (256 queries per workgroup); cross-attention (a few
 // hundred keys, where the per-stream prologue dominates) and fp32 use the four-wave kernel.
 template <typename T, int HD, int KIND>
 hipError_t launch_hd(const T* q, int64_t q_bs, int64_t q_ss, KVStream kv, int B, int S, int H, float c_log2,
                      T* o, int64_t o_bs, int64_t o_ss, float* lse, const KeySplit& ks, int accum, hipStream_t s) {
-  if constexpr (sizeof(T) == 2 && WAN_ATTN_PP && KIND == 0) {
+  if constexpr (sizeof(T) == 2 && KIND == 0) {
     dim3 grid((unsigned)ceil_div(S, 256), (unsigned)H, (unsigned)(B * ks.n));
     hipLaunchKernelGGL((attention_pp_kernel<T, HD, KIND>), grid, dim3(512), 0, s, q, q_bs, q_ss, kv, S, H, c_log2, o,
                        o_bs, o_ss, lse, ks);
@@ -1201,7 +1197,7 @@ hipError_t launch_attention(const T* q, int64_t q_bs, int64_t q_ss, KVStream kv,
   if (ks.n > 1 && (ks.chunk <= 0 || ks.chunk % KT != 0 || (int64_t)(ks.n - 1) * ks.chunk >= kv.L))
     return hipErrorInvalidValue;
   // the ping-pong kernel (bf16 self-attention) stores only; accumulation is the four-wave kernel's
-  if (accumulate && ((sizeof(T) == 2 && WAN_ATTN_PP && kind == 0) || ks.n > 1)) return hipErrorInvalidValue;
+  if (accumulate && ((sizeof(T) == 2 && kind == 0) || ks.n > 1)) return hipErrorInvalidValue;
   const int acc = accumulate ? 1 : 0;
   const float c_log2 = scale * 1.4426950408889634f;
   if (hd == 128) {
@@ -1336,7 +1332,7 @@ template hipError_t launch_attention<bf16>(const bf16*, int64_t, int64_t, KVStre
 
 template <typename T>
 void attention_tile(int kind, int& rows, int& per_cu) {
-  if (sizeof(T) == 2 && WAN_ATTN_PP && kind == 0) {
+  if (sizeof(T) == 2 && kind == 0) {
     rows = 256;  // ping-pong kernel: 8 waves, one workgroup per compute unit
     per_cu = 1;
   } else {

@@ -535,10 +535,6 @@ hipError_t launch_cfg(const T* A, int64_t lda, const T* W, int64_t ldw, int M, i
   return hipGetLastError();
 }
 
-#ifndef WAN_GEMM_FORCE
-#define WAN_GEMM_FORCE 0
-#endif
-
 // Tile choice.  bf16 products with many rows and K a multiple of 128 use the asynchronous-copy
 // kernel (256 x 256 tiles, 8 waves of 64 x 128, BK 32, four LDS stages); other bf16 products with
 // many rows use the register-staged kernel with 256-row tiles; small products and fp32 use 128 x 128.
@@ -552,7 +548,6 @@ hipError_t run_gemm(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int
     if (M >= 4096 && N >= 1024 && K % 128 == 0 && lda % 8 == 0 && ldw % 8 == 0) cfg = 1;
     else if (M >= 4096 && N % 256 == 0 && N >= 1024) cfg = 2;
     else if (M >= 4096 && N % 128 == 0 && N >= 1024) cfg = 3;
-    if (WAN_GEMM_FORCE) cfg = WAN_GEMM_FORCE;
     if (cfg == 1) return launch_lds<256, 256, 32, 4, 4, 2>(A, lda, W, ldw, M, N, K, epi, s);
     if (cfg == 2) return launch_cfg<T, 256, 256, 4, 2>(A, lda, W, ldw, M, N, K, epi, s);
     if (cfg == 3) return launch_cfg<T, 256, 128, 4, 2>(A, lda, W, ldw, M, N, K, epi, s);

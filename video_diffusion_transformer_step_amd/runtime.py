@@ -183,11 +183,13 @@ def alloc_step(c, B, device="cuda", fp8_attn=False, fp8_gemm=False) -> StepBuffe
 
 def dit_forward(c, model: DeviceModel, blocks, caches, x_latent, z_img, t, buf: StepBuffers, B,
                 known_pixel_frames=None, fp8_attn=False, fp8_gemm=False, attn_cache=None,
-                attn_mode=0):
+                attn_mode=0, tap=None):
     """One DiT evaluation over B rows sharing the latent x_latent [1, C, T, H, W] (CFG rows see the same
     x_in).  Result in buf.v [B, C_out, T, H, W].  fp8_attn / fp8_gemm: quantised self-attention / E4M3
     products in every block (buf from alloc_step with the same flags).  attn_cache / attn_mode: the
-    attention cache of every block (AttnCache, its rows 0 .. B-1) and WAN_ATTN_CACHE_STORE / _REUSE."""
+    attention cache of every block (AttnCache, its rows 0 .. B-1) and WAN_ATTN_CACHE_STORE / _REUSE.
+    tap: None, or {block index: list}; for each listed block a dict of device copies of its input x,
+    its e0 and its output x is appended (for checking one block inside a running chain)."""
     cfg = cfg_of(c, fp8_attn=fp8_attn, fp8_gemm=fp8_gemm)
     one = x_latent.shape[0]
     for b in range(B):
@@ -200,21 +202,25 @@ def dit_forward(c, model: DeviceModel, blocks, caches, x_latent, z_img, t, buf: 
     L.patch_embed(cfg, buf.p[:B], c.in_channels, model.w_pe, model.b_pe, buf.x, buf.ws)
     L.time_embed(cfg, c.freq_dim, model.tw, [t] * B, buf.e, buf.e0)
     for i, (blk, kc) in enumerate(zip(blocks, caches)):
+        if tap is not None and i in tap:
+            tap[i].append({"x_in": buf.x[:B].clone(), "e0": buf.e0[:B].clone()})
         if attn_cache is None or attn_mode == L.WAN_ATTN_CACHE_OFF:
             L.dit_block_fwd(cfg, blk.bw, c.grid, B, buf.x, buf.e0, kc.kv, buf.ws)
         else:
             L.dit_block_fwd(cfg, blk.bw, c.grid, B, buf.x, buf.e0, kc.kv, buf.ws, attn_y=attn_cache.t[i],
                             attn_mode=attn_mode)
+        if tap is not None and i in tap:
+            tap[i][-1]["x_out"] = buf.x[:B].clone()
     L.head_fwd(cfg, model.hw, c.out_channels, B, c.S, buf.x, buf.e, buf.head_out, buf.ws)
     L.unpatchify(buf.head_out, buf.v)
     return buf.v
 
 
 def denoise_step(c, model, blocks, caches, x_latent, z_img, t, dt, guidance, buf: StepBuffers, B,
-                 known_pixel_frames=None, fp8_attn=False, fp8_gemm=False, attn_cache=None, attn_mode=0):
+                 known_pixel_frames=None, fp8_attn=False, fp8_gemm=False, attn_cache=None, attn_mode=0, tap=None):
     """x_latent <- x_latent + dt * v, v = CFG(v_cond, v_uncond) when B == 2 (row 0 conditional)."""
     v = dit_forward(c, model, blocks, caches, x_latent, z_img, t, buf, B, known_pixel_frames, fp8_attn, fp8_gemm,
-                    attn_cache, attn_mode)
+                    attn_cache, attn_mode, tap)
     L.fm_euler_step(x_latent, v[0:1], v[1:2] if B > 1 else None, guidance, dt)
     return x_latent
 

@@ -18,7 +18,7 @@ from dataclasses import dataclass
 import numpy as np
 
 __all__ = ["WanConfig", "CONFIGS", "get_config", "rng", "bf16_round", "normal",
-           "make_block_weights", "make_model_weights", "make_latents",
+           "make_block_weights", "make_blocks_weights", "make_model_weights", "make_latents",
            "make_contexts", "make_attention_qkv", "sample_rows", "TENSOR_IDS",
            "BLOCK_MATRICES"]
 
@@ -122,10 +122,14 @@ def rng(seed: int, stream_id: int, tensor: str, block: int = 0) -> np.random.Gen
 
 
 def bf16_round(a: np.ndarray) -> np.ndarray:
-    """Round float32 values to the nearest bf16 value (ties to even); result is float32."""
-    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32)
+    """Round float32 values to the nearest bf16 value (ties to even); result is float32.
+    (bits + 0x7FFF + lsb) with the low 16 bits cleared, in wrapping 32-bit arithmetic."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = (u >> 16) & 1
+    r += 0x7FFF
+    r += u
+    r &= 0xFFFF0000
+    return r.view(np.float32)
 
 
 def normal(seed, cfg: WanConfig, tensor: str, shape, std=1.0, mean=0.0, block=0,
@@ -168,6 +172,14 @@ def make_block_weights(cfg: WanConfig, block: int = 0, seed: int = 0, std: float
         w.update({"wki": n("wki", (d, d)), "bki": n("bki", (d,), quantize=False),
                   "wvi": n("wvi", (d, d)), "bvi": n("bvi", (d,), quantize=False)})
     return w
+
+
+def make_blocks_weights(cfg: WanConfig, nblocks: int, seed: int = 0, std: float = 0.02, workers: int = 16):
+    """``make_block_weights`` for blocks 0 .. nblocks-1, drawn on `workers` threads (every tensor has its
+    own stream, so the values do not depend on the thread count)."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=max(1, min(workers, nblocks))) as ex:
+        return list(ex.map(lambda i: make_block_weights(cfg, i, seed, std), range(nblocks)))
 
 
 def make_model_weights(cfg: WanConfig, seed: int = 0, std: float = 0.02):
