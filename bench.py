@@ -196,6 +196,126 @@ def measure_sharded(c, ulysses=4, ring=8, reps=10):
     return out
 
 
+def measure_attention_720p(reps=3):
+    """The 720p self-attention stress workload: latent [16, 21, 90, 160] -> 21 x 45 x 80 = 75600 tokens,
+    40 heads x 128, q, k, v ~N(0,1) bf16, 3D RoPE on q and k.  One wan_attention_fwd call (RoPE on q and k,
+    V transposed into the workspace, the attention kernel) timed with events on the stream it runs on;
+    FLOPs 4 S^2 dim."""
+    import torch
+
+    import wan_inputs as wi
+    from video_diffusion_transformer_step_amd import _lib as L
+    c = wi.get_config("attn-720p")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(720)
+    q, k, v = (torch.randn(1, c.S, c.heads, c.head_dim, generator=gen, device="cuda").to(torch.bfloat16)
+               for _ in range(3))
+    o = torch.empty_like(q)
+    ws = torch.empty(L.attention_ws_bytes(L.WAN_BF16, c.grid, 1, c.heads, c.head_dim), dtype=torch.uint8,
+                     device="cuda")
+    L.attention_fwd(q, k, v, c.grid, o, ws)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        L.attention_fwd(q, k, v, c.grid, o, ws)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / reps
+    assert bool(torch.isfinite(o).all()), "non-finite 720p attention output"
+    fl = 4 * c.S * c.S * c.heads * c.head_dim
+    tf = fl / (ms * 1e-3) / 1e12
+    del q, k, v, o, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"{c.name}: [1, {c.S}, {c.heads}, {c.head_dim}] bf16, 3D RoPE on grid {c.grid}",
+            "ms": round(ms, 3), "tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "flops": fl, "bound_ms_at_half_peak": round(fl / (0.5 * PEAK_BF16_TFLOPS * 1e12) * 1e3, 1),
+            "note": "whole wan_attention_fwd call (RoPE pass on q and k, V transpose, attention) per launch"}
+
+
+def measure_other_step(name, steps, warmup, seed=5):
+    """A whole denoise-step workload other than the headline one, on device-drawn random weights:
+    i2v-14b = the 14B-shaped image-to-video step (40 blocks, dim 5120, CFG batch 2, text + image
+    cross-attention), ti2v-5b = the TI2V-5B-shaped sampling run (30 blocks, dim 3072, CFG batch 2,
+    100-channel input, 4 Euler steps from t = 1, timed as one whole run)."""
+    import numpy as np
+    import torch
+
+    import wan_inputs as wi
+    from video_diffusion_transformer_step_amd import _lib as L
+    from video_diffusion_transformer_step_amd import runtime as R
+    c = wi.get_config(name)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    model = R.DeviceModel(wi.make_model_weights(c, seed=seed), c.dtype)
+    blocks = [R.DeviceBlock(None, c.dtype, tensors=device_block_tensors(c, gen)) for _ in range(c.layers)]
+    x_t, z = wi.make_latents(c, seed=seed)
+    txt, img = wi.make_contexts(c, seed=seed)
+    t_emb, i_emb = R.embed_contexts(c, model, txt, img, c.B)
+    caches = R.cross_kv_all(c, blocks, t_emb, i_emb, c.B)
+    buf = R.alloc_step(c, c.B)
+    xg = torch.from_numpy(x_t).cuda()
+    zg = torch.from_numpy(z).cuda() if z is not None else None
+    nsteps = c.steps if name == "ti2v-5b" else steps
+    dt = -1.0 / nsteps
+    for k in range(warmup):
+        R.denoise_step(c, model, blocks, caches, xg, zg, 1.0 + k * dt, dt, c.guidance, buf, c.B)
+    torch.cuda.synchronize()
+    xg.copy_(torch.from_numpy(x_t))
+    timer = L.KernelTimer(capacity=nsteps * c.layers, kernels=("self_attn",))
+    t0 = time.perf_counter()
+    with timer:
+        for k in range(nsteps):
+            R.denoise_step(c, model, blocks, caches, xg, zg, 1.0 + k * dt, dt, c.guidance, buf, c.B)
+    torch.cuda.synchronize()
+    total_ms = (time.perf_counter() - t0) * 1e3
+    assert np.isfinite(xg.float().cpu().numpy()).all(), f"non-finite latent after the {name} steps"
+    fl_step, attn_fl = step_flops(c, c.layers)
+    ms = total_ms / nsteps
+    a = float(np.mean(timer.times_ms().get("self_attn", [float("nan")])))
+    out = {"workload": (f"{c.name}: latent [{c.latent_channels},{c.T},{c.H},{c.W}] -> {c.S} tokens, "
+                        f"{c.layers} blocks, dim {c.dim}, {c.heads}x{c.head_dim}, FFN {c.ffn_dim}, B {c.B}"
+                        + (f", image {c.img_len} keys" if c.img_len else "")),
+           "ms_per_step": round(ms, 2), "ms_per_block": round(ms / c.layers, 3),
+           "step_tflops": round(fl_step / (ms * 1e-3) / 1e12, 1),
+           "step_frac_of_bf16_peak": round(fl_step / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "attention_ms": round(a, 3),
+           "attention_frac_of_bf16_peak": round(attn_fl / (a * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    if name == "ti2v-5b":
+        out["sampling_run_ms"] = round(total_ms, 1)
+        out["steps"] = nsteps
+    del blocks, caches, buf, model, xg, zg
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_tiny_full():
+    """The oracle in full on the tiny image-to-video config: build the 36-channel input, one DiT
+    evaluation (patchify, patch embedding, time embedding, one block, head, unpatchify) and the Euler
+    step, timed end to end on the host (float64 NumPy; best of 3)."""
+    import threadpoolctl
+
+    import oracle
+    import wan_inputs as wi
+    c = wi.get_config("tiny")
+    mw = wi.make_model_weights(c, seed=0)
+    bw = [wi.make_block_weights(c, 0, seed=0)]
+    x_t, z = wi.make_latents(c, seed=0)
+    txt, img = wi.make_contexts(c, seed=0)
+    cores = len(os.sched_getaffinity(0))
+    best = float("inf")
+    with threadpoolctl.threadpool_limits(cores):
+        for _ in range(3):
+            t = time.perf_counter()
+            v = oracle.dit_fwd(oracle.build_i2v_input(x_t, z), c.t, mw, bw, txt, img, c.heads, freq_dim=c.freq_dim,
+                               out_channels=c.out_channels)
+            oracle.euler_step(x_t, v, c.dt)
+            best = min(best, time.perf_counter() - t)
+    return {"ms_per_step": round(best * 1e3, 2), "cores": cores,
+            "sample": (f"{c.name}: the whole step (I2V input, patchify, embeddings, 1 block of dim {c.dim}, head, "
+                       f"unpatchify, Euler) on {c.S} tokens, in full, best of 3")}
+
+
 def cpu_baseline(c, layers, seed=0):
     """The CPU oracle on a bounded sample: one block in sampled-row mode (K/V for all tokens,
     then R1 and R2 query rows), extrapolated to all S rows and `layers` blocks."""
@@ -375,6 +495,10 @@ def main():
                     help="capture each timed step as a HIP graph beforehand and replay it (launch-bound small shapes)")
     ap.add_argument("--no-sharded", action="store_true",
                     help="skip the one-GPU shares of sequence-parallel attention (Ulysses head shard, ring step, merge)")
+    ap.add_argument("--no-720p", action="store_true",
+                    help="skip the 75600-token self-attention stress measurement")
+    ap.add_argument("--no-other-steps", action="store_true",
+                    help="skip the 14B-shaped I2V step and the TI2V-5B-shaped sampling run")
     ap.add_argument("--no-device-probe", action="store_true",
                     help="skip the device ceilings (register-only MFMA rate, plain copy rate)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -579,11 +703,25 @@ def main():
         two_expert["ms_per_step_vs_one_expert"] = round(two_expert["ms_per_step"] / ms_per_step, 3)
         log(f"two experts: {json.dumps(two_expert)}")
 
+    attn720 = None
+    if not args.no_720p:
+        attn720 = measure_attention_720p()
+        log(f"720p attention: {json.dumps(attn720)}")
+
+    other = None
+    if not args.no_other_steps and args.config == "t2v-1.3b":
+        other = {}
+        for name in ("i2v-14b", "ti2v-5b"):
+            other[name] = measure_other_step(name, steps=2, warmup=1)
+            log(f"{name}: {json.dumps(other[name])}")
+
     cpu = None
     if not args.no_cpu_baseline:
         t = time.perf_counter()
         cpu = cpu_baseline(c, layers, seed=seed)
-        log(f"cpu baseline {time.perf_counter() - t:.1f} s: {cpu['value']} ms/step")
+        cpu["tiny_full"] = cpu_tiny_full()
+        log(f"cpu baseline {time.perf_counter() - t:.1f} s: {cpu['value']} ms/step; tiny in full "
+            f"{cpu['tiny_full']['ms_per_step']} ms")
 
     traffic = counters_traffic(attn_avg)
     out = {
@@ -623,6 +761,8 @@ def main():
         "fp8_attention_step": fp8.get("fp8_attention_step"),
         "fp8_step": fp8.get("fp8_step"),
         "sharded_attention": sharded,
+        "attention_720p": attn720,
+        "other_workloads": other,
         "diffusion_cache": cache,
         "two_expert": two_expert,
         "cpu_baseline": cpu,

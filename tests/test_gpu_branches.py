@@ -117,7 +117,7 @@ def _check_branches(c, x, e0, bw, t_emb, i_emb, rows, ref, tol_y, tol_ffn, tol_c
     gf, _ = _gpu(c, x, e0f, bwf, t_emb, i_emb, fp8_attn=fp8_attn, fp8_gemm=fp8_gemm)
     e_f = rel_l2(_rows(gf, rows) - xr, ref["ffn"])
     e_dx = rel_l2(_rows(got, rows) - xr, ref["dx"])
-    print(f"[branches {c.name}{label}] rel-L2 self-attention y={e_y:.3e} cross={e_c:.3e} ffn={e_f:.3e} "
+    print(f"[branches {c.name} {c.dtype} S={c.S} B={c.B} dim={c.dim}{label}] rel-L2 self-attention y={e_y:.3e} cross={e_c:.3e} ffn={e_f:.3e} "
           f"dx={e_dx:.3e}", flush=True)
     assert e_y <= tol_y and e_c <= tol_cross and e_f <= tol_ffn
     return e_dx
