@@ -232,6 +232,20 @@ int wan_dit_block_fwd_cached(const wan_block_cfg* cfg, const wan_block_weights* 
                              const float* e0, const wan_cross_kv* kv, float* attn_y, int32_t attn_mode, void* ws,
                              size_t ws_bytes, wan_stream_t stream);
 
+/* The block for callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): wan_dit_block_fwd without ws / ws_bytes.  Its scratch is a
+ * static device array of WAN_NOALLOC_SCRATCH_BYTES in the library, one per device, held until the process
+ * ends; the call allocates nothing (no hipMalloc / hipFree / allocating library routine).  The caller
+ * still passes x, e0, the weights and kv as for wan_dit_block_fwd, and the result is the same.
+ * Errors: as wan_dit_block_fwd, and WAN_EWORKSPACE (nothing enqueued) when
+ * wan_dit_block_workspace_bytes(cfg, grid, B) exceeds WAN_NOALLOC_SCRATCH_BYTES.
+ * Every call on one device shares that device's array: calls that overlap on one device (two streams,
+ * two threads) race and must be serialised by the caller.  The block never reads scratch it has not
+ * written in the same call, so what an earlier call left there does not matter. */
+#define WAN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int wan_dit_block_fwd_noalloc(const wan_block_cfg* cfg, const wan_block_weights* w, wan_grid grid, int32_t B,
+                              float* x, const float* e0, const wan_cross_kv* kv, wan_stream_t stream);
+
 /* a11 -- head ([I2V] §5.5): (shift, scale) = head_mod + e[b];
  * out [B*S, 4*C_out] float32 = (LN(x)(1 + scale) + shift) wh^T + bh, x [B, S, dim] float32,
  * e [B, dim] float32.  Follow with wan_unpatchify.  Workspace: wan_head_workspace_bytes(). */

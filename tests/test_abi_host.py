@@ -120,6 +120,27 @@ def test_block_validation(lib):
                ws_need - 1, None) == L.WAN_EWORKSPACE
 
 
+def test_block_noalloc_validation(lib):
+    """wan_dit_block_fwd_noalloc rejects a block whose workspace exceeds its static scratch, and bad
+    arguments, on the host before touching the device (so these calls need no GPU)."""
+    m = re.search(r"#define WAN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == L.NOALLOC_SCRATCH_BYTES
+    kv = L.CrossKV(FAKE, FAKE, None, None)
+    w = L.BlockWeights(*([FAKE] * 17))
+    big = _cfg(dtype=L.WAN_BF16, dim=1536, heads=12, head_dim=128, ffn_dim=8960)
+    g = L.Grid(21, 30, 52)  # 32760 tokens: about 1.1 GB of workspace
+    assert lib.wan_dit_block_workspace_bytes(C.byref(big), g, 1) > L.NOALLOC_SCRATCH_BYTES
+    assert lib.wan_dit_block_fwd_noalloc(C.byref(big), C.byref(w), g, 1, FAKE, FAKE, C.byref(kv), None) \
+        == L.WAN_EWORKSPACE
+    assert "scratch" in _err(lib)
+    assert lib.wan_dit_block_fwd_noalloc(C.byref(_cfg(dim=130)), C.byref(w), L.Grid(2, 4, 4), 1, FAKE, FAKE,
+                                         C.byref(kv), None) == L.WAN_EINVAL
+    assert lib.wan_dit_block_fwd_noalloc(C.byref(_cfg()), C.byref(w), L.Grid(0, 4, 4), 1, FAKE, FAKE, C.byref(kv),
+                                         None) == L.WAN_EINVAL
+    assert lib.wan_dit_block_fwd_noalloc(C.byref(_cfg()), C.byref(w), L.Grid(2, 4, 4), 0, FAKE, FAKE, C.byref(kv),
+                                         None) == L.WAN_EINVAL
+
+
 def test_other_entry_validation(lib):
     cfg = _cfg()
     tw = L.TimeWeights(*([FAKE] * 6))

@@ -78,6 +78,8 @@ _SIGS = {
                            vp, C.c_size_t, vp], C.c_int),
     "wan_dit_block_fwd_cached": ([C.POINTER(BlockCfg), C.POINTER(BlockWeights), Grid, C.c_int32, vp, vp,
                                   C.POINTER(CrossKV), vp, C.c_int32, vp, C.c_size_t, vp], C.c_int),
+    "wan_dit_block_fwd_noalloc": ([C.POINTER(BlockCfg), C.POINTER(BlockWeights), Grid, C.c_int32, vp, vp,
+                                   C.POINTER(CrossKV), vp], C.c_int),
     "wan_head_workspace_bytes": ([C.POINTER(BlockCfg), C.c_int64], C.c_size_t),
     "wan_head_fwd": ([C.POINTER(BlockCfg), C.POINTER(HeadWeights), C.c_int32, C.c_int32, C.c_int32, vp, vp, vp, vp,
                       C.c_size_t, vp], C.c_int),
@@ -254,6 +256,15 @@ def dit_block_fwd(cfg, bw: BlockWeights, grid, B, x, e0, kv: CrossKV, ws, stream
         _check(lib().wan_dit_block_fwd_cached(C.byref(cfg), C.byref(bw), Grid(*grid), B, _p(x), _p(e0), C.byref(kv),
                                               _p(attn_y), attn_mode, _p(ws), ws.numel() * ws.element_size(),
                                               _stream(stream)), "wan_dit_block_fwd_cached")
+
+
+# size of the static scratch behind wan_dit_block_fwd_noalloc (WAN_NOALLOC_SCRATCH_BYTES in wan.h)
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def dit_block_fwd_noalloc(cfg, bw: BlockWeights, grid, B, x, e0, kv: CrossKV, stream=None):
+    _check(lib().wan_dit_block_fwd_noalloc(C.byref(cfg), C.byref(bw), Grid(*grid), B, _p(x), _p(e0), C.byref(kv),
+                                           _stream(stream)), "wan_dit_block_fwd_noalloc")
 
 
 def head_ws_bytes(cfg, tokens):

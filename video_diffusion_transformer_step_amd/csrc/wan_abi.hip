@@ -8,6 +8,7 @@
 #include "wan.h"
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "wan_internal.h"
 
@@ -550,6 +551,51 @@ int wan_dit_block_fwd_cached(const wan_block_cfg* cfg, const wan_block_weights* 
   if (cfg->dtype == WAN_BF16)
     return block_fwd_t<bf16>(*cfg, *w, grid, B, x, e0, *kv, ws, hs(stream), attn_y, attn_mode);
   return block_fwd_t<float>(*cfg, *w, grid, B, x, e0, *kv, ws, hs(stream), attn_y, attn_mode);
+}
+
+// ---- the block without a caller workspace: the scratch lives in a static device array ----------------
+// One array per device the library runs on, held until the process ends.  In host code `scratch` names
+// a host-side stand-in: its device address comes from hipGetSymbolAddress, taken once per device (with
+// that device current) and kept in g_scratch_dev; only that address is ever passed to kernels.
+static __device__ __align__(256) unsigned char scratch[WAN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[SCRATCH_MAX_DEVICES];
+
+// Device address of the current device's scratch array (looked up on the first call on that device).
+int scratch_address(void** out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return fail(WAN_EUNSUPPORTED, "device %d has no scratch slot", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (p == nullptr) return fail(WAN_EHIP, "hipGetSymbolAddress returned no address for the scratch array");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return WAN_OK;
+}
+
+}  // namespace
+
+int wan_dit_block_fwd_noalloc(const wan_block_cfg* cfg, const wan_block_weights* w, wan_grid grid, int32_t B,
+                              float* x, const float* e0, const wan_cross_kv* kv, wan_stream_t stream) {
+  WAN_TRY(check_cfg(cfg));
+  WAN_TRY(check_grid(grid));
+  if (B <= 0) return fail(WAN_EINVAL, "B must be positive");
+  const size_t need = wan_dit_block_workspace_bytes(cfg, grid, B);
+  if (need > WAN_NOALLOC_SCRATCH_BYTES)
+    return fail(WAN_EWORKSPACE,
+                "block needs %zu bytes of scratch; wan_dit_block_fwd_noalloc holds %zu (use wan_dit_block_fwd with "
+                "a caller workspace)", need, (size_t)WAN_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  WAN_TRY(scratch_address(&ws));
+  return wan_dit_block_fwd(cfg, w, grid, B, x, e0, kv, ws, WAN_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t wan_head_workspace_bytes(const wan_block_cfg* cfg, int64_t tokens) {
