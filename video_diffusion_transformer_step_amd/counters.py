@@ -111,13 +111,15 @@ def reduce(folders):
     res = {}
     for label, e in per.items():
         res[label] = {"kernel": e["name"], "n": {c: len(v) for c, v in e["counters"].items()},
-                      "mean": {c: sum(v) / len(v) for c, v in e["counters"].items()}}
+                      "mean": {c: sum(v) / len(v) for c, v in e["counters"].items()},
+                      "max": {c: max(v) for c, v in e["counters"].items()}}
     return res
 
 
 def derive(res, copy_bytes):
     out = {}
-    cp = res.get("copy", {}).get("mean", {})
+    # the calibration copy is the largest device copy of the run (the runtime also copies small buffers)
+    cp = res.get("copy", {}).get("max", {})
     fscale = (copy_bytes / 1024.0) / cp["FETCH_SIZE"] if cp.get("FETCH_SIZE") else None
     wscale = (copy_bytes / 1024.0) / cp["WRITE_SIZE"] if cp.get("WRITE_SIZE") else None
     probe = res.get("mfma_probe", {}).get("mean", {})
