@@ -32,8 +32,14 @@ PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (int8: 5.0 POP/s)
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 METRIC = "ms per DiT denoise step + attention TFLOP/s (% MFMA peak) at 32760 tokens"
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "self_attn_counters.json")
-ATTN_SRC = os.path.join(ROOT, "video_diffusion_transformer_step_amd", "csrc", "attention.hip")
+BLOCK_COUNTERS_FILE = os.path.join(ROOT, "profiles", "block_kernels_counters.json")
+CSRC = os.path.join(ROOT, "video_diffusion_transformer_step_amd", "csrc")
+# which source file holds each block launch's kernel (its counters are stale once that file changes)
+KERNEL_SOURCE = {"ln1": "norm.hip", "ln2": "norm.hip", "ln3": "norm.hip", "qk_norm_rope": "norm.hip",
+                 "vt_tail": "layout.hip", "mod_combine": "layout.hip", "self_attn": "attention.hip",
+                 "cross_attn": "attention.hip", "qkv_gemm": "gemm.hip", "o_gemm": "gemm.hip",
+                 "cross_q_gemm": "gemm.hip", "cross_o_gemm": "gemm.hip", "ffn1_gemm": "gemm.hip",
+                 "ffn2_gemm": "gemm.hip"}
 
 
 def log(msg):
@@ -78,18 +84,33 @@ def device_block_tensors(c, gen, device="cuda"):
     return g
 
 
-def counters_traffic(launch_ms):
-    """HBM bytes per launch of the self-attention kernel from committed rocprofv3 counter
-    runs, only while the kernel source is the one the counters were taken on."""
+def counters_traffic():
+    """HBM bytes per launch of the self-attention kernel (copy-calibrated FETCH_SIZE + WRITE_SIZE) from
+    the committed rocprofv3 reduction, only while the kernel source is the one the counters were taken
+    on."""
+    e = block_counters().get("self_attn")
+    return None if e is None or "hbm_bytes" not in e else float(e["hbm_bytes"])
+
+
+def block_counters():
+    """Per-launch counter figures of the block's kernels from the committed rocprofv3 reduction
+    (profiles/block_kernels_counters.json, written by video_diffusion_transformer_step_amd.counters), each
+    kept only while its kernel's source file is the one the counters were taken on."""
     try:
-        with open(COUNTERS_FILE) as fh:
+        with open(BLOCK_COUNTERS_FILE) as fh:
             rec = json.load(fh)
-        src_hash = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
-        if rec.get("attention_hip_sha256") != src_hash:
-            return None
-        return float(rec["hbm_bytes_per_launch"])
-    except (OSError, ValueError, KeyError):
-        return None
+    except (OSError, ValueError):
+        return {}
+    taken = rec.get("meta", {}).get("source_sha256", {})
+    out = {}
+    for label, e in rec.get("kernels", {}).items():
+        src = KERNEL_SOURCE.get(label)
+        if src is None or taken.get(src) is None:
+            continue
+        if hashlib.sha256(open(os.path.join(CSRC, src), "rb").read()).hexdigest() != taken[src]:
+            continue
+        out[label] = e
+    return out
 
 
 def measure_device():
@@ -613,15 +634,41 @@ def main():
         # algorithmic bytes of the bandwidth-bound kernels: LN reads fp32 x and writes the bf16 operand;
         # the QK norm + RoPE pass reads and writes bf16 q and k
         hbm_bytes = {"ln1": 6 * S * d, "ln2": 6 * S * d, "ln3": 6 * S * d, "qk_norm_rope": 8 * S * d}
+        # algorithmic bytes of every launch (each operand read once, each result written once; the
+        # residual products read and write the fp32 x), per batch row except the weights
+        L_ctx = c.text_len + c.img_len
+        alg_bytes = dict(hbm_bytes)
+        alg_bytes.update({
+            "qkv_gemm": 2 * S * d + 2 * S * 3 * d, "o_gemm": 2 * S * d + 8 * S * d,
+            "cross_q_gemm": 4 * S * d, "cross_o_gemm": 2 * S * d + 8 * S * d, "ffn1_gemm": 2 * S * d + 2 * S * f,
+            "ffn2_gemm": 2 * S * f + 8 * S * d, "self_attn": 8 * S * d, "cross_attn": 4 * S * d + 4 * L_ctx * d})
+        w_bytes = {"qkv_gemm": 6 * d * d, "o_gemm": 2 * d * d, "cross_q_gemm": 2 * d * d, "cross_o_gemm": 2 * d * d,
+                   "ffn1_gemm": 2 * f * d, "ffn2_gemm": 2 * f * d}
+        # counter-backed figures (only for the workload the counters were taken on)
+        cnt = block_counters() if args.config == "t2v-1.3b" else {}
         breakdown = {}
         for k_, v in bd.items():
             ms = float(np.sum(v)) / layers  # per block (the I2V cross-attention is two launches)
             e = {"ms": round(ms, 4)}
             if k_ in fl:
                 e["tflops"] = round(fl[k_] * c.B / (ms * 1e-3) / 1e12, 1)
+                e["frac_of_bf16_peak"] = round(e["tflops"] / PEAK_BF16_TFLOPS, 4)
+            if k_ in alg_bytes:
+                e["alg_bytes"] = alg_bytes[k_] * c.B + w_bytes.get(k_, 0)
             if k_ in hbm_bytes:
                 e["gbs"] = round(hbm_bytes[k_] * c.B / (ms * 1e-3) / 1e9, 1)
                 e["frac_of_hbm"] = round(e["gbs"] / PEAK_HBM_GBS, 3)
+            ce = cnt.get(k_)
+            if ce is not None:
+                # L2-miss bytes (FETCH_SIZE + WRITE_SIZE, copy-calibrated; MALL hits included) per launch,
+                # and the MFMA busy fraction relative to the register-only probe, from the counter runs
+                if "hbm_bytes" in ce:
+                    e["counter_bytes"] = round(ce["hbm_bytes"])
+                    e["counter_gbs"] = round(ce["hbm_bytes"] / (ms * 1e-3) / 1e9, 1)
+                    if k_ in hbm_bytes:
+                        e["counter_frac_of_hbm"] = round(e["counter_gbs"] / PEAK_HBM_GBS, 3)
+                if ce.get("mfma_busy_vs_probe"):
+                    e["counter_mfma_busy_vs_probe"] = round(ce["mfma_busy_vs_probe"], 3)
             breakdown[k_] = e
         breakdown["block_sum_ms"] = round(sum(e["ms"] for e in breakdown.values()), 3)
         log(f"breakdown: {json.dumps(breakdown)}")
@@ -723,7 +770,7 @@ def main():
         log(f"cpu baseline {time.perf_counter() - t:.1f} s: {cpu['value']} ms/step; tiny in full "
             f"{cpu['tiny_full']['ms_per_step']} ms")
 
-    traffic = counters_traffic(attn_avg)
+    traffic = counters_traffic() if args.config == "t2v-1.3b" else None  # counters are of that workload
     out = {
         "metric": METRIC,
         "value": round(ms_per_step, 3),

@@ -16,7 +16,12 @@ Derived figures:
   * VALU and LDS activity: SQ_ACTIVE_INST_VALU, SQ_ACTIVE_INST_LDS per GRBM_GUI_ACTIVE cycle and wave,
     and SQ_LDS_BANK_CONFLICT against SQ_INSTS_LDS.
 
-Usage: python -m video_diffusion_transformer_step_amd.counters DIR [DIR ...] --out JSON
+With --trace DIR (a `rocprofv3 --kernel-trace --output-format csv` folder of the same workload) the
+launches are labelled the same way and their mean durations added; with --md FILE a table of the
+figures is written as markdown.
+
+Usage: python -m video_diffusion_transformer_step_amd.counters DIR [DIR ...] --out JSON [--trace DIR]
+       [--md FILE] [--command TEXT]
 """
 from __future__ import annotations
 
@@ -26,6 +31,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 
 # Order of the launches of one bf16 block (no attention cache, no quantised path).
@@ -70,11 +76,17 @@ def read_dispatches(folder):
     return out
 
 
+# launches that mark a block as not the plain bf16 one (quantised attention, E4M3 products, cache modes)
+FOREIGN = ("EpiScaled", "q8", "quant", "e4m3", "cache")
+
+
 def label_dispatches(disp):
-    """[(label, dispatch)] for block launches, plus the copy and probe dispatches."""
+    """[(label, dispatch)] for the launches of complete bf16 blocks, plus the copy and probe dispatches.
+    A block's launches are kept only once its last launch (FFN2) is seen and none of its launches
+    belongs to another block variant."""
     labelled = []
     seen = {}
-    in_block = False
+    cur = None  # the current block's labelled launches, or None outside a block
     for did in sorted(disp):
         d = disp[did]
         name = d["name"]
@@ -86,19 +98,43 @@ def label_dispatches(disp):
             continue
         if "mod_combine" in name:
             seen = {}
-            in_block = True
-        if not in_block:
+            cur = []
+        if cur is None:
+            continue
+        if any(f in name for f in FOREIGN):
+            cur = None
             continue
         for frag, labels in BY_NAME:
             if frag in name:
                 k = seen.get(frag, 0)
                 seen[frag] = k + 1
                 if k < len(labels):
-                    labelled.append((labels[k], d))
+                    cur.append((labels[k], d))
                     if labels[k] == "ffn2_gemm":
-                        in_block = False
+                        labelled.extend(cur)
+                        cur = None
                 break
     return labelled
+
+
+def read_trace(folder):
+    """{dispatch id: {"name", "ns"}} from one rocprofv3 kernel-trace output folder."""
+    out = {}
+    for path in glob.glob(os.path.join(folder, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path, newline="") as fh:
+            for row in csv.DictReader(fh):
+                did = int(_col(row, "Dispatch_Id", "Dispatch_ID", "Correlation_Id"))
+                ns = int(_col(row, "End_Timestamp")) - int(_col(row, "Start_Timestamp"))
+                out[did] = {"name": _col(row, "Kernel_Name", "Kernel-Name") or "", "ns": ns}
+    return out
+
+
+def trace_means(folder):
+    """{label: mean duration in ns} of the block launches in a kernel trace."""
+    acc = {}
+    for label, d in label_dispatches(read_trace(folder)):
+        acc.setdefault(label, []).append(d["ns"])
+    return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
 def reduce(folders):
@@ -159,6 +195,52 @@ def derive(res, copy_bytes):
     return {"meta": meta, "kernels": out}
 
 
+def short_name(kernel):
+    """The kernel's base name (and the GEMM epilogue, if any) from a mangled or demangled name."""
+    m = re.search(r"_GLOBAL__N_1(\d+)", kernel)
+    if m:  # mangled: <length><identifier> follows the anonymous namespace
+        n = int(m.group(1))
+        base = kernel[m.end():m.end() + n]
+    else:
+        base = re.sub(r"^void |wan::|\(anonymous namespace\)::", "", kernel)
+        base = re.split(r"[<(]", base, maxsplit=1)[0]
+    epi = re.findall(r"Epi(?:Scaled|QKV|Residual|Store)", kernel)
+    return base + (" / " + ", ".join(dict.fromkeys(epi)) if epi else "")
+
+
+def markdown(res, command=None):
+    """A table of the per-launch figures (one row per block launch, in block order)."""
+    meta = res["meta"]
+    lines = ["# Per-launch hardware counters of one DiT block", ""]
+    if command:
+        lines += ["Command (one rocprofv3 run per counter set, then this reduction):", "", "```", command, "```", ""]
+    lines += [f"Byte counters scaled by the plain-copy calibration: FETCH_SIZE x {meta['fetch_scale']:.3f}, "
+              f"WRITE_SIZE x {meta['write_scale']:.3f} (a {meta['copy_bytes'] / 2**30:.0f} GiB device copy in the "
+              "same run). MFMA busy is SQ_VALU_MFMA_BUSY_CYCLES per GRBM_GUI_ACTIVE cycle relative to the "
+              "register-only MFMA probe's ratio in the same run. VALU / LDS activity: SQ_ACTIVE_INST_VALU and "
+              "SQ_ACTIVE_INST_LDS per GUI cycle (summed over the chip). Sources hashed in the JSON beside this "
+              "file; the figures hold for those sources only.", "",
+              "| launch | kernel | mean us | HBM bytes (fetch + write) | GB/s | MFMA busy vs probe | "
+              "VALU active / GUI cycle | LDS active / GUI cycle | LDS bank-conflict cycles per LDS instr |",
+              "|---|---|---|---|---|---|---|---|---|"]
+    for label in BLOCK_ORDER:
+        e = res["kernels"].get(label)
+        if e is None:
+            continue
+        ns = e.get("mean_ns")
+        hb = e.get("hbm_bytes")
+        gbs = hb / ns if (hb is not None and ns) else None  # bytes per ns = GB/s
+        name = short_name(e["kernel"])
+
+        def f(v, fmt):
+            return "-" if v is None else format(v, fmt)
+        lines.append(f"| {label} | `{name}` | {f(ns / 1e3 if ns else None, '.1f')} | {f(hb, '.3e')} | {f(gbs, '.0f')} | "
+                     f"{f(e.get('mfma_busy_vs_probe'), '.3f')} | {f(e.get('SQ_ACTIVE_INST_VALU_per_gui_cycle'), '.2f')} | "
+                     f"{f(e.get('SQ_ACTIVE_INST_LDS_per_gui_cycle'), '.2f')} | "
+                     f"{f(e.get('lds_bank_conflict_cycles_per_lds_inst'), '.3f')} |")
+    return "\n".join(lines) + "\n"
+
+
 def _sha(src):
     p = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", src)
     return hashlib.sha256(open(p, "rb").read()).hexdigest()
@@ -169,8 +251,18 @@ def main(argv=None):
     ap.add_argument("folders", nargs="+")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     ap.add_argument("--out", required=True)
+    ap.add_argument("--trace", help="kernel-trace folder of the same workload (mean durations per launch)")
+    ap.add_argument("--md", help="also write a markdown table here")
+    ap.add_argument("--command", help="the profiling command, quoted in the markdown")
     a = ap.parse_args(argv)
     res = derive(reduce(a.folders), a.copy_bytes)
+    if a.trace:
+        for label, ns in trace_means(a.trace).items():
+            if label in res["kernels"]:
+                res["kernels"][label]["mean_ns"] = ns
+    if a.md:
+        with open(a.md, "w") as fh:
+            fh.write(markdown(res, a.command))
     with open(a.out, "w") as fh:
         json.dump(res, fh, indent=1, sort_keys=True)
     print(json.dumps(res, indent=1, sort_keys=True))

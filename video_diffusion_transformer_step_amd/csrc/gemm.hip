@@ -9,8 +9,8 @@
 // Two kernels share the tile order and the epilogues:
 //  * gemm_lds_kernel (bf16, K a multiple of 128; the block's large products):
 //    256 x 256 tiles, 8 waves of 64 x 128, K steps of 32 copied global -> LDS by
-//    asynchronous global_load_lds_dwordx4 into a ring of four stages, two steps
-//    ahead of their use (no staging registers);
+//    asynchronous direct-to-LDS buffer loads (16 bytes a lane) into a ring of four
+//    stages, three steps ahead of their use (no staging registers);
 //  * gemm_nt_kernel (everything else): K steps of 128 bytes staged through
 //    double-buffered, row-padded LDS with register prefetch of the next step;
 //    loads are predicate-free (out-of-range rows clamped, a final partial K step
@@ -53,28 +53,36 @@ __device__ __forceinline__ float apply_act(float v, int act) {
   return v;
 }
 
-// Epilogues receive four consecutive columns n..n+3 of row m.
+// Epilogues receive four consecutive columns n..n+3 of row m, in two phases: pre(m, n) issues every
+// load the group needs (bias, residual, gate, scales) and returns them; post(m, n, v, pre) does the
+// arithmetic and the stores.  run_epilogue issues the loads of the next 32 x 32 block before the stores
+// of the current one, so a lane waits about one memory latency per block rather than one per group.
+__device__ __forceinline__ float4 load_bias4(const float* bias, int n) {
+  return bias ? *reinterpret_cast<const float4*>(bias + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
 template <typename OutT, int ACT>
 struct EpiStore {
   OutT* out;
   int64_t ldo;
   const float* bias;
-  __device__ __forceinline__ void operator()(int m, int n, float4 v) const {
-    if (bias) {
-      const float4 b = *reinterpret_cast<const float4*>(bias + n);
-      v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
-    }
+  struct Pre {
+    float4 b;
+  };
+  __device__ __forceinline__ Pre pre(int, int n) const { return Pre{load_bias4(bias, n)}; }
+  __device__ __forceinline__ void post(int m, int n, float4 v, const Pre& p) const {
+    v.x += p.b.x; v.y += p.b.y; v.z += p.b.z; v.w += p.b.w;
     if constexpr (ACT != ACT_NONE) {
       v.x = apply_act(v.x, ACT); v.y = apply_act(v.y, ACT);
       v.z = apply_act(v.z, ACT); v.w = apply_act(v.w, ACT);
     }
-    OutT* p = out + (int64_t)m * ldo + n;
+    OutT* q = out + (int64_t)m * ldo + n;
     if constexpr (sizeof(OutT) == 2) {
       bf16x4 o;
       o[0] = (bf16)v.x; o[1] = (bf16)v.y; o[2] = (bf16)v.z; o[3] = (bf16)v.w;
-      *reinterpret_cast<bf16x4*>(p) = o;
+      *reinterpret_cast<bf16x4*>(q) = o;
     } else {
-      *reinterpret_cast<float4*>(p) = v;
+      *reinterpret_cast<float4*>(q) = v;
     }
   }
 };
@@ -90,29 +98,30 @@ struct EpiQKV {
   const float* bias;
   T* vt;
   int vcol0, S, H, hd, Spad;
-  __device__ __forceinline__ void operator()(int m, int n, float4 v) const {
-    if (bias) {
-      const float4 b = *reinterpret_cast<const float4*>(bias + n);
-      v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
-    }
+  struct Pre {
+    float4 b;
+  };
+  __device__ __forceinline__ Pre pre(int, int n) const { return Pre{load_bias4(bias, n)}; }
+  __device__ __forceinline__ void post(int m, int n, float4 v, const Pre& p) const {
+    v.x += p.b.x; v.y += p.b.y; v.z += p.b.z; v.w += p.b.w;
     if (n < vcol0) {
-      T* p = out + (int64_t)m * ldo + n;
+      T* q = out + (int64_t)m * ldo + n;
       if constexpr (sizeof(T) == 2) {
         bf16x4 o;
         o[0] = (bf16)v.x; o[1] = (bf16)v.y; o[2] = (bf16)v.z; o[3] = (bf16)v.w;
-        *reinterpret_cast<bf16x4*>(p) = o;
+        *reinterpret_cast<bf16x4*>(q) = o;
       } else {
-        *reinterpret_cast<float4*>(p) = v;
+        *reinterpret_cast<float4*>(q) = v;
       }
     } else {
       const int nn = n - vcol0, h = nn / hd, d = nn - h * hd;  // 4 channels d..d+3 of head h
       const int b = m / S, pos = m - b * S;
       const int pp = sizeof(T) == 2 ? ((pos & ~12) | ((pos & 4) << 1) | ((pos & 8) >> 1)) : pos;
-      T* p = vt + (((int64_t)b * H + h) * hd + d) * Spad + pp;
-      p[0] = from_f32<T>(v.x);
-      p[Spad] = from_f32<T>(v.y);
-      p[2 * (int64_t)Spad] = from_f32<T>(v.z);
-      p[3 * (int64_t)Spad] = from_f32<T>(v.w);
+      T* q = vt + (((int64_t)b * H + h) * hd + d) * Spad + pp;
+      q[0] = from_f32<T>(v.x);
+      q[Spad] = from_f32<T>(v.y);
+      q[2 * (int64_t)Spad] = from_f32<T>(v.z);
+      q[3 * (int64_t)Spad] = from_f32<T>(v.w);
     }
   }
 };
@@ -121,33 +130,54 @@ struct EpiResidual {
   float* x;
   int64_t ldx;
   const float* bias;
-  const float* e0;  // [B, 6, N] or null (gate 1)
-  const float* mb;  // [6, N]
+  const float* gate;  // [B, 6, N] or null (gate 1)
   int chunk, S, N;
   float* y = nullptr;  // optional: also record the branch output C + bias (row stride N)
-  __device__ __forceinline__ void operator()(int m, int n, float4 v) const {
-    if (bias) {
-      const float4 b = *reinterpret_cast<const float4*>(bias + n);
-      v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
-    }
+  struct Pre {
+    float4 b, r, g;  // bias, residual x, gate
+  };
+  __device__ __forceinline__ Pre pre(int m, int n) const {
+    Pre p;
+    p.b = load_bias4(bias, n);
+    p.r = *reinterpret_cast<const float4*>(x + (int64_t)m * ldx + n);
+    p.g = gate ? *reinterpret_cast<const float4*>(gate + ((int64_t)(m / S) * 6 + chunk) * N + n)
+               : make_float4(1.f, 1.f, 1.f, 1.f);
+    return p;
+  }
+  __device__ __forceinline__ void post(int m, int n, float4 v, const Pre& p) const {
+    v.x += p.b.x; v.y += p.b.y; v.z += p.b.z; v.w += p.b.w;
     if (y) *reinterpret_cast<float4*>(y + (int64_t)m * N + n) = v;
-    float* p = x + (int64_t)m * ldx + n;
-    float4 r = *reinterpret_cast<const float4*>(p);
-    if (e0) {
-      const int b = m / S;
-      float4 g = *reinterpret_cast<const float4*>(e0 + ((int64_t)b * 6 + chunk) * N + n);
-      if (mb) {
-        const float4 h = *reinterpret_cast<const float4*>(mb + (int64_t)chunk * N + n);
-        g.x += h.x; g.y += h.y; g.z += h.z; g.w += h.w;
-      }
-      r.x = fmaf(g.x, v.x, r.x); r.y = fmaf(g.y, v.y, r.y);
-      r.z = fmaf(g.z, v.z, r.z); r.w = fmaf(g.w, v.w, r.w);
-    } else {
-      r.x += v.x; r.y += v.y; r.z += v.z; r.w += v.w;
-    }
-    *reinterpret_cast<float4*>(p) = r;
+    float4 r = p.r;
+    r.x = fmaf(p.g.x, v.x, r.x); r.y = fmaf(p.g.y, v.y, r.y);
+    r.z = fmaf(p.g.z, v.z, r.z); r.w = fmaf(p.g.w, v.w, r.w);
+    *reinterpret_cast<float4*>(x + (int64_t)m * ldx + n) = r;
   }
 };
+
+// The epilogue of a lane's FM x FN 32 x 32 accumulator blocks: lane row mrow + 32 i, columns
+// ncol + 32 j + 8 g + 0..3 (g < 4) in elements 4g..4g+3 of block (i, j).  A block's four groups issue
+// all their loads together (clamped coordinates: in range, their values unused where a group is out of
+// range), then do their arithmetic and guarded stores, so a lane waits about one memory latency per
+// block rather than one per group.  (Issuing the next block's loads before this block's stores as well
+// needs a second set of registers and spills.)
+template <int FM, int FN, class Epi>
+__device__ __forceinline__ void run_epilogue(const Epi& epi, const f32x16 (&acc)[FM][FN], int mrow, int ncol, int M,
+                                             int N) {
+#pragma unroll
+  for (int q = 0; q < FM * FN; ++q) {
+    const int i = q / FN, j = q % FN, m = mrow + i * 32, mc = min(m, M - 1);
+    typename Epi::Pre pre[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) pre[g] = epi.pre(mc, min(ncol + j * 32 + g * 8, N - 4));
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int n = ncol + j * 32 + g * 8;
+      if (m < M && n < N)
+        epi.post(m, n, make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]),
+                 pre[g]);
+    }
+  }
+}
 
 // Map a linear block id to (tile_m, tile_n): XCD-contiguous runs, then groups of gm row-tiles
 // (column tiles vary slowest inside a group).
@@ -272,35 +302,22 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restric
 
   // acc[i][j]: lane holds row m = m0 + wm*TM + i*32 + lrow and columns
   // n = n0 + wn*TN + j*32 + g*8 + lhalf*4 + (0..3) in elements 4g..4g+3.
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm * TM + i * 32 + lrow;
-    if (m >= M) continue;
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * TN + j * 32 + g * 8 + lhalf * 4;
-        if (n < N)
-          epi(m, n, make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]));
-      }
-  }
+  run_epilogue<FM, FN>(epi, acc, m0 + wm * TM + lrow, n0 + wn * TN + lhalf * 4, M, N);
 }
 
 // ---------------------------------------------------------------------------
 // bf16 GEMM with asynchronous global -> LDS copies and a ring of ST LDS stages.
 //
-// One workgroup = WM x WN waves owning a BM x BN tile; a wave owns (BM/WM) x (BN/WN) (128 x 128:
-// 16 MFMA blocks, 256 accumulator registers, so one wave per SIMD).  Each K step of BK elements
-// is copied by global_load_lds_dwordx4 straight into LDS, ST - 1 steps ahead of its use, so the
-// copies need no staging registers and have ST - 1 steps of MFMA work to land.  Row r of a stage
-// holds BK * 2 bytes; its 16-byte chunk c sits at slot c ^ ((r / RPB) % CH) (RPB rows share one
-// 256-byte bank window), which makes the 16 rows one ds_read_b128 phase reads hit 16 distinct
-// bank groups.  The copy instead permutes which global chunk each lane fetches: lanes still write
-// LDS linearly.  Requires K % BK == 0 (callers fall back to gemm_nt_kernel otherwise).
+// One workgroup = WM x WN waves owning a BM x BN tile; a wave owns (BM/WM) x (BN/WN) (the block's
+// products use 8 waves of 64 x 128: 8 MFMA blocks, 128 accumulator registers, two waves per SIMD).
+// Each K step of BK elements is copied by direct-to-LDS loads straight into LDS, ST - 1 steps ahead
+// of its use, so the copies need no staging registers and have ST - 1 steps of MFMA work to land.
+// Row r of a stage holds BK * 2 bytes; its 16-byte chunk c sits at slot c ^ ((r / RPB) % CH) (RPB
+// rows share one 256-byte bank window), which makes the 16 rows one ds_read_b128 phase reads hit 16
+// distinct bank groups.  The copy instead permutes which global chunk each lane fetches: lanes still
+// write LDS linearly.  Requires K % BK == 0 (callers fall back to gemm_nt_kernel otherwise).
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
 
 // s_waitcnt with only the vector-memory counter constrained to <= n (gfx9 encoding).
 template <int n>
@@ -320,35 +337,54 @@ struct LdsGemmCfg {
   __device__ static __forceinline__ int off(int r, int c) { return r * ROWB + ((c ^ ((r / RPB) & (CH - 1))) << 4); }
 };
 
+// The copies go through buffer resources (the MUBUF form of the direct-to-LDS load: lane i writes its
+// 16 bytes at lds + 16 i).  The compiler counts them as plain vector-memory loads, so the fragment
+// reads of a step wait only for their own results; with the FLAT form in flight every LDS read would
+// wait for all outstanding LDS accesses.  Each operand tile has one wave-uniform base (its first row),
+// a 32-bit per-lane byte offset (row clamped to the last valid one, permuted chunk) and the K position
+// as the scalar offset.
+__device__ __forceinline__ void buffer_copy16(const void* base, uint32_t voff, uint32_t soff, char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1,
+                                                                             0x00020000),
+                                           (lds_void*)lds, 16, voff, soff, 0, 0);
+}
+
 template <int BM, int BN, int BK, int NW>
 struct LdsCopyPlan {
   using C = LdsGemmCfg<BM, BN, BK, NW>;
-  const bf16* ga[C::LA];
-  const bf16* gb[C::LB];
+  const bf16* ba;  // wave-uniform tile bases
+  const bf16* bb;
+  uint32_t oa[C::LA];
+  uint32_t ob[C::LB];
+  __device__ static __forceinline__ const bf16* uniform(const bf16* p) {
+    const uint64_t a = (uint64_t)p;
+    return (const bf16*)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a));
+  }
   __device__ __forceinline__ LdsCopyPlan(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int m0, int n0,
                                          int M, int N) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    ba = uniform(A + (int64_t)m0 * lda);
+    bb = uniform(W + (int64_t)n0 * ldw);
 #pragma unroll
     for (int i = 0; i < C::LA; ++i) {
       const int p = (i * NW + wave) * 64 + lane, r = p / C::CH, s = p % C::CH;
       const int c = s ^ ((r / C::RPB) & (C::CH - 1));
-      ga[i] = A + (int64_t)min(m0 + r, M - 1) * lda + c * 8;
+      oa[i] = (uint32_t)(((int64_t)(min(m0 + r, M - 1) - m0) * lda + c * 8) * 2);
     }
 #pragma unroll
     for (int i = 0; i < C::LB; ++i) {
       const int p = (i * NW + wave) * 64 + lane, r = p / C::CH, s = p % C::CH;
       const int c = s ^ ((r / C::RPB) & (C::CH - 1));
-      gb[i] = W + (int64_t)min(n0 + r, N - 1) * ldw + c * 8;
+      ob[i] = (uint32_t)(((int64_t)(min(n0 + r, N - 1) - n0) * ldw + c * 8) * 2);
     }
   }
   __device__ __forceinline__ void issue(int k0, char* sa, char* sb) const {
     const int wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < C::LA; ++i)
-      __builtin_amdgcn_global_load_lds((glb_void*)(ga[i] + k0), (lds_void*)(sa + (i * NW + wave) * 1024), 16, 0, 0);
+    for (int i = 0; i < C::LA; ++i) buffer_copy16(ba, oa[i], k0 * 2, sa + (i * NW + wave) * 1024);
 #pragma unroll
-    for (int i = 0; i < C::LB; ++i)
-      __builtin_amdgcn_global_load_lds((glb_void*)(gb[i] + k0), (lds_void*)(sb + (i * NW + wave) * 1024), 16, 0, 0);
+    for (int i = 0; i < C::LB; ++i) buffer_copy16(bb, ob[i], k0 * 2, sb + (i * NW + wave) * 1024);
   }
 };
 
@@ -476,19 +512,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(const bf16* __res
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lrow = lane & 31, lhalf = lane >> 5;
   const int wm = wave / WN, wn = wave % WN;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm * (BM / WM) + i * 32 + lrow;
-    if (m >= M) continue;
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * (BN / WN) + j * 32 + g * 8 + lhalf * 4;
-        if (n < N)
-          epi(m, n, make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]));
-      }
-  }
+  run_epilogue<FM, FN>(epi, acc, m0 + wm * (BM / WM) + lrow, n0 + wn * (BN / WN) + lhalf * 4, M, N);
 }
 
 template <int BM, int BN, int BK, int ST, int WM, int WN, class Epi, bool F8 = false>
@@ -507,10 +531,14 @@ struct EpiScaled {
   const float* row_scale;
   const float* w_scale;  // one value, on the device
   Epi inner;
-  __device__ __forceinline__ void operator()(int m, int n, float4 v) const {
-    const float sc = row_scale[m] * *w_scale;
-    v.x *= sc; v.y *= sc; v.z *= sc; v.w *= sc;
-    inner(m, n, v);
+  struct Pre {
+    float sc;
+    typename Epi::Pre in;
+  };
+  __device__ __forceinline__ Pre pre(int m, int n) const { return Pre{row_scale[m] * *w_scale, inner.pre(m, n)}; }
+  __device__ __forceinline__ void post(int m, int n, float4 v, const Pre& p) const {
+    v.x *= p.sc; v.y *= p.sc; v.z *= p.sc; v.w *= p.sc;
+    inner.post(m, n, v, p.in);
   }
 };
 
@@ -545,7 +573,10 @@ hipError_t run_gemm(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int
   if (N % 4 != 0 || K % dtype_traits<T>::per16 != 0) return hipErrorInvalidValue;
   if constexpr (sizeof(T) == 2) {
     int cfg = 0;
-    if (M >= 4096 && N >= 1024 && K % 128 == 0 && lda % 8 == 0 && ldw % 8 == 0) cfg = 1;
+    // (the asynchronous-copy kernel addresses a 256-row operand tile with 32-bit byte offsets)
+    if (M >= 4096 && N >= 1024 && K % 128 == 0 && lda % 8 == 0 && ldw % 8 == 0 &&
+        (int64_t)256 * (lda > ldw ? lda : ldw) * 2 < ((int64_t)1 << 31))
+      cfg = 1;
     else if (M >= 4096 && N % 256 == 0 && N >= 1024) cfg = 2;
     else if (M >= 4096 && N % 128 == 0 && N >= 1024) cfg = 3;
     if (cfg == 1) return launch_lds<256, 256, 32, 4, 4, 2>(A, lda, W, ldw, M, N, K, epi, s);
@@ -625,9 +656,8 @@ hipError_t gemm_qkv(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int
 
 template <typename T>
 hipError_t gemm_residual(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const float* bias,
-                         const float* e0, const float* mb, int chunk, int S, float* x, int64_t ldx, hipStream_t s,
-                         float* ystore) {
-  EpiResidual epi{x, ldx, bias, e0, mb, chunk, S, N, ystore};
+                         const float* gate, int chunk, int S, float* x, int64_t ldx, hipStream_t s, float* ystore) {
+  EpiResidual epi{x, ldx, bias, gate, chunk, S, N, ystore};
   return run_gemm<T>(A, lda, W, ldw, M, N, K, epi, s);
 }
 
@@ -648,10 +678,10 @@ hipError_t gemm_qkv_e4m3(const uint8_t* A, int64_t lda, const float* a_scales, c
 }
 
 hipError_t gemm_e4m3_residual(const uint8_t* A, int64_t lda, const float* a_scales, const uint8_t* W, int64_t ldw,
-                              const float* w_scale, int M, int N, int K, const float* bias, const float* e0, const float* mb,
+                              const float* w_scale, int M, int N, int K, const float* bias, const float* gate,
                               int chunk, int S, float* x, int64_t ldx, hipStream_t s, float* ystore) {
-  return run_gemm_e4m3(A, lda, a_scales, W, ldw, w_scale, M, N, K,
-                       EpiResidual{x, ldx, bias, e0, mb, chunk, S, N, ystore}, s);
+  return run_gemm_e4m3(A, lda, a_scales, W, ldw, w_scale, M, N, K, EpiResidual{x, ldx, bias, gate, chunk, S, N, ystore},
+                       s);
 }
 
 template <typename T>
@@ -683,9 +713,9 @@ template hipError_t gemm_qkv<float>(const float*, int64_t, const float*, int64_t
 template hipError_t gemm_qkv<bf16>(const bf16*, int64_t, const bf16*, int64_t, int, int, int, const float*, bf16*,
                                    int64_t, bf16*, int, int, int, int, hipStream_t);
 template hipError_t gemm_residual<float>(const float*, int64_t, const float*, int64_t, int, int, int, const float*,
-                                         const float*, const float*, int, int, float*, int64_t, hipStream_t, float*);
+                                         const float*, int, int, float*, int64_t, hipStream_t, float*);
 template hipError_t gemm_residual<bf16>(const bf16*, int64_t, const bf16*, int64_t, int, int, int, const float*,
-                                        const float*, const float*, int, int, float*, int64_t, hipStream_t, float*);
+                                        const float*, int, int, float*, int64_t, hipStream_t, float*);
 template hipError_t gemv<float>(const float*, int, int, const float*, int, const float*, int, int, float*,
                                 hipStream_t);
 template hipError_t gemv<bf16>(const bf16*, int, int, const float*, int, const float*, int, int, float*,

@@ -228,9 +228,9 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
     if (f8g) {
       PROF_TRY(WAN_K_QUANT, launch_quant_rows_e4m3((const bf16*)w.o, dim, BS, dim, w.a8, dim, w.sa, st));
       PROF_TRY(WAN_K_O_GEMM, gemm_e4m3_residual(w.a8, dim, w.sa, (const uint8_t*)Q8->wo, dim, Q8->s_wo, BS, dim, dim, W.bo,
-                                                w.mod, nullptr, 2, S, x, dim, st, ystore));
+                                                w.mod, 2, S, x, dim, st, ystore));
     } else {
-      PROF_TRY(WAN_K_O_GEMM, gemm_residual<T>(w.o, dim, (const T*)W.wo, dim, BS, dim, dim, W.bo, w.mod, nullptr, 2, S, x,
+      PROF_TRY(WAN_K_O_GEMM, gemm_residual<T>(w.o, dim, (const T*)W.wo, dim, BS, dim, dim, W.bo, w.mod, 2, S, x,
                                               dim, st, ystore));
     }
   }  // self-attention branch
@@ -248,7 +248,7 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
   if (Li > 0)
     PROF_TRY(WAN_K_CROSS_ATTN, launch_attention<T>(qc, (int64_t)S * dim, dim, st_img, B, S, H, hd, scale,
                                                    w.o, (int64_t)S * dim, dim, 1, st, nullptr, KeySplit{}, true));
-  PROF_TRY(WAN_K_CROSS_O_GEMM, gemm_residual<T>(w.o, dim, (const T*)W.wco, dim, BS, dim, dim, W.bco, nullptr, nullptr, 0, S, x, dim, st));
+  PROF_TRY(WAN_K_CROSS_O_GEMM, gemm_residual<T>(w.o, dim, (const T*)W.wco, dim, BS, dim, dim, W.bco, nullptr, 0, S, x, dim, st));
   // FFN branch
   PROF_TRY(WAN_K_LN2, launch_ln_mod<T>(x, BS, dim, S, 0, w.mod, nullptr, 3, 4, c.ln_eps, w.u, st));
   if (f8g) {
@@ -258,12 +258,12 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
                                               ACT_GELU, (bf16*)w.h, F, st));
     PROF_TRY(WAN_K_QUANT, launch_quant_rows_e4m3((const bf16*)w.h, F, BS, F, w.a8, F, w.sa, st));
     PROF_TRY(WAN_K_FFN2_GEMM, gemm_e4m3_residual(w.a8, F, w.sa, (const uint8_t*)Q8->w2, F, Q8->s_w2, BS, dim, F, W.b2,
-                                                 w.mod, nullptr, 5, S, x, dim, st));
+                                                 w.mod, 5, S, x, dim, st));
   } else {
     PROF_TRY(WAN_K_FFN1_GEMM, (gemm_store<T, T>(w.u, dim, (const T*)W.w1, dim, BS, c.ffn_dim, dim, W.b1, ACT_GELU, w.h,
                                                 c.ffn_dim, st)));
     PROF_TRY(WAN_K_FFN2_GEMM, gemm_residual<T>(w.h, c.ffn_dim, (const T*)W.w2, c.ffn_dim, BS, dim, c.ffn_dim, W.b2, w.mod,
-                                               nullptr, 5, S, x, dim, st));
+                                               5, S, x, dim, st));
   }
   return WAN_OK;
 }

@@ -62,8 +62,9 @@ hipError_t launch_qk_norm_rope(const T* q_in, const T* k_in, int64_t ld_in, T* q
 // C[m, n] = sum_k A[m, k] * W[n, k]   (A [M, K] row-major, W [N, K] row-major)
 // Epilogues:
 //   store:      out[m, n] = act(C + bias[n])  (OutT = T or float)
-//   residual:   x[m, n] += g(m, n) * (C + bias[n]), g = e0[m / S][chunk][n] + mb[chunk][n] (mb null: no
-//               addition), or 1 if e0 null; ystore (optional, row stride N) also receives C + bias.
+//   residual:   x[m, n] += g(m, n) * (C + bias[n]), g = gate[m / S][chunk][n] from a [B, 6, N] table
+//               (the block's e0 + modulation bias), or 1 if gate is null; ystore (optional, row stride N)
+//               also receives C + bias.
 template <typename T, typename OutT>
 hipError_t gemm_store(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const float* bias,
                       int act, OutT* out, int64_t ldo, hipStream_t s);
@@ -76,7 +77,7 @@ hipError_t gemm_qkv(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int
                     T* qk, int64_t ldo, T* vt, int S, int H, int hd, int Spad, hipStream_t s);
 template <typename T>
 hipError_t gemm_residual(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const float* bias,
-                         const float* e0, const float* mb, int chunk, int S, float* x, int64_t ldx, hipStream_t s,
+                         const float* gate, int chunk, int S, float* x, int64_t ldx, hipStream_t s,
                          float* ystore = nullptr);
 // E4M3 products: C = (sum_k A[m, k] W[n, k]) * a_scales[m] * w_scale[0] over E4M3 codes (A row stride
 // lda bytes, W row stride ldw bytes, K % 256 == 0, strides % 16 == 0), then the store (bf16 out, act
@@ -85,9 +86,8 @@ hipError_t gemm_e4m3_store(const uint8_t* A, int64_t lda, const float* a_scales,
                            const float* w_scale, int M, int N, int K, const float* bias, int act, bf16* out,
                            int64_t ldo, hipStream_t s);
 hipError_t gemm_e4m3_residual(const uint8_t* A, int64_t lda, const float* a_scales, const uint8_t* W, int64_t ldw,
-                              const float* w_scale, int M, int N, int K, const float* bias, const float* e0,
-                              const float* mb, int chunk, int S, float* x, int64_t ldx, hipStream_t s,
-                              float* ystore = nullptr);
+                              const float* w_scale, int M, int N, int K, const float* bias, const float* gate,
+                              int chunk, int S, float* x, int64_t ldx, hipStream_t s, float* ystore = nullptr);
 hipError_t gemm_qkv_e4m3(const uint8_t* A, int64_t lda, const float* a_scales, const uint8_t* W, int64_t ldw,
                          const float* w_scale, int M, int dim, int K, const float* bias, bf16* qk, int64_t ldo, bf16* vt,
                          int S, int H, int hd, int Spad, hipStream_t s);
