@@ -41,12 +41,15 @@ def test_labels_calibration_and_markdown(tmp_path):
     seq = [("__amd_rocclr_copyBuffer", {"FETCH_SIZE": 10.0, "WRITE_SIZE": 5.0}),
            ("__amd_rocclr_copyBuffer", {"FETCH_SIZE": 2048.0, "WRITE_SIZE": 1024.0}),  # 1 MiB copy: x0.5 / x1
            ("mfma_peak_kernel<0>", {"SQ_VALU_MFMA_BUSY_CYCLES": 400.0, "GRBM_GUI_ACTIVE": 4.0})]
+    seq.append(("wan::patchify_kernel(float const*)", {"FETCH_SIZE": 8.0, "WRITE_SIZE": 16.0}))
     for blk in range(2):
         for i, (name, label) in enumerate(BLOCK):
             seq.append((name, {"FETCH_SIZE": 100.0 * (i + 1) + blk, "WRITE_SIZE": 10.0 * (i + 1),
                                "SQ_VALU_MFMA_BUSY_CYCLES": 50.0 * (i + 1), "GRBM_GUI_ACTIVE": 2.0,
                                "SQ_ACTIVE_INST_VALU": 6.0}))
     fields = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    seq.append(("wan::unpatchify_kernel(float const*)", {"FETCH_SIZE": 4.0, "WRITE_SIZE": 16.0}))
+    seq.append(("wan::euler_kernel(float*)", {"FETCH_SIZE": 32.0, "WRITE_SIZE": 16.0}))
     _write(tmp_path / "pmc", _pmc_rows(seq), fields, "p_counter_collection.csv")
     trace = [{"Dispatch_Id": i + 1, "Kernel_Name": n, "Start_Timestamp": 1000 * i,
               "End_Timestamp": 1000 * i + 500 + 10 * i} for i, (n, _) in enumerate(seq)]
@@ -56,7 +59,8 @@ def test_labels_calibration_and_markdown(tmp_path):
     labelled = C.label_dispatches(C.read_dispatches(str(tmp_path / "pmc")))
     labels = [lab for lab, _ in labelled]
     assert labels.count("copy") == 2 and labels.count("mfma_probe") == 1
-    assert [lab for lab in labels if lab not in ("copy", "mfma_probe")] == [b for _, b in BLOCK] * 2
+    assert [lab for lab in labels if lab not in ("copy", "mfma_probe")] == (["patchify"] + [b for _, b in BLOCK] * 2 +
+                                                                          ["unpatchify", "euler"])
 
     res = C.derive(C.reduce([str(tmp_path / "pmc")]), copy_bytes)
     assert abs(res["meta"]["fetch_scale"] - 0.5) < 1e-12 and abs(res["meta"]["write_scale"] - 1.0) < 1e-12
@@ -67,15 +71,18 @@ def test_labels_calibration_and_markdown(tmp_path):
     # MFMA busy per GUI cycle 350 / 2 against the probe's 100
     assert abs(k["o_gemm"]["mfma_busy_vs_probe"] - 1.75) < 1e-12
     assert abs(k["ln1"]["SQ_ACTIVE_INST_VALU_per_gui_cycle"] - 3.0) < 1e-12
+    # once-per-step kernels: "unpatchify" must not be taken for "patchify"
+    assert abs(k["euler"]["hbm_bytes"] - (32 * 1024 * 0.5 + 16 * 1024)) < 1e-6
+    assert abs(k["unpatchify"]["fetch_bytes"] - 4 * 1024 * 0.5) < 1e-6
 
     means = C.trace_means(str(tmp_path / "kt"))
-    # self_attn is dispatch 9 (block 0) and 23 (block 1): durations 500 + 10 * (8, 22)
-    assert abs(means["self_attn"] - (500 + 10 * 15)) < 1e-9
+    # self_attn is dispatch 10 (block 0) and 24 (block 1): durations 500 + 10 * (9, 23)
+    assert abs(means["self_attn"] - (500 + 10 * 16)) < 1e-9
     out = tmp_path / "c.json"
     md = tmp_path / "c.md"
     assert C.main([str(tmp_path / "pmc"), "--copy-bytes", str(copy_bytes), "--out", str(out), "--trace",
                    str(tmp_path / "kt"), "--md", str(md), "--command", "rocprofv3 ..."]) == 0
     rec = json.loads(out.read_text())
-    assert abs(rec["kernels"]["self_attn"]["mean_ns"] - 650.0) < 1e-9
+    assert abs(rec["kernels"]["self_attn"]["mean_ns"] - 660.0) < 1e-9
     text = md.read_text()
-    assert "| self_attn |" in text and "| ffn2_gemm |" in text and "rocprofv3 ..." in text
+    assert "| self_attn |" in text and "| ffn2_gemm |" in text and "| euler |" in text and "rocprofv3 ..." in text

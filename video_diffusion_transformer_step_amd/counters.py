@@ -1,4 +1,5 @@
-"""Reduce rocprofv3 hardware-counter runs of bench.py to per-kernel figures of one DiT block.
+"""Reduce rocprofv3 hardware-counter runs of bench.py to per-kernel figures of one DiT block (and of
+the once-per-step layout kernels: patchify, unpatchify, the Euler update, the I2V input).
 
 Measurement tooling, not part of the compute path.  Input: the output folders of several
 `rocprofv3 --pmc ... --output-format csv -d DIR -- python3 bench.py ...` runs (one counter set per
@@ -47,6 +48,10 @@ BY_NAME = [("mod_combine", ["mod_combine"]),
            ("EpiResidual", ["o_gemm", "cross_o_gemm", "ffn2_gemm"]),
            ("EpiStore", ["cross_q_gemm", "ffn1_gemm"]),
            ("attention_kernel", ["cross_attn"])]
+# once-per-step kernels outside the blocks (name fragment -> label; the first match wins)
+STEP_KERNELS = [("unpatchify_kernel", "unpatchify"), ("patchify_kernel", "patchify"), ("euler_kernel", "euler"),
+                ("i2v_input_kernel", "i2v_input")]
+STEP_ORDER = ["i2v_input", "patchify", "unpatchify", "euler"]
 COPY_NAME = "copyBuffer"
 PROBE_NAME = "mfma_peak_kernel<0>"  # the bf16 register-only MFMA probe
 SOURCES = ["attention.hip", "gemm.hip", "norm.hip", "layout.hip"]
@@ -95,6 +100,10 @@ def label_dispatches(disp):
             continue
         if PROBE_NAME in name:
             labelled.append(("mfma_probe", d))
+            continue
+        step = next((lab for frag, lab in STEP_KERNELS if frag in name), None)
+        if step is not None:
+            labelled.append((step, d))
             continue
         if "mod_combine" in name:
             seen = {}
@@ -161,7 +170,7 @@ def derive(res, copy_bytes):
     probe = res.get("mfma_probe", {}).get("mean", {})
     probe_busy = (probe["SQ_VALU_MFMA_BUSY_CYCLES"] / probe["GRBM_GUI_ACTIVE"]
                   if probe.get("SQ_VALU_MFMA_BUSY_CYCLES") and probe.get("GRBM_GUI_ACTIVE") else None)
-    for label in BLOCK_ORDER:
+    for label in BLOCK_ORDER + STEP_ORDER:
         if label not in res:
             continue
         m = res[label]["mean"]
@@ -211,7 +220,7 @@ def short_name(kernel):
 def markdown(res, command=None):
     """A table of the per-launch figures (one row per block launch, in block order)."""
     meta = res["meta"]
-    lines = ["# Per-launch hardware counters of one DiT block", ""]
+    lines = ["# Per-launch hardware counters of one DiT block and the step's layout kernels", ""]
     if command:
         lines += ["Command (one rocprofv3 run per counter set, then this reduction):", "", "```", command, "```", ""]
     lines += [f"Byte counters scaled by the plain-copy calibration: FETCH_SIZE x {meta['fetch_scale']:.3f}, "
@@ -223,7 +232,7 @@ def markdown(res, command=None):
               "| launch | kernel | mean us | HBM bytes (fetch + write) | GB/s | MFMA busy vs probe | "
               "VALU active / GUI cycle | LDS active / GUI cycle | LDS bank-conflict cycles per LDS instr |",
               "|---|---|---|---|---|---|---|---|---|"]
-    for label in BLOCK_ORDER:
+    for label in BLOCK_ORDER + STEP_ORDER:
         e = res["kernels"].get(label)
         if e is None:
             continue
