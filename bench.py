@@ -116,7 +116,8 @@ def block_counters():
 def measure_device():
     """Device ceilings measured beside the nominal ones: compute units and peak engine clock as the
     runtime reports them, the matrix-core rate of a kernel issuing only MFMAs on register operands
-    (bf16 and E4M3), and the rate of a plain 1 GiB device-to-device copy."""
+    (bf16 and E4M3 on constant operands, bf16 on hashed operands that toggle like real data), and the
+    rate of a plain 1 GiB device-to-device copy."""
     import torch
 
     from video_diffusion_transformer_step_amd import _lib as L
@@ -140,6 +141,18 @@ def measure_device():
         expect = 64.0 * L.MFMA_PROBE_K[kind] * iters
         assert bool((out == expect).all()), f"MFMA probe ({key}) returned wrong sums"
         res[f"measured_{key}_tflops"] = round(flop / (ms * 1e-3) / 1e12, 1)
+    # the same bf16 loop on operands that differ per lane and instruction (real data toggles operand
+    # bits, which costs matrix-core power; constant operands toggle none)
+    L.mfma_peak_probe(2, 0x9E3779B9, 0x7F4A7C15, blocks, 16, out)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(10):
+        flop = L.mfma_peak_probe(2, 0x9E3779B9, 0x7F4A7C15, blocks, 4000, out)
+    ev1.record()
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()), "MFMA probe (bf16, hashed operands) returned non-finite sums"
+    res["measured_bf16_random_operands_tflops"] = round(flop / (ev0.elapsed_time(ev1) / 10 * 1e-3) / 1e12, 1)
     res["sustained_mfma_clock_mhz"] = round(res["measured_bf16_tflops"] * 1e12 / (cus * 4096) / 1e6, 1)
     del out
     n = 1 << 28
@@ -802,7 +815,11 @@ def main():
                      "launch_ms": round(attn_avg, 4), "flops_per_launch": attn_flops,
                      "peak_measured": device["measured_bf16_tflops"] if device else None,
                      "frac_of_measured_peak": (round(attn_tflops / device["measured_bf16_tflops"], 4)
-                                               if device else None)},
+                                               if device else None),
+                     "peak_measured_random_operands": (device["measured_bf16_random_operands_tflops"]
+                                                       if device else None),
+                     "frac_of_measured_random_operand_peak": (
+                         round(attn_tflops / device["measured_bf16_random_operands_tflops"], 4) if device else None)},
         "device": device,
         "breakdown_ms_per_block": breakdown,
         "fp8_attention_step": fp8.get("fp8_attention_step"),

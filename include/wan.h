@@ -370,11 +370,15 @@ int32_t wan_profile_end(void);
  *     kind 0: v_mfma_f32_32x32x16_bf16, every A element = the bf16 in each half of a_word, B likewise
  *             from b_word; 32768 flop per instruction and wave;
  *     kind 1: v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3 with unit block scales, every element = the
- *             code in each byte of a_word / b_word; 131072 flop per instruction and wave.
+ *             code in each byte of a_word / b_word; 131072 flop per instruction and wave;
+ *     kind 2: v_mfma_f32_32x32x16_bf16 on operands that differ per lane and per instruction (hashed
+ *             sign and mantissa, magnitude in [0.5, 2); a_word and b_word seed the hash): the rate
+ *             under the operand bit toggling of real data, which costs matrix-core power.
  *   out [blocks * 256] float32 (caller-owned device memory) receives each lane's sum of its four
- *   accumulators, 64 * K * iters * a * b (K = 16, resp. 64), so a caller can check the work was done.
+ *   accumulators: for kinds 0 and 1, 64 * K * iters * a * b (K = 16, resp. 64), so a caller can check
+ *   the work was done; for kind 2, a finite value.
  *   Time it with events on `stream`; flop per launch = blocks * 4 * 4 * iters * (flop per instruction).
- *   Errors: WAN_EINVAL for kind outside 0..1, blocks or iters outside 1..2^20, or a NULL / misaligned
+ *   Errors: WAN_EINVAL for kind outside 0..2, blocks or iters outside 1..2^20, or a NULL / misaligned
  *   out (nothing is enqueued). */
 int wan_device_info(int32_t* compute_units, int32_t* clock_khz);
 int wan_mfma_peak_probe(int32_t kind, uint32_t a_word, uint32_t b_word, int32_t blocks, int32_t iters, float* out,

@@ -200,7 +200,7 @@ def test_ring_attention_validation(lib):
 
 def test_device_probe_validation(lib):
     assert lib.wan_device_info(None, None) == L.WAN_EINVAL
-    for kind, blocks, iters, out in ((2, 1, 1, FAKE), (-1, 1, 1, FAKE), (0, 0, 1, FAKE), (1, 1, 0, FAKE),
+    for kind, blocks, iters, out in ((3, 1, 1, FAKE), (-1, 1, 1, FAKE), (0, 0, 1, FAKE), (1, 1, 0, FAKE),
                                      (0, 1 << 21, 1, FAKE), (0, 1, 1 << 21, FAKE), (0, 1, 1, None),
                                      (1, 1, 1, FAKE + 2)):
         assert lib.wan_mfma_peak_probe(kind, 0, 0, blocks, iters, out, None) == L.WAN_EINVAL, (kind, blocks, iters)

@@ -228,3 +228,20 @@ def test_mfma_peak_probe_sums(kind, a_word, b_word, a, b):
     expect = 64.0 * L.MFMA_PROBE_K[kind] * iters * a * b
     got = host(out)
     assert np.all(got == expect), (got.min(), got.max(), expect)
+
+
+def test_mfma_peak_probe_hashed_operands():
+    """Kind 2 (bf16 on hashed operands, a measurement aid): every lane's sum is finite, the same seed
+    gives the same sums, and another seed gives other sums."""
+    require_gpu()
+    case("mfma probe kind 2")
+    blocks, iters = 3, 5
+    out = torch.full((blocks * 256,), float("nan"), dtype=torch.float32, device="cuda")
+    flop = L.mfma_peak_probe(2, 0x9E3779B9, 0x7F4A7C15, blocks, iters, out)
+    assert flop == blocks * 16 * iters * L.MFMA_PROBE_FLOP[2]
+    first = host(out).copy()
+    L.mfma_peak_probe(2, 0x9E3779B9, 0x7F4A7C15, blocks, iters, out)
+    second = host(out).copy()
+    L.mfma_peak_probe(2, 0x12345678, 0x7F4A7C15, blocks, iters, out)
+    third = host(out)
+    assert np.all(np.isfinite(first)) and np.array_equal(first, second) and not np.array_equal(first, third)

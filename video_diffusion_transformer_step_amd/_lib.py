@@ -376,12 +376,13 @@ def device_info():
     return cus.value, khz.value
 
 
-MFMA_PROBE_FLOP = {0: 2 * 32 * 32 * 16, 1: 2 * 32 * 32 * 64}  # per instruction and wave
+MFMA_PROBE_FLOP = {0: 2 * 32 * 32 * 16, 1: 2 * 32 * 32 * 64, 2: 2 * 32 * 32 * 16}  # per instruction and wave
 MFMA_PROBE_K = {0: 16, 1: 64}
 
 
 def mfma_peak_probe(kind, a_word, b_word, blocks, iters, out, stream=None):
-    """Enqueue the register-only MFMA kernel (kind 0 bf16, 1 E4M3); out [blocks * 256] float32.
+    """Enqueue the register-only MFMA kernel (kind 0 bf16, 1 E4M3, 2 bf16 on hashed operands);
+    out [blocks * 256] float32.
     Returns the launch's flop count."""
     assert out.numel() >= blocks * 256
     _check(lib().wan_mfma_peak_probe(kind, a_word, b_word, blocks, iters, _p(out), _stream(stream)),

@@ -959,7 +959,8 @@ int wan_device_info(int32_t* compute_units, int32_t* clock_khz) {
 
 int wan_mfma_peak_probe(int32_t kind, uint32_t a_word, uint32_t b_word, int32_t blocks, int32_t iters, float* out,
                         wan_stream_t stream) {
-  if (kind != 0 && kind != 1) return fail(WAN_EINVAL, "kind must be 0 (bf16) or 1 (E4M3), got %d", kind);
+  if (kind < 0 || kind > 2)
+    return fail(WAN_EINVAL, "kind must be 0 (bf16), 1 (E4M3) or 2 (bf16, hashed operands), got %d", kind);
   if (blocks < 1 || blocks > (1 << 20)) return fail(WAN_EINVAL, "blocks must be in 1..2^20, got %d", blocks);
   if (iters < 1 || iters > (1 << 20)) return fail(WAN_EINVAL, "iters must be in 1..2^20, got %d", iters);
   WAN_TRY(need_f32(out, "out"));
