@@ -23,8 +23,9 @@
 //  * the 1D grid is remapped so each XCD (blockIdx % 8) receives a contiguous run
 //    of tiles, grouped a few row-tiles at a time (group_m), so concurrent tiles
 //    share A rows and W columns in that XCD's L2;
-//  * k is accumulated in increasing order in every configuration, so all tile
-//    shapes give bitwise-identical results;
+//  * k is accumulated in increasing order in every configuration; a configuration's results
+//    are bitwise repeatable, and configurations on different MFMA shapes (16 x 16 x 32 for the
+//    store and residual products, 32 x 32 x 16 elsewhere) may differ in the last bits;
 //  * epilogues fuse the bias, GELU / SiLU, the output cast and the adaLN-gated
 //    residual update x += gate * (.) ("图解 Wan2.1 I2V" §5.2).
 #include "wan_internal.h"
@@ -175,6 +176,28 @@ __device__ __forceinline__ void run_epilogue(const Epi& epi, const f32x16 (&acc)
       if (m < M && n < N)
         epi.post(m, n, make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]),
                  pre[g]);
+    }
+  }
+}
+
+// The epilogue of a lane's FM x FN 16 x 16 accumulator blocks: lane row mrow + 16 i, columns
+// ncol + 16 j + 0..3 in block (i, j).  Four blocks of a row issue their loads together, then do their
+// arithmetic and guarded stores.
+template <int FM, int FN, class Epi>
+__device__ __forceinline__ void run_epilogue16(const Epi& epi, const f32x4 (&acc)[FM][FN], int mrow, int ncol, int M,
+                                               int N) {
+  static_assert(FN % 4 == 0, "groups of four blocks");
+#pragma unroll
+  for (int q = 0; q < FM * FN / 4; ++q) {
+    const int i = q / (FN / 4), j0 = (q % (FN / 4)) * 4, m = mrow + i * 16, mc = min(m, M - 1);
+    typename Epi::Pre pre[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) pre[g] = epi.pre(mc, min(ncol + (j0 + g) * 16, N - 4));
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int n = ncol + (j0 + g) * 16;
+      const f32x4& a = acc[i][j0 + g];
+      if (m < M && n < N) epi.post(m, n, make_float4(a[0], a[1], a[2], a[3]), pre[g]);
     }
   }
 }
@@ -388,6 +411,18 @@ struct LdsCopyPlan {
   }
 };
 
+// Accumulators of one wave: 32 x 32 blocks (v_mfma_f32_32x32x16_bf16, or the E4M3
+// v_mfma_scale_f32_32x32x64_f8f6f4), or 16 x 16 blocks (v_mfma_f32_16x16x32_bf16, which sustains ~12 %
+// more than the 32 x 32 x 16 form on gfx950 in a register-only loop).
+template <int TM, int TN, bool M16>
+struct LdsAcc {
+  using type = f32x16[TM / 32][TN / 32];
+};
+template <int TM, int TN>
+struct LdsAcc<TM, TN, true> {
+  using type = f32x4[TM / 16][TN / 16];
+};
+
 template <int BM, int BN, int BK, int ST, int WM, int WN>
 struct LdsSlots {
   char* a[4];
@@ -403,10 +438,11 @@ struct LdsSlots {
 // the copies and the LDS layout are unchanged; each K step is then one
 // v_mfma_scale_f32_32x32x64_f8f6f4 per output block (unit block scales) on 32-byte fragments
 // (lane half h reads 16-byte chunks 2h and 2h + 1 of its row, the same k for A and W).
-template <int BM, int BN, int BK, int ST, int WM, int WN, int P, bool F8 = false>
+// M16 (bf16 only): 16 x 16 x 32 products on 16 x 16 accumulator blocks instead of 32 x 32 x 16 ones.
+template <int BM, int BN, int BK, int ST, int WM, int WN, int P, bool F8, bool M16>
 __device__ __forceinline__ void lds_gemm_step(const LdsCopyPlan<BM, BN, BK, WM * WN>& cp,
                                               const LdsSlots<BM, BN, BK, ST, WM, WN>& sl, int kt, int nk,
-                                              f32x16 (&acc)[BM / WM / 32][BN / WN / 32]) {
+                                              typename LdsAcc<BM / WM, BN / WN, M16>::type& acc) {
   using C = LdsGemmCfg<BM, BN, BK, WM * WN>;
   constexpr int FM = BM / WM / 32, FN = BN / WN / 32, PER = C::LA + C::LB;
   wait_vmcnt<(ST - 2) * PER>();  // this wave's copies of stage kt have landed
@@ -427,6 +463,7 @@ __device__ __forceinline__ void lds_gemm_step(const LdsCopyPlan<BM, BN, BK, WM *
   const int wm = wave / WN, wn = wave % WN;
   const char* sa = sl.a[P];
   const char* sb = sl.b[P];
+  static_assert(!(F8 && M16), "E4M3 products use 32 x 32 blocks");
   if constexpr (F8) {
     static_assert(BK == 32, "one 64-code step per E4M3 product");
     u32x4 af[FM][2], bfr[FN][2];
@@ -454,24 +491,48 @@ __device__ __forceinline__ void lds_gemm_step(const LdsCopyPlan<BM, BN, BK, WM *
     if constexpr (ST > 2) cp.issue((kn < nk ? kn : 0) * BK, sl.a[Q], sl.b[Q]);
     return;
   }
+  if constexpr (M16) {
+    // 16 x 16 x 32 products: lane l reads row l % 16 of a 16-row block, 16-byte chunk l / 16 of the
+    // 32-deep k-chunk (k = 8 (l / 16) .. +7), for both operands; 16 rows of one chunk fill the 64
+    // banks once under the row swizzle.
+    constexpr int FM16 = BM / WM / 16, FN16 = BN / WN / 16;
+    const int l16 = lane & 15, lq = lane >> 4;
 #pragma unroll
-  for (int kc = 0; kc < BK / 16; ++kc) {
-    u32x4 af[FM], bfr[FN];
+    for (int kc = 0; kc < BK / 32; ++kc) {
+      u32x4 af[FM16], bfr[FN16];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-      af[i] = *reinterpret_cast<const u32x4*>(sa + C::off(wm * (BM / WM) + i * 32 + lrow, kc * 2 + lhalf));
+      for (int i = 0; i < FM16; ++i)
+        af[i] = *reinterpret_cast<const u32x4*>(sa + C::off(wm * (BM / WM) + i * 16 + l16, kc * 4 + lq));
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      bfr[j] = *reinterpret_cast<const u32x4*>(sb + C::off(wn * (BN / WN) + j * 32 + lrow, kc * 2 + lhalf));
+      for (int j = 0; j < FN16; ++j)
+        bfr[j] = *reinterpret_cast<const u32x4*>(sb + C::off(wn * (BN / WN) + j * 16 + l16, kc * 4 + lq));
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM16; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) mfma_chunk(bfr[j], af[i], acc[i][j], bf16());  // C^T = W A^T
+        for (int j = 0; j < FN16; ++j)  // C^T = W A^T
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr[j]),
+                                                              __builtin_bit_cast(bf16x8, af[i]), acc[i][j], 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int kc = 0; kc < BK / 16; ++kc) {
+      u32x4 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = *reinterpret_cast<const u32x4*>(sa + C::off(wm * (BM / WM) + i * 32 + lrow, kc * 2 + lhalf));
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = *reinterpret_cast<const u32x4*>(sb + C::off(wn * (BN / WN) + j * 32 + lrow, kc * 2 + lhalf));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) mfma_chunk(bfr[j], af[i], acc[i][j], bf16());  // C^T = W A^T
+    }
   }
   if constexpr (ST > 2) cp.issue((kn < nk ? kn : 0) * BK, sl.a[Q], sl.b[Q]);
 }
 
-template <int BM, int BN, int BK, int ST, int WM, int WN, class Epi, bool F8 = false>
+template <int BM, int BN, int BK, int ST, int WM, int WN, class Epi, bool F8, bool M16>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(const bf16* __restrict__ A, int64_t lda,
                                                                 const bf16* __restrict__ W, int64_t ldw, int M,
                                                                 int N, int K, int tiles_m, int tiles_n, int gm,
@@ -493,33 +554,56 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(const bf16* __res
   const int m0 = tm * BM, n0 = tn * BN;
   const LdsCopyPlan<BM, BN, BK, NW> cp(A, lda, W, ldw, m0, n0, M, N);
 
-  f32x16 acc[FM][FN];
+  typename LdsAcc<BM / WM, BN / WN, M16>::type acc;
+  if constexpr (M16) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM * 2; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = zero16();
+      for (int j = 0; j < FN * 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = zero16();
+  }
 
   const int nk = K / BK;  // a multiple of ST
 #pragma unroll
   for (int s = 0; s < ST - 1; ++s) cp.issue(s * BK, sl.a[s], sl.b[s]);
   for (int kt = 0; kt < nk; kt += ST) {
-    lds_gemm_step<BM, BN, BK, ST, WM, WN, 0, F8>(cp, sl, kt, nk, acc);
-    lds_gemm_step<BM, BN, BK, ST, WM, WN, 1, F8>(cp, sl, kt + 1, nk, acc);
-    if constexpr (ST > 2) lds_gemm_step<BM, BN, BK, ST, WM, WN, 2 % ST, F8>(cp, sl, kt + 2, nk, acc);
-    if constexpr (ST > 3) lds_gemm_step<BM, BN, BK, ST, WM, WN, 3 % ST, F8>(cp, sl, kt + 3, nk, acc);
+    lds_gemm_step<BM, BN, BK, ST, WM, WN, 0, F8, M16>(cp, sl, kt, nk, acc);
+    lds_gemm_step<BM, BN, BK, ST, WM, WN, 1, F8, M16>(cp, sl, kt + 1, nk, acc);
+    if constexpr (ST > 2) lds_gemm_step<BM, BN, BK, ST, WM, WN, 2 % ST, F8, M16>(cp, sl, kt + 2, nk, acc);
+    if constexpr (ST > 3) lds_gemm_step<BM, BN, BK, ST, WM, WN, 3 % ST, F8, M16>(cp, sl, kt + 3, nk, acc);
   }
   wait_vmcnt<0>();  // the surplus copies past the last stage land before the LDS is released
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lrow = lane & 31, lhalf = lane >> 5;
   const int wm = wave / WN, wn = wave % WN;
-  run_epilogue<FM, FN>(epi, acc, m0 + wm * (BM / WM) + lrow, n0 + wn * (BN / WN) + lhalf * 4, M, N);
+  if constexpr (M16)
+    run_epilogue16<FM * 2, FN * 2>(epi, acc, m0 + wm * (BM / WM) + (lane & 15), n0 + wn * (BN / WN) + (lane >> 4) * 4,
+                                   M, N);
+  else
+    run_epilogue<FM, FN>(epi, acc, m0 + wm * (BM / WM) + lrow, n0 + wn * (BN / WN) + lhalf * 4, M, N);
 }
+
+// Which bf16 products take 16 x 16 x 32 MFMAs: the store and residual epilogues.  The Q/K/V epilogue keeps
+// 32 x 32 blocks, whose 32 consecutive tokens per lane group write 64-byte runs of the transposed V.
+template <class Epi>
+struct UseMfma16 {
+  static constexpr bool value = true;
+};
+template <typename OutT>
+struct UseMfma16<EpiQKV<OutT>> {
+  static constexpr bool value = false;
+};
 
 template <int BM, int BN, int BK, int ST, int WM, int WN, class Epi, bool F8 = false>
 hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K, const Epi& epi,
                       hipStream_t s) {
   const int tm = (int)ceil_div(M, BM), tn = (int)ceil_div(N, BN);
-  hipLaunchKernelGGL((gemm_lds_kernel<BM, BN, BK, ST, WM, WN, Epi, F8>), dim3((unsigned)(tm * tn)),
+  constexpr bool M16 = !F8 && UseMfma16<Epi>::value;
+  hipLaunchKernelGGL((gemm_lds_kernel<BM, BN, BK, ST, WM, WN, Epi, F8, M16>), dim3((unsigned)(tm * tn)),
                      dim3(WM * WN * 64), 0, s, A, lda, W, ldw, M, N, K, tm, tn, group_m(tn, K), epi);
   return hipGetLastError();
 }
