@@ -349,7 +349,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int BM, int BN, int BK, int NW>
+// M16: the stage is read by 16 x 16 x 32 fragments (lane l: row l % 16 of a 16-row block, chunk l / 16)
+// instead of 32 x 32 x 16 ones (lane l: row l % 32, chunk 2 kc + l / 32).  The two read patterns need
+// different row swizzles: measured with every 4-row-window swizzle in a read-only loop, the 32 x 32
+// pattern is conflict-free under slot = c ^ ((r / RPB) % CH) (221 B per clock and CU) where the 16 x 16
+// pattern runs 2-way conflicted (121 B); for the 16 x 16 pattern, slot = c ^ (2 bit3(r) + bit1(r)) reads
+// 202 B per clock (K steps of 32: four chunks per row).
+template <int BM, int BN, int BK, int NW, bool M16 = false>
 struct LdsGemmCfg {
   static constexpr int CH = BK / 8;        // 16-byte chunks per row
   static constexpr int RPB = 16 / CH;      // rows per 256-byte bank window
@@ -357,7 +363,12 @@ struct LdsGemmCfg {
   static constexpr int ABYTES = BM * ROWB, BBYTES = BN * ROWB;
   static constexpr int LA = ABYTES / 1024 / NW, LB = BBYTES / 1024 / NW;  // copies per wave per stage
   static_assert(CH >= 1 && CH <= 16 && LA * NW * 1024 == ABYTES && LB * NW * 1024 == BBYTES, "shape");
-  __device__ static __forceinline__ int off(int r, int c) { return r * ROWB + ((c ^ ((r / RPB) & (CH - 1))) << 4); }
+  static_assert(!M16 || CH == 4, "the 16 x 16 swizzle is for K steps of 32");
+  __device__ static __forceinline__ int swz(int r) {
+    if constexpr (M16) return ((r >> 2) & 2) | ((r >> 1) & 1);
+    return (r / RPB) & (CH - 1);
+  }
+  __device__ static __forceinline__ int off(int r, int c) { return r * ROWB + ((c ^ swz(r)) << 4); }
 };
 
 // The copies go through buffer resources (the MUBUF form of the direct-to-LDS load: lane i writes its
@@ -372,9 +383,9 @@ __device__ __forceinline__ void buffer_copy16(const void* base, uint32_t voff, u
                                            (lds_void*)lds, 16, voff, soff, 0, 0);
 }
 
-template <int BM, int BN, int BK, int NW>
+template <int BM, int BN, int BK, int NW, bool M16 = false>
 struct LdsCopyPlan {
-  using C = LdsGemmCfg<BM, BN, BK, NW>;
+  using C = LdsGemmCfg<BM, BN, BK, NW, M16>;
   const bf16* ba;  // wave-uniform tile bases
   const bf16* bb;
   uint32_t oa[C::LA];
@@ -392,13 +403,13 @@ struct LdsCopyPlan {
 #pragma unroll
     for (int i = 0; i < C::LA; ++i) {
       const int p = (i * NW + wave) * 64 + lane, r = p / C::CH, s = p % C::CH;
-      const int c = s ^ ((r / C::RPB) & (C::CH - 1));
+      const int c = s ^ C::swz(r);
       oa[i] = (uint32_t)(((int64_t)(min(m0 + r, M - 1) - m0) * lda + c * 8) * 2);
     }
 #pragma unroll
     for (int i = 0; i < C::LB; ++i) {
       const int p = (i * NW + wave) * 64 + lane, r = p / C::CH, s = p % C::CH;
-      const int c = s ^ ((r / C::RPB) & (C::CH - 1));
+      const int c = s ^ C::swz(r);
       ob[i] = (uint32_t)(((int64_t)(min(n0 + r, N - 1) - n0) * ldw + c * 8) * 2);
     }
   }
@@ -440,10 +451,10 @@ struct LdsSlots {
 // (lane half h reads 16-byte chunks 2h and 2h + 1 of its row, the same k for A and W).
 // M16 (bf16 only): 16 x 16 x 32 products on 16 x 16 accumulator blocks instead of 32 x 32 x 16 ones.
 template <int BM, int BN, int BK, int ST, int WM, int WN, int P, bool F8, bool M16>
-__device__ __forceinline__ void lds_gemm_step(const LdsCopyPlan<BM, BN, BK, WM * WN>& cp,
+__device__ __forceinline__ void lds_gemm_step(const LdsCopyPlan<BM, BN, BK, WM * WN, M16>& cp,
                                               const LdsSlots<BM, BN, BK, ST, WM, WN>& sl, int kt, int nk,
                                               typename LdsAcc<BM / WM, BN / WN, M16>::type& acc) {
-  using C = LdsGemmCfg<BM, BN, BK, WM * WN>;
+  using C = LdsGemmCfg<BM, BN, BK, WM * WN, M16>;
   constexpr int FM = BM / WM / 32, FN = BN / WN / 32, PER = C::LA + C::LB;
   wait_vmcnt<(ST - 2) * PER>();  // this wave's copies of stage kt have landed
   // Every wave's copies of stage kt are visible and slot (kt - 1) % ST is free after this barrier.
@@ -538,7 +549,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(const bf16* __res
                                                                 int N, int K, int tiles_m, int tiles_n, int gm,
                                                                Epi epi) {
   constexpr int NW = WM * WN;
-  using C = LdsGemmCfg<BM, BN, BK, NW>;
+  using C = LdsGemmCfg<BM, BN, BK, NW, M16>;
   constexpr int FM = BM / WM / 32, FN = BN / WN / 32;
   static_assert(ST >= 2 && ST <= 4, "stages");
   // One __shared__ object per ring slot, so the compiler can tell a slot being read from the slots
@@ -552,7 +563,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(const bf16* __res
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, gm, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const LdsCopyPlan<BM, BN, BK, NW> cp(A, lda, W, ldw, m0, n0, M, N);
+  const LdsCopyPlan<BM, BN, BK, NW, M16> cp(A, lda, W, ldw, m0, n0, M, N);
 
   typename LdsAcc<BM / WM, BN / WN, M16>::type acc;
   if constexpr (M16) {
