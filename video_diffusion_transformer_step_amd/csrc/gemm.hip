@@ -56,8 +56,8 @@ __device__ __forceinline__ float apply_act(float v, int act) {
 
 // Epilogues receive four consecutive columns n..n+3 of row m, in two phases: pre(m, n) issues every
 // load the group needs (bias, residual, gate, scales) and returns them; post(m, n, v, pre) does the
-// arithmetic and the stores.  run_epilogue issues the loads of the next 32 x 32 block before the stores
-// of the current one, so a lane waits about one memory latency per block rather than one per group.
+// arithmetic and the stores.  run_epilogue issues the loads of four groups before any of their stores,
+// so a lane waits about one memory latency per four groups rather than one per group.
 __device__ __forceinline__ float4 load_bias4(const float* bias, int n) {
   return bias ? *reinterpret_cast<const float4*>(bias + n) : make_float4(0.f, 0.f, 0.f, 0.f);
 }
@@ -332,7 +332,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restric
 // bf16 GEMM with asynchronous global -> LDS copies and a ring of ST LDS stages.
 //
 // One workgroup = WM x WN waves owning a BM x BN tile; a wave owns (BM/WM) x (BN/WN) (the block's
-// products use 8 waves of 64 x 128: 8 MFMA blocks, 128 accumulator registers, two waves per SIMD).
+// products use 8 waves of 64 x 128: 8 blocks of 32 x 32 or 32 of 16 x 16, 128 accumulator registers
+// either way, two waves per SIMD).
 // Each K step of BK elements is copied by direct-to-LDS loads straight into LDS, ST - 1 steps ahead
 // of its use, so the copies need no staging registers and have ST - 1 steps of MFMA work to land.
 // Row r of a stage holds BK * 2 bytes; its 16-byte chunk c sits at slot c ^ ((r / RPB) % CH) (RPB
@@ -351,7 +352,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // M16: the stage is read by 16 x 16 x 32 fragments (lane l: row l % 16 of a 16-row block, chunk l / 16)
 // instead of 32 x 32 x 16 ones (lane l: row l % 32, chunk 2 kc + l / 32).  The two read patterns need
-// different row swizzles: measured with every 4-row-window swizzle in a read-only loop, the 32 x 32
+// different row swizzles: measured in a read-only loop of each pattern, the 32 x 32
 // pattern is conflict-free under slot = c ^ ((r / RPB) % CH) (221 B per clock and CU) where the 16 x 16
 // pattern runs 2-way conflicted (121 B); for the 16 x 16 pattern, slot = c ^ (2 bit3(r) + bit1(r)) reads
 // 202 B per clock (K steps of 32: four chunks per row).
