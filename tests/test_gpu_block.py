@@ -183,6 +183,24 @@ def test_block_full_size_sampled_rows(name):
     _check(c, got, ref, x, rows=rows)
 
 
+@pytest.mark.timeout(600)
+def test_block_ragged_product_tiles():
+    """A bf16 block whose products all take the asynchronous-copy GEMM (4800 rows, K a multiple of 128)
+    with partial tiles in both directions: M = 4800 (last row tile 192 of 256), N = 1152, 3200 and 3456
+    (last column tile 128 of 256), on both MFMA forms (16 x 16 x 32 for O, cross-q, cross-O, FFN1, FFN2;
+    32 x 32 x 16 for Q/K/V), against the oracle on sampled rows."""
+    require_gpu()
+    c = wi.get_config("tiny").replace(dtype="bf16", T=5, H=48, W=80, B=1, dim=1152, heads=9, head_dim=128,
+                                      ffn_dim=3200, text_len=70)
+    assert c.S == 4800
+    case(f"block ragged product tiles {c.name} S={c.S} dim={c.dim} ffn={c.ffn_dim}")
+    rows = wi.sample_rows(c, 48, seed=4)
+    x, e0, t_emb, i_emb, bw = _inputs(c, seed=4)
+    got, = _gpu_block(c, x, e0, t_emb, i_emb, bw)
+    ref = _oracle_block(c, x, e0, t_emb, i_emb, bw, rows=rows)
+    _check(c, got, ref, x, rows=rows)
+
+
 # Quantised self-attention (WAN_FLAG_FP8_ATTN): its output carries the E4M3-bounded error of the
 # quantised path (<= 2^-4 rel-L2, see test_gpu_fp8.py); it reaches dx through W_o and gate1 while the
 # other branches keep bf16 accuracy, so dx is held to the same 2^-4.
