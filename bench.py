@@ -35,8 +35,8 @@ METRIC = "ms per DiT denoise step + attention TFLOP/s (% MFMA peak) at 32760 tok
 BLOCK_COUNTERS_FILE = os.path.join(ROOT, "profiles", "block_kernels_counters.json")
 CSRC = os.path.join(ROOT, "video_diffusion_transformer_step_amd", "csrc")
 # which source file holds each block launch's kernel (its counters are stale once that file changes)
-KERNEL_SOURCE = {"ln1": "norm.hip", "ln2": "norm.hip", "ln3": "norm.hip", "qk_norm_rope": "norm.hip",
-                 "vt_tail": "layout.hip", "mod_combine": "layout.hip", "self_attn": "attention.hip",
+KERNEL_SOURCE = {"ln1": "norm.hip", "ln2": "norm.hip", "ln3": "norm.hip", "qk_rms": "norm.hip",
+                 "attn_prologue": "layout.hip", "mod_combine": "layout.hip", "self_attn": "attention.hip",
                  "cross_attn": "attention.hip", "qkv_gemm": "gemm.hip", "o_gemm": "gemm.hip",
                  "cross_q_gemm": "gemm.hip", "cross_o_gemm": "gemm.hip", "ffn1_gemm": "gemm.hip",
                  "ffn2_gemm": "gemm.hip"}
@@ -645,14 +645,15 @@ def main():
               "cross_q_gemm": 2 * S * d * d, "cross_attn": 4 * S * (c.text_len + c.img_len) * d,
               "cross_o_gemm": 2 * S * d * d, "ffn1_gemm": 2 * S * d * f, "ffn2_gemm": 2 * S * f * d}
         # algorithmic bytes of the bandwidth-bound kernels: LN reads fp32 x and writes the bf16 operand;
-        # the QK norm + RoPE pass reads and writes bf16 q and k
-        hbm_bytes = {"ln1": 6 * S * d, "ln2": 6 * S * d, "ln3": 6 * S * d, "qk_norm_rope": 8 * S * d}
+        # the Q/K RMS pass reads the epilogue's sums of squares (2 d / 32 floats per token), reads and
+        # writes bf16 k and writes one float r_q per token
+        hbm_bytes = {"ln1": 6 * S * d, "ln2": 6 * S * d, "ln3": 6 * S * d, "qk_rms": 4 * S * d + S * d // 4 + 4 * S}
         # algorithmic bytes of every launch (each operand read once, each result written once; the
         # residual products read and write the fp32 x), per batch row except the weights
         L_ctx = c.text_len + c.img_len
         alg_bytes = dict(hbm_bytes)
         alg_bytes.update({
-            "qkv_gemm": 2 * S * d + 2 * S * 3 * d, "o_gemm": 2 * S * d + 8 * S * d,
+            "qkv_gemm": 2 * S * d + 2 * S * 3 * d + S * d // 4, "o_gemm": 2 * S * d + 8 * S * d,
             "cross_q_gemm": 4 * S * d, "cross_o_gemm": 2 * S * d + 8 * S * d, "ffn1_gemm": 2 * S * d + 2 * S * f,
             "ffn2_gemm": 2 * S * f + 8 * S * d, "self_attn": 8 * S * d, "cross_attn": 4 * S * d + 4 * L_ctx * d})
         w_bytes = {"qkv_gemm": 6 * d * d, "o_gemm": 2 * d * d, "cross_q_gemm": 2 * d * d, "cross_o_gemm": 2 * d * d,

@@ -349,11 +349,14 @@ int wan_gemm_e4m3(const void* a, int64_t lda, const float* a_scales, const void*
  * receives its wan_kernel_id, until capacity pairs are used.  The arrays must stay valid until
  * wan_profile_end, which returns the number of pairs recorded and disables recording.  Process-wide
  * state, not thread-safe; calls that overlap on several threads must not use it.
- * Ids name the block's launches in order; WAN_K_VT_TAIL is the zero fill of the padded keys of V^T
- * (the Q/K/V GEMM writes V^T itself); WAN_K_QUANT marks the three quantiser launches that precede
- * the self-attention under WAN_FLAG_FP8_ATTN. */
+ * Ids name the block's launches in order.  WAN_K_ATTN_PROLOGUE precedes the Q/K/V GEMM: it zero-fills
+ * the padded keys of V^T (the GEMM writes V^T itself) and writes the 3D RoPE table the GEMM's epilogue
+ * reads.  WAN_K_QK_RMS is the Q/K RMSNorm pass after the Q/K/V GEMM (whose epilogue applies the gains
+ * and the RoPE): it scales the k rows and keeps the q rows' factors for the attention's score scale.
+ * WAN_K_QUANT marks the three quantiser launches that precede the self-attention under
+ * WAN_FLAG_FP8_ATTN. */
 typedef enum {
-  WAN_K_LN1 = 0, WAN_K_QKV_GEMM = 1, WAN_K_QK_NORM_ROPE = 2, WAN_K_VT_TAIL = 3, WAN_K_SELF_ATTN = 4,
+  WAN_K_LN1 = 0, WAN_K_QKV_GEMM = 1, WAN_K_QK_RMS = 2, WAN_K_ATTN_PROLOGUE = 3, WAN_K_SELF_ATTN = 4,
   WAN_K_O_GEMM = 5, WAN_K_LN3 = 6, WAN_K_CROSS_Q_GEMM = 7, WAN_K_CROSS_ATTN = 8, WAN_K_CROSS_O_GEMM = 9,
   WAN_K_LN2 = 10, WAN_K_FFN1_GEMM = 11, WAN_K_FFN2_GEMM = 12, WAN_K_QUANT = 13
 } wan_kernel_id;

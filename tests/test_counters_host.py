@@ -7,8 +7,8 @@ import json
 from video_diffusion_transformer_step_amd import counters as C
 
 # kernel names as the block launches them (fragments are what the labeller matches)
-BLOCK = [("mod_combine_kernel", "mod_combine"), ("ln_mod_kernel", "ln1"), ("vt_tail_zero_kernel", "vt_tail"),
-         ("gemm_lds_kernel<EpiQKV>", "qkv_gemm"), ("qk_norm_rope_kernel", "qk_norm_rope"),
+BLOCK = [("mod_combine_kernel", "mod_combine"), ("ln_mod_kernel", "ln1"), ("attn_prologue_kernel", "attn_prologue"),
+         ("gemm_lds_kernel<EpiQKV>", "qkv_gemm"), ("qk_rms_kernel", "qk_rms"),
          ("attention_pp_kernel<bf16>", "self_attn"), ("gemm_lds_kernel<EpiResidual>", "o_gemm"),
          ("ln_mod_kernel", "ln3"), ("gemm_lds_kernel<EpiStore>", "cross_q_gemm"),
          ("attention_kernel<bf16,1>", "cross_attn"), ("gemm_lds_kernel<EpiResidual>", "cross_o_gemm"),

@@ -390,7 +390,7 @@ def mfma_peak_probe(kind, a_word, b_word, blocks, iters, out, stream=None):
     return blocks * 4 * 4 * iters * MFMA_PROBE_FLOP[kind]
 
 
-KERNEL_IDS = ["ln1", "qkv_gemm", "qk_norm_rope", "vt_tail", "self_attn", "o_gemm", "ln3", "cross_q_gemm",
+KERNEL_IDS = ["ln1", "qkv_gemm", "qk_rms", "attn_prologue", "self_attn", "o_gemm", "ln3", "cross_q_gemm",
               "cross_attn", "cross_o_gemm", "ln2", "ffn1_gemm", "ffn2_gemm", "quant"]
 
 

@@ -36,14 +36,14 @@ import re
 import sys
 
 # Order of the launches of one bf16 block (no attention cache, no quantised path).
-BLOCK_ORDER = ["mod_combine", "ln1", "vt_tail", "qkv_gemm", "qk_norm_rope", "self_attn", "o_gemm", "ln3",
+BLOCK_ORDER = ["mod_combine", "ln1", "attn_prologue", "qkv_gemm", "qk_rms", "self_attn", "o_gemm", "ln3",
                "cross_q_gemm", "cross_attn", "cross_o_gemm", "ln2", "ffn1_gemm", "ffn2_gemm"]
 # kernel-name fragment -> the labels its launches take, in their order inside a block
 BY_NAME = [("mod_combine", ["mod_combine"]),
            ("ln_mod", ["ln1", "ln3", "ln2"]),
-           ("vt_tail_zero", ["vt_tail"]),
+           ("attn_prologue", ["attn_prologue"]),
            ("EpiQKV", ["qkv_gemm"]),
-           ("qk_norm_rope", ["qk_norm_rope"]),
+           ("qk_rms", ["qk_rms"]),
            ("attention_pp_kernel", ["self_attn"]),
            ("EpiResidual", ["o_gemm", "cross_o_gemm", "ffn2_gemm"]),
            ("EpiStore", ["cross_q_gemm", "ffn1_gemm"]),

@@ -687,6 +687,13 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[AttnCfg<T, HD>::N
 }
 
 // Q^T as the B operand: lane holds query qrow (clamped), 16 bytes per 32-byte chunk of hd.
+// The score scale of one query (exp2 units): c_log2, times the query row's factor when qscale [B, S]
+// is given (the block's RMSNorm factor r_q, folded here instead of into the stored q row).  Both
+// lanes holding a query (l and l + 32) read the same value.
+__device__ __forceinline__ float query_scale(float c_log2, const float* __restrict__ qscale, int b, int qrow, int S) {
+  return qscale ? c_log2 * qscale[(int64_t)b * S + min(qrow, S - 1)] : c_log2;
+}
+
 template <typename T, int HD>
 __device__ __forceinline__ void load_q(const T* __restrict__ q, int64_t q_bs, int64_t q_ss, int b, int h, int qrow,
                                        int S, u32x4 (&qf)[AttnCfg<T, HD>::NCH]) {
@@ -701,8 +708,9 @@ __device__ __forceinline__ void load_q(const T* __restrict__ q, int64_t q_bs, in
 template <typename T, int HD, int KIND>
 __global__ __launch_bounds__(256, 2) void attention_kernel(const T* __restrict__ q, int64_t q_bs, int64_t q_ss,
                                                             KVStream kv, int S, int H, float c_log2,
-                                                            T* __restrict__ out, int64_t o_bs, int64_t o_ss,
-                                                            float* __restrict__ lse, KeySplit ks, int accum) {
+                                                            const float* __restrict__ qscale, T* __restrict__ out,
+                                                            int64_t o_bs, int64_t o_ss, float* __restrict__ lse,
+                                                            KeySplit ks, int accum) {
   using C = AttnCfg<T, HD>;
   __shared__ u32x4 k0_raw[C::KBYTES / 16], k1_raw[C::KBYTES / 16], v0_raw[C::VBYTES / 16], v1_raw[C::VBYTES / 16];
   const Slots<T, HD> sl{reinterpret_cast<char*>(k0_raw), reinterpret_cast<char*>(k1_raw),
@@ -715,6 +723,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const T* __restrict__
   const FragAddr<T, HD> fa;
   u32x4 qf[C::NCH];
   load_q<T, HD>(q, q_bs, q_ss, b, h, qrow, S, qf);
+  const float cq = query_scale(c_log2, qscale, b, qrow, S);
 
   f32x16 o[C::ND], acc[C::ND];
   SoftState st;
@@ -722,7 +731,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const T* __restrict__
   for (int d = 0; d < C::ND; ++d) o[d] = zero16();
   st.m = -__builtin_inff();
   st.l = 0.f;
-  attend_stream<T, HD>(qf, fa, kv, b, h, H, c_log2, sl, o, st);
+  attend_stream<T, HD>(qf, fa, kv, b, h, H, cq, sl, o, st);
   finish_stream<T, HD>(o, st, acc);
   if (lse != nullptr) write_lse(st, lse, b, h, H, qrow, S);
   store_rows<T, HD>(acc, out, o_bs, o_ss, b, h, qrow, S, accum != 0);
@@ -834,6 +843,7 @@ __device__ __forceinline__ void attend_stream_pp(const u32x4 (&qf)[AttnCfg<T, HD
 template <typename T, int HD, int KIND>
 __global__ __launch_bounds__(512, 1) void attention_pp_kernel(const T* __restrict__ q, int64_t q_bs, int64_t q_ss,
                                                                KVStream kv, int S, int H, float c_log2,
+                                                               const float* __restrict__ qscale,
                                                                T* __restrict__ out, int64_t o_bs, int64_t o_ss,
                                                                float* __restrict__ lse, KeySplit ks) {
   using C = AttnCfg<T, HD>;
@@ -850,6 +860,7 @@ __global__ __launch_bounds__(512, 1) void attention_pp_kernel(const T* __restric
   const FragAddr<T, HD> fa;
   u32x4 qf[C::NCH];
   load_q<T, HD>(q, q_bs, q_ss, b, h, qrow, S, qf);
+  const float cq = query_scale(c_log2, qscale, b, qrow, S);
 
   f32x16 o[C::ND], acc[C::ND];
   SoftState st;
@@ -857,7 +868,7 @@ __global__ __launch_bounds__(512, 1) void attention_pp_kernel(const T* __restric
   for (int d = 0; d < C::ND; ++d) o[d] = zero16();
   st.m = -__builtin_inff();
   st.l = 0.f;
-  attend_stream_pp<T, HD>(qf, fa, kv, b, h, H, grp, c_log2, sl, o, st);
+  attend_stream_pp<T, HD>(qf, fa, kv, b, h, H, grp, cq, sl, o, st);
   finish_stream<T, HD>(o, st, acc);
   if (lse != nullptr) write_lse(st, lse, b, h, H, qrow, S);
   store_rows<T, HD>(acc, out, o_bs, o_ss, b, h, qrow, S);
@@ -1091,7 +1102,8 @@ __device__ __forceinline__ void pp_tile_q8(const u32x4 (&qf)[AttnCfg<uint8_t, HD
 template <int HD>
 __global__ __launch_bounds__(512, 1) void attention_q8_kernel(const uint8_t* __restrict__ q, int64_t q_bs,
                                                               int64_t q_ss, const float* __restrict__ sq, KVq8 kv,
-                                                              int S, int H, float c_log2, bf16* __restrict__ out,
+                                                              int S, int H, float c_log2,
+                                                              const float* __restrict__ qscale, bf16* __restrict__ out,
                                                               int64_t o_bs, int64_t o_ss, float* __restrict__ lse) {
   using C = AttnCfg<uint8_t, HD>;
   using CP = CopyPlan<uint8_t, HD, 8>;
@@ -1107,7 +1119,7 @@ __global__ __launch_bounds__(512, 1) void attention_q8_kernel(const uint8_t* __r
   const FragQ8<HD> fa;
   u32x4 qf[C::NCH];
   load_q<uint8_t, HD>(q, q_bs, q_ss, b, h, qrow, S, qf);
-  const float cq = c_log2 * sq[((int64_t)b * H + h) * S + min(qrow, S - 1)];
+  const float cq = query_scale(c_log2, qscale, b, qrow, S) * sq[((int64_t)b * H + h) * S + min(qrow, S - 1)];
 
   const uint8_t* kbase = kv.k + (int64_t)b * kv.k_bs + (int64_t)h * HD;
   const uint8_t* vtb = kv.vt + ((int64_t)b * H + h) * HD * (int64_t)kv.Lpad;
@@ -1160,10 +1172,11 @@ __global__ __launch_bounds__(512, 1) void attention_q8_kernel(const uint8_t* __r
 
 template <int HD>
 hipError_t launch_q8_hd(const uint8_t* q, int64_t q_bs, int64_t q_ss, const float* sq, const KVq8& kv, int B, int S,
-                        int H, float c_log2, bf16* o, int64_t o_bs, int64_t o_ss, float* lse, hipStream_t s) {
+                        int H, float c_log2, const float* qscale, bf16* o, int64_t o_bs, int64_t o_ss, float* lse,
+                        hipStream_t s) {
   dim3 grid((unsigned)ceil_div(S, 256), (unsigned)H, (unsigned)B);
-  hipLaunchKernelGGL((attention_q8_kernel<HD>), grid, dim3(512), 0, s, q, q_bs, q_ss, sq, kv, S, H, c_log2, o, o_bs,
-                     o_ss, lse);
+  hipLaunchKernelGGL((attention_q8_kernel<HD>), grid, dim3(512), 0, s, q, q_bs, q_ss, sq, kv, S, H, c_log2, qscale, o,
+                     o_bs, o_ss, lse);
   return hipGetLastError();
 }
 
@@ -1172,15 +1185,16 @@ hipError_t launch_q8_hd(const uint8_t* q, int64_t q_bs, int64_t q_ss, const floa
 // hundred keys, where the per-stream prologue dominates) and fp32 use the four-wave kernel.
 template <typename T, int HD, int KIND>
 hipError_t launch_hd(const T* q, int64_t q_bs, int64_t q_ss, KVStream kv, int B, int S, int H, float c_log2,
-                     T* o, int64_t o_bs, int64_t o_ss, float* lse, const KeySplit& ks, int accum, hipStream_t s) {
+                     const float* qscale, T* o, int64_t o_bs, int64_t o_ss, float* lse, const KeySplit& ks, int accum,
+                     hipStream_t s) {
   if constexpr (sizeof(T) == 2 && KIND == 0) {
     dim3 grid((unsigned)ceil_div(S, 256), (unsigned)H, (unsigned)(B * ks.n));
-    hipLaunchKernelGGL((attention_pp_kernel<T, HD, KIND>), grid, dim3(512), 0, s, q, q_bs, q_ss, kv, S, H, c_log2, o,
-                       o_bs, o_ss, lse, ks);
+    hipLaunchKernelGGL((attention_pp_kernel<T, HD, KIND>), grid, dim3(512), 0, s, q, q_bs, q_ss, kv, S, H, c_log2,
+                       qscale, o, o_bs, o_ss, lse, ks);
   } else {
     dim3 grid((unsigned)ceil_div(S, 128), (unsigned)H, (unsigned)(B * ks.n));
-    hipLaunchKernelGGL((attention_kernel<T, HD, KIND>), grid, dim3(256), 0, s, q, q_bs, q_ss, kv, S, H, c_log2, o,
-                       o_bs, o_ss, lse, ks, accum);
+    hipLaunchKernelGGL((attention_kernel<T, HD, KIND>), grid, dim3(256), 0, s, q, q_bs, q_ss, kv, S, H, c_log2,
+                       qscale, o, o_bs, o_ss, lse, ks, accum);
   }
   return hipGetLastError();
 }
@@ -1190,7 +1204,7 @@ hipError_t launch_hd(const T* q, int64_t q_bs, int64_t q_ss, KVStream kv, int B,
 template <typename T>
 hipError_t launch_attention(const T* q, int64_t q_bs, int64_t q_ss, KVStream kv, int B, int S, int H, int hd,
                             float scale, T* o, int64_t o_bs, int64_t o_ss, int kind, hipStream_t s, float* lse,
-                            KeySplit ks, bool accumulate) {
+                            KeySplit ks, bool accumulate, const float* qscale) {
   if (S <= 0 || B <= 0 || H <= 0) return hipSuccess;
   if (kv.L <= 0 || kv.Lpad % KT != 0 || kv.Lpad < kv.L) return hipErrorInvalidValue;
   if (ks.n < 1 || (int64_t)B * ks.n > 65535) return hipErrorInvalidValue;
@@ -1202,20 +1216,20 @@ hipError_t launch_attention(const T* q, int64_t q_bs, int64_t q_ss, KVStream kv,
   const float c_log2 = scale * 1.4426950408889634f;
   if (hd == 128) {
     if (kind)
-      return launch_hd<T, 128, 1>(q, q_bs, q_ss, kv, B, S, H, c_log2, o, o_bs, o_ss, lse, ks, acc, s);
-    return launch_hd<T, 128, 0>(q, q_bs, q_ss, kv, B, S, H, c_log2, o, o_bs, o_ss, lse, ks, acc, s);
+      return launch_hd<T, 128, 1>(q, q_bs, q_ss, kv, B, S, H, c_log2, qscale, o, o_bs, o_ss, lse, ks, acc, s);
+    return launch_hd<T, 128, 0>(q, q_bs, q_ss, kv, B, S, H, c_log2, qscale, o, o_bs, o_ss, lse, ks, acc, s);
   }
   if (hd == 64) {
     if (kind)
-      return launch_hd<T, 64, 1>(q, q_bs, q_ss, kv, B, S, H, c_log2, o, o_bs, o_ss, lse, ks, acc, s);
-    return launch_hd<T, 64, 0>(q, q_bs, q_ss, kv, B, S, H, c_log2, o, o_bs, o_ss, lse, ks, acc, s);
+      return launch_hd<T, 64, 1>(q, q_bs, q_ss, kv, B, S, H, c_log2, qscale, o, o_bs, o_ss, lse, ks, acc, s);
+    return launch_hd<T, 64, 0>(q, q_bs, q_ss, kv, B, S, H, c_log2, qscale, o, o_bs, o_ss, lse, ks, acc, s);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_attention_q8(const uint8_t* q8, const float* sq, const uint8_t* k8, const float* sk,
                                const uint8_t* v8t, const float* sv, int B, int S, int L, int H, int hd, bf16* o,
-                               float* lse, hipStream_t s) {
+                               float* lse, hipStream_t s, const float* qscale) {
   if (S <= 0 || B <= 0 || H <= 0) return hipSuccess;
   if (L <= 0) return hipErrorInvalidValue;
   const int64_t dim = (int64_t)H * hd;
@@ -1223,7 +1237,8 @@ hipError_t launch_attention_q8(const uint8_t* q8, const float* sq, const uint8_t
   const float c_log2 = 1.4426950408889634f / sqrtf((float)hd);
   // head_dim 128 only: a 64-key tile of 64-byte rows is too small to split over the 8 waves' copies
   if (hd == 128)
-    return launch_q8_hd<128>(q8, (int64_t)S * dim, dim, sq, kv, B, S, H, c_log2, o, (int64_t)S * dim, dim, lse, s);
+    return launch_q8_hd<128>(q8, (int64_t)S * dim, dim, sq, kv, B, S, H, c_log2, qscale, o, (int64_t)S * dim, dim,
+                             lse, s);
   return hipErrorInvalidValue;
 }
 
@@ -1326,9 +1341,10 @@ template hipError_t launch_lse_merge<bf16>(const void* const*, const float* cons
                                            float*, hipStream_t);
 
 template hipError_t launch_attention<float>(const float*, int64_t, int64_t, KVStream, int, int, int, int, float,
-                                            float*, int64_t, int64_t, int, hipStream_t, float*, KeySplit, bool);
+                                            float*, int64_t, int64_t, int, hipStream_t, float*, KeySplit, bool,
+                                            const float*);
 template hipError_t launch_attention<bf16>(const bf16*, int64_t, int64_t, KVStream, int, int, int, int, float, bf16*,
-                                           int64_t, int64_t, int, hipStream_t, float*, KeySplit, bool);
+                                           int64_t, int64_t, int, hipStream_t, float*, KeySplit, bool, const float*);
 
 template <typename T>
 void attention_tile(int kind, int& rows, int& per_cu) {

@@ -26,9 +26,13 @@
 //  * k is accumulated in increasing order in every configuration; a configuration's results
 //    are bitwise repeatable, and configurations on different MFMA shapes (16 x 16 x 32 for the
 //    store and residual products, 32 x 32 x 16 elsewhere) may differ in the last bits;
-//  * epilogues fuse the bias, GELU / SiLU, the output cast and the adaLN-gated
-//    residual update x += gate * (.) ("图解 Wan2.1 I2V" §5.2).
+//  * epilogues fuse the bias, GELU / SiLU, the output cast, the adaLN-gated
+//    residual update x += gate * (.) ("图解 Wan2.1 I2V" §5.2), and for the Q/K/V
+//    projection the q/k RMSNorm gains, the 3D RoPE and the row sums of squares of
+//    the RMSNorm, plus the transposed V layout (§5.3).
 #include "wan_internal.h"
+
+#include <type_traits>
 
 namespace wan {
 
@@ -54,10 +58,27 @@ __device__ __forceinline__ float apply_act(float v, int act) {
   return v;
 }
 
+// Whether an epilogue reports per-row block sums (its kBlockSums member; false if it has none).
+template <class E, class = void>
+struct BlockSums : std::false_type {};
+template <class E>
+struct BlockSums<E, std::void_t<decltype(E::kBlockSums)>> : std::integral_constant<bool, E::kBlockSums> {};
+
 // Epilogues receive four consecutive columns n..n+3 of row m, in two phases: pre(m, n) issues every
 // load the group needs (bias, residual, gate, scales) and returns them; post(m, n, v, pre) does the
 // arithmetic and the stores.  run_epilogue issues the loads of four groups before any of their stores,
 // so a lane waits about one memory latency per four groups rather than one per group.
+// Loads through the constant address space (memory the kernel only reads).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float4 load_const4(const float* p) {
+  const f32x4 v = *(const __attribute__((address_space(4))) f32x4*)p;
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ float2 load_const2(const float2* p) {
+  const f32x2 v = *(const __attribute__((address_space(4))) f32x2*)p;
+  return make_float2(v[0], v[1]);
+}
+
 __device__ __forceinline__ float4 load_bias4(const float* bias, int n) {
   return bias ? *reinterpret_cast<const float4*>(bias + n) : make_float4(0.f, 0.f, 0.f, 0.f);
 }
@@ -88,42 +109,90 @@ struct EpiStore {
   }
 };
 
-// Q/K/V projection: columns [0, vcol0) (q, k) are stored row-major like EpiStore; columns >= vcol0
-// (v) go straight to the per-head transposed layout V^T[b, h, d, pos] the attention kernels read
-// (pos = token within its batch row, bf16 keys permuted within 16-key groups: position p holds key
-// p with bits 2 and 3 swapped).
+// Q/K/V projection ("图解 Wan2.1 I2V" §5.3): columns [0, vcol0) hold q, then k (dim = vcol0 / 2 each);
+// columns >= vcol0 hold v.
+//  * q, k are stored row-major as RoPE(g * (C + bias)): the RMSNorm gains g (gq, gk), then the 3D
+//    rotation of the token's (frame, row, column) position.  The RMS factor itself needs the whole
+//    row, which spans several column tiles, so post returns the group's sum of squares of C + bias;
+//    run_epilogue adds these up over each 32-column block and passes the block's sum to ssq_store.
+//    The factor is applied later: to the k rows by launch_qk_rms, and to the q rows inside the
+//    attention's score scale (both the gains and the rotation are linear, so it commutes with them).
+//  * v goes straight to the per-head transposed layout V^T[b, h, d, pos] the attention kernels read
+//    (pos = token within its batch row, bf16 keys permuted within 16-key groups: position p holds
+//    key p with bits 2 and 3 swapped).
 template <typename T>
 struct EpiQKV {
+  static constexpr bool kBlockSums = true;
   T* out;
   int64_t ldo;
   const float* bias;
   T* vt;
   int vcol0, S, H, hd, Spad;
+  const float* gq;
+  const float* gk;
+  float* ssq;          // [vcol0 / 32, ldp]
+  int64_t ldp;         // the product's M
+  const float2* rope;  // (cos, sin) table, layout at QKNormRope
+  int Hp, Wp, npT, npH, baseH, baseW;
   struct Pre {
-    float4 b;
+    float4 b, g;      // bias, gains
+    float2 cs0, cs1;  // (cos, sin) of the pairs (n, n+1), (n+2, n+3)
   };
-  __device__ __forceinline__ Pre pre(int, int n) const { return Pre{load_bias4(bias, n)}; }
-  __device__ __forceinline__ void post(int m, int n, float4 v, const Pre& p) const {
+  __device__ __forceinline__ int rope_entry(int p, const RopePos& t) const {
+    return p < npT         ? t.f * npT + p
+           : p < npT + npH ? baseH + t.i * npH + (p - npT)
+                           : baseW + t.j * npH + (p - npT - npH);
+  }
+  // Bias, gains and table are read through the constant address space: the compiler then knows the
+  // epilogue's stores cannot change them, so a lane's loads of the same column for its two rows (and
+  // the row's position decode, outside the region test) merge into one.
+  __device__ __forceinline__ Pre pre(int m, int n) const {
+    const int dim = vcol0 >> 1;
+    Pre p;
+    p.b = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (bias) p.b = load_const4(bias + n);
+    const int c = n < dim ? n : min(n - dim, dim - 4);
+    p.g = load_const4((n < dim ? gq : gk) + c);
+    const RopePos t = rope_pos(m % S, Hp, Wp);
+    const int p0 = (c & (hd - 1)) >> 1;  // channels 2 p0 .. 2 p0 + 3 of one head
+    if (n < vcol0) {
+      p.cs0 = load_const2(rope + rope_entry(p0, t));
+      p.cs1 = load_const2(rope + rope_entry(p0 + 1, t));
+    } else {
+      p.cs0 = p.cs1 = make_float2(1.f, 0.f);
+    }
+    return p;
+  }
+  __device__ __forceinline__ float post(int m, int n, float4 v, const Pre& p) const {
     v.x += p.b.x; v.y += p.b.y; v.z += p.b.z; v.w += p.b.w;
     if (n < vcol0) {
+      const float ss = (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
+      const float a0 = v.x * p.g.x, b0 = v.y * p.g.y, a1 = v.z * p.g.z, b1 = v.w * p.g.w;
+      const float r0 = a0 * p.cs0.x - b0 * p.cs0.y, r1 = a0 * p.cs0.y + b0 * p.cs0.x;
+      const float r2 = a1 * p.cs1.x - b1 * p.cs1.y, r3 = a1 * p.cs1.y + b1 * p.cs1.x;
       T* q = out + (int64_t)m * ldo + n;
       if constexpr (sizeof(T) == 2) {
         bf16x4 o;
-        o[0] = (bf16)v.x; o[1] = (bf16)v.y; o[2] = (bf16)v.z; o[3] = (bf16)v.w;
+        o[0] = (bf16)r0; o[1] = (bf16)r1; o[2] = (bf16)r2; o[3] = (bf16)r3;
         *reinterpret_cast<bf16x4*>(q) = o;
       } else {
-        *reinterpret_cast<float4*>(q) = v;
+        *reinterpret_cast<float4*>(q) = make_float4(r0, r1, r2, r3);
       }
-    } else {
-      const int nn = n - vcol0, h = nn / hd, d = nn - h * hd;  // 4 channels d..d+3 of head h
-      const int b = m / S, pos = m - b * S;
-      const int pp = sizeof(T) == 2 ? ((pos & ~12) | ((pos & 4) << 1) | ((pos & 8) >> 1)) : pos;
-      T* q = vt + (((int64_t)b * H + h) * hd + d) * Spad + pp;
-      q[0] = from_f32<T>(v.x);
-      q[Spad] = from_f32<T>(v.y);
-      q[2 * (int64_t)Spad] = from_f32<T>(v.z);
-      q[3 * (int64_t)Spad] = from_f32<T>(v.w);
+      return ss;
     }
+    const int nn = n - vcol0, h = nn / hd, d = nn - h * hd;  // 4 channels d..d+3 of head h
+    const int b = m / S, pos = m - b * S;
+    const int pp = sizeof(T) == 2 ? ((pos & ~12) | ((pos & 4) << 1) | ((pos & 8) >> 1)) : pos;
+    T* q = vt + (((int64_t)b * H + h) * hd + d) * Spad + pp;
+    q[0] = from_f32<T>(v.x);
+    q[Spad] = from_f32<T>(v.y);
+    q[2 * (int64_t)Spad] = from_f32<T>(v.z);
+    q[3 * (int64_t)Spad] = from_f32<T>(v.w);
+    return 0.f;
+  }
+  // Row m's sum of squares over the 32 columns n0 .. n0 + 31 (n0 a multiple of 32).
+  __device__ __forceinline__ void ssq_store(int m, int n0, float sum) const {
+    if (n0 < vcol0) ssq[(int64_t)(n0 >> 5) * ldp + m] = sum;
   }
 };
 
@@ -161,21 +230,35 @@ struct EpiResidual {
 // range), then do their arithmetic and guarded stores, so a lane waits about one memory latency per
 // block rather than one per group.  (Issuing the next block's loads before this block's stores as well
 // needs a second set of registers and spills.)
+// An epilogue with kBlockSums set (the Q/K/V one) returns a float from post and receives, through
+// ssq_store, the sum of those values over each 32-column block of a row: lanes l and l + 32 hold the
+// row's 32 columns.
 template <int FM, int FN, class Epi>
 __device__ __forceinline__ void run_epilogue(const Epi& epi, const f32x16 (&acc)[FM][FN], int mrow, int ncol, int M,
                                              int N) {
+  constexpr bool kBlockSums = BlockSums<Epi>::value;
 #pragma unroll
   for (int q = 0; q < FM * FN; ++q) {
     const int i = q / FN, j = q % FN, m = mrow + i * 32, mc = min(m, M - 1);
     typename Epi::Pre pre[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) pre[g] = epi.pre(mc, min(ncol + j * 32 + g * 8, N - 4));
+    float sum = 0.f;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int n = ncol + j * 32 + g * 8;
-      if (m < M && n < N)
-        epi.post(m, n, make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]),
-                 pre[g]);
+      if (m < M && n < N) {
+        const float4 v =
+            make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+        if constexpr (kBlockSums)
+          sum += epi.post(m, n, v, pre[g]);
+        else
+          epi.post(m, n, v, pre[g]);
+      }
+    }
+    if constexpr (kBlockSums) {
+      sum = half_sum(sum);  // every lane of the wave takes part
+      if ((threadIdx.x & 32) == 0 && m < M) epi.ssq_store(m, (ncol + j * 32) & ~31, sum);
     }
   }
 }
@@ -624,6 +707,7 @@ hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, in
 // wrapped epilogue.
 template <class Epi>
 struct EpiScaled {
+  static constexpr bool kBlockSums = BlockSums<Epi>::value;
   const float* row_scale;
   const float* w_scale;  // one value, on the device
   Epi inner;
@@ -632,10 +716,11 @@ struct EpiScaled {
     typename Epi::Pre in;
   };
   __device__ __forceinline__ Pre pre(int m, int n) const { return Pre{row_scale[m] * *w_scale, inner.pre(m, n)}; }
-  __device__ __forceinline__ void post(int m, int n, float4 v, const Pre& p) const {
+  __device__ __forceinline__ auto post(int m, int n, float4 v, const Pre& p) const {
     v.x *= p.sc; v.y *= p.sc; v.z *= p.sc; v.w *= p.sc;
-    inner.post(m, n, v, p.in);
+    return inner.post(m, n, v, p.in);
   }
+  __device__ __forceinline__ void ssq_store(int m, int n0, float sum) const { inner.ssq_store(m, n0, sum); }
 };
 
 // E4M3 product ("Wan 技术深度解析" §5.3: per-token activation, per-tensor weight scales): A codes [M, K]
@@ -743,11 +828,29 @@ hipError_t gemm_store(const T* A, int64_t lda, const T* W, int64_t ldw, int M, i
   return run_gemm<T>(A, lda, W, ldw, M, N, K, EpiStore<OutT, ACT_NONE>{out, ldo, bias}, s);
 }
 
+namespace {
+
+template <typename T>
+EpiQKV<T> make_epi_qkv(T* qk, int64_t ldo, const float* bias, T* vt, int M, int dim, int S, int H, int hd, int Spad,
+                       const QKNormRope& nr) {
+  const int npT = rope_pairs_time(hd), npH = rope_pairs_space(hd);
+  const int baseH = nr.T * npT, baseW = baseH + nr.Hp * npH;
+  return EpiQKV<T>{qk, ldo, bias, vt, 2 * dim, S, H, hd, Spad, nr.gq, nr.gk, nr.ssq, M, nr.rope, nr.Hp, nr.Wp, npT,
+                   npH, baseH, baseW};
+}
+
+bool qkv_args_ok(int M, int dim, int S, int hd, const QKNormRope& nr) {
+  return hd >= 4 && (hd & (hd - 1)) == 0 && dim % 32 == 0 && dim % hd == 0 && nr.gq && nr.gk && nr.ssq && nr.rope &&
+         nr.T > 0 && nr.Hp > 0 && nr.Wp > 0 && (int64_t)nr.T * nr.Hp * nr.Wp == S && M % S == 0;
+}
+
+}  // namespace
+
 template <typename T>
 hipError_t gemm_qkv(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int dim, int K, const float* bias,
-                    T* qk, int64_t ldo, T* vt, int S, int H, int hd, int Spad, hipStream_t s) {
-  if (hd % 4 != 0) return hipErrorInvalidValue;
-  return run_gemm<T>(A, lda, W, ldw, M, 3 * dim, K, EpiQKV<T>{qk, ldo, bias, vt, 2 * dim, S, H, hd, Spad}, s);
+                    T* qk, int64_t ldo, T* vt, int S, int H, int hd, int Spad, const QKNormRope& nr, hipStream_t s) {
+  if (!qkv_args_ok(M, dim, S, hd, nr)) return hipErrorInvalidValue;
+  return run_gemm<T>(A, lda, W, ldw, M, 3 * dim, K, make_epi_qkv<T>(qk, ldo, bias, vt, M, dim, S, H, hd, Spad, nr), s);
 }
 
 template <typename T>
@@ -767,10 +870,10 @@ hipError_t gemm_e4m3_store(const uint8_t* A, int64_t lda, const float* a_scales,
 
 hipError_t gemm_qkv_e4m3(const uint8_t* A, int64_t lda, const float* a_scales, const uint8_t* W, int64_t ldw,
                          const float* w_scale, int M, int dim, int K, const float* bias, bf16* qk, int64_t ldo, bf16* vt,
-                         int S, int H, int hd, int Spad, hipStream_t s) {
-  if (hd % 4 != 0) return hipErrorInvalidValue;
+                         int S, int H, int hd, int Spad, const QKNormRope& nr, hipStream_t s) {
+  if (!qkv_args_ok(M, dim, S, hd, nr)) return hipErrorInvalidValue;
   return run_gemm_e4m3(A, lda, a_scales, W, ldw, w_scale, M, 3 * dim, K,
-                       EpiQKV<bf16>{qk, ldo, bias, vt, 2 * dim, S, H, hd, Spad}, s);
+                       make_epi_qkv<bf16>(qk, ldo, bias, vt, M, dim, S, H, hd, Spad, nr), s);
 }
 
 hipError_t gemm_e4m3_residual(const uint8_t* A, int64_t lda, const float* a_scales, const uint8_t* W, int64_t ldw,
@@ -805,9 +908,9 @@ template hipError_t gemm_store<bf16, bf16>(const bf16*, int64_t, const bf16*, in
 template hipError_t gemm_store<bf16, float>(const bf16*, int64_t, const bf16*, int64_t, int, int, int,
                                             const float*, int, float*, int64_t, hipStream_t);
 template hipError_t gemm_qkv<float>(const float*, int64_t, const float*, int64_t, int, int, int, const float*, float*,
-                                    int64_t, float*, int, int, int, int, hipStream_t);
+                                    int64_t, float*, int, int, int, int, const QKNormRope&, hipStream_t);
 template hipError_t gemm_qkv<bf16>(const bf16*, int64_t, const bf16*, int64_t, int, int, int, const float*, bf16*,
-                                   int64_t, bf16*, int, int, int, int, hipStream_t);
+                                   int64_t, bf16*, int, int, int, int, const QKNormRope&, hipStream_t);
 template hipError_t gemm_residual<float>(const float*, int64_t, const float*, int64_t, int, int, int, const float*,
                                          const float*, int, int, float*, int64_t, hipStream_t, float*);
 template hipError_t gemm_residual<bf16>(const bf16*, int64_t, const bf16*, int64_t, int, int, int, const float*,

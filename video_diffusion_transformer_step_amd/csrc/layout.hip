@@ -163,13 +163,35 @@ __global__ __launch_bounds__(256) void mod_combine_kernel(const float* __restric
     mod[i] = e0[i] + mb[i % (6 * (int64_t)dim)];
 }
 
+// The launch before the block's Q/K/V product (see launch_attn_prologue): entries [0, nrope) write the
+// 3D RoPE table ("图解 Wan2.1 I2V" §5.3 ②) the product's epilogue reads, the rest clear the padded key
+// positions S .. Spad - 1 of each V^T row.  Table entry (pos, m) of a segment of width n holds the
+// cosine and sine of pos * theta^(-2m/n), computed in double precision: frame rows (nT x npT pairs),
+// then height rows (nH x npH), then width rows (nW x npH).
 template <typename T>
-__global__ __launch_bounds__(256) void vt_tail_zero_kernel(T* __restrict__ vt, int64_t rows, int S, int Spad) {
+__global__ __launch_bounds__(256) void attn_prologue_kernel(T* __restrict__ vt, int64_t rows, int S, int Spad,
+                                                            float2* __restrict__ rope, int nT, int nH, int nW,
+                                                            int npT, int npH, double log2_theta) {
   const int w = Spad - S;
-  const int64_t n = rows * w;
+  const int64_t eT = (int64_t)nT * npT, eH = (int64_t)nH * npH;
+  const int64_t nrope = eT + eH + (int64_t)nW * npH;
+  const int64_t n = nrope + rows * w;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = i / w;
-    vt[r * Spad + S + (i - r * w)] = from_f32<T>(0.f);
+    if (i < nrope) {
+      int64_t k = i;
+      int np = npT;
+      if (k >= eT) {
+        k -= eT;
+        np = npH;
+        if (k >= eH) k -= eH;
+      }
+      const int pos = (int)(k / np), m = (int)(k % np);
+      const double a = (double)pos * exp2(-(double)(2 * m) / (double)(2 * np) * log2_theta);
+      rope[i] = make_float2((float)cos(a), (float)sin(a));
+    } else {
+      const int64_t t = i - nrope, r = t / w;
+      vt[r * Spad + S + (t - r * w)] = from_f32<T>(0.f);
+    }
   }
 }
 
@@ -242,18 +264,24 @@ hipError_t launch_mod_combine(const float* e0, const float* mb, int B, int dim, 
 }
 
 template <typename T>
-hipError_t launch_vt_tail_zero(T* vt, int64_t rows, int S, int Spad, hipStream_t s) {
+hipError_t launch_attn_prologue(T* vt, int64_t rows, int S, int Spad, float2* rope, int T_, int Hp, int Wp, int hd,
+                                float theta, hipStream_t s) {
+  if (hd < 4 || !(theta > 0.f)) return hipErrorInvalidValue;
   // bf16 V^T permutes keys within 16-key groups, so a padded key of the last group can sit at a
   // position below S: clear from the start of that group (the real keys are written afterwards).
   const int S16 = S & ~15;
-  if (Spad <= S16 || rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(vt_tail_zero_kernel<T>, dim3(grid_for(rows * (Spad - S16))), dim3(256), 0, s, vt, rows, S16,
-                     Spad);
+  const int npT = rope_pairs_time(hd), npH = rope_pairs_space(hd);
+  const int64_t nrope = (int64_t)T_ * npT + (int64_t)(Hp + Wp) * npH;
+  const int64_t ntail = Spad > S16 && rows > 0 ? rows * (Spad - S16) : 0;
+  hipLaunchKernelGGL(attn_prologue_kernel<T>, dim3(grid_for(nrope + ntail)), dim3(256), 0, s, vt, ntail ? rows : 0,
+                     S16, Spad, rope, T_, Hp, Wp, npT, npH, (double)log2f(theta));
   return hipGetLastError();
 }
 
-template hipError_t launch_vt_tail_zero<float>(float*, int64_t, int, int, hipStream_t);
-template hipError_t launch_vt_tail_zero<bf16>(bf16*, int64_t, int, int, hipStream_t);
+template hipError_t launch_attn_prologue<float>(float*, int64_t, int, int, float2*, int, int, int, int, float,
+                                                hipStream_t);
+template hipError_t launch_attn_prologue<bf16>(bf16*, int64_t, int, int, float2*, int, int, int, int, float,
+                                               hipStream_t);
 template hipError_t launch_convert<float>(const float*, float*, int64_t, hipStream_t);
 template hipError_t launch_convert<bf16>(const float*, bf16*, int64_t, hipStream_t);
 template hipError_t launch_transpose_heads<float>(const float*, int64_t, int64_t, int, int, int, int, int, float*,

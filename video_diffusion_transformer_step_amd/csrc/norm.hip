@@ -1,8 +1,9 @@
 // Row-wise normalisation kernels (HBM-bound): LayerNorm + adaLN modulation,
-// affine LayerNorm, the head's modulated LayerNorm, and the Q/K RMSNorm + gain +
-// 3D RoPE pass.  A 64-lane wave owns a few consecutive token rows, one at a time; a
-// row stays in registers between the statistics and the write, and per-channel
-// parameters are kept in registers across the wave's rows.
+// affine LayerNorm, the head's modulated LayerNorm, the block's Q/K RMSNorm factors
+// (finished from the Q/K/V projection epilogue's sums of squares), and the standalone
+// attention's 3D RoPE pass.  For the LayerNorms a 64-lane wave owns a few consecutive
+// token rows, one at a time; a row stays in registers between the statistics and the
+// write, and per-channel parameters are kept in registers across the wave's rows.
 #include "wan_internal.h"
 
 namespace wan {
@@ -250,250 +251,99 @@ template <> __device__ __forceinline__ void store8<float>(float* p, const float 
   reinterpret_cast<float4*>(p)[1] = make_float4(o[4], o[5], o[6], o[7]);
 }
 
-constexpr int QK_MAX8 = 12;  // 8-element chunks per lane: dim <= 12 * 512 = 6144
-constexpr int QK_ROWS = 4;   // token rows per wave
+// ---------------------------------------------------------------------------
+// Q/K rotation for the standalone attention, and the block's Q/K RMSNorm factors.
+// ---------------------------------------------------------------------------
 
-// 3D RoPE ("图解 Wan2.1 I2V" §5.3 ②): head channels split into time / height / width segments of
-// sizes hd - 4*(hd/6), 2*(hd/6), 2*(hd/6); pair (2m, 2m+1) of a segment of width n rotates by
-// pos * theta^(-2m/n), pos being the token's frame / row / column index.  A lane's 8-channel
-// chunks all sit at the same offset within their heads (hd divides 512), so its 4 pairs' frequencies
-// (fixed per lane) and angles (per token) serve every chunk of the row and both q and k.
-struct RopeLane {
-  float freq[4];
-  int axis[4];  // 0 frame, 1 row, 2 column
-};
-
-__device__ __forceinline__ RopeLane rope_lane(int d0, int hd, float log2_theta) {
-  const int q6 = hd / 6;
-  const int dT = hd - 4 * q6, dH = 2 * q6;
-  RopeLane r;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int d = d0 + 2 * p;
-    int m, n;
-    if (d < dT) {
-      m = d >> 1; n = dT; r.axis[p] = 0;
-    } else if (d < dT + dH) {
-      m = (d - dT) >> 1; n = dH; r.axis[p] = 1;
-    } else {
-      m = (d - dT - dH) >> 1; n = dH; r.axis[p] = 2;
-    }
-    r.freq[p] = exp2f(-(float)(2 * m) / (float)n * log2_theta);
-  }
-  return r;
-}
-
-// The lane's pair angles at token position (f, i, j), by the hardware sine / cosine (angles here are
-// at most a few hundred radians, where their error stays near 1e-6).
-__device__ __forceinline__ void rope_angles(const RopeLane& r, int f, int i, int j, float (&cs)[4], float (&sn)[4]) {
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int pos = r.axis[p] == 0 ? f : (r.axis[p] == 1 ? i : j);
-    const float a = (float)pos * r.freq[p];
-    sn[p] = __sinf(a);
-    cs[p] = __cosf(a);
-  }
-}
-
-// One 8-channel chunk: scale by the row's RMS factor r and the gains g, rotate the lane's 4 pairs by
-// their angles, store.
+// 3D RoPE of q and k rows, without norm: one thread per 8-channel chunk of one token row (hd is a
+// multiple of 8, so the chunk's four pairs sit in one head).  In place is allowed (a thread reads its
+// chunks before writing them).
 template <typename T>
-__device__ __forceinline__ void rotate_store8(const float (&v)[8], float r, const float (&g)[8], const float (&cs)[4],
-                                              const float (&sn)[4], T* __restrict__ out) {
-  float o[8];
+__global__ __launch_bounds__(256) void rope_qk_kernel(const T* q_in, const T* k_in, int64_t ld_in, T* q_out, T* k_out,
+                                                      int64_t ld_out, int64_t rows, int S, int Hp, int Wp, int dim,
+                                                      int hd, float log2_theta) {
+  const int nc = dim / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = idx / nc;
+  if (row >= rows) return;
+  const int c0 = (int)(idx - row * nc) * 8, d0 = c0 % hd;
+  float vq[8], vk[8];
+  load8<T>(q_in + row * ld_in + c0, vq);
+  load8<T>(k_in + row * ld_in + c0, vk);
+  const RopePos t = rope_pos((int)(row % S), Hp, Wp);
+  float oq[8], ok[8];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const float a = v[2 * p] * r * g[2 * p], b = v[2 * p + 1] * r * g[2 * p + 1];
-    o[2 * p] = a * cs[p] - b * sn[p];
-    o[2 * p + 1] = a * sn[p] + b * cs[p];
+    float c, s;
+    rope_cs(rope_pair(d0 + 2 * p, hd, log2_theta), t, c, s);
+    oq[2 * p] = vq[2 * p] * c - vq[2 * p + 1] * s;
+    oq[2 * p + 1] = vq[2 * p] * s + vq[2 * p + 1] * c;
+    ok[2 * p] = vk[2 * p] * c - vk[2 * p + 1] * s;
+    ok[2 * p + 1] = vk[2 * p] * s + vk[2 * p + 1] * c;
   }
-  store8<T>(out, o);
+  store8<T>(q_out + row * ld_out + c0, oq);
+  store8<T>(k_out + row * ld_out + c0, ok);
 }
 
-// The q and k rows of one token: RMSNorm over the full row ("图解 Wan2.1 I2V" §5.3 ①, optional), the
-// gains (this lane's in gq / gk), then the rotation by the lane's pair angles.  Both rows are loaded
-// before either reduction so their loads are in flight together.
-template <typename T, int NC8>
-__device__ __forceinline__ void norm_rope_qk(const T* __restrict__ qi, const T* __restrict__ ki, T* __restrict__ qo,
-                                             T* __restrict__ ko, int dim, const float (&gq)[NC8][8],
-                                             const float (&gk)[NC8][8], int do_norm, float eps, const float (&cs)[4],
-                                             const float (&sn)[4], int lane) {
-  float vq[NC8][8], vk[NC8][8];
-#pragma unroll
-  for (int c = 0; c < NC8; ++c) {
-    const int c0 = c * 512 + lane * 8;
-    if (c0 < dim) {
-      load8<T>(qi + c0, vq[c]);
-      load8<T>(ki + c0, vk[c]);
-    }
-  }
-  float sq = 0.f, sk = 0.f;
-#pragma unroll
-  for (int c = 0; c < NC8; ++c) {
-    const int c0 = c * 512 + lane * 8;
-    if (c0 < dim) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sq += vq[c][e] * vq[c][e];
-        sk += vk[c][e] * vk[c][e];
-      }
-    }
-  }
-  float rq = 1.f, rk = 1.f;
-  if (do_norm) {
-    rq = 1.f / sqrtf(wave_sum(sq) / (float)dim + eps);
-    rk = 1.f / sqrtf(wave_sum(sk) / (float)dim + eps);
-  }
-#pragma unroll
-  for (int c = 0; c < NC8; ++c) {
-    const int c0 = c * 512 + lane * 8;
-    if (c0 < dim) {
-      rotate_store8<T>(vq[c], rq, gq[c], cs, sn, qo + c0);
-      rotate_store8<T>(vk[c], rk, gk[c], cs, sn, ko + c0);
-    }
-  }
-}
+// The block's Q/K RMSNorm ("图解 Wan2.1 I2V" §5.3 ①), finished from the Q/K/V projection epilogue's
+// partial sums of squares: ssq[nb * rows + row] is the sum of squares of the row's projected q
+// channels 32 nb .. 32 nb + 31 (nb < dim/32), then of its k channels (the next dim/32 blocks), taken
+// before the gains and the rotation.  With r = (sum / dim + eps)^-1/2 per row, this writes r_q to rq
+// (the attention multiplies its score scale by it) and scales the k row in place by r_k (the epilogue
+// already applied the gains and the rotation, both linear, so r commutes with them).
+// QKR_ROWS rows per wave: their sums with lane = (part, row), then the k rows RB at a time, NC8
+// 8-channel chunks per lane and row (dim <= 512 NC8), all of a batch's loads before its stores.
+constexpr int QKR_ROWS = 8;
 
-// NC8 = 8-channel chunks per lane (dim <= 512 NC8).
-template <typename T, int NC8>
-__global__ __launch_bounds__(256) void qk_norm_rope_kernel(const T* q_in, const T* k_in, int64_t ld_in, T* q_out,
-                                                            T* k_out, int64_t ld_out, int64_t rows, int S, int Hp,
-                                                            int Wp, int dim, int hd, const float* __restrict__ gq,
-                                                            const float* __restrict__ gk, int do_norm, float eps,
-                                                            float log2_theta) {
+template <typename T, int NC8, int RB>
+__global__ __launch_bounds__(256) void qk_rms_kernel(const float* __restrict__ ssq, int64_t rows, int dim, float eps,
+                                                     T* __restrict__ k, int64_t ldk, float* __restrict__ rq) {
+  static_assert(QKR_ROWS % RB == 0, "whole batches of rows");
   const int lane = threadIdx.x & 63;
-  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * QK_ROWS;
-  if (row0 >= rows) return;
-  float gql[NC8][8], gkl[NC8][8];
-#pragma unroll
-  for (int c = 0; c < NC8; ++c) {
-    const int c0 = c * 512 + lane * 8;
-    if (c0 < dim && gq) {
-      load8<float>(gq + c0, gql[c]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) gql[c][e] = 1.f;
-    }
-    if (c0 < dim && gk) {
-      load8<float>(gk + c0, gkl[c]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) gkl[c][e] = 1.f;
-    }
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * QKR_ROWS;
+  if (row0 >= rows) return;  // uniform in the wave
+  const int np = dim / 32, part = lane >> 3, r = lane & 7;
+  const int64_t myrow = row0 + r < rows ? row0 + r : rows - 1;
+  float sq = 0.f, sk = 0.f;
+  for (int nb = part; nb < 2 * np; nb += 8) {
+    const float v = ssq[(int64_t)nb * rows + myrow];
+    if (nb < np)
+      sq += v;
+    else
+      sk += v;
   }
-  const RopeLane rl = rope_lane((lane * 8) % hd, hd, log2_theta);
-  for (int rr = 0; rr < QK_ROWS; ++rr) {
-    const int64_t row = row0 + rr;
-    if (row >= rows) return;
-    const int s = (int)(row % S);
-    const int jj = s % Wp, ii = (s / Wp) % Hp, ff = s / (Wp * Hp);
-    float cs[4], sn[4];
-    rope_angles(rl, ff, ii, jj, cs, sn);
-    norm_rope_qk<T, NC8>(q_in + row * ld_in, k_in + row * ld_in, q_out + row * ld_out, k_out + row * ld_out, dim,
-                         gql, gkl, do_norm, eps, cs, sn, lane);
-  }
-}
-
-// Rows wider than 1536 channels: one workgroup of NT threads per token row (256 up to 4096 channels,
-// 512 up to 6144), QKW_ROWS consecutive rows per workgroup.  Thread t holds the 8-channel chunks at
-// t * 8 + c * 8 NT of q and of k; hd divides 8 NT, so they sit at one offset within their heads and the
-// thread's pair frequencies are fixed.  The next row is loaded before this row's sums, which cross the
-// waves through LDS (slots alternate by row, so one barrier per row suffices).
-constexpr int QKW_ROWS = 8;
-constexpr int QKW_CH = 2;  // 8-channel chunks per thread, of q and of k
-
-template <typename T, int NT>
-__global__ __launch_bounds__(NT) void qk_norm_rope_wide_kernel(const T* q_in, const T* k_in, int64_t ld_in,
-                                                                T* q_out, T* k_out, int64_t ld_out, int64_t rows,
-                                                                int S, int Hp, int Wp, int dim, int hd,
-                                                                const float* __restrict__ gq,
-                                                                const float* __restrict__ gk, int do_norm, float eps,
-                                                                float log2_theta) {
-  constexpr int NWV = NT / 64;
-  __shared__ float part[2][NWV][2];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t row0 = (int64_t)blockIdx.x * QKW_ROWS;
-  float gql[QKW_CH][8], gkl[QKW_CH][8];
+  // the eight parts of row r sit in lanes r, r + 8, ..., r + 56
+  sq += __shfl_xor(sq, 8);
+  sq += __shfl_xor(sq, 16);
+  sq += __shfl_xor(sq, 32);
+  sk += __shfl_xor(sk, 8);
+  sk += __shfl_xor(sk, 16);
+  sk += __shfl_xor(sk, 32);
+  const float fq = 1.f / sqrtf(sq / (float)dim + eps);
+  const float fk = 1.f / sqrtf(sk / (float)dim + eps);
+  if (part == 0 && row0 + r < rows) rq[row0 + r] = fq;
+  const int nr = rows - row0 < QKR_ROWS ? (int)(rows - row0) : QKR_ROWS;
 #pragma unroll
-  for (int c = 0; c < QKW_CH; ++c) {
-    const int c0 = c * NT * 8 + tid * 8;
-    if (c0 < dim && gq) {
-      load8<float>(gq + c0, gql[c]);
-    } else {
+  for (int r0 = 0; r0 < QKR_ROWS; r0 += RB) {
+    float v[RB][NC8][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) gql[c][e] = 1.f;
-    }
-    if (c0 < dim && gk) {
-      load8<float>(gk + c0, gkl[c]);
-    } else {
+    for (int b = 0; b < RB; ++b)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) gkl[c][e] = 1.f;
-    }
-  }
-  const RopeLane rl = rope_lane((tid * 8) % hd, hd, log2_theta);
-  float nq[QKW_CH][8], nk[QKW_CH][8];
-  auto load_row = [&](int64_t row) {
-#pragma unroll
-    for (int c = 0; c < QKW_CH; ++c) {
-      const int c0 = c * NT * 8 + tid * 8;
-      if (c0 < dim) {
-        load8<T>(q_in + row * ld_in + c0, nq[c]);
-        load8<T>(k_in + row * ld_in + c0, nk[c]);
+      for (int c = 0; c < NC8; ++c) {
+        const int c0 = c * 512 + lane * 8;
+        if (r0 + b < nr && c0 < dim) load8<T>(k + (row0 + r0 + b) * ldk + c0, v[b][c]);
       }
-    }
-  };
-  load_row(row0);  // the grid holds no workgroup past the last row
-  for (int rr = 0; rr < QKW_ROWS; ++rr) {
-    const int64_t row = row0 + rr;
-    if (row >= rows) return;  // uniform in the workgroup
-    float vq[QKW_CH][8], vk[QKW_CH][8];
 #pragma unroll
-    for (int c = 0; c < QKW_CH; ++c)
+    for (int b = 0; b < RB; ++b) {
+      const float f = __shfl(fk, r0 + b);  // lane r0 + b (part 0) holds row r0 + b's factor
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        vq[c][e] = nq[c][e];
-        vk[c][e] = nk[c][e];
-      }
-    if (rr + 1 < QKW_ROWS && row + 1 < rows) load_row(row + 1);
-    const int s = (int)(row % S);
-    const int jj = s % Wp, ii = (s / Wp) % Hp, ff = s / (Wp * Hp);
-    float cs[4], sn[4];
-    rope_angles(rl, ff, ii, jj, cs, sn);
-    float rq = 1.f, rk = 1.f;
-    if (do_norm) {  // uniform
-      float sq = 0.f, sk = 0.f;
+      for (int c = 0; c < NC8; ++c) {
+        const int c0 = c * 512 + lane * 8;
+        if (r0 + b < nr && c0 < dim) {
 #pragma unroll
-      for (int c = 0; c < QKW_CH; ++c)
-        if (c * NT * 8 + tid * 8 < dim) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            sq += vq[c][e] * vq[c][e];
-            sk += vk[c][e] * vk[c][e];
-          }
+          for (int e = 0; e < 8; ++e) v[b][c][e] *= f;
+          store8<T>(k + (row0 + r0 + b) * ldk + c0, v[b][c]);
         }
-      sq = wave_sum(sq);
-      sk = wave_sum(sk);
-      const int slot = rr & 1;
-      if (lane == 0) {
-        part[slot][wave][0] = sq;
-        part[slot][wave][1] = sk;
-      }
-      __syncthreads();
-      float tq = 0.f, tk = 0.f;
-#pragma unroll
-      for (int w = 0; w < NWV; ++w) {
-        tq += part[slot][w][0];
-        tk += part[slot][w][1];
-      }
-      rq = 1.f / sqrtf(tq / (float)dim + eps);
-      rk = 1.f / sqrtf(tk / (float)dim + eps);
-    }
-#pragma unroll
-    for (int c = 0; c < QKW_CH; ++c) {
-      const int c0 = c * NT * 8 + tid * 8;
-      if (c0 < dim) {
-        rotate_store8<T>(vq[c], rq, gql[c], cs, sn, q_out + row * ld_out + c0);
-        rotate_store8<T>(vk[c], rk, gkl[c], cs, sn, k_out + row * ld_out + c0);
       }
     }
   }
@@ -523,28 +373,30 @@ hipError_t launch_ln_mod(const float* x, int64_t rows, int dim, int S, int mode,
 }
 
 template <typename T>
-hipError_t launch_qk_norm_rope(const T* q_in, const T* k_in, int64_t ld_in, T* q_out, T* k_out, int64_t ld_out,
-                               int B, int T_, int Hp, int Wp, int heads, int hd, const float* gq, const float* gk,
-                               int do_norm, float eps, float theta, hipStream_t s) {
-  const int dim = heads * hd;
-  if (dim % 8 != 0 || dim > QK_MAX8 * 512 || hd % 8 != 0 || 512 % hd != 0) return hipErrorInvalidValue;
-  const int S = T_ * Hp * Wp;
+hipError_t launch_rope_qk(const T* q_in, const T* k_in, int64_t ld_in, T* q_out, T* k_out, int64_t ld_out, int B,
+                          int T_, int Hp, int Wp, int heads, int hd, float theta, hipStream_t s) {
+  if (hd % 8 != 0 || !(theta > 0.f)) return hipErrorInvalidValue;
+  const int dim = heads * hd, S = T_ * Hp * Wp;
   const int64_t rows = (int64_t)B * S;
+  if (rows <= 0 || dim <= 0) return hipSuccess;
+  const int64_t n = rows * (dim / 8);
+  hipLaunchKernelGGL((rope_qk_kernel<T>), dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, q_in, k_in, ld_in, q_out,
+                     k_out, ld_out, rows, S, Hp, Wp, dim, hd, log2f(theta));
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_qk_rms(const float* ssq, int64_t rows, int dim, float eps, T* k, int64_t ldk, float* rq,
+                         hipStream_t s) {
+  if (dim % 32 != 0 || dim > 12 * 512 || ldk % 8 != 0) return hipErrorInvalidValue;
   if (rows <= 0) return hipSuccess;
-  const float l2t = log2f(theta);
-  if (dim <= 3 * 512) {
-    const dim3 grid((unsigned)ceil_div(rows, 4 * QK_ROWS));
-    hipLaunchKernelGGL((qk_norm_rope_kernel<T, 3>), grid, dim3(256), 0, s, q_in, k_in, ld_in, q_out, k_out, ld_out,
-                       rows, S, Hp, Wp, dim, hd, gq, gk, do_norm, eps, l2t);
-  } else {
-    const dim3 grid((unsigned)ceil_div(rows, (int64_t)QKW_ROWS));
-    if (dim <= QKW_CH * 8 * 256)
-      hipLaunchKernelGGL((qk_norm_rope_wide_kernel<T, 256>), grid, dim3(256), 0, s, q_in, k_in, ld_in, q_out, k_out,
-                         ld_out, rows, S, Hp, Wp, dim, hd, gq, gk, do_norm, eps, l2t);
-    else
-      hipLaunchKernelGGL((qk_norm_rope_wide_kernel<T, 512>), grid, dim3(512), 0, s, q_in, k_in, ld_in, q_out, k_out,
-                         ld_out, rows, S, Hp, Wp, dim, hd, gq, gk, do_norm, eps, l2t);
-  }
+  const dim3 grid((unsigned)ceil_div(rows, 4 * QKR_ROWS));
+  if (dim <= 3 * 512)
+    hipLaunchKernelGGL((qk_rms_kernel<T, 3, 4>), grid, dim3(256), 0, s, ssq, rows, dim, eps, k, ldk, rq);
+  else if (dim <= 6 * 512)
+    hipLaunchKernelGGL((qk_rms_kernel<T, 6, 2>), grid, dim3(256), 0, s, ssq, rows, dim, eps, k, ldk, rq);
+  else
+    hipLaunchKernelGGL((qk_rms_kernel<T, 12, 1>), grid, dim3(256), 0, s, ssq, rows, dim, eps, k, ldk, rq);
   return hipGetLastError();
 }
 
@@ -552,11 +404,11 @@ template hipError_t launch_ln_mod<float>(const float*, int64_t, int, int, int, c
                                          float, float*, hipStream_t);
 template hipError_t launch_ln_mod<bf16>(const float*, int64_t, int, int, int, const float*, const float*, int, int,
                                         float, bf16*, hipStream_t);
-template hipError_t launch_qk_norm_rope<float>(const float*, const float*, int64_t, float*, float*, int64_t, int, int,
-                                               int, int, int, int, const float*, const float*, int, float, float,
-                                               hipStream_t);
-template hipError_t launch_qk_norm_rope<bf16>(const bf16*, const bf16*, int64_t, bf16*, bf16*, int64_t, int, int,
-                                              int, int, int, int, const float*, const float*, int, float, float,
-                                              hipStream_t);
+template hipError_t launch_rope_qk<float>(const float*, const float*, int64_t, float*, float*, int64_t, int, int, int,
+                                          int, int, int, float, hipStream_t);
+template hipError_t launch_rope_qk<bf16>(const bf16*, const bf16*, int64_t, bf16*, bf16*, int64_t, int, int, int,
+                                         int, int, int, float, hipStream_t);
+template hipError_t launch_qk_rms<float>(const float*, int64_t, int, float, float*, int64_t, float*, hipStream_t);
+template hipError_t launch_qk_rms<bf16>(const float*, int64_t, int, float, bf16*, int64_t, float*, hipStream_t);
 
 }  // namespace wan

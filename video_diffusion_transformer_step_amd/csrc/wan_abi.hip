@@ -142,6 +142,9 @@ template <typename T>
 struct BlockWs {
   T *u, *qkv, *vt, *o, *h;
   float* mod;  // [B, 6, dim]: e0 + the block's modulation bias
+  // Q/K RMSNorm: the Q/K/V epilogue's sums of squares [2 dim / 32, B S] and the q rows' factors [B S]
+  float *ssq, *rq;
+  float2* rope;  // 3D RoPE (cos, sin) table of the grid (launch_attn_prologue)
   // quantised self-attention (WAN_FLAG_FP8_ATTN only): codes and scales of q, k, v
   uint8_t *q8, *k8, *v8t;
   float *sq, *sk, *sv;
@@ -160,6 +163,9 @@ size_t block_plan(const wan_block_cfg& c, const wan_grid& g, int B, char* base, 
   w.o = cv.take<T>(BS * dim);
   w.h = cv.take<T>(BS * c.ffn_dim);
   w.mod = cv.take<float>((size_t)B * 6 * dim);
+  w.ssq = cv.take<float>((size_t)(2 * dim / 32) * BS);
+  w.rq = cv.take<float>((size_t)BS);
+  w.rope = cv.take<float2>((size_t)rope_table_entries(g.T, g.Hp, g.Wp, c.head_dim));
   w.q8 = w.k8 = w.v8t = nullptr;
   w.sq = w.sk = w.sv = nullptr;
   if (c.flags & WAN_FLAG_FP8_ATTN) {
@@ -200,30 +206,37 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
   } else {
     float* ystore = attn_mode == WAN_ATTN_CACHE_STORE ? attn_y : nullptr;
     PROF_TRY(WAN_K_LN1, launch_ln_mod<T>(x, BS, dim, S, 0, w.mod, nullptr, 0, 1, c.ln_eps, w.u, st));
-    // q, k -> qkv[:, 0 .. 2 dim) (row stride 2 dim); v -> V^T directly
-    PROF_TRY(WAN_K_VT_TAIL, launch_vt_tail_zero<T>(w.vt, (int64_t)B * dim, S, Spad, st));
+    // q, k -> qkv[:, 0 .. 2 dim) (row stride 2 dim), with the RMSNorm gains and the 3D RoPE applied
+    // ("图解 Wan2.1 I2V" §5.3 ①②) and the rows' sums of squares in ssq; v -> V^T directly.  The
+    // prologue clears V^T's padded keys and writes the rotation table the epilogue reads.
+    PROF_TRY(WAN_K_ATTN_PROLOGUE, launch_attn_prologue<T>(w.vt, (int64_t)B * dim, S, Spad, w.rope, g.T, g.Hp, g.Wp,
+                                                          hd, c.rope_theta, st));
+    const QKNormRope nr{W.gq, W.gk, w.ssq, w.rope, g.T, g.Hp, g.Wp};
     if (f8g) {  // E4M3 products ("Wan 技术深度解析" §5.3): per-token codes of u, then the product
       PROF_TRY(WAN_K_QUANT, launch_quant_rows_e4m3((const bf16*)w.u, dim, BS, dim, w.a8, dim, w.sa, st));
       PROF_TRY(WAN_K_QKV_GEMM, gemm_qkv_e4m3(w.a8, dim, w.sa, (const uint8_t*)Q8->wqkv, dim, Q8->s_wqkv, BS, dim, dim,
-                                             W.bqkv, (bf16*)w.qkv, 2 * dim, (bf16*)w.vt, S, H, hd, Spad, st));
+                                             W.bqkv, (bf16*)w.qkv, 2 * dim, (bf16*)w.vt, S, H, hd, Spad, nr, st));
     } else {
       PROF_TRY(WAN_K_QKV_GEMM, gemm_qkv<T>(w.u, dim, (const T*)W.wqkv, dim, BS, dim, dim, W.bqkv, w.qkv, 2 * dim, w.vt,
-                                           S, H, hd, Spad, st));
+                                           S, H, hd, Spad, nr, st));
     }
-    PROF_TRY(WAN_K_QK_NORM_ROPE, launch_qk_norm_rope<T>(w.qkv, w.qkv + dim, 2 * dim, w.qkv, w.qkv + dim, 2 * dim, B, g.T, g.Hp, g.Wp, H, hd,
-                                   W.gq, W.gk, 1, c.rms_eps, c.rope_theta, st));
+    // the RMS factors: k rows scaled in place, r_q kept for the attention's score scale
+    PROF_TRY(WAN_K_QK_RMS, launch_qk_rms<T>(w.ssq, BS, dim, c.rms_eps, w.qkv + dim, 2 * dim, w.rq, st));
     if constexpr (sizeof(T) == 2) {
       if (c.flags & WAN_FLAG_FP8_ATTN) {  // quantised self-attention ("Wan 技术深度解析" §5.3)
+        // q codes of the rows before r_q, which the attention applies with the codes' scales
         PROF_TRY(WAN_K_QUANT, launch_quant_q(w.qkv, 2 * dim, B, S, H, hd, (int8_t*)w.q8, w.sq, st));
         PROF_TRY(WAN_K_QUANT, launch_quant_k(w.qkv + dim, 2 * dim, B, S, H, hd, (int8_t*)w.k8, w.sk, st));
         PROF_TRY(WAN_K_QUANT, launch_quant_vt(w.vt, (int64_t)B * dim, Spad, (int)round_up(S, 128), w.v8t, w.sv, st));
-        PROF_TRY(WAN_K_SELF_ATTN, launch_attention_q8(w.q8, w.sq, w.k8, w.sk, w.v8t, w.sv, B, S, S, H, hd, w.o, nullptr, st));
+        PROF_TRY(WAN_K_SELF_ATTN, launch_attention_q8(w.q8, w.sq, w.k8, w.sk, w.v8t, w.sv, B, S, S, H, hd, w.o, nullptr,
+                                                      st, w.rq));
       }
     }
     if (!(c.flags & WAN_FLAG_FP8_ATTN)) {
       KVStream self{w.qkv + dim, (int64_t)S * 2 * dim, 2 * dim, w.vt, S, Spad};
       PROF_TRY(WAN_K_SELF_ATTN, launch_attention<T>(w.qkv, (int64_t)S * 2 * dim, 2 * dim, self, B, S, H, hd,
-                                                    scale, w.o, (int64_t)S * dim, dim, 0, st));
+                                                    scale, w.o, (int64_t)S * dim, dim, 0, st, nullptr, KeySplit{},
+                                                    false, w.rq));
     }
     if (f8g) {
       PROF_TRY(WAN_K_QUANT, launch_quant_rows_e4m3((const bf16*)w.o, dim, BS, dim, w.a8, dim, w.sa, st));
@@ -659,7 +672,7 @@ static int attention_t(const T* q, const T* k, const T* v, const wan_grid& g, in
   T* qr = cv.take<T>((size_t)B * S * dim);
   T* kr = cv.take<T>((size_t)B * S * dim);
   T* vt = cv.take<T>((size_t)B * dim * Spad);
-  HIP_TRY(launch_qk_norm_rope<T>(q, k, dim, qr, kr, dim, B, g.T, g.Hp, g.Wp, H, hd, nullptr, nullptr, 0, 0.f, theta, st));
+  HIP_TRY(launch_rope_qk<T>(q, k, dim, qr, kr, dim, B, g.T, g.Hp, g.Wp, H, hd, theta, st));
   HIP_TRY(launch_transpose_heads<T>(v, dim, 0, B, S, H, hd, Spad, vt, st));
   KVStream s0{kr, (int64_t)S * dim, dim, vt, S, Spad};
   HIP_TRY(launch_attention<T>(qr, (int64_t)S * dim, dim, s0, B, S, H, hd, 1.f / sqrtf((float)hd), o,

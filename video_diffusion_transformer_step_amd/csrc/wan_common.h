@@ -118,6 +118,49 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
+// ---------------------------------------------------------------------------
+// 3D RoPE ("图解 Wan2.1 I2V" §5.3 ②), shared by the Q/K/V projection epilogue and the standalone
+// rotation pass.  A head's channels split into time / height / width segments of sizes
+// hd - 4*(hd/6), 2*(hd/6), 2*(hd/6); pair (2m, 2m+1) of a segment of width n rotates by
+// pos * theta^(-2m/n), pos being the token's frame / row / column index.
+// ---------------------------------------------------------------------------
+// Pairs per head in the time segment, and in each of the two spatial segments.
+__host__ __device__ __forceinline__ int rope_pairs_time(int hd) { return (hd - 4 * (hd / 6)) / 2; }
+__host__ __device__ __forceinline__ int rope_pairs_space(int hd) { return hd / 6; }
+struct RopePair {
+  float freq;
+  int axis;  // 0 frame, 1 row, 2 column
+};
+// The pair starting at head channel d (even).
+__device__ __forceinline__ RopePair rope_pair(int d, int hd, float log2_theta) {
+  const int q6 = hd / 6;
+  const int dT = hd - 4 * q6, dH = 2 * q6;
+  int m, n, axis;
+  if (d < dT) {
+    m = d >> 1; n = dT; axis = 0;
+  } else if (d < dT + dH) {
+    m = (d - dT) >> 1; n = dH; axis = 1;
+  } else {
+    m = (d - dT - dH) >> 1; n = dH; axis = 2;
+  }
+  return RopePair{exp2f(-(float)(2 * m) / (float)n * log2_theta), axis};
+}
+// (frame, row, column) of position s in a frames x Hp x Wp token grid (row-major).
+struct RopePos {
+  int f, i, j;
+};
+__device__ __forceinline__ RopePos rope_pos(int s, int Hp, int Wp) {
+  return RopePos{s / (Wp * Hp), (s / Wp) % Hp, s % Wp};
+}
+// The pair's cosine and sine at a token position, by the hardware sine / cosine (angles here are at
+// most a few hundred radians, where their error stays near 1e-6).
+__device__ __forceinline__ void rope_cs(const RopePair& p, const RopePos& t, float& c, float& s) {
+  const int pos = p.axis == 0 ? t.f : (p.axis == 1 ? t.i : t.j);
+  const float a = (float)pos * p.freq;
+  s = __sinf(a);
+  c = __cosf(a);
+}
+
 __host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ __forceinline__ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 

@@ -36,11 +36,18 @@ hipError_t launch_gated_add(float* x, const float* y, const float* mod, int chun
 // (e0 [B, 6, dim] from the shared timestep MLP, mb [6, dim] the block's own bias).
 hipError_t launch_mod_combine(const float* e0, const float* mb, int B, int dim, float* mod, hipStream_t s);
 
-// Zero V^T[r, S16 .. Spad) for rows r < rows (row stride Spad), S16 = S rounded down to 16: every position
-// that can hold a padded key of the last tile (bf16 V^T permutes keys within 16-key groups).  Runs before
-// the keys < S are written.
+// The block's launch before its Q/K/V product, two jobs in one grid:
+//  * zero V^T[r, S16 .. Spad) for rows r < rows (row stride Spad), S16 = S rounded down to 16: every
+//    position that can hold a padded key of the last tile (bf16 V^T permutes keys within 16-key
+//    groups); runs before the keys < S are written;
+//  * write the 3D RoPE table of a T_ x Hp x Wp grid and head dim hd (rope_table_entries float2 of
+//    (cos, sin); layout at QKNormRope) for the product's epilogue.
 template <typename T>
-hipError_t launch_vt_tail_zero(T* vt, int64_t rows, int S, int Spad, hipStream_t s);
+hipError_t launch_attn_prologue(T* vt, int64_t rows, int S, int Spad, float2* rope, int T_, int Hp, int Wp, int hd,
+                                float theta, hipStream_t s);
+inline int64_t rope_table_entries(int T_, int Hp, int Wp, int hd) {
+  return (int64_t)T_ * rope_pairs_time(hd) + (int64_t)(Hp + Wp) * rope_pairs_space(hd);
+}
 
 // ---- norms (norm.hip) -------------------------------------------------------
 // Row-wise LayerNorm of fp32 x [rows, dim] followed by one of:
@@ -52,11 +59,17 @@ hipError_t launch_vt_tail_zero(T* vt, int64_t rows, int S, int Spad, hipStream_t
 template <typename T>
 hipError_t launch_ln_mod(const float* x, int64_t rows, int dim, int S, int mode, const float* p0, const float* p1,
                          int c_shift, int c_scale, float eps, T* u, hipStream_t s);
-// In-place RMSNorm (optional) + gain + 3D RoPE on the q and k column blocks of token rows.
+// 3D RoPE (no norm) on the q and k rows of B * T_ * Hp * Wp tokens (row strides ld_in / ld_out; in place
+// allowed); hd % 8 == 0.
 template <typename T>
-hipError_t launch_qk_norm_rope(const T* q_in, const T* k_in, int64_t ld_in, T* q_out, T* k_out, int64_t ld_out,
-                               int B, int T_, int Hp, int Wp, int heads, int hd, const float* gq,
-                               const float* gk, int do_norm, float eps, float theta, hipStream_t s);
+hipError_t launch_rope_qk(const T* q_in, const T* k_in, int64_t ld_in, T* q_out, T* k_out, int64_t ld_out, int B,
+                          int T_, int Hp, int Wp, int heads, int hd, float theta, hipStream_t s);
+// The block's Q/K RMSNorm factors from the Q/K/V epilogue's partial sums of squares ssq [2 dim / 32, rows]
+// (see QKNormRope): rq[row] = (sum_q / dim + eps)^-1/2, and the k rows (row stride ldk) scaled in place
+// by (sum_k / dim + eps)^-1/2.  dim % 32 == 0, dim <= 6144.
+template <typename T>
+hipError_t launch_qk_rms(const float* ssq, int64_t rows, int dim, float eps, T* k, int64_t ldk, float* rq,
+                         hipStream_t s);
 
 // ---- GEMM (gemm.hip) --------------------------------------------------------
 // C[m, n] = sum_k A[m, k] * W[n, k]   (A [M, K] row-major, W [N, K] row-major)
@@ -71,10 +84,26 @@ hipError_t gemm_store(const T* A, int64_t lda, const T* W, int64_t ldw, int M, i
 // Q/K/V projection (N = 3 dim): q, k columns to qk[m, 0 .. 2 dim) (row stride ldo), v columns to
 // V^T [B, H, hd, Spad] (keys permuted within 16-key groups for bf16; see launch_transpose_heads);
 // m = b * S + pos.  Only keys pos < S are written: the positions of keys S .. Spad - 1 are left as they
-// were (launch_vt_tail_zero clears them first).
+// were (launch_attn_prologue clears them first).
+// The q and k columns leave the epilogue as RoPE(g * (C + bias)) with the RMSNorm gains g (gq for q,
+// gk for k) and the 3D rotation of token m's position (frame, row, column) in the T x Hp x Wp grid of
+// its batch row (m % S); the per-row RMS factor comes later (launch_qk_rms): the epilogue writes the
+// sums of squares of C + bias over each 32-column block, ssq[(n / 32) * M + m] for n < 2 dim.
+// The rotation reads (cos, sin) from rope (launch_attn_prologue writes it): with npT =
+// rope_pairs_time(hd), npH = rope_pairs_space(hd), pair p of a head at frame f, row i, column j is
+// entry f npT + p (p < npT), T npT + i npH + (p - npT) (p < npT + npH), else
+// T npT + Hp npH + j npH + (p - npT - npH).  dim % 32 == 0, hd a power of 2 (>= 4).
+struct QKNormRope {
+  const float* gq;
+  const float* gk;
+  float* ssq;  // [2 dim / 32, M]
+  const float2* rope;
+  int T, Hp, Wp;
+};
 template <typename T>
 hipError_t gemm_qkv(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int dim, int K, const float* bias,
-                    T* qk, int64_t ldo, T* vt, int S, int H, int hd, int Spad, hipStream_t s);
+                    T* qk, int64_t ldo, T* vt, int S, int H, int hd, int Spad, const QKNormRope& nr,
+                    hipStream_t s);
 template <typename T>
 hipError_t gemm_residual(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const float* bias,
                          const float* gate, int chunk, int S, float* x, int64_t ldx, hipStream_t s,
@@ -90,7 +119,7 @@ hipError_t gemm_e4m3_residual(const uint8_t* A, int64_t lda, const float* a_scal
                               int chunk, int S, float* x, int64_t ldx, hipStream_t s, float* ystore = nullptr);
 hipError_t gemm_qkv_e4m3(const uint8_t* A, int64_t lda, const float* a_scales, const uint8_t* W, int64_t ldw,
                          const float* w_scale, int M, int dim, int K, const float* bias, bf16* qk, int64_t ldo, bf16* vt,
-                         int S, int H, int hd, int Spad, hipStream_t s);
+                         int S, int H, int hd, int Spad, const QKNormRope& nr, hipStream_t s);
 // y[b, n] = out_act(sum_k W[n, k] * in_act(x[b, k]) + bias[n]) for b < B (fp32 x, y).
 template <typename T>
 hipError_t gemv(const T* W, int N, int K, const float* x, int B, const float* bias, int in_act, int out_act,
@@ -124,18 +153,21 @@ void attention_tile(int kind, int& rows, int& per_cu);
 // kind: 0 self-attention, 1 cross-attention (separate kernel symbols).  lse (NULL = not written):
 // [B, H, S] float32, the natural log of each query row's softmax normaliser.  accumulate: the result is
 // added to what o holds (a second key/value stream after a first launch; not with key splits, and not
-// for bf16 kind 0, which runs the ping-pong kernel).
+// for bf16 kind 0, which runs the ping-pong kernel).  qscale (NULL = 1): [B, S] float32, a per-query
+// factor of the score scale (the block's RMSNorm factor r_q of a query whose row is not yet normalised).
 template <typename T>
 hipError_t launch_attention(const T* q, int64_t q_bs, int64_t q_ss, KVStream kv, int B, int S, int H, int hd,
                             float scale, T* o, int64_t o_bs, int64_t o_ss, int kind, hipStream_t s,
-                            float* lse = nullptr, KeySplit ks = KeySplit{}, bool accumulate = false);
+                            float* lse = nullptr, KeySplit ks = KeySplit{}, bool accumulate = false,
+                            const float* qscale = nullptr);
 
 // Quantised attention (INT8 Q.K, FP8 P.V): q8 [B, S, H, hd] INT8 codes with sq [B, H, S]; k8 [B, L, H, hd]
 // INT8 codes with sk [B, H, ceil(L / 64)]; v8t [B, H, hd, round_up(L, 128)] E4M3 codes (keys in P.V
-// order, zero past L) with sv [B, H, hd]; o [B, S, H, hd] bf16; lse [B, H, S] or NULL.
+// order, zero past L) with sv [B, H, hd]; o [B, S, H, hd] bf16; lse [B, H, S] or NULL; qscale [B, S] or
+// NULL, as for launch_attention.
 hipError_t launch_attention_q8(const uint8_t* q8, const float* sq, const uint8_t* k8, const float* sk,
                                const uint8_t* v8t, const float* sv, int B, int S, int L, int H, int hd, bf16* o,
-                               float* lse, hipStream_t s);
+                               float* lse, hipStream_t s, const float* qscale = nullptr);
 
 // ---- quantisers (quant.hip) --------------------------------------------------
 // x rows [B*S, *] bf16 with head h at columns h*hd (row stride ld elements).
