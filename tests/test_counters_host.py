@@ -86,3 +86,33 @@ def test_labels_calibration_and_markdown(tmp_path):
     assert abs(rec["kernels"]["self_attn"]["mean_ns"] - 660.0) < 1e-9
     text = md.read_text()
     assert "| self_attn |" in text and "| ffn2_gemm |" in text and "| euler |" in text and "rocprofv3 ..." in text
+
+
+def test_by_name_fractions_and_trace(tmp_path):
+    """--by-name: per-fragment means over dispatches, SQ fractions of SQ_WAVE_CYCLES, MFMA busy per GUI
+    cycle, trace durations; dispatches of other kernels are ignored."""
+    fields = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    seq = [("attention_q8_kernel<128>", {"SQ_WAVE_CYCLES": 100.0, "SQ_WAIT_ANY": 40.0, "GRBM_GUI_ACTIVE": 10.0,
+                                         "SQ_VALU_MFMA_BUSY_CYCLES": 300.0}),
+           ("ln_mod_kernel", {"SQ_WAVE_CYCLES": 7.0}),
+           ("attention_q8_kernel<128>", {"SQ_WAVE_CYCLES": 300.0, "SQ_WAIT_ANY": 200.0, "GRBM_GUI_ACTIVE": 30.0,
+                                         "SQ_VALU_MFMA_BUSY_CYCLES": 500.0}),
+           ("attention_pp_kernel<bf16>", {"SQ_WAVE_CYCLES": 50.0, "SQ_ACTIVE_INST_VALU": 10.0})]
+    _write(tmp_path / "p", _pmc_rows(seq), fields, "p_counter_collection.csv")
+    trace = [{"Dispatch_Id": i + 1, "Kernel_Name": n, "Start_Timestamp": 0, "End_Timestamp": 1000 * (i + 1)}
+             for i, (n, _) in enumerate(seq)]
+    _write(tmp_path / "kt", trace, ["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"],
+           "k_kernel_trace.csv")
+    res = C.by_name([str(tmp_path / "p")], ["attention_q8_kernel", "attention_pp_kernel"], str(tmp_path / "kt"))
+    q8 = res["attention_q8_kernel"]
+    assert q8["n"] == 2 and abs(q8["mean"]["SQ_WAVE_CYCLES"] - 200.0) < 1e-12
+    assert abs(q8["wave_fraction"]["SQ_WAIT_ANY"] - 120.0 / 200.0) < 1e-12
+    assert abs(q8["mfma_busy_per_gui"] - 400.0 / 20.0) < 1e-12
+    assert abs(q8["mean_ns"] - (1000 + 3000) / 2) < 1e-9 and q8["trace_n"] == 2
+    pp = res["attention_pp_kernel"]
+    assert abs(pp["wave_fraction"]["SQ_ACTIVE_INST_VALU"] - 0.2) < 1e-12 and "mfma_busy_per_gui" not in pp
+    md = tmp_path / "k.md"
+    assert C.main([str(tmp_path / "p"), "--by-name", "attention_q8_kernel,attention_pp_kernel", "--out",
+                   str(tmp_path / "k.json"), "--md", str(md), "--command", "rocprofv3 ..."]) == 0
+    text = md.read_text()
+    assert "| SQ_WAIT_ANY / SQ_WAVE_CYCLES | 0.600 |" in text and "rocprofv3 ..." in text

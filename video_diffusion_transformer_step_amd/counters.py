@@ -5,8 +5,9 @@ Measurement tooling, not part of the compute path.  Input: the output folders of
 `rocprofv3 --pmc ... --output-format csv -d DIR -- python3 bench.py ...` runs (one counter set per
 run) of the same workload.  Each dispatch is labelled by its kernel name and its position inside a
 block (a block starts with the modulation-combine launch, and the block's launches come in a fixed
-order: LN1, V^T tail, Q/K/V product, QK norm + RoPE, self-attention, O product, LN3, cross-q product,
-cross-attention, cross-O product, LN2, FFN1, FFN2).  Counter values are averaged per label.
+order: LN1, attention prologue, Q/K/V product, QK RMS finish, self-attention, O product, LN3,
+cross-q product, cross-attention, cross-O product, LN2, FFN1, FFN2).  Counter values are averaged per
+label.
 
 Derived figures:
   * HBM bytes per launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by what the same counter
@@ -21,8 +22,12 @@ With --trace DIR (a `rocprofv3 --kernel-trace --output-format csv` folder of the
 launches are labelled the same way and their mean durations added; with --md FILE a table of the
 figures is written as markdown.
 
+With --by-name FRAG[,FRAG...] the dispatches are grouped by kernel-name fragment instead (any workload):
+per fragment, the mean of every counter over its dispatches, the SQ activity and wait counters as
+fractions of SQ_WAVE_CYCLES, MFMA busy per GRBM_GUI_ACTIVE cycle, and the kernel-trace mean duration.
+
 Usage: python -m video_diffusion_transformer_step_amd.counters DIR [DIR ...] --out JSON [--trace DIR]
-       [--md FILE] [--command TEXT]
+       [--md FILE] [--command TEXT] [--by-name FRAG[,FRAG...]]
 """
 from __future__ import annotations
 
@@ -255,6 +260,72 @@ def _sha(src):
     return hashlib.sha256(open(p, "rb").read()).hexdigest()
 
 
+# SQ counters reported as fractions of a wave's lifetime (SQ_WAVE_CYCLES) in --by-name mode
+WAVE_FRACTIONS = ["SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_SCA",
+                  "SQ_ACTIVE_INST_MISC", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS"]
+
+
+def by_name(folders, fragments, trace=None):
+    """{fragment: {"n", "mean": {counter: value}, "wave_fraction": {...}, "mfma_busy_per_gui", "mean_ns"}}:
+    every dispatch whose kernel name contains the fragment, averaged per counter over the folders."""
+    acc = {f: {} for f in fragments}
+    for folder in folders:
+        for d in read_dispatches(folder).values():
+            frag = next((f for f in fragments if f in d["name"]), None)
+            if frag is None:
+                continue
+            for c, v in d["counters"].items():
+                acc[frag].setdefault(c, []).append(v)
+    res = {}
+    for frag, cnt in acc.items():
+        mean = {c: sum(v) / len(v) for c, v in cnt.items()}
+        e = {"n": min((len(v) for v in cnt.values()), default=0), "mean": mean}
+        wc = mean.get("SQ_WAVE_CYCLES")
+        if wc:
+            e["wave_fraction"] = {c: mean[c] / wc for c in WAVE_FRACTIONS if c in mean}
+        gui = mean.get("GRBM_GUI_ACTIVE")
+        if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+            e["mfma_busy_per_gui"] = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / gui
+        res[frag] = e
+    if trace:
+        durs = {}
+        for d in read_trace(trace).values():
+            frag = next((f for f in fragments if f in d["name"]), None)
+            if frag is not None:
+                durs.setdefault(frag, []).append(d["ns"])
+        for frag, v in durs.items():
+            res[frag]["mean_ns"] = sum(v) / len(v)
+            res[frag]["trace_n"] = len(v)
+    return res
+
+
+def by_name_markdown(res, command=None):
+    lines = ["# Hardware counters per kernel", ""]
+    if command:
+        lines += ["Command:", "", "```", command, "```", ""]
+    frags = list(res)
+    lines += ["| counter | " + " | ".join(f"`{f}`" for f in frags) + " |",
+              "|---|" + "---:|" * len(frags)]
+    lines.append("| dispatches per counter / in the trace | " +
+                 " | ".join(f"{res[f]['n']} / {res[f].get('trace_n', 0)}" for f in frags) + " |")
+    lines.append("| mean duration, trace (ms) | " +
+                 " | ".join(f"{res[f]['mean_ns'] / 1e6:.4f}" if "mean_ns" in res[f] else "—" for f in frags) + " |")
+    counters = sorted({c for f in frags for c in res[f]["mean"]})
+    for c in counters:
+        lines.append(f"| {c} | " + " | ".join(f"{res[f]['mean'][c]:.4e}" if c in res[f]["mean"] else "—"
+                                              for f in frags) + " |")
+    for c in WAVE_FRACTIONS:
+        if any(c in res[f].get("wave_fraction", {}) for f in frags):
+            lines.append(f"| {c} / SQ_WAVE_CYCLES | " +
+                         " | ".join(f"{res[f]['wave_fraction'][c]:.3f}" if c in res[f].get("wave_fraction", {})
+                                    else "—" for f in frags) + " |")
+    if any("mfma_busy_per_gui" in res[f] for f in frags):
+        lines.append("| SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE | " +
+                     " | ".join(f"{res[f]['mfma_busy_per_gui']:.1f}" if "mfma_busy_per_gui" in res[f] else "—"
+                                for f in frags) + " |")
+    return "\n".join(lines) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("folders", nargs="+")
@@ -263,7 +334,17 @@ def main(argv=None):
     ap.add_argument("--trace", help="kernel-trace folder of the same workload (mean durations per launch)")
     ap.add_argument("--md", help="also write a markdown table here")
     ap.add_argument("--command", help="the profiling command, quoted in the markdown")
+    ap.add_argument("--by-name", help="comma-separated kernel-name fragments: group dispatches by kernel")
     a = ap.parse_args(argv)
+    if a.by_name:
+        res = by_name(a.folders, [f for f in a.by_name.split(",") if f], a.trace)
+        if a.md:
+            with open(a.md, "w") as fh:
+                fh.write(by_name_markdown(res, a.command))
+        with open(a.out, "w") as fh:
+            json.dump(res, fh, indent=1, sort_keys=True)
+        print(json.dumps(res, indent=1, sort_keys=True))
+        return 0
     res = derive(reduce(a.folders), a.copy_bytes)
     if a.trace:
         for label, ns in trace_means(a.trace).items():
