@@ -152,6 +152,24 @@ def test_branches_small_fp8():
                     fp8_gemm=True, label=" fp8 attention + e4m3 products")
 
 
+@pytest.mark.timeout(600)
+def test_branches_hd64_async_copy_products():
+    """Head dim 64 on the large-row product path: B = 2 rows of 4096 tokens (4 frames of 32 x 32
+    patches), dim 640 = 10 heads of 64.  The Q/K/V product then runs the asynchronous-copy kernel, whose
+    waves' 128 columns span two heads, so the epilogue's gains, RoPE and row sums of squares cross a
+    head boundary inside a wave tile, and batch row 1 exercises the position decode m % S.  Sampled
+    rows of every branch at the bf16 bar."""
+    require_gpu()
+    c = wi.get_config("tiny").replace(dtype="bf16", T=4, H=64, W=64, B=2, dim=640, heads=10, head_dim=64,
+                                      ffn_dim=1280, text_len=64)
+    case(f"branches hd64 async-copy products {c.name} S={c.S} B={c.B}")
+    rows = wi.sample_rows(c, 24, seed=11)
+    x, e0, t_emb, i_emb, bw = _inputs(c, seed=11)
+    ref = _branch_refs(c, x, e0, bw, t_emb, i_emb, rows)
+    t = TOL["bf16"]
+    _check_branches(c, x, e0, bw, t_emb, i_emb, rows, ref, t, t, t)
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["t2v-1.3b", "ti2v-5b", pytest.param("i2v-14b", marks=pytest.mark.slow)])
 def test_branches_full_size(name):
