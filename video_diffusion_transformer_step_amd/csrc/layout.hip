@@ -3,6 +3,8 @@
 // per-head transpose of V used by the attention kernels.
 #include "wan_internal.h"
 
+#include <cmath>
+
 namespace wan {
 
 namespace {
@@ -274,7 +276,7 @@ hipError_t launch_attn_prologue(T* vt, int64_t rows, int S, int Spad, float2* ro
   const int64_t nrope = (int64_t)T_ * npT + (int64_t)(Hp + Wp) * npH;
   const int64_t ntail = Spad > S16 && rows > 0 ? rows * (Spad - S16) : 0;
   hipLaunchKernelGGL(attn_prologue_kernel<T>, dim3(grid_for(nrope + ntail)), dim3(256), 0, s, vt, ntail ? rows : 0,
-                     S16, Spad, rope, T_, Hp, Wp, npT, npH, (double)log2f(theta));
+                     S16, Spad, rope, T_, Hp, Wp, npT, npH, std::log2((double)theta));
   return hipGetLastError();
 }
 
