@@ -170,6 +170,32 @@ def test_branches_hd64_async_copy_products():
     _check_branches(c, x, e0, bw, t_emb, i_emb, rows, ref, t, t, t)
 
 
+DEGENERATE = [
+    # one row of patches (Hp = 1: every height-segment rotation is the identity), 5 frames, two rows
+    ("hp1", {"dtype": "bf16", "T": 5, "H": 2, "W": 40, "B": 2, "dim": 256, "heads": 2, "head_dim": 128,
+             "ffn_dim": 512, "text_len": 32}, None),
+    # a single frame (T = 1: every time-segment rotation is the identity) large enough for the
+    # asynchronous-copy products: B = 2 rows of 64 x 32 patches = 4096 product rows
+    ("image-async-copy", {"dtype": "bf16", "T": 1, "H": 128, "W": 64, "B": 2, "dim": 512, "heads": 4,
+                          "head_dim": 128, "ffn_dim": 1024, "text_len": 64}, 24),
+]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("label,over,n_rows", DEGENERATE, ids=[d[0] for d in DEGENERATE])
+def test_branches_degenerate_grids(label, over, n_rows):
+    """Grids where an axis of the 3D RoPE has a single position, through the Q/K/V epilogue's rotation
+    table: every branch at the bf16 bar (all rows, or sampled rows for the larger grid)."""
+    require_gpu()
+    c = wi.get_config("tiny").replace(**over)
+    case(f"branches degenerate grid {label} {c.grid} S={c.S} B={c.B}")
+    rows = None if n_rows is None else wi.sample_rows(c, n_rows, seed=12)
+    x, e0, t_emb, i_emb, bw = _inputs(c, seed=12)
+    ref = _branch_refs(c, x, e0, bw, t_emb, i_emb, rows)
+    t = TOL["bf16"]
+    _check_branches(c, x, e0, bw, t_emb, i_emb, rows, ref, t, t, t)
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["t2v-1.3b", "ti2v-5b", pytest.param("i2v-14b", marks=pytest.mark.slow)])
 def test_branches_full_size(name):
