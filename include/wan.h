@@ -211,7 +211,9 @@ int wan_cross_kv_fwd(const wan_block_cfg* cfg, const wan_cross_kv_weights* w, co
  *   x += gate2 * FFN(LN(x)(1 + scale2) + shift2),  FFN = Linear -> GELU -> Linear
  * e0 [B, 6, dim] float32 from wan_time_embed; kv from wan_cross_kv_fwd.  LN has no affine (except the
  * cross-attention pre-norm), eps = cfg->ln_eps; attention scale 1/sqrt(head_dim).
- * Workspace: wan_dit_block_workspace_bytes() (about B*S*(5*dim + ffn_dim) dtype elements). */
+ * Workspace: wan_dit_block_workspace_bytes() (about B*S*(5*dim + ffn_dim) dtype elements, plus
+ * B*S*(dim/16 + 1) float32 of Q/K sums of squares and query scales, 6*B*dim float32 of
+ * modulation and the RoPE table's (T + Hp + Wp) * head_dim/2 or fewer float2). */
 size_t wan_dit_block_workspace_bytes(const wan_block_cfg* cfg, wan_grid grid, int32_t B);
 int wan_dit_block_fwd(const wan_block_cfg* cfg, const wan_block_weights* w, wan_grid grid, int32_t B, float* x,
                       const float* e0, const wan_cross_kv* kv, void* ws, size_t ws_bytes, wan_stream_t stream);
