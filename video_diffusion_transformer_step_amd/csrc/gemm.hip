@@ -10,7 +10,10 @@
 //  * gemm_lds_kernel (bf16, K a multiple of 128; the block's large products):
 //    256 x 256 tiles, 8 waves of 64 x 128, K steps of 32 copied global -> LDS by
 //    asynchronous direct-to-LDS buffer loads (16 bytes a lane) into a ring of four
-//    stages, three steps ahead of their use (no staging registers);
+//    stages, three steps ahead of their use (no staging registers); rows past the
+//    operands' ends are zeros from the buffers' range check; the plain-store products
+//    run one workgroup per CU walking several tiles, the next tile's first stages
+//    copied during the current tile's last steps;
 //  * gemm_nt_kernel (everything else): K steps of 128 bytes staged through
 //    double-buffered, row-padded LDS with register prefetch of the next step;
 //    loads are predicate-free (out-of-range rows clamped, a final partial K step
@@ -32,6 +35,7 @@
 //    the RMSNorm, plus the transposed V layout (§5.3).
 #include "wan_internal.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace wan {
@@ -458,20 +462,28 @@ struct LdsGemmCfg {
 // The copies go through buffer resources (the MUBUF form of the direct-to-LDS load: lane i writes its
 // 16 bytes at lds + 16 i).  The compiler counts them as plain vector-memory loads, so the fragment
 // reads of a step wait only for their own results; with the FLAT form in flight every LDS read would
-// wait for all outstanding LDS accesses.  Each operand tile has one wave-uniform base (its first row),
-// a 32-bit per-lane byte offset (row clamped to the last valid one, permuted chunk) and the K position
-// as the scalar offset.
-__device__ __forceinline__ void buffer_copy16(const void* base, uint32_t voff, uint32_t soff, char* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1,
-                                                                             0x00020000),
-                                           (lds_void*)lds, 16, voff, soff, 0, 0);
+// wait for all outstanding LDS accesses.  Each operand tile has one wave-uniform base (its first row)
+// and a record count (the bytes from there to the end of the operand); each lane a 32-bit byte offset
+// (row, permuted chunk) that is the same for every tile; the K position is the scalar offset.  Rows
+// past the operand's last one start at or beyond the record count, so the buffer's range check turns
+// their copies into zeros without a memory access; such rows only feed outputs that are not stored.
+__device__ __forceinline__ void buffer_copy16(const void* base, uint32_t records, uint32_t voff, uint32_t soff,
+                                              char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)records, 0x00020000),
+      (lds_void*)lds, 16, voff, soff, 0, 0);
 }
+
+// Where one output tile's operands start: A's row m0 and W's row n0, with their record counts.
+struct LdsTileSrc {
+  const bf16* ba;
+  const bf16* bb;
+  uint32_t na, nb;
+};
 
 template <int BM, int BN, int BK, int NW, bool M16 = false>
 struct LdsCopyPlan {
   using C = LdsGemmCfg<BM, BN, BK, NW, M16>;
-  const bf16* ba;  // wave-uniform tile bases
-  const bf16* bb;
   uint32_t oa[C::LA];
   uint32_t ob[C::LB];
   __device__ static __forceinline__ const bf16* uniform(const bf16* p) {
@@ -479,30 +491,38 @@ struct LdsCopyPlan {
     return (const bf16*)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
                          (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a));
   }
-  __device__ __forceinline__ LdsCopyPlan(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int m0, int n0,
-                                         int M, int N) {
+  // Records of the rows from r0 to the end of a [rows, ld] operand, capped at 2^32 - 1 (a tile's own
+  // offsets stay below 2^31).
+  __device__ static __forceinline__ uint32_t records(int rows, int r0, int64_t ld) {
+    const int64_t b = (int64_t)(rows - r0) * ld * 2;
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b < 0xFFFFFFFFll ? b : 0xFFFFFFFFll));
+  }
+  __device__ __forceinline__ LdsCopyPlan(int64_t lda, int64_t ldw) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    ba = uniform(A + (int64_t)m0 * lda);
-    bb = uniform(W + (int64_t)n0 * ldw);
 #pragma unroll
     for (int i = 0; i < C::LA; ++i) {
       const int p = (i * NW + wave) * 64 + lane, r = p / C::CH, s = p % C::CH;
       const int c = s ^ C::swz(r);
-      oa[i] = (uint32_t)(((int64_t)(min(m0 + r, M - 1) - m0) * lda + c * 8) * 2);
+      oa[i] = (uint32_t)(((int64_t)r * lda + c * 8) * 2);
     }
 #pragma unroll
     for (int i = 0; i < C::LB; ++i) {
       const int p = (i * NW + wave) * 64 + lane, r = p / C::CH, s = p % C::CH;
       const int c = s ^ C::swz(r);
-      ob[i] = (uint32_t)(((int64_t)(min(n0 + r, N - 1) - n0) * ldw + c * 8) * 2);
+      ob[i] = (uint32_t)(((int64_t)r * ldw + c * 8) * 2);
     }
   }
-  __device__ __forceinline__ void issue(int k0, char* sa, char* sb) const {
+  __device__ static __forceinline__ LdsTileSrc tile(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int m0,
+                                                    int n0, int M, int N) {
+    return LdsTileSrc{uniform(A + (int64_t)m0 * lda), uniform(W + (int64_t)n0 * ldw), records(M, m0, lda),
+                      records(N, n0, ldw)};
+  }
+  __device__ __forceinline__ void issue(const LdsTileSrc& t, int k0, char* sa, char* sb) const {
     const int wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < C::LA; ++i) buffer_copy16(ba, oa[i], k0 * 2, sa + (i * NW + wave) * 1024);
+    for (int i = 0; i < C::LA; ++i) buffer_copy16(t.ba, t.na, oa[i], k0 * 2, sa + (i * NW + wave) * 1024);
 #pragma unroll
-    for (int i = 0; i < C::LB; ++i) buffer_copy16(bb, ob[i], k0 * 2, sb + (i * NW + wave) * 1024);
+    for (int i = 0; i < C::LB; ++i) buffer_copy16(t.bb, t.nb, ob[i], k0 * 2, sb + (i * NW + wave) * 1024);
   }
 };
 
@@ -525,9 +545,11 @@ struct LdsSlots {
 };
 
 // One K step kt with static ring slot P = kt % ST.  The K loop runs a multiple of ST steps and
-// always refills the freed slot (past the last stage it re-copies stage 0, which is never read), so
-// the body is straight-line code with a constant wait count: at the start of step kt exactly
-// ST - 2 later stages are in flight.
+// always refills the freed slot: past the last stage with the next tile's first stages (tile source
+// nxt), or, after a workgroup's last tile, with this tile's first stages again (never read).  So the
+// body is straight-line code with a constant wait count: at the start of step kt at least ST - 2
+// later stages' copies were issued after stage kt's (other vector-memory operations issued in
+// between only make the wait stricter).
 //
 // F8: the operands are E4M3 codes.  A row of 2 BK codes occupies the bytes of BK bf16 elements, so
 // the copies and the LDS layout are unchanged; each K step is then one
@@ -535,8 +557,9 @@ struct LdsSlots {
 // (lane half h reads 16-byte chunks 2h and 2h + 1 of its row, the same k for A and W).
 // M16 (bf16 only): 16 x 16 x 32 products on 16 x 16 accumulator blocks instead of 32 x 32 x 16 ones.
 template <int BM, int BN, int BK, int ST, int WM, int WN, int P, bool F8, bool M16>
-__device__ __forceinline__ void lds_gemm_step(const LdsCopyPlan<BM, BN, BK, WM * WN, M16>& cp,
-                                              const LdsSlots<BM, BN, BK, ST, WM, WN>& sl, int kt, int nk,
+__device__ __forceinline__ void lds_gemm_step(const LdsCopyPlan<BM, BN, BK, WM * WN, M16>& cp, const LdsTileSrc& cur,
+                                              const LdsTileSrc& nxt, const LdsSlots<BM, BN, BK, ST, WM, WN>& sl,
+                                              int kt, int nk,
                                               typename LdsAcc<BM / WM, BN / WN, M16>::type& acc) {
   using C = LdsGemmCfg<BM, BN, BK, WM * WN, M16>;
   constexpr int FM = BM / WM / 32, FN = BN / WN / 32, PER = C::LA + C::LB;
@@ -552,7 +575,13 @@ __device__ __forceinline__ void lds_gemm_step(const LdsCopyPlan<BM, BN, BK, WM *
   // then has this whole step to land), with more slots after this step's LDS reads.
   constexpr int Q = (P + ST - 1) % ST;
   const int kn = kt + ST - 1;
-  if constexpr (ST == 2) cp.issue((kn < nk ? kn : 0) * BK, sl.a[Q], sl.b[Q]);
+  auto refill = [&]() {
+    if (kn < nk)
+      cp.issue(cur, kn * BK, sl.a[Q], sl.b[Q]);
+    else
+      cp.issue(nxt, (kn - nk) * BK, sl.a[Q], sl.b[Q]);
+  };
+  if constexpr (ST == 2) refill();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lrow = lane & 31, lhalf = lane >> 5;
   const int wm = wave / WN, wn = wave % WN;
@@ -583,7 +612,7 @@ __device__ __forceinline__ void lds_gemm_step(const LdsCopyPlan<BM, BN, BK, WM *
                          (int)af[i][1].x, (int)af[i][1].y, (int)af[i][1].z, (int)af[i][1].w};
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 0, 0, 0, 127, 0, 127);
       }
-    if constexpr (ST > 2) cp.issue((kn < nk ? kn : 0) * BK, sl.a[Q], sl.b[Q]);
+    if constexpr (ST > 2) refill();
     return;
   }
   if constexpr (M16) {
@@ -624,10 +653,10 @@ __device__ __forceinline__ void lds_gemm_step(const LdsCopyPlan<BM, BN, BK, WM *
         for (int j = 0; j < FN; ++j) mfma_chunk(bfr[j], af[i], acc[i][j], bf16());  // C^T = W A^T
     }
   }
-  if constexpr (ST > 2) cp.issue((kn < nk ? kn : 0) * BK, sl.a[Q], sl.b[Q]);
+  if constexpr (ST > 2) refill();
 }
 
-template <int BM, int BN, int BK, int ST, int WM, int WN, class Epi, bool F8, bool M16>
+template <int BM, int BN, int BK, int ST, int WM, int WN, class Epi, bool F8, bool M16, bool PERSIST>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(const bf16* __restrict__ A, int64_t lda,
                                                                 const bf16* __restrict__ W, int64_t ldw, int M,
                                                                 int N, int K, int tiles_m, int tiles_n, int gm,
@@ -644,42 +673,60 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(const bf16* __res
       b3[ST > 3 ? C::BBYTES / 16 : 1];
   const LdsSlots<BM, BN, BK, ST, WM, WN> sl{{(char*)a0, (char*)a1, (char*)a2, (char*)a3},
                                             {(char*)b0, (char*)b1, (char*)b2, (char*)b3}};
-  int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, gm, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const LdsCopyPlan<BM, BN, BK, NW, M16> cp(A, lda, W, ldw, m0, n0, M, N);
-
-  typename LdsAcc<BM / WM, BN / WN, M16>::type acc;
-  if constexpr (M16) {
-#pragma unroll
-    for (int i = 0; i < FM * 2; ++i)
-#pragma unroll
-      for (int j = 0; j < FN * 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  } else {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = zero16();
-  }
-
+  // A fixed grid walks the tiles blockIdx.x, blockIdx.x + gridDim.x, ...  The last ST - 1 refills of a
+  // tile's K loop copy the first stages of the next tile (slot s for stage s, as nk is a multiple of
+  // ST), so those copies land while this tile's epilogue runs.  The epilogue touches no LDS.
+  const int ntiles = tiles_m * tiles_n;
+  int id = blockIdx.x, tm, tn;
+  tile_coords(id, tiles_m, tiles_n, gm, tm, tn);
+  using Plan = LdsCopyPlan<BM, BN, BK, NW, M16>;
+  const Plan cp(lda, ldw);
+  LdsTileSrc cur = Plan::tile(A, lda, W, ldw, tm * BM, tn * BN, M, N);
   const int nk = K / BK;  // a multiple of ST
 #pragma unroll
-  for (int s = 0; s < ST - 1; ++s) cp.issue(s * BK, sl.a[s], sl.b[s]);
-  for (int kt = 0; kt < nk; kt += ST) {
-    lds_gemm_step<BM, BN, BK, ST, WM, WN, 0, F8, M16>(cp, sl, kt, nk, acc);
-    lds_gemm_step<BM, BN, BK, ST, WM, WN, 1, F8, M16>(cp, sl, kt + 1, nk, acc);
-    if constexpr (ST > 2) lds_gemm_step<BM, BN, BK, ST, WM, WN, 2 % ST, F8, M16>(cp, sl, kt + 2, nk, acc);
-    if constexpr (ST > 3) lds_gemm_step<BM, BN, BK, ST, WM, WN, 3 % ST, F8, M16>(cp, sl, kt + 3, nk, acc);
-  }
-  wait_vmcnt<0>();  // the surplus copies past the last stage land before the LDS is released
-
+  for (int s = 0; s < ST - 1; ++s) cp.issue(cur, s * BK, sl.a[s], sl.b[s]);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lrow = lane & 31, lhalf = lane >> 5;
   const int wm = wave / WN, wn = wave % WN;
-  if constexpr (M16)
-    run_epilogue16<FM * 2, FN * 2>(epi, acc, m0 + wm * (BM / WM) + (lane & 15), n0 + wn * (BN / WN) + (lane >> 4) * 4,
-                                   M, N);
-  else
-    run_epilogue<FM, FN>(epi, acc, m0 + wm * (BM / WM) + lrow, n0 + wn * (BN / WN) + lhalf * 4, M, N);
+
+  for (;;) {
+    const int m0 = tm * BM, n0 = tn * BN, next = PERSIST ? id + (int)gridDim.x : ntiles;
+    int tm2 = tm, tn2 = tn;
+    LdsTileSrc nxt = cur;  // past the last tile the surplus refills re-copy this tile's stages (never read)
+    if (next < ntiles) {
+      tile_coords(next, tiles_m, tiles_n, gm, tm2, tn2);
+      nxt = Plan::tile(A, lda, W, ldw, tm2 * BM, tn2 * BN, M, N);
+    }
+
+    typename LdsAcc<BM / WM, BN / WN, M16>::type acc;
+    if constexpr (M16) {
+#pragma unroll
+      for (int i = 0; i < FM * 2; ++i)
+#pragma unroll
+        for (int j = 0; j < FN * 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = zero16();
+    }
+    for (int kt = 0; kt < nk; kt += ST) {
+      lds_gemm_step<BM, BN, BK, ST, WM, WN, 0, F8, M16>(cp, cur, nxt, sl, kt, nk, acc);
+      lds_gemm_step<BM, BN, BK, ST, WM, WN, 1, F8, M16>(cp, cur, nxt, sl, kt + 1, nk, acc);
+      if constexpr (ST > 2) lds_gemm_step<BM, BN, BK, ST, WM, WN, 2 % ST, F8, M16>(cp, cur, nxt, sl, kt + 2, nk, acc);
+      if constexpr (ST > 3) lds_gemm_step<BM, BN, BK, ST, WM, WN, 3 % ST, F8, M16>(cp, cur, nxt, sl, kt + 3, nk, acc);
+    }
+    if constexpr (M16)
+      run_epilogue16<FM * 2, FN * 2>(epi, acc, m0 + wm * (BM / WM) + (lane & 15),
+                                     n0 + wn * (BN / WN) + (lane >> 4) * 4, M, N);
+    else
+      run_epilogue<FM, FN>(epi, acc, m0 + wm * (BM / WM) + lrow, n0 + wn * (BN / WN) + lhalf * 4, M, N);
+    if (next >= ntiles) break;
+    id = next;
+    tm = tm2;
+    tn = tn2;
+    cur = nxt;
+  }
+  wait_vmcnt<0>();  // the surplus copies past the last stage land before the LDS is released
 }
 
 // Which bf16 products take 16 x 16 x 32 MFMAs: the store and residual epilogues.  The Q/K/V epilogue keeps
@@ -693,12 +740,36 @@ struct UseMfma16<EpiQKV<OutT>> {
   static constexpr bool value = false;
 };
 
+// Which products walk their tiles with a fixed grid: the plain-store ones (bf16 and E4M3).  Measured
+// in the block against one workgroup per tile: FFN1 2 % and the cross-attention q product 1.5 % faster;
+// the residual products gained nothing (FFN2 1 % slower) and the Q/K/V epilogue has no registers to
+// spare for a second tile's state.
+template <class Epi>
+struct EpiScaled;
+template <class Epi>
+struct UsePersistent {
+  static constexpr bool value = false;
+};
+template <typename OutT, int ACT>
+struct UsePersistent<EpiStore<OutT, ACT>> {
+  static constexpr bool value = true;
+};
+template <typename OutT, int ACT>
+struct UsePersistent<EpiScaled<EpiStore<OutT, ACT>>> {
+  static constexpr bool value = true;
+};
+
 template <int BM, int BN, int BK, int ST, int WM, int WN, class Epi, bool F8 = false>
 hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K, const Epi& epi,
                       hipStream_t s) {
   const int tm = (int)ceil_div(M, BM), tn = (int)ceil_div(N, BN);
   constexpr bool M16 = !F8 && UseMfma16<Epi>::value;
-  hipLaunchKernelGGL((gemm_lds_kernel<BM, BN, BK, ST, WM, WN, Epi, F8, M16>), dim3((unsigned)(tm * tn)),
+  constexpr bool PERSIST = UsePersistent<Epi>::value;
+  // One workgroup per compute unit: the ring takes ST * (BM + BN) * BK * 2 bytes of LDS.
+  static_assert(2 * ST * (BM + BN) * BK * 2 > 160 * 1024, "the persistent grid assumes one workgroup per CU");
+  const int64_t ntiles = (int64_t)tm * tn;
+  const int grid = PERSIST ? (int)std::min<int64_t>(ntiles, device_compute_units()) : (int)ntiles;
+  hipLaunchKernelGGL((gemm_lds_kernel<BM, BN, BK, ST, WM, WN, Epi, F8, M16, PERSIST>), dim3((unsigned)grid),
                      dim3(WM * WN * 64), 0, s, A, lda, W, ldw, M, N, K, tm, tn, group_m(tn, K), epi);
   return hipGetLastError();
 }
@@ -819,6 +890,20 @@ __global__ void sinusoid_kernel(SinArgs a, int B, int freq_dim, float* __restric
 }
 
 }  // namespace
+
+int device_compute_units() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
 
 template <typename T, typename OutT>
 hipError_t gemm_store(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const float* bias,

@@ -706,21 +706,6 @@ int wan_attention_fwd(int32_t dtype, const void* q, const void* k, const void* v
 
 namespace {
 
-// Compute units of the current device, queried once per device (256 when no device answers).
-int device_compute_units() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64) {
-    const int v = cache[dev].load(std::memory_order_relaxed);
-    if (v > 0) return v;
-  }
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
-  return cus;
-}
-
 // Key split of a partial attention whose grid would leave compute units idle: n parts of `chunk` keys
 // (a multiple of 64, at least 256).  Cost in units of one workgroup's 64-key tile:
 //   rounds(n) * (tiles(n) + SPLIT_FIXED_TILES) + merge(n),

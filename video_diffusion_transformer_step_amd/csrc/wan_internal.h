@@ -9,6 +9,9 @@
 
 namespace wan {
 
+// Compute units of the current device, queried once per device (256 when no device answers).
+int device_compute_units();
+
 // Activation applied in a GEMM / GEMV epilogue.
 enum Act { ACT_NONE = 0, ACT_GELU = 1, ACT_SILU = 2 };
 
