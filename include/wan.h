@@ -58,7 +58,7 @@ typedef struct {
   int32_t T, Hp, Wp;
 } wan_grid;
 
-/* Block hyper-parameters.  dim = heads * head_dim; head_dim 64 or 128; dim % 8 == 0, dim <= 6144;
+/* Block hyper-parameters.  dim = heads * head_dim; head_dim 64 or 128; dim <= 6144; ffn_dim % 32 == 0;
  * text_len > 0 text keys; img_len >= 0 image keys (0 = single-stream cross-attention).
  * Proposed eps 1e-6 for both norms and rope_theta 10000.  flags: 0 or WAN_FLAG_FP8_ATTN | WAN_FLAG_FP8_GEMM. */
 /* WAN_FLAG_FP8_ATTN: the block's self-attention runs the quantised path of wan_attention_q8_fwd (INT8
@@ -78,14 +78,27 @@ typedef struct {
   float ln_eps, rms_eps, rope_theta;
 } wan_block_cfg;
 
+/* K panels: the weight layout of the block's products.  A matrix W [N, K] (y = x W^T) is stored as
+ * K / 32 panels, each holding 32 consecutive k of every row n: element (n, k) at
+ * ((k / 32) * Np + n) * 32 + k % 32, where Np = N rounded up to a multiple of 256 and rows N .. Np - 1
+ * are zero.  wan_pack_weight_bytes(elem_bytes, N, K) = Np * K * elem_bytes (0 for invalid sizes:
+ * elem_bytes not 1, 2 or 4, N or K not positive, K % 32 != 0); wan_pack_weight writes the panels of
+ * a row-major W [N, K] (row stride K) with elem_bytes-byte elements (2 for bf16, 4 for float32, 1 for
+ * E4M3 codes) into `packed`.  Errors: WAN_EINVAL for those sizes or a NULL / misaligned pointer.
+ * Why: the products copy 32-deep K steps of 256-row weight tiles, and in panels each such step is one
+ * contiguous run of whole cache lines instead of 256 half-line segments. */
+size_t wan_pack_weight_bytes(int32_t elem_bytes, int64_t N, int64_t K);
+int wan_pack_weight(int32_t elem_bytes, const void* w, int64_t N, int64_t K, void* packed, wan_stream_t stream);
+
 /* Weights of one DiT block ([I2V] §5.2-§5.5; per-block modulation bias [DEEP] §2.5).
- * dtype matrices: wqkv [3*dim, dim] = rows [W_q; W_k; W_v]; wo, wcq, wco [dim, dim];
- * w1 [ffn_dim, dim]; w2 [dim, ffn_dim].  float32 vectors: mod_bias [6, dim] (chunks shift1, scale1,
- * gate1, shift2, scale2, gate2); bqkv [3*dim]; gq, gk [dim] RMSNorm gains; bo; ln3_w, ln3_b [dim]
- * (affine LayerNorm before cross-attention); bcq, bco [dim]; b1 [ffn_dim]; b2 [dim].
+ * dtype matrices, each in K panels (wan_pack_weight): wqkv [3*dim, dim] = rows [W_q; W_k; W_v];
+ * wo, wcq, wco [dim, dim]; w1 [ffn_dim, dim]; w2 [dim, ffn_dim].  float32 vectors: mod_bias [6, dim]
+ * (chunks shift1, scale1, gate1, shift2, scale2, gate2); bqkv [3*dim]; gq, gk [dim] RMSNorm gains; bo;
+ * ln3_w, ln3_b [dim] (affine LayerNorm before cross-attention); bcq, bco [dim]; b1 [ffn_dim]; b2 [dim].
  * Bias pointers may be NULL (zero bias); all others are required.  e4m3: NULL, or (required under
- * WAN_FLAG_FP8_GEMM) the E4M3 codes of wqkv, wo, w1, w2 with one float32 device scale each, as made by
- * wan_quantize_tensor_e4m3. */
+ * WAN_FLAG_FP8_GEMM) the E4M3 codes of wqkv, wo, w1, w2 in K panels with one float32 device scale
+ * each: wan_quantize_tensor_e4m3 of the packed bf16 matrices (codes are per element, so the codes of
+ * packed values are packed codes). */
 typedef struct {
   const void *wqkv, *wo, *w1, *w2;
   const float *s_wqkv, *s_wo, *s_w1, *s_w2;
@@ -334,13 +347,14 @@ int wan_attention_q8_fwd(const void* q8, const float* sq, const void* k8, const 
  * wan_quantize_tensor_e4m3: x [n] bf16 (n % 8 == 0) -> codes [n] and one float32 scale, both on the
  *   device; ws: at least 256 bytes of device scratch.
  * wan_gemm_e4m3: y [M, N] bf16 (row stride ldy elements) = act((A W^T) * a_scales[m] * w_scale[0] + bias[n])
- *   from codes A [M, K] (row stride lda bytes) and W [N, K] (row stride ldw bytes); K % 256 == 0,
- *   N % 4 == 0, strides % 16 == 0; act 0 = none, 1 = GELU (erf); bias may be NULL. */
+ *   from codes A [M, K] (row stride lda bytes, % 16 == 0) and W [N, K] in K panels (wan_pack_weight,
+ *   elem_bytes 1); K % 256 == 0, N % 4 == 0, ldy % 4 == 0; act 0 = none, 1 = GELU (erf); bias may be
+ *   NULL.  WAN_EUNSUPPORTED when the panels reach 2 GiB. */
 int wan_quantize_rows_e4m3(const void* x, int64_t ld, int32_t rows, int32_t cols, void* codes, int64_t ldc,
                            float* scales, wan_stream_t stream);
 int wan_quantize_tensor_e4m3(const void* x, int64_t n, void* codes, float* scale, void* ws, size_t ws_bytes,
                              wan_stream_t stream);
-int wan_gemm_e4m3(const void* a, int64_t lda, const float* a_scales, const void* w, int64_t ldw, const float* w_scale,
+int wan_gemm_e4m3(const void* a, int64_t lda, const float* a_scales, const void* w, const float* w_scale,
                   int32_t M, int32_t N, int32_t K, const float* bias, int32_t act, void* y, int64_t ldy,
                   wan_stream_t stream);
 

@@ -169,6 +169,25 @@ def test_other_entry_validation(lib):
                                  None) == L.WAN_EINVAL
 
 
+def test_weight_panel_sizes_and_validation(lib):
+    """K panels of 32 with N rounded up to 256 rows (the layout wan.h defines for the block's matrices)."""
+    assert lib.wan_pack_weight_bytes(2, 1536, 8960) == 1536 * 8960 * 2
+    assert lib.wan_pack_weight_bytes(2, 260, 768) == 512 * 768 * 2
+    assert lib.wan_pack_weight_bytes(1, 1, 256) == 256 * 256
+    assert lib.wan_pack_weight_bytes(4, 300, 32) == 512 * 32 * 4
+    for bad in ((3, 256, 256), (2, 0, 256), (2, 256, 0), (2, 256, 48), (1, -1, 64)):
+        assert lib.wan_pack_weight_bytes(*bad) == 0, bad
+    assert lib.wan_pack_weight(2, FAKE, 256, 48, FAKE, None) == L.WAN_EINVAL
+    assert lib.wan_pack_weight(3, FAKE, 256, 64, FAKE, None) == L.WAN_EINVAL
+    assert lib.wan_pack_weight(2, None, 256, 64, FAKE, None) == L.WAN_EINVAL
+    assert lib.wan_pack_weight(2, FAKE, 256, 64, FAKE + 8, None) == L.WAN_EINVAL
+    # E4M3 product: K % 256, and the panels must stay below 2 GiB
+    assert lib.wan_gemm_e4m3(FAKE, 512, FAKE, FAKE, FAKE, 64, 256, 384, None, 0, FAKE, 256, None) \
+        == L.WAN_EUNSUPPORTED
+    assert lib.wan_gemm_e4m3(FAKE, 1 << 17, FAKE, FAKE, FAKE, 64, 1 << 17, 1 << 17, None, 0, FAKE, 1 << 17,
+                             None) == L.WAN_EUNSUPPORTED
+
+
 def test_ring_attention_validation(lib):
     need = lib.wan_attention_partial_workspace_bytes(L.WAN_BF16, 1, 50, 100, 2, 64)
     assert need == 2 * 64 * 128 * 2  # V^T of 100 keys padded to 128; too few keys to split

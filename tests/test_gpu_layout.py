@@ -113,3 +113,37 @@ def test_fm_straight_line_on_gpu():
             L.fm_euler_step(xd, v, None, 1.0, 1.0 / N)
         # fp32 accumulation over N steps: each step rounds once
         assert np.abs(host(xd) - x1.astype(np.float64)).max() <= N * 4e-7 * 8
+
+
+def _panels_reference(w):
+    """The K-panel layout wan.h defines, written out: element (n, k) at ((k / 32) * Np + n) * 32 + k % 32
+    with Np = N rounded up to 256 and zero rows past N."""
+    N, K = w.shape
+    Np = (N + 255) // 256 * 256
+    p = np.zeros((K // 32, Np, 32), dtype=w.dtype)
+    for j in range(K // 32):
+        p[j, :N, :] = w[:, 32 * j:32 * j + 32]
+    return p.reshape(-1)
+
+
+@pytest.mark.parametrize("N,K,dtype", [(260, 96, torch.bfloat16), (1, 32, torch.float32), (512, 256, torch.uint8),
+                                       (1536, 8960, torch.bfloat16), (300, 288, torch.uint8)],
+                         ids=lambda v: str(v).replace("torch.", ""))
+def test_pack_weight_bit_exact(N, K, dtype):
+    """wan_pack_weight against the layout definition, bit for bit (ragged rows, all three element sizes,
+    the 1.3B block's FFN2 weight)."""
+    require_gpu()
+    case(f"pack_weight N={N} K={K} {dtype}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(N * 7 + K)
+    if dtype == torch.uint8:
+        w = torch.randint(0, 256, (N, K), generator=g, device="cuda", dtype=torch.int32).to(torch.uint8)
+        raw = host(w)
+    else:
+        w = torch.randn((N, K), generator=g, device="cuda").to(dtype)
+        raw = host(w.view(torch.int16 if dtype == torch.bfloat16 else torch.int32))
+    got = L.pack_weight(w)
+    torch.cuda.synchronize()
+    got_raw = host(got if dtype == torch.uint8 else got.view(torch.int16 if dtype == torch.bfloat16 else torch.int32))
+    assert got.numel() == L.lib().wan_pack_weight_bytes(w.element_size(), N, K) // w.element_size()
+    np.testing.assert_array_equal(got_raw, _panels_reference(raw))

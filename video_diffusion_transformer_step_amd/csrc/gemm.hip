@@ -311,8 +311,8 @@ inline int group_m(int tiles_n, int K) { return (K >= 4096 && tiles_n < 32) ? 2 
 
 template <typename T, int BM, int BN, int WM, int WN, class Epi>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restrict__ A, int64_t lda,
-                                                               const T* __restrict__ W, int64_t ldw, int M,
-                                                               int N, int K, int tiles_m, int tiles_n, int gm,
+                                                               const T* __restrict__ W, int64_t ldw, int64_t wpr,
+                                                               int M, int N, int K, int tiles_m, int tiles_n, int gm,
                                                                Epi epi) {
   constexpr int NT = WM * WN * 64;
   constexpr int E16 = dtype_traits<T>::per16;  // elements per 16 bytes
@@ -345,16 +345,18 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restric
 #pragma unroll
   for (int i = 0; i < BC; ++i) {
     const int c = tid + i * NT, r = c >> 3, kc = (c & 7) * E16;
-    pb[i] = W + (int64_t)min(n0 + r, N - 1) * ldw + kc;
+    const int64_t n = min(n0 + r, N - 1);
+    pb[i] = wpr ? W + ((kc / 32) * wpr + n) * 32 + kc % 32 : W + n * ldw + kc;  // K step k0 adds k0 * wstep
     lb[i] = BM * ROW + r * ROW + kc;
   }
+  const int64_t wstep = wpr ? wpr : 1;
 
   u32x4 ra[AC], rb[BC];
   auto load_full = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < AC; ++i) ra[i] = *reinterpret_cast<const u32x4*>(pa[i] + k0);
 #pragma unroll
-    for (int i = 0; i < BC; ++i) rb[i] = *reinterpret_cast<const u32x4*>(pb[i] + k0);
+    for (int i = 0; i < BC; ++i) rb[i] = *reinterpret_cast<const u32x4*>(pb[i] + k0 * wstep);
   };
   auto load_tail = [&](int k0) {  // last, partial K step: zero-fill k >= K
 #pragma unroll
@@ -365,7 +367,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restric
 #pragma unroll
     for (int i = 0; i < BC; ++i) {
       const int kk = k0 + ((tid + i * NT) & 7) * E16;
-      rb[i] = kk < K ? *reinterpret_cast<const u32x4*>(pb[i] + k0) : u32x4{0, 0, 0, 0};
+      rb[i] = kk < K ? *reinterpret_cast<const u32x4*>(pb[i] + k0 * wstep) : u32x4{0, 0, 0, 0};
     }
   };
   auto store_stage = [&](int buf) {
@@ -464,9 +466,15 @@ struct LdsGemmCfg {
 // reads of a step wait only for their own results; with the FLAT form in flight every LDS read would
 // wait for all outstanding LDS accesses.  Each operand tile has one wave-uniform base (its first row)
 // and a record count (the bytes from there to the end of the operand); each lane a 32-bit byte offset
-// (row, permuted chunk) that is the same for every tile; the K position is the scalar offset.  Rows
-// past the operand's last one start at or beyond the record count, so the buffer's range check turns
-// their copies into zeros without a memory access; such rows only feed outputs that are not stored.
+// (row, permuted chunk) that is the same for every tile; the K position is the scalar offset.
+//  * A (activations, row-major): a stage copies 64-byte segments of 256 rows.  Rows past the
+//    operand's last one start at or beyond the record count, so the buffer's range check turns their
+//    copies into zeros without a memory access; such rows only feed outputs that are not stored.
+//  * W (weights, in K panels of 32 elements; see WMat): the stage of a 256-row tile is one contiguous
+//    run, 16 KB of bf16 or two runs of 8 KB of E4M3 codes (the two panels of a 64-code step), so every
+//    copy instruction reads whole 128-byte lines.  In a lab loop on the block's shapes this made the
+//    products 3-8 % faster than 64-byte segments of row-major weights.  The panels hold N rounded up to
+//    256 rows (zero past N), so a tile's rows all exist.
 __device__ __forceinline__ void buffer_copy16(const void* base, uint32_t records, uint32_t voff, uint32_t soff,
                                               char* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -481,11 +489,14 @@ struct LdsTileSrc {
   uint32_t na, nb;
 };
 
-template <int BM, int BN, int BK, int NW, bool M16 = false>
+// F8: the operands are E4M3 codes (a K step of BK bf16 units = 2 BK codes = two W panels).
+template <int BM, int BN, int BK, int NW, bool M16, bool F8>
 struct LdsCopyPlan {
   using C = LdsGemmCfg<BM, BN, BK, NW, M16>;
+  static_assert(BK == 32, "one W panel (bf16) or two (E4M3) per K step");
   uint32_t oa[C::LA];
   uint32_t ob[C::LB];
+  uint32_t wstage;  // bytes between consecutive K steps of W: 64 * panel rows
   __device__ static __forceinline__ const bf16* uniform(const bf16* p) {
     const uint64_t a = (uint64_t)p;
     return (const bf16*)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
@@ -497,7 +508,8 @@ struct LdsCopyPlan {
     const int64_t b = (int64_t)(rows - r0) * ld * 2;
     return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b < 0xFFFFFFFFll ? b : 0xFFFFFFFFll));
   }
-  __device__ __forceinline__ LdsCopyPlan(int64_t lda, int64_t ldw) {
+  // wpr: rows per W panel (N rounded up to 256); 64 * K * wpr / BK bytes of panels stay below 2^31.
+  __device__ __forceinline__ LdsCopyPlan(int64_t lda, int64_t wpr) : wstage((uint32_t)(64 * wpr)) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < C::LA; ++i) {
@@ -509,20 +521,24 @@ struct LdsCopyPlan {
     for (int i = 0; i < C::LB; ++i) {
       const int p = (i * NW + wave) * 64 + lane, r = p / C::CH, s = p % C::CH;
       const int c = s ^ C::swz(r);
-      ob[i] = (uint32_t)(((int64_t)r * ldw + c * 8) * 2);
+      // bf16: chunk c of row r's 64-byte panel row; E4M3: chunk c % 2 of row r's 32-byte row in panel c / 2
+      ob[i] = F8 ? (uint32_t)((c >> 1) * 32 * wpr + r * 32 + (c & 1) * 16) : (uint32_t)(r * 64 + c * 16);
     }
   }
-  __device__ static __forceinline__ LdsTileSrc tile(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int m0,
-                                                    int n0, int M, int N) {
-    return LdsTileSrc{uniform(A + (int64_t)m0 * lda), uniform(W + (int64_t)n0 * ldw), records(M, m0, lda),
-                      records(N, n0, ldw)};
+  // K: the product depth in bf16 units (the panels hold 2 K wpr bytes).
+  __device__ static __forceinline__ LdsTileSrc tile(const bf16* A, int64_t lda, const bf16* W, int64_t wpr, int K,
+                                                    int m0, int n0, int M) {
+    const int64_t wofs = (int64_t)n0 * (F8 ? 32 : 64);  // bytes from the panels' start to row n0 of panel 0
+    return LdsTileSrc{uniform(A + (int64_t)m0 * lda), uniform(W + wofs / 2), records(M, m0, lda),
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(2 * (int64_t)K * wpr - wofs))};
   }
   __device__ __forceinline__ void issue(const LdsTileSrc& t, int k0, char* sa, char* sb) const {
     const int wave = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < C::LA; ++i) buffer_copy16(t.ba, t.na, oa[i], k0 * 2, sa + (i * NW + wave) * 1024);
+    const uint32_t ws = (uint32_t)(k0 / BK) * wstage;
 #pragma unroll
-    for (int i = 0; i < C::LB; ++i) buffer_copy16(t.bb, t.nb, ob[i], k0 * 2, sb + (i * NW + wave) * 1024);
+    for (int i = 0; i < C::LB; ++i) buffer_copy16(t.bb, t.nb, ob[i], ws, sb + (i * NW + wave) * 1024);
   }
 };
 
@@ -557,7 +573,7 @@ struct LdsSlots {
 // (lane half h reads 16-byte chunks 2h and 2h + 1 of its row, the same k for A and W).
 // M16 (bf16 only): 16 x 16 x 32 products on 16 x 16 accumulator blocks instead of 32 x 32 x 16 ones.
 template <int BM, int BN, int BK, int ST, int WM, int WN, int P, bool F8, bool M16>
-__device__ __forceinline__ void lds_gemm_step(const LdsCopyPlan<BM, BN, BK, WM * WN, M16>& cp, const LdsTileSrc& cur,
+__device__ __forceinline__ void lds_gemm_step(const LdsCopyPlan<BM, BN, BK, WM * WN, M16, F8>& cp, const LdsTileSrc& cur,
                                               const LdsTileSrc& nxt, const LdsSlots<BM, BN, BK, ST, WM, WN>& sl,
                                               int kt, int nk,
                                               typename LdsAcc<BM / WM, BN / WN, M16>::type& acc) {
@@ -658,7 +674,7 @@ __device__ __forceinline__ void lds_gemm_step(const LdsCopyPlan<BM, BN, BK, WM *
 
 template <int BM, int BN, int BK, int ST, int WM, int WN, class Epi, bool F8, bool M16, bool PERSIST>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(const bf16* __restrict__ A, int64_t lda,
-                                                                const bf16* __restrict__ W, int64_t ldw, int M,
+                                                                const bf16* __restrict__ W, int64_t wpr, int M,
                                                                 int N, int K, int tiles_m, int tiles_n, int gm,
                                                                Epi epi) {
   constexpr int NW = WM * WN;
@@ -679,9 +695,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(const bf16* __res
   const int ntiles = tiles_m * tiles_n;
   int id = blockIdx.x, tm, tn;
   tile_coords(id, tiles_m, tiles_n, gm, tm, tn);
-  using Plan = LdsCopyPlan<BM, BN, BK, NW, M16>;
-  const Plan cp(lda, ldw);
-  LdsTileSrc cur = Plan::tile(A, lda, W, ldw, tm * BM, tn * BN, M, N);
+  using Plan = LdsCopyPlan<BM, BN, BK, NW, M16, F8>;
+  const Plan cp(lda, wpr);
+  LdsTileSrc cur = Plan::tile(A, lda, W, wpr, K, tm * BM, tn * BN, M);
   const int nk = K / BK;  // a multiple of ST
 #pragma unroll
   for (int s = 0; s < ST - 1; ++s) cp.issue(cur, s * BK, sl.a[s], sl.b[s]);
@@ -694,7 +710,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(const bf16* __res
     LdsTileSrc nxt = cur;  // past the last tile the surplus refills re-copy this tile's stages (never read)
     if (next < ntiles) {
       tile_coords(next, tiles_m, tiles_n, gm, tm2, tn2);
-      nxt = Plan::tile(A, lda, W, ldw, tm2 * BM, tn2 * BN, M, N);
+      nxt = Plan::tile(A, lda, W, wpr, K, tm2 * BM, tn2 * BN, M);
     }
 
     typename LdsAcc<BM / WM, BN / WN, M16>::type acc;
@@ -760,7 +776,7 @@ struct UsePersistent<EpiScaled<EpiStore<OutT, ACT>>> {
 };
 
 template <int BM, int BN, int BK, int ST, int WM, int WN, class Epi, bool F8 = false>
-hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K, const Epi& epi,
+hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t wpr, int M, int N, int K, const Epi& epi,
                       hipStream_t s) {
   const int tm = (int)ceil_div(M, BM), tn = (int)ceil_div(N, BN);
   constexpr bool M16 = !F8 && UseMfma16<Epi>::value;
@@ -770,7 +786,7 @@ hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, in
   const int64_t ntiles = (int64_t)tm * tn;
   const int grid = PERSIST ? (int)std::min<int64_t>(ntiles, device_compute_units()) : (int)ntiles;
   hipLaunchKernelGGL((gemm_lds_kernel<BM, BN, BK, ST, WM, WN, Epi, F8, M16, PERSIST>), dim3((unsigned)grid),
-                     dim3(WM * WN * 64), 0, s, A, lda, W, ldw, M, N, K, tm, tn, group_m(tn, K), epi);
+                     dim3(WM * WN * 64), 0, s, A, lda, W, wpr, M, N, K, tm, tn, group_m(tn, K), epi);
   return hipGetLastError();
 }
 
@@ -795,47 +811,50 @@ struct EpiScaled {
 };
 
 // E4M3 product ("Wan 技术深度解析" §5.3: per-token activation, per-tensor weight scales): A codes [M, K]
-// (row stride lda bytes) with per-row scales, W codes [N, K] (row stride ldw bytes) with one tensor scale.  K a multiple of 256, strides multiples of 16 bytes.
+// (row stride lda bytes) with per-row scales, W codes [N, K] in K panels (see WMat) with one tensor
+// scale.  K a multiple of 256, lda a multiple of 16 bytes.
 template <class Epi>
-hipError_t run_gemm_e4m3(const uint8_t* A, int64_t lda, const float* a_scales, const uint8_t* W, int64_t ldw,
+hipError_t run_gemm_e4m3(const uint8_t* A, int64_t lda, const float* a_scales, WMat<uint8_t> W,
                          const float* w_scale, int M, int N, int K, const Epi& epi, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  if (N % 4 != 0 || K % 256 != 0 || lda % 16 != 0 || ldw % 16 != 0) return hipErrorInvalidValue;
+  if (N % 4 != 0 || K % 256 != 0 || lda % 16 != 0 || !w_panels_ok(W, N, K) ||
+      (int64_t)K * W.panel >= ((int64_t)1 << 31) || (int64_t)256 * lda >= ((int64_t)1 << 31))
+    return hipErrorInvalidValue;
   return launch_lds<256, 256, 32, 4, 4, 2, EpiScaled<Epi>, true>(
-      reinterpret_cast<const bf16*>(A), lda / 2, reinterpret_cast<const bf16*>(W), ldw / 2, M, N, K / 2,
+      reinterpret_cast<const bf16*>(A), lda / 2, reinterpret_cast<const bf16*>(W.p), W.panel, M, N, K / 2,
       EpiScaled<Epi>{a_scales, w_scale, epi}, s);
 }
 
 template <typename T, int BM, int BN, int WM, int WN, class Epi>
-hipError_t launch_cfg(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const Epi& epi,
-                      hipStream_t s) {
+hipError_t launch_cfg(const T* A, int64_t lda, WMat<T> W, int M, int N, int K, const Epi& epi, hipStream_t s) {
   const int tm = (int)ceil_div(M, BM), tn = (int)ceil_div(N, BN);
   hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, WM, WN, Epi>), dim3((unsigned)(tm * tn)), dim3(WM * WN * 64), 0,
-                     s, A, lda, W, ldw, M, N, K, tm, tn, group_m(tn, K), epi);
+                     s, A, lda, W.p, W.ld, W.panel, M, N, K, tm, tn, group_m(tn, K), epi);
   return hipGetLastError();
 }
 
-// Tile choice.  bf16 products with many rows and K a multiple of 128 use the asynchronous-copy
-// kernel (256 x 256 tiles, 8 waves of 64 x 128, BK 32, four LDS stages); other bf16 products with
-// many rows use the register-staged kernel with 256-row tiles; small products and fp32 use 128 x 128.
+// Tile choice.  bf16 products with many rows, K a multiple of 128 and weights in K panels use the
+// asynchronous-copy kernel (256 x 256 tiles, 8 waves of 64 x 128, BK 32, four LDS stages); other bf16
+// products with many rows use the register-staged kernel with 256-row tiles; small products and fp32
+// use 128 x 128.
 template <typename T, class Epi>
-hipError_t run_gemm(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const Epi& epi,
-                    hipStream_t s) {
+hipError_t run_gemm(const T* A, int64_t lda, WMat<T> W, int M, int N, int K, const Epi& epi, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (N % 4 != 0 || K % dtype_traits<T>::per16 != 0) return hipErrorInvalidValue;
+  if (W.panel ? !w_panels_ok(W, N, K) : W.ld % dtype_traits<T>::per16 != 0) return hipErrorInvalidValue;
   if constexpr (sizeof(T) == 2) {
     int cfg = 0;
-    // (the asynchronous-copy kernel addresses a 256-row operand tile with 32-bit byte offsets)
-    if (M >= 4096 && N >= 1024 && K % 128 == 0 && lda % 8 == 0 && ldw % 8 == 0 &&
-        (int64_t)256 * (lda > ldw ? lda : ldw) * 2 < ((int64_t)1 << 31))
+    // (the asynchronous-copy kernel addresses a 256-row A tile and the W panels with 32-bit byte offsets)
+    if (W.panel && M >= 4096 && N >= 1024 && K % 128 == 0 && lda % 8 == 0 &&
+        (int64_t)256 * lda * 2 < ((int64_t)1 << 31) && (int64_t)2 * K * W.panel < ((int64_t)1 << 31))
       cfg = 1;
     else if (M >= 4096 && N % 256 == 0 && N >= 1024) cfg = 2;
     else if (M >= 4096 && N % 128 == 0 && N >= 1024) cfg = 3;
-    if (cfg == 1) return launch_lds<256, 256, 32, 4, 4, 2>(A, lda, W, ldw, M, N, K, epi, s);
-    if (cfg == 2) return launch_cfg<T, 256, 256, 4, 2>(A, lda, W, ldw, M, N, K, epi, s);
-    if (cfg == 3) return launch_cfg<T, 256, 128, 4, 2>(A, lda, W, ldw, M, N, K, epi, s);
+    if (cfg == 1) return launch_lds<256, 256, 32, 4, 4, 2>(A, lda, W.p, W.panel, M, N, K, epi, s);
+    if (cfg == 2) return launch_cfg<T, 256, 256, 4, 2>(A, lda, W, M, N, K, epi, s);
+    if (cfg == 3) return launch_cfg<T, 256, 128, 4, 2>(A, lda, W, M, N, K, epi, s);
   }
-  return launch_cfg<T, 128, 128, 2, 2>(A, lda, W, ldw, M, N, K, epi, s);
+  return launch_cfg<T, 128, 128, 2, 2>(A, lda, W, M, N, K, epi, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -906,11 +925,11 @@ int device_compute_units() {
 }
 
 template <typename T, typename OutT>
-hipError_t gemm_store(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const float* bias,
-                      int act, OutT* out, int64_t ldo, hipStream_t s) {
-  if (act == ACT_GELU) return run_gemm<T>(A, lda, W, ldw, M, N, K, EpiStore<OutT, ACT_GELU>{out, ldo, bias}, s);
-  if (act == ACT_SILU) return run_gemm<T>(A, lda, W, ldw, M, N, K, EpiStore<OutT, ACT_SILU>{out, ldo, bias}, s);
-  return run_gemm<T>(A, lda, W, ldw, M, N, K, EpiStore<OutT, ACT_NONE>{out, ldo, bias}, s);
+hipError_t gemm_store(const T* A, int64_t lda, WMat<T> W, int M, int N, int K, const float* bias, int act, OutT* out,
+                      int64_t ldo, hipStream_t s) {
+  if (act == ACT_GELU) return run_gemm<T>(A, lda, W, M, N, K, EpiStore<OutT, ACT_GELU>{out, ldo, bias}, s);
+  if (act == ACT_SILU) return run_gemm<T>(A, lda, W, M, N, K, EpiStore<OutT, ACT_SILU>{out, ldo, bias}, s);
+  return run_gemm<T>(A, lda, W, M, N, K, EpiStore<OutT, ACT_NONE>{out, ldo, bias}, s);
 }
 
 namespace {
@@ -932,39 +951,39 @@ bool qkv_args_ok(int M, int dim, int S, int hd, const QKNormRope& nr) {
 }  // namespace
 
 template <typename T>
-hipError_t gemm_qkv(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int dim, int K, const float* bias,
+hipError_t gemm_qkv(const T* A, int64_t lda, WMat<T> W, int M, int dim, int K, const float* bias,
                     T* qk, int64_t ldo, T* vt, int S, int H, int hd, int Spad, const QKNormRope& nr, hipStream_t s) {
   if (!qkv_args_ok(M, dim, S, hd, nr)) return hipErrorInvalidValue;
-  return run_gemm<T>(A, lda, W, ldw, M, 3 * dim, K, make_epi_qkv<T>(qk, ldo, bias, vt, M, dim, S, H, hd, Spad, nr), s);
+  return run_gemm<T>(A, lda, W, M, 3 * dim, K, make_epi_qkv<T>(qk, ldo, bias, vt, M, dim, S, H, hd, Spad, nr), s);
 }
 
 template <typename T>
-hipError_t gemm_residual(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const float* bias,
+hipError_t gemm_residual(const T* A, int64_t lda, WMat<T> W, int M, int N, int K, const float* bias,
                          const float* gate, int chunk, int S, float* x, int64_t ldx, hipStream_t s, float* ystore) {
   EpiResidual epi{x, ldx, bias, gate, chunk, S, N, ystore};
-  return run_gemm<T>(A, lda, W, ldw, M, N, K, epi, s);
+  return run_gemm<T>(A, lda, W, M, N, K, epi, s);
 }
 
-hipError_t gemm_e4m3_store(const uint8_t* A, int64_t lda, const float* a_scales, const uint8_t* W, int64_t ldw,
+hipError_t gemm_e4m3_store(const uint8_t* A, int64_t lda, const float* a_scales, WMat<uint8_t> W,
                            const float* w_scale, int M, int N, int K, const float* bias, int act, bf16* out, int64_t ldo,
                            hipStream_t s) {
   if (act == ACT_GELU)
-    return run_gemm_e4m3(A, lda, a_scales, W, ldw, w_scale, M, N, K, EpiStore<bf16, ACT_GELU>{out, ldo, bias}, s);
-  return run_gemm_e4m3(A, lda, a_scales, W, ldw, w_scale, M, N, K, EpiStore<bf16, ACT_NONE>{out, ldo, bias}, s);
+    return run_gemm_e4m3(A, lda, a_scales, W, w_scale, M, N, K, EpiStore<bf16, ACT_GELU>{out, ldo, bias}, s);
+  return run_gemm_e4m3(A, lda, a_scales, W, w_scale, M, N, K, EpiStore<bf16, ACT_NONE>{out, ldo, bias}, s);
 }
 
-hipError_t gemm_qkv_e4m3(const uint8_t* A, int64_t lda, const float* a_scales, const uint8_t* W, int64_t ldw,
+hipError_t gemm_qkv_e4m3(const uint8_t* A, int64_t lda, const float* a_scales, WMat<uint8_t> W,
                          const float* w_scale, int M, int dim, int K, const float* bias, bf16* qk, int64_t ldo, bf16* vt,
                          int S, int H, int hd, int Spad, const QKNormRope& nr, hipStream_t s) {
   if (!qkv_args_ok(M, dim, S, hd, nr)) return hipErrorInvalidValue;
-  return run_gemm_e4m3(A, lda, a_scales, W, ldw, w_scale, M, 3 * dim, K,
+  return run_gemm_e4m3(A, lda, a_scales, W, w_scale, M, 3 * dim, K,
                        make_epi_qkv<bf16>(qk, ldo, bias, vt, M, dim, S, H, hd, Spad, nr), s);
 }
 
-hipError_t gemm_e4m3_residual(const uint8_t* A, int64_t lda, const float* a_scales, const uint8_t* W, int64_t ldw,
+hipError_t gemm_e4m3_residual(const uint8_t* A, int64_t lda, const float* a_scales, WMat<uint8_t> W,
                               const float* w_scale, int M, int N, int K, const float* bias, const float* gate,
                               int chunk, int S, float* x, int64_t ldx, hipStream_t s, float* ystore) {
-  return run_gemm_e4m3(A, lda, a_scales, W, ldw, w_scale, M, N, K, EpiResidual{x, ldx, bias, gate, chunk, S, N, ystore},
+  return run_gemm_e4m3(A, lda, a_scales, W, w_scale, M, N, K, EpiResidual{x, ldx, bias, gate, chunk, S, N, ystore},
                        s);
 }
 
@@ -986,20 +1005,20 @@ hipError_t launch_sinusoid(const float* t_host, int B, int freq_dim, float* emb,
   return hipGetLastError();
 }
 
-template hipError_t gemm_store<float, float>(const float*, int64_t, const float*, int64_t, int, int, int,
-                                             const float*, int, float*, int64_t, hipStream_t);
-template hipError_t gemm_store<bf16, bf16>(const bf16*, int64_t, const bf16*, int64_t, int, int, int, const float*,
-                                           int, bf16*, int64_t, hipStream_t);
-template hipError_t gemm_store<bf16, float>(const bf16*, int64_t, const bf16*, int64_t, int, int, int,
-                                            const float*, int, float*, int64_t, hipStream_t);
-template hipError_t gemm_qkv<float>(const float*, int64_t, const float*, int64_t, int, int, int, const float*, float*,
-                                    int64_t, float*, int, int, int, int, const QKNormRope&, hipStream_t);
-template hipError_t gemm_qkv<bf16>(const bf16*, int64_t, const bf16*, int64_t, int, int, int, const float*, bf16*,
-                                   int64_t, bf16*, int, int, int, int, const QKNormRope&, hipStream_t);
-template hipError_t gemm_residual<float>(const float*, int64_t, const float*, int64_t, int, int, int, const float*,
+template hipError_t gemm_store<float, float>(const float*, int64_t, WMat<float>, int, int, int, const float*, int,
+                                             float*, int64_t, hipStream_t);
+template hipError_t gemm_store<bf16, bf16>(const bf16*, int64_t, WMat<bf16>, int, int, int, const float*, int, bf16*,
+                                           int64_t, hipStream_t);
+template hipError_t gemm_store<bf16, float>(const bf16*, int64_t, WMat<bf16>, int, int, int, const float*, int,
+                                            float*, int64_t, hipStream_t);
+template hipError_t gemm_qkv<float>(const float*, int64_t, WMat<float>, int, int, int, const float*, float*, int64_t,
+                                    float*, int, int, int, int, const QKNormRope&, hipStream_t);
+template hipError_t gemm_qkv<bf16>(const bf16*, int64_t, WMat<bf16>, int, int, int, const float*, bf16*, int64_t,
+                                   bf16*, int, int, int, int, const QKNormRope&, hipStream_t);
+template hipError_t gemm_residual<float>(const float*, int64_t, WMat<float>, int, int, int, const float*,
                                          const float*, int, int, float*, int64_t, hipStream_t, float*);
-template hipError_t gemm_residual<bf16>(const bf16*, int64_t, const bf16*, int64_t, int, int, int, const float*,
-                                        const float*, int, int, float*, int64_t, hipStream_t, float*);
+template hipError_t gemm_residual<bf16>(const bf16*, int64_t, WMat<bf16>, int, int, int, const float*, const float*,
+                                        int, int, float*, int64_t, hipStream_t, float*);
 template hipError_t gemv<float>(const float*, int, int, const float*, int, const float*, int, int, float*,
                                 hipStream_t);
 template hipError_t gemv<bf16>(const bf16*, int, int, const float*, int, const float*, int, int, float*,

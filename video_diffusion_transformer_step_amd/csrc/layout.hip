@@ -280,6 +280,35 @@ hipError_t launch_attn_prologue(T* vt, int64_t rows, int S, int Spad, float2* ro
   return hipGetLastError();
 }
 
+// Row-major [rows, cols] -> K panels of 32 elements ([cols / 32][prow][32], rows past `rows` zero): one
+// thread per 16-byte chunk of the destination, which is written in order.
+__global__ __launch_bounds__(256) void pack_panels_kernel(const uint8_t* __restrict__ src, int64_t rows,
+                                                           int64_t ld_bytes, int64_t prow, int pb, int64_t nchunks,
+                                                           uint8_t* __restrict__ dst) {
+  const int cpr = pb / 16;  // chunks per panel row
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nchunks; q += (int64_t)gridDim.x * blockDim.x) {
+    const int j = (int)(q % cpr);
+    const int64_t t = q / cpr, n = t % prow, p = t / prow;
+    u32x4 v{0u, 0u, 0u, 0u};
+    if (n < rows) v = *reinterpret_cast<const u32x4*>(src + n * ld_bytes + p * pb + j * 16);
+    *reinterpret_cast<u32x4*>(dst + q * 16) = v;
+  }
+}
+
+hipError_t launch_pack_panels(const void* src, int64_t rows, int64_t cols, int64_t ld, int elem_bytes, void* dst,
+                              hipStream_t s) {
+  if (rows < 0 || cols < 0 || cols % 32 != 0 || (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4) ||
+      (ld * elem_bytes) % 16 != 0 || ld < cols)
+    return hipErrorInvalidValue;
+  const int64_t prow = panel_rows(rows), pb = 32 * elem_bytes;
+  const int64_t nchunks = cols / 32 * prow * (pb / 16);
+  if (nchunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_panels_kernel, dim3(grid_for(nchunks)), dim3(256), 0, s,
+                     static_cast<const uint8_t*>(src), rows, ld * elem_bytes, prow, (int)pb, nchunks,
+                     static_cast<uint8_t*>(dst));
+  return hipGetLastError();
+}
+
 template hipError_t launch_attn_prologue<float>(float*, int64_t, int, int, float2*, int, int, int, int, float,
                                                 hipStream_t);
 template hipError_t launch_attn_prologue<bf16>(bf16*, int64_t, int, int, float2*, int, int, int, int, float,

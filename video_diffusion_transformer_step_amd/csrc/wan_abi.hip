@@ -114,7 +114,8 @@ int check_cfg(const wan_block_cfg* c) {
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(WAN_EUNSUPPORTED, "head_dim %d not supported (64 or 128)", c->head_dim);
   if (c->dim % 8 != 0 || c->dim > 6144) return fail(WAN_EUNSUPPORTED, "dim %d must be a multiple of 8 and <= 6144", c->dim);
-  if (c->ffn_dim <= 0 || c->ffn_dim % 8 != 0) return fail(WAN_EINVAL, "ffn_dim %d must be a positive multiple of 8", c->ffn_dim);
+  if (c->ffn_dim <= 0 || c->ffn_dim % 32 != 0)
+    return fail(WAN_EINVAL, "ffn_dim %d must be a positive multiple of 32", c->ffn_dim);
   if (c->text_len <= 0 || c->img_len < 0) return fail(WAN_EINVAL, "text_len must be > 0 and img_len >= 0");
   if (!(c->ln_eps >= 0.f) || !(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f))
     return fail(WAN_EINVAL, "eps must be >= 0 and rope_theta > 0");
@@ -214,10 +215,10 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
     const QKNormRope nr{W.gq, W.gk, w.ssq, w.rope, g.T, g.Hp, g.Wp};
     if (f8g) {  // E4M3 products ("Wan 技术深度解析" §5.3): per-token codes of u, then the product
       PROF_TRY(WAN_K_QUANT, launch_quant_rows_e4m3((const bf16*)w.u, dim, BS, dim, w.a8, dim, w.sa, st));
-      PROF_TRY(WAN_K_QKV_GEMM, gemm_qkv_e4m3(w.a8, dim, w.sa, (const uint8_t*)Q8->wqkv, dim, Q8->s_wqkv, BS, dim, dim,
+      PROF_TRY(WAN_K_QKV_GEMM, gemm_qkv_e4m3(w.a8, dim, w.sa, w_panels<uint8_t>(Q8->wqkv, 3 * dim), Q8->s_wqkv, BS, dim, dim,
                                              W.bqkv, (bf16*)w.qkv, 2 * dim, (bf16*)w.vt, S, H, hd, Spad, nr, st));
     } else {
-      PROF_TRY(WAN_K_QKV_GEMM, gemm_qkv<T>(w.u, dim, (const T*)W.wqkv, dim, BS, dim, dim, W.bqkv, w.qkv, 2 * dim, w.vt,
+      PROF_TRY(WAN_K_QKV_GEMM, gemm_qkv<T>(w.u, dim, w_panels<T>(W.wqkv, 3 * dim), BS, dim, dim, W.bqkv, w.qkv, 2 * dim, w.vt,
                                            S, H, hd, Spad, nr, st));
     }
     // the RMS factors: k rows scaled in place, r_q kept for the attention's score scale
@@ -240,17 +241,17 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
     }
     if (f8g) {
       PROF_TRY(WAN_K_QUANT, launch_quant_rows_e4m3((const bf16*)w.o, dim, BS, dim, w.a8, dim, w.sa, st));
-      PROF_TRY(WAN_K_O_GEMM, gemm_e4m3_residual(w.a8, dim, w.sa, (const uint8_t*)Q8->wo, dim, Q8->s_wo, BS, dim, dim, W.bo,
+      PROF_TRY(WAN_K_O_GEMM, gemm_e4m3_residual(w.a8, dim, w.sa, w_panels<uint8_t>(Q8->wo, dim), Q8->s_wo, BS, dim, dim, W.bo,
                                                 w.mod, 2, S, x, dim, st, ystore));
     } else {
-      PROF_TRY(WAN_K_O_GEMM, gemm_residual<T>(w.o, dim, (const T*)W.wo, dim, BS, dim, dim, W.bo, w.mod, 2, S, x,
+      PROF_TRY(WAN_K_O_GEMM, gemm_residual<T>(w.o, dim, w_panels<T>(W.wo, dim), BS, dim, dim, W.bo, w.mod, 2, S, x,
                                               dim, st, ystore));
     }
   }  // self-attention branch
   // cross-attention branch (no adaLN, no RoPE)
   PROF_TRY(WAN_K_LN3, launch_ln_mod<T>(x, BS, dim, S, 1, W.ln3_w, W.ln3_b, 0, 0, c.ln_eps, w.u, st));
   T* qc = w.qkv;  // reuse: [BS, dim]
-  PROF_TRY(WAN_K_CROSS_Q_GEMM, (gemm_store<T, T>(w.u, dim, (const T*)W.wcq, dim, BS, dim, dim, W.bcq, ACT_NONE, qc, dim, st)));
+  PROF_TRY(WAN_K_CROSS_Q_GEMM, (gemm_store<T, T>(w.u, dim, w_panels<T>(W.wcq, dim), BS, dim, dim, W.bcq, ACT_NONE, qc, dim, st)));
   const int Lt = c.text_len, Li = c.img_len;
   KVStream st_txt{kv.k_txt, (int64_t)Lt * dim, dim, kv.vt_txt, Lt, (int)pad64(Lt)};
   KVStream st_img{kv.k_img, (int64_t)Li * dim, dim, kv.vt_img, Li, (int)pad64(Li > 0 ? Li : 1)};
@@ -261,21 +262,21 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
   if (Li > 0)
     PROF_TRY(WAN_K_CROSS_ATTN, launch_attention<T>(qc, (int64_t)S * dim, dim, st_img, B, S, H, hd, scale,
                                                    w.o, (int64_t)S * dim, dim, 1, st, nullptr, KeySplit{}, true));
-  PROF_TRY(WAN_K_CROSS_O_GEMM, gemm_residual<T>(w.o, dim, (const T*)W.wco, dim, BS, dim, dim, W.bco, nullptr, 0, S, x, dim, st));
+  PROF_TRY(WAN_K_CROSS_O_GEMM, gemm_residual<T>(w.o, dim, w_panels<T>(W.wco, dim), BS, dim, dim, W.bco, nullptr, 0, S, x, dim, st));
   // FFN branch
   PROF_TRY(WAN_K_LN2, launch_ln_mod<T>(x, BS, dim, S, 0, w.mod, nullptr, 3, 4, c.ln_eps, w.u, st));
   if (f8g) {
     const int F = c.ffn_dim;
     PROF_TRY(WAN_K_QUANT, launch_quant_rows_e4m3((const bf16*)w.u, dim, BS, dim, w.a8, dim, w.sa, st));
-    PROF_TRY(WAN_K_FFN1_GEMM, gemm_e4m3_store(w.a8, dim, w.sa, (const uint8_t*)Q8->w1, dim, Q8->s_w1, BS, F, dim, W.b1,
+    PROF_TRY(WAN_K_FFN1_GEMM, gemm_e4m3_store(w.a8, dim, w.sa, w_panels<uint8_t>(Q8->w1, F), Q8->s_w1, BS, F, dim, W.b1,
                                               ACT_GELU, (bf16*)w.h, F, st));
     PROF_TRY(WAN_K_QUANT, launch_quant_rows_e4m3((const bf16*)w.h, F, BS, F, w.a8, F, w.sa, st));
-    PROF_TRY(WAN_K_FFN2_GEMM, gemm_e4m3_residual(w.a8, F, w.sa, (const uint8_t*)Q8->w2, F, Q8->s_w2, BS, dim, F, W.b2,
+    PROF_TRY(WAN_K_FFN2_GEMM, gemm_e4m3_residual(w.a8, F, w.sa, w_panels<uint8_t>(Q8->w2, dim), Q8->s_w2, BS, dim, F, W.b2,
                                                  w.mod, 5, S, x, dim, st));
   } else {
-    PROF_TRY(WAN_K_FFN1_GEMM, (gemm_store<T, T>(w.u, dim, (const T*)W.w1, dim, BS, c.ffn_dim, dim, W.b1, ACT_GELU, w.h,
+    PROF_TRY(WAN_K_FFN1_GEMM, (gemm_store<T, T>(w.u, dim, w_panels<T>(W.w1, c.ffn_dim), BS, c.ffn_dim, dim, W.b1, ACT_GELU, w.h,
                                                 c.ffn_dim, st)));
-    PROF_TRY(WAN_K_FFN2_GEMM, gemm_residual<T>(w.h, c.ffn_dim, (const T*)W.w2, c.ffn_dim, BS, dim, c.ffn_dim, W.b2, w.mod,
+    PROF_TRY(WAN_K_FFN2_GEMM, gemm_residual<T>(w.h, c.ffn_dim, w_panels<T>(W.w2, dim), BS, dim, c.ffn_dim, W.b2, w.mod,
                                                5, S, x, dim, st));
   }
   return WAN_OK;
@@ -401,9 +402,9 @@ int wan_patch_embed(const wan_block_cfg* cfg, const float* p, int64_t tokens, in
   if (cfg->dtype == WAN_BF16) {
     bf16* pb = reinterpret_cast<bf16*>(ws);
     HIP_TRY(launch_convert<bf16>(p, pb, (int64_t)M * K, hs(stream)));
-    HIP_TRY((gemm_store<bf16, float>(pb, K, (const bf16*)w_pe, K, M, cfg->dim, K, b_pe, ACT_NONE, x, cfg->dim, hs(stream))));
+    HIP_TRY((gemm_store<bf16, float>(pb, K, w_rows<bf16>(w_pe, K), M, cfg->dim, K, b_pe, ACT_NONE, x, cfg->dim, hs(stream))));
   } else {
-    HIP_TRY((gemm_store<float, float>(p, K, (const float*)w_pe, K, M, cfg->dim, K, b_pe, ACT_NONE, x, cfg->dim, hs(stream))));
+    HIP_TRY((gemm_store<float, float>(p, K, w_rows<float>(w_pe, K), M, cfg->dim, K, b_pe, ACT_NONE, x, cfg->dim, hs(stream))));
   }
   return WAN_OK;
 }
@@ -449,8 +450,8 @@ template <typename T>
 static int context_embed_t(const wan_block_cfg& c, const void* ctx, int rows, int in_dim, const void* w1,
                            const float* b1, const void* w2, const float* b2, void* out, void* ws, hipStream_t st) {
   T* hid = reinterpret_cast<T*>(ws);
-  HIP_TRY((gemm_store<T, T>((const T*)ctx, in_dim, (const T*)w1, in_dim, rows, c.dim, in_dim, b1, ACT_GELU, hid, c.dim, st)));
-  HIP_TRY((gemm_store<T, T>(hid, c.dim, (const T*)w2, c.dim, rows, c.dim, c.dim, b2, ACT_NONE, (T*)out, c.dim, st)));
+  HIP_TRY((gemm_store<T, T>((const T*)ctx, in_dim, w_rows<T>(w1, in_dim), rows, c.dim, in_dim, b1, ACT_GELU, hid, c.dim, st)));
+  HIP_TRY((gemm_store<T, T>(hid, c.dim, w_rows<T>(w2, c.dim), rows, c.dim, c.dim, b2, ACT_NONE, (T*)out, c.dim, st)));
   return WAN_OK;
 }
 
@@ -504,8 +505,8 @@ static int cross_kv_t(const wan_block_cfg& c, const wan_cross_kv_weights& w, con
     T* k = (T*)(which == 0 ? out.k_txt : out.k_img);
     T* vt = (T*)(which == 0 ? out.vt_txt : out.vt_img);
     const int M = B * L;
-    HIP_TRY((gemm_store<T, T>(ctx, dim, wkv, dim, M, dim, dim, bkv, ACT_NONE, k, dim, st)));
-    HIP_TRY((gemm_store<T, T>(ctx, dim, wkv + (int64_t)dim * dim, dim, M, dim, dim, bkv ? bkv + dim : nullptr,
+    HIP_TRY((gemm_store<T, T>(ctx, dim, w_rows<T>(wkv, dim), M, dim, dim, bkv, ACT_NONE, k, dim, st)));
+    HIP_TRY((gemm_store<T, T>(ctx, dim, w_rows<T>(wkv + (int64_t)dim * dim, dim), M, dim, dim, bkv ? bkv + dim : nullptr,
                               ACT_NONE, tmp, dim, st)));
     HIP_TRY(launch_transpose_heads<T>(tmp, dim, 0, B, L, c.heads, c.head_dim, (int)pad64(L), vt, st));
   }
@@ -637,11 +638,11 @@ int wan_head_fwd(const wan_block_cfg* cfg, const wan_head_weights* w, int32_t ou
   if (cfg->dtype == WAN_BF16) {
     bf16* u = reinterpret_cast<bf16*>(ws);
     HIP_TRY(launch_ln_mod<bf16>(x, rows, dim, S, 2, w->head_mod, e, 0, 1, cfg->ln_eps, u, st));
-    HIP_TRY((gemm_store<bf16, float>(u, dim, (const bf16*)w->wh, dim, (int)rows, N, dim, w->bh, ACT_NONE, out, N, st)));
+    HIP_TRY((gemm_store<bf16, float>(u, dim, w_rows<bf16>(w->wh, dim), (int)rows, N, dim, w->bh, ACT_NONE, out, N, st)));
   } else {
     float* u = reinterpret_cast<float*>(ws);
     HIP_TRY(launch_ln_mod<float>(x, rows, dim, S, 2, w->head_mod, e, 0, 1, cfg->ln_eps, u, st));
-    HIP_TRY((gemm_store<float, float>(u, dim, (const float*)w->wh, dim, (int)rows, N, dim, w->bh, ACT_NONE, out, N, st)));
+    HIP_TRY((gemm_store<float, float>(u, dim, w_rows<float>(w->wh, dim), (int)rows, N, dim, w->bh, ACT_NONE, out, N, st)));
   }
   return WAN_OK;
 }
@@ -927,13 +928,28 @@ int wan_quantize_tensor_e4m3(const void* x, int64_t n, void* codes, float* scale
   return WAN_OK;
 }
 
-int wan_gemm_e4m3(const void* a, int64_t lda, const float* a_scales, const void* w, int64_t ldw, const float* w_scale,
+size_t wan_pack_weight_bytes(int32_t elem_bytes, int64_t N, int64_t K) {
+  if ((elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4) || N <= 0 || K <= 0 || K % 32 != 0) return 0;
+  return (size_t)panel_rows(N) * (size_t)K * (size_t)elem_bytes;
+}
+
+int wan_pack_weight(int32_t elem_bytes, const void* w, int64_t N, int64_t K, void* packed, wan_stream_t stream) {
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4) return fail(WAN_EINVAL, "elem_bytes must be 1, 2 or 4");
+  if (N <= 0 || K <= 0 || K % 32 != 0) return fail(WAN_EINVAL, "N > 0 and K a positive multiple of 32");
+  WAN_TRY(need_ptr(w, "w"));
+  WAN_TRY(need_ptr(packed, "packed"));
+  HIP_TRY(launch_pack_panels(w, N, K, K, elem_bytes, packed, hs(stream)));
+  return WAN_OK;
+}
+
+int wan_gemm_e4m3(const void* a, int64_t lda, const float* a_scales, const void* w, const float* w_scale,
                   int32_t M, int32_t N, int32_t K, const float* bias, int32_t act, void* y, int64_t ldy,
                   wan_stream_t stream) {
   if (M <= 0 || N <= 0 || N % 4 != 0) return fail(WAN_EINVAL, "M > 0 and N a positive multiple of 4");
   if (K <= 0 || K % 256 != 0) return fail(WAN_EUNSUPPORTED, "K %d must be a positive multiple of 256", K);
-  if (lda < K || ldw < K || lda % 16 != 0 || ldw % 16 != 0 || ldy < N || ldy % 4 != 0)
-    return fail(WAN_EINVAL, "bad row strides");
+  if (lda < K || lda % 16 != 0 || ldy < N || ldy % 4 != 0) return fail(WAN_EINVAL, "bad row strides");
+  if ((int64_t)K * panel_rows(N) >= ((int64_t)1 << 31)) return fail(WAN_EUNSUPPORTED, "W panels of 2 GiB or more");
+  if ((int64_t)256 * lda >= ((int64_t)1 << 31)) return fail(WAN_EUNSUPPORTED, "lda too large");
   if (act != ACT_NONE && act != ACT_GELU) return fail(WAN_EINVAL, "act must be 0 or 1");
   WAN_TRY(need_ptr(a, "a"));
   WAN_TRY(need_ptr(w, "w"));
@@ -941,7 +957,7 @@ int wan_gemm_e4m3(const void* a, int64_t lda, const float* a_scales, const void*
   WAN_TRY(need_f32(w_scale, "w_scale"));
   WAN_TRY(opt_ptr(bias, "bias"));
   WAN_TRY(need_ptr(y, "y"));
-  HIP_TRY(gemm_e4m3_store((const uint8_t*)a, lda, a_scales, (const uint8_t*)w, ldw, w_scale, M, N, K, bias, act,
+  HIP_TRY(gemm_e4m3_store((const uint8_t*)a, lda, a_scales, w_panels<uint8_t>(w, N), w_scale, M, N, K, bias, act,
                           (bf16*)y, ldy, hs(stream)));
   return WAN_OK;
 }

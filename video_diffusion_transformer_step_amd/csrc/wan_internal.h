@@ -75,15 +75,43 @@ hipError_t launch_qk_rms(const float* ssq, int64_t rows, int dim, float eps, T* 
                          hipStream_t s);
 
 // ---- GEMM (gemm.hip) --------------------------------------------------------
-// C[m, n] = sum_k A[m, k] * W[n, k]   (A [M, K] row-major, W [N, K] row-major)
+// A weight operand W [N, K]: row-major with row stride ld (panel == 0), or in K panels of 32 elements
+// (panel > 0, the rows of each panel: N rounded up to a multiple of 256): element (n, k) at
+// ((k / 32) * panel + n) * 32 + k % 32, rows N .. panel - 1 zero (launch_pack_panels writes it).  In
+// panels, the 32-deep K step of a 256-row weight tile is one contiguous run of whole cache lines.
+template <typename T>
+struct WMat {
+  const T* p;
+  int64_t ld;
+  int64_t panel;
+};
+inline int64_t panel_rows(int64_t N) { return (N + 255) / 256 * 256; }
+template <typename T>
+inline WMat<T> w_rows(const void* p, int64_t ld) {
+  return WMat<T>{static_cast<const T*>(p), ld, 0};
+}
+template <typename T>
+inline WMat<T> w_panels(const void* p, int64_t N) {
+  return WMat<T>{static_cast<const T*>(p), 0, panel_rows(N)};
+}
+template <typename T>
+inline bool w_panels_ok(const WMat<T>& w, int64_t N, int64_t K) {
+  return w.panel >= N && w.panel % 256 == 0 && K % 32 == 0;
+}
+// Row-major [rows, cols] of elem_bytes-byte elements (row stride ld elements) -> K panels of 32
+// ([cols / 32][panel_rows(rows)][32], zero rows past `rows`).  cols % 32 == 0, ld * elem_bytes % 16 == 0.
+hipError_t launch_pack_panels(const void* src, int64_t rows, int64_t cols, int64_t ld, int elem_bytes, void* dst,
+                              hipStream_t s);
+
+// C[m, n] = sum_k A[m, k] * W[n, k]   (A [M, K] row-major, W [N, K] as a WMat)
 // Epilogues:
 //   store:      out[m, n] = act(C + bias[n])  (OutT = T or float)
 //   residual:   x[m, n] += g(m, n) * (C + bias[n]), g = gate[m / S][chunk][n] from a [B, 6, N] table
 //               (the block's e0 + modulation bias), or 1 if gate is null; ystore (optional, row stride N)
 //               also receives C + bias.
 template <typename T, typename OutT>
-hipError_t gemm_store(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const float* bias,
-                      int act, OutT* out, int64_t ldo, hipStream_t s);
+hipError_t gemm_store(const T* A, int64_t lda, WMat<T> W, int M, int N, int K, const float* bias, int act, OutT* out,
+                      int64_t ldo, hipStream_t s);
 // Q/K/V projection (N = 3 dim): q, k columns to qk[m, 0 .. 2 dim) (row stride ldo), v columns to
 // V^T [B, H, hd, Spad] (keys permuted within 16-key groups for bf16; see launch_transpose_heads);
 // m = b * S + pos.  Only keys pos < S are written: the positions of keys S .. Spad - 1 are left as they
@@ -104,23 +132,23 @@ struct QKNormRope {
   int T, Hp, Wp;
 };
 template <typename T>
-hipError_t gemm_qkv(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int dim, int K, const float* bias,
+hipError_t gemm_qkv(const T* A, int64_t lda, WMat<T> W, int M, int dim, int K, const float* bias,
                     T* qk, int64_t ldo, T* vt, int S, int H, int hd, int Spad, const QKNormRope& nr,
                     hipStream_t s);
 template <typename T>
-hipError_t gemm_residual(const T* A, int64_t lda, const T* W, int64_t ldw, int M, int N, int K, const float* bias,
+hipError_t gemm_residual(const T* A, int64_t lda, WMat<T> W, int M, int N, int K, const float* bias,
                          const float* gate, int chunk, int S, float* x, int64_t ldx, hipStream_t s,
                          float* ystore = nullptr);
 // E4M3 products: C = (sum_k A[m, k] W[n, k]) * a_scales[m] * w_scale[0] over E4M3 codes (A row stride
-// lda bytes, W row stride ldw bytes, K % 256 == 0, strides % 16 == 0), then the store (bf16 out, act
-// NONE or GELU) or residual epilogue.
-hipError_t gemm_e4m3_store(const uint8_t* A, int64_t lda, const float* a_scales, const uint8_t* W, int64_t ldw,
+// lda bytes, a multiple of 16; W in K panels; K % 256 == 0), then the store (bf16 out, act NONE or GELU)
+// or residual epilogue.
+hipError_t gemm_e4m3_store(const uint8_t* A, int64_t lda, const float* a_scales, WMat<uint8_t> W,
                            const float* w_scale, int M, int N, int K, const float* bias, int act, bf16* out,
                            int64_t ldo, hipStream_t s);
-hipError_t gemm_e4m3_residual(const uint8_t* A, int64_t lda, const float* a_scales, const uint8_t* W, int64_t ldw,
+hipError_t gemm_e4m3_residual(const uint8_t* A, int64_t lda, const float* a_scales, WMat<uint8_t> W,
                               const float* w_scale, int M, int N, int K, const float* bias, const float* gate,
                               int chunk, int S, float* x, int64_t ldx, hipStream_t s, float* ystore = nullptr);
-hipError_t gemm_qkv_e4m3(const uint8_t* A, int64_t lda, const float* a_scales, const uint8_t* W, int64_t ldw,
+hipError_t gemm_qkv_e4m3(const uint8_t* A, int64_t lda, const float* a_scales, WMat<uint8_t> W,
                          const float* w_scale, int M, int dim, int K, const float* bias, bf16* qk, int64_t ldo, bf16* vt,
                          int S, int H, int hd, int Spad, const QKNormRope& nr, hipStream_t s);
 // y[b, n] = out_act(sum_k W[n, k] * in_act(x[b, k]) + bias[n]) for b < B (fp32 x, y).

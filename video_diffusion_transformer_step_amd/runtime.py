@@ -50,8 +50,13 @@ def cfg_of(c, dtype=None, fp8_attn=False, fp8_gemm=False):
                        L.WAN_BF16 if d == "bf16" else L.WAN_F32, c.ln_eps, c.rms_eps, c.rope_theta, flags)
 
 
+# The block matrices the products read in K panels (wan_pack_weight), packed once at set-up.
+PANEL_MATRICES = ("wqkv", "wo", "wcq", "wco", "w1", "w2")
+
+
 class DeviceBlock:
-    """One block's weights on the device + its BlockWeights / CrossKVWeights structs."""
+    """One block's weights on the device + its BlockWeights / CrossKVWeights structs.  The six product
+    matrices are held in K panels only (the row-major tensors passed in are not kept)."""
 
     def __init__(self, w: dict, dtype: str, device="cuda", tensors=None):
         wd = _dt(dtype)
@@ -71,6 +76,9 @@ class DeviceBlock:
             if "wki" in w:
                 g["wkv_img"] = to_dev(np.concatenate([w["wki"], w["wvi"]]), wd, device)
                 g["bkv_img"] = to_dev(np.concatenate([w["bki"], w["bvi"]]), torch.float32, device)
+        g = dict(g)
+        for n in PANEL_MATRICES:
+            g[n] = L.pack_weight(g[n].contiguous())
         self.bw = L.BlockWeights(*[k.put(n, g[n]) for n in (
             "mod_bias", "wqkv", "bqkv", "gq", "gk", "wo", "bo", "ln3_w", "ln3_b", "wcq", "bcq", "wco", "bco",
             "w1", "b1", "w2", "b2")])
@@ -79,8 +87,9 @@ class DeviceBlock:
         self._keep = k
 
     def enable_e4m3(self):
-        """E4M3 codes of wqkv, wo, w1, w2 with one scale each (wan_quantize_tensor_e4m3), linked into bw
-        for WAN_FLAG_FP8_GEMM.  bf16 blocks only."""
+        """E4M3 codes of wqkv, wo, w1, w2 with one scale each (wan_quantize_tensor_e4m3 of the packed
+        matrices: per-element codes of packed values are the packed codes), linked into bw for
+        WAN_FLAG_FP8_GEMM.  bf16 blocks only."""
         k = self._keep
         ws = torch.empty(256, dtype=torch.uint8, device=k.t["wqkv"].device)
         ptrs, scales = [], []
