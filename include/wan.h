@@ -78,7 +78,7 @@ typedef struct {
   float ln_eps, rms_eps, rope_theta;
 } wan_block_cfg;
 
-/* K panels: the weight layout of the block's products.  A matrix W [N, K] (y = x W^T) is stored as
+/* K panels: the operand layout of the block's products.  A matrix W [N, K] (y = x W^T) is stored as
  * K / 32 panels, each holding 32 consecutive k of every row n: element (n, k) at
  * ((k / 32) * Np + n) * 32 + k % 32, where Np = N rounded up to a multiple of 256 and rows N .. Np - 1
  * are zero.  wan_pack_weight_bytes(elem_bytes, N, K) = Np * K * elem_bytes (0 for invalid sizes:
@@ -224,9 +224,11 @@ int wan_cross_kv_fwd(const wan_block_cfg* cfg, const wan_cross_kv_weights* w, co
  *   x += gate2 * FFN(LN(x)(1 + scale2) + shift2),  FFN = Linear -> GELU -> Linear
  * e0 [B, 6, dim] float32 from wan_time_embed; kv from wan_cross_kv_fwd.  LN has no affine (except the
  * cross-attention pre-norm), eps = cfg->ln_eps; attention scale 1/sqrt(head_dim).
- * Workspace: wan_dit_block_workspace_bytes() (about B*S*(5*dim + ffn_dim) dtype elements, plus
- * B*S*(dim/16 + 1) float32 of Q/K sums of squares and query scales, 6*B*dim float32 of
- * modulation and the RoPE table's (T + Hp + Wp) * head_dim/2 or fewer float2). */
+ * Workspace: wan_dit_block_workspace_bytes() (about B*S*(5*dim + ffn_dim) dtype elements, the
+ * products' inputs (LayerNorm outputs, attention outputs, FFN hidden state) held in K panels of
+ * B*S rounded up to 256 rows; plus B*S*(dim/16 + 1) float32 of Q/K sums of squares and query
+ * scales, 6*B*dim float32 of modulation and the RoPE table's (T + Hp + Wp) * head_dim/2 or fewer
+ * float2). */
 size_t wan_dit_block_workspace_bytes(const wan_block_cfg* cfg, wan_grid grid, int32_t B);
 int wan_dit_block_fwd(const wan_block_cfg* cfg, const wan_block_weights* w, wan_grid grid, int32_t B, float* x,
                       const float* e0, const wan_cross_kv* kv, void* ws, size_t ws_bytes, wan_stream_t stream);
@@ -347,16 +349,15 @@ int wan_attention_q8_fwd(const void* q8, const float* sq, const void* k8, const 
  * wan_quantize_tensor_e4m3: x [n] bf16 (n % 8 == 0) -> codes [n] and one float32 scale, both on the
  *   device; ws: at least 256 bytes of device scratch.
  * wan_gemm_e4m3: y [M, N] bf16 (row stride ldy elements) = act((A W^T) * a_scales[m] * w_scale[0] + bias[n])
- *   from codes A [M, K] (row stride lda bytes, % 16 == 0) and W [N, K] in K panels (wan_pack_weight,
- *   elem_bytes 1); K % 256 == 0, N % 4 == 0, ldy % 4 == 0; act 0 = none, 1 = GELU (erf); bias may be
- *   NULL.  WAN_EUNSUPPORTED when the panels reach 2 GiB. */
+ *   from codes A [M, K] and W [N, K], both in K panels (wan_pack_weight with elem_bytes 1: rows M and
+ *   N rounded up to 256); K % 256 == 0, N % 4 == 0, ldy % 4 == 0; act 0 = none, 1 = GELU (erf); bias
+ *   may be NULL.  WAN_EUNSUPPORTED when either operand's panels reach 2 GiB. */
 int wan_quantize_rows_e4m3(const void* x, int64_t ld, int32_t rows, int32_t cols, void* codes, int64_t ldc,
                            float* scales, wan_stream_t stream);
 int wan_quantize_tensor_e4m3(const void* x, int64_t n, void* codes, float* scale, void* ws, size_t ws_bytes,
                              wan_stream_t stream);
-int wan_gemm_e4m3(const void* a, int64_t lda, const float* a_scales, const void* w, const float* w_scale,
-                  int32_t M, int32_t N, int32_t K, const float* bias, int32_t act, void* y, int64_t ldy,
-                  wan_stream_t stream);
+int wan_gemm_e4m3(const void* a, const float* a_scales, const void* w, const float* w_scale, int32_t M, int32_t N,
+                  int32_t K, const float* bias, int32_t act, void* y, int64_t ldy, wan_stream_t stream);
 
 /* Kernel timing (measurement only).  wan_profile_begin hands the library `capacity` caller-created
  * HIP events (hipEvent_t, passed as void*) for starts and stops plus an int32 tag array; until

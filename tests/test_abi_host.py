@@ -182,10 +182,12 @@ def test_weight_panel_sizes_and_validation(lib):
     assert lib.wan_pack_weight(2, None, 256, 64, FAKE, None) == L.WAN_EINVAL
     assert lib.wan_pack_weight(2, FAKE, 256, 64, FAKE + 8, None) == L.WAN_EINVAL
     # E4M3 product: K % 256, and the panels must stay below 2 GiB
-    assert lib.wan_gemm_e4m3(FAKE, 512, FAKE, FAKE, FAKE, 64, 256, 384, None, 0, FAKE, 256, None) \
+    assert lib.wan_gemm_e4m3(FAKE, FAKE, FAKE, FAKE, 64, 256, 384, None, 0, FAKE, 256, None) == L.WAN_EUNSUPPORTED
+    assert lib.wan_gemm_e4m3(FAKE, FAKE, FAKE, FAKE, 64, 1 << 17, 1 << 17, None, 0, FAKE, 1 << 17, None) \
         == L.WAN_EUNSUPPORTED
-    assert lib.wan_gemm_e4m3(FAKE, 1 << 17, FAKE, FAKE, FAKE, 64, 1 << 17, 1 << 17, None, 0, FAKE, 1 << 17,
-                             None) == L.WAN_EUNSUPPORTED
+    assert lib.wan_gemm_e4m3(FAKE, FAKE, FAKE, FAKE, 1 << 17, 256, 1 << 14, None, 0, FAKE, 256, None) \
+        == L.WAN_EUNSUPPORTED
+    assert lib.wan_gemm_e4m3(FAKE, FAKE, FAKE, FAKE, 64, 256, 256, None, 0, FAKE, 255, None) == L.WAN_EINVAL
 
 
 def test_ring_attention_validation(lib):

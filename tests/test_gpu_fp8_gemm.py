@@ -79,7 +79,7 @@ def test_gemm_e4m3_small(M, N, K, act):
     xc, xs = _rows_quant(dev(x, torch.bfloat16))
     wc, wsc = _tensor_quant(dev(w, torch.bfloat16))
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    L.gemm_e4m3(xc, xs, L.pack_weight(wc), wsc, y, bias=dev(bias), act=act)
+    L.gemm_e4m3(L.pack_weight(xc), xs, L.pack_weight(wc), wsc, y, K, bias=dev(bias), act=act)
     _check_gemm(x, w, bias, act, host(y))
 
 
@@ -97,7 +97,7 @@ def test_gemm_e4m3_ffn_shapes(N, K, act):
     xc, xs = _rows_quant(xd)
     wc, wsc = _tensor_quant(wd)
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    L.gemm_e4m3(xc, xs, L.pack_weight(wc), wsc, y, bias=bias, act=act)
+    L.gemm_e4m3(L.pack_weight(xc), xs, L.pack_weight(wc), wsc, y, K, bias=bias, act=act)
     rows = np.unique(np.concatenate([[0, 255, 256, M - 1], np.random.default_rng(5).choice(M, 28, replace=False)]))
     rt = torch.from_numpy(rows).cuda()
     _check_gemm(host(xd[rt]).astype(np.float32), host(wd).astype(np.float32), host(bias), act, host(y[rt]))

@@ -100,8 +100,8 @@ _SIGS = {
                               vp], C.c_int),
     "wan_quantize_rows_e4m3": ([vp, C.c_int64, C.c_int32, C.c_int32, vp, C.c_int64, vp, vp], C.c_int),
     "wan_quantize_tensor_e4m3": ([vp, C.c_int64, vp, vp, vp, C.c_size_t, vp], C.c_int),
-    "wan_gemm_e4m3": ([vp, C.c_int64, vp, vp, vp, C.c_int32, C.c_int32, C.c_int32, vp, C.c_int32, vp,
-                       C.c_int64, vp], C.c_int),
+    "wan_gemm_e4m3": ([vp, vp, vp, vp, C.c_int32, C.c_int32, C.c_int32, vp, C.c_int32, vp, C.c_int64, vp],
+                      C.c_int),
     "wan_pack_weight_bytes": ([C.c_int32, C.c_int64, C.c_int64], C.c_size_t),
     "wan_pack_weight": ([C.c_int32, vp, C.c_int64, C.c_int64, vp, vp], C.c_int),
     "wan_profile_begin": ([C.POINTER(C.c_void_p), C.POINTER(C.c_void_p), C.POINTER(C.c_int32), C.c_int32,
@@ -363,17 +363,16 @@ def quantize_tensor_e4m3(x, codes, scale, ws, stream=None):
            "wan_quantize_tensor_e4m3")
 
 
-def gemm_e4m3(a_codes, a_scales, w_panels, w_scale, y, bias=None, act=0, stream=None):
-    """y [M, N] from A codes [M, K] and W codes in K panels (pack_weight of the [N, K] codes)."""
-    M, K = a_codes.shape
-    N = y.shape[1]
-    _check(lib().wan_gemm_e4m3(_p(a_codes), a_codes.stride(0), _p(a_scales), _p(w_panels), _p(w_scale), M, N, K,
-                               _p(bias), act, _p(y), y.stride(0), _stream(stream)),
+def gemm_e4m3(a_panels, a_scales, w_panels, w_scale, y, K, bias=None, act=0, stream=None):
+    """y [M, N] from A codes and W codes, each in K panels (pack_weight of the [M, K] / [N, K] codes)."""
+    M, N = y.shape
+    _check(lib().wan_gemm_e4m3(_p(a_panels), _p(a_scales), _p(w_panels), _p(w_scale), M, N, K, _p(bias), act,
+                               _p(y), y.stride(0), _stream(stream)),
            "wan_gemm_e4m3")
 
 
 def pack_weight(w, stream=None):
-    """A row-major weight w [N, K] (bf16, float32 or uint8 E4M3 codes, contiguous) in K panels
+    """A row-major operand w [R, K] (bf16, float32 or uint8 E4M3 codes, contiguous) in K panels
     (wan_pack_weight): a new flat tensor of w's dtype, wan_pack_weight_bytes(...) bytes."""
     import torch
     N, K = w.shape

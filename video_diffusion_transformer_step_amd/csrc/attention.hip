@@ -649,39 +649,41 @@ __device__ __forceinline__ void write_lse(const SoftState& st, float* __restrict
     lse[((int64_t)b * H + h) * S + qrow] = (st.m + log2f(l)) * 0.69314718055994531f;
 }
 
-// Write the wave's O rows (lane: query qrow, d = 32 dblk + 8 g + 4 lhalf + 0..3).
-template <typename T, int HD>
+// Write the wave's O rows (lane: query qrow, d = 32 dblk + 8 g + 4 lhalf + 0..3).  Output channel
+// n = h HD + d of query row (b, qrow) sits at out + b o_bs + qrow o_ss + (n / 32) o_cs + n % 32
+// (row-major: o_cs = 32; the products' K panels: o_ss = 32, o_cs = 32 * rows per panel).
 // add: the rows are added to what out holds (a second key/value stream's launch adding to the first's
 // result), in fp32 before the store's rounding.
+template <typename T, int HD>
 __device__ __forceinline__ void store_rows(const f32x16 (&acc)[AttnCfg<T, HD>::ND], T* __restrict__ out,
-                                           int64_t o_bs, int64_t o_ss, int b, int h, int qrow, int S,
+                                           int64_t o_bs, int64_t o_ss, int64_t o_cs, int b, int h, int qrow, int S,
                                            bool add = false) {
   const int lhalf = (threadIdx.x & 63) >> 5;
   if (qrow >= S) return;
-  T* op = out + (int64_t)b * o_bs + (int64_t)qrow * o_ss + (int64_t)h * HD;
+  T* op0 = out + (int64_t)b * o_bs + (int64_t)qrow * o_ss + (int64_t)h * (HD / 32) * o_cs;
 #pragma unroll
   for (int d = 0; d < AttnCfg<T, HD>::ND; ++d)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int dd = d * 32 + g * 8 + lhalf * 4;
+      T* op = op0 + d * o_cs + g * 8 + lhalf * 4;  // channels 32 d + 8 g + 4 lhalf .. + 3 of the head
       if constexpr (sizeof(T) == 2) {
         bf16x4 v;
         if (add) {
-          const bf16x4 old = *reinterpret_cast<const bf16x4*>(op + dd);
+          const bf16x4 old = *reinterpret_cast<const bf16x4*>(op);
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[i] = (bf16)((float)old[i] + acc[d][4 * g + i]);
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[i] = (bf16)acc[d][4 * g + i];
         }
-        *reinterpret_cast<bf16x4*>(op + dd) = v;
+        *reinterpret_cast<bf16x4*>(op) = v;
       } else {
         float4 v = make_float4(acc[d][4 * g], acc[d][4 * g + 1], acc[d][4 * g + 2], acc[d][4 * g + 3]);
         if (add) {
-          const float4 old = *reinterpret_cast<const float4*>(op + dd);
+          const float4 old = *reinterpret_cast<const float4*>(op);
           v = make_float4(old.x + v.x, old.y + v.y, old.z + v.z, old.w + v.w);
         }
-        *reinterpret_cast<float4*>(op + dd) = v;
+        *reinterpret_cast<float4*>(op) = v;
       }
     }
 }
@@ -709,8 +711,8 @@ template <typename T, int HD, int KIND>
 __global__ __launch_bounds__(256, 2) void attention_kernel(const T* __restrict__ q, int64_t q_bs, int64_t q_ss,
                                                             KVStream kv, int S, int H, float c_log2,
                                                             const float* __restrict__ qscale, T* __restrict__ out,
-                                                            int64_t o_bs, int64_t o_ss, float* __restrict__ lse,
-                                                            KeySplit ks, int accum) {
+                                                            int64_t o_bs, int64_t o_ss, int64_t o_cs,
+                                                            float* __restrict__ lse, KeySplit ks, int accum) {
   using C = AttnCfg<T, HD>;
   __shared__ u32x4 k0_raw[C::KBYTES / 16], k1_raw[C::KBYTES / 16], v0_raw[C::VBYTES / 16], v1_raw[C::VBYTES / 16];
   const Slots<T, HD> sl{reinterpret_cast<char*>(k0_raw), reinterpret_cast<char*>(k1_raw),
@@ -734,7 +736,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const T* __restrict__
   attend_stream<T, HD>(qf, fa, kv, b, h, H, cq, sl, o, st);
   finish_stream<T, HD>(o, st, acc);
   if (lse != nullptr) write_lse(st, lse, b, h, H, qrow, S);
-  store_rows<T, HD>(acc, out, o_bs, o_ss, b, h, qrow, S, accum != 0);
+  store_rows<T, HD>(acc, out, o_bs, o_ss, o_cs, b, h, qrow, S, accum != 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -845,7 +847,7 @@ __global__ __launch_bounds__(512, 1) void attention_pp_kernel(const T* __restric
                                                                KVStream kv, int S, int H, float c_log2,
                                                                const float* __restrict__ qscale,
                                                                T* __restrict__ out, int64_t o_bs, int64_t o_ss,
-                                                               float* __restrict__ lse, KeySplit ks) {
+                                                               int64_t o_cs, float* __restrict__ lse, KeySplit ks) {
   using C = AttnCfg<T, HD>;
   __shared__ u32x4 k0_raw[C::KBYTES / 16], k1_raw[C::KBYTES / 16], v0_raw[C::VBYTES / 16], v1_raw[C::VBYTES / 16];
   const Slots<T, HD> sl{reinterpret_cast<char*>(k0_raw), reinterpret_cast<char*>(k1_raw),
@@ -871,7 +873,7 @@ __global__ __launch_bounds__(512, 1) void attention_pp_kernel(const T* __restric
   attend_stream_pp<T, HD>(qf, fa, kv, b, h, H, grp, cq, sl, o, st);
   finish_stream<T, HD>(o, st, acc);
   if (lse != nullptr) write_lse(st, lse, b, h, H, qrow, S);
-  store_rows<T, HD>(acc, out, o_bs, o_ss, b, h, qrow, S);
+  store_rows<T, HD>(acc, out, o_bs, o_ss, o_cs, b, h, qrow, S);
 }
 
 // ---------------------------------------------------------------------------
@@ -1104,7 +1106,8 @@ __global__ __launch_bounds__(512, 1) void attention_q8_kernel(const uint8_t* __r
                                                               int64_t q_ss, const float* __restrict__ sq, KVq8 kv,
                                                               int S, int H, float c_log2,
                                                               const float* __restrict__ qscale, bf16* __restrict__ out,
-                                                              int64_t o_bs, int64_t o_ss, float* __restrict__ lse) {
+                                                              int64_t o_bs, int64_t o_ss, int64_t o_cs,
+                                                              float* __restrict__ lse) {
   using C = AttnCfg<uint8_t, HD>;
   using CP = CopyPlan<uint8_t, HD, 8>;
   __shared__ u32x4 k0_raw[C::KBYTES / 16], k1_raw[C::KBYTES / 16], v0_raw[C::VBYTES / 16], v1_raw[C::VBYTES / 16];
@@ -1167,16 +1170,16 @@ __global__ __launch_bounds__(512, 1) void attention_q8_kernel(const uint8_t* __r
       acc[d][4 * g + 2] = o[d][4 * g + 2] * inv * sc.z;
       acc[d][4 * g + 3] = o[d][4 * g + 3] * inv * sc.w;
     }
-  store_rows<bf16, HD>(acc, out, o_bs, o_ss, b, h, qrow, S);
+  store_rows<bf16, HD>(acc, out, o_bs, o_ss, o_cs, b, h, qrow, S);
 }
 
 template <int HD>
 hipError_t launch_q8_hd(const uint8_t* q, int64_t q_bs, int64_t q_ss, const float* sq, const KVq8& kv, int B, int S,
-                        int H, float c_log2, const float* qscale, bf16* o, int64_t o_bs, int64_t o_ss, float* lse,
-                        hipStream_t s) {
+                        int H, float c_log2, const float* qscale, bf16* o, int64_t o_bs, int64_t o_ss, int64_t o_cs,
+                        float* lse, hipStream_t s) {
   dim3 grid((unsigned)ceil_div(S, 256), (unsigned)H, (unsigned)B);
   hipLaunchKernelGGL((attention_q8_kernel<HD>), grid, dim3(512), 0, s, q, q_bs, q_ss, sq, kv, S, H, c_log2, qscale, o,
-                     o_bs, o_ss, lse);
+                     o_bs, o_ss, o_cs, lse);
   return hipGetLastError();
 }
 
@@ -1185,16 +1188,16 @@ hipError_t launch_q8_hd(const uint8_t* q, int64_t q_bs, int64_t q_ss, const floa
 // hundred keys, where the per-stream prologue dominates) and fp32 use the four-wave kernel.
 template <typename T, int HD, int KIND>
 hipError_t launch_hd(const T* q, int64_t q_bs, int64_t q_ss, KVStream kv, int B, int S, int H, float c_log2,
-                     const float* qscale, T* o, int64_t o_bs, int64_t o_ss, float* lse, const KeySplit& ks, int accum,
-                     hipStream_t s) {
+                     const float* qscale, T* o, int64_t o_bs, int64_t o_ss, int64_t o_cs, float* lse, const KeySplit& ks,
+                     int accum, hipStream_t s) {
   if constexpr (sizeof(T) == 2 && KIND == 0) {
     dim3 grid((unsigned)ceil_div(S, 256), (unsigned)H, (unsigned)(B * ks.n));
     hipLaunchKernelGGL((attention_pp_kernel<T, HD, KIND>), grid, dim3(512), 0, s, q, q_bs, q_ss, kv, S, H, c_log2,
-                       qscale, o, o_bs, o_ss, lse, ks);
+                       qscale, o, o_bs, o_ss, o_cs, lse, ks);
   } else {
     dim3 grid((unsigned)ceil_div(S, 128), (unsigned)H, (unsigned)(B * ks.n));
     hipLaunchKernelGGL((attention_kernel<T, HD, KIND>), grid, dim3(256), 0, s, q, q_bs, q_ss, kv, S, H, c_log2,
-                       qscale, o, o_bs, o_ss, lse, ks, accum);
+                       qscale, o, o_bs, o_ss, o_cs, lse, ks, accum);
   }
   return hipGetLastError();
 }
@@ -1204,7 +1207,7 @@ hipError_t launch_hd(const T* q, int64_t q_bs, int64_t q_ss, KVStream kv, int B,
 template <typename T>
 hipError_t launch_attention(const T* q, int64_t q_bs, int64_t q_ss, KVStream kv, int B, int S, int H, int hd,
                             float scale, T* o, int64_t o_bs, int64_t o_ss, int kind, hipStream_t s, float* lse,
-                            KeySplit ks, bool accumulate, const float* qscale) {
+                            KeySplit ks, bool accumulate, const float* qscale, int64_t o_cs) {
   if (S <= 0 || B <= 0 || H <= 0) return hipSuccess;
   if (kv.L <= 0 || kv.Lpad % KT != 0 || kv.Lpad < kv.L) return hipErrorInvalidValue;
   if (ks.n < 1 || (int64_t)B * ks.n > 65535) return hipErrorInvalidValue;
@@ -1216,20 +1219,20 @@ hipError_t launch_attention(const T* q, int64_t q_bs, int64_t q_ss, KVStream kv,
   const float c_log2 = scale * 1.4426950408889634f;
   if (hd == 128) {
     if (kind)
-      return launch_hd<T, 128, 1>(q, q_bs, q_ss, kv, B, S, H, c_log2, qscale, o, o_bs, o_ss, lse, ks, acc, s);
-    return launch_hd<T, 128, 0>(q, q_bs, q_ss, kv, B, S, H, c_log2, qscale, o, o_bs, o_ss, lse, ks, acc, s);
+      return launch_hd<T, 128, 1>(q, q_bs, q_ss, kv, B, S, H, c_log2, qscale, o, o_bs, o_ss, o_cs, lse, ks, acc, s);
+    return launch_hd<T, 128, 0>(q, q_bs, q_ss, kv, B, S, H, c_log2, qscale, o, o_bs, o_ss, o_cs, lse, ks, acc, s);
   }
   if (hd == 64) {
     if (kind)
-      return launch_hd<T, 64, 1>(q, q_bs, q_ss, kv, B, S, H, c_log2, qscale, o, o_bs, o_ss, lse, ks, acc, s);
-    return launch_hd<T, 64, 0>(q, q_bs, q_ss, kv, B, S, H, c_log2, qscale, o, o_bs, o_ss, lse, ks, acc, s);
+      return launch_hd<T, 64, 1>(q, q_bs, q_ss, kv, B, S, H, c_log2, qscale, o, o_bs, o_ss, o_cs, lse, ks, acc, s);
+    return launch_hd<T, 64, 0>(q, q_bs, q_ss, kv, B, S, H, c_log2, qscale, o, o_bs, o_ss, o_cs, lse, ks, acc, s);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_attention_q8(const uint8_t* q8, const float* sq, const uint8_t* k8, const float* sk,
                                const uint8_t* v8t, const float* sv, int B, int S, int L, int H, int hd, bf16* o,
-                               float* lse, hipStream_t s, const float* qscale) {
+                               ActLayout lo, float* lse, hipStream_t s, const float* qscale) {
   if (S <= 0 || B <= 0 || H <= 0) return hipSuccess;
   if (L <= 0) return hipErrorInvalidValue;
   const int64_t dim = (int64_t)H * hd;
@@ -1237,8 +1240,8 @@ hipError_t launch_attention_q8(const uint8_t* q8, const float* sq, const uint8_t
   const float c_log2 = 1.4426950408889634f / sqrtf((float)hd);
   // head_dim 128 only: a 64-key tile of 64-byte rows is too small to split over the 8 waves' copies
   if (hd == 128)
-    return launch_q8_hd<128>(q8, (int64_t)S * dim, dim, sq, kv, B, S, H, c_log2, qscale, o, (int64_t)S * dim, dim,
-                             lse, s);
+    return launch_q8_hd<128>(q8, (int64_t)S * dim, dim, sq, kv, B, S, H, c_log2, qscale, o, (int64_t)S * lo.ld, lo.ld,
+                             lo.bs, lse, s);
   return hipErrorInvalidValue;
 }
 
@@ -1342,9 +1345,10 @@ template hipError_t launch_lse_merge<bf16>(const void* const*, const float* cons
 
 template hipError_t launch_attention<float>(const float*, int64_t, int64_t, KVStream, int, int, int, int, float,
                                             float*, int64_t, int64_t, int, hipStream_t, float*, KeySplit, bool,
-                                            const float*);
+                                            const float*, int64_t);
 template hipError_t launch_attention<bf16>(const bf16*, int64_t, int64_t, KVStream, int, int, int, int, float, bf16*,
-                                           int64_t, int64_t, int, hipStream_t, float*, KeySplit, bool, const float*);
+                                           int64_t, int64_t, int, hipStream_t, float*, KeySplit, bool, const float*,
+                                           int64_t);
 
 template <typename T>
 void attention_tile(int kind, int& rows, int& per_cu) {

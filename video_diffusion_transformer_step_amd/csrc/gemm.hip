@@ -90,7 +90,7 @@ __device__ __forceinline__ float4 load_bias4(const float* bias, int n) {
 template <typename OutT, int ACT>
 struct EpiStore {
   OutT* out;
-  int64_t ldo;
+  int64_t ldo, obs;  // element (m, n) at out + m ldo + (n / 32) obs + n % 32 (see ActLayout)
   const float* bias;
   struct Pre {
     float4 b;
@@ -102,7 +102,7 @@ struct EpiStore {
       v.x = apply_act(v.x, ACT); v.y = apply_act(v.y, ACT);
       v.z = apply_act(v.z, ACT); v.w = apply_act(v.w, ACT);
     }
-    OutT* q = out + (int64_t)m * ldo + n;
+    OutT* q = out + (int64_t)m * ldo + (n >> 5) * obs + (n & 31);
     if constexpr (sizeof(OutT) == 2) {
       bf16x4 o;
       o[0] = (bf16)v.x; o[1] = (bf16)v.y; o[2] = (bf16)v.z; o[3] = (bf16)v.w;
@@ -310,7 +310,7 @@ __device__ __forceinline__ void tile_coords(int id, int tiles_m, int tiles_n, in
 inline int group_m(int tiles_n, int K) { return (K >= 4096 && tiles_n < 32) ? 2 : 4; }
 
 template <typename T, int BM, int BN, int WM, int WN, class Epi>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restrict__ A, int64_t lda,
+__global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restrict__ A, int64_t lda, int64_t apr,
                                                                const T* __restrict__ W, int64_t ldw, int64_t wpr,
                                                                int M, int N, int K, int tiles_m, int tiles_n, int gm,
                                                                Epi epi) {
@@ -339,9 +339,11 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restric
 #pragma unroll
   for (int i = 0; i < AC; ++i) {
     const int c = tid + i * NT, r = c >> 3, kc = (c & 7) * E16;
-    pa[i] = A + (int64_t)min(m0 + r, M - 1) * lda + kc;
+    const int64_t m = min(m0 + r, M - 1);
+    pa[i] = apr ? A + ((kc / 32) * apr + m) * 32 + kc % 32 : A + m * lda + kc;  // K step k0 adds k0 * astep
     la[i] = r * ROW + kc;
   }
+  const int64_t astep = apr ? apr : 1;
 #pragma unroll
   for (int i = 0; i < BC; ++i) {
     const int c = tid + i * NT, r = c >> 3, kc = (c & 7) * E16;
@@ -354,7 +356,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restric
   u32x4 ra[AC], rb[BC];
   auto load_full = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < AC; ++i) ra[i] = *reinterpret_cast<const u32x4*>(pa[i] + k0);
+    for (int i = 0; i < AC; ++i) ra[i] = *reinterpret_cast<const u32x4*>(pa[i] + k0 * astep);
 #pragma unroll
     for (int i = 0; i < BC; ++i) rb[i] = *reinterpret_cast<const u32x4*>(pb[i] + k0 * wstep);
   };
@@ -362,7 +364,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restric
 #pragma unroll
     for (int i = 0; i < AC; ++i) {
       const int kk = k0 + ((tid + i * NT) & 7) * E16;
-      ra[i] = kk < K ? *reinterpret_cast<const u32x4*>(pa[i] + k0) : u32x4{0, 0, 0, 0};
+      ra[i] = kk < K ? *reinterpret_cast<const u32x4*>(pa[i] + k0 * astep) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < BC; ++i) {
@@ -470,7 +472,7 @@ struct LdsGemmCfg {
 //  * A (activations, row-major): a stage copies 64-byte segments of 256 rows.  Rows past the
 //    operand's last one start at or beyond the record count, so the buffer's range check turns their
 //    copies into zeros without a memory access; such rows only feed outputs that are not stored.
-//  * W (weights, in K panels of 32 elements; see WMat): the stage of a 256-row tile is one contiguous
+//  * W (weights, in K panels of 32 elements; see KMat): the stage of a 256-row tile is one contiguous
 //    run, 16 KB of bf16 or two runs of 8 KB of E4M3 codes (the two panels of a 64-code step), so every
 //    copy instruction reads whole 128-byte lines.  In a lab loop on the block's shapes this made the
 //    products 3-8 % faster than 64-byte segments of row-major weights.  The panels hold N rounded up to
@@ -496,46 +498,45 @@ struct LdsCopyPlan {
   static_assert(BK == 32, "one W panel (bf16) or two (E4M3) per K step");
   uint32_t oa[C::LA];
   uint32_t ob[C::LB];
-  uint32_t wstage;  // bytes between consecutive K steps of W: 64 * panel rows
+  uint32_t astage, wstage;  // bytes between consecutive K steps of A and W: 64 * panel rows
   __device__ static __forceinline__ const bf16* uniform(const bf16* p) {
     const uint64_t a = (uint64_t)p;
     return (const bf16*)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
                          (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a));
   }
-  // Records of the rows from r0 to the end of a [rows, ld] operand, capped at 2^32 - 1 (a tile's own
-  // offsets stay below 2^31).
-  __device__ static __forceinline__ uint32_t records(int rows, int r0, int64_t ld) {
-    const int64_t b = (int64_t)(rows - r0) * ld * 2;
-    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b < 0xFFFFFFFFll ? b : 0xFFFFFFFFll));
+  // Byte offset of LDS chunk p's source in a tile's panels (pr rows each): row r = p / CH, global chunk
+  // c = slot ^ swizzle; bf16: chunk c of row r's 64-byte panel row; E4M3: chunk c % 2 of row r's
+  // 32-byte row in panel c / 2.
+  __device__ static __forceinline__ uint32_t chunk_offset(int p, int64_t pr) {
+    const int r = p / C::CH, c = (p % C::CH) ^ C::swz(r);
+    return F8 ? (uint32_t)((c >> 1) * 32 * pr + r * 32 + (c & 1) * 16) : (uint32_t)(r * 64 + c * 16);
   }
-  // wpr: rows per W panel (N rounded up to 256); 64 * K * wpr / BK bytes of panels stay below 2^31.
-  __device__ __forceinline__ LdsCopyPlan(int64_t lda, int64_t wpr) : wstage((uint32_t)(64 * wpr)) {
+  // apr, wpr: rows per A and W panel (M and N rounded up to 256); the panels of each operand stay below
+  // 2^31 bytes.
+  __device__ __forceinline__ LdsCopyPlan(int64_t apr, int64_t wpr)
+      : astage((uint32_t)(64 * apr)), wstage((uint32_t)(64 * wpr)) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < C::LA; ++i) {
-      const int p = (i * NW + wave) * 64 + lane, r = p / C::CH, s = p % C::CH;
-      const int c = s ^ C::swz(r);
-      oa[i] = (uint32_t)(((int64_t)r * lda + c * 8) * 2);
-    }
+    for (int i = 0; i < C::LA; ++i) oa[i] = chunk_offset((i * NW + wave) * 64 + lane, apr);
 #pragma unroll
-    for (int i = 0; i < C::LB; ++i) {
-      const int p = (i * NW + wave) * 64 + lane, r = p / C::CH, s = p % C::CH;
-      const int c = s ^ C::swz(r);
-      // bf16: chunk c of row r's 64-byte panel row; E4M3: chunk c % 2 of row r's 32-byte row in panel c / 2
-      ob[i] = F8 ? (uint32_t)((c >> 1) * 32 * wpr + r * 32 + (c & 1) * 16) : (uint32_t)(r * 64 + c * 16);
-    }
+    for (int i = 0; i < C::LB; ++i) ob[i] = chunk_offset((i * NW + wave) * 64 + lane, wpr);
   }
-  // K: the product depth in bf16 units (the panels hold 2 K wpr bytes).
-  __device__ static __forceinline__ LdsTileSrc tile(const bf16* A, int64_t lda, const bf16* W, int64_t wpr, int K,
-                                                    int m0, int n0, int M) {
-    const int64_t wofs = (int64_t)n0 * (F8 ? 32 : 64);  // bytes from the panels' start to row n0 of panel 0
-    return LdsTileSrc{uniform(A + (int64_t)m0 * lda), uniform(W + wofs / 2), records(M, m0, lda),
-                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(2 * (int64_t)K * wpr - wofs))};
+  // Records of the bytes from a tile's first row r0 of panel 0 to the end of the panels (2 K pr bytes
+  // with K in bf16 units).
+  __device__ static __forceinline__ uint32_t records(int K, int64_t pr, int r0) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(2 * (int64_t)K * pr - (int64_t)r0 * (F8 ? 32 : 64)));
+  }
+  // K: the product depth in bf16 units.  Row r0 of panel 0 sits r0 * (F8 ? 32 : 64) bytes in.
+  __device__ static __forceinline__ LdsTileSrc tile(const bf16* A, int64_t apr, const bf16* W, int64_t wpr, int K,
+                                                    int m0, int n0) {
+    return LdsTileSrc{uniform(A + (int64_t)m0 * (F8 ? 16 : 32)), uniform(W + (int64_t)n0 * (F8 ? 16 : 32)),
+                      records(K, apr, m0), records(K, wpr, n0)};
   }
   __device__ __forceinline__ void issue(const LdsTileSrc& t, int k0, char* sa, char* sb) const {
     const int wave = threadIdx.x >> 6;
+    const uint32_t as = (uint32_t)(k0 / BK) * astage;
 #pragma unroll
-    for (int i = 0; i < C::LA; ++i) buffer_copy16(t.ba, t.na, oa[i], k0 * 2, sa + (i * NW + wave) * 1024);
+    for (int i = 0; i < C::LA; ++i) buffer_copy16(t.ba, t.na, oa[i], as, sa + (i * NW + wave) * 1024);
     const uint32_t ws = (uint32_t)(k0 / BK) * wstage;
 #pragma unroll
     for (int i = 0; i < C::LB; ++i) buffer_copy16(t.bb, t.nb, ob[i], ws, sb + (i * NW + wave) * 1024);
@@ -673,7 +674,7 @@ __device__ __forceinline__ void lds_gemm_step(const LdsCopyPlan<BM, BN, BK, WM *
 }
 
 template <int BM, int BN, int BK, int ST, int WM, int WN, class Epi, bool F8, bool M16, bool PERSIST>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(const bf16* __restrict__ A, int64_t lda,
+__global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(const bf16* __restrict__ A, int64_t apr,
                                                                 const bf16* __restrict__ W, int64_t wpr, int M,
                                                                 int N, int K, int tiles_m, int tiles_n, int gm,
                                                                Epi epi) {
@@ -696,8 +697,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(const bf16* __res
   int id = blockIdx.x, tm, tn;
   tile_coords(id, tiles_m, tiles_n, gm, tm, tn);
   using Plan = LdsCopyPlan<BM, BN, BK, NW, M16, F8>;
-  const Plan cp(lda, wpr);
-  LdsTileSrc cur = Plan::tile(A, lda, W, wpr, K, tm * BM, tn * BN, M);
+  const Plan cp(apr, wpr);
+  LdsTileSrc cur = Plan::tile(A, apr, W, wpr, K, tm * BM, tn * BN);
   const int nk = K / BK;  // a multiple of ST
 #pragma unroll
   for (int s = 0; s < ST - 1; ++s) cp.issue(cur, s * BK, sl.a[s], sl.b[s]);
@@ -710,7 +711,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_lds_kernel(const bf16* __res
     LdsTileSrc nxt = cur;  // past the last tile the surplus refills re-copy this tile's stages (never read)
     if (next < ntiles) {
       tile_coords(next, tiles_m, tiles_n, gm, tm2, tn2);
-      nxt = Plan::tile(A, lda, W, wpr, K, tm2 * BM, tn2 * BN, M);
+      nxt = Plan::tile(A, apr, W, wpr, K, tm2 * BM, tn2 * BN);
     }
 
     typename LdsAcc<BM / WM, BN / WN, M16>::type acc;
@@ -776,7 +777,7 @@ struct UsePersistent<EpiScaled<EpiStore<OutT, ACT>>> {
 };
 
 template <int BM, int BN, int BK, int ST, int WM, int WN, class Epi, bool F8 = false>
-hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t wpr, int M, int N, int K, const Epi& epi,
+hipError_t launch_lds(const bf16* A, int64_t apr, const bf16* W, int64_t wpr, int M, int N, int K, const Epi& epi,
                       hipStream_t s) {
   const int tm = (int)ceil_div(M, BM), tn = (int)ceil_div(N, BN);
   constexpr bool M16 = !F8 && UseMfma16<Epi>::value;
@@ -786,7 +787,7 @@ hipError_t launch_lds(const bf16* A, int64_t lda, const bf16* W, int64_t wpr, in
   const int64_t ntiles = (int64_t)tm * tn;
   const int grid = PERSIST ? (int)std::min<int64_t>(ntiles, device_compute_units()) : (int)ntiles;
   hipLaunchKernelGGL((gemm_lds_kernel<BM, BN, BK, ST, WM, WN, Epi, F8, M16, PERSIST>), dim3((unsigned)grid),
-                     dim3(WM * WN * 64), 0, s, A, lda, W, wpr, M, N, K, tm, tn, group_m(tn, K), epi);
+                     dim3(WM * WN * 64), 0, s, A, apr, W, wpr, M, N, K, tm, tn, group_m(tn, K), epi);
   return hipGetLastError();
 }
 
@@ -811,50 +812,51 @@ struct EpiScaled {
 };
 
 // E4M3 product ("Wan 技术深度解析" §5.3: per-token activation, per-tensor weight scales): A codes [M, K]
-// (row stride lda bytes) with per-row scales, W codes [N, K] in K panels (see WMat) with one tensor
-// scale.  K a multiple of 256, lda a multiple of 16 bytes.
+// with per-row scales and W codes [N, K] with one tensor scale, both in K panels (see KMat).  K a
+// multiple of 256; each operand's panels below 2^31 bytes.
 template <class Epi>
-hipError_t run_gemm_e4m3(const uint8_t* A, int64_t lda, const float* a_scales, WMat<uint8_t> W,
-                         const float* w_scale, int M, int N, int K, const Epi& epi, hipStream_t s) {
+hipError_t run_gemm_e4m3(KMat<uint8_t> A, const float* a_scales, KMat<uint8_t> W, const float* w_scale, int M, int N,
+                         int K, const Epi& epi, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  if (N % 4 != 0 || K % 256 != 0 || lda % 16 != 0 || !w_panels_ok(W, N, K) ||
-      (int64_t)K * W.panel >= ((int64_t)1 << 31) || (int64_t)256 * lda >= ((int64_t)1 << 31))
+  if (N % 4 != 0 || K % 256 != 0 || !k_panels_ok(A, M, K) || !k_panels_ok(W, N, K) ||
+      (int64_t)K * A.panel >= ((int64_t)1 << 31) || (int64_t)K * W.panel >= ((int64_t)1 << 31))
     return hipErrorInvalidValue;
   return launch_lds<256, 256, 32, 4, 4, 2, EpiScaled<Epi>, true>(
-      reinterpret_cast<const bf16*>(A), lda / 2, reinterpret_cast<const bf16*>(W.p), W.panel, M, N, K / 2,
+      reinterpret_cast<const bf16*>(A.p), A.panel, reinterpret_cast<const bf16*>(W.p), W.panel, M, N, K / 2,
       EpiScaled<Epi>{a_scales, w_scale, epi}, s);
 }
 
 template <typename T, int BM, int BN, int WM, int WN, class Epi>
-hipError_t launch_cfg(const T* A, int64_t lda, WMat<T> W, int M, int N, int K, const Epi& epi, hipStream_t s) {
+hipError_t launch_cfg(KMat<T> A, KMat<T> W, int M, int N, int K, const Epi& epi, hipStream_t s) {
   const int tm = (int)ceil_div(M, BM), tn = (int)ceil_div(N, BN);
   hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, WM, WN, Epi>), dim3((unsigned)(tm * tn)), dim3(WM * WN * 64), 0,
-                     s, A, lda, W.p, W.ld, W.panel, M, N, K, tm, tn, group_m(tn, K), epi);
+                     s, A.p, A.ld, A.panel, W.p, W.ld, W.panel, M, N, K, tm, tn, group_m(tn, K), epi);
   return hipGetLastError();
 }
 
-// Tile choice.  bf16 products with many rows, K a multiple of 128 and weights in K panels use the
-// asynchronous-copy kernel (256 x 256 tiles, 8 waves of 64 x 128, BK 32, four LDS stages); other bf16
-// products with many rows use the register-staged kernel with 256-row tiles; small products and fp32
-// use 128 x 128.
+// Tile choice.  bf16 products with many rows, K a multiple of 128 and both operands in K panels use
+// the asynchronous-copy kernel (256 x 256 tiles, 8 waves of 64 x 128, BK 32, four LDS stages); other
+// bf16 products with many rows use the register-staged kernel with 256-row tiles; small products and
+// fp32 use 128 x 128.  The register-staged kernel reads either layout.
 template <typename T, class Epi>
-hipError_t run_gemm(const T* A, int64_t lda, WMat<T> W, int M, int N, int K, const Epi& epi, hipStream_t s) {
+hipError_t run_gemm(KMat<T> A, KMat<T> W, int M, int N, int K, const Epi& epi, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (N % 4 != 0 || K % dtype_traits<T>::per16 != 0) return hipErrorInvalidValue;
-  if (W.panel ? !w_panels_ok(W, N, K) : W.ld % dtype_traits<T>::per16 != 0) return hipErrorInvalidValue;
+  if (A.panel ? !k_panels_ok(A, M, K) : A.ld % dtype_traits<T>::per16 != 0) return hipErrorInvalidValue;
+  if (W.panel ? !k_panels_ok(W, N, K) : W.ld % dtype_traits<T>::per16 != 0) return hipErrorInvalidValue;
   if constexpr (sizeof(T) == 2) {
     int cfg = 0;
-    // (the asynchronous-copy kernel addresses a 256-row A tile and the W panels with 32-bit byte offsets)
-    if (W.panel && M >= 4096 && N >= 1024 && K % 128 == 0 && lda % 8 == 0 &&
-        (int64_t)256 * lda * 2 < ((int64_t)1 << 31) && (int64_t)2 * K * W.panel < ((int64_t)1 << 31))
+    // (the asynchronous-copy kernel addresses the panels with 32-bit byte offsets)
+    if (A.panel && W.panel && M >= 4096 && N >= 1024 && K % 128 == 0 &&
+        (int64_t)2 * K * A.panel < ((int64_t)1 << 31) && (int64_t)2 * K * W.panel < ((int64_t)1 << 31))
       cfg = 1;
     else if (M >= 4096 && N % 256 == 0 && N >= 1024) cfg = 2;
     else if (M >= 4096 && N % 128 == 0 && N >= 1024) cfg = 3;
-    if (cfg == 1) return launch_lds<256, 256, 32, 4, 4, 2>(A, lda, W.p, W.panel, M, N, K, epi, s);
-    if (cfg == 2) return launch_cfg<T, 256, 256, 4, 2>(A, lda, W, M, N, K, epi, s);
-    if (cfg == 3) return launch_cfg<T, 256, 128, 4, 2>(A, lda, W, M, N, K, epi, s);
+    if (cfg == 1) return launch_lds<256, 256, 32, 4, 4, 2>(A.p, A.panel, W.p, W.panel, M, N, K, epi, s);
+    if (cfg == 2) return launch_cfg<T, 256, 256, 4, 2>(A, W, M, N, K, epi, s);
+    if (cfg == 3) return launch_cfg<T, 256, 128, 4, 2>(A, W, M, N, K, epi, s);
   }
-  return launch_cfg<T, 128, 128, 2, 2>(A, lda, W, M, N, K, epi, s);
+  return launch_cfg<T, 128, 128, 2, 2>(A, W, M, N, K, epi, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -925,11 +927,12 @@ int device_compute_units() {
 }
 
 template <typename T, typename OutT>
-hipError_t gemm_store(const T* A, int64_t lda, WMat<T> W, int M, int N, int K, const float* bias, int act, OutT* out,
-                      int64_t ldo, hipStream_t s) {
-  if (act == ACT_GELU) return run_gemm<T>(A, lda, W, M, N, K, EpiStore<OutT, ACT_GELU>{out, ldo, bias}, s);
-  if (act == ACT_SILU) return run_gemm<T>(A, lda, W, M, N, K, EpiStore<OutT, ACT_SILU>{out, ldo, bias}, s);
-  return run_gemm<T>(A, lda, W, M, N, K, EpiStore<OutT, ACT_NONE>{out, ldo, bias}, s);
+hipError_t gemm_store(KMat<T> A, KMat<T> W, int M, int N, int K, const float* bias, int act, OutT* out, ActLayout lo,
+                      hipStream_t s) {
+  if (lo.bs != 32 && N % 32 != 0) return hipErrorInvalidValue;
+  if (act == ACT_GELU) return run_gemm<T>(A, W, M, N, K, EpiStore<OutT, ACT_GELU>{out, lo.ld, lo.bs, bias}, s);
+  if (act == ACT_SILU) return run_gemm<T>(A, W, M, N, K, EpiStore<OutT, ACT_SILU>{out, lo.ld, lo.bs, bias}, s);
+  return run_gemm<T>(A, W, M, N, K, EpiStore<OutT, ACT_NONE>{out, lo.ld, lo.bs, bias}, s);
 }
 
 namespace {
@@ -951,39 +954,39 @@ bool qkv_args_ok(int M, int dim, int S, int hd, const QKNormRope& nr) {
 }  // namespace
 
 template <typename T>
-hipError_t gemm_qkv(const T* A, int64_t lda, WMat<T> W, int M, int dim, int K, const float* bias,
+hipError_t gemm_qkv(KMat<T> A, KMat<T> W, int M, int dim, int K, const float* bias,
                     T* qk, int64_t ldo, T* vt, int S, int H, int hd, int Spad, const QKNormRope& nr, hipStream_t s) {
   if (!qkv_args_ok(M, dim, S, hd, nr)) return hipErrorInvalidValue;
-  return run_gemm<T>(A, lda, W, M, 3 * dim, K, make_epi_qkv<T>(qk, ldo, bias, vt, M, dim, S, H, hd, Spad, nr), s);
+  return run_gemm<T>(A, W, M, 3 * dim, K, make_epi_qkv<T>(qk, ldo, bias, vt, M, dim, S, H, hd, Spad, nr), s);
 }
 
 template <typename T>
-hipError_t gemm_residual(const T* A, int64_t lda, WMat<T> W, int M, int N, int K, const float* bias,
+hipError_t gemm_residual(KMat<T> A, KMat<T> W, int M, int N, int K, const float* bias,
                          const float* gate, int chunk, int S, float* x, int64_t ldx, hipStream_t s, float* ystore) {
   EpiResidual epi{x, ldx, bias, gate, chunk, S, N, ystore};
-  return run_gemm<T>(A, lda, W, M, N, K, epi, s);
+  return run_gemm<T>(A, W, M, N, K, epi, s);
 }
 
-hipError_t gemm_e4m3_store(const uint8_t* A, int64_t lda, const float* a_scales, WMat<uint8_t> W,
-                           const float* w_scale, int M, int N, int K, const float* bias, int act, bf16* out, int64_t ldo,
-                           hipStream_t s) {
+hipError_t gemm_e4m3_store(KMat<uint8_t> A, const float* a_scales, KMat<uint8_t> W, const float* w_scale, int M,
+                           int N, int K, const float* bias, int act, bf16* out, ActLayout lo, hipStream_t s) {
+  if (lo.bs != 32 && N % 32 != 0) return hipErrorInvalidValue;
   if (act == ACT_GELU)
-    return run_gemm_e4m3(A, lda, a_scales, W, w_scale, M, N, K, EpiStore<bf16, ACT_GELU>{out, ldo, bias}, s);
-  return run_gemm_e4m3(A, lda, a_scales, W, w_scale, M, N, K, EpiStore<bf16, ACT_NONE>{out, ldo, bias}, s);
+    return run_gemm_e4m3(A, a_scales, W, w_scale, M, N, K, EpiStore<bf16, ACT_GELU>{out, lo.ld, lo.bs, bias}, s);
+  return run_gemm_e4m3(A, a_scales, W, w_scale, M, N, K, EpiStore<bf16, ACT_NONE>{out, lo.ld, lo.bs, bias}, s);
 }
 
-hipError_t gemm_qkv_e4m3(const uint8_t* A, int64_t lda, const float* a_scales, WMat<uint8_t> W,
+hipError_t gemm_qkv_e4m3(KMat<uint8_t> A, const float* a_scales, KMat<uint8_t> W,
                          const float* w_scale, int M, int dim, int K, const float* bias, bf16* qk, int64_t ldo, bf16* vt,
                          int S, int H, int hd, int Spad, const QKNormRope& nr, hipStream_t s) {
   if (!qkv_args_ok(M, dim, S, hd, nr)) return hipErrorInvalidValue;
-  return run_gemm_e4m3(A, lda, a_scales, W, w_scale, M, 3 * dim, K,
+  return run_gemm_e4m3(A, a_scales, W, w_scale, M, 3 * dim, K,
                        make_epi_qkv<bf16>(qk, ldo, bias, vt, M, dim, S, H, hd, Spad, nr), s);
 }
 
-hipError_t gemm_e4m3_residual(const uint8_t* A, int64_t lda, const float* a_scales, WMat<uint8_t> W,
+hipError_t gemm_e4m3_residual(KMat<uint8_t> A, const float* a_scales, KMat<uint8_t> W,
                               const float* w_scale, int M, int N, int K, const float* bias, const float* gate,
                               int chunk, int S, float* x, int64_t ldx, hipStream_t s, float* ystore) {
-  return run_gemm_e4m3(A, lda, a_scales, W, w_scale, M, N, K, EpiResidual{x, ldx, bias, gate, chunk, S, N, ystore},
+  return run_gemm_e4m3(A, a_scales, W, w_scale, M, N, K, EpiResidual{x, ldx, bias, gate, chunk, S, N, ystore},
                        s);
 }
 
@@ -1005,20 +1008,20 @@ hipError_t launch_sinusoid(const float* t_host, int B, int freq_dim, float* emb,
   return hipGetLastError();
 }
 
-template hipError_t gemm_store<float, float>(const float*, int64_t, WMat<float>, int, int, int, const float*, int,
-                                             float*, int64_t, hipStream_t);
-template hipError_t gemm_store<bf16, bf16>(const bf16*, int64_t, WMat<bf16>, int, int, int, const float*, int, bf16*,
-                                           int64_t, hipStream_t);
-template hipError_t gemm_store<bf16, float>(const bf16*, int64_t, WMat<bf16>, int, int, int, const float*, int,
-                                            float*, int64_t, hipStream_t);
-template hipError_t gemm_qkv<float>(const float*, int64_t, WMat<float>, int, int, int, const float*, float*, int64_t,
-                                    float*, int, int, int, int, const QKNormRope&, hipStream_t);
-template hipError_t gemm_qkv<bf16>(const bf16*, int64_t, WMat<bf16>, int, int, int, const float*, bf16*, int64_t,
-                                   bf16*, int, int, int, int, const QKNormRope&, hipStream_t);
-template hipError_t gemm_residual<float>(const float*, int64_t, WMat<float>, int, int, int, const float*,
-                                         const float*, int, int, float*, int64_t, hipStream_t, float*);
-template hipError_t gemm_residual<bf16>(const bf16*, int64_t, WMat<bf16>, int, int, int, const float*, const float*,
-                                        int, int, float*, int64_t, hipStream_t, float*);
+template hipError_t gemm_store<float, float>(KMat<float>, KMat<float>, int, int, int, const float*, int, float*,
+                                             ActLayout, hipStream_t);
+template hipError_t gemm_store<bf16, bf16>(KMat<bf16>, KMat<bf16>, int, int, int, const float*, int, bf16*, ActLayout,
+                                           hipStream_t);
+template hipError_t gemm_store<bf16, float>(KMat<bf16>, KMat<bf16>, int, int, int, const float*, int, float*,
+                                            ActLayout, hipStream_t);
+template hipError_t gemm_qkv<float>(KMat<float>, KMat<float>, int, int, int, const float*, float*, int64_t, float*,
+                                    int, int, int, int, const QKNormRope&, hipStream_t);
+template hipError_t gemm_qkv<bf16>(KMat<bf16>, KMat<bf16>, int, int, int, const float*, bf16*, int64_t, bf16*, int,
+                                   int, int, int, const QKNormRope&, hipStream_t);
+template hipError_t gemm_residual<float>(KMat<float>, KMat<float>, int, int, int, const float*, const float*, int,
+                                         int, float*, int64_t, hipStream_t, float*);
+template hipError_t gemm_residual<bf16>(KMat<bf16>, KMat<bf16>, int, int, int, const float*, const float*, int, int,
+                                        float*, int64_t, hipStream_t, float*);
 template hipError_t gemv<float>(const float*, int, int, const float*, int, const float*, int, int, float*,
                                 hipStream_t);
 template hipError_t gemv<bf16>(const bf16*, int, int, const float*, int, const float*, int, int, float*,

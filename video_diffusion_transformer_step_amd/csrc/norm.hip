@@ -67,7 +67,7 @@ template <typename T, int NC>
 __global__ __launch_bounds__(256) void ln_mod_kernel(const float* __restrict__ x, int64_t rows, int dim, int S,
                                                       int mode, const float* __restrict__ p0,
                                                       const float* __restrict__ p1, int c_shift, int c_scale,
-                                                      float eps, T* __restrict__ u) {
+                                                      float eps, T* __restrict__ u, int64_t ldu, int64_t ubs) {
   constexpr bool CACHE = NC <= 12;
   const int lane = threadIdx.x & 63;
   const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * LN_ROWS;
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void ln_mod_kernel(const float* __restrict__ x
       }
     }
     const float rstd = 1.f / sqrtf(wave_sum(sq) / (float)dim + eps);
-    T* ur = u + row * dim;
+    T* ur = u + row * ldu;  // channel c at ur + (c / 32) ubs + c % 32
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       const int idx = i * 64 + lane;
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256) void ln_mod_kernel(const float* __restrict__ x
         }
         const float n0 = (v[i].x - mean) * rstd, n1 = (v[i].y - mean) * rstd;
         const float n2 = (v[i].z - mean) * rstd, n3 = (v[i].w - mean) * rstd;
-        store4<T>(ur + idx * 4, fmaf(n0, vsc.x, vsh.x), fmaf(n1, vsc.y, vsh.y), fmaf(n2, vsc.z, vsh.z),
+        store4<T>(ur + (idx >> 3) * ubs + (idx & 7) * 4, fmaf(n0, vsc.x, vsh.x), fmaf(n1, vsc.y, vsh.y), fmaf(n2, vsc.z, vsh.z),
                   fmaf(n3, vsc.w, vsh.w));
       }
     }
@@ -159,7 +159,7 @@ template <typename T, int NT>
 __global__ __launch_bounds__(NT) void ln_mod_wide_kernel(const float* __restrict__ x, int64_t rows, int dim, int S,
                                                           int mode, const float* __restrict__ p0,
                                                           const float* __restrict__ p1, int c_shift, int c_scale,
-                                                          float eps, T* __restrict__ u) {
+                                                          float eps, T* __restrict__ u, int64_t ldu, int64_t ubs) {
   constexpr int NWV = NT / 64;
   __shared__ float part[2][NWV];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -214,14 +214,14 @@ __global__ __launch_bounds__(NT) void ln_mod_wide_kernel(const float* __restrict
         sq += (a * a + bb * bb) + (c * c + d * d);
       }
     const float rstd = 1.f / sqrtf(block_sum(sq, 1) / (float)dim + eps);
-    T* ur = u + row * dim;
+    T* ur = u + row * ldu;  // channel c at ur + (c / 32) ubs + c % 32
 #pragma unroll
     for (int i = 0; i < LNW_CH; ++i) {
       const int idx = i * NT + tid;
       if (idx < n4) {
         const float n0 = (v[i].x - mean) * rstd, n1 = (v[i].y - mean) * rstd;
         const float n2 = (v[i].z - mean) * rstd, n3 = (v[i].w - mean) * rstd;
-        store4<T>(ur + idx * 4, fmaf(n0, sc[i].x, sh[i].x), fmaf(n1, sc[i].y, sh[i].y), fmaf(n2, sc[i].z, sh[i].z),
+        store4<T>(ur + (idx >> 3) * ubs + (idx & 7) * 4, fmaf(n0, sc[i].x, sh[i].x), fmaf(n1, sc[i].y, sh[i].y), fmaf(n2, sc[i].z, sh[i].z),
                   fmaf(n3, sc[i].w, sh[i].w));
       }
     }
@@ -353,21 +353,22 @@ __global__ __launch_bounds__(256) void qk_rms_kernel(const float* __restrict__ s
 
 template <typename T>
 hipError_t launch_ln_mod(const float* x, int64_t rows, int dim, int S, int mode, const float* p0, const float* p1,
-                         int c_shift, int c_scale, float eps, T* u, hipStream_t s) {
+                         int c_shift, int c_scale, float eps, T* u, ActLayout lu, hipStream_t s) {
   if (dim % 4 != 0 || dim > LN_MAX4 * 256) return hipErrorInvalidValue;
+  if (lu.bs != 32 && dim % 32 != 0) return hipErrorInvalidValue;
   if (rows <= 0) return hipSuccess;
   if (dim <= 6 * 256) {
     const dim3 grid((unsigned)ceil_div(rows, 4 * LN_ROWS));
     hipLaunchKernelGGL((ln_mod_kernel<T, 6>), grid, dim3(256), 0, s, x, rows, dim, S, mode, p0, p1, c_shift, c_scale,
-                       eps, u);
+                       eps, u, lu.ld, lu.bs);
   } else {
     const dim3 grid((unsigned)ceil_div(rows, (int64_t)LNW_ROWS));
     if (dim <= 4 * LNW_CH * 256)
       hipLaunchKernelGGL((ln_mod_wide_kernel<T, 256>), grid, dim3(256), 0, s, x, rows, dim, S, mode, p0, p1, c_shift,
-                         c_scale, eps, u);
+                         c_scale, eps, u, lu.ld, lu.bs);
     else
       hipLaunchKernelGGL((ln_mod_wide_kernel<T, 512>), grid, dim3(512), 0, s, x, rows, dim, S, mode, p0, p1, c_shift,
-                         c_scale, eps, u);
+                         c_scale, eps, u, lu.ld, lu.bs);
   }
   return hipGetLastError();
 }
@@ -401,9 +402,9 @@ hipError_t launch_qk_rms(const float* ssq, int64_t rows, int dim, float eps, T* 
 }
 
 template hipError_t launch_ln_mod<float>(const float*, int64_t, int, int, int, const float*, const float*, int, int,
-                                         float, float*, hipStream_t);
+                                         float, float*, ActLayout, hipStream_t);
 template hipError_t launch_ln_mod<bf16>(const float*, int64_t, int, int, int, const float*, const float*, int, int,
-                                        float, bf16*, hipStream_t);
+                                        float, bf16*, ActLayout, hipStream_t);
 template hipError_t launch_rope_qk<float>(const float*, const float*, int64_t, float*, float*, int64_t, int, int, int,
                                           int, int, int, float, hipStream_t);
 template hipError_t launch_rope_qk<bf16>(const bf16*, const bf16*, int64_t, bf16*, bf16*, int64_t, int, int, int,

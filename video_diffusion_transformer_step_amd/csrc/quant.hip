@@ -176,15 +176,17 @@ __global__ __launch_bounds__(256) void quant_vt_kernel(const bf16* __restrict__ 
 }
 
 // Per-row E4M3 codes (scale = amax / 448): one workgroup per row of `cols` bf16 values (cols % 8 == 0).
-__global__ __launch_bounds__(256) void quant_rows_kernel(const bf16* __restrict__ x, int64_t ld, int cols,
-                                                         uint8_t* __restrict__ codes, int64_t ldc,
+// Element (row, n) of x at x + row ld + (n / 32) xbs + n % 32, its code at codes + row ldc + (n / 32) cbs +
+// n % 32 (row-major: xbs = cbs = 32; K panels: see ActLayout).
+__global__ __launch_bounds__(256) void quant_rows_kernel(const bf16* __restrict__ x, int64_t ld, int64_t xbs, int cols,
+                                                         uint8_t* __restrict__ codes, int64_t ldc, int64_t cbs,
                                                          float* __restrict__ scales) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
   const bf16* src = x + row * ld;
   float m = 0.f;
-  for (int c = threadIdx.x; c < cols / 8; c += 256) {
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(src + c * 8);
+  for (int c = threadIdx.x; c < cols / 8; c += 256) {  // chunk c: elements 8c .. 8c + 7
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(src + (c >> 2) * xbs + (c & 3) * 8);
     const bf16* e = reinterpret_cast<const bf16*>(&raw);
 #pragma unroll
     for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf((float)e[j]));
@@ -196,12 +198,12 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const bf16* __restrict_
   const float inv = m > 0.f ? 448.f / m : 0.f;
   uint8_t* dst = codes + row * ldc;
   for (int c = threadIdx.x; c < cols / 8; c += 256) {
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(src + c * 8);
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(src + (c >> 2) * xbs + (c & 3) * 8);
     const bf16* e = reinterpret_cast<const bf16*>(&raw);
     float y[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) y[j] = fminf(fmaxf((float)e[j] * inv, -448.f), 448.f);
-    *reinterpret_cast<uint2*>(dst + c * 8) = make_uint2(e4m3x4(y[0], y[1], y[2], y[3]), e4m3x4(y[4], y[5], y[6], y[7]));
+    *reinterpret_cast<uint2*>(dst + (c >> 2) * cbs + (c & 3) * 8) = make_uint2(e4m3x4(y[0], y[1], y[2], y[3]), e4m3x4(y[4], y[5], y[6], y[7]));
   }
   if (threadIdx.x == 0) scales[row] = m > 0.f ? m / 448.f : 0.f;
 }
@@ -243,11 +245,12 @@ __global__ __launch_bounds__(256) void quant_tensor_kernel(const bf16* __restric
 
 }  // namespace
 
-hipError_t launch_quant_rows_e4m3(const bf16* x, int64_t ld, int rows, int cols, uint8_t* codes, int64_t ldc,
+hipError_t launch_quant_rows_e4m3(const bf16* x, ActLayout lx, int rows, int cols, uint8_t* codes, ActLayout lc,
                                   float* scales, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (cols <= 0 || cols % 8 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)rows), dim3(256), 0, s, x, ld, cols, codes, ldc, scales);
+  if (cols <= 0 || cols % 8 != 0 || ((lx.bs != 32 || lc.bs != 32) && cols % 32 != 0)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)rows), dim3(256), 0, s, x, lx.ld, lx.bs, cols, codes, lc.ld,
+                     lc.bs, scales);
   return hipGetLastError();
 }
 

@@ -158,11 +158,13 @@ size_t block_plan(const wan_block_cfg& c, const wan_grid& g, int B, char* base, 
   const int64_t S = (int64_t)g.T * g.Hp * g.Wp, BS = (int64_t)B * S, dim = c.dim;
   Carve cv{base};
   BlockWs<T> w;
-  w.u = cv.take<T>(BS * dim);
+  // u, o, h (and the E4M3 codes a8) are the products' A operands, held in K panels of Mp rows
+  const int64_t Mp = panel_rows(BS);
+  w.u = cv.take<T>(Mp * dim);
   w.qkv = cv.take<T>(BS * 2 * dim);  // q | k per token (v goes to vt)
   w.vt = cv.take<T>((size_t)B * dim * pad64(S));
-  w.o = cv.take<T>(BS * dim);
-  w.h = cv.take<T>(BS * c.ffn_dim);
+  w.o = cv.take<T>(Mp * dim);
+  w.h = cv.take<T>(Mp * c.ffn_dim);
   w.mod = cv.take<float>((size_t)B * 6 * dim);
   w.ssq = cv.take<float>((size_t)(2 * dim / 32) * BS);
   w.rq = cv.take<float>((size_t)BS);
@@ -180,7 +182,7 @@ size_t block_plan(const wan_block_cfg& c, const wan_grid& g, int B, char* base, 
   w.a8 = nullptr;
   w.sa = nullptr;
   if (c.flags & WAN_FLAG_FP8_GEMM) {
-    w.a8 = cv.take<uint8_t>(BS * std::max<int64_t>(dim, c.ffn_dim));
+    w.a8 = cv.take<uint8_t>(Mp * std::max<int64_t>(dim, c.ffn_dim));
     w.sa = cv.take<float>(BS);
   }
   if (out) *out = w;
@@ -196,6 +198,9 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
   const int S = g.T * g.Hp * g.Wp, BS = B * S, dim = c.dim, H = c.heads, hd = c.head_dim;
   const int Spad = (int)pad64(S);
   const float scale = 1.f / sqrtf((float)hd);
+  // The products' A operands (u, o, h and their E4M3 codes) live in K panels (see KMat / ActLayout).
+  const ActLayout pan = act_panels(BS);
+  const int64_t o_cs = pan.bs;  // attention output: channel block stride of the panels (row stride 32)
   // self-attention branch
   // the block's six modulation vectors e0 + mod_bias ("Wan 技术深度解析" §2.5), formed once
   HIP_TRY(launch_mod_combine(e0, W.mod_bias, B, dim, w.mod, st));
@@ -206,7 +211,7 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
     PROF_TRY(WAN_K_O_GEMM, launch_gated_add(x, attn_y, w.mod, 2, (int64_t)BS, dim, S, st));
   } else {
     float* ystore = attn_mode == WAN_ATTN_CACHE_STORE ? attn_y : nullptr;
-    PROF_TRY(WAN_K_LN1, launch_ln_mod<T>(x, BS, dim, S, 0, w.mod, nullptr, 0, 1, c.ln_eps, w.u, st));
+    PROF_TRY(WAN_K_LN1, launch_ln_mod<T>(x, BS, dim, S, 0, w.mod, nullptr, 0, 1, c.ln_eps, w.u, pan, st));
     // q, k -> qkv[:, 0 .. 2 dim) (row stride 2 dim), with the RMSNorm gains and the 3D RoPE applied
     // ("图解 Wan2.1 I2V" §5.3 ①②) and the rows' sums of squares in ssq; v -> V^T directly.  The
     // prologue clears V^T's padded keys and writes the rotation table the epilogue reads.
@@ -214,11 +219,11 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
                                                           hd, c.rope_theta, st));
     const QKNormRope nr{W.gq, W.gk, w.ssq, w.rope, g.T, g.Hp, g.Wp};
     if (f8g) {  // E4M3 products ("Wan 技术深度解析" §5.3): per-token codes of u, then the product
-      PROF_TRY(WAN_K_QUANT, launch_quant_rows_e4m3((const bf16*)w.u, dim, BS, dim, w.a8, dim, w.sa, st));
-      PROF_TRY(WAN_K_QKV_GEMM, gemm_qkv_e4m3(w.a8, dim, w.sa, w_panels<uint8_t>(Q8->wqkv, 3 * dim), Q8->s_wqkv, BS, dim, dim,
+      PROF_TRY(WAN_K_QUANT, launch_quant_rows_e4m3((const bf16*)w.u, pan, BS, dim, w.a8, pan, w.sa, st));
+      PROF_TRY(WAN_K_QKV_GEMM, gemm_qkv_e4m3(k_panels<uint8_t>(w.a8, BS), w.sa, k_panels<uint8_t>(Q8->wqkv, 3 * dim), Q8->s_wqkv, BS, dim, dim,
                                              W.bqkv, (bf16*)w.qkv, 2 * dim, (bf16*)w.vt, S, H, hd, Spad, nr, st));
     } else {
-      PROF_TRY(WAN_K_QKV_GEMM, gemm_qkv<T>(w.u, dim, w_panels<T>(W.wqkv, 3 * dim), BS, dim, dim, W.bqkv, w.qkv, 2 * dim, w.vt,
+      PROF_TRY(WAN_K_QKV_GEMM, gemm_qkv<T>(k_panels<T>(w.u, BS), k_panels<T>(W.wqkv, 3 * dim), BS, dim, dim, W.bqkv, w.qkv, 2 * dim, w.vt,
                                            S, H, hd, Spad, nr, st));
     }
     // the RMS factors: k rows scaled in place, r_q kept for the attention's score scale
@@ -229,54 +234,57 @@ int block_fwd_t(const wan_block_cfg& c, const wan_block_weights& W, const wan_gr
         PROF_TRY(WAN_K_QUANT, launch_quant_q(w.qkv, 2 * dim, B, S, H, hd, (int8_t*)w.q8, w.sq, st));
         PROF_TRY(WAN_K_QUANT, launch_quant_k(w.qkv + dim, 2 * dim, B, S, H, hd, (int8_t*)w.k8, w.sk, st));
         PROF_TRY(WAN_K_QUANT, launch_quant_vt(w.vt, (int64_t)B * dim, Spad, (int)round_up(S, 128), w.v8t, w.sv, st));
-        PROF_TRY(WAN_K_SELF_ATTN, launch_attention_q8(w.q8, w.sq, w.k8, w.sk, w.v8t, w.sv, B, S, S, H, hd, w.o, nullptr,
+        PROF_TRY(WAN_K_SELF_ATTN, launch_attention_q8(w.q8, w.sq, w.k8, w.sk, w.v8t, w.sv, B, S, S, H, hd, w.o, pan, nullptr,
                                                       st, w.rq));
       }
     }
     if (!(c.flags & WAN_FLAG_FP8_ATTN)) {
       KVStream self{w.qkv + dim, (int64_t)S * 2 * dim, 2 * dim, w.vt, S, Spad};
       PROF_TRY(WAN_K_SELF_ATTN, launch_attention<T>(w.qkv, (int64_t)S * 2 * dim, 2 * dim, self, B, S, H, hd,
-                                                    scale, w.o, (int64_t)S * dim, dim, 0, st, nullptr, KeySplit{},
-                                                    false, w.rq));
+                                                    scale, w.o, (int64_t)S * pan.ld, pan.ld, 0, st, nullptr,
+                                                    KeySplit{}, false, w.rq, o_cs));
     }
     if (f8g) {
-      PROF_TRY(WAN_K_QUANT, launch_quant_rows_e4m3((const bf16*)w.o, dim, BS, dim, w.a8, dim, w.sa, st));
-      PROF_TRY(WAN_K_O_GEMM, gemm_e4m3_residual(w.a8, dim, w.sa, w_panels<uint8_t>(Q8->wo, dim), Q8->s_wo, BS, dim, dim, W.bo,
+      PROF_TRY(WAN_K_QUANT, launch_quant_rows_e4m3((const bf16*)w.o, pan, BS, dim, w.a8, pan, w.sa, st));
+      PROF_TRY(WAN_K_O_GEMM, gemm_e4m3_residual(k_panels<uint8_t>(w.a8, BS), w.sa, k_panels<uint8_t>(Q8->wo, dim), Q8->s_wo, BS, dim, dim, W.bo,
                                                 w.mod, 2, S, x, dim, st, ystore));
     } else {
-      PROF_TRY(WAN_K_O_GEMM, gemm_residual<T>(w.o, dim, w_panels<T>(W.wo, dim), BS, dim, dim, W.bo, w.mod, 2, S, x,
+      PROF_TRY(WAN_K_O_GEMM, gemm_residual<T>(k_panels<T>(w.o, BS), k_panels<T>(W.wo, dim), BS, dim, dim, W.bo, w.mod, 2, S, x,
                                               dim, st, ystore));
     }
   }  // self-attention branch
   // cross-attention branch (no adaLN, no RoPE)
-  PROF_TRY(WAN_K_LN3, launch_ln_mod<T>(x, BS, dim, S, 1, W.ln3_w, W.ln3_b, 0, 0, c.ln_eps, w.u, st));
+  PROF_TRY(WAN_K_LN3, launch_ln_mod<T>(x, BS, dim, S, 1, W.ln3_w, W.ln3_b, 0, 0, c.ln_eps, w.u, pan, st));
   T* qc = w.qkv;  // reuse: [BS, dim]
-  PROF_TRY(WAN_K_CROSS_Q_GEMM, (gemm_store<T, T>(w.u, dim, w_panels<T>(W.wcq, dim), BS, dim, dim, W.bcq, ACT_NONE, qc, dim, st)));
+  PROF_TRY(WAN_K_CROSS_Q_GEMM, (gemm_store<T, T>(k_panels<T>(w.u, BS), k_panels<T>(W.wcq, dim), BS, dim, dim, W.bcq, ACT_NONE,
+                                                qc, act_rows(dim), st)));
   const int Lt = c.text_len, Li = c.img_len;
   KVStream st_txt{kv.k_txt, (int64_t)Lt * dim, dim, kv.vt_txt, Lt, (int)pad64(Lt)};
   KVStream st_img{kv.k_img, (int64_t)Li * dim, dim, kv.vt_img, Li, (int)pad64(Li > 0 ? Li : 1)};
   // text, then (I2V) image: two launches, the second adding its softmax's result to the first's (one
   // launch holding both streams' state would spill registers)
   PROF_TRY(WAN_K_CROSS_ATTN, launch_attention<T>(qc, (int64_t)S * dim, dim, st_txt, B, S, H, hd, scale, w.o,
-                                                 (int64_t)S * dim, dim, 1, st));
+                                                 (int64_t)S * pan.ld, pan.ld, 1, st, nullptr, KeySplit{}, false,
+                                                 nullptr, o_cs));
   if (Li > 0)
     PROF_TRY(WAN_K_CROSS_ATTN, launch_attention<T>(qc, (int64_t)S * dim, dim, st_img, B, S, H, hd, scale,
-                                                   w.o, (int64_t)S * dim, dim, 1, st, nullptr, KeySplit{}, true));
-  PROF_TRY(WAN_K_CROSS_O_GEMM, gemm_residual<T>(w.o, dim, w_panels<T>(W.wco, dim), BS, dim, dim, W.bco, nullptr, 0, S, x, dim, st));
+                                                   w.o, (int64_t)S * pan.ld, pan.ld, 1, st, nullptr, KeySplit{}, true,
+                                                   nullptr, o_cs));
+  PROF_TRY(WAN_K_CROSS_O_GEMM, gemm_residual<T>(k_panels<T>(w.o, BS), k_panels<T>(W.wco, dim), BS, dim, dim, W.bco, nullptr, 0, S, x, dim, st));
   // FFN branch
-  PROF_TRY(WAN_K_LN2, launch_ln_mod<T>(x, BS, dim, S, 0, w.mod, nullptr, 3, 4, c.ln_eps, w.u, st));
+  PROF_TRY(WAN_K_LN2, launch_ln_mod<T>(x, BS, dim, S, 0, w.mod, nullptr, 3, 4, c.ln_eps, w.u, pan, st));
   if (f8g) {
     const int F = c.ffn_dim;
-    PROF_TRY(WAN_K_QUANT, launch_quant_rows_e4m3((const bf16*)w.u, dim, BS, dim, w.a8, dim, w.sa, st));
-    PROF_TRY(WAN_K_FFN1_GEMM, gemm_e4m3_store(w.a8, dim, w.sa, w_panels<uint8_t>(Q8->w1, F), Q8->s_w1, BS, F, dim, W.b1,
-                                              ACT_GELU, (bf16*)w.h, F, st));
-    PROF_TRY(WAN_K_QUANT, launch_quant_rows_e4m3((const bf16*)w.h, F, BS, F, w.a8, F, w.sa, st));
-    PROF_TRY(WAN_K_FFN2_GEMM, gemm_e4m3_residual(w.a8, F, w.sa, w_panels<uint8_t>(Q8->w2, dim), Q8->s_w2, BS, dim, F, W.b2,
+    PROF_TRY(WAN_K_QUANT, launch_quant_rows_e4m3((const bf16*)w.u, pan, BS, dim, w.a8, pan, w.sa, st));
+    PROF_TRY(WAN_K_FFN1_GEMM, gemm_e4m3_store(k_panels<uint8_t>(w.a8, BS), w.sa, k_panels<uint8_t>(Q8->w1, F), Q8->s_w1,
+                                              BS, F, dim, W.b1, ACT_GELU, (bf16*)w.h, pan, st));
+    PROF_TRY(WAN_K_QUANT, launch_quant_rows_e4m3((const bf16*)w.h, pan, BS, F, w.a8, pan, w.sa, st));
+    PROF_TRY(WAN_K_FFN2_GEMM, gemm_e4m3_residual(k_panels<uint8_t>(w.a8, BS), w.sa, k_panels<uint8_t>(Q8->w2, dim), Q8->s_w2, BS, dim, F, W.b2,
                                                  w.mod, 5, S, x, dim, st));
   } else {
-    PROF_TRY(WAN_K_FFN1_GEMM, (gemm_store<T, T>(w.u, dim, w_panels<T>(W.w1, c.ffn_dim), BS, c.ffn_dim, dim, W.b1, ACT_GELU, w.h,
-                                                c.ffn_dim, st)));
-    PROF_TRY(WAN_K_FFN2_GEMM, gemm_residual<T>(w.h, c.ffn_dim, w_panels<T>(W.w2, dim), BS, dim, c.ffn_dim, W.b2, w.mod,
+    PROF_TRY(WAN_K_FFN1_GEMM, (gemm_store<T, T>(k_panels<T>(w.u, BS), k_panels<T>(W.w1, c.ffn_dim), BS, c.ffn_dim, dim, W.b1,
+                                                ACT_GELU, w.h, pan, st)));
+    PROF_TRY(WAN_K_FFN2_GEMM, gemm_residual<T>(k_panels<T>(w.h, BS), k_panels<T>(W.w2, dim), BS, dim, c.ffn_dim, W.b2, w.mod,
                                                5, S, x, dim, st));
   }
   return WAN_OK;
@@ -402,9 +410,11 @@ int wan_patch_embed(const wan_block_cfg* cfg, const float* p, int64_t tokens, in
   if (cfg->dtype == WAN_BF16) {
     bf16* pb = reinterpret_cast<bf16*>(ws);
     HIP_TRY(launch_convert<bf16>(p, pb, (int64_t)M * K, hs(stream)));
-    HIP_TRY((gemm_store<bf16, float>(pb, K, w_rows<bf16>(w_pe, K), M, cfg->dim, K, b_pe, ACT_NONE, x, cfg->dim, hs(stream))));
+    HIP_TRY((gemm_store<bf16, float>(k_rows<bf16>(pb, K), k_rows<bf16>(w_pe, K), M, cfg->dim, K, b_pe, ACT_NONE, x,
+                                     act_rows(cfg->dim), hs(stream))));
   } else {
-    HIP_TRY((gemm_store<float, float>(p, K, w_rows<float>(w_pe, K), M, cfg->dim, K, b_pe, ACT_NONE, x, cfg->dim, hs(stream))));
+    HIP_TRY((gemm_store<float, float>(k_rows<float>(p, K), k_rows<float>(w_pe, K), M, cfg->dim, K, b_pe, ACT_NONE, x,
+                                      act_rows(cfg->dim), hs(stream))));
   }
   return WAN_OK;
 }
@@ -450,8 +460,10 @@ template <typename T>
 static int context_embed_t(const wan_block_cfg& c, const void* ctx, int rows, int in_dim, const void* w1,
                            const float* b1, const void* w2, const float* b2, void* out, void* ws, hipStream_t st) {
   T* hid = reinterpret_cast<T*>(ws);
-  HIP_TRY((gemm_store<T, T>((const T*)ctx, in_dim, w_rows<T>(w1, in_dim), rows, c.dim, in_dim, b1, ACT_GELU, hid, c.dim, st)));
-  HIP_TRY((gemm_store<T, T>(hid, c.dim, w_rows<T>(w2, c.dim), rows, c.dim, c.dim, b2, ACT_NONE, (T*)out, c.dim, st)));
+  HIP_TRY((gemm_store<T, T>(k_rows<T>(ctx, in_dim), k_rows<T>(w1, in_dim), rows, c.dim, in_dim, b1, ACT_GELU, hid,
+                            act_rows(c.dim), st)));
+  HIP_TRY((gemm_store<T, T>(k_rows<T>(hid, c.dim), k_rows<T>(w2, c.dim), rows, c.dim, c.dim, b2, ACT_NONE, (T*)out,
+                            act_rows(c.dim), st)));
   return WAN_OK;
 }
 
@@ -505,9 +517,9 @@ static int cross_kv_t(const wan_block_cfg& c, const wan_cross_kv_weights& w, con
     T* k = (T*)(which == 0 ? out.k_txt : out.k_img);
     T* vt = (T*)(which == 0 ? out.vt_txt : out.vt_img);
     const int M = B * L;
-    HIP_TRY((gemm_store<T, T>(ctx, dim, w_rows<T>(wkv, dim), M, dim, dim, bkv, ACT_NONE, k, dim, st)));
-    HIP_TRY((gemm_store<T, T>(ctx, dim, w_rows<T>(wkv + (int64_t)dim * dim, dim), M, dim, dim, bkv ? bkv + dim : nullptr,
-                              ACT_NONE, tmp, dim, st)));
+    HIP_TRY((gemm_store<T, T>(k_rows<T>(ctx, dim), k_rows<T>(wkv, dim), M, dim, dim, bkv, ACT_NONE, k, act_rows(dim), st)));
+    HIP_TRY((gemm_store<T, T>(k_rows<T>(ctx, dim), k_rows<T>(wkv + (int64_t)dim * dim, dim), M, dim, dim,
+                              bkv ? bkv + dim : nullptr, ACT_NONE, tmp, act_rows(dim), st)));
     HIP_TRY(launch_transpose_heads<T>(tmp, dim, 0, B, L, c.heads, c.head_dim, (int)pad64(L), vt, st));
   }
   return WAN_OK;
@@ -637,12 +649,14 @@ int wan_head_fwd(const wan_block_cfg* cfg, const wan_head_weights* w, int32_t ou
   hipStream_t st = hs(stream);
   if (cfg->dtype == WAN_BF16) {
     bf16* u = reinterpret_cast<bf16*>(ws);
-    HIP_TRY(launch_ln_mod<bf16>(x, rows, dim, S, 2, w->head_mod, e, 0, 1, cfg->ln_eps, u, st));
-    HIP_TRY((gemm_store<bf16, float>(u, dim, w_rows<bf16>(w->wh, dim), (int)rows, N, dim, w->bh, ACT_NONE, out, N, st)));
+    HIP_TRY(launch_ln_mod<bf16>(x, rows, dim, S, 2, w->head_mod, e, 0, 1, cfg->ln_eps, u, act_rows(dim), st));
+    HIP_TRY((gemm_store<bf16, float>(k_rows<bf16>(u, dim), k_rows<bf16>(w->wh, dim), (int)rows, N, dim, w->bh, ACT_NONE,
+                                     out, act_rows(N), st)));
   } else {
     float* u = reinterpret_cast<float*>(ws);
-    HIP_TRY(launch_ln_mod<float>(x, rows, dim, S, 2, w->head_mod, e, 0, 1, cfg->ln_eps, u, st));
-    HIP_TRY((gemm_store<float, float>(u, dim, w_rows<float>(w->wh, dim), (int)rows, N, dim, w->bh, ACT_NONE, out, N, st)));
+    HIP_TRY(launch_ln_mod<float>(x, rows, dim, S, 2, w->head_mod, e, 0, 1, cfg->ln_eps, u, act_rows(dim), st));
+    HIP_TRY((gemm_store<float, float>(k_rows<float>(u, dim), k_rows<float>(w->wh, dim), (int)rows, N, dim, w->bh,
+                                      ACT_NONE, out, act_rows(N), st)));
   }
   return WAN_OK;
 }
@@ -901,7 +915,7 @@ int wan_attention_q8_fwd(const void* q8, const float* sq, const void* k8, const 
   WAN_TRY(need_ptr(o, "o"));
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3)) return fail(WAN_EINVAL, "lse is not 4-byte aligned");
   HIP_TRY(launch_attention_q8((const uint8_t*)q8, sq, (const uint8_t*)k8, sk, (const uint8_t*)v8t, sv, B, Sq, Sk,
-                              heads, head_dim, (bf16*)o, lse, hs(stream)));
+                              heads, head_dim, (bf16*)o, act_rows((int64_t)heads * head_dim), lse, hs(stream)));
   return WAN_OK;
 }
 
@@ -912,7 +926,8 @@ int wan_quantize_rows_e4m3(const void* x, int64_t ld, int32_t rows, int32_t cols
   WAN_TRY(need_ptr(x, "x"));
   WAN_TRY(need_ptr(codes, "codes"));
   WAN_TRY(need_f32(scales, "scales"));
-  HIP_TRY(launch_quant_rows_e4m3((const bf16*)x, ld, rows, cols, (uint8_t*)codes, ldc, scales, hs(stream)));
+  HIP_TRY(launch_quant_rows_e4m3((const bf16*)x, act_rows(ld), rows, cols, (uint8_t*)codes, act_rows(ldc), scales,
+                                 hs(stream)));
   return WAN_OK;
 }
 
@@ -942,14 +957,13 @@ int wan_pack_weight(int32_t elem_bytes, const void* w, int64_t N, int64_t K, voi
   return WAN_OK;
 }
 
-int wan_gemm_e4m3(const void* a, int64_t lda, const float* a_scales, const void* w, const float* w_scale,
-                  int32_t M, int32_t N, int32_t K, const float* bias, int32_t act, void* y, int64_t ldy,
-                  wan_stream_t stream) {
+int wan_gemm_e4m3(const void* a, const float* a_scales, const void* w, const float* w_scale, int32_t M, int32_t N,
+                  int32_t K, const float* bias, int32_t act, void* y, int64_t ldy, wan_stream_t stream) {
   if (M <= 0 || N <= 0 || N % 4 != 0) return fail(WAN_EINVAL, "M > 0 and N a positive multiple of 4");
   if (K <= 0 || K % 256 != 0) return fail(WAN_EUNSUPPORTED, "K %d must be a positive multiple of 256", K);
-  if (lda < K || lda % 16 != 0 || ldy < N || ldy % 4 != 0) return fail(WAN_EINVAL, "bad row strides");
-  if ((int64_t)K * panel_rows(N) >= ((int64_t)1 << 31)) return fail(WAN_EUNSUPPORTED, "W panels of 2 GiB or more");
-  if ((int64_t)256 * lda >= ((int64_t)1 << 31)) return fail(WAN_EUNSUPPORTED, "lda too large");
+  if (ldy < N || ldy % 4 != 0) return fail(WAN_EINVAL, "bad row stride ldy");
+  if ((int64_t)K * panel_rows(N) >= ((int64_t)1 << 31) || (int64_t)K * panel_rows(M) >= ((int64_t)1 << 31))
+    return fail(WAN_EUNSUPPORTED, "operand panels of 2 GiB or more");
   if (act != ACT_NONE && act != ACT_GELU) return fail(WAN_EINVAL, "act must be 0 or 1");
   WAN_TRY(need_ptr(a, "a"));
   WAN_TRY(need_ptr(w, "w"));
@@ -957,8 +971,8 @@ int wan_gemm_e4m3(const void* a, int64_t lda, const float* a_scales, const void*
   WAN_TRY(need_f32(w_scale, "w_scale"));
   WAN_TRY(opt_ptr(bias, "bias"));
   WAN_TRY(need_ptr(y, "y"));
-  HIP_TRY(gemm_e4m3_store((const uint8_t*)a, lda, a_scales, w_panels<uint8_t>(w, N), w_scale, M, N, K, bias, act,
-                          (bf16*)y, ldy, hs(stream)));
+  HIP_TRY(gemm_e4m3_store(k_panels<uint8_t>(a, M), a_scales, k_panels<uint8_t>(w, N), w_scale, M, N, K, bias, act,
+                          (bf16*)y, act_rows(ldy), hs(stream)));
   return WAN_OK;
 }
 

@@ -59,9 +59,18 @@ inline int64_t rope_table_entries(int T_, int Hp, int Wp, int hd) {
 //                    already holds the sums), b = row / S;
 //  mode 1 (affine):  u = LN(x) * w + bias (w = p0, bias = p1, each [dim]);
 //  mode 2 (head):    u = LN(x) * (1 + (hm[1] + e[b])) + (hm[0] + e[b]) with hm = p0 [2, dim], e = p1 [B, dim].
+// Where a kernel writes (or reads) an activation [M, N]: element (m, n) at m * ld + (n / 32) * bs + n % 32.
+// Row-major with row stride ld: bs = 32.  K panels of the products' A operand (KMat): ld = 32,
+// bs = 32 * panel_rows(M), N % 32 == 0.
+struct ActLayout {
+  int64_t ld, bs;
+};
+inline ActLayout act_rows(int64_t ld) { return ActLayout{ld, 32}; }
+inline ActLayout act_panels(int64_t M) { return ActLayout{32, 32 * ((M + 255) / 256 * 256)}; }
+// u in the layout lu (see ActLayout; panels need dim % 32 == 0).
 template <typename T>
 hipError_t launch_ln_mod(const float* x, int64_t rows, int dim, int S, int mode, const float* p0, const float* p1,
-                         int c_shift, int c_scale, float eps, T* u, hipStream_t s);
+                         int c_shift, int c_scale, float eps, T* u, ActLayout lu, hipStream_t s);
 // 3D RoPE (no norm) on the q and k rows of B * T_ * Hp * Wp tokens (row strides ld_in / ld_out; in place
 // allowed); hd % 8 == 0.
 template <typename T>
@@ -75,43 +84,45 @@ hipError_t launch_qk_rms(const float* ssq, int64_t rows, int dim, float eps, T* 
                          hipStream_t s);
 
 // ---- GEMM (gemm.hip) --------------------------------------------------------
-// A weight operand W [N, K]: row-major with row stride ld (panel == 0), or in K panels of 32 elements
-// (panel > 0, the rows of each panel: N rounded up to a multiple of 256): element (n, k) at
-// ((k / 32) * panel + n) * 32 + k % 32, rows N .. panel - 1 zero (launch_pack_panels writes it).  In
-// panels, the 32-deep K step of a 256-row weight tile is one contiguous run of whole cache lines.
+// A product operand X [R, K] (the activations A [M, K] or the weights W [N, K]): row-major with row
+// stride ld (panel == 0), or in K panels of 32 elements (panel > 0, the rows of each panel: R rounded
+// up to a multiple of 256): element (r, k) at ((k / 32) * panel + r) * 32 + k % 32.  Weight panels hold
+// zeros in rows N .. panel - 1 (launch_pack_panels); activation panels hold whatever the workspace
+// held there, which only reaches outputs that are not stored.  In panels, the 32-deep K step of a
+// 256-row tile is one contiguous run of whole cache lines.
 template <typename T>
-struct WMat {
+struct KMat {
   const T* p;
   int64_t ld;
   int64_t panel;
 };
-inline int64_t panel_rows(int64_t N) { return (N + 255) / 256 * 256; }
+inline int64_t panel_rows(int64_t R) { return (R + 255) / 256 * 256; }
 template <typename T>
-inline WMat<T> w_rows(const void* p, int64_t ld) {
-  return WMat<T>{static_cast<const T*>(p), ld, 0};
+inline KMat<T> k_rows(const void* p, int64_t ld) {
+  return KMat<T>{static_cast<const T*>(p), ld, 0};
 }
 template <typename T>
-inline WMat<T> w_panels(const void* p, int64_t N) {
-  return WMat<T>{static_cast<const T*>(p), 0, panel_rows(N)};
+inline KMat<T> k_panels(const void* p, int64_t R) {
+  return KMat<T>{static_cast<const T*>(p), 0, panel_rows(R)};
 }
 template <typename T>
-inline bool w_panels_ok(const WMat<T>& w, int64_t N, int64_t K) {
-  return w.panel >= N && w.panel % 256 == 0 && K % 32 == 0;
+inline bool k_panels_ok(const KMat<T>& x, int64_t R, int64_t K) {
+  return x.panel >= R && x.panel % 256 == 0 && K % 32 == 0;
 }
 // Row-major [rows, cols] of elem_bytes-byte elements (row stride ld elements) -> K panels of 32
 // ([cols / 32][panel_rows(rows)][32], zero rows past `rows`).  cols % 32 == 0, ld * elem_bytes % 16 == 0.
 hipError_t launch_pack_panels(const void* src, int64_t rows, int64_t cols, int64_t ld, int elem_bytes, void* dst,
                               hipStream_t s);
 
-// C[m, n] = sum_k A[m, k] * W[n, k]   (A [M, K] row-major, W [N, K] as a WMat)
+// C[m, n] = sum_k A[m, k] * W[n, k]   (A [M, K] and W [N, K], each a KMat)
 // Epilogues:
 //   store:      out[m, n] = act(C + bias[n])  (OutT = T or float)
 //   residual:   x[m, n] += g(m, n) * (C + bias[n]), g = gate[m / S][chunk][n] from a [B, 6, N] table
 //               (the block's e0 + modulation bias), or 1 if gate is null; ystore (optional, row stride N)
 //               also receives C + bias.
 template <typename T, typename OutT>
-hipError_t gemm_store(const T* A, int64_t lda, WMat<T> W, int M, int N, int K, const float* bias, int act, OutT* out,
-                      int64_t ldo, hipStream_t s);
+hipError_t gemm_store(KMat<T> A, KMat<T> W, int M, int N, int K, const float* bias, int act, OutT* out, ActLayout lo,
+                      hipStream_t s);
 // Q/K/V projection (N = 3 dim): q, k columns to qk[m, 0 .. 2 dim) (row stride ldo), v columns to
 // V^T [B, H, hd, Spad] (keys permuted within 16-key groups for bf16; see launch_transpose_heads);
 // m = b * S + pos.  Only keys pos < S are written: the positions of keys S .. Spad - 1 are left as they
@@ -132,23 +143,22 @@ struct QKNormRope {
   int T, Hp, Wp;
 };
 template <typename T>
-hipError_t gemm_qkv(const T* A, int64_t lda, WMat<T> W, int M, int dim, int K, const float* bias,
+hipError_t gemm_qkv(KMat<T> A, KMat<T> W, int M, int dim, int K, const float* bias,
                     T* qk, int64_t ldo, T* vt, int S, int H, int hd, int Spad, const QKNormRope& nr,
                     hipStream_t s);
 template <typename T>
-hipError_t gemm_residual(const T* A, int64_t lda, WMat<T> W, int M, int N, int K, const float* bias,
+hipError_t gemm_residual(KMat<T> A, KMat<T> W, int M, int N, int K, const float* bias,
                          const float* gate, int chunk, int S, float* x, int64_t ldx, hipStream_t s,
                          float* ystore = nullptr);
-// E4M3 products: C = (sum_k A[m, k] W[n, k]) * a_scales[m] * w_scale[0] over E4M3 codes (A row stride
-// lda bytes, a multiple of 16; W in K panels; K % 256 == 0), then the store (bf16 out, act NONE or GELU)
-// or residual epilogue.
-hipError_t gemm_e4m3_store(const uint8_t* A, int64_t lda, const float* a_scales, WMat<uint8_t> W,
+// E4M3 products: C = (sum_k A[m, k] W[n, k]) * a_scales[m] * w_scale[0] over E4M3 codes (A and W in K
+// panels; K % 256 == 0), then the store (bf16 out, act NONE or GELU) or residual epilogue.
+hipError_t gemm_e4m3_store(KMat<uint8_t> A, const float* a_scales, KMat<uint8_t> W,
                            const float* w_scale, int M, int N, int K, const float* bias, int act, bf16* out,
-                           int64_t ldo, hipStream_t s);
-hipError_t gemm_e4m3_residual(const uint8_t* A, int64_t lda, const float* a_scales, WMat<uint8_t> W,
+                           ActLayout lo, hipStream_t s);
+hipError_t gemm_e4m3_residual(KMat<uint8_t> A, const float* a_scales, KMat<uint8_t> W,
                               const float* w_scale, int M, int N, int K, const float* bias, const float* gate,
                               int chunk, int S, float* x, int64_t ldx, hipStream_t s, float* ystore = nullptr);
-hipError_t gemm_qkv_e4m3(const uint8_t* A, int64_t lda, const float* a_scales, WMat<uint8_t> W,
+hipError_t gemm_qkv_e4m3(KMat<uint8_t> A, const float* a_scales, KMat<uint8_t> W,
                          const float* w_scale, int M, int dim, int K, const float* bias, bf16* qk, int64_t ldo, bf16* vt,
                          int S, int H, int hd, int Spad, const QKNormRope& nr, hipStream_t s);
 // y[b, n] = out_act(sum_k W[n, k] * in_act(x[b, k]) + bias[n]) for b < B (fp32 x, y).
@@ -186,19 +196,21 @@ void attention_tile(int kind, int& rows, int& per_cu);
 // added to what o holds (a second key/value stream after a first launch; not with key splits, and not
 // for bf16 kind 0, which runs the ping-pong kernel).  qscale (NULL = 1): [B, S] float32, a per-query
 // factor of the score scale (the block's RMSNorm factor r_q of a query whose row is not yet normalised).
+// o_cs: channel n of a row at (n / 32) o_cs + n % 32 from the row's start (32: row-major; the products'
+// K panels: o_ss = 32 and o_cs = 32 * rows per panel, see ActLayout).
 template <typename T>
 hipError_t launch_attention(const T* q, int64_t q_bs, int64_t q_ss, KVStream kv, int B, int S, int H, int hd,
                             float scale, T* o, int64_t o_bs, int64_t o_ss, int kind, hipStream_t s,
                             float* lse = nullptr, KeySplit ks = KeySplit{}, bool accumulate = false,
-                            const float* qscale = nullptr);
+                            const float* qscale = nullptr, int64_t o_cs = 32);
 
 // Quantised attention (INT8 Q.K, FP8 P.V): q8 [B, S, H, hd] INT8 codes with sq [B, H, S]; k8 [B, L, H, hd]
 // INT8 codes with sk [B, H, ceil(L / 64)]; v8t [B, H, hd, round_up(L, 128)] E4M3 codes (keys in P.V
 // order, zero past L) with sv [B, H, hd]; o [B, S, H, hd] bf16; lse [B, H, S] or NULL; qscale [B, S] or
-// NULL, as for launch_attention.
+// NULL, as for launch_attention; o row (b, s) = row b S + s of the layout lo.
 hipError_t launch_attention_q8(const uint8_t* q8, const float* sq, const uint8_t* k8, const float* sk,
                                const uint8_t* v8t, const float* sv, int B, int S, int L, int H, int hd, bf16* o,
-                               float* lse, hipStream_t s, const float* qscale = nullptr);
+                               ActLayout lo, float* lse, hipStream_t s, const float* qscale = nullptr);
 
 // ---- quantisers (quant.hip) --------------------------------------------------
 // x rows [B*S, *] bf16 with head h at columns h*hd (row stride ld elements).
@@ -214,7 +226,8 @@ hipError_t launch_quant_vt(const bf16* vt, int64_t rows, int Lpad_in, int Lpad_o
 
 // E4M3 codes of activations per row (scale = amax / 448 per row) and of a whole tensor (one scale,
 // written to *scale on the device; amax_word is a 4-byte device scratch word).
-hipError_t launch_quant_rows_e4m3(const bf16* x, int64_t ld, int rows, int cols, uint8_t* codes, int64_t ldc,
+// (x and the codes in the layouts lx, lc: element (row, n) as in ActLayout, the codes in bytes)
+hipError_t launch_quant_rows_e4m3(const bf16* x, ActLayout lx, int rows, int cols, uint8_t* codes, ActLayout lc,
                                   float* scales, hipStream_t s);
 hipError_t launch_quant_tensor_e4m3(const bf16* x, int64_t n, uint8_t* codes, float* scale, uint32_t* amax_word,
                                     hipStream_t s);
