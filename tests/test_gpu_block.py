@@ -80,10 +80,13 @@ SMALL = [
     ("tiny", {"T": 3, "H": 12, "W": 20, "B": 2, "img_len": 7, "img_dim": 32}),  # 180 tokens, 2 rows
     ("tiny", {"dtype": "bf16", "T": 3, "H": 12, "W": 20, "B": 2, "dim": 256, "heads": 2, "head_dim": 128,
             "ffn_dim": 640, "text_len": 70, "img_len": 9, "img_dim": 32}),  # hd 128, ragged tiles
+    # 45-token grid, B = 3: an odd row count (135) and a batch boundary inside a pair of LayerNorm rows
+    ("tiny", {"dtype": "bf16", "T": 3, "H": 6, "W": 10, "B": 3}),
 ]
 
 
-@pytest.mark.parametrize("name,over", SMALL, ids=["tiny", "tiny-dual", "tiny-bf16", "tiny-180tok-B2", "bf16-hd128-ragged"])
+@pytest.mark.parametrize("name,over", SMALL, ids=["tiny", "tiny-dual", "tiny-bf16", "tiny-180tok-B2", "bf16-hd128-ragged",
+                                                  "bf16-45tok-B3"])
 def test_block_small_full(name, over):
     require_gpu()
     c = wi.get_config(name).replace(**over)

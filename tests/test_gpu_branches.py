@@ -124,7 +124,7 @@ def _check_branches(c, x, e0, bw, t_emb, i_emb, rows, ref, tol_y, tol_ffn, tol_c
 
 
 @pytest.mark.parametrize("name,over", SMALL, ids=["tiny", "tiny-dual", "tiny-bf16", "tiny-180tok-B2",
-                                                   "bf16-hd128-ragged"])
+                                                   "bf16-hd128-ragged", "bf16-45tok-B3"])
 def test_branches_small_full(name, over):
     """Every element of each branch output, at the small block configurations."""
     require_gpu()

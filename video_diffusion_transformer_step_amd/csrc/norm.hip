@@ -90,6 +90,7 @@ __global__ __launch_bounds__(256) void ln_mod_kernel(const float* __restrict__ x
   if (row0 >= rows) return;
   if constexpr (CACHE) load_row(row0);  // (wide rows: no registers to spare for the next row)
   int64_t bcur = -1;
+  uint2 held[sizeof(T) == 2 ? NC : 1];  // K panels, bf16: the even row of a pair (see below)
   for (int rr = 0; rr < LN_ROWS; ++rr) {
     const int64_t row = row0 + rr;
     if (row >= rows) return;
@@ -125,6 +126,57 @@ __global__ __launch_bounds__(256) void ln_mod_kernel(const float* __restrict__ x
     }
     const float rstd = 1.f / sqrtf(wave_sum(sq) / (float)dim + eps);
     T* ur = u + row * ldu;  // channel c at ur + (c / 32) ubs + c % 32
+    if constexpr (sizeof(T) == 2) {
+      if (ldu == 32) {
+        // K panels: a bf16 row's 32 channels of a panel are 64 bytes, half a line whose other half is
+        // the next row.  Rows pair up: the even row's packed outputs wait for the odd row's, then one
+        // v_permlane32_swap per dword gives the lower 32 lanes the even row's chunks i 64 + 32 .. + 63
+        // and the upper lanes the odd row's chunks i 64 .. + 31, so each store instruction writes both
+        // rows of the same panels: whole 128-byte lines.
+        uint2 w[NC];
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+          const int idx = i * 64 + lane;
+          float4 vsh, vsc;
+          if constexpr (CACHE) {
+            vsh = sh[i];
+            vsc = sc[i];
+          } else if (idx < n4) {
+            modulation(b, idx, vsh, vsc);
+          }
+          bf16x4 o;
+          o[0] = (bf16)fmaf((v[i].x - mean) * rstd, vsc.x, vsh.x);
+          o[1] = (bf16)fmaf((v[i].y - mean) * rstd, vsc.y, vsh.y);
+          o[2] = (bf16)fmaf((v[i].z - mean) * rstd, vsc.z, vsh.z);
+          o[3] = (bf16)fmaf((v[i].w - mean) * rstd, vsc.w, vsh.w);
+          w[i] = __builtin_bit_cast(uint2, o);  // lanes past n4 hold values that are never stored
+        }
+        if ((rr & 1) == 0 && rr + 1 < LN_ROWS && row + 1 < rows) {  // even row of a pair: wait
+#pragma unroll
+          for (int i = 0; i < NC; ++i) held[i] = w[i];
+          continue;
+        }
+        if (rr & 1) {  // odd row: rows row - 1 (held) and row, one line per panel and store
+          const int64_t prow = row - 1 + (lane >> 5);
+          T* pr = u + prow * 32;
+#pragma unroll
+          for (int i = 0; i < NC; ++i) {
+            const auto x = __builtin_amdgcn_permlane32_swap(held[i].x, w[i].x, false, false);
+            const auto y = __builtin_amdgcn_permlane32_swap(held[i].y, w[i].y, false, false);
+            const int c1 = i * 64 + (lane & 31), c2 = c1 + 32;  // chunks of row prow
+            if (c1 < n4) *reinterpret_cast<uint2*>(pr + (c1 >> 3) * ubs + (c1 & 7) * 4) = make_uint2(x[0], y[0]);
+            if (c2 < n4) *reinterpret_cast<uint2*>(pr + (c2 >> 3) * ubs + (c2 & 7) * 4) = make_uint2(x[1], y[1]);
+          }
+        } else {  // a row without a partner
+#pragma unroll
+          for (int i = 0; i < NC; ++i) {
+            const int idx = i * 64 + lane;
+            if (idx < n4) *reinterpret_cast<uint2*>(ur + (idx >> 3) * ubs + (idx & 7) * 4) = w[i];
+          }
+        }
+        continue;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       const int idx = i * 64 + lane;

@@ -208,6 +208,44 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const bf16* __restrict_
   if (threadIdx.x == 0) scales[row] = m > 0.f ? m / 448.f : 0.f;
 }
 
+// The same codes for x and codes in K panels (ActLayout ld = 32; xbs, cbs = 32 * rows per panel): a wave
+// takes 8 consecutive rows.  Lane l reads the 8 values (16 bytes) of row r0 + (l % 32) / 4 at chunk l % 4
+// of panel 2 j + l / 32, so each load covers the 512-byte runs of two panels, and the codes leave as
+// 256-byte runs.  Rows past `rows` (up to the panels' padded row count) are read and coded but get no
+// scale.
+__global__ __launch_bounds__(256) void quant_rows_panels_kernel(const bf16* __restrict__ x, int64_t xbs, int rows,
+                                                                int npanel, uint8_t* __restrict__ codes, int64_t cbs,
+                                                                float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 8;
+  if (r0 >= rows) return;  // uniform in the wave
+  const int half = lane >> 5, ch = lane & 3;
+  const int64_t row = r0 + ((lane & 31) >> 2);
+  const bf16* src = x + row * 32 + ch * 8;  // panel p at src + p xbs
+  float m = 0.f;
+  for (int p = half; p < npanel; p += 2) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(src + p * xbs);
+    const bf16* e = reinterpret_cast<const bf16*>(&raw);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf((float)e[j]));
+  }
+  // the row's 8 lanes: chunk (lane bits 0, 1) and panel parity (bit 5)
+  m = fmaxf(m, __shfl_xor(m, 1, 64));
+  m = fmaxf(m, __shfl_xor(m, 2, 64));
+  m = fmaxf(m, __shfl_xor(m, 32, 64));
+  const float inv = m > 0.f ? 448.f / m : 0.f;
+  uint8_t* dst = codes + row * 32 + ch * 8;
+  for (int p = half; p < npanel; p += 2) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(src + p * xbs);
+    const bf16* e = reinterpret_cast<const bf16*>(&raw);
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = fminf(fmaxf((float)e[j] * inv, -448.f), 448.f);
+    *reinterpret_cast<uint2*>(dst + p * cbs) = make_uint2(e4m3x4(y[0], y[1], y[2], y[3]), e4m3x4(y[4], y[5], y[6], y[7]));
+  }
+  if (half == 0 && ch == 0 && row < rows) scales[row] = m > 0.f ? m / 448.f : 0.f;
+}
+
 // Per-tensor E4M3 codes: amax over the whole tensor (non-negative floats order like their bits, so an
 // unsigned atomic max collects it), then the codes.
 __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* p, uint32_t v) { *p = v; }
@@ -249,6 +287,12 @@ hipError_t launch_quant_rows_e4m3(const bf16* x, ActLayout lx, int rows, int col
                                   float* scales, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (cols <= 0 || cols % 8 != 0 || ((lx.bs != 32 || lc.bs != 32) && cols % 32 != 0)) return hipErrorInvalidValue;
+  const int64_t pbs = 32 * panel_rows(rows);
+  if (lx.ld == 32 && lc.ld == 32 && lx.bs == pbs && lc.bs == pbs) {  // both in K panels
+    hipLaunchKernelGGL(quant_rows_panels_kernel, dim3((unsigned)ceil_div((int64_t)rows, (int64_t)32)), dim3(256), 0, s,
+                       x, lx.bs, rows, cols / 32, codes, lc.bs, scales);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)rows), dim3(256), 0, s, x, lx.ld, lx.bs, cols, codes, lc.ld,
                      lc.bs, scales);
   return hipGetLastError();
