@@ -4,20 +4,21 @@
 //
 // Every linear layer computes y = x W^T + b with W stored [out, in] ("图解 Wan2.1
 // I2V" §5.3-§5.5 and the Conv3d patch embedding of §5.1), so both operands are
-// contiguous along K (an "NT" product).
+// contiguous along K (an "NT" product).  The block's products take both operands in
+// K panels of 32 (KMat: each 32-deep K step of a 256-row tile is one contiguous run);
+// the other linear layers take them row-major.
 //
 // Two kernels share the tile order and the epilogues:
-//  * gemm_lds_kernel (bf16, K a multiple of 128; the block's large products):
-//    256 x 256 tiles, 8 waves of 64 x 128, K steps of 32 copied global -> LDS by
-//    asynchronous direct-to-LDS buffer loads (16 bytes a lane) into a ring of four
-//    stages, three steps ahead of their use (no staging registers); rows past the
-//    operands' ends are zeros from the buffers' range check; the plain-store products
-//    run one workgroup per CU walking several tiles, the next tile's first stages
-//    copied during the current tile's last steps;
+//  * gemm_lds_kernel (bf16 / E4M3, K a multiple of 128, both operands in panels; the
+//    block's large products): 256 x 256 tiles, 8 waves of 64 x 128, K steps of 32
+//    copied global -> LDS by asynchronous direct-to-LDS buffer loads (16 bytes a lane)
+//    into a ring of four stages, three steps ahead of their use (no staging
+//    registers); the plain-store products run one workgroup per CU walking several
+//    tiles, the next tile's first stages copied during the current tile's last steps;
 //  * gemm_nt_kernel (everything else): K steps of 128 bytes staged through
-//    double-buffered, row-padded LDS with register prefetch of the next step;
-//    loads are predicate-free (out-of-range rows clamped, a final partial K step
-//    zero-filled).
+//    double-buffered, row-padded LDS with register prefetch of the next step, either
+//    operand row-major or in panels; loads are predicate-free (out-of-range rows
+//    clamped, a final partial K step zero-filled).
 // Common to both:
 //  * the MFMA is issued as C^T = W A^T (A-operand = weight rows), so a lane's
 //    accumulator holds 4 consecutive output columns of one row: the epilogue
@@ -467,16 +468,14 @@ struct LdsGemmCfg {
 // 16 bytes at lds + 16 i).  The compiler counts them as plain vector-memory loads, so the fragment
 // reads of a step wait only for their own results; with the FLAT form in flight every LDS read would
 // wait for all outstanding LDS accesses.  Each operand tile has one wave-uniform base (its first row)
-// and a record count (the bytes from there to the end of the operand); each lane a 32-bit byte offset
-// (row, permuted chunk) that is the same for every tile; the K position is the scalar offset.
-//  * A (activations, row-major): a stage copies 64-byte segments of 256 rows.  Rows past the
-//    operand's last one start at or beyond the record count, so the buffer's range check turns their
-//    copies into zeros without a memory access; such rows only feed outputs that are not stored.
-//  * W (weights, in K panels of 32 elements; see KMat): the stage of a 256-row tile is one contiguous
-//    run, 16 KB of bf16 or two runs of 8 KB of E4M3 codes (the two panels of a 64-code step), so every
-//    copy instruction reads whole 128-byte lines.  In a lab loop on the block's shapes this made the
-//    products 3-8 % faster than 64-byte segments of row-major weights.  The panels hold N rounded up to
-//    256 rows (zero past N), so a tile's rows all exist.
+// and a record count (the bytes from there to the end of its panels); each lane a 32-bit byte offset
+// (row, permuted chunk) that is the same for every tile; the K step sets the scalar offset.  Both
+// operands are in K panels of 32 elements (see KMat): the stage of a 256-row tile is one contiguous
+// run, 16 KB of bf16 or two runs of 8 KB of E4M3 codes (the two panels of a 64-code step), so every
+// copy instruction reads whole 128-byte lines.  In a lab loop on the block's shapes this made the
+// products 6-12 % faster than 64-byte segments of row-major operands.  The panels hold the rows
+// rounded up to 256 (weights: zero past N; activations: unstored rows past M), so a tile's rows all
+// exist.
 __device__ __forceinline__ void buffer_copy16(const void* base, uint32_t records, uint32_t voff, uint32_t soff,
                                               char* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
