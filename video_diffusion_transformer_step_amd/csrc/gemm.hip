@@ -306,9 +306,14 @@ __device__ __forceinline__ void tile_coords(int id, int tiles_m, int tiles_n, in
   tn = w / gsz;
 }
 
-// Row-group size of the tile order (measured on the block's shapes): wide products (>= 32 column
-// tiles) share weights best in groups of 4, long-K products in groups of 2, the rest in groups of 8.
-inline int group_m(int tiles_n, int K) { return (K >= 4096 && tiles_n < 32) ? 2 : 4; }
+// Row-group size of the tile order (measured on the block's shapes with both operands in K panels):
+// long-K products with few column tiles (FFN2) share weights best in groups of 2, products of 16 to
+// 31 column tiles (Q/K/V) in groups of 8, the rest (O, cross-q, cross-O; FFN1's 35 column tiles) in
+// groups of 4.
+inline int group_m(int tiles_n, int K) {
+  if (K >= 4096 && tiles_n < 32) return 2;
+  return tiles_n >= 16 && tiles_n < 32 ? 8 : 4;
+}
 
 template <typename T, int BM, int BN, int WM, int WN, class Epi>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const T* __restrict__ A, int64_t lda, int64_t apr,
